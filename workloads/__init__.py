@@ -1,0 +1,16 @@
+"""Seeded synthetic inputs for IKBO target attention.
+
+This package draws inputs only: sequence lengths, candidate-to-user mappings and
+N(0,1) tensors quantised to the dtype the kernel receives.  It holds none of the
+attention arithmetic, so both the fp64 oracle's tests and the GPU path can use it
+without sharing any of the method's code.
+"""
+
+from .ikbo import (  # noqa: F401
+    CONFIG_NAMES,
+    Workload,
+    bf16_bits_to_f32,
+    f32_to_bf16_bits,
+    make_custom,
+    make_workload,
+)
