@@ -1,0 +1,300 @@
+"""Benchmark of IKBO target attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2_typical]
+
+One step is the whole hot path for one request batch: validation, the host
+grouping pass and work list built from the host copy of the candidate-to-user
+mapping (as an inference runtime holds it), the work-list upload, and the
+persistent attention kernel.  Inputs are resident in HBM before timing.
+Rank 0 prints one JSON line (the contract fields plus ``roofline`` and
+``cpu_baseline``); with ``--report`` extra measurements (cold-cache kernel
+times, the materialised-broadcast comparator) are added under ``extra``.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "IKBO attn BF16 TFLOP/s (+% MFMA peak) and HBM bytes vs materialized broadcast"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3
+DOMINANT_KERNEL = "ikbo_attn_bf16_kernel<128>"
+
+WORKLOAD_TEXT = {
+    "c1_tiny_f32": "tiny fp32: 4 users, L~U[16,64], 20 candidates, n_q=1, H=2, d=32",
+    "c2_typical": "typical request: 1024 candidates over 15 users (multinomial), L~U[256,2048], n_q=1, H=4, d=128, bf16",
+    "c3_skewed": "skewed: 1023 candidates over 32 users (Zipf 1.2), L~U[1,4096] with two L=1 users, n_q=1, H=4, d=128, bf16",
+    "c4_large": "large: 10000 candidates over 150 users, L~U[512,4096], n_q=4, H=8, d=128, bf16",
+    "c5_fused": "fused self+target: 2048 candidates over 30 users, causal self over L~U[256,2048], H=4, d=128, bf16",
+    "p_app11": "App. 11 shape: 32 users x 64 candidates, n_q=64, L=1024, H=2, d=128, bf16",
+}
+
+
+def algorithmic_counts(w):
+    """FLOPs (FA convention, softmax not counted) and HBM bytes of one step."""
+    L = w.lengths.astype(np.float64)
+    cnt = w.counts.astype(np.float64)
+    elem = 2 if w.dtype == "bf16" else 4
+    flops = 4.0 * w.n_q * w.d * w.H * float(np.dot(cnt, L))
+    rows = w.n_cand * w.n_q
+    byts = elem * w.H * w.d * (2.0 * rows + 2.0 * w.total_len)  # Q read + O write, K + V once
+    if w.with_self:
+        flops += 4.0 * w.d * w.H * float(np.sum(L * (L + 1.0) / 2.0))
+        byts += 2.0 * elem * w.H * w.d * w.total_len  # q_user read + out_user write
+    bcast_len = float(np.dot(cnt, L))
+    mat_bytes = elem * w.H * w.d * (2.0 * rows + 2.0 * w.total_len) + 2.0 * 2.0 * elem * w.H * w.d * bcast_len
+    return flops, byts, mat_bytes
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("ikbo_kernels.hip", "ikbo_kernels.h", "ikbo_plan.cpp", "ikbo_plan.h"):
+        with open(os.path.join(ROOT, "broadcast_free_target_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload):
+    """Per-launch HBM bytes from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"ikbo_attn_bf16_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as fh:
+            s = json.load(fh)
+        if s.get("kernel_source_hash") != kernel_source_hash():
+            return None
+        return float(s["hbm_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def upload(w):
+    import torch
+    t = {}
+    for name in w.tensors:
+        a = np.ascontiguousarray(w.raw(name))
+        if w.dtype == "bf16":
+            t[name] = torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        else:
+            t[name] = torch.from_numpy(a).cuda()
+    t["user_offsets"] = torch.from_numpy(w.user_offsets.copy()).cuda()
+    t["cand_to_user"] = torch.from_numpy(w.cand_to_user.copy()).cuda()
+    return t
+
+
+def cpu_baseline(w, reps):
+    """The fp64 oracle as it stands, timed on this host's cores."""
+    from oracle import ikbo_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    q, k, v = w.values("q_cand"), w.values("k_user"), w.values("v_user")
+    flops, _, _ = algorithmic_counts(w)
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        O.target_attention(q, k, v, w.user_offsets, w.cand_to_user, w.scale)
+        if w.with_self:
+            O.self_attention_causal(w.values("q_user"), k, v, w.user_offsets, w.scale)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"whole {w.name} batch ({w.n_cand} candidates), fp64 numpy with explicit per-candidate "
+                      f"K/V replication, median of {reps} runs of {t:.2f} s",
+            "seconds": t, "cands_per_s": w.n_cand / t}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c2_typical")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--report", action="store_true", help="add cold-cache and materialised-broadcast figures")
+    ap.add_argument("--kernel-only", action="store_true", help="loop only the planned launch (for profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import broadcast_free_target_amd as ikbo
+    from workloads import make_workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = make_workload(args.config)
+    dev = upload(w)
+    dt_code = ikbo.IKBO_DTYPE_BF16 if w.dtype == "bf16" else ikbo.IKBO_DTYPE_F32
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    out_c = torch.empty(w.raw("q_cand").shape, dtype=tdt, device="cuda")
+    out_u = torch.empty(w.raw("q_user").shape, dtype=tdt, device="cuda") if w.with_self else None
+    stream = torch.cuda.current_stream()
+    plan = ikbo.ikbo_plan_create()
+    offs_h = np.ascontiguousarray(w.user_offsets, dtype=np.int32)
+    c2u_h = np.ascontiguousarray(w.cand_to_user, dtype=np.int32)
+    ws = 1 if w.with_self else 0
+
+    def build():
+        ikbo.ikbo_plan_build(plan, offs_h, c2u_h, w.n_users, w.n_cand, w.n_q, w.H, w.d, dt_code, ws, stream)
+
+    def launch():
+        ikbo.ikbo_attn_fwd_planned(plan, dev["q_cand"], dev.get("q_user"), dev["k_user"], dev["v_user"], w.scale,
+                                   out_c, out_u, stream)
+
+    build()
+    info = ikbo.ikbo_plan_info(plan)
+    for _ in range(args.warmup):
+        build()
+        launch()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    if args.kernel_only:
+        build()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        if not args.kernel_only:
+            build()
+        ev[i][0].record(stream)
+        launch()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    k_avg_ms = float(np.mean(kern_ms))
+
+    flops, byts, mat_bytes = algorithmic_counts(w)
+    ms_per_step = wall * 1e3 / K
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    ai = flops / byts
+    peak_flops = (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS) * 1e12
+    bound = "hbm" if ai < peak_flops / (PEAK_HBM_GBS * 1e9) else "mfma"
+    if bound == "hbm":
+        achieved = byts / (k_avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    else:
+        achieved = flops / (k_avg_ms * 1e-3) / 1e12
+        pk = peak_flops / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": pk, "unit": "TFLOP/s", "frac": achieved / pk}
+    roof["traffic"] = traffic_from_profiles(args.config)
+    roof["kernel"] = DOMINANT_KERNEL if w.dtype == "bf16" else "ikbo_attn_f32_kernel"
+    roof["kernel_avg_us"] = k_avg_ms * 1e3
+    roof["algorithmic_bytes_per_launch"] = byts
+    roof["algorithmic_flops_per_launch"] = flops
+
+    extra = {
+        "kernel_tflops": flops / (k_avg_ms * 1e-3) / 1e12,
+        "kernel_frac_mfma_peak": flops / (k_avg_ms * 1e-3) / peak_flops,
+        "kernel_hbm_gbs": byts / (k_avg_ms * 1e-3) / 1e9,
+        "kernel_us_median": float(np.median(kern_ms)) * 1e3,
+        "arith_intensity": ai,
+        "cands_per_s": w.n_cand / (ms_per_step * 1e-3),
+        "plan": info,
+        "materialized_algorithmic_bytes": mat_bytes,
+        "ikbo_vs_materialized_bytes_ratio": mat_bytes / byts,
+    }
+
+    if args.report:
+        # cold cache: overwrite 2 GiB between launches so neither L2 nor MALL holds K/V
+        flush = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+        cold = []
+        for _ in range(30):
+            flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            launch()
+            b.record(stream)
+            torch.cuda.synchronize()
+            cold.append(a.elapsed_time(b))
+        del flush
+        c_ms = float(np.median(cold))
+        extra["cold_kernel_us_median"] = c_ms * 1e3
+        extra["cold_kernel_tflops"] = flops / (c_ms * 1e-3) / 1e12
+        extra["cold_kernel_hbm_gbs"] = byts / (c_ms * 1e-3) / 1e9
+        # end-to-end spec call (device mapping: D2H copy + sync + host plan + launch)
+        if not w.with_self:
+            for _ in range(5):
+                ikbo.ikbo_attn_fwd_ex(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"],
+                                      dev["cand_to_user"], w.n_users, w.n_cand, w.n_q, w.H, w.d, w.scale,
+                                      dt_code, out_c, stream)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            n_e2e = 50
+            for _ in range(n_e2e):
+                ikbo.ikbo_attn_fwd_ex(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"],
+                                      dev["cand_to_user"], w.n_users, w.n_cand, w.n_q, w.H, w.d, w.scale,
+                                      dt_code, out_c, stream)
+            torch.cuda.synchronize()
+            extra["e2e_device_mapping_us"] = (time.perf_counter() - t1) / n_e2e * 1e6
+            # materialised broadcast comparator (copy kernel + the same attention kernel)
+            if mat_bytes < 64e9:
+                for _ in range(2):
+                    ikbo.ikbo_attn_fwd_materialized(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"],
+                                                    dev["cand_to_user"], w.n_users, w.n_cand, w.n_q, w.H, w.d,
+                                                    w.scale, dt_code, out_c, stream)
+                torch.cuda.synchronize()
+                t1 = time.perf_counter()
+                n_mat = 5
+                for _ in range(n_mat):
+                    ikbo.ikbo_attn_fwd_materialized(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"],
+                                                    dev["cand_to_user"], w.n_users, w.n_cand, w.n_q, w.H, w.d,
+                                                    w.scale, dt_code, out_c, stream)
+                torch.cuda.synchronize()
+                extra["materialized_us"] = (time.perf_counter() - t1) / n_mat * 1e6
+        # host grouping + work list alone
+        t1 = time.perf_counter()
+        for _ in range(100):
+            build()
+        torch.cuda.synchronize()
+        extra["host_plan_build_us"] = (time.perf_counter() - t1) / 100 * 1e6
+
+    ikbo.ikbo_plan_destroy(plan)
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, jagged lengths and mappings drawn per config)",
+        "config": {"workload": f"{args.config}: {WORKLOAD_TEXT[args.config]}", "n_cand": w.n_cand,
+                   "n_users": w.n_users, "n_q": w.n_q, "H": w.H, "d": w.d, "total_len": w.total_len,
+                   "seed": w.seed},
+        "roofline": roof,
+        "cpu_baseline": None,
+        "extra": extra,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_reps)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

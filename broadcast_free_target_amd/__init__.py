@@ -1,0 +1,33 @@
+"""IKBO (In-Kernel Broadcast Optimization) target attention for MI355X.
+
+The compute lives in libikbo.so (hand-written HIP kernels for gfx950 behind a
+C ABI, include/ikbo.h).  This package holds the sources, the build script and
+a ctypes binding whose functions carry the C entry points' names.
+"""
+
+from .ikbo import (  # noqa: F401
+    IKBO_DTYPE_BF16,
+    IKBO_DTYPE_F32,
+    IKBO_ERR_BAD_MAPPING,
+    IKBO_ERR_BAD_OFFSETS,
+    IKBO_ERR_HIP,
+    IKBO_ERR_INVALID_ARG,
+    IKBO_ERR_NOMEM,
+    IKBO_ERR_UNSUPPORTED,
+    IKBO_OK,
+    SIGNATURES,
+    IkboError,
+    ikbo_attn_fwd,
+    ikbo_attn_fwd_ex,
+    ikbo_attn_fwd_materialized,
+    ikbo_attn_fwd_planned,
+    ikbo_group_csr,
+    ikbo_last_error,
+    ikbo_plan_build,
+    ikbo_plan_create,
+    ikbo_plan_destroy,
+    ikbo_plan_info,
+    ikbo_self_target_fwd,
+    ikbo_version,
+    load_library,
+)

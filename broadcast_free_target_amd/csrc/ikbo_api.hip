@@ -1,0 +1,596 @@
+// C ABI of libikbo.so (declared in include/ikbo.h).
+//
+// Host responsibilities: argument checks, the host grouping pass and work
+// list (ikbo_plan.cpp), workspaces, uploads and launches.  All device work is
+// stream-ordered; the only host-device synchronisations are the ones the
+// header documents (copying a device-resident mapping to the host).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <limits>
+#include <map>
+#include <mutex>
+#include <new>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "ikbo.h"
+#include "ikbo_kernels.h"
+#include "ikbo_plan.h"
+
+namespace {
+
+using ikbo::HostPlan;
+using ikbo::PlanParams;
+using ikbo::WorkItem;
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int fail_hip(hipError_t e, const char* what) {
+  return fail(IKBO_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define IKBO_HIP(call)                          \
+  do {                                          \
+    hipError_t e_ = (call);                     \
+    if (e_ != hipSuccess) return fail_hip(e_, #call); \
+  } while (0)
+
+int env_int(const char* name, int dflt) {
+  const char* s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  return std::atoi(s);
+}
+
+size_t elem_size(int32_t dtype) { return dtype == IKBO_DTYPE_F32 ? 4 : 2; }
+
+// Grow-only device buffer.
+struct DevBuf {
+  void* ptr = nullptr;
+  size_t cap = 0;
+  int ensure(size_t bytes, bool zero) {
+    if (bytes <= cap) return IKBO_OK;
+    if (ptr) {
+      hipError_t e = hipFree(ptr);  // hipFree waits for work that may still use the buffer
+      ptr = nullptr;
+      cap = 0;
+      if (e != hipSuccess) return fail_hip(e, "hipFree");
+    }
+    size_t want = std::max<size_t>(bytes, 256);
+    hipError_t e = hipMalloc(&ptr, want);
+    if (e != hipSuccess) {
+      ptr = nullptr;
+      return fail(IKBO_ERR_NOMEM, std::string("hipMalloc: ") + hipGetErrorString(e));
+    }
+    if (zero) {
+      e = hipMemset(ptr, 0, want);
+      if (e != hipSuccess) return fail_hip(e, "hipMemset");
+    }
+    cap = want;
+    return IKBO_OK;
+  }
+  void release() {
+    if (ptr) (void)hipFree(ptr);
+    ptr = nullptr;
+    cap = 0;
+  }
+};
+
+// Grow-only pinned host buffer.
+struct PinnedBuf {
+  void* ptr = nullptr;
+  size_t cap = 0;
+  int ensure(size_t bytes) {
+    if (bytes <= cap) return IKBO_OK;
+    if (ptr) (void)hipHostFree(ptr);
+    ptr = nullptr;
+    cap = 0;
+    size_t want = std::max<size_t>(bytes, 4096);
+    hipError_t e = hipHostMalloc(&ptr, want, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      ptr = nullptr;
+      return fail(IKBO_ERR_NOMEM, std::string("hipHostMalloc: ") + hipGetErrorString(e));
+    }
+    cap = want;
+    return IKBO_OK;
+  }
+  void release() {
+    if (ptr) (void)hipHostFree(ptr);
+    ptr = nullptr;
+    cap = 0;
+  }
+};
+
+struct Plan {
+  int device = -1;
+  int n_cu = 0;
+  // last build
+  bool built = false;
+  int32_t n_users = 0, n_cand = 0, n_q = 1, H = 0, d = 0, dtype = IKBO_DTYPE_BF16, with_self = 0;
+  int64_t total_len = 0;
+  HostPlan hp;
+  // device copies of the work list
+  DevBuf d_items, d_perm, d_ws_o, d_ws_ml, d_counters;
+  // two pinned upload buffers, each guarded by the event of its last upload
+  PinnedBuf stage[2];
+  hipEvent_t stage_ev[2] = {nullptr, nullptr};
+  bool stage_used[2] = {false, false};
+  int next_stage = 0;
+  // pinned landing area for device-resident mappings (synchronous entry points)
+  PinnedBuf d2h;
+
+  ~Plan() {
+    for (int i = 0; i < 2; ++i) {
+      if (stage_ev[i]) (void)hipEventDestroy(stage_ev[i]);
+      stage[i].release();
+    }
+    d2h.release();
+    d_items.release();
+    d_perm.release();
+    d_ws_o.release();
+    d_ws_ml.release();
+    d_counters.release();
+  }
+};
+
+int plan_init(Plan* p) {
+  IKBO_HIP(hipGetDevice(&p->device));
+  hipDeviceProp_t prop;
+  IKBO_HIP(hipGetDeviceProperties(&prop, p->device));
+  p->n_cu = prop.multiProcessorCount;
+  for (int i = 0; i < 2; ++i) IKBO_HIP(hipEventCreateWithFlags(&p->stage_ev[i], hipEventDisableTiming));
+  return IKBO_OK;
+}
+
+PlanParams params_for(const Plan& p, int32_t dtype) {
+  PlanParams pp;
+  if (dtype == IKBO_DTYPE_BF16) {
+    pp.bm = ikbo::kBf16TileRows;
+    pp.bn = ikbo::kBf16TileKeys;
+    pp.grid_slots = std::max(1, p.n_cu * ikbo::kBf16WgsPerCu);
+    pp.min_chunk = 256;
+    pp.allow_split = true;
+  } else {
+    pp.bm = ikbo::kF32TileRows;
+    pp.bn = ikbo::kF32TileKeys;
+    pp.grid_slots = std::max(1, p.n_cu * 4);
+    pp.allow_split = false;
+  }
+  // Test and tuning overrides.  IKBO_GRID_WGS changes only the launched grid;
+  // IKBO_SPLIT_SLOTS and IKBO_MIN_CHUNK change how key ranges are split.
+  pp.grid_slots = std::max(1, env_int("IKBO_SPLIT_SLOTS", pp.grid_slots));
+  pp.launch_grid = std::max(0, env_int("IKBO_GRID_WGS", 0));
+  pp.min_chunk = std::max(pp.bn, env_int("IKBO_MIN_CHUNK", pp.min_chunk));
+  if (env_int("IKBO_NO_SPLIT", 0)) pp.allow_split = false;
+  return pp;
+}
+
+int check_dims(int32_t n_users, int32_t n_cand, int32_t n_q, int32_t H, int32_t d, int32_t dtype) {
+  if (n_users < 0 || n_cand < 0) return fail(IKBO_ERR_INVALID_ARG, "n_users and n_cand must be >= 0");
+  if (H < 1) return fail(IKBO_ERR_INVALID_ARG, "H must be >= 1");
+  if (n_q < 1) return fail(IKBO_ERR_INVALID_ARG, "n_q must be >= 1");
+  if (dtype != IKBO_DTYPE_BF16 && dtype != IKBO_DTYPE_F32) return fail(IKBO_ERR_UNSUPPORTED, "dtype");
+  if (d != 32 && d != 64 && d != 128) return fail(IKBO_ERR_UNSUPPORTED, "head dim must be 32, 64 or 128");
+  if (n_cand > 0 && n_users == 0) return fail(IKBO_ERR_BAD_MAPPING, "candidates present but n_users == 0");
+  return IKBO_OK;
+}
+
+int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n_users, int32_t n_cand,
+                     int32_t n_q, int32_t H, int32_t d, int32_t dtype, int32_t with_self, hipStream_t stream) {
+  int rc = check_dims(n_users, n_cand, n_q, H, d, dtype);
+  if (rc != IKBO_OK) return rc;
+  if (!offs || (n_cand > 0 && !c2u)) return fail(IKBO_ERR_INVALID_ARG, "null host mapping");
+  int dev = -1;
+  IKBO_HIP(hipGetDevice(&dev));
+  if (dev != p->device) return fail(IKBO_ERR_INVALID_ARG, "plan belongs to another device");
+  std::string err;
+  HostPlan hp;
+  rc = ikbo::build_plan(offs, c2u, n_users, n_cand, n_q, H, with_self != 0, params_for(*p, dtype), &hp, &err);
+  if (rc != ikbo::kOk) return fail(rc, err);
+
+  const int tile_rows = dtype == IKBO_DTYPE_BF16 ? ikbo::kBf16TileRows : ikbo::kF32TileRows;
+  const size_t items_bytes = hp.items.size() * sizeof(WorkItem);
+  const size_t perm_bytes = hp.cand_perm.size() * sizeof(int32_t);
+  if ((rc = p->d_items.ensure(items_bytes, false)) != IKBO_OK) return rc;
+  if ((rc = p->d_perm.ensure(perm_bytes, false)) != IKBO_OK) return rc;
+  if ((rc = p->d_ws_o.ensure(static_cast<size_t>(hp.n_slots) * tile_rows * d * sizeof(float), false)) != IKBO_OK)
+    return rc;
+  if ((rc = p->d_ws_ml.ensure(static_cast<size_t>(hp.n_slots) * tile_rows * 2 * sizeof(float), false)) != IKBO_OK)
+    return rc;
+  if ((rc = p->d_counters.ensure(static_cast<size_t>(hp.n_groups) * sizeof(int32_t), true)) != IKBO_OK) return rc;
+
+  // Stage into the pinned buffer whose previous upload is complete.
+  const int s = p->next_stage;
+  p->next_stage ^= 1;
+  if (p->stage_used[s]) IKBO_HIP(hipEventSynchronize(p->stage_ev[s]));
+  if ((rc = p->stage[s].ensure(items_bytes + perm_bytes + 16)) != IKBO_OK) return rc;
+  char* hb = static_cast<char*>(p->stage[s].ptr);
+  if (items_bytes) std::memcpy(hb, hp.items.data(), items_bytes);
+  if (perm_bytes) std::memcpy(hb + items_bytes, hp.cand_perm.data(), perm_bytes);
+  if (items_bytes) IKBO_HIP(hipMemcpyAsync(p->d_items.ptr, hb, items_bytes, hipMemcpyHostToDevice, stream));
+  if (perm_bytes)
+    IKBO_HIP(hipMemcpyAsync(p->d_perm.ptr, hb + items_bytes, perm_bytes, hipMemcpyHostToDevice, stream));
+  IKBO_HIP(hipEventRecord(p->stage_ev[s], stream));
+  p->stage_used[s] = true;
+
+  p->hp = std::move(hp);
+  p->n_users = n_users;
+  p->n_cand = n_cand;
+  p->n_q = n_q;
+  p->H = H;
+  p->d = d;
+  p->dtype = dtype;
+  p->with_self = with_self;
+  p->total_len = offs[n_users];
+  p->built = true;
+  return IKBO_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const char* pa = static_cast<const char*>(a);
+  const char* pb = static_cast<const char*>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* k, const void* v, float scale,
+                   void* out_cand, void* out_user, hipStream_t stream) {
+  if (!p->built) return fail(IKBO_ERR_INVALID_ARG, "plan has not been built");
+  int dev = -1;
+  IKBO_HIP(hipGetDevice(&dev));
+  if (dev != p->device) return fail(IKBO_ERR_INVALID_ARG, "plan belongs to another device");
+  if (!std::isfinite(scale)) return fail(IKBO_ERR_INVALID_ARG, "scale must be finite");
+  const size_t es = elem_size(p->dtype);
+  const size_t row = static_cast<size_t>(p->H) * p->d * es;
+  const size_t cand_bytes = static_cast<size_t>(p->n_cand) * p->n_q * row;
+  const size_t kv_bytes = static_cast<size_t>(p->total_len) * row;
+  const bool has_target = p->n_cand > 0;
+  const bool has_self = p->with_self && p->total_len > 0;
+  if (has_target && (!q_cand || !out_cand)) return fail(IKBO_ERR_INVALID_ARG, "null q_cand or out");
+  if ((has_target || has_self) && p->total_len > 0 && (!k || !v)) return fail(IKBO_ERR_INVALID_ARG, "null k or v");
+  if (has_self && (!q_user || !out_user)) return fail(IKBO_ERR_INVALID_ARG, "null q_user or out_user");
+  const void* ins[4] = {q_cand, k, v, q_user};
+  const size_t in_sz[4] = {cand_bytes, kv_bytes, kv_bytes, has_self ? kv_bytes : 0};
+  for (int i = 0; i < 4; ++i) {
+    if (has_target && overlaps(out_cand, cand_bytes, ins[i], in_sz[i]))
+      return fail(IKBO_ERR_INVALID_ARG, "out_cand aliases an input");
+    if (has_self && overlaps(out_user, kv_bytes, ins[i], in_sz[i]))
+      return fail(IKBO_ERR_INVALID_ARG, "out_user aliases an input");
+  }
+  if (has_target && has_self && overlaps(out_cand, cand_bytes, out_user, kv_bytes))
+    return fail(IKBO_ERR_INVALID_ARG, "out_cand and out_user overlap");
+  const uintptr_t align_or = reinterpret_cast<uintptr_t>(q_cand) | reinterpret_cast<uintptr_t>(k) |
+                             reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out_cand) |
+                             reinterpret_cast<uintptr_t>(q_user) | reinterpret_cast<uintptr_t>(out_user);
+  if (align_or & 15) return fail(IKBO_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (p->hp.items.empty()) return IKBO_OK;
+
+  ikbo::AttnParams ap{};
+  ap.q_cand = q_cand;
+  ap.q_user = q_user;
+  ap.k = k;
+  ap.v = v;
+  ap.out_cand = out_cand;
+  ap.out_user = out_user;
+  ap.cand_perm = static_cast<const int32_t*>(p->d_perm.ptr);
+  ap.items = static_cast<const WorkItem*>(p->d_items.ptr);
+  ap.n_items = static_cast<int32_t>(p->hp.items.size());
+  ap.H = p->H;
+  ap.n_q = p->n_q;
+  ap.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  ap.ws_o = static_cast<float*>(p->d_ws_o.ptr);
+  ap.ws_ml = static_cast<float*>(p->d_ws_ml.ptr);
+  ap.counters = static_cast<int32_t*>(p->d_counters.ptr);
+  hipError_t e = p->dtype == IKBO_DTYPE_BF16 ? ikbo::launch_attn_bf16(ap, p->d, p->hp.grid, stream)
+                                             : ikbo::launch_attn_f32(ap, p->d, p->hp.grid, stream);
+  if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  return IKBO_OK;
+}
+
+// Library-owned plans for the entry points that take device-resident mappings,
+// one per (device, stream).
+std::mutex g_cache_mu;
+std::map<std::pair<int, void*>, Plan*> g_plan_cache;
+
+int cached_plan(hipStream_t stream, int slot, Plan** out) {
+  int dev = -1;
+  IKBO_HIP(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  auto key = std::make_pair(dev * 4 + slot, static_cast<void*>(stream));
+  auto it = g_plan_cache.find(key);
+  if (it != g_plan_cache.end()) {
+    *out = it->second;
+    return IKBO_OK;
+  }
+  Plan* p = new (std::nothrow) Plan();
+  if (!p) return fail(IKBO_ERR_NOMEM, "plan allocation");
+  int rc = plan_init(p);
+  if (rc != IKBO_OK) {
+    delete p;
+    return rc;
+  }
+  g_plan_cache[key] = p;
+  *out = p;
+  return IKBO_OK;
+}
+
+// Copies a device-resident mapping to pinned host memory and waits for it.
+int fetch_mapping(Plan* p, const int32_t* offs_dev, const int32_t* c2u_dev, int32_t n_users, int32_t n_cand,
+                  hipStream_t stream, const int32_t** offs_host, const int32_t** c2u_host) {
+  if (!offs_dev || (n_cand > 0 && !c2u_dev)) return fail(IKBO_ERR_INVALID_ARG, "null user_offsets or cand_to_user");
+  const size_t ob = (static_cast<size_t>(n_users) + 1) * sizeof(int32_t);
+  const size_t cb = static_cast<size_t>(n_cand) * sizeof(int32_t);
+  int rc = p->d2h.ensure(ob + cb + 16);
+  if (rc != IKBO_OK) return rc;
+  char* hb = static_cast<char*>(p->d2h.ptr);
+  IKBO_HIP(hipMemcpyAsync(hb, offs_dev, ob, hipMemcpyDeviceToHost, stream));
+  if (cb) IKBO_HIP(hipMemcpyAsync(hb + ob, c2u_dev, cb, hipMemcpyDeviceToHost, stream));
+  IKBO_HIP(hipStreamSynchronize(stream));
+  *offs_host = reinterpret_cast<const int32_t*>(hb);
+  *c2u_host = reinterpret_cast<const int32_t*>(hb + ob);
+  return IKBO_OK;
+}
+
+int attn_device_mapping(const void* q_cand, const void* q_user, const void* k, const void* v, const int32_t* offs,
+                        const int32_t* c2u, int32_t n_users, int32_t n_cand, int32_t n_q, int32_t H, int32_t d,
+                        float scale, int32_t dtype, int32_t with_self, void* out_cand, void* out_user,
+                        void* stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  int rc = check_dims(n_users, n_cand, n_q, H, d, dtype);
+  if (rc != IKBO_OK) return rc;
+  if (n_cand == 0 && !with_self) return IKBO_OK;
+  Plan* p = nullptr;
+  if ((rc = cached_plan(stream, 0, &p)) != IKBO_OK) return rc;
+  const int32_t *ho = nullptr, *hc = nullptr;
+  if ((rc = fetch_mapping(p, offs, c2u, n_users, n_cand, stream, &ho, &hc)) != IKBO_OK) return rc;
+  if ((rc = build_and_upload(p, ho, hc, n_users, n_cand, n_q, H, d, dtype, with_self, stream)) != IKBO_OK) return rc;
+  return launch_planned(p, q_cand, q_user, k, v, scale, out_cand, out_user, stream);
+}
+
+// Broadcast buffers of the materialised comparator, per device.
+struct BcastWs {
+  DevBuf kb, vb, meta;
+  PinnedBuf host_meta;
+};
+std::mutex g_bcast_mu;
+std::map<int, BcastWs*> g_bcast;
+
+}  // namespace
+
+extern "C" {
+
+int ikbo_version(void) { return 100; }
+
+const char* ikbo_last_error(void) { return g_last_error.c_str(); }
+
+int ikbo_group_csr(const int32_t* cand_to_user_host, int32_t n_cand, int32_t n_users, int32_t n_q, int32_t bm,
+                   int32_t* counts, int32_t* cand_offsets, int32_t* cand_perm, int32_t* tiles, int32_t max_tiles,
+                   int32_t* n_tiles) {
+  try {
+    if ((n_cand > 0 && (!cand_to_user_host || !cand_perm)) || !cand_offsets || (n_users > 0 && !counts) ||
+        !n_tiles || (max_tiles > 0 && !tiles) || max_tiles < 0)
+      return fail(IKBO_ERR_INVALID_ARG, "null pointer or negative max_tiles");
+    std::vector<int32_t> tv;
+    std::string err;
+    int64_t nt = 0;
+    int rc = ikbo::group_csr(cand_to_user_host, n_cand, n_users, n_q, bm, counts, cand_offsets, cand_perm, &tv, &nt,
+                             &err);
+    if (rc != ikbo::kOk) return fail(rc, err);
+    if (nt > std::numeric_limits<int32_t>::max()) return fail(IKBO_ERR_INVALID_ARG, "too many tiles");
+    *n_tiles = static_cast<int32_t>(nt);
+    if (nt > max_tiles) return fail(IKBO_ERR_INVALID_ARG, "max_tiles too small (n_tiles holds the size needed)");
+    if (nt) std::memcpy(tiles, tv.data(), tv.size() * sizeof(int32_t));
+    return IKBO_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(IKBO_ERR_NOMEM, "host allocation");
+  } catch (...) {
+    return fail(IKBO_ERR_INVALID_ARG, "unexpected host error");
+  }
+}
+
+int ikbo_plan_create(void** plan) {
+  if (!plan) return fail(IKBO_ERR_INVALID_ARG, "plan is null");
+  *plan = nullptr;
+  Plan* p = new (std::nothrow) Plan();
+  if (!p) return fail(IKBO_ERR_NOMEM, "plan allocation");
+  int rc = plan_init(p);
+  if (rc != IKBO_OK) {
+    delete p;
+    return rc;
+  }
+  *plan = p;
+  return IKBO_OK;
+}
+
+int ikbo_plan_build(void* plan, const int32_t* user_offsets_host, const int32_t* cand_to_user_host, int32_t n_users,
+                    int32_t n_cand, int32_t n_q, int32_t H, int32_t d, int32_t dtype, int32_t with_self,
+                    void* stream) {
+  if (!plan) return fail(IKBO_ERR_INVALID_ARG, "plan is null");
+  try {
+    return build_and_upload(static_cast<Plan*>(plan), user_offsets_host, cand_to_user_host, n_users, n_cand, n_q, H,
+                            d, dtype, with_self, static_cast<hipStream_t>(stream));
+  } catch (const std::bad_alloc&) {
+    return fail(IKBO_ERR_NOMEM, "host allocation");
+  } catch (...) {
+    return fail(IKBO_ERR_INVALID_ARG, "unexpected host error");
+  }
+}
+
+int ikbo_attn_fwd_planned(void* plan, const void* q_cand, const void* q_user, const void* k_user,
+                          const void* v_user, float scale, void* out_cand, void* out_user, void* stream) {
+  if (!plan) return fail(IKBO_ERR_INVALID_ARG, "plan is null");
+  return launch_planned(static_cast<Plan*>(plan), q_cand, q_user, k_user, v_user, scale, out_cand, out_user,
+                        static_cast<hipStream_t>(stream));
+}
+
+void ikbo_plan_destroy(void* plan) {
+  if (!plan) return;
+  Plan* p = static_cast<Plan*>(plan);
+  int cur = -1;
+  if (hipGetDevice(&cur) == hipSuccess && p->device >= 0) {
+    (void)hipSetDevice(p->device);
+    (void)hipDeviceSynchronize();
+    (void)hipSetDevice(cur);
+  }
+  delete p;
+}
+
+int ikbo_plan_info(void* plan, int64_t* info, int32_t n_info) {
+  if (!plan || !info || n_info < 1) return fail(IKBO_ERR_INVALID_ARG, "null plan or info");
+  const Plan* p = static_cast<const Plan*>(plan);
+  const int64_t v[8] = {static_cast<int64_t>(p->hp.items.size()),
+                        p->hp.grid,
+                        p->hp.n_groups,
+                        p->hp.n_slots,
+                        static_cast<int64_t>(p->hp.n_slots) *
+                            (p->dtype == IKBO_DTYPE_BF16 ? ikbo::kBf16TileRows : ikbo::kF32TileRows) * (p->d + 2) * 4,
+                        p->hp.n_target_tiles,
+                        p->hp.n_self_tiles,
+                        p->n_cu};
+  for (int i = 0; i < n_info && i < 8; ++i) info[i] = v[i];
+  return IKBO_OK;
+}
+
+int ikbo_attn_fwd(const void* q_cand, const void* k_user, const void* v_user, const int32_t* user_offsets,
+                  const int32_t* cand_to_user, int32_t n_users, int32_t n_cand, int32_t H, int32_t d, float scale,
+                  void* out, void* stream) {
+  try {
+    return attn_device_mapping(q_cand, nullptr, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, 1, H, d,
+                               scale, IKBO_DTYPE_BF16, 0, out, nullptr, stream);
+  } catch (...) {
+    return fail(IKBO_ERR_NOMEM, "unexpected host error");
+  }
+}
+
+int ikbo_attn_fwd_ex(const void* q_cand, const void* k_user, const void* v_user, const int32_t* user_offsets,
+                     const int32_t* cand_to_user, int32_t n_users, int32_t n_cand, int32_t n_q, int32_t H, int32_t d,
+                     float scale, int32_t dtype, void* out, void* stream) {
+  try {
+    return attn_device_mapping(q_cand, nullptr, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, n_q, H,
+                               d, scale, dtype, 0, out, nullptr, stream);
+  } catch (...) {
+    return fail(IKBO_ERR_NOMEM, "unexpected host error");
+  }
+}
+
+int ikbo_self_target_fwd(const void* q_user, const void* q_cand, const void* k_user, const void* v_user,
+                         const int32_t* user_offsets, const int32_t* cand_to_user, int32_t n_users, int32_t n_cand,
+                         int32_t H, int32_t d, float scale, int32_t dtype, void* out_user, void* out_cand,
+                         void* stream) {
+  try {
+    return attn_device_mapping(q_cand, q_user, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, 1, H, d,
+                               scale, dtype, 1, out_cand, out_user, stream);
+  } catch (...) {
+    return fail(IKBO_ERR_NOMEM, "unexpected host error");
+  }
+}
+
+int ikbo_attn_fwd_materialized(const void* q_cand, const void* k_user, const void* v_user,
+                               const int32_t* user_offsets, const int32_t* cand_to_user, int32_t n_users,
+                               int32_t n_cand, int32_t n_q, int32_t H, int32_t d, float scale, int32_t dtype,
+                               void* out, void* stream_) {
+  try {
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    int rc = check_dims(n_users, n_cand, n_q, H, d, dtype);
+    if (rc != IKBO_OK) return rc;
+    if (n_cand == 0) return IKBO_OK;
+    if (!q_cand || !out || !k_user || !v_user) return fail(IKBO_ERR_INVALID_ARG, "null tensor pointer");
+    Plan* p = nullptr;
+    if ((rc = cached_plan(stream, 1, &p)) != IKBO_OK) return rc;
+    const int32_t *ho = nullptr, *hc = nullptr;
+    if ((rc = fetch_mapping(p, user_offsets, cand_to_user, n_users, n_cand, stream, &ho, &hc)) != IKBO_OK) return rc;
+    std::string err;
+    if ((rc = ikbo::check_offsets(ho, n_users, &err)) != ikbo::kOk) return fail(rc, err);
+    for (int32_t c = 0; c < n_cand; ++c)
+      if (hc[c] < 0 || hc[c] >= n_users) return fail(IKBO_ERR_BAD_MAPPING, "cand_to_user entry outside [0, n_users)");
+    // Copy the mapping out of the pinned landing area (the plan build below reuses the plan's buffers).
+    std::vector<int32_t> offs(ho, ho + n_users + 1), c2u(hc, hc + n_cand);
+
+    const size_t es = elem_size(dtype);
+    const int64_t row_bytes = static_cast<int64_t>(H) * d * static_cast<int64_t>(es);
+    const double max_gb = std::max(0.001, std::atof(std::getenv("IKBO_BCAST_MAX_GB") ? std::getenv("IKBO_BCAST_MAX_GB")
+                                                                                        : "32"));
+    const int64_t max_bytes = static_cast<int64_t>(max_gb * 1e9);
+    int dev = -1;
+    IKBO_HIP(hipGetDevice(&dev));
+    BcastWs* ws = nullptr;
+    {
+      std::lock_guard<std::mutex> lock(g_bcast_mu);
+      auto it = g_bcast.find(dev);
+      if (it == g_bcast.end()) it = g_bcast.emplace(dev, new BcastWs()).first;
+      ws = it->second;
+    }
+    const char* qc = static_cast<const char*>(q_cand);
+    char* oc = static_cast<char*>(out);
+    const int64_t cand_row_bytes = static_cast<int64_t>(n_q) * row_bytes;
+    int32_t c0 = 0;
+    while (c0 < n_cand) {
+      // Candidates [c0, c1): the broadcast copy (K and V) must fit in max_bytes.
+      int32_t c1 = c0;
+      int64_t rows = 0;
+      while (c1 < n_cand && c1 - c0 < 65535) {
+        const int64_t L = offs[c2u[c1] + 1] - offs[c2u[c1]];
+        if (c1 > c0 && 2 * (rows + L) * row_bytes > max_bytes) break;
+        rows += L;
+        ++c1;
+      }
+      if (rows > std::numeric_limits<int32_t>::max()) return fail(IKBO_ERR_INVALID_ARG, "broadcast chunk too large");
+      const int32_t n = c1 - c0;
+      if ((rc = ws->kb.ensure(static_cast<size_t>(std::max<int64_t>(rows, 1)) * row_bytes, false)) != IKBO_OK)
+        return rc;
+      if ((rc = ws->vb.ensure(static_cast<size_t>(std::max<int64_t>(rows, 1)) * row_bytes, false)) != IKBO_OK)
+        return rc;
+      // Per-candidate copy descriptors and the identity mapping of the broadcast problem.
+      const size_t meta_bytes = static_cast<size_t>(n) * (8 + 8 + 4);
+      if ((rc = ws->meta.ensure(meta_bytes + 64, false)) != IKBO_OK) return rc;
+      if ((rc = ws->host_meta.ensure(meta_bytes + 64)) != IKBO_OK) return rc;
+      int64_t* src = static_cast<int64_t*>(ws->host_meta.ptr);
+      int64_t* dst = src + n;
+      int32_t* len = reinterpret_cast<int32_t*>(dst + n);
+      std::vector<int32_t> offs_b(static_cast<size_t>(n) + 1, 0), c2u_b(n);
+      int32_t max_len = 0;
+      for (int32_t i = 0; i < n; ++i) {
+        const int32_t u = c2u[c0 + i];
+        src[i] = offs[u];
+        len[i] = offs[u + 1] - offs[u];
+        dst[i] = offs_b[i];
+        offs_b[i + 1] = offs_b[i] + len[i];
+        c2u_b[i] = i;
+        max_len = std::max(max_len, len[i]);
+      }
+      char* dmeta = static_cast<char*>(ws->meta.ptr);
+      IKBO_HIP(hipMemcpyAsync(dmeta, src, meta_bytes, hipMemcpyHostToDevice, stream));
+      hipError_t e = ikbo::launch_bcast_copy(k_user, v_user, ws->kb.ptr, ws->vb.ptr,
+                                             reinterpret_cast<const int64_t*>(dmeta),
+                                             reinterpret_cast<const int64_t*>(dmeta) + n,
+                                             reinterpret_cast<const int32_t*>(dmeta + 16 * static_cast<size_t>(n)), n,
+                                             row_bytes, max_len, stream);
+      if (e != hipSuccess) return fail_hip(e, "broadcast copy launch");
+      if ((rc = build_and_upload(p, offs_b.data(), c2u_b.data(), n, n, n_q, H, d, dtype, 0, stream)) != IKBO_OK)
+        return rc;
+      if ((rc = launch_planned(p, qc + c0 * cand_row_bytes, nullptr, ws->kb.ptr, ws->vb.ptr, scale,
+                               oc + c0 * cand_row_bytes, nullptr, stream)) != IKBO_OK)
+        return rc;
+      c0 = c1;
+      // The pinned descriptors and broadcast buffers are reused by the next chunk.
+      if (c0 < n_cand) IKBO_HIP(hipStreamSynchronize(stream));
+    }
+    return IKBO_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(IKBO_ERR_NOMEM, "host allocation");
+  } catch (...) {
+    return fail(IKBO_ERR_INVALID_ARG, "unexpected host error");
+  }
+}
+
+}  // extern "C"

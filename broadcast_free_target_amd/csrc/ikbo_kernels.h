@@ -1,0 +1,47 @@
+// Launch interface of the IKBO device kernels (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "ikbo_plan.h"
+
+namespace ikbo {
+
+// Rows per workgroup tile and keys per K/V tile of the bf16 MFMA kernel.
+constexpr int kBf16TileRows = 128;
+constexpr int kBf16TileKeys = 64;
+constexpr int kBf16WgsPerCu = 2;
+// Rows per tile of the fp32 kernel (one thread per row) and keys per tile.
+constexpr int kF32TileRows = 64;
+constexpr int kF32TileKeys = 32;
+
+struct AttnParams {
+  const void* q_cand;     // [n_cand, n_q, H, d]
+  const void* q_user;     // [total_len, H, d] or null
+  const void* k;          // [total_len, H, d]
+  const void* v;          // [total_len, H, d]
+  void* out_cand;         // [n_cand, n_q, H, d]
+  void* out_user;         // [total_len, H, d] or null
+  const int32_t* cand_perm;
+  const WorkItem* items;
+  int32_t n_items;
+  int32_t H;
+  int32_t n_q;
+  float scale_log2;       // scale * log2(e): scores are kept in base 2
+  float* ws_o;            // split partials: [slots, tile_rows, d] fp32, unnormalised
+  float* ws_ml;           // split partials: [slots, tile_rows, 2] (running max, sum)
+  int32_t* counters;      // [groups] arrival counters, zero between launches
+};
+
+hipError_t launch_attn_bf16(const AttnParams& p, int d, int grid, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnParams& p, int d, int grid, hipStream_t stream);
+
+// Materialised broadcast: for each of n local candidates, copy `len[c]` rows of
+// `row_bytes` bytes from k/v at src_row[c] to kb/vb at dst_row[c].
+hipError_t launch_bcast_copy(const void* k, const void* v, void* kb, void* vb,
+                             const int64_t* src_row, const int64_t* dst_row, const int32_t* len,
+                             int32_t n, int64_t row_bytes, int32_t max_len, hipStream_t stream);
+
+}  // namespace ikbo

@@ -1,0 +1,191 @@
+"""ctypes binding of libikbo.so (argument marshalling only).
+
+Every function has the name of the C entry point it calls (include/ikbo.h).
+Tensor arguments are torch tensors on the current HIP device (or, for the
+``*_host`` arguments, numpy int32 arrays); they are passed as raw pointers.
+A negative status raises :class:`IkboError` carrying the library's message.
+All computation happens in the library's HIP kernels; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libikbo.so")
+
+IKBO_OK = 0
+IKBO_ERR_INVALID_ARG = -1
+IKBO_ERR_BAD_OFFSETS = -2
+IKBO_ERR_BAD_MAPPING = -3
+IKBO_ERR_UNSUPPORTED = -4
+IKBO_ERR_HIP = -5
+IKBO_ERR_NOMEM = -6
+IKBO_DTYPE_BF16 = 0
+IKBO_DTYPE_F32 = 1
+
+# Every symbol include/ikbo.h declares, with (restype, argtypes).
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_F = ctypes.c_float
+_IP = ctypes.POINTER(ctypes.c_int32)
+_LP = ctypes.POINTER(ctypes.c_int64)
+SIGNATURES = {
+    "ikbo_version": (ctypes.c_int, []),
+    "ikbo_last_error": (ctypes.c_char_p, []),
+    "ikbo_group_csr": (ctypes.c_int, [_IP, _I, _I, _I, _I, _IP, _IP, _IP, _IP, _I, _IP]),
+    "ikbo_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P]),
+    "ikbo_attn_fwd_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P]),
+    "ikbo_self_target_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P]),
+    "ikbo_attn_fwd_materialized": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P]),
+    "ikbo_plan_create": (ctypes.c_int, [ctypes.POINTER(_P)]),
+    "ikbo_plan_build": (ctypes.c_int, [_P, _IP, _IP, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "ikbo_attn_fwd_planned": (ctypes.c_int, [_P, _P, _P, _P, _P, _F, _P, _P, _P]),
+    "ikbo_plan_destroy": (None, [_P]),
+    "ikbo_plan_info": (ctypes.c_int, [_P, _LP, _I]),
+}
+
+_lib = None
+
+
+class IkboError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"ikbo status {status}: {msg}")
+        self.status = status
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Loads libikbo.so (built in-tree by broadcast_free_target_amd._build)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing: build it with `python -m broadcast_free_target_amd._build`")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int) -> int:
+    if status < 0:
+        raise IkboError(status, load_library().ikbo_last_error().decode())
+    return status
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _i32(a: np.ndarray):
+    assert a.dtype == np.int32 and a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(_IP)
+
+
+def ikbo_version() -> int:
+    return load_library().ikbo_version()
+
+
+def ikbo_last_error() -> str:
+    return load_library().ikbo_last_error().decode()
+
+
+def ikbo_group_csr(cand_to_user_host: np.ndarray, n_users: int, n_q: int, bm: int):
+    """Host CSR grouping.  Returns (counts, cand_offsets, cand_perm, tiles[T, 3])."""
+    lib = load_library()
+    c2u = np.ascontiguousarray(cand_to_user_host, dtype=np.int32)
+    n_cand = int(c2u.shape[0])
+    counts = np.zeros(max(n_users, 1), np.int32)
+    offs = np.zeros(n_users + 1, np.int32)
+    perm = np.zeros(max(n_cand, 1), np.int32)
+    nt = ctypes.c_int32(0)
+    rc = lib.ikbo_group_csr(_i32(c2u), n_cand, n_users, n_q, bm, _i32(counts), _i32(offs), _i32(perm),
+                            None, 0, ctypes.byref(nt))
+    if rc == IKBO_ERR_INVALID_ARG and nt.value > 0:
+        pass  # size query: tiles buffer too small
+    elif rc < 0:
+        _check(rc)
+    tiles = np.zeros((max(nt.value, 1), 3), np.int32)
+    _check(lib.ikbo_group_csr(_i32(c2u), n_cand, n_users, n_q, bm, _i32(counts), _i32(offs), _i32(perm),
+                              _i32(tiles), nt.value, ctypes.byref(nt)))
+    return counts[:n_users], offs, perm[:n_cand], tiles[:nt.value]
+
+
+def ikbo_attn_fwd(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, H, d, scale, out,
+                  stream=None) -> int:
+    return _check(load_library().ikbo_attn_fwd(
+        _ptr(q_cand), _ptr(k_user), _ptr(v_user), _ptr(user_offsets), _ptr(cand_to_user),
+        n_users, n_cand, H, d, float(scale), _ptr(out), _stream(stream)))
+
+
+def ikbo_attn_fwd_ex(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, n_q, H, d, scale,
+                     dtype, out, stream=None) -> int:
+    return _check(load_library().ikbo_attn_fwd_ex(
+        _ptr(q_cand), _ptr(k_user), _ptr(v_user), _ptr(user_offsets), _ptr(cand_to_user),
+        n_users, n_cand, n_q, H, d, float(scale), dtype, _ptr(out), _stream(stream)))
+
+
+def ikbo_self_target_fwd(q_user, q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, H, d,
+                         scale, dtype, out_user, out_cand, stream=None) -> int:
+    return _check(load_library().ikbo_self_target_fwd(
+        _ptr(q_user), _ptr(q_cand), _ptr(k_user), _ptr(v_user), _ptr(user_offsets), _ptr(cand_to_user),
+        n_users, n_cand, H, d, float(scale), dtype, _ptr(out_user), _ptr(out_cand), _stream(stream)))
+
+
+def ikbo_attn_fwd_materialized(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, n_q, H, d,
+                               scale, dtype, out, stream=None) -> int:
+    return _check(load_library().ikbo_attn_fwd_materialized(
+        _ptr(q_cand), _ptr(k_user), _ptr(v_user), _ptr(user_offsets), _ptr(cand_to_user),
+        n_users, n_cand, n_q, H, d, float(scale), dtype, _ptr(out), _stream(stream)))
+
+
+def ikbo_plan_create() -> int:
+    h = _P()
+    _check(load_library().ikbo_plan_create(ctypes.byref(h)))
+    return h.value
+
+
+def ikbo_plan_build(plan, user_offsets_host, cand_to_user_host, n_users, n_cand, n_q, H, d, dtype,
+                    with_self=0, stream=None) -> int:
+    offs = np.ascontiguousarray(user_offsets_host, dtype=np.int32)
+    c2u = np.ascontiguousarray(cand_to_user_host, dtype=np.int32)
+    return _check(load_library().ikbo_plan_build(
+        plan, _i32(offs), _i32(c2u) if c2u.size else None, n_users, n_cand, n_q, H, d, dtype,
+        int(with_self), _stream(stream)))
+
+
+def ikbo_attn_fwd_planned(plan, q_cand, q_user, k_user, v_user, scale, out_cand, out_user=None,
+                          stream=None) -> int:
+    return _check(load_library().ikbo_attn_fwd_planned(
+        plan, _ptr(q_cand), _ptr(q_user), _ptr(k_user), _ptr(v_user), float(scale), _ptr(out_cand),
+        _ptr(out_user), _stream(stream)))
+
+
+def ikbo_plan_destroy(plan) -> None:
+    load_library().ikbo_plan_destroy(plan)
+
+
+def ikbo_plan_info(plan) -> dict:
+    info = (ctypes.c_int64 * 8)()
+    _check(load_library().ikbo_plan_info(plan, info, 8))
+    keys = ("n_items", "grid", "n_groups", "n_slots", "partial_bytes", "n_target_tiles", "n_self_tiles", "n_cu")
+    return dict(zip(keys, list(info)))

@@ -1,0 +1,179 @@
+/*
+ * ikbo.h -- C ABI of libikbo.so: In-Kernel Broadcast Optimization (IKBO)
+ * target attention for MI355X (gfx950).
+ *
+ * The operation (IKBO blog, "In-Kernel Broadcast Optimization: Co-Designing
+ * Kernels for RecSys Inference", sections 1.1-1.3 and 3.1, Fig. 10): a
+ * request carries two batch sizes.  Request-only (RO) tensors are per user
+ * (here the user's key/value history), non-request-only (NRO) tensors are per
+ * candidate (here the candidate queries).  A runtime-supplied mapping names
+ * the user of every candidate.  Each candidate query attends, without a causal
+ * mask (section 3: the models are encoder-driven), over the whole key/value
+ * sequence of its user.  The user sequence is never copied out per candidate:
+ * the kernel reads the mapping and indexes the user's K/V itself.  The result
+ * equals softmax(scale * q k^T) v computed on an explicitly broadcast K/V.
+ *
+ * Tensor layouts (row-major, contiguous, element type given by `dtype`):
+ *   q_cand   [n_cand, n_q, H, d]   candidate queries (n_q query tokens each)
+ *   k_user   [total_len, H, d]     user keys, packed user after user
+ *   v_user   [total_len, H, d]     user values, same packing
+ *   q_user   [total_len, H, d]     user queries (fused self + target only)
+ *   out_cand [n_cand, n_q, H, d]   same dtype as q_cand
+ *   out_user [total_len, H, d]     same dtype (fused self + target only)
+ *   user_offsets int32 [n_users + 1]: rows of user u are
+ *                user_offsets[u] .. user_offsets[u+1]-1; user_offsets[0] = 0.
+ *   cand_to_user int32 [n_cand]: user of each candidate, any order.
+ * `d` is 32, 64 or 128.  Element types: IKBO_DTYPE_BF16 (bf16 in, fp32
+ * accumulation, bf16 out) or IKBO_DTYPE_F32.  Rows must be 16-byte aligned
+ * (true for the layouts above with d >= 32 and 16-byte aligned base pointers).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named *_host are host memory; every other tensor pointer is
+ *     device memory on the current HIP device.
+ *   - `stream` is a hipStream_t (NULL = the default stream); all device work is
+ *     enqueued on it, and the call returns before that work completes, except
+ *     where a call says it synchronises.
+ *   - The caller owns every tensor and must keep it alive until the stream
+ *     work completes.  The library owns only its plans and workspaces.
+ *   - A negative return is an error; nothing has been launched and no output
+ *     has been written.  ikbo_last_error() gives a message (thread-local).
+ *     No C++ exception crosses this boundary.
+ *   - Output rows are fully overwritten.  Results are deterministic: the same
+ *     inputs give bitwise-identical outputs, whatever the grid size.
+ *   - A user with zero keys but with candidates gets all-zero output rows
+ *     (softmax over an empty set is undefined; this library's reading).
+ *   - n_cand = 0 is a successful no-op.  n_users = 0 with n_cand > 0 is
+ *     IKBO_ERR_BAD_MAPPING.
+ */
+#ifndef IKBO_H_
+#define IKBO_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  IKBO_OK = 0,
+  IKBO_ERR_INVALID_ARG = -1, /* null pointer, negative size, H < 1, aliasing output */
+  IKBO_ERR_BAD_OFFSETS = -2, /* user_offsets not starting at 0 or decreasing     */
+  IKBO_ERR_BAD_MAPPING = -3, /* a cand_to_user entry outside [0, n_users)        */
+  IKBO_ERR_UNSUPPORTED = -4, /* d or dtype not supported                          */
+  IKBO_ERR_HIP = -5,         /* a HIP runtime call failed                          */
+  IKBO_ERR_NOMEM = -6        /* device or pinned host allocation failed            */
+};
+
+enum { IKBO_DTYPE_BF16 = 0, IKBO_DTYPE_F32 = 1 };
+
+/* Library version as an integer (major * 10000 + minor * 100 + patch). */
+int ikbo_version(void);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* ikbo_last_error(void);
+
+/*
+ * Host-side grouping of candidates by user (CSR).  Host pointers only; no GPU
+ * is touched.  The pages hand the kernel the candidate-to-user mapping
+ * (IKBO blog section 1.3) and pair neighbouring candidates of one user inside
+ * a thread block (section 3.2, Alg. 1); this generalises the pairing to any
+ * order and any count.
+ *   counts[n_users]          candidates per user
+ *   cand_offsets[n_users+1]  exclusive prefix sum of counts
+ *   cand_perm[n_cand]        candidate indices sorted by user; ascending
+ *                            original index within a user (stable)
+ *   tiles[3 * max_tiles]     (u, row_start, row_len) triples: user u owns
+ *                            counts[u] * n_q rows, row r being query r % n_q of
+ *                            candidate cand_perm[cand_offsets[u] + r / n_q];
+ *                            rows are cut into tiles of `bm` (the last may be
+ *                            shorter); users ascending, tiles ascending.
+ *   *n_tiles                 number of tiles written.
+ * Returns IKBO_ERR_INVALID_ARG if max_tiles is too small (then *n_tiles holds
+ * the number needed), IKBO_ERR_BAD_MAPPING for an out-of-range mapping.
+ */
+int ikbo_group_csr(const int32_t* cand_to_user_host, int32_t n_cand, int32_t n_users,
+                   int32_t n_q, int32_t bm, int32_t* counts, int32_t* cand_offsets,
+                   int32_t* cand_perm, int32_t* tiles, int32_t max_tiles, int32_t* n_tiles);
+
+/*
+ * IKBO target attention, bf16, one query token per candidate: the call the
+ * problem statement names.  user_offsets and cand_to_user are DEVICE pointers;
+ * the call copies them to the host, waits for the stream (one synchronisation),
+ * groups candidates on the host, uploads the work list and launches.  `scale`
+ * multiplies q.k (typically 1/sqrt(d)).  out: [n_cand, 1, H, d] bf16.
+ */
+int ikbo_attn_fwd(const void* q_cand, const void* k_user, const void* v_user,
+                  const int32_t* user_offsets, const int32_t* cand_to_user,
+                  int32_t n_users, int32_t n_cand, int32_t H, int32_t d, float scale,
+                  void* out, void* stream);
+
+/* As ikbo_attn_fwd, with n_q query tokens per candidate and a dtype. */
+int ikbo_attn_fwd_ex(const void* q_cand, const void* k_user, const void* v_user,
+                     const int32_t* user_offsets, const int32_t* cand_to_user,
+                     int32_t n_users, int32_t n_cand, int32_t n_q, int32_t H, int32_t d,
+                     float scale, int32_t dtype, void* out, void* stream);
+
+/*
+ * Fused self + target attention (IKBO blog section 3.3): both attentions read
+ * the same user K/V.  Self rows: query q_user[user_offsets[u] + t] attends
+ * causally to keys 0..t of its own user (diagonal included).  Target rows: as
+ * ikbo_attn_fwd_ex with n_q = 1 (non-causal over the whole user sequence).
+ * One launch covers both kinds of work.
+ */
+int ikbo_self_target_fwd(const void* q_user, const void* q_cand, const void* k_user,
+                         const void* v_user, const int32_t* user_offsets,
+                         const int32_t* cand_to_user, int32_t n_users, int32_t n_cand,
+                         int32_t H, int32_t d, float scale, int32_t dtype,
+                         void* out_user, void* out_cand, void* stream);
+
+/*
+ * Materialised-broadcast comparator (measurement only; IKBO blog section 1.4
+ * "system-level broadcast" and Fig. 10, left).  A copy kernel first writes a
+ * per-candidate copy of its user's K and V into a library-owned buffer
+ * [sum_c L_{u(c)}, H, d]; the same attention kernel then runs with the
+ * identity mapping.  Output equals ikbo_attn_fwd_ex.  Candidates are processed
+ * in chunks so the broadcast buffer stays within IKBO_BCAST_MAX_GB
+ * (environment, default 32).  Synchronises like ikbo_attn_fwd.
+ */
+int ikbo_attn_fwd_materialized(const void* q_cand, const void* k_user, const void* v_user,
+                               const int32_t* user_offsets, const int32_t* cand_to_user,
+                               int32_t n_users, int32_t n_cand, int32_t n_q, int32_t H,
+                               int32_t d, float scale, int32_t dtype, void* out, void* stream);
+
+/*
+ * Plans: the host grouping and work list, built from HOST copies of the
+ * mapping (as an inference runtime holds them), then reused by launches
+ * without any host-device synchronisation.
+ *
+ * ikbo_plan_create: allocates an empty plan bound to the current device.
+ * ikbo_plan_build: validates, groups candidates (ikbo_group_csr), builds the
+ *   load-balanced work list over (user, head, row tile, key chunk) and enqueues
+ *   its upload on `stream`.  Does not synchronise.  A plan may be rebuilt for a
+ *   new request at any time; the library keeps two upload buffers and waits,
+ *   if needed, only for the upload issued two builds earlier.
+ *   with_self = 1 adds causal self-attention rows (then n_q must be 1).
+ * ikbo_attn_fwd_planned: launches the attention for the plan's last build.
+ *   q_user/out_user are used only when the plan was built with with_self.
+ * ikbo_plan_destroy: frees the plan after synchronising its device.
+ */
+int ikbo_plan_create(void** plan);
+int ikbo_plan_build(void* plan, const int32_t* user_offsets_host, const int32_t* cand_to_user_host,
+                    int32_t n_users, int32_t n_cand, int32_t n_q, int32_t H, int32_t d,
+                    int32_t dtype, int32_t with_self, void* stream);
+int ikbo_attn_fwd_planned(void* plan, const void* q_cand, const void* q_user,
+                          const void* k_user, const void* v_user, float scale,
+                          void* out_cand, void* out_user, void* stream);
+void ikbo_plan_destroy(void* plan);
+
+/*
+ * Introspection of a built plan (host values): number of work items, grid
+ * size of the persistent launch, split groups, and the planned bytes of the
+ * split-KV partial workspace.  For tests and measurement.
+ */
+int ikbo_plan_info(void* plan, int64_t* info, int32_t n_info);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IKBO_H_ */

@@ -1,0 +1,350 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerances: bf16 inputs with fp32 accumulation -> max |err| <= 2e-2 and mean
+|err| <= 2e-3 per output tensor; fp32 -> max |err| <= 1e-4; integer work
+(grouping) bit-exact (CPU suite).  Bitwise checks: a single-key user returns
+its value row exactly, candidate permutations permute outputs exactly, and
+repeated launches and different launch grids give identical bits.
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+from oracle import ikbo_oracle as O
+from workloads import make_custom, make_workload
+
+from gpu_helpers import (assert_close, dtype_code, empty_out, run_planned, say, to_f64, upload)
+
+pytestmark = pytest.mark.gpu
+
+_W = {}
+
+
+def _wl(name):
+    if name not in _W:
+        _W[name] = make_workload(name)
+    return _W[name]
+
+
+def _oracle_target(w):
+    return O.target_attention(w.values("q_cand"), w.values("k_user"), w.values("v_user"), w.user_offsets,
+                              w.cand_to_user, w.scale)
+
+
+@pytest.fixture(autouse=True)
+def _clean_env():
+    saved = {k: os.environ.get(k) for k in ("IKBO_GRID_WGS", "IKBO_MIN_CHUNK", "IKBO_NO_SPLIT", "IKBO_SPLIT_SLOTS")}
+    yield
+    for k, v in saved.items():
+        if v is None:
+            os.environ.pop(k, None)
+        else:
+            os.environ[k] = v
+
+
+# ---------------------------------------------------------------------------
+# the five configurations
+# ---------------------------------------------------------------------------
+
+def test_c1_tiny_f32():
+    from broadcast_free_target_amd import ikbo_attn_fwd_ex
+    w = _wl("c1_tiny_f32")
+    say(f"case c1 planned C={w.n_cand}")
+    dev = upload(w)
+    ref = _oracle_target(w)
+    out = empty_out(w.raw("q_cand").shape, "f32")
+    run_planned(w, dev, out)
+    assert_close(to_f64(out), ref, "f32", "c1 planned")
+    say("case c1 device-mapping entry point")
+    out2 = empty_out(w.raw("q_cand").shape, "f32")
+    ikbo_attn_fwd_ex(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"], dev["cand_to_user"],
+                     w.n_users, w.n_cand, w.n_q, w.H, w.d, w.scale, dtype_code("f32"), out2)
+    import torch
+    torch.cuda.synchronize()
+    assert_close(to_f64(out2), ref, "f32", "c1 ex")
+
+
+def test_c2_typical_planned_and_north_star_call():
+    from broadcast_free_target_amd import ikbo_attn_fwd
+    import torch
+    w = _wl("c2_typical")
+    say("case c2 planned")
+    dev = upload(w)
+    ref = _oracle_target(w)
+    out = empty_out(w.raw("q_cand").shape, "bf16")
+    info = run_planned(w, dev, out)
+    say(f"  plan {info}")
+    mx, mean = assert_close(to_f64(out), ref, "bf16", "c2 planned")
+    say(f"  c2 max {mx:.3g} mean {mean:.3g}")
+    say("case c2 ikbo_attn_fwd (device mapping)")
+    out2 = empty_out(w.raw("q_cand").shape, "bf16")
+    ikbo_attn_fwd(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"], dev["cand_to_user"],
+                  w.n_users, w.n_cand, w.H, w.d, w.scale, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+def test_c3_skewed_with_single_key_users():
+    w = _wl("c3_skewed")
+    say("case c3 planned")
+    dev = upload(w)
+    ref = _oracle_target(w)
+    out = empty_out(w.raw("q_cand").shape, "bf16")
+    run_planned(w, dev, out)
+    got = to_f64(out)
+    mx, mean = assert_close(got, ref, "bf16", "c3")
+    say(f"  c3 max {mx:.3g} mean {mean:.3g}")
+    # P3: a user of length 1 returns its value row bit for bit
+    v = w.raw("v_user")
+    bits = out.view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    ones = np.where(w.lengths == 1)[0]
+    n_checked = 0
+    for c in range(w.n_cand):
+        u = w.cand_to_user[c]
+        if u in ones:
+            assert np.array_equal(bits[c, 0], v[w.user_offsets[u]]), f"cand {c} of length-1 user {u}"
+            n_checked += 1
+    assert n_checked > 0
+
+
+def test_c4_large_sampled():
+    import torch
+    w = _wl("c4_large")
+    say("case c4 planned (full size, sampled oracle rows)")
+    dev = upload(w)
+    out = empty_out(w.raw("q_cand").shape, "bf16")
+    info = run_planned(w, dev, out)
+    say(f"  plan {info}")
+    got = to_f64(out)
+    rng = np.random.default_rng(44)
+    rows = [(int(rng.integers(w.n_cand)), int(rng.integers(w.n_q)), int(rng.integers(w.H))) for _ in range(192)]
+    ref = O.target_attention_rows(w.values("q_cand"), w.values("k_user"), w.values("v_user"), w.user_offsets,
+                                  w.cand_to_user, w.scale, rows)
+    sampled = np.stack([got[c, i, h] for c, i, h in rows])
+    mx, mean = assert_close(sampled, ref, "bf16", "c4 sampled")
+    say(f"  c4 sampled max {mx:.3g} mean {mean:.3g}")
+    # every output lies in the convex hull (per coordinate) of its user's values, up to bf16 rounding
+    vv = w.values("v_user")
+    vmin = np.minimum.reduceat(vv, w.user_offsets[:-1], axis=0)
+    vmax = np.maximum.reduceat(vv, w.user_offsets[:-1], axis=0)
+    u = w.cand_to_user
+    slack = 2.0 ** -8 * np.maximum(np.abs(vmin), np.abs(vmax))[u][:, None]
+    assert np.all(got >= vmin[u][:, None] - slack - 1e-6)
+    assert np.all(got <= vmax[u][:, None] + slack + 1e-6)
+    del dev, out
+    torch.cuda.empty_cache()
+
+
+def test_c5_fused_self_target():
+    from broadcast_free_target_amd import ikbo_self_target_fwd
+    import torch
+    w = _wl("c5_fused")
+    say("case c5 fused self + target")
+    dev = upload(w)
+    out_c = empty_out(w.raw("q_cand").shape, "bf16")
+    out_u = empty_out(w.raw("q_user").shape, "bf16")
+    ikbo_self_target_fwd(dev["q_user"], dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"],
+                         dev["cand_to_user"], w.n_users, w.n_cand, w.H, w.d, w.scale, dtype_code("bf16"),
+                         out_u, out_c)
+    torch.cuda.synchronize()
+    ref_t = _oracle_target(w)
+    mx, mean = assert_close(to_f64(out_c), ref_t, "bf16", "c5 target")
+    say(f"  c5 target max {mx:.3g} mean {mean:.3g}")
+    ref_s = O.self_attention_causal(w.values("q_user"), w.values("k_user"), w.values("v_user"), w.user_offsets,
+                                    w.scale)
+    mx, mean = assert_close(to_f64(out_u), ref_s, "bf16", "c5 self")
+    say(f"  c5 self max {mx:.3g} mean {mean:.3g}")
+    bits = out_u.view(torch.int16).cpu().numpy().view(np.uint16)
+    v = w.raw("v_user")
+    for u in range(w.n_users):  # token 0 sees only key 0
+        assert np.array_equal(bits[w.user_offsets[u]], v[w.user_offsets[u]])
+    # the planned path gives the same bits as the device-mapping entry point
+    out_c2 = empty_out(w.raw("q_cand").shape, "bf16")
+    out_u2 = empty_out(w.raw("q_user").shape, "bf16")
+    run_planned(w, dev, out_c2, out_u2)
+    assert torch.equal(out_c.view(torch.int16), out_c2.view(torch.int16))
+    assert torch.equal(out_u.view(torch.int16), out_u2.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# edge matrix
+# ---------------------------------------------------------------------------
+
+EDGE = [
+    # lengths, counts per user, n_q, H, d, dtype
+    ((1, 63, 64, 65), (3, 1, 2, 5), 1, 2, 128, "bf16"),
+    ((129, 0, 7, 300), (127, 2, 0, 129), 1, 3, 128, "bf16"),
+    ((64, 1), (128, 1), 1, 1, 128, "bf16"),
+    ((500, 33), (1, 200), 3, 2, 64, "bf16"),
+    ((40, 2, 97), (5, 9, 33), 2, 2, 32, "bf16"),
+    ((1, 63, 64, 65), (3, 1, 2, 5), 1, 2, 32, "f32"),
+    ((129, 0, 7, 300), (70, 2, 1, 3), 2, 3, 64, "f32"),
+    ((33, 5), (4, 65), 1, 2, 128, "f32"),
+]
+
+
+def _custom(i, lengths, counts, n_q, H, d, dtype, with_self=False):
+    rng = np.random.default_rng(1000 + i)
+    c2u = rng.permutation(np.repeat(np.arange(len(counts)), counts)).astype(np.int32)
+    return make_custom(2000 + i, lengths, c2u, n_q=n_q, H=H, d=d, dtype=dtype, with_self=with_self,
+                       name=f"edge{i}")
+
+
+@pytest.mark.parametrize("i", range(len(EDGE)))
+@pytest.mark.parametrize("split", ["default", "forced", "off"])
+def test_edge_matrix(i, split):
+    lengths, counts, n_q, H, d, dtype = EDGE[i]
+    if split == "forced":
+        os.environ["IKBO_MIN_CHUNK"] = "64"
+        os.environ["IKBO_SPLIT_SLOTS"] = "4096"
+    elif split == "off":
+        os.environ["IKBO_NO_SPLIT"] = "1"
+    w = _custom(i, lengths, counts, n_q, H, d, dtype)
+    say(f"case edge{i} split={split} L={lengths} counts={counts} n_q={n_q} H={H} d={d} {dtype}")
+    dev = upload(w)
+    out = empty_out(w.raw("q_cand").shape, dtype)
+    run_planned(w, dev, out)
+    got = to_f64(out)
+    ref = _oracle_target(w)
+    assert_close(got, ref, dtype, f"edge{i}")
+    # zero-length users give zero rows
+    for c in range(w.n_cand):
+        if w.lengths[w.cand_to_user[c]] == 0:
+            assert np.all(got[c] == 0)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 32)])
+@pytest.mark.parametrize("split", ["default", "forced"])
+def test_edge_fused(dtype, d, split):
+    from broadcast_free_target_amd import ikbo_self_target_fwd
+    import torch
+    if split == "forced":
+        os.environ["IKBO_MIN_CHUNK"] = "64"
+        os.environ["IKBO_SPLIT_SLOTS"] = "4096"
+    w = _custom(50 + d, (1, 130, 64, 257, 0), (2, 3, 0, 1, 1), 1, 2, d, dtype, with_self=True)
+    say(f"case fused-edge {dtype} d={d} split={split}")
+    dev = upload(w)
+    out_c = empty_out(w.raw("q_cand").shape, dtype)
+    out_u = empty_out(w.raw("q_user").shape, dtype)
+    ikbo_self_target_fwd(dev["q_user"], dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"],
+                         dev["cand_to_user"], w.n_users, w.n_cand, w.H, w.d, w.scale, dtype_code(dtype), out_u, out_c)
+    torch.cuda.synchronize()
+    assert_close(to_f64(out_c), _oracle_target(w), dtype, "fused-edge target")
+    ref_s = O.self_attention_causal(w.values("q_user"), w.values("k_user"), w.values("v_user"), w.user_offsets, w.scale)
+    assert_close(to_f64(out_u), ref_s, dtype, "fused-edge self")
+
+
+# ---------------------------------------------------------------------------
+# bitwise properties
+# ---------------------------------------------------------------------------
+
+def test_p6_permutation_bitwise():
+    import torch
+    w = _custom(7, (700, 90, 1500), (130, 7, 60), 1, 2, 128, "bf16")
+    dev = upload(w)
+    say("case P6 permutation")
+    out = empty_out(w.raw("q_cand").shape, "bf16")
+    run_planned(w, dev, out)
+    perm = np.random.default_rng(5).permutation(w.n_cand)
+    w2 = make_custom(2007, w.lengths, w.cand_to_user[perm], n_q=1, H=2, d=128, dtype="bf16")
+    w2.tensors = dict(w.tensors)
+    w2.tensors["q_cand"] = w.raw("q_cand")[perm]
+    dev2 = upload(w2)
+    out2 = empty_out(w.raw("q_cand").shape, "bf16")
+    run_planned(w2, dev2, out2)
+    a = out.view(torch.int16).cpu().numpy()
+    b = out2.view(torch.int16).cpu().numpy()
+    assert np.array_equal(a[perm], b)
+
+
+@pytest.mark.parametrize("name", ["c2_typical", "c3_skewed"])
+def test_p13_determinism_across_runs_and_grids(name):
+    import torch
+    w = _wl(name)
+    dev = upload(w)
+    say(f"case P13 {name}")
+    ref = empty_out(w.raw("q_cand").shape, "bf16")
+    run_planned(w, dev, ref)
+    for grid in (None, "None", "8", "37", "1"):
+        if grid in (None, "None"):
+            os.environ.pop("IKBO_GRID_WGS", None)
+        else:
+            os.environ["IKBO_GRID_WGS"] = grid
+        out = empty_out(w.raw("q_cand").shape, "bf16")
+        run_planned(w, dev, out)
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"grid {grid}"
+
+
+# ---------------------------------------------------------------------------
+# materialised-broadcast comparator
+# ---------------------------------------------------------------------------
+
+def test_materialized_matches_oracle():
+    from broadcast_free_target_amd import ikbo_attn_fwd_materialized
+    import torch
+    w = _wl("c2_typical")
+    dev = upload(w)
+    say("case materialized c2")
+    out = empty_out(w.raw("q_cand").shape, "bf16")
+    ikbo_attn_fwd_materialized(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"],
+                               dev["cand_to_user"], w.n_users, w.n_cand, w.n_q, w.H, w.d, w.scale,
+                               dtype_code("bf16"), out)
+    torch.cuda.synchronize()
+    assert_close(to_f64(out), _oracle_target(w), "bf16", "materialized c2")
+
+
+def test_materialized_chunked_multi_query():
+    from broadcast_free_target_amd import ikbo_attn_fwd_materialized
+    import torch
+    w = _custom(9, (300, 64, 1, 1000), (4, 9, 2, 3), 2, 2, 128, "bf16")
+    dev = upload(w)
+    os.environ["IKBO_BCAST_MAX_GB"] = "0.002"  # forces several candidate chunks
+    try:
+        out = empty_out(w.raw("q_cand").shape, "bf16")
+        say("case materialized chunked")
+        ikbo_attn_fwd_materialized(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"],
+                                   dev["cand_to_user"], w.n_users, w.n_cand, w.n_q, w.H, w.d, w.scale,
+                                   dtype_code("bf16"), out)
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("IKBO_BCAST_MAX_GB", None)
+    assert_close(to_f64(out), _oracle_target(w), "bf16", "materialized chunked")
+
+
+# ---------------------------------------------------------------------------
+# errors: no launch, no write
+# ---------------------------------------------------------------------------
+
+def test_errors_leave_output_untouched():
+    from broadcast_free_target_amd import (IKBO_ERR_BAD_MAPPING, IKBO_ERR_BAD_OFFSETS, IKBO_ERR_UNSUPPORTED,
+                                           IkboError, ikbo_attn_fwd, ikbo_attn_fwd_ex)
+    import torch
+    w = _custom(11, (10, 20), (3, 4), 1, 2, 128, "bf16")
+    dev = upload(w)
+    say("case errors")
+    out = empty_out(w.raw("q_cand").shape, "bf16", fill=7.0)
+    bad = dev["cand_to_user"].clone()
+    bad[2] = 5
+    with pytest.raises(IkboError) as e:
+        ikbo_attn_fwd(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"], bad, w.n_users, w.n_cand,
+                      w.H, w.d, w.scale, out)
+    assert e.value.status == IKBO_ERR_BAD_MAPPING
+    bad_offs = dev["user_offsets"].clone()
+    bad_offs[1] = 25
+    with pytest.raises(IkboError) as e:
+        ikbo_attn_fwd(dev["q_cand"], dev["k_user"], dev["v_user"], bad_offs, dev["cand_to_user"], w.n_users,
+                      w.n_cand, w.H, w.d, w.scale, out)
+    assert e.value.status == IKBO_ERR_BAD_OFFSETS
+    with pytest.raises(IkboError) as e:
+        ikbo_attn_fwd_ex(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"], dev["cand_to_user"],
+                         w.n_users, w.n_cand, 1, w.H, 96, w.scale, 0, out)
+    assert e.value.status == IKBO_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.all(out.float() == 7.0)
+    # n_cand = 0 is a no-op
+    ikbo_attn_fwd(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"], dev["cand_to_user"], w.n_users,
+                  0, w.H, w.d, w.scale, out)
+    torch.cuda.synchronize()
+    assert torch.all(out.float() == 7.0)

@@ -1,0 +1,234 @@
+"""CPU-only checks of the library: exports, CSR grouping bit-exact against the
+oracle through the C ABI, argument errors, and the work-list planner built
+with AddressSanitizer/UBSan."""
+
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle import ikbo_oracle as O
+from workloads import make_workload
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ikbo.h")
+CSRC = os.path.join(ROOT, "broadcast_free_target_amd", "csrc")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from broadcast_free_target_amd import ikbo
+    return ikbo.load_library()
+
+
+def _declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ikbo_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(lib):
+    from broadcast_free_target_amd import ikbo
+    names = _declared_symbols()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in ikbo.h but not exported"
+    assert sorted(ikbo.SIGNATURES) == names, "binding and header disagree"
+    assert lib.ikbo_version() >= 100
+
+
+CSR_CASES = ["c1_tiny_f32", "c2_typical", "c3_skewed"]
+
+
+@pytest.mark.parametrize("name", CSR_CASES)
+@pytest.mark.parametrize("n_q,bm", [(1, 128), (4, 128), (1, 32), (3, 7)])
+def test_csr_bit_exact_vs_oracle(name, n_q, bm):
+    from broadcast_free_target_amd import ikbo_group_csr
+    w = make_workload(name)
+    got = ikbo_group_csr(w.cand_to_user, w.n_users, n_q, bm)
+    ref = O.group_csr(w.cand_to_user, w.n_users, n_q, bm)
+    for g, key in zip(got, ("counts", "cand_offsets", "cand_perm", "tiles")):
+        assert g.dtype == np.int32
+        assert np.array_equal(g, ref[key]), key
+
+
+def test_csr_bit_exact_large_mappings():
+    from broadcast_free_target_amd import ikbo_group_csr
+    rng = np.random.default_rng(3)
+    for U, C in [(150, 10000), (30, 2048), (1, 500), (1000, 999)]:
+        c2u = rng.integers(0, U, size=C).astype(np.int32)
+        for n_q in (1, 4):
+            got = ikbo_group_csr(c2u, U, n_q, 128)
+            ref = O.group_csr(c2u, U, n_q, 128)
+            assert all(np.array_equal(a, ref[k]) for a, k in zip(got, ("counts", "cand_offsets", "cand_perm", "tiles")))
+
+
+def test_csr_edge_cases():
+    from broadcast_free_target_amd import ikbo_group_csr
+    # no candidates
+    counts, offs, perm, tiles = ikbo_group_csr(np.zeros(0, np.int32), 3, 1, 128)
+    assert counts.tolist() == [0, 0, 0] and offs.tolist() == [0, 0, 0, 0] and perm.size == 0 and tiles.shape[0] == 0
+    # users without candidates, sorted and reverse-sorted mappings
+    for c2u in ([2, 2, 0, 0, 0], [0, 0, 0, 2, 2], [2, 0, 2, 0, 0]):
+        c2u = np.array(c2u, np.int32)
+        got = ikbo_group_csr(c2u, 4, 2, 3)
+        ref = O.group_csr(c2u, 4, 2, 3)
+        assert all(np.array_equal(a, ref[k]) for a, k in zip(got, ("counts", "cand_offsets", "cand_perm", "tiles")))
+
+
+def test_csr_errors(lib):
+    from broadcast_free_target_amd import IKBO_ERR_BAD_MAPPING, IkboError, ikbo_group_csr
+    with pytest.raises(IkboError) as e:
+        ikbo_group_csr(np.array([0, 3], np.int32), 3, 1, 128)
+    assert e.value.status == IKBO_ERR_BAD_MAPPING
+    with pytest.raises(IkboError) as e:
+        ikbo_group_csr(np.array([-1], np.int32), 3, 1, 128)
+    assert e.value.status == IKBO_ERR_BAD_MAPPING
+    with pytest.raises(IkboError) as e:
+        ikbo_group_csr(np.array([0], np.int32), 0, 1, 128)
+    assert e.value.status == IKBO_ERR_BAD_MAPPING
+
+
+# ---------------------------------------------------------------------------
+# work-list planner (host C++, sanitizer build)
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def driver(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("plan") / "plan_driver")
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-I", CSRC, os.path.join(ROOT, "tests", "csrc", "plan_driver.cpp"), os.path.join(CSRC, "ikbo_plan.cpp"),
+           "-o", out]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def _run_driver(driver, offs, c2u, n_q=1, H=2, with_self=0, bm=128, bn=64, grid=512, min_chunk=256, split=1):
+    nums = [len(offs) - 1, len(c2u), n_q, H, with_self, bm, bn, grid, min_chunk, split, *offs, *c2u]
+    r = subprocess.run([driver], input=" ".join(map(str, nums)), capture_output=True, text=True, check=True,
+                       env={**os.environ, "ASAN_OPTIONS": "detect_leaks=1"})
+    lines = r.stdout.splitlines()
+    rc = int(lines[0].split()[1])
+    if rc != 0:
+        return rc, None
+    _, n_items, grid_, n_groups, n_slots = lines[1].split()
+    perm = np.array(lines[2].split()[1:], dtype=np.int64)
+    items = np.array([l.split()[1:] for l in lines[3:]], dtype=np.int64).reshape(-1, 12)
+    return 0, dict(n_items=int(n_items), grid=int(grid_), n_groups=int(n_groups), n_slots=int(n_slots),
+                   perm=perm, items=items)
+
+
+def _check_plan(plan, offs, c2u, n_q, H, with_self, bm, bn, grid_slots):
+    offs = np.asarray(offs, dtype=np.int64)
+    c2u = np.asarray(c2u, dtype=np.int64)
+    U = len(offs) - 1
+    L = np.diff(offs)
+    items = plan["items"]
+    assert plan["n_items"] == len(items)
+    assert plan["grid"] == min(len(items), grid_slots)
+    counts = np.bincount(c2u, minlength=U)
+    cand_offsets = np.concatenate([[0], np.cumsum(counts)])
+
+    def user_of(kind, kb, rb):
+        if kind == 0:
+            us = [u for u in range(U) if offs[u] == kb and cand_offsets[u] == rb and counts[u] > 0]
+        else:
+            us = [u for u in range(U) if offs[u] == kb and L[u] > 0]
+        assert len(us) == 1
+        return us[0]
+
+    # group the chunks of each (kind, user, head, row tile)
+    tiles = {}
+    for it in items:
+        kb, rb, r0, nr, a, b, hh, kd, g, ch, nc, s0 = (int(x) for x in it)
+        assert 1 <= nr <= bm and 0 <= a <= b and kd in (0, 1)
+        if g >= 0:
+            assert a % bn == 0 and nc >= 2
+        else:
+            assert nc == 1 and ch == 0
+        u = user_of(kd, kb, rb)
+        tiles.setdefault((kd, u, hh, r0, nr), []).append((a, b, g, ch, nc, s0))
+    rows = {}
+    for (kd, u, hh, r0, nr), chunks in tiles.items():
+        chunks.sort()
+        assert chunks[0][0] == 0
+        for x, y in zip(chunks[:-1], chunks[1:]):
+            assert x[1] == y[0]
+        assert [c[3] for c in chunks] == list(range(len(chunks)))
+        assert len({(c[2], c[4], c[5]) for c in chunks}) == 1
+        expect_end = L[u] if kd == 0 else r0 + nr  # causal rows never see past their last token
+        assert chunks[-1][1] == expect_end
+        rows.setdefault((kd, u, hh), []).append((r0, nr))
+    for u in range(U):
+        for hh in range(H):
+            t = sorted(rows.get((0, u, hh), []))
+            assert sum(n for _, n in t) == counts[u] * n_q
+            assert all(a + n == b for (a, n), (b, _) in zip(t[:-1], t[1:])) and (not t or t[0][0] == 0)
+            s = sorted(rows.get((1, u, hh), []))
+            assert sum(n for _, n in s) == (L[u] if with_self else 0)
+    # one disjoint slot range per split group
+    groups = {}
+    for it in items:
+        if it[8] >= 0:
+            groups.setdefault(int(it[8]), set()).add((int(it[11]), int(it[10])))
+    assert all(len(v) == 1 for v in groups.values())
+    spans = sorted(next(iter(v)) for v in groups.values())
+    assert sum(nc for _, nc in spans) == plan["n_slots"] and len(groups) == plan["n_groups"]
+    for (s0, nc), (s1, _) in zip(spans[:-1], spans[1:]):
+        assert s0 + nc <= s1
+    # longest first
+    cost = items[:, 5] - items[:, 4]
+    assert np.all(np.diff(cost) <= 0)
+    # the boustrophedon deal gives every item to exactly one workgroup
+    G = plan["grid"]
+    hits = np.zeros(len(items), int)
+    for w in range(G):
+        p = 0
+        while True:
+            pos = p * G + ((G - 1 - w) if p & 1 else w)
+            if pos >= len(items):
+                break
+            hits[pos] += 1
+            p += 1
+    assert np.all(hits == 1)
+    assert np.array_equal(plan["perm"], np.argsort(c2u, kind="stable"))
+
+
+@pytest.mark.parametrize("name", ["c2_typical", "c3_skewed", "c5_fused"])
+def test_planner_on_configs(driver, name):
+    w = make_workload(name) if name != "c5_fused" else None
+    if w is None:
+        rng = np.random.Generator(np.random.PCG64(1005))
+        L = rng.integers(256, 2048, size=30, endpoint=True)
+        counts = rng.multinomial(2048, [1 / 30] * 30)
+        c2u = rng.permutation(np.repeat(np.arange(30), counts)).astype(np.int32)
+        offs = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+        n_q, H, with_self = 1, 4, 1
+    else:
+        offs, c2u, n_q, H, with_self = w.user_offsets, w.cand_to_user, w.n_q, w.H, 0
+    for grid, min_chunk in [(512, 256), (64, 128), (8, 64), (1, 256)]:
+        rc, plan = _run_driver(driver, offs, c2u, n_q=n_q, H=H, with_self=with_self, grid=grid, min_chunk=min_chunk)
+        assert rc == 0
+        _check_plan(plan, offs, c2u, n_q, H, with_self, 128, 64, grid)
+
+
+def test_planner_edge_cases(driver):
+    cases = [
+        ([0, 0, 5, 5], [1, 1, 0, 2]),          # zero-length users holding candidates
+        ([0, 1, 2], [0, 1, 1, 1, 0]),           # length-1 users
+        ([0, 3000], list(range(1)) * 3),        # one long user, few rows: split
+        ([0, 100, 200], []),                    # no candidates
+    ]
+    for offs, c2u in cases:
+        for ws in (0, 1):
+            rc, plan = _run_driver(driver, offs, c2u, n_q=2 if not ws else 1, H=3, with_self=ws)
+            assert rc == 0
+            _check_plan(plan, offs, c2u, 2 if not ws else 1, 3, ws, 128, 64, 512)
+    rc, _ = _run_driver(driver, [1, 2], [0])
+    assert rc == -2
+    rc, _ = _run_driver(driver, [0, 2, 1], [0])
+    assert rc == -2
+    rc, _ = _run_driver(driver, [0, 2], [1])
+    assert rc == -3
