@@ -117,10 +117,11 @@ struct Plan {
   // last build
   bool built = false;
   int32_t n_users = 0, n_cand = 0, n_q = 1, H = 0, d = 0, dtype = IKBO_DTYPE_BF16, with_self = 0;
+  int32_t stages = 2;  // bf16 kernel ring depth chosen at build time
   int64_t total_len = 0;
   HostPlan hp;
   // device copies of the work list
-  DevBuf d_items, d_perm, d_ws_o, d_ws_ml, d_counters;
+  DevBuf d_items, d_perm, d_groups, d_ws_o, d_ws_ml;
   // two pinned upload buffers, each guarded by the event of its last upload
   PinnedBuf stage[2];
   hipEvent_t stage_ev[2] = {nullptr, nullptr};
@@ -139,7 +140,7 @@ struct Plan {
     d_perm.release();
     d_ws_o.release();
     d_ws_ml.release();
-    d_counters.release();
+    d_groups.release();
   }
 };
 
@@ -152,12 +153,18 @@ int plan_init(Plan* p) {
   return IKBO_OK;
 }
 
+// Depth of the bf16 kernel's HBM -> LDS ring (IKBO_STAGES overrides; 2, 3 or 4).
+int bf16_stages() {
+  const int s = env_int("IKBO_STAGES", ikbo::kBf16DefaultStages);
+  return (s == 2 || s == 3 || s == 4) ? s : ikbo::kBf16DefaultStages;
+}
+
 PlanParams params_for(const Plan& p, int32_t dtype) {
   PlanParams pp;
   if (dtype == IKBO_DTYPE_BF16) {
     pp.bm = ikbo::kBf16TileRows;
     pp.bn = ikbo::kBf16TileKeys;
-    pp.grid_slots = std::max(1, p.n_cu * ikbo::kBf16WgsPerCu);
+    pp.grid_slots = std::max(1, p.n_cu * (bf16_stages() == 2 ? 2 : 1));
     pp.min_chunk = 256;
     pp.allow_split = true;
   } else {
@@ -207,19 +214,24 @@ int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n
     return rc;
   if ((rc = p->d_ws_ml.ensure(static_cast<size_t>(hp.n_slots) * tile_rows * 2 * sizeof(float), false)) != IKBO_OK)
     return rc;
-  if ((rc = p->d_counters.ensure(static_cast<size_t>(hp.n_groups) * sizeof(int32_t), true)) != IKBO_OK) return rc;
+  const size_t groups_bytes = hp.groups.size() * sizeof(ikbo::MergeItem);
+  if ((rc = p->d_groups.ensure(groups_bytes, false)) != IKBO_OK) return rc;
 
   // Stage into the pinned buffer whose previous upload is complete.
   const int s = p->next_stage;
   p->next_stage ^= 1;
   if (p->stage_used[s]) IKBO_HIP(hipEventSynchronize(p->stage_ev[s]));
-  if ((rc = p->stage[s].ensure(items_bytes + perm_bytes + 16)) != IKBO_OK) return rc;
+  if ((rc = p->stage[s].ensure(items_bytes + perm_bytes + groups_bytes + 16)) != IKBO_OK) return rc;
   char* hb = static_cast<char*>(p->stage[s].ptr);
   if (items_bytes) std::memcpy(hb, hp.items.data(), items_bytes);
   if (perm_bytes) std::memcpy(hb + items_bytes, hp.cand_perm.data(), perm_bytes);
+  if (groups_bytes) std::memcpy(hb + items_bytes + perm_bytes, hp.groups.data(), groups_bytes);
   if (items_bytes) IKBO_HIP(hipMemcpyAsync(p->d_items.ptr, hb, items_bytes, hipMemcpyHostToDevice, stream));
   if (perm_bytes)
     IKBO_HIP(hipMemcpyAsync(p->d_perm.ptr, hb + items_bytes, perm_bytes, hipMemcpyHostToDevice, stream));
+  if (groups_bytes)
+    IKBO_HIP(hipMemcpyAsync(p->d_groups.ptr, hb + items_bytes + perm_bytes, groups_bytes, hipMemcpyHostToDevice,
+                            stream));
   IKBO_HIP(hipEventRecord(p->stage_ev[s], stream));
   p->stage_used[s] = true;
 
@@ -231,6 +243,7 @@ int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n
   p->d = d;
   p->dtype = dtype;
   p->with_self = with_self;
+  p->stages = bf16_stages();
   p->total_len = offs[n_users];
   p->built = true;
   return IKBO_OK;
@@ -290,10 +303,13 @@ int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* 
   ap.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   ap.ws_o = static_cast<float*>(p->d_ws_o.ptr);
   ap.ws_ml = static_cast<float*>(p->d_ws_ml.ptr);
-  ap.counters = static_cast<int32_t*>(p->d_counters.ptr);
-  hipError_t e = p->dtype == IKBO_DTYPE_BF16 ? ikbo::launch_attn_bf16(ap, p->d, p->hp.grid, stream)
+  hipError_t e = p->dtype == IKBO_DTYPE_BF16 ? ikbo::launch_attn_bf16(ap, p->d, p->stages, p->hp.grid, stream)
                                              : ikbo::launch_attn_f32(ap, p->d, p->hp.grid, stream);
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  if (p->hp.n_groups > 0) {
+    e = ikbo::launch_merge(ap, static_cast<const ikbo::MergeItem*>(p->d_groups.ptr), p->hp.n_groups, p->d, stream);
+    if (e != hipSuccess) return fail_hip(e, "merge launch");
+  }
   return IKBO_OK;
 }
 

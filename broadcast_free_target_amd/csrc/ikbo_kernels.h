@@ -12,7 +12,7 @@ namespace ikbo {
 // Rows per workgroup tile and keys per K/V tile of the bf16 MFMA kernel.
 constexpr int kBf16TileRows = 128;
 constexpr int kBf16TileKeys = 64;
-constexpr int kBf16WgsPerCu = 2;
+constexpr int kBf16DefaultStages = 2;
 // Rows per tile of the fp32 kernel (one thread per row) and keys per tile.
 constexpr int kF32TileRows = 64;
 constexpr int kF32TileKeys = 32;
@@ -32,11 +32,14 @@ struct AttnParams {
   float scale_log2;       // scale * log2(e): scores are kept in base 2
   float* ws_o;            // split partials: [slots, tile_rows, d] fp32, unnormalised
   float* ws_ml;           // split partials: [slots, tile_rows, 2] (running max, sum)
-  int32_t* counters;      // [groups] arrival counters, zero between launches
 };
 
-hipError_t launch_attn_bf16(const AttnParams& p, int d, int grid, hipStream_t stream);
+// stages: depth of the HBM -> LDS ring (2, 3 or 4); 2 stages allow two
+// resident workgroups per CU, 3-4 stages one.
+hipError_t launch_attn_bf16(const AttnParams& p, int d, int stages, int grid, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParams& p, int d, int grid, hipStream_t stream);
+// Merges the split-KV partials of n_groups groups into the bf16 outputs.
+hipError_t launch_merge(const AttnParams& p, const MergeItem* groups, int n_groups, int d, hipStream_t stream);
 
 // Materialised broadcast: for each of n local candidates, copy `len[c]` rows of
 // `row_bytes` bytes from k/v at src_row[c] to kb/vb at dst_row[c].

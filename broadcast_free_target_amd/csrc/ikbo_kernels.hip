@@ -7,29 +7,34 @@
 // once per tile through LDS and every row of the tile reuses each K/V tile.
 //
 // bf16 kernel, one workgroup = 4 wave64s = 128 rows (32 rows per wave):
-//   * S^T = K . Q^T with v_mfma_f32_32x32x16_bf16.  Keys are the MFMA M
+//   * K/V tiles of 64 keys move HBM -> LDS with global_load_lds_dwordx4
+//     (no register staging) through a ring of NST stages, so up to NST-1
+//     tiles are in flight while one is being computed.  Each tile is stored
+//     in natural [key][d] order with its 16-byte chunks XOR-swizzled per row
+//     (bank-conflict-free reads).  Keys past the user's end load the user's
+//     last key again (finite data) and are masked to -inf in the scores.
+//   * S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: keys are the MFMA M
 //     dimension and query rows the N dimension, so each lane owns one query
-//     row: the row max and row sum of the online softmax reduce inside the
-//     lane plus one exchange with the lane 32 apart.
+//     row; the online-softmax row max and row sum reduce inside the lane plus
+//     one exchange with the lane 32 apart.
 //   * O^T = V^T . P^T with the same instruction: P^T is the lane's own
-//     probabilities (no re-layout), V^T comes from a transposed LDS copy.
-//   * K rows enter the A operand in an order that swaps bits 2 and 3 of the
-//     row index; then the 8 probabilities a lane feeds to one PV step belong
-//     to 8 consecutive keys, and the V^T operand is one 16-byte LDS read.
+//     probabilities (no re-layout).  The V^T operand is read with
+//     ds_read_b64_tr_b16, which hands each lane 4 consecutive keys of one
+//     d column out of the natural-layout tile; two such reads make one
+//     8-key MFMA operand whose key order matches the probabilities' order.
 //   * Online softmax (AI-infra guide, section 4.6.1): running max m, running
 //     sum l, O rescaled by exp2(m_old - m_new); scores carry the log2(e)
 //     factor so exp2 is used.  Only the last, partial K/V tile and tiles on
 //     the causal diagonal run the masked variant (loop peeling, TLX jagged
 //     attention post, "loop peeling").
-//   * Keys past the user's end are zero-filled in LDS, never loaded.
 //   * Persistent launch: items arrive longest-first; logical workgroup w
 //     takes the items of a boustrophedon deal.  Logical ids are mapped so that
 //     neighbouring ids run on one XCD (workgroups are dealt to the 8 XCDs
 //     round-robin), keeping row tiles of one (user, head) on one L2.
-//   * Split key ranges write unnormalised partials (O, m, l); the last
-//     workgroup of a group to arrive merges all chunks in chunk order
-//     (log-sum-exp merge, AI-infra guide section 4.6.4), so the result does
-//     not depend on arrival order.
+//   * Split key ranges write unnormalised partials (O, m, l); a second,
+//     wide kernel merges each group's chunks in chunk order (the
+//     log-sum-exp merge of the AI-infra guide, section 4.6.4), so the result
+//     does not depend on the schedule and no workgroup waits on another.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -45,20 +50,35 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int kBM = kBf16TileRows;  // rows per workgroup
 constexpr int kBN = kBf16TileKeys;  // keys per K/V tile
 constexpr int kThreads = 256;       // 4 wave64
 constexpr float kNegInf = -__builtin_inff();
 
+// One K or V tile in LDS: kBN rows of D bf16, 16-byte chunks swizzled per row.
 template <int D>
-struct Smem {
-  static constexpr int kStride = D + 8;    // K tile row stride, bf16 elements (pad: bank spread)
-  static constexpr int vStride = kBN + 8;  // V^T tile row stride
-  static constexpr int kElems = kBN * kStride;
-  static constexpr int vElems = D * vStride;
-  static constexpr int stage = kElems + vElems;
+struct Tile {
+  static constexpr int NCH = D / 8;                 // 16-byte chunks per row
+  static constexpr int elems = kBN * D;             // one K or V tile
+  static constexpr int stage = 2 * elems;           // K tile then V tile
+  static constexpr int loads = kBN * NCH / kThreads;  // 16-byte loads per thread per tile
+  static_assert(loads >= 1 && loads * kThreads == kBN * NCH, "tile shape");
 };
+
+// Per-row XOR applied to the 16-byte chunk index.  Over 16 consecutive rows it
+// takes 16 distinct values, and over 4 consecutive rows (aligned) its bits 2-3
+// differ, which keeps both the K-operand reads and the transposed V reads
+// free of bank conflicts.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int chunk) {
+  return (row * Tile<D>::NCH + (chunk ^ (swz(row) & (Tile<D>::NCH - 1)))) * 8;
+}
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t x) { return __builtin_bit_cast(bf16x8_t, x); }
 
@@ -73,12 +93,31 @@ __device__ __forceinline__ u32x2_t pack4_bf16(float a, float b, float c, float d
   return r;
 }
 
-// Row of the A operand that carries key `m` of a 32-key block: bits 2 and 3 swapped.
-__device__ __forceinline__ int swap_bits23(int m) {
-  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// One 16-byte-per-lane HBM -> LDS copy (global_load_lds_dwordx4): lane l's 16
+// bytes land at LDS byte address lds_byte + 16*l.  Written as inline assembly so
+// that the compiler's wait insertion, which cannot tell ring stages apart and
+// would wait for every copy in flight before any LDS read, leaves the ring
+// alone; completion is awaited explicitly with wait_vmcnt before a barrier.
+// M0 holds the LDS base; nothing else in these kernels keeps a value in M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_byte) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
 }
 
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // Item position of logical workgroup w in a given pass of the boustrophedon
 // deal (same rule as ikbo::zigzag_position on the host).
@@ -98,59 +137,88 @@ __device__ __forceinline__ int logical_wg() {
 
 // One K/V tile for one wave: S^T, online softmax update, O^T += V^T P^T.
 template <int D, bool MASK>
-__device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks,
-                                          const uint16_t* __restrict__ Vt,
+__device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const uint16_t* __restrict__ Vs,
                                           const u32x4_t (&qf)[D / 16], f32x16_t (&oacc)[D / 32],
                                           float& m_run, float& l_run, int key_base, int key_end,
-                                          bool causal, int row_tok, float c, int n, int g) {
-  using S = Smem<D>;
+                                          bool causal, int row_tok, float c, int lane) {
+  const int n = lane & 31, g = lane >> 5;
   f32x16_t s[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
+    const int row = b * 32 + n;
+    u32x4_t a[D / 16];
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st)
+      a[st] = *reinterpret_cast<const u32x4_t*>(Ks + tile_off<D>(row, st * 2 + g));
     s[b] = f32x16_t{};
-    const uint16_t* kr = Ks + (b * 32 + swap_bits23(n)) * S::kStride + g * 8;
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kr + st * 16);
-      s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qf[st]), s[b], 0, 0, 0);
-    }
+    for (int st = 0; st < D / 16; ++st)
+      s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[st]), as_bf16x8(qf[st]), s[b], 0, 0, 0);
   }
-  // Lane value i of block b holds key  b*32 + (i/8)*16 + g*8 + i%8  of row n.
-  float mx = kNegInf;
+  // Lane value i of block b holds key  b*32 + (i/4)*8 + g*4 + i%4  of query row n.
+  // Scores stay unscaled; p = exp2(c*s - m_ref).  The masked variant keeps a
+  // bit per value for live keys (key inside the range, and not in the causal
+  // future of the row).
+  uint32_t live = 0xffffffffu;
+  if (MASK) {
+    live = 0u;
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float x = s[b][i] * c;
-      if (MASK) {
-        const int key = key_base + b * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
+      for (int i = 0; i < 16; ++i) {
+        const int key = key_base + b * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
         const bool ok = key < key_end && (!causal || key <= row_tok);
-        x = ok ? x : kNegInf;
+        live |= (ok ? 1u : 0u) << (b * 16 + i);
       }
-      s[b][i] = x;
-      mx = fmaxf(mx, x);
-    }
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(m_run, mx);
-  const float m_use = (m_new == kNegInf) ? 0.0f : m_new;  // a row with no live key yet
-  const float alpha = exp2_fast(m_run - m_use);
+  float mx;
+  if (c >= 0.0f) {
+    mx = kNegInf;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, (MASK && !((live >> (b * 16 + i)) & 1u)) ? kNegInf : s[b][i]);
+  } else {
+    mx = -kNegInf;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fminf(mx, (MASK && !((live >> (b * 16 + i)) & 1u)) ? -kNegInf : s[b][i]);
+  }
+  // Largest scaled score of the row in this tile; -inf when no key is live
+  // (mx * c is then -inf, or NaN for c == 0, both mapped to -inf).
+  float m_tile = mx * c;
+  if (!(m_tile == m_tile)) m_tile = kNegInf;
+  m_tile = fmaxf(m_tile, __shfl_xor(m_tile, 32));
+  // Lazy rescale: the reference m_ref only moves when the row max exceeds it by
+  // more than 8 (a factor 256 in p), so most tiles skip the O rescale.  O and l
+  // always share one reference, so the final O / l is unchanged.
+  const bool need = m_tile > m_run + 8.0f;
+  if (__any(need)) {
+    const float m_new = need ? m_tile : m_run;
+    const float alpha = exp2_fast(m_run - m_new);  // 0 when m_run was -inf
+    l_run *= alpha;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
+    m_run = m_new;
+  }
+  const float m_use = (m_run == kNegInf) ? 0.0f : m_run;  // a row with no live key yet
   float rs = 0.0f;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float p = exp2_fast(s[b][i] - m_use);
+      float p = exp2_fast(fmaf(s[b][i], c, -m_use));
+      if (MASK) p = ((live >> (b * 16 + i)) & 1u) ? p : 0.0f;
       s[b][i] = p;
       rs += p;
     }
   }
   rs += __shfl_xor(rs, 32);
-  l_run = l_run * alpha + rs;
-  m_run = m_new;
-#pragma unroll
-  for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
+  l_run += rs;
 
+  // P^T operand of K-step (b, s2): the lane's values i = 8*s2 .. 8*s2+7, i.e. keys
+  // b*32 + 16*s2 + {g*4 + 0..3, 8 + g*4 + 0..3}.
   bf16x8_t pb[2][2];
 #pragma unroll
   for (int b = 0; b < 2; ++b)
@@ -159,40 +227,55 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks,
 #pragma unroll
       for (int j = 0; j < 8; ++j) pb[b][s2][j] = static_cast<__bf16>(s[b][s2 * 8 + j]);
 
+  // V^T operand: lane k of each 16-lane group points at V[K0 + k/4][D0 + 4*(k%4)];
+  // the transposed read returns V[K0 .. K0+3][D0 + k] to lane k.
+  const int kq = lane & 15, half = (lane >> 4) & 1;
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) {
-    const uint16_t* vr = Vt + (mb * 32 + n) * S::vStride + g * 8;
+    const int col = mb * 32 + half * 16 + 4 * (kq & 3);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(vr + b * 32 + s2 * 16);
-        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb[b][s2], oacc[mb], 0, 0, 0);
+        const int r0 = b * 32 + 16 * s2 + g * 4 + (kq >> 2);
+        const int offa = tile_off<D>(r0, col >> 3) + (col & 4);
+        const int offb = tile_off<D>(r0 + 8, col >> 3) + (col & 4);
+        const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(Vs + offa));
+        const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(Vs + offb));
+        const i16x8_t v8 = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, v8), pb[b][s2], oacc[mb],
+                                                          0, 0, 0);
       }
     }
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void ikbo_attn_bf16_kernel(AttnParams P) {
-  using S = Smem<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * S::stage];
-  __shared__ int s_last;
+template <int D, int NST>
+__global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_kernel(AttnParams P) {
+  using T = Tile<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[NST * T::stage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, g = lane >> 5;
   const int r_w = wave * 32 + n;  // this lane's row within the tile
 
-  // Loader mapping: thread -> (16-byte column chunk, group of KPT consecutive keys).
-  constexpr int CH = D / 8;
-  constexpr int KPT = kBN * CH / kThreads;
-  static_assert(KPT >= 1 && KPT <= 4 && kBN * CH == KPT * kThreads, "loader shape");
-  const int lc = tid % CH, lq = tid / CH;
-
   const uint16_t* __restrict__ Kg = static_cast<const uint16_t*>(P.k);
   const uint16_t* __restrict__ Vg = static_cast<const uint16_t*>(P.v);
   const int64_t row_stride = static_cast<int64_t>(P.H) * D;  // elements between consecutive tokens
+
+  // Loader mapping: 16-byte unit u = tid + 256*r of a tile lands at LDS unit u;
+  // it holds row u / NCH and (swizzled) chunk u % NCH.
+  int ld_row[T::loads], ld_chunk[T::loads];
+#pragma unroll
+  for (int r = 0; r < T::loads; ++r) {
+    const int u = tid + kThreads * r;
+    ld_row[r] = u / T::NCH;
+    ld_chunk[r] = (u % T::NCH) ^ (swz(ld_row[r]) & (T::NCH - 1));
+  }
+
+  const uint32_t lds_base = lds_address(smem);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
   const int G = gridDim.x;
   const int w = logical_wg();
@@ -229,43 +312,19 @@ __global__ __launch_bounds__(kThreads, 2) void ikbo_attn_bf16_kernel(AttnParams 
 
     const int nkv = it.k1 - it.k0;
     const int ntiles = (nkv + kBN - 1) / kBN;
-    const uint16_t* kbase = Kg + (static_cast<int64_t>(it.kv_base) + it.k0) * row_stride + it.h * D + lc * 8;
-    const uint16_t* vbase = Vg + (static_cast<int64_t>(it.kv_base) + it.k0) * row_stride + it.h * D + lc * 8;
-    u32x4_t kreg[KPT], vreg[KPT];
+    const uint16_t* kbase = Kg + (static_cast<int64_t>(it.kv_base) + it.k0) * row_stride + it.h * D;
+    const uint16_t* vbase = Vg + (static_cast<int64_t>(it.kv_base) + it.k0) * row_stride + it.h * D;
 
-    auto gload = [&](int t) {
+    // Issue the HBM -> LDS copies of tile t into stage t % NST.
+    auto issue = [&](int t) {
+      const uint32_t st = lds_base + static_cast<uint32_t>((t % NST) * T::stage * 2);
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int key = t * kBN + lq * KPT + i;  // relative to k0
-        if (key < nkv) {
-          kreg[i] = *reinterpret_cast<const u32x4_t*>(kbase + key * row_stride);
-          vreg[i] = *reinterpret_cast<const u32x4_t*>(vbase + key * row_stride);
-        } else {
-          kreg[i] = u32x4_t{0, 0, 0, 0};
-          vreg[i] = u32x4_t{0, 0, 0, 0};
-        }
-      }
-    };
-    auto lstore = [&](int buf) {
-      uint16_t* Ks = smem + buf * S::stage;
-      uint16_t* Vt = Ks + S::kElems;
-#pragma unroll
-      for (int i = 0; i < KPT; ++i)
-        *reinterpret_cast<u32x4_t*>(Ks + (lq * KPT + i) * S::kStride + lc * 8) = kreg[i];
-      // Transposed V: column element e of the chunk becomes row lc*8+e; the KPT keys are contiguous.
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t h16[KPT];
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) h16[i] = (vreg[i][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-        uint16_t* dst = Vt + (lc * 8 + e) * S::vStride + lq * KPT;
-        if constexpr (KPT == 4) {
-          *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16)};
-        } else if constexpr (KPT == 2) {
-          *reinterpret_cast<uint32_t*>(dst) = h16[0] | (h16[1] << 16);
-        } else {
-          *dst = static_cast<uint16_t>(h16[0]);
-        }
+      for (int r = 0; r < T::loads; ++r) {
+        const int key = min(t * kBN + ld_row[r], nkv - 1);
+        const int64_t off = key * row_stride + ld_chunk[r] * 8;
+        const uint32_t dk = st + static_cast<uint32_t>((kThreads * r + 64 * wave_u) * 16);
+        copy16_to_lds(kbase + off, dk);
+        copy16_to_lds(vbase + off, dk + static_cast<uint32_t>(T::elems * 2));
       }
     };
 
@@ -274,27 +333,39 @@ __global__ __launch_bounds__(kThreads, 2) void ikbo_attn_bf16_kernel(AttnParams 
     const int wave_last_tok = it.row0 + wave * 32 + 31;  // largest token of this wave's rows
     const float c = P.scale_log2;
 
-    if (ntiles > 0) {
-      gload(0);
-      lstore(0);
-    }
-    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NST - 1; ++t)
+      if (t < ntiles) issue(t);
+    // The query fragment must be resident before the loop: the compiler then
+    // has no load of its own outstanding inside the loop and adds no wait
+    // there (its wait here also covers the prologue copies just issued).
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) asm volatile("" ::"v"(qf[st]));
     for (int t = 0; t < ntiles; ++t) {
-      if (t + 1 < ntiles) gload(t + 1);
+      // Wait for this thread's copies of tile t: later tiles may stay in flight.
+      const int after = min(NST - 2, ntiles - 1 - t);
+      if (after <= 0) {
+        wait_vmcnt<0>();
+      } else if (after == 1) {
+        wait_vmcnt<2 * T::loads>();
+      } else {
+        wait_vmcnt<(NST >= 4 ? 2 : 1) * 2 * T::loads>();
+      }
+      __syncthreads();  // every thread's copies of tile t are in LDS; stage (t-1) % NST is free
+      if (t + NST - 1 < ntiles) issue(t + NST - 1);
       const int key_base = it.k0 + t * kBN;  // first key of this tile, user-relative
       const bool skip = !wave_has_rows || (causal && key_base > wave_last_tok);
       if (!skip) {
-        const uint16_t* Ks = smem + (t & 1) * S::stage;
-        const uint16_t* Vt = Ks + S::kElems;
+        const uint16_t* Ks = smem + (t % NST) * T::stage;
+        const uint16_t* Vs = Ks + T::elems;
         const bool need_mask = (key_base + kBN > it.k1) || (causal && key_base + kBN - 1 > it.row0 + wave * 32);
         if (need_mask)
-          tile_step<D, true>(Ks, Vt, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, n, g);
+          tile_step<D, true>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, lane);
         else
-          tile_step<D, false>(Ks, Vt, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, n, g);
+          tile_step<D, false>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, lane);
       }
-      if (t + 1 < ntiles) lstore((t + 1) & 1);
-      __syncthreads();
     }
+    __syncthreads();  // all stages free before the next item's copies
 
     // ---- epilogue
     // Lane holds O^T rows d = mb*32 + (i/4)*8 + g*4 + i%4 of query row r_w.
@@ -326,49 +397,58 @@ __global__ __launch_bounds__(kThreads, 2) void ikbo_attn_bf16_kernel(AttnParams 
           P.ws_ml[(slot * kBM + r_w) * 2 + 1] = l_run;
         }
       }
-      __threadfence();  // release this workgroup's partials device-wide
-      __syncthreads();
-      if (tid == 0) {
-        const int prev = atomicAdd(P.counters + it.grp, 1);
-        const int last = prev == it.nchunk - 1;
-        if (last) atomicExch(P.counters + it.grp, 0);  // ready for the next launch
-        s_last = last;
-      }
-      __syncthreads();
-      if (s_last) {
-        __threadfence();  // acquire the other chunks' partials
-        const int64_t s0 = it.slot0;
-        constexpr int D4 = D / 4;
-        for (int idx = tid; idx < it.nrows * D4; idx += kThreads) {
-          const int r = idx / D4, d4 = idx % D4;
-          float mmax = kNegInf;
-          for (int ch = 0; ch < it.nchunk; ++ch) mmax = fmaxf(mmax, P.ws_ml[((s0 + ch) * kBM + r) * 2]);
-          const float mu = (mmax == kNegInf) ? 0.0f : mmax;
-          float lsum = 0.0f;
-          f32x4_t acc = f32x4_t{0, 0, 0, 0};
-          for (int ch = 0; ch < it.nchunk; ++ch) {
-            const float wgt = exp2_fast(P.ws_ml[((s0 + ch) * kBM + r) * 2] - mu);
-            lsum += wgt * P.ws_ml[((s0 + ch) * kBM + r) * 2 + 1];
-            const f32x4_t o = *reinterpret_cast<const f32x4_t*>(P.ws_o + ((s0 + ch) * kBM + r) * D + d4 * 4);
-            acc += wgt * o;
-          }
-          const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-          const int rr = it.row0 + r;
-          int64_t orow;
-          if (!causal) {
-            const int cand = P.cand_perm[it.row_base + rr / P.n_q];
-            orow = static_cast<int64_t>(cand) * P.n_q + rr % P.n_q;
-          } else {
-            orow = static_cast<int64_t>(it.row_base) + rr;
-          }
-          uint16_t* ob = static_cast<uint16_t*>(causal ? P.out_user : P.out_cand);
-          *reinterpret_cast<u32x2_t*>(ob + (orow * P.H + it.h) * D + d4 * 4) =
-              pack4_bf16(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-        }
-      }
-      __syncthreads();
     }
+    wait_vmcnt<0>();  // epilogue stores retire before the next item's copies are counted
   }
+}
+
+// ---------------------------------------------------------------------------
+// split-KV merge: one workgroup per (group, 32-row block); thread -> (row, 16 d)
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256) void ikbo_merge_kernel(AttnParams P, const MergeItem* __restrict__ groups) {
+  constexpr int DPT = 16;          // d values per thread
+  constexpr int TPR = D / DPT;     // threads per row
+  constexpr int RPB = 256 / TPR;   // rows per block
+  const MergeItem gi = groups[blockIdx.x];
+  const int r = blockIdx.y * RPB + threadIdx.x / TPR;
+  if (r >= gi.nrows) return;
+  const int d0 = (threadIdx.x % TPR) * DPT;
+  float M = kNegInf, L = 0.0f;
+  f32x4_t acc[DPT / 4];
+#pragma unroll
+  for (int q = 0; q < DPT / 4; ++q) acc[q] = f32x4_t{0, 0, 0, 0};
+  for (int ch = 0; ch < gi.nchunk; ++ch) {  // fixed chunk order: deterministic
+    const int64_t row = (static_cast<int64_t>(gi.slot0) + ch) * kBM + r;
+    const float mc = P.ws_ml[row * 2 + 0];
+    const float lc = P.ws_ml[row * 2 + 1];
+    f32x4_t o[DPT / 4];
+#pragma unroll
+    for (int q = 0; q < DPT / 4; ++q) o[q] = *reinterpret_cast<const f32x4_t*>(P.ws_o + row * D + d0 + 4 * q);
+    const float Mn = fmaxf(M, mc);
+    const float mu = (Mn == kNegInf) ? 0.0f : Mn;
+    const float a = exp2_fast(M - mu), b = exp2_fast(mc - mu);
+    L = L * a + lc * b;
+#pragma unroll
+    for (int q = 0; q < DPT / 4; ++q) acc[q] = acc[q] * a + o[q] * b;
+    M = Mn;
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  const int rr = gi.row0 + r;
+  int64_t orow;
+  if (gi.kind != kKindSelf) {
+    const int cand = P.cand_perm[gi.row_base + rr / P.n_q];
+    orow = static_cast<int64_t>(cand) * P.n_q + rr % P.n_q;
+  } else {
+    orow = static_cast<int64_t>(gi.row_base) + rr;
+  }
+  uint16_t* ob = static_cast<uint16_t*>(gi.kind == kKindSelf ? P.out_user : P.out_cand);
+  uint16_t* op = ob + (orow * P.H + gi.h) * D + d0;
+#pragma unroll
+  for (int q = 0; q < DPT / 4; ++q)
+    *reinterpret_cast<u32x2_t*>(op + 4 * q) =
+        pack4_bf16(acc[q][0] * inv, acc[q][1] * inv, acc[q][2] * inv, acc[q][3] * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -491,12 +571,46 @@ __global__ __launch_bounds__(256) void ikbo_bcast_copy_kernel(const u32x4_t* __r
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const AttnParams& p, int d, int grid, hipStream_t stream) {
+hipError_t launch_attn_bf16(const AttnParams& p, int d, int stages, int grid, hipStream_t stream) {
   if (grid <= 0 || p.n_items <= 0) return hipSuccess;
+#define IKBO_LAUNCH_BF16(DD, SS) \
+  hipLaunchKernelGGL((ikbo_attn_bf16_kernel<DD, SS>), dim3(grid), dim3(kThreads), 0, stream, p)
+  if (stages == 2) {
+    switch (d) {
+      case 128: IKBO_LAUNCH_BF16(128, 2); break;
+      case 64: IKBO_LAUNCH_BF16(64, 2); break;
+      case 32: IKBO_LAUNCH_BF16(32, 2); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (stages == 3) {
+    switch (d) {
+      case 128: IKBO_LAUNCH_BF16(128, 3); break;
+      case 64: IKBO_LAUNCH_BF16(64, 3); break;
+      case 32: IKBO_LAUNCH_BF16(32, 3); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (stages == 4) {
+    switch (d) {
+      case 128: IKBO_LAUNCH_BF16(128, 4); break;
+      case 64: IKBO_LAUNCH_BF16(64, 4); break;
+      case 32: IKBO_LAUNCH_BF16(32, 4); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef IKBO_LAUNCH_BF16
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const AttnParams& p, const MergeItem* groups, int n_groups, int d, hipStream_t stream) {
+  if (n_groups <= 0) return hipSuccess;
+  const int rpb = 256 / (d / 16);
+  const dim3 grid(n_groups, (kBM + rpb - 1) / rpb);
   switch (d) {
-    case 128: hipLaunchKernelGGL(ikbo_attn_bf16_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, p); break;
-    case 64: hipLaunchKernelGGL(ikbo_attn_bf16_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, p); break;
-    case 32: hipLaunchKernelGGL(ikbo_attn_bf16_kernel<32>, dim3(grid), dim3(kThreads), 0, stream, p); break;
+    case 128: hipLaunchKernelGGL(ikbo_merge_kernel<128>, grid, dim3(256), 0, stream, p, groups); break;
+    case 64: hipLaunchKernelGGL(ikbo_merge_kernel<64>, grid, dim3(256), 0, stream, p, groups); break;
+    case 32: hipLaunchKernelGGL(ikbo_merge_kernel<32>, grid, dim3(256), 0, stream, p, groups); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -169,6 +169,7 @@ int build_plan(const int32_t* user_offsets, const int32_t* cand_to_user, int32_t
   items.reserve(base.size());
   out->n_groups = 0;
   out->n_slots = 0;
+  out->groups.clear();
   for (const auto& b : base) {
     const int64_t len = b.it.k1 - b.it.k0;
     int64_t nchunk = 1;
@@ -180,6 +181,8 @@ int build_plan(const int32_t* user_offsets, const int32_t* cand_to_user, int32_t
         const int32_t g = out->n_groups++;
         const int32_t slot0 = out->n_slots;
         out->n_slots += static_cast<int32_t>(nchunk);
+        out->groups.push_back(MergeItem{b.it.row_base, b.it.row0, b.it.nrows, b.it.h, b.it.kind, slot0,
+                                        static_cast<int32_t>(nchunk), 0});
         for (int64_t c = 0; c < nchunk; ++c) {
           Proto q = b;
           q.it.k0 = static_cast<int32_t>(b.it.k0 + c * clen);

@@ -37,6 +37,13 @@ static_assert(sizeof(WorkItem) == 48, "WorkItem layout is shared with the kernel
 
 enum : int32_t { kKindTarget = 0, kKindSelf = 1 };
 
+// One split group (a row tile whose key range was cut into chunks), for the
+// merge kernel.  The layout is read by the device code.
+struct MergeItem {
+  int32_t row_base, row0, nrows, h, kind, slot0, nchunk, pad;
+};
+static_assert(sizeof(MergeItem) == 32, "MergeItem layout is shared with the kernels");
+
 struct PlanParams {
   int32_t bm = 128;           // rows per tile (one workgroup)
   int32_t bn = 64;            // keys per K/V tile; chunk boundaries align to it
@@ -53,6 +60,7 @@ struct HostPlan {
   std::vector<int32_t> cand_offsets;  // [n_users + 1]
   std::vector<int32_t> cand_perm;     // [n_cand]
   std::vector<WorkItem> items;        // execution order
+  std::vector<MergeItem> groups;      // [n_groups], split groups in group order
   int32_t n_groups = 0;               // split groups (one counter each)
   int32_t n_slots = 0;                // partial-result slots
   int32_t grid = 0;                   // workgroups to launch

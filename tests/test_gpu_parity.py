@@ -332,7 +332,7 @@ def test_errors_leave_output_untouched():
                       w.H, w.d, w.scale, out)
     assert e.value.status == IKBO_ERR_BAD_MAPPING
     bad_offs = dev["user_offsets"].clone()
-    bad_offs[1] = 25
+    bad_offs[1] = 31  # above user_offsets[2] = 30: decreasing
     with pytest.raises(IkboError) as e:
         ikbo_attn_fwd(dev["q_cand"], dev["k_user"], dev["v_user"], bad_offs, dev["cand_to_user"], w.n_users,
                       w.n_cand, w.H, w.d, w.scale, out)
