@@ -129,6 +129,8 @@ def main():
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--report", action="store_true", help="add cold-cache and materialised-broadcast figures")
     ap.add_argument("--kernel-only", action="store_true", help="loop only the planned launch (for profiling)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (to scale memory counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -141,6 +143,16 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                          "launches": args.steps}), flush=True)
+        return
     w = make_workload(args.config)
     dev = upload(w)
     dt_code = ikbo.IKBO_DTYPE_BF16 if w.dtype == "bf16" else ikbo.IKBO_DTYPE_F32
@@ -168,21 +180,24 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     if args.kernel_only:
         build()
+    # Timed region: K whole steps.  The library records HIP events on this
+    # stream around the attention kernel and the merge kernel of every launch.
+    ikbo.ikbo_plan_timing(plan, True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         if not args.kernel_only:
             build()
-        ev[i][0].record(stream)
         launch()
-        ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    attn_ms, merge_ms = ikbo.ikbo_plan_timing_read(plan, K)
+    ikbo.ikbo_plan_timing(plan, False)
+    kern_ms = attn_ms
     k_avg_ms = float(np.mean(kern_ms))
+    merge_avg_ms = float(np.mean(merge_ms))
 
     flops, byts, mat_bytes = algorithmic_counts(w)
     ms_per_step = wall * 1e3 / K
@@ -201,10 +216,13 @@ def main():
     roof["traffic"] = traffic_from_profiles(args.config)
     roof["kernel"] = DOMINANT_KERNEL if w.dtype == "bf16" else "ikbo_attn_f32_kernel"
     roof["kernel_avg_us"] = k_avg_ms * 1e3
+    roof["merge_kernel_avg_us"] = merge_avg_ms * 1e3
     roof["algorithmic_bytes_per_launch"] = byts
     roof["algorithmic_flops_per_launch"] = flops
 
     extra = {
+        "attn_plus_merge_us": (k_avg_ms + merge_avg_ms) * 1e3,
+        "attn_plus_merge_tflops": flops / ((k_avg_ms + merge_avg_ms) * 1e-3) / 1e12,
         "kernel_tflops": flops / (k_avg_ms * 1e-3) / 1e12,
         "kernel_frac_mfma_peak": flops / (k_avg_ms * 1e-3) / peak_flops,
         "kernel_hbm_gbs": byts / (k_avg_ms * 1e-3) / 1e9,
@@ -219,17 +237,16 @@ def main():
     if args.report:
         # cold cache: overwrite 2 GiB between launches so neither L2 nor MALL holds K/V
         flush = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
-        cold = []
+        ikbo.ikbo_plan_timing(plan, True)
         for _ in range(30):
             flush.fill_(1)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
             launch()
-            b.record(stream)
             torch.cuda.synchronize()
-            cold.append(a.elapsed_time(b))
+        cold, cold_m = ikbo.ikbo_plan_timing_read(plan, 30)
+        ikbo.ikbo_plan_timing(plan, False)
         del flush
         c_ms = float(np.median(cold))
+        extra["cold_merge_us_median"] = float(np.median(cold_m)) * 1e3
         extra["cold_kernel_us_median"] = c_ms * 1e3
         extra["cold_kernel_tflops"] = flops / (c_ms * 1e-3) / 1e12
         extra["cold_kernel_hbm_gbs"] = byts / (c_ms * 1e-3) / 1e9

@@ -54,6 +54,8 @@ int env_int(const char* name, int dflt) {
 
 size_t elem_size(int32_t dtype) { return dtype == IKBO_DTYPE_F32 ? 4 : 2; }
 
+constexpr int kMaxTimed = 4096;  // launches a plan can time between resets
+
 // Grow-only device buffer.
 struct DevBuf {
   void* ptr = nullptr;
@@ -86,17 +88,18 @@ struct DevBuf {
   }
 };
 
-// Grow-only pinned host buffer.
+// Grow-only pinned host buffer.  Coherent buffers are read by kernels in
+// place (the GPU does not cache them), so a later host write is always seen.
 struct PinnedBuf {
   void* ptr = nullptr;
   size_t cap = 0;
-  int ensure(size_t bytes) {
+  int ensure(size_t bytes, bool coherent = false) {
     if (bytes <= cap) return IKBO_OK;
     if (ptr) (void)hipHostFree(ptr);
     ptr = nullptr;
     cap = 0;
     size_t want = std::max<size_t>(bytes, 4096);
-    hipError_t e = hipHostMalloc(&ptr, want, hipHostMallocDefault);
+    hipError_t e = hipHostMalloc(&ptr, want, coherent ? hipHostMallocCoherent : hipHostMallocDefault);
     if (e != hipSuccess) {
       ptr = nullptr;
       return fail(IKBO_ERR_NOMEM, std::string("hipHostMalloc: ") + hipGetErrorString(e));
@@ -121,26 +124,37 @@ struct Plan {
   int64_t total_len = 0;
   HostPlan hp;
   // device copies of the work list
-  DevBuf d_items, d_perm, d_groups, d_ws_o, d_ws_ml;
-  // two pinned upload buffers, each guarded by the event of its last upload
+  DevBuf d_items, d_ws_o, d_ws_ml;  // d_items: device copy of the plan buffer (copy mode)
+  // Two pinned plan buffers, used alternately by successive builds.  With
+  // in-place reads (the default) the kernels read the work list from them;
+  // otherwise they stage a copy to the device buffers above.  Each is guarded
+  // by an event recorded after its last reader.
+  bool read_in_place = true;
   PinnedBuf stage[2];
   hipEvent_t stage_ev[2] = {nullptr, nullptr};
   bool stage_used[2] = {false, false};
   int next_stage = 0;
+  int cur_stage = 0;
+  const WorkItem* k_items = nullptr;            // what the kernels read
+  const int32_t* k_perm = nullptr;
+  const ikbo::MergeItem* k_groups = nullptr;
+  // optional kernel timing (measurement)
+  bool timing = false;
+  std::vector<hipEvent_t> tev;                  // 3 per timed launch
+  int n_timed = 0;
   // pinned landing area for device-resident mappings (synchronous entry points)
   PinnedBuf d2h;
 
   ~Plan() {
+    for (hipEvent_t e : tev) (void)hipEventDestroy(e);
     for (int i = 0; i < 2; ++i) {
       if (stage_ev[i]) (void)hipEventDestroy(stage_ev[i]);
       stage[i].release();
     }
     d2h.release();
     d_items.release();
-    d_perm.release();
     d_ws_o.release();
     d_ws_ml.release();
-    d_groups.release();
   }
 };
 
@@ -150,6 +164,8 @@ int plan_init(Plan* p) {
   IKBO_HIP(hipGetDeviceProperties(&prop, p->device));
   p->n_cu = prop.multiProcessorCount;
   for (int i = 0; i < 2; ++i) IKBO_HIP(hipEventCreateWithFlags(&p->stage_ev[i], hipEventDisableTiming));
+  const char* up = std::getenv("IKBO_PLAN_UPLOAD");
+  p->read_in_place = !(up && std::strcmp(up, "copy") == 0);
   return IKBO_OK;
 }
 
@@ -208,32 +224,40 @@ int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n
   const int tile_rows = dtype == IKBO_DTYPE_BF16 ? ikbo::kBf16TileRows : ikbo::kF32TileRows;
   const size_t items_bytes = hp.items.size() * sizeof(WorkItem);
   const size_t perm_bytes = hp.cand_perm.size() * sizeof(int32_t);
-  if ((rc = p->d_items.ensure(items_bytes, false)) != IKBO_OK) return rc;
-  if ((rc = p->d_perm.ensure(perm_bytes, false)) != IKBO_OK) return rc;
+  const size_t groups_bytes = hp.groups.size() * sizeof(ikbo::MergeItem);
   if ((rc = p->d_ws_o.ensure(static_cast<size_t>(hp.n_slots) * tile_rows * d * sizeof(float), false)) != IKBO_OK)
     return rc;
   if ((rc = p->d_ws_ml.ensure(static_cast<size_t>(hp.n_slots) * tile_rows * 2 * sizeof(float), false)) != IKBO_OK)
     return rc;
-  const size_t groups_bytes = hp.groups.size() * sizeof(ikbo::MergeItem);
-  if ((rc = p->d_groups.ensure(groups_bytes, false)) != IKBO_OK) return rc;
 
-  // Stage into the pinned buffer whose previous upload is complete.
+  // Write the work list into the pinned buffer whose last reader has finished.
   const int s = p->next_stage;
   p->next_stage ^= 1;
   if (p->stage_used[s]) IKBO_HIP(hipEventSynchronize(p->stage_ev[s]));
-  if ((rc = p->stage[s].ensure(items_bytes + perm_bytes + groups_bytes + 16)) != IKBO_OK) return rc;
+  const size_t a0 = 0, a1 = (items_bytes + 255) & ~size_t(255), a2 = a1 + ((perm_bytes + 255) & ~size_t(255));
+  if ((rc = p->stage[s].ensure(a2 + groups_bytes + 256, p->read_in_place)) != IKBO_OK) return rc;
   char* hb = static_cast<char*>(p->stage[s].ptr);
-  if (items_bytes) std::memcpy(hb, hp.items.data(), items_bytes);
-  if (perm_bytes) std::memcpy(hb + items_bytes, hp.cand_perm.data(), perm_bytes);
-  if (groups_bytes) std::memcpy(hb + items_bytes + perm_bytes, hp.groups.data(), groups_bytes);
-  if (items_bytes) IKBO_HIP(hipMemcpyAsync(p->d_items.ptr, hb, items_bytes, hipMemcpyHostToDevice, stream));
-  if (perm_bytes)
-    IKBO_HIP(hipMemcpyAsync(p->d_perm.ptr, hb + items_bytes, perm_bytes, hipMemcpyHostToDevice, stream));
-  if (groups_bytes)
-    IKBO_HIP(hipMemcpyAsync(p->d_groups.ptr, hb + items_bytes + perm_bytes, groups_bytes, hipMemcpyHostToDevice,
-                            stream));
-  IKBO_HIP(hipEventRecord(p->stage_ev[s], stream));
-  p->stage_used[s] = true;
+  if (items_bytes) std::memcpy(hb + a0, hp.items.data(), items_bytes);
+  if (perm_bytes) std::memcpy(hb + a1, hp.cand_perm.data(), perm_bytes);
+  if (groups_bytes) std::memcpy(hb + a2, hp.groups.data(), groups_bytes);
+  if (p->read_in_place) {
+    void* dev = nullptr;
+    IKBO_HIP(hipHostGetDevicePointer(&dev, hb, 0));
+    char* db = static_cast<char*>(dev);
+    p->k_items = reinterpret_cast<const WorkItem*>(db + a0);
+    p->k_perm = reinterpret_cast<const int32_t*>(db + a1);
+    p->k_groups = reinterpret_cast<const ikbo::MergeItem*>(db + a2);
+  } else {
+    if ((rc = p->d_items.ensure(a2 + groups_bytes + 256, false)) != IKBO_OK) return rc;
+    IKBO_HIP(hipMemcpyAsync(p->d_items.ptr, hb, a2 + groups_bytes, hipMemcpyHostToDevice, stream));
+    IKBO_HIP(hipEventRecord(p->stage_ev[s], stream));
+    p->stage_used[s] = true;
+    char* db = static_cast<char*>(p->d_items.ptr);
+    p->k_items = reinterpret_cast<const WorkItem*>(db + a0);
+    p->k_perm = reinterpret_cast<const int32_t*>(db + a1);
+    p->k_groups = reinterpret_cast<const ikbo::MergeItem*>(db + a2);
+  }
+  p->cur_stage = s;
 
   p->hp = std::move(hp);
   p->n_users = n_users;
@@ -295,20 +319,40 @@ int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* 
   ap.v = v;
   ap.out_cand = out_cand;
   ap.out_user = out_user;
-  ap.cand_perm = static_cast<const int32_t*>(p->d_perm.ptr);
-  ap.items = static_cast<const WorkItem*>(p->d_items.ptr);
+  ap.cand_perm = p->k_perm;
+  ap.items = p->k_items;
   ap.n_items = static_cast<int32_t>(p->hp.items.size());
   ap.H = p->H;
   ap.n_q = p->n_q;
   ap.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   ap.ws_o = static_cast<float*>(p->d_ws_o.ptr);
   ap.ws_ml = static_cast<float*>(p->d_ws_ml.ptr);
+  hipEvent_t* te = nullptr;
+  if (p->timing && p->n_timed < kMaxTimed) {
+    if (p->tev.size() < static_cast<size_t>(3 * (p->n_timed + 1))) {
+      for (int i = 0; i < 3; ++i) {
+        hipEvent_t ev;
+        IKBO_HIP(hipEventCreate(&ev));
+        p->tev.push_back(ev);
+      }
+    }
+    te = &p->tev[3 * p->n_timed];
+    ++p->n_timed;
+    IKBO_HIP(hipEventRecord(te[0], stream));
+  }
   hipError_t e = p->dtype == IKBO_DTYPE_BF16 ? ikbo::launch_attn_bf16(ap, p->d, p->stages, p->hp.grid, stream)
                                              : ikbo::launch_attn_f32(ap, p->d, p->hp.grid, stream);
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  if (te) IKBO_HIP(hipEventRecord(te[1], stream));
   if (p->hp.n_groups > 0) {
-    e = ikbo::launch_merge(ap, static_cast<const ikbo::MergeItem*>(p->d_groups.ptr), p->hp.n_groups, p->d, stream);
+    e = ikbo::launch_merge(ap, p->k_groups, p->hp.n_groups, p->d, stream);
     if (e != hipSuccess) return fail_hip(e, "merge launch");
+  }
+  if (te) IKBO_HIP(hipEventRecord(te[2], stream));
+  if (p->read_in_place) {
+    // The pinned work list of this build stays in use until these kernels end.
+    IKBO_HIP(hipEventRecord(p->stage_ev[p->cur_stage], stream));
+    p->stage_used[p->cur_stage] = true;
   }
   return IKBO_OK;
 }
@@ -474,6 +518,28 @@ int ikbo_plan_info(void* plan, int64_t* info, int32_t n_info) {
                         p->hp.n_self_tiles,
                         p->n_cu};
   for (int i = 0; i < n_info && i < 8; ++i) info[i] = v[i];
+  return IKBO_OK;
+}
+
+int ikbo_plan_timing(void* plan, int32_t enable) {
+  if (!plan) return fail(IKBO_ERR_INVALID_ARG, "plan is null");
+  Plan* p = static_cast<Plan*>(plan);
+  p->timing = enable != 0;
+  p->n_timed = 0;
+  return IKBO_OK;
+}
+
+int ikbo_plan_timing_read(void* plan, float* attn_ms, float* merge_ms, int32_t max_n, int32_t* n) {
+  if (!plan || !n || max_n < 0 || (max_n > 0 && (!attn_ms || !merge_ms)))
+    return fail(IKBO_ERR_INVALID_ARG, "null argument");
+  Plan* p = static_cast<Plan*>(plan);
+  const int m = std::min<int>(p->n_timed, max_n);
+  for (int i = 0; i < m; ++i) {
+    IKBO_HIP(hipEventSynchronize(p->tev[3 * i + 2]));
+    IKBO_HIP(hipEventElapsedTime(&attn_ms[i], p->tev[3 * i], p->tev[3 * i + 1]));
+    IKBO_HIP(hipEventElapsedTime(&merge_ms[i], p->tev[3 * i + 1], p->tev[3 * i + 2]));
+  }
+  *n = m;
   return IKBO_OK;
 }
 

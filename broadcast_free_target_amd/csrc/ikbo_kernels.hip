@@ -95,6 +95,31 @@ __device__ __forceinline__ u32x2_t pack4_bf16(float a, float b, float c, float d
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// {x[l], x[l ^ 32]} for every lane l, via v_permlane32_swap: with both
+// operands holding x, the first comes back with the lower half's values in
+// both halves and the second with the upper half's, so a symmetric op of the
+// two is the pair's reduction.  Written as assembly: the compiler's model of
+// the swap builtin treats its two results as equal and folds the op.  The
+// s_nop pairs give the wait states around a VALU write read by the swap.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void swap_halves(float x, float& a, float& b) {
+  a = x;
+  b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ float pair_max(float x) {
+  float a, b;
+  swap_halves(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  float a, b;
+  swap_halves(x, a, b);
+  return a + b;
+}
+
 // One 16-byte-per-lane HBM -> LDS copy (global_load_lds_dwordx4): lane l's 16
 // bytes land at LDS byte address lds_byte + 16*l.  Written as inline assembly so
 // that the compiler's wait insertion, which cannot tell ring stages apart and
@@ -189,7 +214,7 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const
   // (mx * c is then -inf, or NaN for c == 0, both mapped to -inf).
   float m_tile = mx * c;
   if (!(m_tile == m_tile)) m_tile = kNegInf;
-  m_tile = fmaxf(m_tile, __shfl_xor(m_tile, 32));
+  m_tile = pair_max(m_tile);
   // Lazy rescale: the reference m_ref only moves when the row max exceeds it by
   // more than 8 (a factor 256 in p), so most tiles skip the O rescale.  O and l
   // always share one reference, so the final O / l is unchanged.
@@ -214,8 +239,7 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const
       rs += p;
     }
   }
-  rs += __shfl_xor(rs, 32);
-  l_run += rs;
+  l_run += pair_sum(rs);
 
   // P^T operand of K-step (b, s2): the lane's values i = 8*s2 .. 8*s2+7, i.e. keys
   // b*32 + 16*s2 + {g*4 + 0..3, 8 + g*4 + 0..3}.
@@ -411,6 +435,7 @@ __global__ __launch_bounds__(256) void ikbo_merge_kernel(AttnParams P, const Mer
   constexpr int DPT = 16;          // d values per thread
   constexpr int TPR = D / DPT;     // threads per row
   constexpr int RPB = 256 / TPR;   // rows per block
+  constexpr int CB = 4;            // chunks loaded together
   const MergeItem gi = groups[blockIdx.x];
   const int r = blockIdx.y * RPB + threadIdx.x / TPR;
   if (r >= gi.nrows) return;
@@ -419,20 +444,30 @@ __global__ __launch_bounds__(256) void ikbo_merge_kernel(AttnParams P, const Mer
   f32x4_t acc[DPT / 4];
 #pragma unroll
   for (int q = 0; q < DPT / 4; ++q) acc[q] = f32x4_t{0, 0, 0, 0};
-  for (int ch = 0; ch < gi.nchunk; ++ch) {  // fixed chunk order: deterministic
-    const int64_t row = (static_cast<int64_t>(gi.slot0) + ch) * kBM + r;
-    const float mc = P.ws_ml[row * 2 + 0];
-    const float lc = P.ws_ml[row * 2 + 1];
-    f32x4_t o[DPT / 4];
+  for (int c0 = 0; c0 < gi.nchunk; c0 += CB) {
+    // Issue the loads of CB chunks first, then fold them in chunk order (deterministic).
+    float mc[CB], lc[CB];
+    f32x4_t o[CB][DPT / 4];
 #pragma unroll
-    for (int q = 0; q < DPT / 4; ++q) o[q] = *reinterpret_cast<const f32x4_t*>(P.ws_o + row * D + d0 + 4 * q);
-    const float Mn = fmaxf(M, mc);
-    const float mu = (Mn == kNegInf) ? 0.0f : Mn;
-    const float a = exp2_fast(M - mu), b = exp2_fast(mc - mu);
-    L = L * a + lc * b;
+    for (int k = 0; k < CB; ++k) {
+      const int ch = min(c0 + k, gi.nchunk - 1);
+      const int64_t row = (static_cast<int64_t>(gi.slot0) + ch) * kBM + r;
+      mc[k] = P.ws_ml[row * 2 + 0];
+      lc[k] = P.ws_ml[row * 2 + 1];
 #pragma unroll
-    for (int q = 0; q < DPT / 4; ++q) acc[q] = acc[q] * a + o[q] * b;
-    M = Mn;
+      for (int q = 0; q < DPT / 4; ++q) o[k][q] = *reinterpret_cast<const f32x4_t*>(P.ws_o + row * D + d0 + 4 * q);
+    }
+#pragma unroll
+    for (int k = 0; k < CB; ++k) {
+      if (c0 + k >= gi.nchunk) break;
+      const float Mn = fmaxf(M, mc[k]);
+      const float mu = (Mn == kNegInf) ? 0.0f : Mn;
+      const float a = exp2_fast(M - mu), b = exp2_fast(mc[k] - mu);
+      L = L * a + lc[k] * b;
+#pragma unroll
+      for (int q = 0; q < DPT / 4; ++q) acc[q] = acc[q] * a + o[k][q] * b;
+      M = Mn;
+    }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   const int rr = gi.row0 + r;

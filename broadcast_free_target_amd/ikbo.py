@@ -46,6 +46,9 @@ SIGNATURES = {
     "ikbo_attn_fwd_planned": (ctypes.c_int, [_P, _P, _P, _P, _P, _F, _P, _P, _P]),
     "ikbo_plan_destroy": (None, [_P]),
     "ikbo_plan_info": (ctypes.c_int, [_P, _LP, _I]),
+    "ikbo_plan_timing": (ctypes.c_int, [_P, _I]),
+    "ikbo_plan_timing_read": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
+                                             _I, _IP]),
 }
 
 _lib = None
@@ -189,3 +192,16 @@ def ikbo_plan_info(plan) -> dict:
     _check(load_library().ikbo_plan_info(plan, info, 8))
     keys = ("n_items", "grid", "n_groups", "n_slots", "partial_bytes", "n_target_tiles", "n_self_tiles", "n_cu")
     return dict(zip(keys, list(info)))
+
+
+def ikbo_plan_timing(plan, enable: bool) -> int:
+    return _check(load_library().ikbo_plan_timing(plan, 1 if enable else 0))
+
+
+def ikbo_plan_timing_read(plan, max_n: int = 4096):
+    """Per-launch (attention, merge) kernel durations in ms of the timed launches."""
+    a = (ctypes.c_float * max(max_n, 1))()
+    m = (ctypes.c_float * max(max_n, 1))()
+    n = ctypes.c_int32(0)
+    _check(load_library().ikbo_plan_timing_read(plan, a, m, max_n, ctypes.byref(n)))
+    return list(a[:n.value]), list(m[:n.value])

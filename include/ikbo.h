@@ -146,11 +146,12 @@ int ikbo_attn_fwd_materialized(const void* q_cand, const void* k_user, const voi
  * without any host-device synchronisation.
  *
  * ikbo_plan_create: allocates an empty plan bound to the current device.
- * ikbo_plan_build: validates, groups candidates (ikbo_group_csr), builds the
- *   load-balanced work list over (user, head, row tile, key chunk) and enqueues
- *   its upload on `stream`.  Does not synchronise.  A plan may be rebuilt for a
- *   new request at any time; the library keeps two upload buffers and waits,
- *   if needed, only for the upload issued two builds earlier.
+ * ikbo_plan_build: validates, groups candidates (ikbo_group_csr) and builds
+ *   the load-balanced work list over (user, head, row tile, key chunk) in a
+ *   pinned host buffer that the kernels read in place (no copy is enqueued).
+ *   Does not synchronise.  A plan may be rebuilt for a new request at any
+ *   time: it alternates between two buffers and waits, if needed, only for
+ *   the launches of the build two builds earlier to finish.
  *   with_self = 1 adds causal self-attention rows (then n_q must be 1).
  * ikbo_attn_fwd_planned: launches the attention for the plan's last build.
  *   q_user/out_user are used only when the plan was built with with_self.
@@ -164,6 +165,18 @@ int ikbo_attn_fwd_planned(void* plan, const void* q_cand, const void* q_user,
                           const void* k_user, const void* v_user, float scale,
                           void* out_cand, void* out_user, void* stream);
 void ikbo_plan_destroy(void* plan);
+
+/*
+ * Kernel timing, for measurement.  ikbo_plan_timing(plan, 1) starts recording
+ * HIP events on the launch stream around the attention kernel and around the
+ * split-KV merge kernel of each later ikbo_attn_fwd_planned call (at most 4096
+ * launches; 0 stops and both calls reset the record).  ikbo_plan_timing_read
+ * waits for the recorded events and writes per-launch durations in
+ * milliseconds (merge_ms is 0 for launches without split groups); *n receives
+ * the number written.
+ */
+int ikbo_plan_timing(void* plan, int32_t enable);
+int ikbo_plan_timing_read(void* plan, float* attn_ms, float* merge_ms, int32_t max_n, int32_t* n);
 
 /*
  * Introspection of a built plan (host values): number of work items, grid

@@ -348,3 +348,58 @@ def test_errors_leave_output_untouched():
                   0, w.H, w.d, w.scale, out)
     torch.cuda.synchronize()
     assert torch.all(out.float() == 7.0)
+
+
+# ---------------------------------------------------------------------------
+# plans: rebuilding for new requests, kernel timing
+# ---------------------------------------------------------------------------
+
+def test_plan_rebuilt_for_alternating_requests():
+    """One plan serves a stream of different requests back to back (the work
+    list of each build is read in place while the next one is written)."""
+    from broadcast_free_target_amd import (ikbo_attn_fwd_planned, ikbo_plan_build, ikbo_plan_create,
+                                           ikbo_plan_destroy)
+    import torch
+    ws = [_custom(60, (300, 900, 64), (40, 3, 90), 1, 2, 128, "bf16"),
+          _custom(61, (1200, 17), (2, 200), 1, 2, 128, "bf16"),
+          _custom(62, (65, 700, 1, 513), (5, 60, 9, 33), 1, 2, 128, "bf16")]
+    devs = [upload(w) for w in ws]
+    refs = [_oracle_target(w) for w in ws]
+    outs = [[empty_out(w.raw("q_cand").shape, "bf16") for _ in range(4)] for w in ws]
+    plan = ikbo_plan_create()
+    say("case plan rebuilds")
+    try:
+        for rep in range(4):
+            for i, w in enumerate(ws):
+                ikbo_plan_build(plan, w.user_offsets, w.cand_to_user, w.n_users, w.n_cand, 1, 2, 128, 0, 0)
+                ikbo_attn_fwd_planned(plan, devs[i]["q_cand"], None, devs[i]["k_user"], devs[i]["v_user"], w.scale,
+                                      outs[i][rep])
+        torch.cuda.synchronize()
+    finally:
+        ikbo_plan_destroy(plan)
+    for i, w in enumerate(ws):
+        for rep in range(4):
+            assert_close(to_f64(outs[i][rep]), refs[i], "bf16", f"request {i} round {rep}")
+            assert torch.equal(outs[i][rep].view(torch.int16), outs[i][0].view(torch.int16))
+
+
+def test_plan_timing_records_each_launch():
+    from broadcast_free_target_amd import (ikbo_attn_fwd_planned, ikbo_plan_build, ikbo_plan_create,
+                                           ikbo_plan_destroy, ikbo_plan_timing, ikbo_plan_timing_read)
+    import torch
+    w = _wl("c2_typical")
+    dev = upload(w)
+    out = empty_out(w.raw("q_cand").shape, "bf16")
+    plan = ikbo_plan_create()
+    try:
+        ikbo_plan_build(plan, w.user_offsets, w.cand_to_user, w.n_users, w.n_cand, 1, w.H, w.d, 0, 0)
+        ikbo_plan_timing(plan, True)
+        for _ in range(5):
+            ikbo_attn_fwd_planned(plan, dev["q_cand"], None, dev["k_user"], dev["v_user"], w.scale, out)
+        attn, merge = ikbo_plan_timing_read(plan)
+        ikbo_plan_timing(plan, False)
+        torch.cuda.synchronize()
+    finally:
+        ikbo_plan_destroy(plan)
+    assert len(attn) == 5 and len(merge) == 5
+    assert all(a > 0 for a in attn) and all(m >= 0 for m in merge)
