@@ -88,8 +88,10 @@ struct DevBuf {
   }
 };
 
-// Grow-only pinned host buffer.  Coherent buffers are read by kernels in
-// place (the GPU does not cache them), so a later host write is always seen.
+// Grow-only pinned host buffer (host-cached).  Work lists read in place by a
+// kernel are written before the launch that reads them and never rewritten
+// until that launch has completed (stage events), so the kernel boundary
+// orders every host write before the device reads it.
 struct PinnedBuf {
   void* ptr = nullptr;
   size_t cap = 0;
@@ -140,7 +142,8 @@ struct Plan {
   const ikbo::MergeItem* k_groups = nullptr;
   // optional kernel timing (measurement)
   bool timing = false;
-  std::vector<hipEvent_t> tev;                  // 3 per timed launch
+  std::vector<hipEvent_t> tev;                  // 4 per timed launch
+  std::vector<char> timed_merge;                // that launch had a merge kernel
   int n_timed = 0;
   // pinned landing area for device-resident mappings (synchronous entry points)
   PinnedBuf d2h;
@@ -217,7 +220,10 @@ int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n
   IKBO_HIP(hipGetDevice(&dev));
   if (dev != p->device) return fail(IKBO_ERR_INVALID_ARG, "plan belongs to another device");
   std::string err;
-  HostPlan hp;
+  // Build into the plan's own storage (reused across builds); until this build
+  // completes the plan cannot be launched.
+  p->built = false;
+  HostPlan& hp = p->hp;
   rc = ikbo::build_plan(offs, c2u, n_users, n_cand, n_q, H, with_self != 0, params_for(*p, dtype), &hp, &err);
   if (rc != ikbo::kOk) return fail(rc, err);
 
@@ -235,7 +241,7 @@ int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n
   p->next_stage ^= 1;
   if (p->stage_used[s]) IKBO_HIP(hipEventSynchronize(p->stage_ev[s]));
   const size_t a0 = 0, a1 = (items_bytes + 255) & ~size_t(255), a2 = a1 + ((perm_bytes + 255) & ~size_t(255));
-  if ((rc = p->stage[s].ensure(a2 + groups_bytes + 256, p->read_in_place)) != IKBO_OK) return rc;
+  if ((rc = p->stage[s].ensure(a2 + groups_bytes + 256)) != IKBO_OK) return rc;
   char* hb = static_cast<char*>(p->stage[s].ptr);
   if (items_bytes) std::memcpy(hb + a0, hp.items.data(), items_bytes);
   if (perm_bytes) std::memcpy(hb + a1, hp.cand_perm.data(), perm_bytes);
@@ -259,7 +265,6 @@ int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n
   }
   p->cur_stage = s;
 
-  p->hp = std::move(hp);
   p->n_users = n_users;
   p->n_cand = n_cand;
   p->n_q = n_q;
@@ -327,28 +332,25 @@ int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* 
   ap.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   ap.ws_o = static_cast<float*>(p->d_ws_o.ptr);
   ap.ws_ml = static_cast<float*>(p->d_ws_ml.ptr);
-  hipEvent_t* te = nullptr;
+  hipEvent_t* te = nullptr;  // attention start/end, merge start/end (stamped by the dispatches)
   if (p->timing && p->n_timed < kMaxTimed) {
-    if (p->tev.size() < static_cast<size_t>(3 * (p->n_timed + 1))) {
-      for (int i = 0; i < 3; ++i) {
-        hipEvent_t ev;
-        IKBO_HIP(hipEventCreate(&ev));
-        p->tev.push_back(ev);
-      }
+    while (p->tev.size() < static_cast<size_t>(4 * (p->n_timed + 1))) {
+      hipEvent_t ev;
+      IKBO_HIP(hipEventCreate(&ev));
+      p->tev.push_back(ev);
     }
-    te = &p->tev[3 * p->n_timed];
+    te = &p->tev[4 * p->n_timed];
+    p->timed_merge.resize(p->n_timed + 1);
+    p->timed_merge[p->n_timed] = p->hp.n_groups > 0;
     ++p->n_timed;
-    IKBO_HIP(hipEventRecord(te[0], stream));
   }
-  hipError_t e = p->dtype == IKBO_DTYPE_BF16 ? ikbo::launch_attn_bf16(ap, p->d, p->stages, p->hp.grid, stream)
-                                             : ikbo::launch_attn_f32(ap, p->d, p->hp.grid, stream);
+  hipError_t e = p->dtype == IKBO_DTYPE_BF16 ? ikbo::launch_attn_bf16(ap, p->d, p->stages, p->hp.grid, stream, te)
+                                             : ikbo::launch_attn_f32(ap, p->d, p->hp.grid, stream, te);
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
-  if (te) IKBO_HIP(hipEventRecord(te[1], stream));
   if (p->hp.n_groups > 0) {
-    e = ikbo::launch_merge(ap, p->k_groups, p->hp.n_groups, p->d, stream);
+    e = ikbo::launch_merge(ap, p->k_groups, p->hp.n_groups, p->d, stream, te ? te + 2 : nullptr);
     if (e != hipSuccess) return fail_hip(e, "merge launch");
   }
-  if (te) IKBO_HIP(hipEventRecord(te[2], stream));
   if (p->read_in_place) {
     // The pinned work list of this build stays in use until these kernels end.
     IKBO_HIP(hipEventRecord(p->stage_ev[p->cur_stage], stream));
@@ -535,9 +537,13 @@ int ikbo_plan_timing_read(void* plan, float* attn_ms, float* merge_ms, int32_t m
   Plan* p = static_cast<Plan*>(plan);
   const int m = std::min<int>(p->n_timed, max_n);
   for (int i = 0; i < m; ++i) {
-    IKBO_HIP(hipEventSynchronize(p->tev[3 * i + 2]));
-    IKBO_HIP(hipEventElapsedTime(&attn_ms[i], p->tev[3 * i], p->tev[3 * i + 1]));
-    IKBO_HIP(hipEventElapsedTime(&merge_ms[i], p->tev[3 * i + 1], p->tev[3 * i + 2]));
+    IKBO_HIP(hipEventSynchronize(p->tev[4 * i + 1]));
+    IKBO_HIP(hipEventElapsedTime(&attn_ms[i], p->tev[4 * i], p->tev[4 * i + 1]));
+    merge_ms[i] = 0.0f;
+    if (p->timed_merge[i]) {
+      IKBO_HIP(hipEventSynchronize(p->tev[4 * i + 3]));
+      IKBO_HIP(hipEventElapsedTime(&merge_ms[i], p->tev[4 * i + 2], p->tev[4 * i + 3]));
+    }
   }
   *n = m;
   return IKBO_OK;

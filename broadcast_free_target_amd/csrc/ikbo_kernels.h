@@ -35,11 +35,14 @@ struct AttnParams {
 };
 
 // stages: depth of the HBM -> LDS ring (2, 3 or 4); 2 stages allow two
-// resident workgroups per CU, 3-4 stages one.
-hipError_t launch_attn_bf16(const AttnParams& p, int d, int stages, int grid, hipStream_t stream);
-hipError_t launch_attn_f32(const AttnParams& p, int d, int grid, hipStream_t stream);
+// resident workgroups per CU, 3-4 stages one.  ev (optional): two events the
+// dispatch stamps at the kernel's start and end.
+hipError_t launch_attn_bf16(const AttnParams& p, int d, int stages, int grid, hipStream_t stream,
+                            hipEvent_t* ev = nullptr);
+hipError_t launch_attn_f32(const AttnParams& p, int d, int grid, hipStream_t stream, hipEvent_t* ev = nullptr);
 // Merges the split-KV partials of n_groups groups into the bf16 outputs.
-hipError_t launch_merge(const AttnParams& p, const MergeItem* groups, int n_groups, int d, hipStream_t stream);
+hipError_t launch_merge(const AttnParams& p, const MergeItem* groups, int n_groups, int d, hipStream_t stream,
+                        hipEvent_t* ev = nullptr);
 
 // Materialised broadcast: for each of n local candidates, copy `len[c]` rows of
 // `row_bytes` bytes from k/v at src_row[c] to kb/vb at dst_row[c].

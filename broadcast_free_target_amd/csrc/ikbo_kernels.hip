@@ -35,6 +35,7 @@
 //     wide kernel merges each group's chunks in chunk order (the
 //     log-sum-exp merge of the AI-infra guide, section 4.6.4), so the result
 //     does not depend on the schedule and no workgroup waits on another.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -309,26 +310,6 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
     const WorkItem it = P.items[pos];
     const bool causal = it.kind == kKindSelf;
 
-    // ---- query fragment (B operand of S^T): row r_w, 16 bytes per MFMA K-step
-    int64_t qrow = -1;
-    if (r_w < it.nrows) {
-      const int r = it.row0 + r_w;
-      if (!causal) {
-        const int cand = P.cand_perm[it.row_base + r / P.n_q];
-        qrow = static_cast<int64_t>(cand) * P.n_q + r % P.n_q;
-      } else {
-        qrow = static_cast<int64_t>(it.row_base) + r;
-      }
-    }
-    u32x4_t qf[D / 16];
-    {
-      const uint16_t* qb = static_cast<const uint16_t*>(causal ? P.q_user : P.q_cand);
-      const uint16_t* qp = qb + (qrow < 0 ? 0 : (qrow * P.H + it.h) * D) + g * 8;
-#pragma unroll
-      for (int st = 0; st < D / 16; ++st)
-        qf[st] = (qrow < 0) ? u32x4_t{0, 0, 0, 0} : *reinterpret_cast<const u32x4_t*>(qp + st * 16);
-    }
-
     f32x16_t oacc[D / 32];
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = f32x16_t{};
@@ -357,9 +338,32 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
     const int wave_last_tok = it.row0 + wave * 32 + 31;  // largest token of this wave's rows
     const float c = P.scale_log2;
 
+    // The ring's first copies depend only on the item: issue them before the
+    // candidate gather, so their latency overlaps the cand_perm -> Q chain.
 #pragma unroll
     for (int t = 0; t < NST - 1; ++t)
       if (t < ntiles) issue(t);
+
+    // ---- query fragment (B operand of S^T): row r_w, 16 bytes per MFMA K-step
+    int64_t qrow = -1;
+    if (r_w < it.nrows) {
+      const int r = it.row0 + r_w;
+      if (!causal) {
+        const int cand = P.cand_perm[it.row_base + r / P.n_q];
+        qrow = static_cast<int64_t>(cand) * P.n_q + r % P.n_q;
+      } else {
+        qrow = static_cast<int64_t>(it.row_base) + r;
+      }
+    }
+    u32x4_t qf[D / 16];
+    {
+      const uint16_t* qb = static_cast<const uint16_t*>(causal ? P.q_user : P.q_cand);
+      const uint16_t* qp = qb + (qrow < 0 ? 0 : (qrow * P.H + it.h) * D) + g * 8;
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st)
+        qf[st] = (qrow < 0) ? u32x4_t{0, 0, 0, 0} : *reinterpret_cast<const u32x4_t*>(qp + st * 16);
+    }
+
     // The query fragment must be resident before the loop: the compiler then
     // has no load of its own outstanding inside the loop and adds no wait
     // there (its wait here also covers the prologue copies just issued).
@@ -606,10 +610,20 @@ __global__ __launch_bounds__(256) void ikbo_bcast_copy_kernel(const u32x4_t* __r
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const AttnParams& p, int d, int stages, int grid, hipStream_t stream) {
+// With ev != nullptr, ev[0] / ev[1] are stamped by the dispatch itself at the
+// kernel's start and end (hipExtLaunchKernelGGL), for timing.
+#define IKBO_LAUNCH(KERNEL, GRID, BLOCK, ...)                                              \
+  do {                                                                                    \
+    if (ev)                                                                               \
+      hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, stream, ev[0], ev[1], 0, __VA_ARGS__); \
+    else                                                                                  \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, stream, __VA_ARGS__);                    \
+  } while (0)
+
+hipError_t launch_attn_bf16(const AttnParams& p, int d, int stages, int grid, hipStream_t stream,
+                            hipEvent_t* ev) {
   if (grid <= 0 || p.n_items <= 0) return hipSuccess;
-#define IKBO_LAUNCH_BF16(DD, SS) \
-  hipLaunchKernelGGL((ikbo_attn_bf16_kernel<DD, SS>), dim3(grid), dim3(kThreads), 0, stream, p)
+#define IKBO_LAUNCH_BF16(DD, SS) IKBO_LAUNCH((ikbo_attn_bf16_kernel<DD, SS>), dim3(grid), dim3(kThreads), p)
   if (stages == 2) {
     switch (d) {
       case 128: IKBO_LAUNCH_BF16(128, 2); break;
@@ -638,25 +652,26 @@ hipError_t launch_attn_bf16(const AttnParams& p, int d, int stages, int grid, hi
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const AttnParams& p, const MergeItem* groups, int n_groups, int d, hipStream_t stream) {
+hipError_t launch_merge(const AttnParams& p, const MergeItem* groups, int n_groups, int d, hipStream_t stream,
+                        hipEvent_t* ev) {
   if (n_groups <= 0) return hipSuccess;
   const int rpb = 256 / (d / 16);
   const dim3 grid(n_groups, (kBM + rpb - 1) / rpb);
   switch (d) {
-    case 128: hipLaunchKernelGGL(ikbo_merge_kernel<128>, grid, dim3(256), 0, stream, p, groups); break;
-    case 64: hipLaunchKernelGGL(ikbo_merge_kernel<64>, grid, dim3(256), 0, stream, p, groups); break;
-    case 32: hipLaunchKernelGGL(ikbo_merge_kernel<32>, grid, dim3(256), 0, stream, p, groups); break;
+    case 128: IKBO_LAUNCH(ikbo_merge_kernel<128>, grid, dim3(256), p, groups); break;
+    case 64: IKBO_LAUNCH(ikbo_merge_kernel<64>, grid, dim3(256), p, groups); break;
+    case 32: IKBO_LAUNCH(ikbo_merge_kernel<32>, grid, dim3(256), p, groups); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_attn_f32(const AttnParams& p, int d, int grid, hipStream_t stream) {
+hipError_t launch_attn_f32(const AttnParams& p, int d, int grid, hipStream_t stream, hipEvent_t* ev) {
   if (grid <= 0 || p.n_items <= 0) return hipSuccess;
   switch (d) {
-    case 128: hipLaunchKernelGGL(ikbo_attn_f32_kernel<128>, dim3(grid), dim3(64), 0, stream, p); break;
-    case 64: hipLaunchKernelGGL(ikbo_attn_f32_kernel<64>, dim3(grid), dim3(64), 0, stream, p); break;
-    case 32: hipLaunchKernelGGL(ikbo_attn_f32_kernel<32>, dim3(grid), dim3(64), 0, stream, p); break;
+    case 128: IKBO_LAUNCH(ikbo_attn_f32_kernel<128>, dim3(grid), dim3(64), p); break;
+    case 64: IKBO_LAUNCH(ikbo_attn_f32_kernel<64>, dim3(grid), dim3(64), p); break;
+    case 32: IKBO_LAUNCH(ikbo_attn_f32_kernel<32>, dim3(grid), dim3(64), p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

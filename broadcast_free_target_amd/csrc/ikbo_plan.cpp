@@ -42,7 +42,8 @@ int check_offsets(const int32_t* user_offsets, int32_t n_users, std::string* err
 
 int group_csr(const int32_t* cand_to_user, int32_t n_cand, int32_t n_users, int32_t n_q,
               int32_t bm, int32_t* counts, int32_t* cand_offsets, int32_t* cand_perm,
-              std::vector<int32_t>* tiles, int64_t* n_tiles, std::string* err) {
+              std::vector<int32_t>* tiles, int64_t* n_tiles, std::string* err,
+              std::vector<int32_t>* cursor_buf) {
   if (n_cand < 0 || n_users < 0 || n_q < 1 || bm < 1) {
     set_err(err, "group_csr: n_cand, n_users >= 0 and n_q, bm >= 1 required");
     return kErrInvalidArg;
@@ -67,7 +68,9 @@ int group_csr(const int32_t* cand_to_user, int32_t n_cand, int32_t n_users, int3
   cand_offsets[0] = 0;
   for (int32_t u = 0; u < n_users; ++u) cand_offsets[u + 1] = cand_offsets[u] + counts[u];
   // Counting sort; scanning candidates in index order keeps it stable.
-  std::vector<int32_t> cursor(cand_offsets, cand_offsets + n_users);
+  std::vector<int32_t> local;
+  std::vector<int32_t>& cursor = cursor_buf ? *cursor_buf : local;
+  cursor.assign(cand_offsets, cand_offsets + n_users);
   for (int32_t c = 0; c < n_cand; ++c) cand_perm[cursor[cand_to_user[c]]++] = c;
   int64_t t = 0;
   if (tiles) tiles->clear();
@@ -98,122 +101,123 @@ int build_plan(const int32_t* user_offsets, const int32_t* cand_to_user, int32_t
   }
   int rc = check_offsets(user_offsets, n_users, err);
   if (rc != kOk) return rc;
-  out->counts.assign(n_users, 0);
-  out->cand_offsets.assign(static_cast<size_t>(n_users) + 1, 0);
-  out->cand_perm.assign(n_cand, 0);
-  rc = group_csr(cand_to_user, n_cand, n_users, n_q, p.bm, out->counts.data(),
-                 out->cand_offsets.data(), out->cand_perm.data(), nullptr, &out->n_target_tiles,
-                 err);
+  out->counts.resize(n_users);
+  out->cand_offsets.resize(static_cast<size_t>(n_users) + 1);
+  out->cand_perm.resize(n_cand);
+  rc = group_csr(cand_to_user, n_cand, n_users, n_q, p.bm, out->counts.data(), out->cand_offsets.data(),
+                 out->cand_perm.data(), nullptr, &out->n_target_tiles, err, &out->cursor);
   if (rc != kOk) return rc;
 
-  // 1. Unsplit items: one per (user, head, row tile), target then self.  Row
-  //    tiles of one (user, head) share its K/V, so they are built adjacently.
-  struct Proto {
-    WorkItem it;
-    int64_t order;  // construction order, the deterministic tie-break
-  };
-  std::vector<Proto> base;
-  int64_t order = 0;
+  // 1. Total cost of the unsplit items: one per (user, head, row tile), target
+  //    then self.  Row tiles of one (user, head) share its K/V and are built
+  //    adjacently.
+  int64_t total = 0, n_base = 0;
   out->n_self_tiles = 0;
+  for (int32_t u = 0; u < n_users; ++u) {
+    const int64_t L = user_offsets[u + 1] - user_offsets[u];
+    const int64_t tiles_t = ceil_div(static_cast<int64_t>(out->counts[u]) * n_q, p.bm);
+    total += H * tiles_t * (L + p.overhead);
+    n_base += H * tiles_t;
+    if (with_self && L > 0) {
+      const int64_t tiles_s = ceil_div(L, p.bm);
+      out->n_self_tiles += tiles_s;
+      n_base += H * tiles_s;
+      for (int64_t r0 = 0; r0 < L; r0 += p.bm) total += H * (std::min<int64_t>(r0 + p.bm, L) + p.overhead);
+    }
+  }
+  // 2. Split long key ranges when there are too few items to fill the grid:
+  //    chunk lengths are multiples of bn; the kernel merges chunk partials by
+  //    log-sum-exp in chunk order, so results do not depend on the schedule.
+  const int64_t target = std::max<int64_t>(p.min_chunk, ceil_div(total, p.grid_slots));
+  out->n_groups = 0;
+  out->n_slots = 0;
+  out->groups.clear();
+  std::vector<WorkItem>& items = out->unsorted;
+  items.clear();
+  items.reserve(static_cast<size_t>(n_base) * 2);
+  auto emit = [&](WorkItem it) {
+    const int64_t len = it.k1 - it.k0;
+    int64_t nchunk = 1, clen = len;
+    if (p.allow_split && len > target + target / 2) {
+      nchunk = std::min<int64_t>(ceil_div(len, target), p.max_chunks);
+      clen = ceil_div(ceil_div(len, nchunk), p.bn) * p.bn;
+      nchunk = ceil_div(len, clen);
+    }
+    if (nchunk <= 1) {
+      items.push_back(it);
+      return;
+    }
+    const int32_t g = out->n_groups++;
+    const int32_t slot0 = out->n_slots;
+    out->n_slots += static_cast<int32_t>(nchunk);
+    out->groups.push_back(MergeItem{it.row_base, it.row0, it.nrows, it.h, it.kind, slot0,
+                                    static_cast<int32_t>(nchunk), 0});
+    const int32_t k0 = it.k0, k1 = it.k1;
+    for (int64_t c = 0; c < nchunk; ++c) {
+      it.k0 = static_cast<int32_t>(k0 + c * clen);
+      it.k1 = static_cast<int32_t>(std::min<int64_t>(k1, k0 + (c + 1) * clen));
+      it.grp = g;
+      it.chunk = static_cast<int32_t>(c);
+      it.nchunk = static_cast<int32_t>(nchunk);
+      it.slot0 = slot0;
+      items.push_back(it);
+    }
+  };
   for (int32_t u = 0; u < n_users; ++u) {
     const int32_t L = user_offsets[u + 1] - user_offsets[u];
     const int64_t rows = static_cast<int64_t>(out->counts[u]) * n_q;
     for (int32_t h = 0; h < H; ++h) {
       for (int64_t r0 = 0; r0 < rows; r0 += p.bm) {
-        WorkItem it{};
-        it.kv_base = user_offsets[u];
-        it.row_base = out->cand_offsets[u];
-        it.row0 = static_cast<int32_t>(r0);
-        it.nrows = static_cast<int32_t>(std::min<int64_t>(p.bm, rows - r0));
-        it.k0 = 0;
-        it.k1 = L;
-        it.h = h;
-        it.kind = kKindTarget;
-        it.grp = -1;
-        it.chunk = 0;
-        it.nchunk = 1;
-        it.slot0 = 0;
-        base.push_back({it, order++});
+        emit(WorkItem{user_offsets[u], out->cand_offsets[u], static_cast<int32_t>(r0),
+                      static_cast<int32_t>(std::min<int64_t>(p.bm, rows - r0)), 0, L, h, kKindTarget, -1, 0, 1, 0});
       }
     }
     if (with_self) {
-      out->n_self_tiles += ceil_div(L, p.bm);
       for (int32_t h = 0; h < H; ++h) {
         for (int64_t r0 = 0; r0 < L; r0 += p.bm) {
-          WorkItem it{};
-          it.kv_base = user_offsets[u];
-          it.row_base = user_offsets[u];
-          it.row0 = static_cast<int32_t>(r0);
-          it.nrows = static_cast<int32_t>(std::min<int64_t>(p.bm, L - r0));
-          it.k0 = 0;
-          it.k1 = it.row0 + it.nrows;  // causal: no row sees past its own token
-          it.h = h;
-          it.kind = kKindSelf;
-          it.grp = -1;
-          it.chunk = 0;
-          it.nchunk = 1;
-          it.slot0 = 0;
-          base.push_back({it, order++});
+          const int32_t nr = static_cast<int32_t>(std::min<int64_t>(p.bm, L - r0));
+          // causal: no row of the tile sees past the tile's last token
+          emit(WorkItem{user_offsets[u], user_offsets[u], static_cast<int32_t>(r0), nr, 0,
+                        static_cast<int32_t>(r0) + nr, h, kKindSelf, -1, 0, 1, 0});
         }
       }
     }
   }
-
-  // 2. Split long key ranges when there are too few items to fill the grid.
-  //    Chunk lengths are multiples of bn; the kernel merges chunk partials by
-  //    log-sum-exp in chunk order, so results do not depend on the schedule.
-  int64_t total = 0;
-  for (const auto& b : base) total += (b.it.k1 - b.it.k0) + p.overhead;
-  const int64_t target = std::max<int64_t>(p.min_chunk, ceil_div(total, p.grid_slots));
-  std::vector<Proto> items;
-  items.reserve(base.size());
-  out->n_groups = 0;
-  out->n_slots = 0;
-  out->groups.clear();
-  for (const auto& b : base) {
-    const int64_t len = b.it.k1 - b.it.k0;
-    int64_t nchunk = 1;
-    if (p.allow_split && len > target + target / 2) nchunk = ceil_div(len, target);
-    if (nchunk > 1) {
-      const int64_t clen = ceil_div(ceil_div(len, nchunk), p.bn) * p.bn;
-      nchunk = ceil_div(len, clen);
-      if (nchunk > 1) {
-        const int32_t g = out->n_groups++;
-        const int32_t slot0 = out->n_slots;
-        out->n_slots += static_cast<int32_t>(nchunk);
-        out->groups.push_back(MergeItem{b.it.row_base, b.it.row0, b.it.nrows, b.it.h, b.it.kind, slot0,
-                                        static_cast<int32_t>(nchunk), 0});
-        for (int64_t c = 0; c < nchunk; ++c) {
-          Proto q = b;
-          q.it.k0 = static_cast<int32_t>(b.it.k0 + c * clen);
-          q.it.k1 = static_cast<int32_t>(std::min<int64_t>(b.it.k1, b.it.k0 + (c + 1) * clen));
-          q.it.grp = g;
-          q.it.chunk = static_cast<int32_t>(c);
-          q.it.nchunk = static_cast<int32_t>(nchunk);
-          q.it.slot0 = slot0;
-          q.order = b.order * 65536 + c;
-          items.push_back(q);
-        }
-        continue;
-      }
-    }
-    Proto q = b;
-    q.order = b.order * 65536;
-    items.push_back(q);
-  }
-
   // 3. Longest first; equal costs keep construction order, so tiles of one
   //    (user, head) stay adjacent and land on one XCD (the kernel maps
   //    neighbouring logical workgroups to the same XCD).
-  std::stable_sort(items.begin(), items.end(), [](const Proto& a, const Proto& b) {
-    const int64_t ca = a.it.k1 - a.it.k0, cb = b.it.k1 - b.it.k0;
-    if (ca != cb) return ca > cb;
-    return a.order < b.order;
-  });
-  out->items.resize(items.size());
-  for (size_t i = 0; i < items.size(); ++i) out->items[i] = items[i].it;
+  const size_t n = items.size();
+  std::vector<uint64_t>& keys = out->keys;
+  int64_t max_cost = 0;
+  for (size_t i = 0; i < n; ++i) max_cost = std::max<int64_t>(max_cost, items[i].k1 - items[i].k0);
+  if (max_cost < 65536) {
+    // Stable LSD radix sort on (65535 - cost), two 8-bit digits.
+    keys.resize(2 * n);
+    uint64_t* a = keys.data();
+    uint64_t* b = a + n;
+    for (size_t i = 0; i < n; ++i)
+      a[i] = (static_cast<uint64_t>(65535 - (items[i].k1 - items[i].k0)) << 32) | static_cast<uint64_t>(i);
+    for (int shift = 32; shift <= 40; shift += 8) {
+      uint32_t cnt[257] = {0};
+      for (size_t i = 0; i < n; ++i) ++cnt[((a[i] >> shift) & 255u) + 1];
+      for (int k = 0; k < 256; ++k) cnt[k + 1] += cnt[k];
+      for (size_t i = 0; i < n; ++i) b[cnt[(a[i] >> shift) & 255u]++] = a[i];
+      std::swap(a, b);
+    }
+    out->items.resize(n);
+    for (size_t i = 0; i < n; ++i) out->items[i] = items[a[i] & 0xffffffffull];
+  } else {
+    keys.resize(n);
+    for (size_t i = 0; i < n; ++i) {
+      const uint64_t cost = static_cast<uint64_t>(items[i].k1 - items[i].k0);
+      keys[i] = ((0xffffffffull - cost) << 32) | static_cast<uint64_t>(i);
+    }
+    std::sort(keys.begin(), keys.end());
+    out->items.resize(n);
+    for (size_t i = 0; i < n; ++i) out->items[i] = items[keys[i] & 0xffffffffull];
+  }
   const int64_t cap = p.launch_grid > 0 ? p.launch_grid : p.grid_slots;
-  out->grid = static_cast<int32_t>(std::min<int64_t>(items.size(), cap));
+  out->grid = static_cast<int32_t>(std::min<int64_t>(out->items.size(), cap));
   return kOk;
 }
 

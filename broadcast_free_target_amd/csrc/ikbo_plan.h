@@ -51,6 +51,7 @@ struct PlanParams {
   int32_t launch_grid = 0;    // workgroups actually launched (0: grid_slots); never
                               // changes the work list, so results do not depend on it
   int32_t min_chunk = 256;    // shortest key chunk a split may produce
+  int32_t max_chunks = 8;     // most chunks one key range is cut into
   int32_t overhead = 128;     // fixed cost of an item, in key units
   bool allow_split = true;    // split long key ranges (log-sum-exp merge)
 };
@@ -66,6 +67,10 @@ struct HostPlan {
   int32_t grid = 0;                   // workgroups to launch
   int64_t n_target_tiles = 0;
   int64_t n_self_tiles = 0;
+  // scratch reused by successive builds (no allocation once warm)
+  std::vector<int32_t> cursor;
+  std::vector<WorkItem> unsorted;
+  std::vector<uint64_t> keys;
 };
 
 // Status codes mirror include/ikbo.h.
@@ -82,9 +87,10 @@ int check_offsets(const int32_t* user_offsets, int32_t n_users, std::string* err
 // triples.  Returns kErrBadMapping for an out-of-range mapping.
 int group_csr(const int32_t* cand_to_user, int32_t n_cand, int32_t n_users, int32_t n_q,
               int32_t bm, int32_t* counts, int32_t* cand_offsets, int32_t* cand_perm,
-              std::vector<int32_t>* tiles, int64_t* n_tiles, std::string* err);
+              std::vector<int32_t>* tiles, int64_t* n_tiles, std::string* err,
+              std::vector<int32_t>* cursor = nullptr);
 
-// Validates, groups, builds and orders the work list.
+// Validates, groups, builds and orders the work list.  Reuses out's storage.
 int build_plan(const int32_t* user_offsets, const int32_t* cand_to_user, int32_t n_users,
                int32_t n_cand, int32_t n_q, int32_t H, bool with_self, const PlanParams& p,
                HostPlan* out, std::string* err);
