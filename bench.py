@@ -132,6 +132,8 @@ def main():
     ap.add_argument("--kernel-only", action="store_true", help="loop only the planned launch (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (to scale memory counters)")
+    ap.add_argument("--materialized-only", action="store_true",
+                    help="loop only the materialised-broadcast comparator (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -173,6 +175,14 @@ def main():
         ikbo.ikbo_attn_fwd_planned(plan, dev["q_cand"], dev.get("q_user"), dev["k_user"], dev["v_user"], w.scale,
                                    out_c, out_u, stream)
 
+    if args.materialized_only:
+        for _ in range(args.steps):
+            ikbo.ikbo_attn_fwd_materialized(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"],
+                                            dev["cand_to_user"], w.n_users, w.n_cand, w.n_q, w.H, w.d, w.scale,
+                                            dt_code, out_c, stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"materialized_launches": args.steps, "config": args.config}), flush=True)
+        return
     build()
     info = ikbo.ikbo_plan_info(plan)
     for _ in range(args.warmup):

@@ -99,7 +99,8 @@ int ikbo_group_csr(const int32_t* cand_to_user_host, int32_t n_cand, int32_t n_u
  * IKBO target attention, bf16, one query token per candidate: the call the
  * problem statement names.  user_offsets and cand_to_user are DEVICE pointers;
  * the call copies them to the host, waits for the stream (one synchronisation),
- * groups candidates on the host, uploads the work list and launches.  `scale`
+ * groups candidates on the host, writes the work list to pinned memory that
+ * the kernels read in place, and launches.  `scale`
  * multiplies q.k (typically 1/sqrt(d)).  out: [n_cand, 1, H, d] bf16.
  */
 int ikbo_attn_fwd(const void* q_cand, const void* k_user, const void* v_user,
@@ -127,8 +128,8 @@ int ikbo_self_target_fwd(const void* q_user, const void* q_cand, const void* k_u
                          void* out_user, void* out_cand, void* stream);
 
 /*
- * Materialised-broadcast comparator (measurement only; IKBO blog section 1.4
- * "system-level broadcast" and Fig. 10, left).  A copy kernel first writes a
+ * Materialised-broadcast comparator (measurement only; the broadcast done
+ * before dispatch that the IKBO blog section 1.4 and Fig. 10 (left) describe).  A copy kernel first writes a
  * per-candidate copy of its user's K and V into a library-owned buffer
  * [sum_c L_{u(c)}, H, d]; the same attention kernel then runs with the
  * identity mapping.  Output equals ikbo_attn_fwd_ex.  Candidates are processed
@@ -155,6 +156,8 @@ int ikbo_attn_fwd_materialized(const void* q_cand, const void* k_user, const voi
  *   with_self = 1 adds causal self-attention rows (then n_q must be 1).
  * ikbo_attn_fwd_planned: launches the attention for the plan's last build.
  *   q_user/out_user are used only when the plan was built with with_self.
+ *   Launches of one plan must be ordered on one stream: they share the plan's
+ *   split-KV workspace.
  * ikbo_plan_destroy: frees the plan after synchronising its device.
  */
 int ikbo_plan_create(void** plan);
