@@ -127,7 +127,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c2_typical")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--cpu-reps", type=int, default=15)
     ap.add_argument("--report", action="store_true", help="add cold-cache and materialised-broadcast figures")
     ap.add_argument("--kernel-only", action="store_true", help="loop only the planned launch (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",

@@ -28,6 +28,8 @@ from .ikbo import (  # noqa: F401
     ikbo_plan_destroy,
     ikbo_plan_info,
     ikbo_plan_timing,
+    ikbo_plan_trace,
+    ikbo_plan_trace_read,
     ikbo_plan_timing_read,
     ikbo_self_target_fwd,
     ikbo_version,

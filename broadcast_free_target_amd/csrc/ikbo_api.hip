@@ -142,6 +142,8 @@ struct Plan {
   const ikbo::MergeItem* k_groups = nullptr;
   // optional kernel timing (measurement)
   bool timing = false;
+  bool tracing = false;
+  DevBuf d_trace;                               // [items, 6] uint64 per-item records
   std::vector<hipEvent_t> tev;                  // 4 per timed launch
   std::vector<char> timed_merge;                // that launch had a merge kernel
   int n_timed = 0;
@@ -158,6 +160,7 @@ struct Plan {
     d_items.release();
     d_ws_o.release();
     d_ws_ml.release();
+    d_trace.release();
   }
 };
 
@@ -332,6 +335,12 @@ int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* 
   ap.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   ap.ws_o = static_cast<float*>(p->d_ws_o.ptr);
   ap.ws_ml = static_cast<float*>(p->d_ws_ml.ptr);
+  ap.trace = nullptr;
+  if (p->tracing && p->dtype == IKBO_DTYPE_BF16) {
+    int rc = p->d_trace.ensure(p->hp.items.size() * 6 * sizeof(uint64_t), false);
+    if (rc != IKBO_OK) return rc;
+    ap.trace = static_cast<uint64_t*>(p->d_trace.ptr);
+  }
   hipEvent_t* te = nullptr;  // attention start/end, merge start/end (stamped by the dispatches)
   if (p->timing && p->n_timed < kMaxTimed) {
     while (p->tev.size() < static_cast<size_t>(4 * (p->n_timed + 1))) {
@@ -546,6 +555,25 @@ int ikbo_plan_timing_read(void* plan, float* attn_ms, float* merge_ms, int32_t m
     }
   }
   *n = m;
+  return IKBO_OK;
+}
+
+int ikbo_plan_trace(void* plan, int32_t enable) {
+  if (!plan) return fail(IKBO_ERR_INVALID_ARG, "plan is null");
+  static_cast<Plan*>(plan)->tracing = enable != 0;
+  return IKBO_OK;
+}
+
+int ikbo_plan_trace_read(void* plan, int64_t* records, int32_t max_items, int32_t* n_items) {
+  if (!plan || !n_items || max_items < 0 || (max_items > 0 && !records))
+    return fail(IKBO_ERR_INVALID_ARG, "null argument");
+  Plan* p = static_cast<Plan*>(plan);
+  const int n = std::min<int>(max_items, static_cast<int>(p->hp.items.size()));
+  *n_items = 0;
+  if (!p->d_trace.ptr || n == 0) return IKBO_OK;
+  IKBO_HIP(hipDeviceSynchronize());
+  IKBO_HIP(hipMemcpy(records, p->d_trace.ptr, static_cast<size_t>(n) * 6 * sizeof(uint64_t), hipMemcpyDeviceToHost));
+  *n_items = n;
   return IKBO_OK;
 }
 

@@ -32,6 +32,7 @@ struct AttnParams {
   float scale_log2;       // scale * log2(e): scores are kept in base 2
   float* ws_o;            // split partials: [slots, tile_rows, d] fp32, unnormalised
   float* ws_ml;           // split partials: [slots, tile_rows, 2] (running max, sum)
+  uint64_t* trace;        // optional: [n_items, 6] per-item records (bf16 kernel), or null
 };
 
 // stages: depth of the HBM -> LDS ring (2, 3 or 4); 2 stages allow two

@@ -145,6 +145,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Optional per-item trace (a measurement aid): 100 MHz real-time stamps and the
+// hardware placement of the workgroup.  s_getreg reads HW_ID (CU, SE) and
+// XCC_ID; s_memrealtime reads the device's constant-rate clock.
+__device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+__device__ __forceinline__ uint32_t hw_place() {
+  const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_ID
+  const uint32_t xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20); // XCC_ID
+  return ((xcc & 15u) << 16) | ((hw >> 8) & 0xffffu);               // xcc | se/sh/cu bits
+}
+
 // Item position of logical workgroup w in a given pass of the boustrophedon
 // deal (same rule as ikbo::zigzag_position on the host).
 __device__ __forceinline__ int64_t deal_position(int64_t pass, int w, int grid) {
@@ -309,6 +319,8 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
     if (pos >= P.n_items) break;
     const WorkItem it = P.items[pos];
     const bool causal = it.kind == kKindSelf;
+    uint64_t t_start = 0, t_ready = 0, t_loop = 0;
+    if (P.trace) t_start = now_ticks();
 
     f32x16_t oacc[D / 32];
 #pragma unroll
@@ -369,6 +381,7 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
     // there (its wait here also covers the prologue copies just issued).
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) asm volatile("" ::"v"(qf[st]));
+    if (P.trace) t_ready = now_ticks();
     for (int t = 0; t < ntiles; ++t) {
       // Wait for this thread's copies of tile t: later tiles may stay in flight.
       const int after = min(NST - 2, ntiles - 1 - t);
@@ -394,6 +407,7 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
       }
     }
     __syncthreads();  // all stages free before the next item's copies
+    if (P.trace) t_loop = now_ticks();
 
     // ---- epilogue
     // Lane holds O^T rows d = mb*32 + (i/4)*8 + g*4 + i%4 of query row r_w.
@@ -427,6 +441,15 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
       }
     }
     wait_vmcnt<0>();  // epilogue stores retire before the next item's copies are counted
+    if (P.trace && tid == 0) {
+      uint64_t* tr = P.trace + pos * 6;
+      tr[0] = (static_cast<uint64_t>(w) << 32) | hw_place();
+      tr[1] = t_start;
+      tr[2] = t_ready;
+      tr[3] = t_loop;
+      tr[4] = now_ticks();
+      tr[5] = static_cast<uint64_t>(ntiles);
+    }
   }
 }
 

@@ -47,6 +47,8 @@ SIGNATURES = {
     "ikbo_plan_destroy": (None, [_P]),
     "ikbo_plan_info": (ctypes.c_int, [_P, _LP, _I]),
     "ikbo_plan_timing": (ctypes.c_int, [_P, _I]),
+    "ikbo_plan_trace": (ctypes.c_int, [_P, _I]),
+    "ikbo_plan_trace_read": (ctypes.c_int, [_P, _LP, _I, _IP]),
     "ikbo_plan_timing_read": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
                                              _I, _IP]),
 }
@@ -205,3 +207,15 @@ def ikbo_plan_timing_read(plan, max_n: int = 4096):
     n = ctypes.c_int32(0)
     _check(load_library().ikbo_plan_timing_read(plan, a, m, max_n, ctypes.byref(n)))
     return list(a[:n.value]), list(m[:n.value])
+
+
+def ikbo_plan_trace(plan, enable: bool) -> int:
+    return _check(load_library().ikbo_plan_trace(plan, 1 if enable else 0))
+
+
+def ikbo_plan_trace_read(plan, max_items: int = 1 << 20) -> np.ndarray:
+    """Per-item trace records of the last launch: int64 [n_items, 6]."""
+    buf = np.zeros((max(max_items, 1), 6), dtype=np.int64)
+    n = ctypes.c_int32(0)
+    _check(load_library().ikbo_plan_trace_read(plan, buf.ctypes.data_as(_LP), max_items, ctypes.byref(n)))
+    return buf[:n.value]

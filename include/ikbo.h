@@ -182,6 +182,18 @@ int ikbo_plan_timing(void* plan, int32_t enable);
 int ikbo_plan_timing_read(void* plan, float* attn_ms, float* merge_ms, int32_t max_n, int32_t* n);
 
 /*
+ * Per-item trace, for load-balance analysis (bf16 kernel).  With tracing on,
+ * each later launch of the plan writes one record of 6 int64 per work item, in
+ * the plan's item order: [0] logical workgroup << 32 | XCC << 16 | HW_ID
+ * CU/SE bits, [1] item start, [2] ring primed and query rows loaded, [3] key
+ * loop done, [4] item done (device real-time clock ticks, 100 MHz), [5] key
+ * tiles.  ikbo_plan_trace_read synchronises the device and copies the records
+ * of the last launch to the host.
+ */
+int ikbo_plan_trace(void* plan, int32_t enable);
+int ikbo_plan_trace_read(void* plan, int64_t* records, int32_t max_items, int32_t* n_items);
+
+/*
  * Introspection of a built plan (host values): number of work items, grid
  * size of the persistent launch, split groups, and the planned bytes of the
  * split-KV partial workspace.  For tests and measurement.

@@ -403,3 +403,25 @@ def test_plan_timing_records_each_launch():
         ikbo_plan_destroy(plan)
     assert len(attn) == 5 and len(merge) == 5
     assert all(a > 0 for a in attn) and all(m >= 0 for m in merge)
+
+
+def test_plan_trace_records_every_item():
+    from broadcast_free_target_amd import (ikbo_attn_fwd_planned, ikbo_plan_build, ikbo_plan_create,
+                                           ikbo_plan_destroy, ikbo_plan_info, ikbo_plan_trace, ikbo_plan_trace_read)
+    w = _wl("c2_typical")
+    dev = upload(w)
+    out = empty_out(w.raw("q_cand").shape, "bf16")
+    plan = ikbo_plan_create()
+    try:
+        ikbo_plan_build(plan, w.user_offsets, w.cand_to_user, w.n_users, w.n_cand, 1, w.H, w.d, 0, 0)
+        ikbo_plan_trace(plan, True)
+        ikbo_attn_fwd_planned(plan, dev["q_cand"], None, dev["k_user"], dev["v_user"], w.scale, out)
+        rec = ikbo_plan_trace_read(plan)
+        info = ikbo_plan_info(plan)
+    finally:
+        ikbo_plan_destroy(plan)
+    assert rec.shape == (info["n_items"], 6)
+    assert np.all(rec[:, 1] <= rec[:, 2]) and np.all(rec[:, 2] <= rec[:, 3]) and np.all(rec[:, 3] <= rec[:, 4])
+    assert np.all(rec[:, 5] >= 1)
+    assert len(np.unique(rec[:, 0] >> 32)) == info["grid"]
+    assert_close(to_f64(out), _oracle_target(w), "bf16", "traced launch")
