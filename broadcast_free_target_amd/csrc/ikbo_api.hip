@@ -123,6 +123,7 @@ struct Plan {
   bool built = false;
   int32_t n_users = 0, n_cand = 0, n_q = 1, H = 0, d = 0, dtype = IKBO_DTYPE_BF16, with_self = 0;
   int32_t stages = 2;  // bf16 kernel ring depth chosen at build time
+  int32_t waves = 8;   // bf16 kernel: 8 waves (two per SIMD) or the 4-wave variant
   int64_t total_len = 0;
   HostPlan hp;
   // device copies of the work list
@@ -181,9 +182,22 @@ int bf16_stages() {
   return (s == 2 || s == 3 || s == 4) ? s : ikbo::kBf16DefaultStages;
 }
 
+// Workgroup shape of the bf16 kernel (IKBO_WAVES overrides: 4 or 8).
+int bf16_waves() {
+  const int w = env_int("IKBO_WAVES", 8);
+  return (w == 4 || w == 8) ? w : 8;
+}
+
 PlanParams params_for(const Plan& p, int32_t dtype) {
   PlanParams pp;
-  if (dtype == IKBO_DTYPE_BF16) {
+  if (dtype == IKBO_DTYPE_BF16 && bf16_waves() == 8) {
+    // one resident 8-wave workgroup per CU; chunks are whole ring stages
+    pp.bm = ikbo::kBf16TileRows;
+    pp.bn = 2 * ikbo::kBf16TileKeys;
+    pp.grid_slots = std::max(1, p.n_cu);
+    pp.min_chunk = 256;
+    pp.allow_split = true;
+  } else if (dtype == IKBO_DTYPE_BF16) {
     pp.bm = ikbo::kBf16TileRows;
     pp.bn = ikbo::kBf16TileKeys;
     pp.grid_slots = std::max(1, p.n_cu * (bf16_stages() == 2 ? 2 : 1));
@@ -276,6 +290,7 @@ int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n
   p->dtype = dtype;
   p->with_self = with_self;
   p->stages = bf16_stages();
+  p->waves = bf16_waves();
   p->total_len = offs[n_users];
   p->built = true;
   return IKBO_OK;
@@ -353,8 +368,13 @@ int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* 
     p->timed_merge[p->n_timed] = p->hp.n_groups > 0;
     ++p->n_timed;
   }
-  hipError_t e = p->dtype == IKBO_DTYPE_BF16 ? ikbo::launch_attn_bf16(ap, p->d, p->stages, p->hp.grid, stream, te)
-                                             : ikbo::launch_attn_f32(ap, p->d, p->hp.grid, stream, te);
+  hipError_t e;
+  if (p->dtype != IKBO_DTYPE_BF16)
+    e = ikbo::launch_attn_f32(ap, p->d, p->hp.grid, stream, te);
+  else if (p->waves == 8)
+    e = ikbo::launch_attn_bf16_w8(ap, p->d, p->hp.grid, stream, te);
+  else
+    e = ikbo::launch_attn_bf16(ap, p->d, p->stages, p->hp.grid, stream, te);
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
   if (p->hp.n_groups > 0) {
     e = ikbo::launch_merge(ap, p->k_groups, p->hp.n_groups, p->d, stream, te ? te + 2 : nullptr);

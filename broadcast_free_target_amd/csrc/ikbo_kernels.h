@@ -40,6 +40,10 @@ struct AttnParams {
 // dispatch stamps at the kernel's start and end.
 hipError_t launch_attn_bf16(const AttnParams& p, int d, int stages, int grid, hipStream_t stream,
                             hipEvent_t* ev = nullptr);
+// Eight-wave variant (two waves per SIMD, key tiles alternating between the
+// two wave halves, one resident workgroup per CU).  Work items are the same;
+// key chunks should be multiples of 2 * kBf16TileKeys to keep both halves busy.
+hipError_t launch_attn_bf16_w8(const AttnParams& p, int d, int grid, hipStream_t stream, hipEvent_t* ev = nullptr);
 hipError_t launch_attn_f32(const AttnParams& p, int d, int grid, hipStream_t stream, hipEvent_t* ev = nullptr);
 // Merges the split-KV partials of n_groups groups into the bf16 outputs.
 hipError_t launch_merge(const AttnParams& p, const MergeItem* groups, int n_groups, int d, hipStream_t stream,

@@ -454,6 +454,243 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
 }
 
 // ---------------------------------------------------------------------------
+// bf16 MFMA kernel, two waves per SIMD: 8 wave64 = two key halves x 4 row blocks
+// ---------------------------------------------------------------------------
+//
+// Waves w and w + 4 own the same 32 rows (row block w % 4).  Each ring stage
+// holds two consecutive K/V tiles; wave half kh = w / 4 computes the tile
+// 2 s + kh of stage s, so the two waves on a SIMD alternate MFMA and softmax
+// work of different tiles.  After the key loop the halves exchange half of
+// their O columns through LDS and each merges the (O, m, l) of both halves for
+// the columns it owns (the split-softmax merge, AI-infra guide, section
+// 4.6.4), then writes them.
+
+template <int D>
+struct Step {
+  static constexpr int NCH = D / 8;                     // 16-byte chunks per row
+  static constexpr int tile = kBN * D;                  // elements of one K (or V) tile
+  static constexpr int stage = 4 * tile;                // K tile 0, K tile 1, V tile 0, V tile 1
+  static constexpr int threads = 512;
+  static constexpr int loads = 2 * kBN * NCH / threads; // 16-byte copies per thread per stage (K; V again)
+  static constexpr int nv = D / 2;                      // O values per lane
+  static constexpr int hv = nv / 2;                     // O values per lane one half owns
+  static_assert(loads >= 1 && loads * threads == 2 * kBN * NCH, "stage shape");
+};
+
+// Merge the partner half's (O, m, l) into this wave's own values v in
+// [V0, V0 + hv) and write them: the final bf16 rows, or the split partial.
+template <int D, int V0>
+__device__ __forceinline__ void finish_half(const AttnParams& P, const WorkItem& it, f32x16_t (&oacc)[D / 32],
+                                            float m_run, float l_run, const float* __restrict__ xo,
+                                            float pm, float pl, int64_t qrow, bool causal, int r_w, int lane,
+                                            bool write_ml) {
+  constexpr int HV = Step<D>::hv;
+  const int g = lane >> 5;
+  const float M = fmaxf(m_run, pm);
+  const float mu = (M == kNegInf) ? 0.0f : M;
+  const float fa = exp2_fast(m_run - mu), fb = exp2_fast(pm - mu);
+  const float L = l_run * fa + pl * fb;
+#pragma unroll
+  for (int j = 0; j < HV; ++j) {
+    const int v = V0 + j;
+    oacc[v / 16][v % 16] = oacc[v / 16][v % 16] * fa + xo[j * 64] * fb;
+  }
+  if (it.grp < 0) {
+    if (qrow >= 0) {
+      uint16_t* ob = static_cast<uint16_t*>(causal ? P.out_user : P.out_cand);
+      uint16_t* op = ob + (qrow * P.H + it.h) * D + g * 4;
+      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+#pragma unroll
+      for (int j = 0; j < HV; j += 4) {
+        const int v = V0 + j, mb = v / 16, i = v % 16;
+        *reinterpret_cast<u32x2_t*>(op + mb * 32 + (i / 4) * 8) =
+            pack4_bf16(oacc[mb][i] * inv, oacc[mb][i + 1] * inv, oacc[mb][i + 2] * inv, oacc[mb][i + 3] * inv);
+      }
+    }
+  } else if (r_w < it.nrows) {
+    const int64_t slot = static_cast<int64_t>(it.slot0) + it.chunk;
+    float* wo = P.ws_o + (slot * kBM + r_w) * D + g * 4;
+#pragma unroll
+    for (int j = 0; j < HV; j += 4) {
+      const int v = V0 + j, mb = v / 16, i = v % 16;
+      *reinterpret_cast<f32x4_t*>(wo + mb * 32 + (i / 4) * 8) =
+          f32x4_t{oacc[mb][i], oacc[mb][i + 1], oacc[mb][i + 2], oacc[mb][i + 3]};
+    }
+    if (write_ml) {
+      P.ws_ml[(slot * kBM + r_w) * 2 + 0] = M;
+      P.ws_ml[(slot * kBM + r_w) * 2 + 1] = L;
+    }
+  }
+}
+
+template <int D, int NST>
+__global__ __launch_bounds__(512, 1) void ikbo_attn_bf16_w8_kernel(AttnParams P) {
+  using S = Step<D>;
+  constexpr int NT = S::threads;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[NST * S::stage];
+  static_assert(NST * S::stage * 2 >= (8 * S::hv * 64 + 8 * 64 * 2) * 4, "exchange area fits in the ring");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31;
+  const int rb = wave & 3, kh = wave >> 2;
+  const int r_w = rb * 32 + n;  // this lane's row within the tile
+
+  const uint16_t* __restrict__ Kg = static_cast<const uint16_t*>(P.k);
+  const uint16_t* __restrict__ Vg = static_cast<const uint16_t*>(P.v);
+  const int64_t row_stride = static_cast<int64_t>(P.H) * D;
+
+  // Loader mapping: 16-byte unit u = tid + 512*r of a stage's K half lands at
+  // LDS unit u; it holds key row u / NCH (0..127: two tiles) and, swizzled,
+  // chunk u % NCH.  The V half mirrors it.
+  int ld_row[S::loads], ld_chunk[S::loads];
+#pragma unroll
+  for (int r = 0; r < S::loads; ++r) {
+    const int u = tid + NT * r;
+    ld_row[r] = u / S::NCH;
+    ld_chunk[r] = (u % S::NCH) ^ (swz(ld_row[r]) & (S::NCH - 1));
+  }
+
+  const uint32_t lds_base = lds_address(smem);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+  const int G = gridDim.x;
+  const int w = logical_wg();
+  for (int64_t pass = 0;; ++pass) {
+    const int64_t pos = deal_position(pass, w, G);
+    if (pos >= P.n_items) break;
+    const WorkItem it = P.items[pos];
+    const bool causal = it.kind == kKindSelf;
+    uint64_t t_start = 0, t_ready = 0, t_loop = 0;
+    if (P.trace) t_start = now_ticks();
+
+    f32x16_t oacc[D / 32];
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = f32x16_t{};
+    float m_run = kNegInf, l_run = 0.0f;
+
+    const int nkv = it.k1 - it.k0;
+    const int ntiles = (nkv + kBN - 1) / kBN;
+    const int nsteps = (ntiles + 1) / 2;
+    const uint16_t* kbase = Kg + (static_cast<int64_t>(it.kv_base) + it.k0) * row_stride + it.h * D;
+    const uint16_t* vbase = Vg + (static_cast<int64_t>(it.kv_base) + it.k0) * row_stride + it.h * D;
+
+    // Issue the HBM -> LDS copies of tiles 2s and 2s+1 into stage s % NST.
+    // Keys past the range load the last key again (in bounds, masked later).
+    auto issue = [&](int st_idx) {
+      const uint32_t st = lds_base + static_cast<uint32_t>((st_idx % NST) * S::stage * 2);
+#pragma unroll
+      for (int r = 0; r < S::loads; ++r) {
+        const int key = min(st_idx * 2 * kBN + ld_row[r], nkv - 1);
+        const int64_t off = key * row_stride + ld_chunk[r] * 8;
+        const uint32_t dk = st + static_cast<uint32_t>((NT * r + 64 * wave_u) * 16);
+        copy16_to_lds(kbase + off, dk);
+        copy16_to_lds(vbase + off, dk + static_cast<uint32_t>(2 * S::tile * 2));
+      }
+    };
+
+    const bool wave_has_rows = rb * 32 < it.nrows;
+    const int row_tok = it.row0 + r_w;
+    const int wave_last_tok = it.row0 + rb * 32 + 31;
+    const float c = P.scale_log2;
+
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s)
+      if (s < nsteps) issue(s);
+
+    int64_t qrow = -1;
+    if (r_w < it.nrows) {
+      const int r = it.row0 + r_w;
+      if (!causal) {
+        const int cand = P.cand_perm[it.row_base + r / P.n_q];
+        qrow = static_cast<int64_t>(cand) * P.n_q + r % P.n_q;
+      } else {
+        qrow = static_cast<int64_t>(it.row_base) + r;
+      }
+    }
+    u32x4_t qf[D / 16];
+    {
+      const int g = lane >> 5;
+      const uint16_t* qb = static_cast<const uint16_t*>(causal ? P.q_user : P.q_cand);
+      const uint16_t* qp = qb + (qrow < 0 ? 0 : (qrow * P.H + it.h) * D) + g * 8;
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st)
+        qf[st] = (qrow < 0) ? u32x4_t{0, 0, 0, 0} : *reinterpret_cast<const u32x4_t*>(qp + st * 16);
+    }
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) asm volatile("" ::"v"(qf[st]));
+    if (P.trace) t_ready = now_ticks();
+
+    for (int s = 0; s < nsteps; ++s) {
+      const int after = min(NST - 2, nsteps - 1 - s);
+      if (after <= 0) {
+        wait_vmcnt<0>();
+      } else if (after == 1) {
+        wait_vmcnt<2 * S::loads>();
+      } else {
+        wait_vmcnt<(NST >= 4 ? 2 : 1) * 2 * S::loads>();
+      }
+      __syncthreads();  // stage s is in LDS for every thread; stage (s-1) % NST is free
+      if (s + NST - 1 < nsteps) issue(s + NST - 1);
+      const int t = 2 * s + kh;
+      const int key_base = it.k0 + t * kBN;
+      const bool skip = t >= ntiles || !wave_has_rows || (causal && key_base > wave_last_tok);
+      if (!skip) {
+        const uint16_t* Ks = smem + (s % NST) * S::stage + kh * S::tile;
+        const uint16_t* Vs = smem + (s % NST) * S::stage + 2 * S::tile + kh * S::tile;
+        const bool need_mask = (key_base + kBN > it.k1) || (causal && key_base + kBN - 1 > it.row0 + rb * 32);
+        if (need_mask)
+          tile_step<D, true>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, lane);
+        else
+          tile_step<D, false>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, lane);
+      }
+    }
+    __syncthreads();  // every ring read is done: the ring becomes the exchange area
+    if (P.trace) t_loop = now_ticks();
+
+    // ---- exchange: half 0 keeps O values [0, hv), half 1 keeps [hv, nv).
+    // Each wave stores the values its partner keeps, lane-major (conflict free).
+    float* xbuf = reinterpret_cast<float*>(smem);
+    float* mlbuf = xbuf + 8 * S::hv * 64;
+    {
+      float* mine = xbuf + wave * S::hv * 64 + lane;
+      if (kh == 0) {
+#pragma unroll
+        for (int j = 0; j < S::hv; ++j) mine[j * 64] = oacc[(S::hv + j) / 16][(S::hv + j) % 16];
+      } else {
+#pragma unroll
+        for (int j = 0; j < S::hv; ++j) mine[j * 64] = oacc[j / 16][j % 16];
+      }
+      mlbuf[(wave * 64 + lane) * 2 + 0] = m_run;
+      mlbuf[(wave * 64 + lane) * 2 + 1] = l_run;
+    }
+    __syncthreads();
+    {
+      const int partner = wave ^ 4;
+      const float* xo = xbuf + partner * S::hv * 64 + lane;
+      const float pm = mlbuf[(partner * 64 + lane) * 2 + 0];
+      const float pl = mlbuf[(partner * 64 + lane) * 2 + 1];
+      const bool write_ml = kh == 0 && (lane >> 5) == 0;
+      if (kh == 0)
+        finish_half<D, 0>(P, it, oacc, m_run, l_run, xo, pm, pl, qrow, causal, r_w, lane, write_ml);
+      else
+        finish_half<D, S::hv>(P, it, oacc, m_run, l_run, xo, pm, pl, qrow, causal, r_w, lane, write_ml);
+    }
+    wait_vmcnt<0>();  // epilogue stores retire before the next item's copies are counted
+    __syncthreads();  // the exchange area is read before the next item's copies overwrite it
+    if (P.trace && tid == 0) {
+      uint64_t* tr = P.trace + pos * 6;
+      tr[0] = (static_cast<uint64_t>(w) << 32) | hw_place();
+      tr[1] = t_start;
+      tr[2] = t_ready;
+      tr[3] = t_loop;
+      tr[4] = now_ticks();
+      tr[5] = static_cast<uint64_t>(ntiles);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // split-KV merge: one workgroup per (group, 32-row block); thread -> (row, 16 d)
 // ---------------------------------------------------------------------------
 
@@ -672,6 +909,17 @@ hipError_t launch_attn_bf16(const AttnParams& p, int d, int stages, int grid, hi
     return hipErrorInvalidValue;
   }
 #undef IKBO_LAUNCH_BF16
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16_w8(const AttnParams& p, int d, int grid, hipStream_t stream, hipEvent_t* ev) {
+  if (grid <= 0 || p.n_items <= 0) return hipSuccess;
+  switch (d) {
+    case 128: IKBO_LAUNCH((ikbo_attn_bf16_w8_kernel<128, 2>), dim3(grid), dim3(512), p); break;
+    case 64: IKBO_LAUNCH((ikbo_attn_bf16_w8_kernel<64, 2>), dim3(grid), dim3(512), p); break;
+    case 32: IKBO_LAUNCH((ikbo_attn_bf16_w8_kernel<32, 2>), dim3(grid), dim3(512), p); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -35,7 +35,8 @@ def _oracle_target(w):
 
 @pytest.fixture(autouse=True)
 def _clean_env():
-    saved = {k: os.environ.get(k) for k in ("IKBO_GRID_WGS", "IKBO_MIN_CHUNK", "IKBO_NO_SPLIT", "IKBO_SPLIT_SLOTS")}
+    saved = {k: os.environ.get(k) for k in ("IKBO_GRID_WGS", "IKBO_MIN_CHUNK", "IKBO_NO_SPLIT", "IKBO_SPLIT_SLOTS",
+                                            "IKBO_WAVES")}
     yield
     for k, v in saved.items():
         if v is None:
@@ -66,11 +67,13 @@ def test_c1_tiny_f32():
     assert_close(to_f64(out2), ref, "f32", "c1 ex")
 
 
-def test_c2_typical_planned_and_north_star_call():
+@pytest.mark.parametrize("waves", ["8", "4"])
+def test_c2_typical_planned_and_north_star_call(waves):
     from broadcast_free_target_amd import ikbo_attn_fwd
     import torch
+    os.environ["IKBO_WAVES"] = waves
     w = _wl("c2_typical")
-    say("case c2 planned")
+    say(f"case c2 planned waves={waves}")
     dev = upload(w)
     ref = _oracle_target(w)
     out = empty_out(w.raw("q_cand").shape, "bf16")
@@ -86,9 +89,11 @@ def test_c2_typical_planned_and_north_star_call():
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
-def test_c3_skewed_with_single_key_users():
+@pytest.mark.parametrize("waves", ["8", "4"])
+def test_c3_skewed_with_single_key_users(waves):
+    os.environ["IKBO_WAVES"] = waves
     w = _wl("c3_skewed")
-    say("case c3 planned")
+    say(f"case c3 planned waves={waves}")
     dev = upload(w)
     ref = _oracle_target(w)
     out = empty_out(w.raw("q_cand").shape, "bf16")
@@ -194,15 +199,19 @@ def _custom(i, lengths, counts, n_q, H, d, dtype, with_self=False):
 
 @pytest.mark.parametrize("i", range(len(EDGE)))
 @pytest.mark.parametrize("split", ["default", "forced", "off"])
-def test_edge_matrix(i, split):
+@pytest.mark.parametrize("waves", ["8", "4"])
+def test_edge_matrix(i, split, waves):
     lengths, counts, n_q, H, d, dtype = EDGE[i]
+    if dtype != "bf16" and waves != "8":
+        pytest.skip("the workgroup shape applies to the bf16 kernel only")
+    os.environ["IKBO_WAVES"] = waves
     if split == "forced":
         os.environ["IKBO_MIN_CHUNK"] = "64"
         os.environ["IKBO_SPLIT_SLOTS"] = "4096"
     elif split == "off":
         os.environ["IKBO_NO_SPLIT"] = "1"
     w = _custom(i, lengths, counts, n_q, H, d, dtype)
-    say(f"case edge{i} split={split} L={lengths} counts={counts} n_q={n_q} H={H} d={d} {dtype}")
+    say(f"case edge{i} split={split} waves={waves} L={lengths} counts={counts} n_q={n_q} H={H} d={d} {dtype}")
     dev = upload(w)
     out = empty_out(w.raw("q_cand").shape, dtype)
     run_planned(w, dev, out)
@@ -215,16 +224,18 @@ def test_edge_matrix(i, split):
             assert np.all(got[c] == 0)
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 32)])
+@pytest.mark.parametrize("dtype,d,waves", [("bf16", 128, "8"), ("bf16", 64, "8"), ("bf16", 128, "4"),
+                                          ("bf16", 32, "4"), ("f32", 32, "8")])
 @pytest.mark.parametrize("split", ["default", "forced"])
-def test_edge_fused(dtype, d, split):
+def test_edge_fused(dtype, d, waves, split):
     from broadcast_free_target_amd import ikbo_self_target_fwd
     import torch
+    os.environ["IKBO_WAVES"] = waves
     if split == "forced":
         os.environ["IKBO_MIN_CHUNK"] = "64"
         os.environ["IKBO_SPLIT_SLOTS"] = "4096"
     w = _custom(50 + d, (1, 130, 64, 257, 0), (2, 3, 0, 1, 1), 1, 2, d, dtype, with_self=True)
-    say(f"case fused-edge {dtype} d={d} split={split}")
+    say(f"case fused-edge {dtype} d={d} waves={waves} split={split}")
     dev = upload(w)
     out_c = empty_out(w.raw("q_cand").shape, dtype)
     out_u = empty_out(w.raw("q_user").shape, dtype)
@@ -260,11 +271,13 @@ def test_p6_permutation_bitwise():
 
 
 @pytest.mark.parametrize("name", ["c2_typical", "c3_skewed"])
-def test_p13_determinism_across_runs_and_grids(name):
+@pytest.mark.parametrize("waves", ["8", "4"])
+def test_p13_determinism_across_runs_and_grids(name, waves):
     import torch
+    os.environ["IKBO_WAVES"] = waves
     w = _wl(name)
     dev = upload(w)
-    say(f"case P13 {name}")
+    say(f"case P13 {name} waves={waves}")
     ref = empty_out(w.raw("q_cand").shape, "bf16")
     run_planned(w, dev, ref)
     for grid in (None, "None", "8", "37", "1"):
