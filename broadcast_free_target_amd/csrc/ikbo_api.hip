@@ -127,7 +127,7 @@ struct Plan {
   int64_t total_len = 0;
   HostPlan hp;
   // device copies of the work list
-  DevBuf d_items, d_ws_o, d_ws_ml;  // d_items: device copy of the plan buffer (copy mode)
+  DevBuf d_items, d_ws_o, d_ws_rec;  // d_items: device copy of the plan buffer (copy mode)
   // Two pinned plan buffers, used alternately by successive builds.  With
   // in-place reads (the default) the kernels read the work list from them;
   // otherwise they stage a copy to the device buffers above.  Each is guarded
@@ -140,7 +140,6 @@ struct Plan {
   int cur_stage = 0;
   const WorkItem* k_items = nullptr;            // what the kernels read
   const int32_t* k_perm = nullptr;
-  const ikbo::MergeItem* k_groups = nullptr;
   // optional kernel timing (measurement)
   bool timing = false;
   bool tracing = false;
@@ -160,7 +159,7 @@ struct Plan {
     d2h.release();
     d_items.release();
     d_ws_o.release();
-    d_ws_ml.release();
+    d_ws_rec.release();
     d_trace.release();
   }
 };
@@ -241,16 +240,19 @@ int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n
   // completes the plan cannot be launched.
   p->built = false;
   HostPlan& hp = p->hp;
-  rc = ikbo::build_plan(offs, c2u, n_users, n_cand, n_q, H, with_self != 0, params_for(*p, dtype), &hp, &err);
+  PlanParams pp = params_for(*p, dtype);
+  // Split partials name their output row as row * H + h in an int32.
+  const int64_t out_units = std::max<int64_t>(static_cast<int64_t>(n_cand) * n_q, with_self ? offs[n_users] : 0) * H;
+  if (out_units >= std::numeric_limits<int32_t>::max()) pp.allow_split = false;
+  rc = ikbo::build_plan(offs, c2u, n_users, n_cand, n_q, H, with_self != 0, pp, &hp, &err);
   if (rc != ikbo::kOk) return fail(rc, err);
 
   const int tile_rows = dtype == IKBO_DTYPE_BF16 ? ikbo::kBf16TileRows : ikbo::kF32TileRows;
   const size_t items_bytes = hp.items.size() * sizeof(WorkItem);
   const size_t perm_bytes = hp.cand_perm.size() * sizeof(int32_t);
-  const size_t groups_bytes = hp.groups.size() * sizeof(ikbo::MergeItem);
   if ((rc = p->d_ws_o.ensure(static_cast<size_t>(hp.n_slots) * tile_rows * d * sizeof(float), false)) != IKBO_OK)
     return rc;
-  if ((rc = p->d_ws_ml.ensure(static_cast<size_t>(hp.n_slots) * tile_rows * 2 * sizeof(float), false)) != IKBO_OK)
+  if ((rc = p->d_ws_rec.ensure(static_cast<size_t>(hp.n_slots) * tile_rows * 4 * sizeof(float), false)) != IKBO_OK)
     return rc;
 
   // Write the work list into the pinned buffer whose last reader has finished.
@@ -258,27 +260,24 @@ int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n
   p->next_stage ^= 1;
   if (p->stage_used[s]) IKBO_HIP(hipEventSynchronize(p->stage_ev[s]));
   const size_t a0 = 0, a1 = (items_bytes + 255) & ~size_t(255), a2 = a1 + ((perm_bytes + 255) & ~size_t(255));
-  if ((rc = p->stage[s].ensure(a2 + groups_bytes + 256)) != IKBO_OK) return rc;
+  if ((rc = p->stage[s].ensure(a2 + 256)) != IKBO_OK) return rc;
   char* hb = static_cast<char*>(p->stage[s].ptr);
   if (items_bytes) std::memcpy(hb + a0, hp.items.data(), items_bytes);
   if (perm_bytes) std::memcpy(hb + a1, hp.cand_perm.data(), perm_bytes);
-  if (groups_bytes) std::memcpy(hb + a2, hp.groups.data(), groups_bytes);
   if (p->read_in_place) {
     void* dev = nullptr;
     IKBO_HIP(hipHostGetDevicePointer(&dev, hb, 0));
     char* db = static_cast<char*>(dev);
     p->k_items = reinterpret_cast<const WorkItem*>(db + a0);
     p->k_perm = reinterpret_cast<const int32_t*>(db + a1);
-    p->k_groups = reinterpret_cast<const ikbo::MergeItem*>(db + a2);
   } else {
-    if ((rc = p->d_items.ensure(a2 + groups_bytes + 256, false)) != IKBO_OK) return rc;
-    IKBO_HIP(hipMemcpyAsync(p->d_items.ptr, hb, a2 + groups_bytes, hipMemcpyHostToDevice, stream));
+    if ((rc = p->d_items.ensure(a2 + 256, false)) != IKBO_OK) return rc;
+    IKBO_HIP(hipMemcpyAsync(p->d_items.ptr, hb, a2, hipMemcpyHostToDevice, stream));
     IKBO_HIP(hipEventRecord(p->stage_ev[s], stream));
     p->stage_used[s] = true;
     char* db = static_cast<char*>(p->d_items.ptr);
     p->k_items = reinterpret_cast<const WorkItem*>(db + a0);
     p->k_perm = reinterpret_cast<const int32_t*>(db + a1);
-    p->k_groups = reinterpret_cast<const ikbo::MergeItem*>(db + a2);
   }
   p->cur_stage = s;
 
@@ -349,7 +348,7 @@ int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* 
   ap.n_q = p->n_q;
   ap.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   ap.ws_o = static_cast<float*>(p->d_ws_o.ptr);
-  ap.ws_ml = static_cast<float*>(p->d_ws_ml.ptr);
+  ap.ws_rec = static_cast<float*>(p->d_ws_rec.ptr);
   ap.trace = nullptr;
   if (p->tracing && p->dtype == IKBO_DTYPE_BF16) {
     int rc = p->d_trace.ensure(p->hp.items.size() * 6 * sizeof(uint64_t), false);
@@ -377,7 +376,7 @@ int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* 
     e = ikbo::launch_attn_bf16(ap, p->d, p->stages, p->hp.grid, stream, te);
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
   if (p->hp.n_groups > 0) {
-    e = ikbo::launch_merge(ap, p->k_groups, p->hp.n_groups, p->d, stream, te ? te + 2 : nullptr);
+    e = ikbo::launch_merge(ap, p->hp.n_groups, p->d, stream, te ? te + 2 : nullptr);
     if (e != hipSuccess) return fail_hip(e, "merge launch");
   }
   if (p->read_in_place) {

@@ -31,7 +31,9 @@ struct AttnParams {
   int32_t n_q;
   float scale_log2;       // scale * log2(e): scores are kept in base 2
   float* ws_o;            // split partials: [slots, tile_rows, d] fp32, unnormalised
-  float* ws_ml;           // split partials: [slots, tile_rows, 2] (running max, sum)
+  float* ws_rec;          // split partials: [slots, tile_rows, 4] row records: running max m,
+                          // running sum l, output unit (row * H + h, -1: no row) and
+                          // nchunk | kind << 16, the last two as int32 bits
   uint64_t* trace;        // optional: [n_items, 6] per-item records (bf16 kernel), or null
 };
 
@@ -45,9 +47,8 @@ hipError_t launch_attn_bf16(const AttnParams& p, int d, int stages, int grid, hi
 // key chunks should be multiples of 2 * kBf16TileKeys to keep both halves busy.
 hipError_t launch_attn_bf16_w8(const AttnParams& p, int d, int grid, hipStream_t stream, hipEvent_t* ev = nullptr);
 hipError_t launch_attn_f32(const AttnParams& p, int d, int grid, hipStream_t stream, hipEvent_t* ev = nullptr);
-// Merges the split-KV partials of n_groups groups into the bf16 outputs.
-hipError_t launch_merge(const AttnParams& p, const MergeItem* groups, int n_groups, int d, hipStream_t stream,
-                        hipEvent_t* ev = nullptr);
+// Merges the split-KV partials of groups 0 .. n_groups-1 into the bf16 outputs.
+hipError_t launch_merge(const AttnParams& p, int n_groups, int d, hipStream_t stream, hipEvent_t* ev = nullptr);
 
 // Materialised broadcast: for each of n local candidates, copy `len[c]` rows of
 // `row_bytes` bytes from k/v at src_row[c] to kb/vb at dst_row[c].

@@ -96,6 +96,13 @@ __device__ __forceinline__ u32x2_t pack4_bf16(float a, float b, float c, float d
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Row record of a split partial: m, l, output unit (-1 when the tile row is
+// empty) and nchunk | kind << 16.
+__device__ __forceinline__ f32x4_t split_record(float m, float l, int64_t qrow, const WorkItem& it, int H) {
+  const int unit = qrow < 0 ? -1 : static_cast<int>(qrow * H + it.h);
+  return f32x4_t{m, l, __builtin_bit_cast(float, unit), __builtin_bit_cast(float, it.nchunk | (it.kind << 16))};
+}
+
 // {x[l], x[l ^ 32]} for every lane l, via v_permlane32_swap: with both
 // operands holding x, the first comes back with the lower half's values in
 // both halves and the second with the upper half's, so a symmetric op of the
@@ -434,11 +441,9 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
           for (int i4 = 0; i4 < 4; ++i4)
             *reinterpret_cast<f32x4_t*>(wo + mb * 32 + i4 * 8) =
                 f32x4_t{oacc[mb][i4 * 4 + 0], oacc[mb][i4 * 4 + 1], oacc[mb][i4 * 4 + 2], oacc[mb][i4 * 4 + 3]};
-        if (g == 0) {
-          P.ws_ml[(slot * kBM + r_w) * 2 + 0] = m_run;
-          P.ws_ml[(slot * kBM + r_w) * 2 + 1] = l_run;
-        }
       }
+      if (g == 0)  // every tile row gets a record; empty rows are marked
+        *reinterpret_cast<f32x4_t*>(P.ws_rec + (slot * kBM + r_w) * 4) = split_record(m_run, l_run, qrow, it, P.H);
     }
     wait_vmcnt<0>();  // epilogue stores retire before the next item's copies are counted
     if (P.trace && tid == 0) {
@@ -478,12 +483,13 @@ struct Step {
 };
 
 // Merge the partner half's (O, m, l) into this wave's own values v in
-// [V0, V0 + hv) and write them: the final bf16 rows, or the split partial.
+// [V0, V0 + hv) and write them: the final bf16 rows, or the split partial
+// (write_rec: this lane also writes the row's record).
 template <int D, int V0>
 __device__ __forceinline__ void finish_half(const AttnParams& P, const WorkItem& it, f32x16_t (&oacc)[D / 32],
                                             float m_run, float l_run, const float* __restrict__ xo,
                                             float pm, float pl, int64_t qrow, bool causal, int r_w, int lane,
-                                            bool write_ml) {
+                                            bool write_rec) {
   constexpr int HV = Step<D>::hv;
   const int g = lane >> 5;
   const float M = fmaxf(m_run, pm);
@@ -507,19 +513,19 @@ __device__ __forceinline__ void finish_half(const AttnParams& P, const WorkItem&
             pack4_bf16(oacc[mb][i] * inv, oacc[mb][i + 1] * inv, oacc[mb][i + 2] * inv, oacc[mb][i + 3] * inv);
       }
     }
-  } else if (r_w < it.nrows) {
+  } else {
     const int64_t slot = static_cast<int64_t>(it.slot0) + it.chunk;
-    float* wo = P.ws_o + (slot * kBM + r_w) * D + g * 4;
+    if (r_w < it.nrows) {
+      float* wo = P.ws_o + (slot * kBM + r_w) * D + g * 4;
 #pragma unroll
-    for (int j = 0; j < HV; j += 4) {
-      const int v = V0 + j, mb = v / 16, i = v % 16;
-      *reinterpret_cast<f32x4_t*>(wo + mb * 32 + (i / 4) * 8) =
-          f32x4_t{oacc[mb][i], oacc[mb][i + 1], oacc[mb][i + 2], oacc[mb][i + 3]};
+      for (int j = 0; j < HV; j += 4) {
+        const int v = V0 + j, mb = v / 16, i = v % 16;
+        *reinterpret_cast<f32x4_t*>(wo + mb * 32 + (i / 4) * 8) =
+            f32x4_t{oacc[mb][i], oacc[mb][i + 1], oacc[mb][i + 2], oacc[mb][i + 3]};
+      }
     }
-    if (write_ml) {
-      P.ws_ml[(slot * kBM + r_w) * 2 + 0] = M;
-      P.ws_ml[(slot * kBM + r_w) * 2 + 1] = L;
-    }
+    if (write_rec)  // every tile row gets a record; empty rows are marked
+      *reinterpret_cast<f32x4_t*>(P.ws_rec + (slot * kBM + r_w) * 4) = split_record(M, L, qrow, it, P.H);
   }
 }
 
@@ -670,11 +676,11 @@ __global__ __launch_bounds__(512, 1) void ikbo_attn_bf16_w8_kernel(AttnParams P)
       const float* xo = xbuf + partner * S::hv * 64 + lane;
       const float pm = mlbuf[(partner * 64 + lane) * 2 + 0];
       const float pl = mlbuf[(partner * 64 + lane) * 2 + 1];
-      const bool write_ml = kh == 0 && (lane >> 5) == 0;
+      const bool write_rec = kh == 0 && (lane >> 5) == 0;
       if (kh == 0)
-        finish_half<D, 0>(P, it, oacc, m_run, l_run, xo, pm, pl, qrow, causal, r_w, lane, write_ml);
+        finish_half<D, 0>(P, it, oacc, m_run, l_run, xo, pm, pl, qrow, causal, r_w, lane, write_rec);
       else
-        finish_half<D, S::hv>(P, it, oacc, m_run, l_run, xo, pm, pl, qrow, causal, r_w, lane, write_ml);
+        finish_half<D, S::hv>(P, it, oacc, m_run, l_run, xo, pm, pl, qrow, causal, r_w, lane, write_rec);
     }
     wait_vmcnt<0>();  // epilogue stores retire before the next item's copies are counted
     __syncthreads();  // the exchange area is read before the next item's copies overwrite it
@@ -691,63 +697,54 @@ __global__ __launch_bounds__(512, 1) void ikbo_attn_bf16_w8_kernel(AttnParams P)
 }
 
 // ---------------------------------------------------------------------------
-// split-KV merge: one workgroup per (group, 32-row block); thread -> (row, 16 d)
+// split-KV merge: block (group, row block); thread -> (row, 4 d)
 // ---------------------------------------------------------------------------
+//
+// Everything the merge needs comes from the partials' row records: the chunk
+// count, the output row and the kind.  A thread loads the records of all
+// kMaxSplit slots of its group at once (slots past nchunk hold stale records
+// and are ignored), then one 16-byte slice of O per chunk, and folds the
+// chunks in chunk order.
 
 template <int D>
-__global__ __launch_bounds__(256) void ikbo_merge_kernel(AttnParams P, const MergeItem* __restrict__ groups) {
-  constexpr int DPT = 16;          // d values per thread
-  constexpr int TPR = D / DPT;     // threads per row
-  constexpr int RPB = 256 / TPR;   // rows per block
-  constexpr int CB = 4;            // chunks loaded together
-  const MergeItem gi = groups[blockIdx.x];
+__global__ __launch_bounds__(256) void ikbo_merge_kernel(AttnParams P) {
+  constexpr int TPR = D / 4;      // threads per row
+  constexpr int RPB = 256 / TPR;  // rows per block
   const int r = blockIdx.y * RPB + threadIdx.x / TPR;
-  if (r >= gi.nrows) return;
-  const int d0 = (threadIdx.x % TPR) * DPT;
+  const int d0 = (threadIdx.x % TPR) * 4;
+  const int64_t slot0 = static_cast<int64_t>(blockIdx.x) * kMaxSplit;
+  f32x4_t rec[kMaxSplit];
+#pragma unroll
+  for (int ch = 0; ch < kMaxSplit; ++ch)
+    rec[ch] = *reinterpret_cast<const f32x4_t*>(P.ws_rec + ((slot0 + ch) * kBM + r) * 4);
+  // The fields are copied out of the vector before the bit cast: clang reads a
+  // bit cast of a vector element as a cast of element 0.
+  const float unit_f = rec[0][2], tag_f = rec[0][3];
+  const int unit = __builtin_bit_cast(int, unit_f);
+  const int tag = __builtin_bit_cast(int, tag_f);
+  const int nchunk = tag & 0xffff;
+  if (unit < 0) return;  // no row here
+  f32x4_t o[kMaxSplit];
+#pragma unroll
+  for (int ch = 0; ch < kMaxSplit; ++ch)
+    if (ch < nchunk) o[ch] = *reinterpret_cast<const f32x4_t*>(P.ws_o + ((slot0 + ch) * kBM + r) * D + d0);
   float M = kNegInf, L = 0.0f;
-  f32x4_t acc[DPT / 4];
+  f32x4_t acc = f32x4_t{0, 0, 0, 0};
 #pragma unroll
-  for (int q = 0; q < DPT / 4; ++q) acc[q] = f32x4_t{0, 0, 0, 0};
-  for (int c0 = 0; c0 < gi.nchunk; c0 += CB) {
-    // Issue the loads of CB chunks first, then fold them in chunk order (deterministic).
-    float mc[CB], lc[CB];
-    f32x4_t o[CB][DPT / 4];
-#pragma unroll
-    for (int k = 0; k < CB; ++k) {
-      const int ch = min(c0 + k, gi.nchunk - 1);
-      const int64_t row = (static_cast<int64_t>(gi.slot0) + ch) * kBM + r;
-      mc[k] = P.ws_ml[row * 2 + 0];
-      lc[k] = P.ws_ml[row * 2 + 1];
-#pragma unroll
-      for (int q = 0; q < DPT / 4; ++q) o[k][q] = *reinterpret_cast<const f32x4_t*>(P.ws_o + row * D + d0 + 4 * q);
-    }
-#pragma unroll
-    for (int k = 0; k < CB; ++k) {
-      if (c0 + k >= gi.nchunk) break;
-      const float Mn = fmaxf(M, mc[k]);
-      const float mu = (Mn == kNegInf) ? 0.0f : Mn;
-      const float a = exp2_fast(M - mu), b = exp2_fast(mc[k] - mu);
-      L = L * a + lc[k] * b;
-#pragma unroll
-      for (int q = 0; q < DPT / 4; ++q) acc[q] = acc[q] * a + o[k][q] * b;
-      M = Mn;
-    }
+  for (int ch = 0; ch < kMaxSplit; ++ch) {
+    if (ch >= nchunk) break;
+    const float mc = rec[ch][0], lc = rec[ch][1];
+    const float Mn = fmaxf(M, mc);
+    const float mu = (Mn == kNegInf) ? 0.0f : Mn;
+    const float a = exp2_fast(M - mu), b = exp2_fast(mc - mu);
+    L = L * a + lc * b;
+    acc = acc * a + o[ch] * b;
+    M = Mn;
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  const int rr = gi.row0 + r;
-  int64_t orow;
-  if (gi.kind != kKindSelf) {
-    const int cand = P.cand_perm[gi.row_base + rr / P.n_q];
-    orow = static_cast<int64_t>(cand) * P.n_q + rr % P.n_q;
-  } else {
-    orow = static_cast<int64_t>(gi.row_base) + rr;
-  }
-  uint16_t* ob = static_cast<uint16_t*>(gi.kind == kKindSelf ? P.out_user : P.out_cand);
-  uint16_t* op = ob + (orow * P.H + gi.h) * D + d0;
-#pragma unroll
-  for (int q = 0; q < DPT / 4; ++q)
-    *reinterpret_cast<u32x2_t*>(op + 4 * q) =
-        pack4_bf16(acc[q][0] * inv, acc[q][1] * inv, acc[q][2] * inv, acc[q][3] * inv);
+  uint16_t* ob = static_cast<uint16_t*>((tag >> 16) == kKindSelf ? P.out_user : P.out_cand);
+  *reinterpret_cast<u32x2_t*>(ob + static_cast<int64_t>(unit) * D + d0) =
+      pack4_bf16(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -923,15 +920,13 @@ hipError_t launch_attn_bf16_w8(const AttnParams& p, int d, int grid, hipStream_t
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const AttnParams& p, const MergeItem* groups, int n_groups, int d, hipStream_t stream,
-                        hipEvent_t* ev) {
+hipError_t launch_merge(const AttnParams& p, int n_groups, int d, hipStream_t stream, hipEvent_t* ev) {
   if (n_groups <= 0) return hipSuccess;
-  const int rpb = 256 / (d / 16);
-  const dim3 grid(n_groups, (kBM + rpb - 1) / rpb);
+  const dim3 grid(n_groups, kBM / (256 / (d / 4)));
   switch (d) {
-    case 128: IKBO_LAUNCH(ikbo_merge_kernel<128>, grid, dim3(256), p, groups); break;
-    case 64: IKBO_LAUNCH(ikbo_merge_kernel<64>, grid, dim3(256), p, groups); break;
-    case 32: IKBO_LAUNCH(ikbo_merge_kernel<32>, grid, dim3(256), p, groups); break;
+    case 128: IKBO_LAUNCH(ikbo_merge_kernel<128>, grid, dim3(256), p); break;
+    case 64: IKBO_LAUNCH(ikbo_merge_kernel<64>, grid, dim3(256), p); break;
+    case 32: IKBO_LAUNCH(ikbo_merge_kernel<32>, grid, dim3(256), p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

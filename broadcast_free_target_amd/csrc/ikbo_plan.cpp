@@ -91,7 +91,8 @@ int group_csr(const int32_t* cand_to_user, int32_t n_cand, int32_t n_users, int3
 int build_plan(const int32_t* user_offsets, const int32_t* cand_to_user, int32_t n_users,
                int32_t n_cand, int32_t n_q, int32_t H, bool with_self, const PlanParams& p,
                HostPlan* out, std::string* err) {
-  if (H < 1 || n_q < 1 || n_cand < 0 || p.bm < 1 || p.bn < 1 || p.grid_slots < 1) {
+  if (H < 1 || n_q < 1 || n_cand < 0 || p.bm < 1 || p.bn < 1 || p.grid_slots < 1 || p.max_chunks < 1 ||
+      p.max_chunks > kMaxSplit) {
     set_err(err, "invalid sizes (H, n_q >= 1, n_cand >= 0 required)");
     return kErrInvalidArg;
   }
@@ -148,8 +149,8 @@ int build_plan(const int32_t* user_offsets, const int32_t* cand_to_user, int32_t
       return;
     }
     const int32_t g = out->n_groups++;
-    const int32_t slot0 = out->n_slots;
-    out->n_slots += static_cast<int32_t>(nchunk);
+    const int32_t slot0 = g * kMaxSplit;
+    out->n_slots = out->n_groups * kMaxSplit;
     out->groups.push_back(MergeItem{it.row_base, it.row0, it.nrows, it.h, it.kind, slot0,
                                     static_cast<int32_t>(nchunk), 0});
     const int32_t k0 = it.k0, k1 = it.k1;

@@ -37,12 +37,16 @@ static_assert(sizeof(WorkItem) == 48, "WorkItem layout is shared with the kernel
 
 enum : int32_t { kKindTarget = 0, kKindSelf = 1 };
 
-// One split group (a row tile whose key range was cut into chunks), for the
-// merge kernel.  The layout is read by the device code.
+// Most key chunks one row tile is split into.  Group g owns the partial-result
+// slots [g * kMaxSplit, g * kMaxSplit + nchunk), so the merge kernel finds a
+// group's slots from its index alone.
+constexpr int32_t kMaxSplit = 8;
+
+// One split group (a row tile whose key range was cut into chunks).  Host-side
+// description only: the kernels find everything in the partials' row records.
 struct MergeItem {
   int32_t row_base, row0, nrows, h, kind, slot0, nchunk, pad;
 };
-static_assert(sizeof(MergeItem) == 32, "MergeItem layout is shared with the kernels");
 
 struct PlanParams {
   int32_t bm = 128;           // rows per tile (one workgroup)
@@ -51,7 +55,7 @@ struct PlanParams {
   int32_t launch_grid = 0;    // workgroups actually launched (0: grid_slots); never
                               // changes the work list, so results do not depend on it
   int32_t min_chunk = 256;    // shortest key chunk a split may produce
-  int32_t max_chunks = 8;     // most chunks one key range is cut into
+  int32_t max_chunks = kMaxSplit;  // most chunks one key range is cut into (<= kMaxSplit)
   int32_t overhead = 128;     // fixed cost of an item, in key units
   bool allow_split = true;    // split long key ranges (log-sum-exp merge)
 };
@@ -62,8 +66,8 @@ struct HostPlan {
   std::vector<int32_t> cand_perm;     // [n_cand]
   std::vector<WorkItem> items;        // execution order
   std::vector<MergeItem> groups;      // [n_groups], split groups in group order
-  int32_t n_groups = 0;               // split groups (one counter each)
-  int32_t n_slots = 0;                // partial-result slots
+  int32_t n_groups = 0;               // split groups
+  int32_t n_slots = 0;                // partial-result slots (n_groups * kMaxSplit)
   int32_t grid = 0;                   // workgroups to launch
   int64_t n_target_tiles = 0;
   int64_t n_self_tiles = 0;

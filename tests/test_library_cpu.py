@@ -168,16 +168,16 @@ def _check_plan(plan, offs, c2u, n_q, H, with_self, bm, bn, grid_slots):
             assert all(a + n == b for (a, n), (b, _) in zip(t[:-1], t[1:])) and (not t or t[0][0] == 0)
             s = sorted(rows.get((1, u, hh), []))
             assert sum(n for _, n in s) == (L[u] if with_self else 0)
-    # one disjoint slot range per split group
+    # split group g owns slots [8 g, 8 g + nchunk): disjoint, found from g alone
     groups = {}
     for it in items:
         if it[8] >= 0:
             groups.setdefault(int(it[8]), set()).add((int(it[11]), int(it[10])))
     assert all(len(v) == 1 for v in groups.values())
-    spans = sorted(next(iter(v)) for v in groups.values())
-    assert sum(nc for _, nc in spans) == plan["n_slots"] and len(groups) == plan["n_groups"]
-    for (s0, nc), (s1, _) in zip(spans[:-1], spans[1:]):
-        assert s0 + nc <= s1
+    assert sorted(groups) == list(range(plan["n_groups"])) and plan["n_slots"] == 8 * plan["n_groups"]
+    for g, v in groups.items():
+        s0, nc = next(iter(v))
+        assert s0 == 8 * g and 2 <= nc <= 8
     # longest first
     cost = items[:, 5] - items[:, 4]
     assert np.all(np.diff(cost) <= 0)
