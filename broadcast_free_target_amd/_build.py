@@ -27,7 +27,7 @@ ARCH = os.environ.get("IKBO_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 VALU forms are disabled for all device code.
 HIP_FLAGS = [
-    "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
+    "-O3", "-std=c++20", f"--offload-arch={ARCH}", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
 ]

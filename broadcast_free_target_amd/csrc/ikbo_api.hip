@@ -123,7 +123,7 @@ struct Plan {
   bool built = false;
   int32_t n_users = 0, n_cand = 0, n_q = 1, H = 0, d = 0, dtype = IKBO_DTYPE_BF16, with_self = 0;
   int32_t stages = 2;  // bf16 kernel ring depth chosen at build time
-  int32_t waves = 8;   // bf16 kernel: 8 waves (two per SIMD) or the 4-wave variant
+  int32_t variant = 0;  // bf16 kernel: kVariantPipe, kVariantW8 or kVariantW4
   int64_t total_len = 0;
   HostPlan hp;
   // device copies of the work list
@@ -181,18 +181,24 @@ int bf16_stages() {
   return (s == 2 || s == 3 || s == 4) ? s : ikbo::kBf16DefaultStages;
 }
 
-// Workgroup shape of the bf16 kernel (IKBO_WAVES overrides: 4 or 8).
-int bf16_waves() {
-  const int w = env_int("IKBO_WAVES", 8);
-  return (w == 4 || w == 8) ? w : 8;
+// bf16 kernel variant: the eight-wave kernel (default), the plain 4-wave
+// kernel (two resident per CU) or the software-pipelined 4-wave kernel
+// (IKBO_KERNEL=w8|w4|pipe).
+enum { kVariantPipe = 0, kVariantW8 = 1, kVariantW4 = 2 };
+int bf16_variant() {
+  const char* s = std::getenv("IKBO_KERNEL");
+  if (s && std::strcmp(s, "pipe") == 0) return kVariantPipe;
+  if (s && std::strcmp(s, "w4") == 0) return kVariantW4;
+  return kVariantW8;
 }
 
 PlanParams params_for(const Plan& p, int32_t dtype) {
   PlanParams pp;
-  if (dtype == IKBO_DTYPE_BF16 && bf16_waves() == 8) {
-    // one resident 8-wave workgroup per CU; chunks are whole ring stages
+  const int variant = bf16_variant();
+  if (dtype == IKBO_DTYPE_BF16 && variant != kVariantW4) {
+    // one resident workgroup per CU; the 8-wave kernel's chunks are whole ring stages
     pp.bm = ikbo::kBf16TileRows;
-    pp.bn = 2 * ikbo::kBf16TileKeys;
+    pp.bn = (variant == kVariantW8 ? 2 : 1) * ikbo::kBf16TileKeys;
     pp.grid_slots = std::max(1, p.n_cu);
     pp.min_chunk = 256;
     pp.allow_split = true;
@@ -289,7 +295,7 @@ int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n
   p->dtype = dtype;
   p->with_self = with_self;
   p->stages = bf16_stages();
-  p->waves = bf16_waves();
+  p->variant = bf16_variant();
   p->total_len = offs[n_users];
   p->built = true;
   return IKBO_OK;
@@ -370,7 +376,9 @@ int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* 
   hipError_t e;
   if (p->dtype != IKBO_DTYPE_BF16)
     e = ikbo::launch_attn_f32(ap, p->d, p->hp.grid, stream, te);
-  else if (p->waves == 8)
+  else if (p->variant == kVariantPipe)
+    e = ikbo::launch_attn_bf16_pipe(ap, p->d, p->hp.grid, scale < 0.0f, stream, te);
+  else if (p->variant == kVariantW8)
     e = ikbo::launch_attn_bf16_w8(ap, p->d, p->hp.grid, stream, te);
   else
     e = ikbo::launch_attn_bf16(ap, p->d, p->stages, p->hp.grid, stream, te);

@@ -36,7 +36,7 @@ def _oracle_target(w):
 @pytest.fixture(autouse=True)
 def _clean_env():
     saved = {k: os.environ.get(k) for k in ("IKBO_GRID_WGS", "IKBO_MIN_CHUNK", "IKBO_NO_SPLIT", "IKBO_SPLIT_SLOTS",
-                                            "IKBO_WAVES")}
+                                            "IKBO_KERNEL")}
     yield
     for k, v in saved.items():
         if v is None:
@@ -67,11 +67,11 @@ def test_c1_tiny_f32():
     assert_close(to_f64(out2), ref, "f32", "c1 ex")
 
 
-@pytest.mark.parametrize("waves", ["8", "4"])
+@pytest.mark.parametrize("waves", ["pipe", "w8", "w4"])
 def test_c2_typical_planned_and_north_star_call(waves):
     from broadcast_free_target_amd import ikbo_attn_fwd
     import torch
-    os.environ["IKBO_WAVES"] = waves
+    os.environ["IKBO_KERNEL"] = waves
     w = _wl("c2_typical")
     say(f"case c2 planned waves={waves}")
     dev = upload(w)
@@ -89,9 +89,9 @@ def test_c2_typical_planned_and_north_star_call(waves):
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
-@pytest.mark.parametrize("waves", ["8", "4"])
+@pytest.mark.parametrize("waves", ["pipe", "w8", "w4"])
 def test_c3_skewed_with_single_key_users(waves):
-    os.environ["IKBO_WAVES"] = waves
+    os.environ["IKBO_KERNEL"] = waves
     w = _wl("c3_skewed")
     say(f"case c3 planned waves={waves}")
     dev = upload(w)
@@ -199,12 +199,12 @@ def _custom(i, lengths, counts, n_q, H, d, dtype, with_self=False):
 
 @pytest.mark.parametrize("i", range(len(EDGE)))
 @pytest.mark.parametrize("split", ["default", "forced", "off"])
-@pytest.mark.parametrize("waves", ["8", "4"])
+@pytest.mark.parametrize("waves", ["pipe", "w8", "w4"])
 def test_edge_matrix(i, split, waves):
     lengths, counts, n_q, H, d, dtype = EDGE[i]
-    if dtype != "bf16" and waves != "8":
+    if dtype != "bf16" and waves != "pipe":
         pytest.skip("the workgroup shape applies to the bf16 kernel only")
-    os.environ["IKBO_WAVES"] = waves
+    os.environ["IKBO_KERNEL"] = waves
     if split == "forced":
         os.environ["IKBO_MIN_CHUNK"] = "64"
         os.environ["IKBO_SPLIT_SLOTS"] = "4096"
@@ -224,13 +224,39 @@ def test_edge_matrix(i, split, waves):
             assert np.all(got[c] == 0)
 
 
-@pytest.mark.parametrize("dtype,d,waves", [("bf16", 128, "8"), ("bf16", 64, "8"), ("bf16", 128, "4"),
-                                          ("bf16", 32, "4"), ("f32", 32, "8")])
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 0.45])
+@pytest.mark.parametrize("kernel", ["pipe", "w8", "w4"])
+def test_scale_sign_and_zero(scale, kernel):
+    """Negative, zero and large scales: the softmax takes c*min(s) as the row
+    maximum for c < 0, and c = 0 gives the plain mean of V."""
+    os.environ["IKBO_KERNEL"] = kernel
+    w = _custom(60, (129, 1, 300, 64), (70, 3, 130, 1), 1, 2, 128, "bf16")
+    say(f"case scale={scale} kernel={kernel}")
+    dev = upload(w)
+    out = empty_out(w.raw("q_cand").shape, "bf16")
+    from broadcast_free_target_amd import (ikbo_attn_fwd_planned, ikbo_plan_build, ikbo_plan_create,
+                                           ikbo_plan_destroy)
+    import torch
+    plan = ikbo_plan_create()
+    try:
+        ikbo_plan_build(plan, w.user_offsets, w.cand_to_user, w.n_users, w.n_cand, w.n_q, w.H, w.d, 0, 0)
+        ikbo_attn_fwd_planned(plan, dev["q_cand"], None, dev["k_user"], dev["v_user"], scale, out)
+        torch.cuda.synchronize()
+    finally:
+        ikbo_plan_destroy(plan)
+    ref = O.target_attention(w.values("q_cand"), w.values("k_user"), w.values("v_user"), w.user_offsets,
+                             w.cand_to_user, scale)
+    assert_close(to_f64(out), ref, "bf16", f"scale {scale}")
+
+
+@pytest.mark.parametrize("dtype,d,waves", [("bf16", 128, "pipe"), ("bf16", 64, "pipe"), ("bf16", 32, "pipe"),
+                                          ("bf16", 128, "w8"), ("bf16", 64, "w8"), ("bf16", 128, "w4"),
+                                          ("bf16", 32, "w4"), ("f32", 32, "pipe")])
 @pytest.mark.parametrize("split", ["default", "forced"])
 def test_edge_fused(dtype, d, waves, split):
     from broadcast_free_target_amd import ikbo_self_target_fwd
     import torch
-    os.environ["IKBO_WAVES"] = waves
+    os.environ["IKBO_KERNEL"] = waves
     if split == "forced":
         os.environ["IKBO_MIN_CHUNK"] = "64"
         os.environ["IKBO_SPLIT_SLOTS"] = "4096"
@@ -271,10 +297,10 @@ def test_p6_permutation_bitwise():
 
 
 @pytest.mark.parametrize("name", ["c2_typical", "c3_skewed"])
-@pytest.mark.parametrize("waves", ["8", "4"])
+@pytest.mark.parametrize("waves", ["pipe", "w8", "w4"])
 def test_p13_determinism_across_runs_and_grids(name, waves):
     import torch
-    os.environ["IKBO_WAVES"] = waves
+    os.environ["IKBO_KERNEL"] = waves
     w = _wl(name)
     dev = upload(w)
     say(f"case P13 {name} waves={waves}")
