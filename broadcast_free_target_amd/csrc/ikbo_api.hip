@@ -181,20 +181,24 @@ int bf16_stages() {
   return (s == 2 || s == 3 || s == 4) ? s : ikbo::kBf16DefaultStages;
 }
 
-// bf16 kernel variant: the eight-wave kernel (default), the plain 4-wave
-// kernel (two resident per CU) or the software-pipelined 4-wave kernel
-// (IKBO_KERNEL=w8|w4|pipe).
-enum { kVariantPipe = 0, kVariantW8 = 1, kVariantW4 = 2 };
+// bf16 kernel variants: the eight-wave kernel (one per CU, two waves per
+// SIMD), the plain 4-wave kernel (two resident per CU) and the
+// software-pipelined 4-wave kernel (one per CU).  By default a build plans for
+// the eight-wave kernel and keeps it when every workgroup gets at most one
+// item; otherwise it plans again for the 4-wave kernel, whose two independent
+// workgroups per CU keep the SIMDs busier over many items.  IKBO_KERNEL =
+// w8 | w4 | pipe forces a variant.
+enum { kVariantPipe = 0, kVariantW8 = 1, kVariantW4 = 2, kVariantAuto = 3 };
 int bf16_variant() {
   const char* s = std::getenv("IKBO_KERNEL");
   if (s && std::strcmp(s, "pipe") == 0) return kVariantPipe;
   if (s && std::strcmp(s, "w4") == 0) return kVariantW4;
-  return kVariantW8;
+  if (s && std::strcmp(s, "w8") == 0) return kVariantW8;
+  return kVariantAuto;
 }
 
-PlanParams params_for(const Plan& p, int32_t dtype) {
+PlanParams params_for(const Plan& p, int32_t dtype, int variant) {
   PlanParams pp;
-  const int variant = bf16_variant();
   if (dtype == IKBO_DTYPE_BF16 && variant != kVariantW4) {
     // one resident workgroup per CU; the 8-wave kernel's chunks are whole ring stages
     pp.bm = ikbo::kBf16TileRows;
@@ -246,12 +250,22 @@ int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n
   // completes the plan cannot be launched.
   p->built = false;
   HostPlan& hp = p->hp;
-  PlanParams pp = params_for(*p, dtype);
   // Split partials name their output row as row * H + h in an int32.
   const int64_t out_units = std::max<int64_t>(static_cast<int64_t>(n_cand) * n_q, with_self ? offs[n_users] : 0) * H;
-  if (out_units >= std::numeric_limits<int32_t>::max()) pp.allow_split = false;
+  const bool split_ok = out_units < std::numeric_limits<int32_t>::max();
+  const int forced = bf16_variant();
+  int variant = forced == kVariantAuto ? kVariantW8 : forced;
+  PlanParams pp = params_for(*p, dtype, variant);
+  if (!split_ok) pp.allow_split = false;
   rc = ikbo::build_plan(offs, c2u, n_users, n_cand, n_q, H, with_self != 0, pp, &hp, &err);
   if (rc != ikbo::kOk) return fail(rc, err);
+  if (dtype == IKBO_DTYPE_BF16 && forced == kVariantAuto && hp.items.size() > static_cast<size_t>(p->n_cu)) {
+    variant = kVariantW4;
+    pp = params_for(*p, dtype, variant);
+    if (!split_ok) pp.allow_split = false;
+    rc = ikbo::build_plan(offs, c2u, n_users, n_cand, n_q, H, with_self != 0, pp, &hp, &err);
+    if (rc != ikbo::kOk) return fail(rc, err);
+  }
 
   const int tile_rows = dtype == IKBO_DTYPE_BF16 ? ikbo::kBf16TileRows : ikbo::kF32TileRows;
   const size_t items_bytes = hp.items.size() * sizeof(WorkItem);
@@ -295,7 +309,7 @@ int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n
   p->dtype = dtype;
   p->with_self = with_self;
   p->stages = bf16_stages();
-  p->variant = bf16_variant();
+  p->variant = variant;
   p->total_len = offs[n_users];
   p->built = true;
   return IKBO_OK;
@@ -546,16 +560,22 @@ void ikbo_plan_destroy(void* plan) {
 int ikbo_plan_info(void* plan, int64_t* info, int32_t n_info) {
   if (!plan || !info || n_info < 1) return fail(IKBO_ERR_INVALID_ARG, "null plan or info");
   const Plan* p = static_cast<const Plan*>(plan);
-  const int64_t v[8] = {static_cast<int64_t>(p->hp.items.size()),
+  // kernel: 0 fp32, 1 bf16 eight-wave, 2 bf16 4-wave, 3 bf16 software-pipelined
+  const int64_t kernel = p->dtype != IKBO_DTYPE_BF16 ? 0
+                         : p->variant == kVariantW8  ? 1
+                         : p->variant == kVariantW4  ? 2
+                                                     : 3;
+  const int64_t v[9] = {static_cast<int64_t>(p->hp.items.size()),
                         p->hp.grid,
                         p->hp.n_groups,
                         p->hp.n_slots,
                         static_cast<int64_t>(p->hp.n_slots) *
-                            (p->dtype == IKBO_DTYPE_BF16 ? ikbo::kBf16TileRows : ikbo::kF32TileRows) * (p->d + 2) * 4,
+                            (p->dtype == IKBO_DTYPE_BF16 ? ikbo::kBf16TileRows : ikbo::kF32TileRows) * (p->d + 4) * 4,
                         p->hp.n_target_tiles,
                         p->hp.n_self_tiles,
-                        p->n_cu};
-  for (int i = 0; i < n_info && i < 8; ++i) info[i] = v[i];
+                        p->n_cu,
+                        kernel};
+  for (int i = 0; i < n_info && i < 9; ++i) info[i] = v[i];
   return IKBO_OK;
 }
 

@@ -194,9 +194,12 @@ int ikbo_plan_trace(void* plan, int32_t enable);
 int ikbo_plan_trace_read(void* plan, int64_t* records, int32_t max_items, int32_t* n_items);
 
 /*
- * Introspection of a built plan (host values): number of work items, grid
- * size of the persistent launch, split groups, and the planned bytes of the
- * split-KV partial workspace.  For tests and measurement.
+ * Introspection of a built plan (host values), for tests and measurement:
+ * info[0] work items, [1] grid of the persistent launch, [2] split groups,
+ * [3] partial-result slots, [4] bytes of the split-KV workspace, [5] target
+ * row tiles, [6] self row tiles, [7] compute units, [8] kernel (0 fp32, 1 bf16
+ * eight-wave, 2 bf16 4-wave, 3 bf16 software-pipelined).  Writes the first
+ * min(n_info, 9) values.
  */
 int ikbo_plan_info(void* plan, int64_t* info, int32_t n_info);
 
