@@ -206,6 +206,7 @@ PlanParams params_for(const Plan& p, int32_t dtype, int variant) {
     pp.grid_slots = std::max(1, p.n_cu);
     pp.min_chunk = 256;
     pp.allow_split = true;
+    pp.single_pass = true;
   } else if (dtype == IKBO_DTYPE_BF16) {
     pp.bm = ikbo::kBf16TileRows;
     pp.bn = ikbo::kBf16TileKeys;

@@ -129,7 +129,49 @@ int build_plan(const int32_t* user_offsets, const int32_t* cand_to_user, int32_t
   // 2. Split long key ranges when there are too few items to fill the grid:
   //    chunk lengths are multiples of bn; the kernel merges chunk partials by
   //    log-sum-exp in chunk order, so results do not depend on the schedule.
+  //    By cost: ranges longer than 1.5x the average load per workgroup are cut
+  //    into chunks of about that load.  Single pass: every workgroup runs one
+  //    item, so the longest item sets the time; the chunk length is the
+  //    shortest multiple of bn (at least min_chunk) whose item count fits the
+  //    grid, found by bisection.
   const int64_t target = std::max<int64_t>(p.min_chunk, ceil_div(total, p.grid_slots));
+  auto chunks_of = [&](int64_t len, int64_t c) {  // chunks of a range of len keys for chunk length c
+    const int64_t floor_len = ceil_div(ceil_div(len, p.max_chunks), p.bn) * p.bn;
+    return std::max<int64_t>(1, ceil_div(len, std::max(c, floor_len)));
+  };
+  int64_t single_len = 0;  // 0: split by cost
+  if (p.allow_split && p.single_pass && n_base < p.grid_slots) {
+    // lengths of the unsplit items, in the order they are built below
+    std::vector<int64_t>& lens = out->lens;
+    lens.clear();
+    int64_t max_len = 0;
+    for (int32_t u = 0; u < n_users; ++u) {
+      const int64_t L = user_offsets[u + 1] - user_offsets[u];
+      const int64_t tiles_t = ceil_div(static_cast<int64_t>(out->counts[u]) * n_q, p.bm);
+      for (int64_t k = 0; k < H * tiles_t; ++k) lens.push_back(L);
+      if (with_self)
+        for (int64_t r0 = 0; r0 < L; r0 += p.bm)
+          for (int32_t h = 0; h < H; ++h) lens.push_back(std::min<int64_t>(r0 + p.bm, L));
+      max_len = std::max(max_len, L);
+    }
+    auto count = [&](int64_t c) {
+      int64_t n = 0;
+      for (int64_t len : lens) n += len > 0 ? chunks_of(len, c) : 1;
+      return n;
+    };
+    int64_t lo = std::max<int64_t>(p.bn, ceil_div(p.min_chunk, p.bn) * p.bn);
+    int64_t hi = std::max<int64_t>(lo, ceil_div(max_len, p.bn) * p.bn);
+    if (count(hi) <= p.grid_slots) {
+      while (lo < hi) {  // smallest multiple of bn in [lo, hi] with count <= grid_slots
+        const int64_t mid = (lo / p.bn + (hi / p.bn - lo / p.bn) / 2) * p.bn;
+        if (count(mid) <= p.grid_slots)
+          hi = mid;
+        else
+          lo = mid + p.bn;
+      }
+      single_len = hi;
+    }
+  }
   out->n_groups = 0;
   out->n_slots = 0;
   out->groups.clear();
@@ -139,7 +181,11 @@ int build_plan(const int32_t* user_offsets, const int32_t* cand_to_user, int32_t
   auto emit = [&](WorkItem it) {
     const int64_t len = it.k1 - it.k0;
     int64_t nchunk = 1, clen = len;
-    if (p.allow_split && len > target + target / 2) {
+    if (single_len > 0 && len > 0) {
+      nchunk = chunks_of(len, single_len);
+      clen = ceil_div(ceil_div(len, nchunk), p.bn) * p.bn;
+      nchunk = ceil_div(len, clen);
+    } else if (single_len == 0 && p.allow_split && len > target + target / 2) {
       nchunk = std::min<int64_t>(ceil_div(len, target), p.max_chunks);
       clen = ceil_div(ceil_div(len, nchunk), p.bn) * p.bn;
       nchunk = ceil_div(len, clen);

@@ -58,6 +58,8 @@ struct PlanParams {
   int32_t max_chunks = kMaxSplit;  // most chunks one key range is cut into (<= kMaxSplit)
   int32_t overhead = 128;     // fixed cost of an item, in key units
   bool allow_split = true;    // split long key ranges (log-sum-exp merge)
+  bool single_pass = false;   // split to the shortest chunk length whose items still
+                              // fit grid_slots (one item per workgroup), else by cost
 };
 
 struct HostPlan {
@@ -75,6 +77,7 @@ struct HostPlan {
   std::vector<int32_t> cursor;
   std::vector<WorkItem> unsorted;
   std::vector<uint64_t> keys;
+  std::vector<int64_t> lens;
 };
 
 // Status codes mirror include/ikbo.h.

@@ -1,7 +1,7 @@
 // Test driver for the host planner (built with g++ and sanitizers by the
 // CPU test suite).  Reads one problem from stdin as whitespace-separated
 // integers:
-//   n_users n_cand n_q H with_self bm bn grid_slots min_chunk allow_split
+//   n_users n_cand n_q H with_self bm bn grid_slots min_chunk allow_split single_pass
 //   user_offsets[n_users+1] cand_to_user[n_cand]
 // and prints "rc <status>", then "plan <n_items> <grid> <n_groups> <n_slots>",
 // "perm <cand_perm...>", and one "item" line per work item (all 12 fields).
@@ -13,9 +13,9 @@
 #include "ikbo_plan.h"
 
 int main() {
-  int32_t n_users, n_cand, n_q, H, with_self, bm, bn, grid_slots, min_chunk, allow_split;
+  int32_t n_users, n_cand, n_q, H, with_self, bm, bn, grid_slots, min_chunk, allow_split, single_pass;
   if (!(std::cin >> n_users >> n_cand >> n_q >> H >> with_self >> bm >> bn >> grid_slots >> min_chunk >>
-        allow_split))
+        allow_split >> single_pass))
     return 2;
   std::vector<int32_t> offs(static_cast<size_t>(n_users) + 1), c2u(n_cand);
   for (auto& x : offs) std::cin >> x;
@@ -26,6 +26,7 @@ int main() {
   p.grid_slots = grid_slots;
   p.min_chunk = min_chunk;
   p.allow_split = allow_split != 0;
+  p.single_pass = single_pass != 0;
   ikbo::HostPlan hp;
   std::string err;
   const int rc = ikbo::build_plan(offs.data(), c2u.data(), n_users, n_cand, n_q, H, with_self != 0, p, &hp, &err);

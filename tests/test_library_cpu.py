@@ -105,8 +105,9 @@ def driver(tmp_path_factory):
     return out
 
 
-def _run_driver(driver, offs, c2u, n_q=1, H=2, with_self=0, bm=128, bn=64, grid=512, min_chunk=256, split=1):
-    nums = [len(offs) - 1, len(c2u), n_q, H, with_self, bm, bn, grid, min_chunk, split, *offs, *c2u]
+def _run_driver(driver, offs, c2u, n_q=1, H=2, with_self=0, bm=128, bn=64, grid=512, min_chunk=256, split=1,
+                single=0):
+    nums = [len(offs) - 1, len(c2u), n_q, H, with_self, bm, bn, grid, min_chunk, split, single, *offs, *c2u]
     r = subprocess.run([driver], input=" ".join(map(str, nums)), capture_output=True, text=True, check=True,
                        env={**os.environ, "ASAN_OPTIONS": "detect_leaks=1"})
     lines = r.stdout.splitlines()
@@ -212,6 +213,67 @@ def test_planner_on_configs(driver, name):
         rc, plan = _run_driver(driver, offs, c2u, n_q=n_q, H=H, with_self=with_self, grid=grid, min_chunk=min_chunk)
         assert rc == 0
         _check_plan(plan, offs, c2u, n_q, H, with_self, 128, 64, grid)
+
+
+def _single_pass_count(lens, c, bn, max_chunks=8):
+    """Items the single-pass rule makes for chunk length c (mirrors its definition)."""
+    n = 0
+    for L in lens:
+        if L == 0:
+            n += 1
+            continue
+        floor_len = -(-(-(-L // max_chunks)) // bn) * bn
+        n += -(-L // max(c, floor_len))
+    return n
+
+
+@pytest.mark.parametrize("name", ["c2_typical", "c3_skewed", "c5_fused"])
+def test_planner_single_pass(driver, name):
+    """Single pass (fewer unsplit items than workgroups): at most grid items, and
+    the chunk length is the shortest multiple of bn (>= min_chunk) that fits;
+    every plan invariant still holds."""
+    if name == "c5_fused":
+        rng = np.random.Generator(np.random.PCG64(1005))
+        L = rng.integers(256, 2048, size=30, endpoint=True)
+        counts = rng.multinomial(2048, [1 / 30] * 30)
+        c2u = rng.permutation(np.repeat(np.arange(30), counts)).astype(np.int32)
+        offs = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+        n_q, H, with_self = 1, 4, 1
+    else:
+        w = make_workload(name)
+        offs, c2u, n_q, H, with_self = w.user_offsets, w.cand_to_user, w.n_q, w.H, 0
+    bn, bm = 128, 128
+    for grid, min_chunk in [(256, 256), (1024, 128), (64, 256)]:
+        rc, plan = _run_driver(driver, offs, c2u, n_q=n_q, H=H, with_self=with_self, bm=bm, bn=bn, grid=grid,
+                               min_chunk=min_chunk, single=1)
+        assert rc == 0
+        _check_plan(plan, offs, c2u, n_q, H, with_self, bm, bn, grid)
+        Ls = np.diff(np.asarray(offs, dtype=np.int64))
+        counts = np.bincount(np.asarray(c2u, dtype=np.int64), minlength=len(Ls))
+        lens = []
+        for u in range(len(Ls)):
+            lens += [int(Ls[u])] * (H * (-(-int(counts[u]) * n_q // bm)))
+            if with_self:
+                lens += [min(r0 + bm, int(Ls[u])) for r0 in range(0, int(Ls[u]), bm) for _ in range(H)]
+        items = plan["items"]
+        if len(lens) >= grid:
+            continue  # more unsplit items than workgroups: the cost rule applies (checked above)
+        assert len(items) <= grid
+        # the shortest admissible chunk length, searched independently
+        lo = max(bn, -(-min_chunk // bn) * bn)
+        c = lo
+        while _single_pass_count(lens, c, bn) > grid:
+            c += bn
+        assert len(items) == _single_pass_count(lens, c, bn)
+        ends = {}  # split group -> end of its key range
+        for it in items:
+            if it[8] >= 0:
+                ends[int(it[8])] = max(ends.get(int(it[8]), 0), int(it[5]))
+        for it in items:  # no chunk longer than the rule allows for its range
+            if it[8] >= 0:
+                L = ends[int(it[8])]
+                floor_len = -(-(-(-L // 8)) // bn) * bn
+                assert int(it[5]) - int(it[4]) <= max(c, floor_len)
 
 
 def test_planner_edge_cases(driver):
