@@ -30,7 +30,9 @@ METRIC = "IKBO attn BF16 TFLOP/s (+% MFMA peak) and HBM bytes vs materialized br
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
-DOMINANT_KERNEL = "ikbo_attn_bf16_kernel<128>"
+# Attention kernel a plan runs (ikbo_plan_info "kernel"), by head dim.
+KERNEL_NAMES = {0: "ikbo_attn_f32_kernel<{d}>", 1: "ikbo_attn_bf16_w8_kernel<{d}, 2>",
+                2: "ikbo_attn_bf16_kernel<{d}, 2>", 3: "ikbo_attn_bf16_pipe_kernel<{d}, 4, false>"}
 
 WORKLOAD_TEXT = {
     "c1_tiny_f32": "tiny fp32: 4 users, L~U[16,64], 20 candidates, n_q=1, H=2, d=32",
@@ -60,7 +62,7 @@ def algorithmic_counts(w):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("ikbo_kernels.hip", "ikbo_kernels.h", "ikbo_plan.cpp", "ikbo_plan.h"):
+    for f in ("ikbo_kernels.hip", "ikbo_kernels.h", "ikbo_plan.cpp", "ikbo_plan.h", "ikbo_api.hip"):
         with open(os.path.join(ROOT, "broadcast_free_target_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -233,7 +235,7 @@ def main():
         pk = peak_flops / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": pk, "unit": "TFLOP/s", "frac": achieved / pk}
     roof["traffic"] = traffic_from_profiles(args.config)
-    roof["kernel"] = DOMINANT_KERNEL if w.dtype == "bf16" else "ikbo_attn_f32_kernel"
+    roof["kernel"] = KERNEL_NAMES[int(info["kernel"])].format(d=w.d)
     roof["kernel_avg_us"] = k_avg_ms * 1e3
     roof["merge_kernel_avg_us"] = merge_avg_ms * 1e3  # split-KV merge, when key ranges were split
     roof["algorithmic_bytes_per_launch"] = byts
