@@ -1,9 +1,9 @@
-"""Seeded synthetic inputs for IKBO target attention.
+"""Seeded synthetic inputs for IKBO target attention and IKBO linear compression.
 
 This package draws inputs only: sequence lengths, candidate-to-user mappings and
 N(0,1) tensors quantised to the dtype the kernel receives.  It holds none of the
-attention arithmetic, so both the fp64 oracle's tests and the GPU path can use it
-without sharing any of the method's code.
+attention or projection arithmetic, so both the fp64 oracle's tests and the GPU
+path can use it without sharing any of the method's code.
 """
 
 from .ikbo import (  # noqa: F401
@@ -14,3 +14,4 @@ from .ikbo import (  # noqa: F401
     make_custom,
     make_workload,
 )
+from .lce import LCE_NAMES, LceWorkload, make_lce, make_lce_custom  # noqa: F401
