@@ -23,6 +23,12 @@ from .ikbo import (  # noqa: F401
     ikbo_attn_fwd_planned,
     ikbo_group_csr,
     ikbo_last_error,
+    ikbo_lce_create,
+    ikbo_lce_destroy,
+    ikbo_lce_errors,
+    ikbo_lce_fwd,
+    ikbo_lce_timing,
+    ikbo_lce_timing_read,
     ikbo_plan_build,
     ikbo_plan_create,
     ikbo_plan_destroy,

@@ -21,6 +21,7 @@
 
 #include "ikbo.h"
 #include "ikbo_kernels.h"
+#include "ikbo_lce.h"
 #include "ikbo_plan.h"
 
 namespace {
@@ -478,6 +479,27 @@ struct BcastWs {
 std::mutex g_bcast_mu;
 std::map<int, BcastWs*> g_bcast;
 
+// IKBO linear compression: packed W blocks, the user-result workspace and the
+// mapping error counter, bound to one device.
+struct Lce {
+  int device = -1;
+  int32_t M = 0, K_u = 0, K_c = 0, M_pad = 0, K_u_pad = 0, K_c_pad = 0;
+  DevBuf wu, wc, y, errors;
+  bool timing = false;
+  std::vector<hipEvent_t> tev;  // 4 per timed call: user GEMM start/end, candidate GEMM start/end
+  std::vector<char> timed_user;
+  int n_timed = 0;
+  ~Lce() {
+    for (hipEvent_t e : tev) (void)hipEventDestroy(e);
+    wu.release();
+    wc.release();
+    y.release();
+    errors.release();
+  }
+};
+
+int32_t round_up(int32_t x, int32_t m) { return (x + m - 1) / m * m; }
+
 }  // namespace
 
 extern "C" {
@@ -755,6 +777,173 @@ int ikbo_attn_fwd_materialized(const void* q_cand, const void* k_user, const voi
   } catch (...) {
     return fail(IKBO_ERR_INVALID_ARG, "unexpected host error");
   }
+}
+
+int ikbo_lce_create(void** lce, const void* w, int32_t M, int32_t K_u, int32_t K_c, int32_t ldw, void* stream_) {
+  try {
+    if (!lce) return fail(IKBO_ERR_INVALID_ARG, "lce is null");
+    *lce = nullptr;
+    if (!w) return fail(IKBO_ERR_INVALID_ARG, "w is null");
+    if (M < 1 || K_u < 0 || K_c < 0 || K_u + K_c < 1) return fail(IKBO_ERR_INVALID_ARG, "M >= 1, K_u, K_c >= 0, K_u + K_c >= 1 required");
+    if (ldw < K_u + K_c) return fail(IKBO_ERR_INVALID_ARG, "ldw must be >= K_u + K_c");
+    if (static_cast<int64_t>(M) * ldw > std::numeric_limits<int32_t>::max())
+      return fail(IKBO_ERR_INVALID_ARG, "W too large");
+    Lce* l = new (std::nothrow) Lce();
+    if (!l) return fail(IKBO_ERR_NOMEM, "lce allocation");
+    hipError_t e = hipGetDevice(&l->device);
+    if (e != hipSuccess) {
+      delete l;
+      return fail_hip(e, "hipGetDevice");
+    }
+    l->M = M;
+    l->K_u = K_u;
+    l->K_c = K_c;
+    l->M_pad = round_up(M, ikbo::kLceTileM);
+    l->K_u_pad = round_up(K_u, ikbo::kLceTileK);
+    l->K_c_pad = round_up(K_c, ikbo::kLceTileK);
+    int rc;
+    if ((rc = l->wu.ensure(static_cast<size_t>(l->M_pad) * std::max(l->K_u_pad, 1) * 2, false)) != IKBO_OK ||
+        (rc = l->wc.ensure(static_cast<size_t>(l->M_pad) * std::max(l->K_c_pad, 1) * 2, false)) != IKBO_OK ||
+        (rc = l->errors.ensure(sizeof(int32_t), true)) != IKBO_OK) {
+      delete l;
+      return rc;
+    }
+    e = ikbo::launch_lce_pack(w, M, ldw, K_u, K_c, l->M_pad, l->K_u_pad, l->K_c_pad, l->wu.ptr, l->wc.ptr,
+                              static_cast<hipStream_t>(stream_));
+    if (e != hipSuccess) {
+      delete l;
+      return fail_hip(e, "pack launch");
+    }
+    *lce = l;
+    return IKBO_OK;
+  } catch (...) {
+    return fail(IKBO_ERR_NOMEM, "unexpected host error");
+  }
+}
+
+int ikbo_lce_fwd(void* lce, const void* x_user, const void* x_cand, const int32_t* cand_to_user, int32_t n_users,
+                 int32_t n_cand, int32_t N, void* out, void* stream_) {
+  try {
+    if (!lce) return fail(IKBO_ERR_INVALID_ARG, "lce is null");
+    Lce* l = static_cast<Lce*>(lce);
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    int dev = -1;
+    IKBO_HIP(hipGetDevice(&dev));
+    if (dev != l->device) return fail(IKBO_ERR_INVALID_ARG, "lce belongs to another device");
+    if (n_users < 0 || n_cand < 0) return fail(IKBO_ERR_INVALID_ARG, "n_users and n_cand must be >= 0");
+    if (N < ikbo::kLceTileN || N % ikbo::kLceTileN != 0) return fail(IKBO_ERR_UNSUPPORTED, "N must be a positive multiple of 128");
+    if (n_cand == 0) return IKBO_OK;
+    if (n_users == 0) return fail(IKBO_ERR_BAD_MAPPING, "candidates present but n_users == 0");
+    if (!out || !cand_to_user || (l->K_c > 0 && !x_cand) || (l->K_u > 0 && !x_user))
+      return fail(IKBO_ERR_INVALID_ARG, "null tensor pointer");
+    const uintptr_t align_or = reinterpret_cast<uintptr_t>(x_user) | reinterpret_cast<uintptr_t>(x_cand) |
+                               reinterpret_cast<uintptr_t>(out);
+    if (align_or & 15) return fail(IKBO_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    const size_t out_bytes = static_cast<size_t>(n_cand) * l->M * N * 2;
+    if (overlaps(out, out_bytes, x_user, static_cast<size_t>(n_users) * l->K_u * N * 2) ||
+        overlaps(out, out_bytes, x_cand, static_cast<size_t>(n_cand) * l->K_c * N * 2) ||
+        overlaps(out, out_bytes, cand_to_user, static_cast<size_t>(n_cand) * 4))
+      return fail(IKBO_ERR_INVALID_ARG, "out aliases an input");
+    const int64_t grid_c = static_cast<int64_t>(n_cand) * (l->M_pad / ikbo::kLceTileM) * (N / ikbo::kLceTileN);
+    const int64_t grid_u = static_cast<int64_t>(n_users) * (l->M_pad / ikbo::kLceTileM) * (N / ikbo::kLceTileN);
+    if (grid_c > std::numeric_limits<int32_t>::max() || grid_u > std::numeric_limits<int32_t>::max() ||
+        static_cast<int64_t>(std::max(n_users, n_cand)) * l->M * N > std::numeric_limits<int32_t>::max() * 8LL)
+      return fail(IKBO_ERR_INVALID_ARG, "problem too large");
+    int rc;
+    if (l->K_u > 0 && (rc = l->y.ensure(static_cast<size_t>(n_users) * l->M * N * 4, false)) != IKBO_OK) return rc;
+    hipEvent_t* te = nullptr;
+    if (l->timing && l->n_timed < kMaxTimed) {
+      while (l->tev.size() < static_cast<size_t>(4 * (l->n_timed + 1))) {
+        hipEvent_t ev;
+        IKBO_HIP(hipEventCreate(&ev));
+        l->tev.push_back(ev);
+      }
+      te = &l->tev[4 * l->n_timed];
+      l->timed_user.resize(l->n_timed + 1);
+      l->timed_user[l->n_timed] = l->K_u > 0;
+      ++l->n_timed;
+    }
+    ikbo::LceParams p{};
+    p.N = N;
+    p.M = l->M;
+    p.m_tiles = l->M_pad / ikbo::kLceTileM;
+    p.n_tiles = N / ikbo::kLceTileN;
+    p.n_users = n_users;
+    p.errors = static_cast<int32_t*>(l->errors.ptr);
+    if (l->K_u > 0) {  // user GEMM at the user batch
+      p.w = l->wu.ptr;
+      p.ldw = l->K_u_pad;
+      p.x = x_user;
+      p.K = l->K_u;
+      p.y = static_cast<float*>(l->y.ptr);
+      hipError_t e = ikbo::launch_lce_gemm(p, 0, n_users, stream, te);
+      if (e != hipSuccess) return fail_hip(e, "user GEMM launch");
+    }
+    // candidate GEMM with the gathered user result added in the epilogue
+    p.w = l->wc.ptr;
+    p.ldw = std::max(l->K_c_pad, 1);
+    p.x = x_cand;
+    p.K = l->K_c;
+    p.y = l->K_u > 0 ? static_cast<float*>(l->y.ptr) : nullptr;
+    p.out = out;
+    p.cand_to_user = cand_to_user;
+    hipError_t e = ikbo::launch_lce_gemm(p, 1, n_cand, stream, te ? te + 2 : nullptr);
+    if (e != hipSuccess) return fail_hip(e, "candidate GEMM launch");
+    return IKBO_OK;
+  } catch (...) {
+    return fail(IKBO_ERR_NOMEM, "unexpected host error");
+  }
+}
+
+int ikbo_lce_errors(void* lce, int64_t* count) {
+  if (!lce || !count) return fail(IKBO_ERR_INVALID_ARG, "null argument");
+  Lce* l = static_cast<Lce*>(lce);
+  int cur = -1;
+  IKBO_HIP(hipGetDevice(&cur));
+  if (cur != l->device) return fail(IKBO_ERR_INVALID_ARG, "lce belongs to another device");
+  IKBO_HIP(hipDeviceSynchronize());
+  int32_t v = 0;
+  IKBO_HIP(hipMemcpy(&v, l->errors.ptr, sizeof(v), hipMemcpyDeviceToHost));
+  IKBO_HIP(hipMemset(l->errors.ptr, 0, sizeof(int32_t)));
+  *count = v;
+  return IKBO_OK;
+}
+
+int ikbo_lce_timing(void* lce, int32_t enable) {
+  if (!lce) return fail(IKBO_ERR_INVALID_ARG, "lce is null");
+  Lce* l = static_cast<Lce*>(lce);
+  l->timing = enable != 0;
+  l->n_timed = 0;
+  return IKBO_OK;
+}
+
+int ikbo_lce_timing_read(void* lce, float* user_ms, float* cand_ms, int32_t max_n, int32_t* n) {
+  if (!lce || !n || max_n < 0 || (max_n > 0 && (!user_ms || !cand_ms))) return fail(IKBO_ERR_INVALID_ARG, "null argument");
+  Lce* l = static_cast<Lce*>(lce);
+  const int m = std::min<int>(l->n_timed, max_n);
+  for (int i = 0; i < m; ++i) {
+    user_ms[i] = 0.0f;
+    if (l->timed_user[i]) {
+      IKBO_HIP(hipEventSynchronize(l->tev[4 * i + 1]));
+      IKBO_HIP(hipEventElapsedTime(&user_ms[i], l->tev[4 * i], l->tev[4 * i + 1]));
+    }
+    IKBO_HIP(hipEventSynchronize(l->tev[4 * i + 3]));
+    IKBO_HIP(hipEventElapsedTime(&cand_ms[i], l->tev[4 * i + 2], l->tev[4 * i + 3]));
+  }
+  *n = m;
+  return IKBO_OK;
+}
+
+void ikbo_lce_destroy(void* lce) {
+  if (!lce) return;
+  Lce* l = static_cast<Lce*>(lce);
+  int cur = -1;
+  if (hipGetDevice(&cur) == hipSuccess) {
+    (void)hipSetDevice(l->device);
+    (void)hipDeviceSynchronize();
+    (void)hipSetDevice(cur);
+  }
+  delete l;
 }
 
 }  // extern "C"

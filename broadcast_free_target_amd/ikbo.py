@@ -51,6 +51,13 @@ SIGNATURES = {
     "ikbo_plan_trace_read": (ctypes.c_int, [_P, _LP, _I, _IP]),
     "ikbo_plan_timing_read": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
                                              _I, _IP]),
+    "ikbo_lce_create": (ctypes.c_int, [ctypes.POINTER(_P), _P, _I, _I, _I, _I, _P]),
+    "ikbo_lce_fwd": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _P, _P]),
+    "ikbo_lce_errors": (ctypes.c_int, [_P, _LP]),
+    "ikbo_lce_timing": (ctypes.c_int, [_P, _I]),
+    "ikbo_lce_timing_read": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
+                                            _I, _IP]),
+    "ikbo_lce_destroy": (None, [_P]),
 }
 
 _lib = None
@@ -220,3 +227,39 @@ def ikbo_plan_trace_read(plan, max_items: int = 1 << 20) -> np.ndarray:
     n = ctypes.c_int32(0)
     _check(load_library().ikbo_plan_trace_read(plan, buf.ctypes.data_as(_LP), max_items, ctypes.byref(n)))
     return buf[:n.value]
+
+
+def ikbo_lce_create(w, M, K_u, K_c, ldw=None, stream=None) -> int:
+    """Packs W [M, ldw] (device bf16, user columns first) into a library handle."""
+    h = _P()
+    _check(load_library().ikbo_lce_create(ctypes.byref(h), _ptr(w), M, K_u, K_c, K_u + K_c if ldw is None else ldw,
+                                          _stream(stream)))
+    return h.value
+
+
+def ikbo_lce_fwd(lce, x_user, x_cand, cand_to_user, n_users, n_cand, N, out, stream=None) -> int:
+    return _check(load_library().ikbo_lce_fwd(lce, _ptr(x_user), _ptr(x_cand), _ptr(cand_to_user), n_users, n_cand,
+                                              N, _ptr(out), _stream(stream)))
+
+
+def ikbo_lce_errors(lce) -> int:
+    c = ctypes.c_int64(0)
+    _check(load_library().ikbo_lce_errors(lce, ctypes.byref(c)))
+    return c.value
+
+
+def ikbo_lce_timing(lce, enable: bool) -> int:
+    return _check(load_library().ikbo_lce_timing(lce, 1 if enable else 0))
+
+
+def ikbo_lce_timing_read(lce, max_n: int = 4096):
+    """Per-call (user GEMM, candidate GEMM) durations in ms of the timed calls."""
+    a = (ctypes.c_float * max(max_n, 1))()
+    b = (ctypes.c_float * max(max_n, 1))()
+    n = ctypes.c_int32(0)
+    _check(load_library().ikbo_lce_timing_read(lce, a, b, max_n, ctypes.byref(n)))
+    return list(a[:n.value]), list(b[:n.value])
+
+
+def ikbo_lce_destroy(lce) -> None:
+    load_library().ikbo_lce_destroy(lce)

@@ -194,6 +194,47 @@ int ikbo_plan_trace(void* plan, int32_t enable);
 int ikbo_plan_trace_read(void* plan, int64_t* records, int32_t max_items, int32_t* n_items);
 
 /*
+ * IKBO linear compression, Type I (IKBO blog section 2: 2.1 the split of the
+ * batched projection along K, Fig. 2; 2.2 zero padding of each decomposed K;
+ * 2.3 the broadcast-add fused into the candidate GEMM's epilogue, Fig. 3; App. 2
+ * gives the shapes B = 1024, M = 433, K = 2044, N = 256).  The linear compression
+ * multiplies one learned W [M, K] with every candidate's K input embeddings of
+ * width N, (M, K) @ (B, K, N) -> (B, M, N), where a candidate's K embeddings are
+ * its user's K_u embeddings followed by its own K_c embeddings.  IKBO computes
+ *   y[u]   = W[:, :K_u] . x_user[u]                    once per user (fp32),
+ *   out[b] = W[:, K_u:] . x_cand[b] + y[cand_to_user[b]]
+ * with fp32 accumulation and bf16 output; the user embeddings are never copied
+ * per candidate and the broadcast add happens in registers.
+ *
+ * ikbo_lce_create: packs W (device, bf16 [M, ldw] row-major, user columns
+ *   [0, K_u), candidate columns [K_u, K_u + K_c), ldw >= K_u + K_c) into two
+ *   library-owned blocks zero-padded to K multiples of 64 and M multiples of
+ *   128 (enqueued on `stream`; W may be freed once that work completes).
+ *   M >= 1, K_u >= 0, K_c >= 0, K_u + K_c >= 1.  *lce receives the handle.
+ * ikbo_lce_fwd: x_user [n_users, K_u, N], x_cand [n_cand, K_c, N], out
+ *   [n_cand, M, N], all bf16 device tensors, 16-byte aligned; cand_to_user is an
+ *   int32 device array [n_cand].  N must be a positive multiple of 128.  Enqueues
+ *   two kernels (user GEMM, then candidate GEMM) and returns without
+ *   synchronising.  Mapping entries outside [0, n_users) are not an error the
+ *   call can see: their output rows are written as zeros and counted (see
+ *   ikbo_lce_errors).  Calls with one handle must be ordered on one stream (they
+ *   share its user-result workspace).  n_cand = 0 is a no-op.
+ * ikbo_lce_errors: synchronises the device and returns (and resets) the number
+ *   of candidates seen with an out-of-range mapping entry since the last call.
+ * ikbo_lce_timing / _timing_read: per-call durations of the user and candidate
+ *   GEMMs from events stamped by the dispatches (measurement; as the plan
+ *   timing functions, at most 4096 calls between resets).
+ * ikbo_lce_destroy: frees the handle after synchronising its device.
+ */
+int ikbo_lce_create(void** lce, const void* w, int32_t M, int32_t K_u, int32_t K_c, int32_t ldw, void* stream);
+int ikbo_lce_fwd(void* lce, const void* x_user, const void* x_cand, const int32_t* cand_to_user, int32_t n_users,
+                 int32_t n_cand, int32_t N, void* out, void* stream);
+int ikbo_lce_errors(void* lce, int64_t* count);
+int ikbo_lce_timing(void* lce, int32_t enable);
+int ikbo_lce_timing_read(void* lce, float* user_ms, float* cand_ms, int32_t max_n, int32_t* n);
+void ikbo_lce_destroy(void* lce);
+
+/*
  * Introspection of a built plan (host values), for tests and measurement:
  * info[0] work items, [1] grid of the persistent launch, [2] split groups,
  * [3] partial-result slots, [4] bytes of the split-KV workspace, [5] target
