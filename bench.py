@@ -41,7 +41,11 @@ WORKLOAD_TEXT = {
     "c4_large": "large: 10000 candidates over 150 users, L~U[512,4096], n_q=4, H=8, d=128, bf16",
     "c5_fused": "fused self+target: 2048 candidates over 30 users, causal self over L~U[256,2048], H=4, d=128, bf16",
     "p_app11": "App. 11 shape: 32 users x 64 candidates, n_q=64, L=1024, H=2, d=128, bf16",
+    "lce_typical": "linear compression: 1024 candidates over 15 users, M=433, K_u=K_c=1022, N=256, bf16",
+    "lce_ratio1000": "linear compression: 2000 candidates over 2 users, M=433, K_u=K_c=1022, N=256, bf16",
 }
+LCE_METRIC = "IKBO linear compression BF16 TFLOP/s (executed work) and FLOPs vs materialized broadcast"
+LCE_KERNEL = "ikbo_lce_gemm_kernel<1>"  # candidate GEMM with the broadcast-add epilogue
 
 
 def algorithmic_counts(w):
@@ -60,24 +64,47 @@ def algorithmic_counts(w):
     return flops, byts, mat_bytes
 
 
-def kernel_source_hash():
+def lce_counts(w):
+    """Algorithmic FLOPs and HBM bytes of one linear-compression call, per kernel.
+
+    user GEMM:      2 M N U K_u flops; reads W_u, x_user, writes y (fp32)
+    candidate GEMM: 2 M N B K_c flops; reads W_c, x_cand, y once per user, writes out
+    baseline:       2 M N B (K_u + K_c) flops on the materialised concatenation
+    """
+    U, B, M, K_u, K_c, N = w.n_users, w.n_cand, w.M, w.K_u, w.K_c, w.N
+    f_user = 2.0 * M * N * U * K_u
+    f_cand = 2.0 * M * N * B * K_c
+    b_user = 2.0 * (M * K_u + U * K_u * N) + 4.0 * U * M * N
+    b_cand = 2.0 * (M * K_c + B * K_c * N + B * M * N) + 4.0 * U * M * N
+    f_base = 2.0 * M * N * B * (K_u + K_c)
+    b_base = 2.0 * (M * (K_u + K_c) + B * (K_u + K_c) * N + B * M * N)
+    return f_user, f_cand, b_user, b_cand, f_base, b_base
+
+
+def kernel_source_hash(files=("ikbo_kernels.hip", "ikbo_kernels.h", "ikbo_device.h", "ikbo_plan.cpp",
+                              "ikbo_plan.h", "ikbo_api.hip")):
     h = hashlib.sha256()
-    for f in ("ikbo_kernels.hip", "ikbo_kernels.h", "ikbo_plan.cpp", "ikbo_plan.h", "ikbo_api.hip"):
+    for f in files:
         with open(os.path.join(ROOT, "broadcast_free_target_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
+LCE_SOURCES = ("ikbo_lce.hip", "ikbo_lce.h", "ikbo_device.h", "ikbo_api.hip")
+
+
 def traffic_from_profiles(workload):
     """Per-launch HBM bytes from the committed rocprofv3 --pmc summary, if it
     was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"ikbo_attn_bf16_{workload}_pmc.json")
+    lce = workload.startswith("lce_")
+    name = f"ikbo_lce_gemm_{workload}_pmc.json" if lce else f"ikbo_attn_bf16_{workload}_pmc.json"
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     try:
         with open(path) as fh:
             s = json.load(fh)
-        if s.get("kernel_source_hash") != kernel_source_hash():
+        if s.get("kernel_source_hash") != (kernel_source_hash(LCE_SOURCES) if lce else kernel_source_hash()):
             return None
         return float(s["hbm_bytes_per_launch"])
     except Exception:
@@ -122,6 +149,164 @@ def cpu_baseline(w, reps):
             "seconds": t, "cands_per_s": w.n_cand / t}
 
 
+def cpu_baseline_lce(w, n_sample, reps):
+    """The fp64 oracle (explicit per-candidate concatenation) on the first
+    n_sample candidates; its time is scaled to the whole batch and the rate is
+    counted in the same executed FLOPs as the GPU figure."""
+    from oracle import lce_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    wv, xu, xc = w.values("w"), w.values("x_user"), w.values("x_cand")[:n_sample]
+    c2u = w.cand_to_user[:n_sample]
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        O.lce_baseline(wv, xu, xc, c2u)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    f_user, f_cand, _, _, _, _ = lce_counts(w)
+    t_whole = t * w.n_cand / n_sample
+    return {"value": (f_user + f_cand) / t_whole / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n_sample} of {w.n_cand} candidates of {w.name}, fp64 numpy with explicit "
+                      f"per-candidate concatenation, median of {reps} runs of {t:.2f} s, scaled to the whole batch "
+                      f"and counted in the same executed FLOPs as the GPU value",
+            "seconds_whole_batch": t_whole, "cands_per_s": w.n_cand / t_whole}
+
+
+def main_lce(args):
+    """One step = one ikbo_lce_fwd: user GEMM, then the candidate GEMM whose
+    epilogue adds each candidate's user result."""
+    import torch
+    import broadcast_free_target_amd as ikbo
+    from workloads import make_lce
+
+    w = make_lce(args.config)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    W, xu, xc = dev(w.raw("w")), dev(w.raw("x_user")), dev(w.raw("x_cand"))
+    c2u = torch.from_numpy(w.cand_to_user.copy()).cuda()
+    out = torch.empty((w.n_cand, w.M, w.N), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    h = ikbo.ikbo_lce_create(W, w.M, w.K_u, w.K_c, stream=stream)
+
+    def step():
+        ikbo.ikbo_lce_fwd(h, xu, xc, c2u, w.n_users, w.n_cand, w.N, out, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ikbo.ikbo_lce_timing(h, True)
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    user_ms, cand_ms = ikbo.ikbo_lce_timing_read(h, K)
+    ikbo.ikbo_lce_timing(h, False)
+    if ikbo.ikbo_lce_errors(h) != 0:
+        raise RuntimeError("linear compression reported out-of-range candidate mappings")
+    u_avg, c_avg = float(np.mean(user_ms)), float(np.mean(cand_ms))
+
+    f_user, f_cand, b_user, b_cand, f_base, b_base = lce_counts(w)
+    ms_per_step = wall * 1e3 / K
+    value = (f_user + f_cand) / (ms_per_step * 1e-3) / 1e12
+    ai = f_cand / b_cand
+    if ai < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        achieved = b_cand / (c_avg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    else:
+        achieved = f_cand / (c_avg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS}
+    roof["traffic"] = traffic_from_profiles(args.config)
+    roof["kernel"] = LCE_KERNEL
+    roof["kernel_avg_us"] = c_avg * 1e3
+    roof["user_kernel_avg_us"] = u_avg * 1e3
+    roof["algorithmic_bytes_per_launch"] = b_cand
+    roof["algorithmic_flops_per_launch"] = f_cand
+    extra = {
+        "candidate_gemm_tflops": f_cand / (c_avg * 1e-3) / 1e12,
+        "candidate_gemm_hbm_gbs": b_cand / (c_avg * 1e-3) / 1e9,
+        "user_gemm_tflops": f_user / (u_avg * 1e-3) / 1e12 if u_avg > 0 else None,
+        "arith_intensity_candidate_gemm": ai,
+        "executed_flops": f_user + f_cand,
+        "baseline_flops": f_base,
+        "flops_saved_frac": 1.0 - (f_user + f_cand) / f_base,
+        "baseline_equivalent_tflops": f_base / (ms_per_step * 1e-3) / 1e12,
+        "algorithmic_bytes_ikbo": b_user + b_cand,
+        "algorithmic_bytes_baseline": b_base,
+        "cands_per_s": w.n_cand / (ms_per_step * 1e-3),
+    }
+    if args.report:
+        # Materialised comparator: the broadcast copy (x_user[u(b)] next to x_cand[b]
+        # along K) and the same GEMM kernel on the full K, no user block.
+        hb = ikbo.ikbo_lce_create(W, w.M, 0, w.K, stream=stream)
+        xfull = torch.empty((w.n_cand, w.K, w.N), dtype=torch.bfloat16, device="cuda")
+        idx = c2u.long()
+
+        def copy():
+            xfull[:, :w.K_u].copy_(xu.index_select(0, idx))
+            xfull[:, w.K_u:].copy_(xc)
+
+        def gemm():
+            ikbo.ikbo_lce_fwd(hb, None, xfull, c2u, w.n_users, w.n_cand, w.N, out, stream)
+
+        for _ in range(3):
+            copy()
+            gemm()
+        torch.cuda.synchronize()
+        n_mat = 20
+        t1 = time.perf_counter()
+        for _ in range(n_mat):
+            copy()
+            gemm()
+        torch.cuda.synchronize()
+        extra["materialized_step_us"] = (time.perf_counter() - t1) / n_mat * 1e6
+        ikbo.ikbo_lce_timing(hb, True)
+        for _ in range(n_mat):
+            gemm()
+        torch.cuda.synchronize()
+        _, mat_ms = ikbo.ikbo_lce_timing_read(hb, n_mat)
+        ikbo.ikbo_lce_destroy(hb)
+        extra["materialized_gemm_us"] = float(np.mean(mat_ms)) * 1e3
+        extra["materialized_gemm_tflops"] = f_base / (float(np.mean(mat_ms)) * 1e-3) / 1e12
+        extra["speedup_vs_materialized_step"] = extra["materialized_step_us"] / (ms_per_step * 1e3)
+        del xfull
+    ikbo.ikbo_lce_destroy(h)
+    result = {
+        "metric": LCE_METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs, W scaled by 1/sqrt(K), multinomial candidate-to-user mapping)",
+        "config": {"workload": f"{args.config}: {WORKLOAD_TEXT[args.config]}", "n_cand": w.n_cand,
+                   "n_users": w.n_users, "M": w.M, "K_u": w.K_u, "K_c": w.K_c, "N": w.N, "seed": w.seed},
+        "roofline": roof,
+        "cpu_baseline": None,
+        "extra": extra,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_lce(w, 256, max(3, args.cpu_reps // 3))
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +342,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
                           "launches": args.steps}), flush=True)
+        return
+    if args.config.startswith("lce_"):
+        main_lce(args)
         return
     w = make_workload(args.config)
     dev = upload(w)

@@ -484,7 +484,7 @@ std::map<int, BcastWs*> g_bcast;
 struct Lce {
   int device = -1;
   int32_t M = 0, K_u = 0, K_c = 0, M_pad = 0, K_u_pad = 0, K_c_pad = 0;
-  DevBuf wu, wc, y, errors;
+  DevBuf wu, wc, y, errors, order;
   bool timing = false;
   std::vector<hipEvent_t> tev;  // 4 per timed call: user GEMM start/end, candidate GEMM start/end
   std::vector<char> timed_user;
@@ -495,6 +495,7 @@ struct Lce {
     wc.release();
     y.release();
     errors.release();
+    order.release();
   }
 };
 
@@ -831,7 +832,8 @@ int ikbo_lce_fwd(void* lce, const void* x_user, const void* x_cand, const int32_
     IKBO_HIP(hipGetDevice(&dev));
     if (dev != l->device) return fail(IKBO_ERR_INVALID_ARG, "lce belongs to another device");
     if (n_users < 0 || n_cand < 0) return fail(IKBO_ERR_INVALID_ARG, "n_users and n_cand must be >= 0");
-    if (N < ikbo::kLceTileN || N % ikbo::kLceTileN != 0) return fail(IKBO_ERR_UNSUPPORTED, "N must be a positive multiple of 128");
+    if (N < ikbo::kLceAlignN || N % ikbo::kLceAlignN != 0)
+      return fail(IKBO_ERR_UNSUPPORTED, "N must be a positive multiple of 128");
     if (n_cand == 0) return IKBO_OK;
     if (n_users == 0) return fail(IKBO_ERR_BAD_MAPPING, "candidates present but n_users == 0");
     if (!out || !cand_to_user || (l->K_c > 0 && !x_cand) || (l->K_u > 0 && !x_user))
@@ -844,13 +846,21 @@ int ikbo_lce_fwd(void* lce, const void* x_user, const void* x_cand, const int32_
         overlaps(out, out_bytes, x_cand, static_cast<size_t>(n_cand) * l->K_c * N * 2) ||
         overlaps(out, out_bytes, cand_to_user, static_cast<size_t>(n_cand) * 4))
       return fail(IKBO_ERR_INVALID_ARG, "out aliases an input");
-    const int64_t grid_c = static_cast<int64_t>(n_cand) * (l->M_pad / ikbo::kLceTileM) * (N / ikbo::kLceTileN);
-    const int64_t grid_u = static_cast<int64_t>(n_users) * (l->M_pad / ikbo::kLceTileM) * (N / ikbo::kLceTileN);
+    const int32_t n_tiles = (N + ikbo::kLceTileN - 1) / ikbo::kLceTileN;
+    const int64_t grid_c = static_cast<int64_t>(n_cand) * (l->M_pad / ikbo::kLceTileM) * n_tiles;
+    const int64_t grid_u = static_cast<int64_t>(n_users) * (l->M_pad / ikbo::kLceTileM) * n_tiles;
     if (grid_c > std::numeric_limits<int32_t>::max() || grid_u > std::numeric_limits<int32_t>::max() ||
         static_cast<int64_t>(std::max(n_users, n_cand)) * l->M * N > std::numeric_limits<int32_t>::max() * 8LL)
       return fail(IKBO_ERR_INVALID_ARG, "problem too large");
     int rc;
-    if (l->K_u > 0 && (rc = l->y.ensure(static_cast<size_t>(n_users) * l->M * N * 4, false)) != IKBO_OK) return rc;
+    if (l->K_u > 0 &&
+        (rc = l->y.ensure(static_cast<size_t>(grid_u) * ikbo::kLceYTileFloats * sizeof(float), false)) != IKBO_OK)
+      return rc;
+    if ((rc = l->order.ensure(static_cast<size_t>(n_cand) * 4, false)) != IKBO_OK) return rc;
+    {
+      hipError_t e = ikbo::launch_lce_order(cand_to_user, n_cand, n_users, static_cast<int32_t*>(l->order.ptr), stream);
+      if (e != hipSuccess) return fail_hip(e, "candidate ordering launch");
+    }
     hipEvent_t* te = nullptr;
     if (l->timing && l->n_timed < kMaxTimed) {
       while (l->tev.size() < static_cast<size_t>(4 * (l->n_timed + 1))) {
@@ -867,7 +877,7 @@ int ikbo_lce_fwd(void* lce, const void* x_user, const void* x_cand, const int32_
     p.N = N;
     p.M = l->M;
     p.m_tiles = l->M_pad / ikbo::kLceTileM;
-    p.n_tiles = N / ikbo::kLceTileN;
+    p.n_tiles = n_tiles;
     p.n_users = n_users;
     p.errors = static_cast<int32_t*>(l->errors.ptr);
     if (l->K_u > 0) {  // user GEMM at the user batch
@@ -887,6 +897,7 @@ int ikbo_lce_fwd(void* lce, const void* x_user, const void* x_cand, const int32_
     p.y = l->K_u > 0 ? static_cast<float*>(l->y.ptr) : nullptr;
     p.out = out;
     p.cand_to_user = cand_to_user;
+    p.order = static_cast<const int32_t*>(l->order.ptr);
     hipError_t e = ikbo::launch_lce_gemm(p, 1, n_cand, stream, te ? te + 2 : nullptr);
     if (e != hipSuccess) return fail_hip(e, "candidate GEMM launch");
     return IKBO_OK;

@@ -8,25 +8,38 @@
 namespace ikbo {
 
 // Output tile of one workgroup and the K rows of one ring stage.
-constexpr int kLceTileM = 128;
-constexpr int kLceTileN = 128;
-constexpr int kLceTileK = 64;
+constexpr int kLceTileM = 256;
+constexpr int kLceTileN = 256;
+constexpr int kLceTileK = 32;
+// Floats of user results per output tile.
+constexpr int kLceYTileFloats = kLceTileM * kLceTileN;
+// N must be a multiple of this (a tile's second 128 columns may lie past N).
+constexpr int kLceAlignN = 128;
 
 struct LceParams {
-  const void* w;               // packed W block [m_tiles * 128, ldw] bf16, zero padded
-  int32_t ldw;                 // row stride of the packed block (K padded to 64)
+  const void* w;               // packed W block [m_tiles * kLceTileM, ldw] bf16, zero padded
+  int32_t ldw;                 // row stride of the packed block (K padded to kLceTileK)
   const void* x;               // [batches, K, N] bf16
-  int32_t K, N, M;             // unpadded K of this block, N (multiple of 128), M
-  int32_t m_tiles, n_tiles;    // ceil(M / 128), N / 128
-  float* y;                    // user results [n_users, M, N] fp32 (written by mode 0, read by mode 1; may be null in mode 1)
+  int32_t K, N, M;             // unpadded K of this block, N (multiple of kLceAlignN), M
+  int32_t m_tiles, n_tiles;    // ceil(M / kLceTileM), ceil(N / kLceTileN)
+  float* y;                    // user results, fp32, tile by tile in accumulator order: kLceYTileFloats per
+                               // (user, m tile, n tile); written by mode 0, read by mode 1 (may be null there)
   void* out;                   // mode 1: [batches, M, N] bf16
   const int32_t* cand_to_user; // mode 1: [batches]
   int32_t n_users;
   int32_t* errors;             // mode 1: count of mapping entries outside [0, n_users)
+  const int32_t* order;        // mode 1: batches processed in this order ([batches], a permutation), or null
 };
 
 hipError_t launch_lce_pack(const void* w, int M, int ldw, int K_u, int K_c, int M_pad, int K_u_pad, int K_c_pad,
                            void* wu, void* wc, hipStream_t stream);
+// Users at most the ordering kernel groups (more: identity order).
+constexpr int kLceOrderMaxUsers = 8192;
+// order[0 .. n_cand) = the candidates grouped by user (users ascending, entries
+// outside [0, n_users) last; the order within a user is unspecified).  One
+// workgroup; the order only decides which tiles run together.
+hipError_t launch_lce_order(const int32_t* cand_to_user, int32_t n_cand, int32_t n_users, int32_t* order,
+                            hipStream_t stream);
 // mode 0: y[b] = W . x[b] (fp32); mode 1: out[b] = bf16(W . x[b] + y[cand_to_user[b]]).
 hipError_t launch_lce_gemm(const LceParams& p, int mode, int batches, hipStream_t stream, hipEvent_t* ev = nullptr);
 

@@ -208,8 +208,8 @@ int ikbo_plan_trace_read(void* plan, int64_t* records, int32_t max_items, int32_
  *
  * ikbo_lce_create: packs W (device, bf16 [M, ldw] row-major, user columns
  *   [0, K_u), candidate columns [K_u, K_u + K_c), ldw >= K_u + K_c) into two
- *   library-owned blocks zero-padded to K multiples of 64 and M multiples of
- *   128 (enqueued on `stream`; W may be freed once that work completes).
+ *   library-owned blocks zero-padded to K multiples of 32 and M multiples of
+ *   256 (enqueued on `stream`; W may be freed once that work completes).
  *   M >= 1, K_u >= 0, K_c >= 0, K_u + K_c >= 1.  *lce receives the handle.
  * ikbo_lce_fwd: x_user [n_users, K_u, N], x_cand [n_cand, K_c, N], out
  *   [n_cand, M, N], all bf16 device tensors, 16-byte aligned; cand_to_user is an
