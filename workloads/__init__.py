@@ -7,10 +7,13 @@ path can use it without sharing any of the method's code.
 """
 
 from .ikbo import (  # noqa: F401
+    BWD_SEED_OFFSET,
     CONFIG_NAMES,
     Workload,
+    add_output_grad,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
+    make_bwd_workload,
     make_custom,
     make_workload,
 )

@@ -188,3 +188,24 @@ def make_custom(seed: int, lengths, cand_to_user, n_q: int = 1, H: int = 2, d: i
     """A workload with caller-chosen lengths and mapping (edge cases); values are seeded N(0,1)."""
     rng = np.random.Generator(np.random.PCG64(int(seed)))
     return _assemble(name, int(seed), dtype, rng, lengths, cand_to_user, n_q, H, d, with_self)
+
+
+# Seed offset of the output-gradient stream of a backward workload.
+BWD_SEED_OFFSET = 100
+
+
+def add_output_grad(w: Workload, seed: int) -> Workload:
+    """Adds ``dout``, a seeded N(0,1) output gradient shaped like ``q_cand`` in
+    the workload's dtype, drawn from its own PCG64(seed) stream so that the
+    forward inputs are unchanged."""
+    rng = np.random.Generator(np.random.PCG64(int(seed)))
+    w.tensors["dout"] = _draw_values(rng, w.tensors["q_cand"].shape, w.dtype)
+    return w
+
+
+def make_bwd_workload(name: str) -> Workload:
+    """A forward config's inputs plus an output gradient (seed + BWD_SEED_OFFSET)."""
+    w = make_workload(name)
+    if w.with_self:
+        raise KeyError("the backward covers target attention only")
+    return add_output_grad(w, w.seed + BWD_SEED_OFFSET)
