@@ -23,6 +23,12 @@ from .ikbo import (  # noqa: F401
     ikbo_attn_fwd_planned,
     ikbo_group_csr,
     ikbo_last_error,
+    ikbo_attn_bwd,
+    ikbo_bwd_create,
+    ikbo_bwd_destroy,
+    ikbo_bwd_info,
+    ikbo_bwd_timing,
+    ikbo_bwd_timing_read,
     ikbo_lce_create,
     ikbo_lce_destroy,
     ikbo_lce_errors,

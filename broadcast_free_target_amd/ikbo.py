@@ -58,6 +58,13 @@ SIGNATURES = {
     "ikbo_lce_timing_read": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
                                             _I, _IP]),
     "ikbo_lce_destroy": (None, [_P]),
+    "ikbo_bwd_create": (ctypes.c_int, [ctypes.POINTER(_P)]),
+    "ikbo_attn_bwd": (ctypes.c_int, [_P, _IP, _IP, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "ikbo_bwd_info": (ctypes.c_int, [_P, _LP, _I]),
+    "ikbo_bwd_timing": (ctypes.c_int, [_P, _I]),
+    "ikbo_bwd_timing_read": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
+                                            _I, _IP]),
+    "ikbo_bwd_destroy": (None, [_P]),
 }
 
 _lib = None
@@ -263,3 +270,43 @@ def ikbo_lce_timing_read(lce, max_n: int = 4096):
 
 def ikbo_lce_destroy(lce) -> None:
     load_library().ikbo_lce_destroy(lce)
+
+
+def ikbo_bwd_create() -> int:
+    h = _P()
+    _check(load_library().ikbo_bwd_create(ctypes.byref(h)))
+    return h.value
+
+
+def ikbo_attn_bwd(bwd, user_offsets_host, cand_to_user_host, n_users, n_cand, n_q, H, d, scale, q_cand, k_user,
+                  v_user, out, dout, dq_cand, dk_user, dv_user, stream=None) -> int:
+    """Gradients of target attention; the mapping arrays are host int32 arrays."""
+    offs = np.ascontiguousarray(user_offsets_host, dtype=np.int32)
+    c2u = np.ascontiguousarray(cand_to_user_host, dtype=np.int32)
+    return _check(load_library().ikbo_attn_bwd(
+        bwd, _i32(offs), _i32(c2u) if c2u.size else None, n_users, n_cand, n_q, H, d, float(scale), _ptr(q_cand),
+        _ptr(k_user), _ptr(v_user), _ptr(out), _ptr(dout), _ptr(dq_cand), _ptr(dk_user), _ptr(dv_user),
+        _stream(stream)))
+
+
+def ikbo_bwd_info(bwd) -> dict:
+    a = (ctypes.c_int64 * 2)()
+    _check(load_library().ikbo_bwd_info(bwd, a, 2))
+    return {"dq_items": a[0], "dkv_items": a[1]}
+
+
+def ikbo_bwd_timing(bwd, enable: bool) -> int:
+    return _check(load_library().ikbo_bwd_timing(bwd, 1 if enable else 0))
+
+
+def ikbo_bwd_timing_read(bwd, max_n: int = 4096):
+    """Per-call (dQ kernel, dK/dV kernel) durations in ms of the timed calls."""
+    a = (ctypes.c_float * max(max_n, 1))()
+    b = (ctypes.c_float * max(max_n, 1))()
+    n = ctypes.c_int32(0)
+    _check(load_library().ikbo_bwd_timing_read(bwd, a, b, max_n, ctypes.byref(n)))
+    return list(a[:n.value]), list(b[:n.value])
+
+
+def ikbo_bwd_destroy(bwd) -> None:
+    load_library().ikbo_bwd_destroy(bwd)

@@ -235,6 +235,50 @@ int ikbo_lce_timing_read(void* lce, float* user_ms, float* cand_ms, int32_t max_
 void ikbo_lce_destroy(void* lce);
 
 /*
+ * Backward of IKBO target attention (IKBO blog section 3.1, Fig. 10 for the
+ * forward; section 1.2: the kernels also serve training when candidates
+ * outnumber users).  The forward attends each candidate's n_q query rows over
+ * its user's K/V without copying it per candidate, so the gradient of a user's
+ * K/V is the sum over all its candidates' rows:
+ *   dq_cand = scale * dS K,  dk_user = scale * sum dS^T q,  dv_user = sum P^T dO,
+ * with P the softmax of scale * q k^T (recomputed from the scores and each
+ * row's log-sum-exp, AI-infra guide section 4.6.3), D = rowsum(dout * out) and
+ * dS = P * (dout v^T - D).  Two kernels (the guide's two loop orders; the TLX
+ * jagged-attention post, section 2.2, for the K/V-block-outer tile list): dQ
+ * per row tile, then dK/dV per 128 keys of a user with the reduction over
+ * candidates in registers (no atomics; results are deterministic).
+ *
+ * ikbo_bwd_create: a handle owning the work lists (pinned host memory, two
+ *   alternating buffers) and a device workspace of 4 * (1 + 2H) * (n_cand*n_q
+ *   + 128) bytes.
+ * ikbo_attn_bwd: user_offsets [n_users + 1] and cand_to_user [n_cand] are HOST
+ *   int32 arrays (as an inference or training runtime holds them); the tensors
+ *   are bf16 device arrays, 16-byte aligned, row-major: q_cand, out (the
+ *   forward output), dout, dq_cand [n_cand, n_q, H, d]; k_user, v_user,
+ *   dk_user, dv_user [user_offsets[n_users], H, d].  d must be 128.  Every
+ *   gradient element is written: users with no candidates get zero dk/dv
+ *   rows, candidates of users with no keys zero dq rows.  Enqueues two kernels
+ *   on `stream` and returns without synchronising (it may wait for the call
+ *   before last on the same handle to finish reading its work list).  Errors
+ *   (INVALID_ARG: null or misaligned tensors, gradients aliasing inputs or
+ *   each other, bad sizes; BAD_OFFSETS; BAD_MAPPING; UNSUPPORTED: d != 128)
+ *   launch nothing.  Calls on one handle must be ordered on one stream.
+ * ikbo_bwd_info: info[0] dQ work items, info[1] dK/dV work items of the last call.
+ * ikbo_bwd_timing / _timing_read: per-call durations of the two kernels from
+ *   events stamped by their dispatches (at most 4096 calls between resets).
+ * ikbo_bwd_destroy: frees the handle after synchronising its device.
+ */
+int ikbo_bwd_create(void** bwd);
+int ikbo_attn_bwd(void* bwd, const int32_t* user_offsets, const int32_t* cand_to_user, int32_t n_users,
+                  int32_t n_cand, int32_t n_q, int32_t H, int32_t d, float scale, const void* q_cand,
+                  const void* k_user, const void* v_user, const void* out, const void* dout, void* dq_cand,
+                  void* dk_user, void* dv_user, void* stream);
+int ikbo_bwd_info(void* bwd, int64_t* info, int32_t n_info);
+int ikbo_bwd_timing(void* bwd, int32_t enable);
+int ikbo_bwd_timing_read(void* bwd, float* dq_ms, float* dkv_ms, int32_t max_n, int32_t* n);
+void ikbo_bwd_destroy(void* bwd);
+
+/*
  * Introspection of a built plan (host values), for tests and measurement:
  * info[0] work items, [1] grid of the persistent launch, [2] split groups,
  * [3] partial-result slots, [4] bytes of the split-KV workspace, [5] target
