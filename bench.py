@@ -41,10 +41,14 @@ WORKLOAD_TEXT = {
     "c4_large": "large: 10000 candidates over 150 users, L~U[512,4096], n_q=4, H=8, d=128, bf16",
     "c5_fused": "fused self+target: 2048 candidates over 30 users, causal self over L~U[256,2048], H=4, d=128, bf16",
     "p_app11": "App. 11 shape: 32 users x 64 candidates, n_q=64, L=1024, H=2, d=128, bf16",
+    "bwd_c2_typical": "backward of the typical request: 1024 candidates over 15 users, L~U[256,2048], n_q=1, H=4, d=128, bf16",
+    "bwd_c4_large": "backward of the large request: 10000 candidates over 150 users, L~U[512,4096], n_q=4, H=8, d=128, bf16",
     "lce_typical": "linear compression: 1024 candidates over 15 users, M=433, K_u=K_c=1022, N=256, bf16",
     "lce_ratio1000": "linear compression: 2000 candidates over 2 users, M=433, K_u=K_c=1022, N=256, bf16",
 }
 LCE_METRIC = "IKBO linear compression BF16 TFLOP/s (executed work) and FLOPs vs materialized broadcast"
+BWD_METRIC = "IKBO attn backward BF16 TFLOP/s (five products: S, dP, dV, dK, dQ)"
+BWD_KERNELS = ("ikbo_bwd_dq_kernel", "ikbo_bwd_dkv_kernel")
 LCE_KERNEL = "ikbo_lce_gemm_kernel<1>"  # candidate GEMM with the broadcast-add epilogue
 
 
@@ -81,6 +85,27 @@ def lce_counts(w):
     return f_user, f_cand, b_user, b_cand, f_base, b_base
 
 
+def bwd_counts(w):
+    """Algorithmic FLOPs and HBM bytes of one backward call, whole and per kernel.
+
+    FLOPs: 2 per multiply-add, softmax not counted; per (candidate row, head,
+    key) the five products S, dP, dV, dK, dQ take 2*d each.  The dQ kernel
+    must form S, dP and dQ; the dK/dV kernel S, dP, dV and dK.
+    Bytes (bf16): dQ kernel reads Q, O, dO and the user's K and V once per
+    (user, head), writes dQ; dK/dV kernel reads K, V, Q and dO once, writes dK
+    and dV (per-row statistics, 8 bytes per row and head, are counted too).
+    """
+    L = w.lengths.astype(np.float64)
+    cnt = w.counts.astype(np.float64)
+    per = 2.0 * w.d * w.H * w.n_q * float(np.dot(cnt, L))   # one product over all rows and keys
+    rows = float(w.n_cand * w.n_q)
+    act = 2.0 * w.H * w.d                                   # bytes of one row (all heads)
+    kv_users = float(np.sum(L[cnt > 0]))                      # keys of users that have candidates
+    b_dq = act * (4.0 * rows + 2.0 * kv_users) + 8.0 * rows * w.H
+    b_dkv = act * (2.0 * rows + 4.0 * w.total_len) + 8.0 * rows * w.H
+    return 5.0 * per, 3.0 * per, 4.0 * per, b_dq, b_dkv
+
+
 def kernel_source_hash(files=("ikbo_kernels.hip", "ikbo_kernels.h", "ikbo_device.h", "ikbo_plan.cpp",
                               "ikbo_plan.h", "ikbo_api.hip")):
     h = hashlib.sha256()
@@ -91,20 +116,25 @@ def kernel_source_hash(files=("ikbo_kernels.hip", "ikbo_kernels.h", "ikbo_device
 
 
 LCE_SOURCES = ("ikbo_lce.hip", "ikbo_lce.h", "ikbo_device.h", "ikbo_api.hip")
+BWD_SOURCES = ("ikbo_bwd.hip", "ikbo_bwd.h", "ikbo_device.h", "ikbo_plan.cpp", "ikbo_api.hip")
 
 
 def traffic_from_profiles(workload):
     """Per-launch HBM bytes from the committed rocprofv3 --pmc summary, if it
     was taken on the current kernel sources; else None."""
     lce = workload.startswith("lce_")
-    name = f"ikbo_lce_gemm_{workload}_pmc.json" if lce else f"ikbo_attn_bf16_{workload}_pmc.json"
+    bwd = workload.startswith("bwd_")
+    name = (f"ikbo_lce_gemm_{workload}_pmc.json" if lce else f"ikbo_bwd_{workload}_pmc.json" if bwd
+            else f"ikbo_attn_bf16_{workload}_pmc.json")
     path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     try:
         with open(path) as fh:
             s = json.load(fh)
-        if s.get("kernel_source_hash") != (kernel_source_hash(LCE_SOURCES) if lce else kernel_source_hash()):
+        want = (kernel_source_hash(LCE_SOURCES) if lce else kernel_source_hash(BWD_SOURCES) if bwd
+                else kernel_source_hash())
+        if s.get("kernel_source_hash") != want:
             return None
         return float(s["hbm_bytes_per_launch"])
     except Exception:
@@ -174,6 +204,114 @@ def cpu_baseline_lce(w, n_sample, reps):
                       f"per-candidate concatenation, median of {reps} runs of {t:.2f} s, scaled to the whole batch "
                       f"and counted in the same executed FLOPs as the GPU value",
             "seconds_whole_batch": t_whole, "cands_per_s": w.n_cand / t_whole}
+
+
+def cpu_baseline_bwd(w, n_sample, reps):
+    """The fp64 backward oracle on the first n_sample candidates (all keys of
+    their users), scaled to the whole batch by candidate count."""
+    from oracle import ikbo_bwd_oracle as B
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    sel = np.arange(min(n_sample, w.n_cand))
+    q, do = w.values("q_cand")[sel], w.values("dout")[sel]
+    k, v = w.values("k_user"), w.values("v_user")
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        B.target_attention_bwd(q, k, v, do, w.user_offsets, w.cand_to_user[sel], w.scale)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    flops = bwd_counts(w)[0]
+    t_whole = t * w.n_cand / len(sel)
+    return {"value": flops / t_whole / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {len(sel)} of {w.n_cand} candidates of {w.name}, fp64 numpy with explicit per-candidate "
+                      f"K/V copies, median of {reps} runs of {t:.2f} s, scaled to the whole batch",
+            "seconds_whole_batch": t_whole}
+
+
+def main_bwd(args):
+    """One step = one ikbo_attn_bwd call: host grouping and work lists from the
+    host mapping, the dQ kernel and the dK/dV kernel.  The forward output it
+    consumes is produced once, before timing, by the forward path."""
+    import torch
+    import broadcast_free_target_amd as ikbo
+    from workloads import make_bwd_workload
+
+    cfg = args.config[len("bwd_"):]
+    w = make_bwd_workload(cfg)
+    dev = upload(w)
+    out = torch.empty_like(dev["q_cand"])
+    stream = torch.cuda.current_stream()
+    ikbo.ikbo_attn_fwd_ex(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"], dev["cand_to_user"],
+                          w.n_users, w.n_cand, w.n_q, w.H, w.d, w.scale, ikbo.IKBO_DTYPE_BF16, out, stream)
+    dq = torch.empty_like(dev["q_cand"])
+    dk = torch.empty_like(dev["k_user"])
+    dv = torch.empty_like(dev["v_user"])
+    offs_h = np.ascontiguousarray(w.user_offsets, dtype=np.int32)
+    c2u_h = np.ascontiguousarray(w.cand_to_user, dtype=np.int32)
+    h = ikbo.ikbo_bwd_create()
+
+    def step():
+        ikbo.ikbo_attn_bwd(h, offs_h, c2u_h, w.n_users, w.n_cand, w.n_q, w.H, w.d, w.scale, dev["q_cand"],
+                           dev["k_user"], dev["v_user"], out, dev["dout"], dq, dk, dv, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ikbo.ikbo_bwd_timing(h, True)
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    dq_ms, dkv_ms = ikbo.ikbo_bwd_timing_read(h, K)
+    ikbo.ikbo_bwd_timing(h, False)
+    info = ikbo.ikbo_bwd_info(h)
+    ikbo.ikbo_bwd_destroy(h)
+    a_ms, b_ms = float(np.mean(dq_ms)), float(np.mean(dkv_ms))
+
+    f_all, f_dq, f_dkv, b_dq, b_dkv = bwd_counts(w)
+    ms_per_step = wall * 1e3 / K
+    value = f_all / (ms_per_step * 1e-3) / 1e12
+    dom = 0 if a_ms >= b_ms else 1
+    f_k, b_k, t_k = (f_dq, b_dq, a_ms) if dom == 0 else (f_dkv, b_dkv, b_ms)
+    if f_k / b_k < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        achieved = b_k / (t_k * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS}
+    else:
+        achieved = f_k / (t_k * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS}
+    roof["traffic"] = traffic_from_profiles(args.config)
+    roof["kernel"] = BWD_KERNELS[dom]
+    roof["kernel_avg_us"] = t_k * 1e3
+    roof["algorithmic_bytes_per_launch"] = b_k
+    roof["algorithmic_flops_per_launch"] = f_k
+    extra = {
+        "dq_kernel_us": a_ms * 1e3, "dkv_kernel_us": b_ms * 1e3,
+        "dq_kernel_tflops": f_dq / (a_ms * 1e-3) / 1e12, "dkv_kernel_tflops": f_dkv / (b_ms * 1e-3) / 1e12,
+        "dq_kernel_hbm_gbs": b_dq / (a_ms * 1e-3) / 1e9, "dkv_kernel_hbm_gbs": b_dkv / (b_ms * 1e-3) / 1e9,
+        "kernels_tflops": f_all / ((a_ms + b_ms) * 1e-3) / 1e12,
+        "work_items": info, "backward_flops": f_all, "forward_flops": w.flops()["target"],
+    }
+    result = {
+        "metric": BWD_METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs and output gradient, jagged lengths and mappings drawn per config)",
+        "config": {"workload": f"{args.config}: {WORKLOAD_TEXT[args.config]}", "n_cand": w.n_cand,
+                   "n_users": w.n_users, "n_q": w.n_q, "H": w.H, "d": w.d, "total_len": w.total_len, "seed": w.seed},
+        "roofline": roof, "cpu_baseline": None, "extra": extra,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_bwd(w, 24 if w.n_cand > 2000 else 128, 3)
+    print(json.dumps(result), flush=True)
 
 
 def main_lce(args):
@@ -360,6 +498,9 @@ def main():
         return
     if args.config.startswith("lce_"):
         main_lce(args)
+        return
+    if args.config.startswith("bwd_"):
+        main_bwd(args)
         return
     w = make_workload(args.config)
     dev = upload(w)
