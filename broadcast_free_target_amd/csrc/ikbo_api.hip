@@ -511,10 +511,13 @@ struct Bwd {
   hipEvent_t stage_ev[2] = {nullptr, nullptr};
   bool stage_used[2] = {false, false};
   int next = 0;
-  DevBuf ws;  // qrow [R + pad] int32, then lse and dd [H][R + pad] fp32
-  std::vector<int32_t> counts, cand_offsets, cand_perm, tiles, cursor;
-  std::vector<WorkItem> items_a, items_b;
-  int64_t n_items_a = 0, n_items_b = 0;
+  int n_cu = 0;
+  DevBuf ws;              // qrow [R + pad] int32, then lse and dd [H][R + pad] fp32
+  DevBuf ws_dq, ws_rec;   // split dQ partials and their row records
+  DevBuf ws_rows;         // Q and dO rows in user-sorted order, per head (zeroed padding)
+  HostPlan hp;            // dQ work items (the forward's planner) and the CSR grouping
+  std::vector<WorkItem> items_b;
+  int64_t n_items_a = 0, n_items_b = 0, n_groups = 0;
   bool timing = false;
   std::vector<hipEvent_t> tev;  // 4 per timed call: dQ kernel start/end, dK/dV kernel start/end
   int n_timed = 0;
@@ -525,6 +528,9 @@ struct Bwd {
       stage[i].release();
     }
     ws.release();
+    ws_dq.release();
+    ws_rec.release();
+    ws_rows.release();
   }
 };
 
@@ -991,6 +997,7 @@ int ikbo_bwd_create(void** bwd) {
     Bwd* b = new (std::nothrow) Bwd();
     if (!b) return fail(IKBO_ERR_NOMEM, "bwd allocation");
     hipError_t e = hipGetDevice(&b->device);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&b->n_cu, hipDeviceAttributeMultiprocessorCount, b->device);
     for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&b->stage_ev[i], hipEventDisableTiming);
     if (e != hipSuccess) {
       delete b;
@@ -1021,12 +1028,15 @@ int ikbo_attn_bwd(void* bwd, const int32_t* user_offsets, const int32_t* cand_to
     int rc = ikbo::check_offsets(user_offsets, n_users, &err);
     if (rc != ikbo::kOk) return fail(rc, err);
     const int64_t T = n_users > 0 ? user_offsets[n_users] : 0;
-    b->counts.resize(std::max(n_users, 1));
-    b->cand_offsets.resize(n_users + 1);
-    b->cand_perm.resize(std::max(n_cand, 1));
-    int64_t n_tiles = 0;
-    rc = ikbo::group_csr(cand_to_user, n_cand, n_users, n_q, ikbo::kBwdRowsA, b->counts.data(), b->cand_offsets.data(),
-                         b->cand_perm.data(), &b->tiles, &n_tiles, &err, &b->cursor);
+    // dQ items: the forward's work list (row tiles of every user and head, long
+    // key ranges split into chunks, longest first) and its CSR grouping.
+    PlanParams pp;
+    pp.bm = ikbo::kBwdRowsA;
+    pp.bn = ikbo::kBwdKeysA;
+    pp.grid_slots = std::max(1, 2 * b->n_cu);
+    pp.min_chunk = 256;
+    pp.allow_split = static_cast<int64_t>(n_cand) * n_q < ikbo::kBwdMaxSplitRows && !env_int("IKBO_NO_SPLIT", 0);
+    rc = ikbo::build_plan(user_offsets, cand_to_user, n_users, n_cand, n_q, H, false, pp, &b->hp, &err);
     if (rc != ikbo::kOk) return fail(rc, err);
     if (T == 0) return IKBO_OK;  // no keys: no gradient to write (and every query gradient row would be empty)
     const int64_t R = static_cast<int64_t>(n_cand) * n_q;
@@ -1049,25 +1059,6 @@ int ikbo_attn_bwd(void* bwd, const int32_t* user_offsets, const int32_t* cand_to
       for (int j = i + 1; j < 3; ++j)
         if (out_sz[j] && overlaps(outs[i], out_sz[i], outs[j], out_sz[j])) return fail(IKBO_ERR_INVALID_ARG, "gradients overlap");
     }
-    // dQ items: the CSR row tiles of every user and head, longest key range first.
-    b->items_a.clear();
-    for (int64_t t = 0; t < n_tiles; ++t) {
-      const int32_t u = b->tiles[3 * t], row0 = b->tiles[3 * t + 1], len = b->tiles[3 * t + 2];
-      for (int32_t h = 0; h < H; ++h) {
-        WorkItem w{};
-        w.kv_base = user_offsets[u];
-        w.row_base = b->cand_offsets[u];
-        w.row0 = row0;
-        w.nrows = len;
-        w.k0 = 0;
-        w.k1 = user_offsets[u + 1] - user_offsets[u];
-        w.h = h;
-        w.grp = -1;
-        b->items_a.push_back(w);
-      }
-    }
-    std::stable_sort(b->items_a.begin(), b->items_a.end(),
-                     [](const WorkItem& x, const WorkItem& y) { return x.k1 - x.k0 > y.k1 - y.k0; });
     // dK/dV items: every kBwdKeysB keys of every user and head, most rows first.
     b->items_b.clear();
     for (int32_t u = 0; u < n_users; ++u) {
@@ -1076,9 +1067,9 @@ int ikbo_attn_bwd(void* bwd, const int32_t* user_offsets, const int32_t* cand_to
         for (int32_t k0 = 0; k0 < L; k0 += ikbo::kBwdKeysB) {
           WorkItem w{};
           w.kv_base = user_offsets[u];
-          w.row_base = b->cand_offsets[u];
+          w.row_base = b->hp.cand_offsets[u];
           w.row0 = 0;
-          w.nrows = b->counts[u] * n_q;
+          w.nrows = b->hp.counts[u] * n_q;
           w.k0 = k0;
           w.k1 = std::min(L, k0 + ikbo::kBwdKeysB);
           w.h = h;
@@ -1088,15 +1079,24 @@ int ikbo_attn_bwd(void* bwd, const int32_t* user_offsets, const int32_t* cand_to
     }
     std::stable_sort(b->items_b.begin(), b->items_b.end(),
                      [](const WorkItem& x, const WorkItem& y) { return x.nrows > y.nrows; });
-    const int64_t na = static_cast<int64_t>(b->items_a.size()), nb = static_cast<int64_t>(b->items_b.size());
+    const int64_t na = static_cast<int64_t>(b->hp.items.size()), nb = static_cast<int64_t>(b->items_b.size());
     if (na > std::numeric_limits<int32_t>::max() || nb > std::numeric_limits<int32_t>::max() ||
         R + ikbo::kBwdPad > std::numeric_limits<int32_t>::max())
       return fail(IKBO_ERR_INVALID_ARG, "problem too large");
     b->n_items_a = na;
     b->n_items_b = nb;
+    b->n_groups = b->hp.n_groups;
     // workspace
     const size_t rp = static_cast<size_t>(R + ikbo::kBwdPad);
     if ((rc = b->ws.ensure(rp * 4 * (1 + 2 * static_cast<size_t>(H)), false)) != IKBO_OK) return rc;
+    // Sorted Q and dO copies, zero-filled when allocated: the padding rows the
+    // dK/dV kernel may read hold zeros or rows of an earlier call, finite either way.
+    const size_t rows_bytes = static_cast<size_t>(H) * rp * ikbo::kBwdHeadDim * 2;
+    if ((rc = b->ws_rows.ensure(2 * rows_bytes, true)) != IKBO_OK) return rc;
+    const size_t slot_rows = static_cast<size_t>(b->hp.n_slots) * ikbo::kBwdRowsA;
+    if (slot_rows > 0 && ((rc = b->ws_dq.ensure(slot_rows * ikbo::kBwdHeadDim * 4, false)) != IKBO_OK ||
+                          (rc = b->ws_rec.ensure(slot_rows * 16, false)) != IKBO_OK))
+      return rc;
     // work lists into the next pinned buffer, once its last reader is done
     const size_t items_bytes = static_cast<size_t>(na + nb) * sizeof(WorkItem);
     const size_t bytes = items_bytes + static_cast<size_t>(std::max(n_cand, 1)) * 4;
@@ -1105,9 +1105,9 @@ int ikbo_attn_bwd(void* bwd, const int32_t* user_offsets, const int32_t* cand_to
     if (b->stage_used[si]) IKBO_HIP(hipEventSynchronize(b->stage_ev[si]));
     if ((rc = b->stage[si].ensure(bytes)) != IKBO_OK) return rc;
     char* base = static_cast<char*>(b->stage[si].ptr);
-    std::memcpy(base, b->items_a.data(), static_cast<size_t>(na) * sizeof(WorkItem));
+    std::memcpy(base, b->hp.items.data(), static_cast<size_t>(na) * sizeof(WorkItem));
     std::memcpy(base + na * sizeof(WorkItem), b->items_b.data(), static_cast<size_t>(nb) * sizeof(WorkItem));
-    if (n_cand > 0) std::memcpy(base + items_bytes, b->cand_perm.data(), static_cast<size_t>(n_cand) * 4);
+    if (n_cand > 0) std::memcpy(base + items_bytes, b->hp.cand_perm.data(), static_cast<size_t>(n_cand) * 4);
     hipEvent_t* te = nullptr;
     if (b->timing && b->n_timed < kMaxTimed) {
       while (b->tev.size() < static_cast<size_t>(4 * (b->n_timed + 1))) {
@@ -1131,14 +1131,22 @@ int ikbo_attn_bwd(void* bwd, const int32_t* user_offsets, const int32_t* cand_to
     p.qrow = static_cast<int32_t*>(b->ws.ptr);
     p.lse = reinterpret_cast<float*>(p.qrow + rp);
     p.dd = p.lse + rp * H;
+    p.qs = static_cast<uint16_t*>(b->ws_rows.ptr);
+    p.dos = p.qs + rows_bytes / 2;
+    p.ws_dq = static_cast<float*>(b->ws_dq.ptr);
+    p.ws_rec = static_cast<float*>(b->ws_rec.ptr);
     p.rows_total = static_cast<int32_t>(R);
     p.H = H;
     p.n_q = n_q;
     p.scale = scale;
     p.scale_log2 = scale * 1.4426950408889634f;
     p.items = reinterpret_cast<const WorkItem*>(base);
-    hipError_t e = ikbo::launch_bwd_dq(p, static_cast<int>(na), stream, te);
+    // timing: the dQ span runs from the dQ kernel's start to the merge's end
+    hipEvent_t ev_dq[2] = {te ? te[0] : nullptr, te && b->n_groups == 0 ? te[1] : nullptr};
+    hipError_t e = ikbo::launch_bwd_dq(p, static_cast<int>(na), stream, te ? ev_dq : nullptr);
     if (e != hipSuccess) return fail_hip(e, "dQ launch");
+    e = ikbo::launch_bwd_merge(p, static_cast<int>(b->n_groups), stream, te ? te[1] : nullptr);
+    if (e != hipSuccess) return fail_hip(e, "dQ merge launch");
     p.items = reinterpret_cast<const WorkItem*>(base) + na;
     e = ikbo::launch_bwd_dkv(p, static_cast<int>(nb), stream, te ? te + 2 : nullptr);
     if (e != hipSuccess) return fail_hip(e, "dK/dV launch");
@@ -1153,8 +1161,8 @@ int ikbo_attn_bwd(void* bwd, const int32_t* user_offsets, const int32_t* cand_to
 int ikbo_bwd_info(void* bwd, int64_t* info, int32_t n_info) {
   if (!bwd || !info || n_info < 0) return fail(IKBO_ERR_INVALID_ARG, "null argument");
   Bwd* b = static_cast<Bwd*>(bwd);
-  const int64_t v[2] = {b->n_items_a, b->n_items_b};
-  for (int i = 0; i < std::min<int32_t>(n_info, 2); ++i) info[i] = v[i];
+  const int64_t v[3] = {b->n_items_a, b->n_items_b, b->n_groups};
+  for (int i = 0; i < std::min<int32_t>(n_info, 3); ++i) info[i] = v[i];
   return IKBO_OK;
 }
 

@@ -34,6 +34,16 @@ struct BwdParams {
   int32_t* qrow;        // [R + pad] row index cand * n_q + query
   float* lse;           // [H][R + pad] base-2 log-sum-exp of the row's scores
   float* dd;            // [H][R + pad] rowsum(dO * O)
+  // Split dQ items (grp >= 0) leave partials in slots: per slot 128 rows x d
+  // fp32 dQ against the chunk's own log-sum-exp, and per row one 16-byte record
+  // {lse_c, D, output unit qrow * H + h (or -1: no row), srow | nchunk << 27}.
+  float* ws_dq;
+  float* ws_rec;
+  // Q and dO rows in user-sorted order, per head: [H][R + pad][d] bf16, written by
+  // the dQ kernel, read by the dK/dV kernel as contiguous row tiles.  The
+  // padding rows are zero (never written).
+  uint16_t* qs;
+  uint16_t* dos;
   int32_t rows_total;   // R = n_cand * n_q
   int32_t H;
   int32_t n_q;
@@ -42,8 +52,16 @@ struct BwdParams {
 };
 
 // dQ (and the per-row log-sum-exp and D): one workgroup per item
-// (kv_base, row_base = cand_offsets[u], row0, nrows <= kBwdRowsA, k0 = 0, k1 = L_u, h).
+// (kv_base, row_base = cand_offsets[u], row0, nrows <= kBwdRowsA, key range
+// [k0, k1), h, split group grp or -1, chunk, nchunk, slot0), the forward's
+// work items.  ev (optional): ev[0] is stamped at the kernel's start, ev[1] at
+// its end unless null.
 hipError_t launch_bwd_dq(const BwdParams& p, int n_items, hipStream_t stream, hipEvent_t* ev = nullptr);
+// Folds the split dQ partials of groups 0 .. n_groups-1 and writes dQ and the
+// rows' log-sum-exp, D and row index.  ev_stop (optional) is stamped at its end.
+hipError_t launch_bwd_merge(const BwdParams& p, int n_groups, hipStream_t stream, hipEvent_t ev_stop = nullptr);
+// Largest sorted-row index the split records can hold (srow < 2^27).
+constexpr int64_t kBwdMaxSplitRows = int64_t(1) << 27;
 // dK and dV: one workgroup per item (kv_base, row_base, row0 = 0, nrows = all
 // rows of the user, [k0, k1) <= kBwdKeysB keys, h).
 hipError_t launch_bwd_dkv(const BwdParams& p, int n_items, hipStream_t stream, hipEvent_t* ev = nullptr);

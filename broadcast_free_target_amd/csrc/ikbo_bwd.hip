@@ -13,11 +13,18 @@
 // blocks outside and query rows inside, from a host-built tile list):
 //
 //   dQ kernel   one workgroup (4 wave64 x 32 rows) per CSR row tile of one
-//               (user, head).  Pass 1 streams the user's K tiles and forms each
-//               row's base-2 log-sum-exp; pass 2 streams K and V, rebuilds
-//               P^T = exp2(S^T - lse), dP^T = V dO^T and dS^T, and accumulates
-//               dQ^T = K^T dS^T.  It also writes, per row in user-sorted order,
-//               the row index, the log-sum-exp and D for the second kernel.
+//               (user, head) and key chunk (long key ranges are split as in
+//               the forward).  Pass 1 streams the chunk's K tiles and forms each
+//               row's base-2 log-sum-exp over the chunk; pass 2 streams K and
+//               V, rebuilds P^T = exp2(S^T - lse), dP^T = V dO^T and dS^T, and
+//               accumulates dQ^T = K^T dS^T.  D = rowsum(dO * O) needs no keys,
+//               so every chunk has it.  An unsplit item writes dQ and, per row
+//               in user-sorted order, the row index, the log-sum-exp and D for
+//               the second kernel; a split item leaves its dQ and log-sum-exp
+//               in a slot and the merge kernel combines the chunks,
+//                   lse = log2 sum_c 2^lse_c,  dQ = scale * sum_c 2^(lse_c - lse) dQ_c,
+//               in chunk order (the log-sum-exp merge of the AI-infra guide,
+//               section 4.6.4, applied to gradients), then writes the same rows.
 //   dK/dV kernel  one workgroup (4 wave64 x 32 keys) per 128 keys of one
 //               (user, head); K and V fragments stay in registers while the
 //               user's candidate rows stream through LDS in 64-row tiles:
@@ -80,6 +87,10 @@ __device__ __forceinline__ bf16x8_t pack8(const f32x16_t& x, int base) {
   return as_bf16x8(r);
 }
 
+// 2^x with the hardware instruction (no denormal range handling: softmax
+// weights below 2^-126 flush to zero).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // A operand of a product that contracts over tile rows, matching a B operand
 // taken from accumulator values v = 8*j0 .. 8*j0+7 of a 32-row block: those
 // values belong to rows K0..K0+3 and K0+8..K0+11 with K0 = block + 16*j0 + 4*g.
@@ -122,7 +133,7 @@ __global__ __launch_bounds__(kNT, 2) void ikbo_bwd_dq_kernel(BwdParams P) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, g = lane >> 5, kq = lane & 15, half = (lane >> 4) & 1;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int L = it.k1 - it.k0;
+  const int L = it.k1 - it.k0;  // keys of this item, from it.k0
   const int64_t rs = static_cast<int64_t>(P.H) * D;
   const int rloc = wave * 32 + n;
   const bool row_ok = rloc < it.nrows;
@@ -151,13 +162,25 @@ __global__ __launch_bounds__(kNT, 2) void ikbo_bwd_dq_kernel(BwdParams P) {
     }
   }
   dsum += __shfl_xor(dsum, 32);
+  // Sorted copies of the rows for the dK/dV kernel (one chunk per row writes).
+  const int64_t srow = static_cast<int64_t>(it.row_base) * P.n_q + r;
+  if (row_ok && (it.grp < 0 || it.chunk == 0)) {
+    const int64_t so = (static_cast<int64_t>(it.h) * (P.rows_total + kBwdPad) + srow) * D + g * 8;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      *reinterpret_cast<u32x4_t*>(P.qs + so + ks * 16) = qf[ks];
+      *reinterpret_cast<u32x4_t*>(P.dos + so + ks * 16) = df[ks];
+    }
+  }
   // The row loads are complete before the ring starts, so the compiler has no
   // load of its own to wait for inside the loops.
   wait_vmcnt<0>();
 
   const uint32_t lds_base = lds_address(smem);
-  const uint16_t* kg = static_cast<const uint16_t*>(P.k) + static_cast<int64_t>(it.kv_base) * rs + it.h * D;
-  const uint16_t* vg = static_cast<const uint16_t*>(P.v) + static_cast<int64_t>(it.kv_base) * rs + it.h * D;
+  const uint16_t* kg =
+      static_cast<const uint16_t*>(P.k) + (static_cast<int64_t>(it.kv_base) + it.k0) * rs + it.h * D;
+  const uint16_t* vg =
+      static_cast<const uint16_t*>(P.v) + (static_cast<int64_t>(it.kv_base) + it.k0) * rs + it.h * D;
   const int ntiles = (L + KT - 1) / KT;
   auto issue = [&](int t, bool with_v) {
     const uint32_t st = lds_base + static_cast<uint32_t>((t & 1) * 2 * TE * 2);
@@ -204,9 +227,9 @@ __global__ __launch_bounds__(kNT, 2) void ikbo_bwd_dq_kernel(BwdParams P) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sum += exp2f(s[kb][v] - mn);
+        for (int v = 0; v < 16; ++v) sum += exp2_hw(s[kb][v] - mn);
       sum += __shfl_xor(sum, 32);
-      l = l * exp2f(m - mn) + sum;
+      l = l * exp2_hw(m - mn) + sum;
       m = mn;
     }
     __syncthreads();
@@ -237,7 +260,7 @@ __global__ __launch_bounds__(kNT, 2) void ikbo_bwd_dq_kernel(BwdParams P) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = t * KT + kb * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
-          const float p = key < L ? exp2f(s[kb][v] * c2 - lse) : 0.0f;
+          const float p = key < L ? exp2_hw(s[kb][v] * c2 - lse) : 0.0f;
           s[kb][v] = p * (dp[kb][v] - dsum);  // dS^T
         }
 #pragma unroll
@@ -255,6 +278,26 @@ __global__ __launch_bounds__(kNT, 2) void ikbo_bwd_dq_kernel(BwdParams P) {
   }
 
   // dQ^T block db: lane value v is d = db*32 + (v/4)*8 + 4*g + v%4 of row n.
+  if (it.grp >= 0) {
+    // split: the unscaled partial against this chunk's log-sum-exp, one record per tile row
+    const int64_t slot_row = (static_cast<int64_t>(it.slot0) + it.chunk) * kBwdRowsA + rloc;
+    if (row_ok) {
+      float* pd = P.ws_dq + slot_row * D;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<f32x4_t*>(pd + db * 32 + q4 * 8 + g * 4) =
+              f32x4_t{dqa[db][q4 * 4 + 0], dqa[db][q4 * 4 + 1], dqa[db][q4 * 4 + 2], dqa[db][q4 * 4 + 3]};
+    }
+    if (g == 0) {
+      const int unit = row_ok ? static_cast<int>(qrow * P.H + it.h) : -1;
+      const int tag = row_ok ? static_cast<int>(srow | (static_cast<int64_t>(it.nchunk) << 27)) : 0;
+      *reinterpret_cast<f32x4_t*>(P.ws_rec + slot_row * 4) =
+          f32x4_t{lse, dsum, __builtin_bit_cast(float, unit), __builtin_bit_cast(float, tag)};
+    }
+    return;
+  }
   if (row_ok) {
     uint16_t* dq = static_cast<uint16_t*>(P.dq) + qoff;
 #pragma unroll
@@ -265,12 +308,63 @@ __global__ __launch_bounds__(kNT, 2) void ikbo_bwd_dq_kernel(BwdParams P) {
             pack4_bf16(P.scale * dqa[db][q4 * 4 + 0], P.scale * dqa[db][q4 * 4 + 1], P.scale * dqa[db][q4 * 4 + 2],
                        P.scale * dqa[db][q4 * 4 + 3]);
     if (g == 0) {
-      const int64_t srow = static_cast<int64_t>(it.row_base) * P.n_q + r;
       const int64_t hb = static_cast<int64_t>(it.h) * (P.rows_total + kBwdPad);
       P.lse[hb + srow] = lse;
       P.dd[hb + srow] = dsum;
       if (it.h == 0) P.qrow[srow] = static_cast<int32_t>(qrow);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// merge of split dQ partials: block (group, 8 rows); thread -> (row, 4 d)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void ikbo_bwd_merge_kernel(BwdParams P) {
+  constexpr int TPR = D / 4;      // threads per row
+  constexpr int RPB = 256 / TPR;  // rows per block
+  const int r = blockIdx.y * RPB + threadIdx.x / TPR;
+  const int d0 = (threadIdx.x % TPR) * 4;
+  const int64_t slot0 = static_cast<int64_t>(blockIdx.x) * kMaxSplit;
+  // Records of every slot of the group at once (slots past nchunk are stale and
+  // ignored), then the partials of the live chunks.
+  f32x4_t rec[kMaxSplit];
+#pragma unroll
+  for (int ch = 0; ch < kMaxSplit; ++ch)
+    rec[ch] = *reinterpret_cast<const f32x4_t*>(P.ws_rec + ((slot0 + ch) * kBwdRowsA + r) * 4);
+  // Fields are copied out of the vector before the bit cast (clang reads a bit
+  // cast of a vector element as a cast of element 0).
+  const float unit_f = rec[0][2], tag_f = rec[0][3];
+  const int unit = __builtin_bit_cast(int, unit_f);
+  const int tag = __builtin_bit_cast(int, tag_f);
+  if (unit < 0) return;
+  const int nchunk = tag >> 27;
+  const int64_t srow = tag & ((1 << 27) - 1);
+  f32x4_t o[kMaxSplit];
+#pragma unroll
+  for (int ch = 0; ch < kMaxSplit; ++ch)
+    if (ch < nchunk) o[ch] = *reinterpret_cast<const f32x4_t*>(P.ws_dq + ((slot0 + ch) * kBwdRowsA + r) * D + d0);
+  float mx = rec[0][0];
+#pragma unroll
+  for (int ch = 1; ch < kMaxSplit; ++ch)
+    if (ch < nchunk) mx = fmaxf(mx, rec[ch][0]);
+  float sum = 0.0f;
+#pragma unroll
+  for (int ch = 0; ch < kMaxSplit; ++ch)
+    if (ch < nchunk) sum += exp2f(rec[ch][0] - mx);
+  const float lse = mx + log2f(sum);
+  f32x4_t acc = f32x4_t{0, 0, 0, 0};
+#pragma unroll
+  for (int ch = 0; ch < kMaxSplit; ++ch)
+    if (ch < nchunk) acc += o[ch] * exp2f(rec[ch][0] - lse);
+  acc *= P.scale;
+  *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(P.dq) + static_cast<int64_t>(unit) * D + d0) =
+      pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
+  if (d0 == 0) {
+    const int h = unit % P.H;
+    const int64_t hb = static_cast<int64_t>(h) * (P.rows_total + kBwdPad);
+    P.lse[hb + srow] = lse;
+    P.dd[hb + srow] = rec[0][1];
+    if (h == 0) P.qrow[srow] = unit / P.H;
   }
 }
 
@@ -281,11 +375,12 @@ __global__ __launch_bounds__(kNT, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
   constexpr int RT = kBwdRowsB;          // rows per tile
   constexpr int TE = RT * D;             // elements per Q or dO tile
   constexpr int LPT = RT * kCH / kNT;    // copies per thread per tile and tensor
-  constexpr int META = 4 * RT;           // per stage: lse[RT], dd[RT], next tile's row ids[RT], spare[RT]
-  constexpr int STAGE = 2 * TE * 2 + META * 4;  // bytes
-  static_assert(LPT * kNT == RT * kCH && RT == 64, "tile shape");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
-  __shared__ int32_t first_rows[RT];
+  constexpr int NST = 3;                 // ring stages: two tiles in flight while one is used
+  constexpr int META = 4 * RT * 4;       // bytes per stage: lse[RT], dd[RT], then 512 spare bytes
+  constexpr int STAGE = 2 * TE * 2 + META;
+  constexpr int L0 = 2 * LPT;            // copies per stage of waves 1-3; wave 0 adds one
+  static_assert(LPT * kNT == RT * kCH && RT == 64 && META == 64 * 16, "tile shape; the meta copy lands 64 x 16 bytes");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NST * STAGE];
 
   const WorkItem it = P.items[blockIdx.x];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -294,8 +389,7 @@ __global__ __launch_bounds__(kNT, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
   const int64_t rs = static_cast<int64_t>(P.H) * D;
   const int nrows = it.nrows;
   const int ntiles = (nrows + RT - 1) / RT;
-  const int64_t srow0 = static_cast<int64_t>(it.row_base) * P.n_q;
-  const int64_t hb = static_cast<int64_t>(it.h) * (P.rows_total + kBwdPad);
+  const int64_t hrow0 = static_cast<int64_t>(it.h) * (P.rows_total + kBwdPad) + static_cast<int64_t>(it.row_base) * P.n_q;
   const int key = it.k0 + wave * 32 + n;
   const bool key_ok = key < it.k1;
   const bool wave_live = it.k0 + wave * 32 < it.k1;
@@ -313,35 +407,42 @@ __global__ __launch_bounds__(kNT, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
       vf[ks] = u32x4_t{0u, 0u, 0u, 0u};
     }
   }
-  if (ntiles > 0 && tid < RT) first_rows[tid] = P.qrow[srow0 + min(tid, nrows - 1)];
   wait_vmcnt<0>();
-  __syncthreads();
 
   const uint32_t lds_base = lds_address(smem);
-  const uint16_t* qg = static_cast<const uint16_t*>(P.q) + static_cast<int64_t>(it.h) * D;
-  const uint16_t* dg = static_cast<const uint16_t*>(P.dout) + static_cast<int64_t>(it.h) * D;
-  // Stage t: the Q and dO rows of tile t (gathered by row id), then one copy by
-  // wave 0 of tile t's log-sum-exp and D and of tile t+1's row ids.
-  auto issue = [&](int t, const int32_t* rows) {
-    const uint32_t st = lds_base + static_cast<uint32_t>((t & 1) * STAGE);
+  // Stage t: rows t*RT .. t*RT + RT-1 of the user's sorted Q and dO (contiguous;
+  // rows past the user's count belong to the next user or to the zeroed
+  // padding), then one copy by wave 0 of those rows' log-sum-exp and D.
+  auto issue = [&](int t) {
+    const uint32_t st = lds_base + static_cast<uint32_t>((t % NST) * STAGE);
+    const int64_t e0 = (hrow0 + static_cast<int64_t>(t) * RT) * D;
 #pragma unroll
     for (int c = 0; c < LPT; ++c) {
       const int u = tid + kNT * c;
       const int row = u / kCH, pos = u % kCH;
-      const int qr = t * RT + row < nrows ? rows[row] : rows[0];
-      const int64_t go = static_cast<int64_t>(qr) * rs + (pos ^ swz(row)) * 8;
+      const int64_t go = e0 + row * D + (pos ^ swz(row)) * 8;
       const uint32_t dst = st + static_cast<uint32_t>((kNT * c + 64 * wave_u) * 16);
-      copy16_to_lds(qg + go, dst);
-      copy16_to_lds(dg + go, dst + TE * 2);
+      copy16_to_lds(P.qs + go, dst);
+      copy16_to_lds(P.dos + go, dst + TE * 2);
     }
     if (wave_u == 0) {
       const int part = lane >> 4, j = lane & 15;
-      const int64_t at = srow0 + static_cast<int64_t>(t) * RT + 4 * j;
-      const void* src = part == 0   ? static_cast<const void*>(P.lse + hb + at)
-                        : part == 1 ? static_cast<const void*>(P.dd + hb + at)
-                        : part == 2 ? static_cast<const void*>(P.qrow + at + RT)
-                                    : static_cast<const void*>(P.lse + hb + srow0);
-      copy16_to_lds(src, st + 2 * TE * 2);
+      const int64_t at = hrow0 + static_cast<int64_t>(t) * RT + 4 * j;
+      // one 16-byte copy per lane lands at 16 * lane: lanes 0-15 lse, 16-31 D,
+      // 32-63 the spare bytes (they repeat the lse source)
+      copy16_to_lds(part == 1 ? P.dd + at : P.lse + at, st + 2 * TE * 2);
+    }
+  };
+  // Waits until stage t has landed: `ahead` later stages may stay in flight.
+  auto wait_stage = [&](int ahead) {
+    if (wave_u == 0) {
+      if (ahead >= 2) wait_vmcnt<2 * (L0 + 1)>();
+      else if (ahead == 1) wait_vmcnt<L0 + 1>();
+      else wait_vmcnt<0>();
+    } else {
+      if (ahead >= 2) wait_vmcnt<2 * L0>();
+      else if (ahead == 1) wait_vmcnt<L0>();
+      else wait_vmcnt<0>();
     }
   };
 
@@ -352,17 +453,18 @@ __global__ __launch_bounds__(kNT, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
     dva[db] = f32x16_t{};
   }
   const float c2 = P.scale_log2;
-  if (ntiles > 0) issue(0, first_rows);
+  for (int t = 0; t < min(ntiles, NST - 1); ++t) issue(t);
   for (int t = 0; t < ntiles; ++t) {
-    const uint8_t* slot = smem + (t & 1) * STAGE;
-    wait_vmcnt<0>();
-    __syncthreads();  // tile t and tile t+1's row ids are in LDS
-    if (t + 1 < ntiles) issue(t + 1, reinterpret_cast<const int32_t*>(slot + 2 * TE * 2) + 2 * RT);
+    wait_stage(min(ntiles - 1 - t, NST - 2));
+    __syncthreads();  // tile t is in LDS; every wave is done with tile t-1's slot
+    if (t + NST - 1 < ntiles) issue(t + NST - 1);
+    const uint8_t* slot = smem + (t % NST) * STAGE;
     if (wave_live) {
       const uint16_t* Qt = reinterpret_cast<const uint16_t*>(slot);
       const uint16_t* Dt = Qt + TE;
       const float* lse_t = reinterpret_cast<const float*>(slot + 2 * TE * 2);
       const float* dd_t = lse_t + RT;
+      const bool full_tile = (t + 1) * RT <= nrows;
       f32x16_t s[2], dp[2];
       tile_products(Qt, kf, s, n, g);   // S: rows x this lane's key
       tile_products(Dt, vf, dp, n, g);  // dP
@@ -375,9 +477,9 @@ __global__ __launch_bounds__(kNT, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
           const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(dd_t + rbase);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const bool ok = t * RT + rbase + i < nrows;
-            // rows past the user's count read padding: both products are forced to 0
-            const float p = ok ? exp2f(s[rb][q4 * 4 + i] * c2 - l4[i]) : 0.0f;
+            // rows past the user's count read other rows or padding: both products are forced to 0
+            const bool ok = full_tile || t * RT + rbase + i < nrows;
+            const float p = ok ? exp2_hw(s[rb][q4 * 4 + i] * c2 - l4[i]) : 0.0f;
             s[rb][q4 * 4 + i] = p;
             dp[rb][q4 * 4 + i] = ok ? p * (dp[rb][q4 * 4 + i] - d4[i]) : 0.0f;  // dS
           }
@@ -391,14 +493,13 @@ __global__ __launch_bounds__(kNT, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
           const int K0 = rb * 32 + j0 * 16 + g * 4;
 #pragma unroll
           for (int db = 0; db < kDB; ++db) {
-            dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_rows(Dt, K0, db * 32 + half * 16, kq), bp, dva[db],
-                                                              0, 0, 0);
-            dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_rows(Qt, K0, db * 32 + half * 16, kq), bs, dka[db],
-                                                              0, 0, 0);
+            dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_rows(Dt, K0, db * 32 + half * 16, kq), bp,
+                                                              dva[db], 0, 0, 0);
+            dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_rows(Qt, K0, db * 32 + half * 16, kq), bs,
+                                                              dka[db], 0, 0, 0);
           }
         }
     }
-    __syncthreads();  // every wave is done with this slot before it is refilled
   }
 
   // dK^T / dV^T block db: lane value v is d = db*32 + (v/4)*8 + 4*g + v%4 of key n.
@@ -427,6 +528,16 @@ hipError_t launch_bwd_dq(const BwdParams& p, int n_items, hipStream_t stream, hi
     hipExtLaunchKernelGGL(ikbo_bwd_dq_kernel, dim3(n_items), dim3(kNT), 0, stream, ev[0], ev[1], 0, p);
   else
     hipLaunchKernelGGL(ikbo_bwd_dq_kernel, dim3(n_items), dim3(kNT), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_merge(const BwdParams& p, int n_groups, hipStream_t stream, hipEvent_t ev_stop) {
+  if (n_groups <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(n_groups), kBwdRowsA / (256 / (D / 4)));
+  if (ev_stop)
+    hipExtLaunchKernelGGL(ikbo_bwd_merge_kernel, grid, dim3(256), 0, stream, nullptr, ev_stop, 0, p);
+  else
+    hipLaunchKernelGGL(ikbo_bwd_merge_kernel, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

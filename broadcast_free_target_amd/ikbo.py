@@ -290,9 +290,9 @@ def ikbo_attn_bwd(bwd, user_offsets_host, cand_to_user_host, n_users, n_cand, n_
 
 
 def ikbo_bwd_info(bwd) -> dict:
-    a = (ctypes.c_int64 * 2)()
-    _check(load_library().ikbo_bwd_info(bwd, a, 2))
-    return {"dq_items": a[0], "dkv_items": a[1]}
+    a = (ctypes.c_int64 * 3)()
+    _check(load_library().ikbo_bwd_info(bwd, a, 3))
+    return {"dq_items": a[0], "dkv_items": a[1], "dq_split_groups": a[2]}
 
 
 def ikbo_bwd_timing(bwd, enable: bool) -> int:

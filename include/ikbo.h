@@ -245,12 +245,15 @@ void ikbo_lce_destroy(void* lce);
  * row's log-sum-exp, AI-infra guide section 4.6.3), D = rowsum(dout * out) and
  * dS = P * (dout v^T - D).  Two kernels (the guide's two loop orders; the TLX
  * jagged-attention post, section 2.2, for the K/V-block-outer tile list): dQ
- * per row tile, then dK/dV per 128 keys of a user with the reduction over
- * candidates in registers (no atomics; results are deterministic).
+ * per row tile and key chunk (plus a merge of split chunks), then dK/dV per
+ * 128 keys of a user with the reduction over candidates in registers (no
+ * atomics; results are deterministic).
  *
  * ikbo_bwd_create: a handle owning the work lists (pinned host memory, two
- *   alternating buffers) and a device workspace of 4 * (1 + 2H) * (n_cand*n_q
- *   + 128) bytes.
+ *   alternating buffers) and device workspaces: 4 * (1 + 2H) * (n_cand*n_q +
+ *   128) bytes of per-row statistics, and 64 KB + 2 KB per split slot of dQ
+ *   partials (long key ranges are split as in the forward and merged in chunk
+ *   order, so results stay deterministic).
  * ikbo_attn_bwd: user_offsets [n_users + 1] and cand_to_user [n_cand] are HOST
  *   int32 arrays (as an inference or training runtime holds them); the tensors
  *   are bf16 device arrays, 16-byte aligned, row-major: q_cand, out (the
@@ -263,7 +266,8 @@ void ikbo_lce_destroy(void* lce);
  *   (INVALID_ARG: null or misaligned tensors, gradients aliasing inputs or
  *   each other, bad sizes; BAD_OFFSETS; BAD_MAPPING; UNSUPPORTED: d != 128)
  *   launch nothing.  Calls on one handle must be ordered on one stream.
- * ikbo_bwd_info: info[0] dQ work items, info[1] dK/dV work items of the last call.
+ * ikbo_bwd_info: info[0] dQ work items, info[1] dK/dV work items, info[2] split dQ
+ *   groups (key ranges cut into chunks, merged by a third kernel) of the last call.
  * ikbo_bwd_timing / _timing_read: per-call durations of the two kernels from
  *   events stamped by their dispatches (at most 4096 calls between resets).
  * ikbo_bwd_destroy: frees the handle after synchronising its device.

@@ -179,3 +179,26 @@ def test_bwd_errors():
         assert torch.count_nonzero(dk).item() == 0 and torch.count_nonzero(dv).item() == 0
     finally:
         ikbo.ikbo_bwd_destroy(h)
+
+
+@pytest.mark.parametrize("no_split", ["1", "0"])
+def test_bwd_split_and_unsplit(no_split, monkeypatch):
+    """Long key ranges split into chunks (merged in chunk order) and the
+    unsplit path both meet the bar; each is bitwise repeatable."""
+    import broadcast_free_target_amd as ikbo
+    monkeypatch.setenv("IKBO_NO_SPLIT", no_split)
+    w = _custom(3700, (2048, 1500, 64, 900), (3, 40, 5, 1), n_q=2, H=2)
+    say(f"case bwd split disabled={no_split}")
+    o = _forward_out_bits(w)
+    h = ikbo.ikbo_bwd_create()
+    try:
+        a = _run(w, o, h)
+        groups = ikbo.ikbo_bwd_info(h)["dq_split_groups"]
+        b = _run(w, o, h)
+    finally:
+        ikbo.ikbo_bwd_destroy(h)
+    assert (groups == 0) == (no_split == "1")
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    for g, r, name in zip(a, _oracle(w), ("dq", "dk", "dv")):
+        _close(g, r, name)
