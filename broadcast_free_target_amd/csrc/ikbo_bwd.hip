@@ -25,12 +25,14 @@
 //                   lse = log2 sum_c 2^lse_c,  dQ = scale * sum_c 2^(lse_c - lse) dQ_c,
 //               in chunk order (the log-sum-exp merge of the AI-infra guide,
 //               section 4.6.4, applied to gradients), then writes the same rows.
-//   dK/dV kernel  one workgroup (4 wave64 x 32 keys) per 128 keys of one
-//               (user, head); K and V fragments stay in registers while the
-//               user's candidate rows stream through LDS in 64-row tiles:
-//               S = Q K^T, P, dP = dO V^T, dS, then dV^T += dO^T P and
-//               dK^T += Q^T dS.  The sum over the user's candidates happens in
-//               the accumulators: no atomics, results independent of schedule.
+//   dK/dV kernel  one workgroup per 128 keys of one (user, head), 8 wave64 in
+//               two roles over the same keys: K (and V) fragments stay in
+//               registers while the user's candidate rows stream through LDS
+//               in 64-row tiles; one role forms S = Q K^T and P and accumulates
+//               dV^T += dO^T P, the other forms S, dP = dO V^T and dS and
+//               accumulates dK^T += Q^T dS.  The sum over the user's candidates
+//               happens in the accumulators: no atomics, results independent
+//               of schedule.
 //
 // MFMA v_mfma_f32_32x32x16_bf16 throughout.  Products that contract over d
 // take the tile operand as a row-major 16-byte LDS read and the other from
@@ -371,41 +373,45 @@ __global__ __launch_bounds__(256) void ikbo_bwd_merge_kernel(BwdParams P) {
 // ---------------------------------------------------------------------------
 // dK / dV kernel
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kNT, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
+// Eight waves in two roles over the same 128 keys and the same staged rows:
+// waves 0-3 form P and accumulate dV, waves 4-7 form P, dP and dS and
+// accumulate dK (S is formed by both).  Waves w and w+4 share a SIMD, so each
+// SIMD holds one wave of each role and the softmax work of one overlaps the
+// products of the other; each role fits two waves per SIMD.
+constexpr int kNT8 = 512;
+__global__ __launch_bounds__(kNT8, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
   constexpr int RT = kBwdRowsB;          // rows per tile
   constexpr int TE = RT * D;             // elements per Q or dO tile
-  constexpr int LPT = RT * kCH / kNT;    // copies per thread per tile and tensor
+  constexpr int LPT = RT * kCH / kNT8;   // copies per thread per tile and tensor
   constexpr int NST = 3;                 // ring stages: two tiles in flight while one is used
   constexpr int META = 4 * RT * 4;       // bytes per stage: lse[RT], dd[RT], then 512 spare bytes
   constexpr int STAGE = 2 * TE * 2 + META;
-  constexpr int L0 = 2 * LPT;            // copies per stage of waves 1-3; wave 0 adds one
-  static_assert(LPT * kNT == RT * kCH && RT == 64 && META == 64 * 16, "tile shape; the meta copy lands 64 x 16 bytes");
+  constexpr int L0 = 2 * LPT;            // copies per stage of waves 1-7; wave 0 adds one
+  static_assert(LPT * kNT8 == RT * kCH && RT == 64 && META == 64 * 16, "tile shape; the meta copy lands 64 x 16 bytes");
   __shared__ __attribute__((aligned(16))) uint8_t smem[NST * STAGE];
 
   const WorkItem it = P.items[blockIdx.x];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, g = lane >> 5, kq = lane & 15, half = (lane >> 4) & 1;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const bool dk_role = wave_u >= 4;       // wave-uniform
+  const int kw = wave & 3;                // this wave's 32 keys
   const int64_t rs = static_cast<int64_t>(P.H) * D;
   const int nrows = it.nrows;
   const int ntiles = (nrows + RT - 1) / RT;
   const int64_t hrow0 = static_cast<int64_t>(it.h) * (P.rows_total + kBwdPad) + static_cast<int64_t>(it.row_base) * P.n_q;
-  const int key = it.k0 + wave * 32 + n;
+  const int key = it.k0 + kw * 32 + n;
   const bool key_ok = key < it.k1;
-  const bool wave_live = it.k0 + wave * 32 < it.k1;
+  const bool wave_live = it.k0 + kw * 32 < it.k1;
   const int64_t koff = (static_cast<int64_t>(it.kv_base) + key) * rs + static_cast<int64_t>(it.h) * D;
 
-  // This lane's key row of K and V as B operands (d = 16*ks + 8*g .. +7).
+  // This lane's key row of K (and, for the dK role, of V) as B operands.
   u32x4_t kf[kKS], vf[kKS];
 #pragma unroll
   for (int ks = 0; ks < kKS; ++ks) {
-    if (key_ok) {
-      kf[ks] = ld16(static_cast<const uint16_t*>(P.k) + koff + ks * 16 + g * 8);
-      vf[ks] = ld16(static_cast<const uint16_t*>(P.v) + koff + ks * 16 + g * 8);
-    } else {
-      kf[ks] = u32x4_t{0u, 0u, 0u, 0u};
-      vf[ks] = u32x4_t{0u, 0u, 0u, 0u};
-    }
+    kf[ks] = key_ok ? ld16(static_cast<const uint16_t*>(P.k) + koff + ks * 16 + g * 8) : u32x4_t{0u, 0u, 0u, 0u};
+    vf[ks] = key_ok && dk_role ? ld16(static_cast<const uint16_t*>(P.v) + koff + ks * 16 + g * 8)
+                               : u32x4_t{0u, 0u, 0u, 0u};
   }
   wait_vmcnt<0>();
 
@@ -418,10 +424,10 @@ __global__ __launch_bounds__(kNT, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
     const int64_t e0 = (hrow0 + static_cast<int64_t>(t) * RT) * D;
 #pragma unroll
     for (int c = 0; c < LPT; ++c) {
-      const int u = tid + kNT * c;
+      const int u = tid + kNT8 * c;
       const int row = u / kCH, pos = u % kCH;
       const int64_t go = e0 + row * D + (pos ^ swz(row)) * 8;
-      const uint32_t dst = st + static_cast<uint32_t>((kNT * c + 64 * wave_u) * 16);
+      const uint32_t dst = st + static_cast<uint32_t>((kNT8 * c + 64 * wave_u) * 16);
       copy16_to_lds(P.qs + go, dst);
       copy16_to_lds(P.dos + go, dst + TE * 2);
     }
@@ -436,22 +442,18 @@ __global__ __launch_bounds__(kNT, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
   // Waits until stage t has landed: `ahead` later stages may stay in flight.
   auto wait_stage = [&](int ahead) {
     if (wave_u == 0) {
-      if (ahead >= 2) wait_vmcnt<2 * (L0 + 1)>();
-      else if (ahead == 1) wait_vmcnt<L0 + 1>();
+      if (ahead >= 1) wait_vmcnt<L0 + 1>();
       else wait_vmcnt<0>();
     } else {
-      if (ahead >= 2) wait_vmcnt<2 * L0>();
-      else if (ahead == 1) wait_vmcnt<L0>();
+      if (ahead >= 1) wait_vmcnt<L0>();
       else wait_vmcnt<0>();
     }
   };
+  static_assert(NST == 3, "wait_stage covers one stage in flight behind the awaited one");
 
-  f32x16_t dka[kDB], dva[kDB];
+  f32x16_t acc[kDB];  // dV^T (waves 0-3) or dK^T (waves 4-7)
 #pragma unroll
-  for (int db = 0; db < kDB; ++db) {
-    dka[db] = f32x16_t{};
-    dva[db] = f32x16_t{};
-  }
+  for (int db = 0; db < kDB; ++db) acc[db] = f32x16_t{};
   const float c2 = P.scale_log2;
   for (int t = 0; t < min(ntiles, NST - 1); ++t) issue(t);
   for (int t = 0; t < ntiles; ++t) {
@@ -465,58 +467,84 @@ __global__ __launch_bounds__(kNT, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
       const float* lse_t = reinterpret_cast<const float*>(slot + 2 * TE * 2);
       const float* dd_t = lse_t + RT;
       const bool full_tile = (t + 1) * RT <= nrows;
-      f32x16_t s[2], dp[2];
-      tile_products(Qt, kf, s, n, g);   // S: rows x this lane's key
-      tile_products(Dt, vf, dp, n, g);  // dP
+      if (dk_role) {
+        // one 32-row block at a time keeps S and dP of one block live
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < 2; ++rb) {
+          f32x16_t sb = f32x16_t{}, dpb = f32x16_t{};
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int rbase = rb * 32 + q4 * 8 + g * 4;
-          const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(lse_t + rbase);
-          const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(dd_t + rbase);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // rows past the user's count read other rows or padding: both products are forced to 0
-            const bool ok = full_tile || t * RT + rbase + i < nrows;
-            const float p = ok ? exp2_hw(s[rb][q4 * 4 + i] * c2 - l4[i]) : 0.0f;
-            s[rb][q4 * 4 + i] = p;
-            dp[rb][q4 * 4 + i] = ok ? p * (dp[rb][q4 * 4 + i] - d4[i]) : 0.0f;  // dS
+          for (int ks = 0; ks < kKS; ++ks) {
+            sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(Qt + t_off(rb * 32 + n, ks * 2 + g))),
+                                                         as_bf16x8(kf[ks]), sb, 0, 0, 0);
+            dpb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(Dt + t_off(rb * 32 + n, ks * 2 + g))),
+                                                          as_bf16x8(vf[ks]), dpb, 0, 0, 0);
           }
-        }
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int rbase = rb * 32 + q4 * 8 + g * 4;
+            const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(lse_t + rbase);
+            const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(dd_t + rbase);
 #pragma unroll
-        for (int j0 = 0; j0 < 2; ++j0) {
-          const bf16x8_t bp = pack8(s[rb], j0 * 8);
-          const bf16x8_t bs = pack8(dp[rb], j0 * 8);
-          const int K0 = rb * 32 + j0 * 16 + g * 4;
-#pragma unroll
-          for (int db = 0; db < kDB; ++db) {
-            dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_rows(Dt, K0, db * 32 + half * 16, kq), bp,
-                                                              dva[db], 0, 0, 0);
-            dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_rows(Qt, K0, db * 32 + half * 16, kq), bs,
-                                                              dka[db], 0, 0, 0);
+            for (int i = 0; i < 4; ++i) {
+              // rows past the user's count read other rows or padding: dS is forced to 0
+              const bool ok = full_tile || t * RT + rbase + i < nrows;
+              const float p = exp2_hw(sb[q4 * 4 + i] * c2 - l4[i]);
+              sb[q4 * 4 + i] = ok ? p * (dpb[q4 * 4 + i] - d4[i]) : 0.0f;  // dS
+            }
           }
+#pragma unroll
+          for (int j0 = 0; j0 < 2; ++j0) {
+            const bf16x8_t bs = pack8(sb, j0 * 8);
+            const int K0 = rb * 32 + j0 * 16 + g * 4;
+#pragma unroll
+            for (int db = 0; db < kDB; ++db)
+              acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_rows(Qt, K0, db * 32 + half * 16, kq), bs, acc[db],
+                                                                0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
+      } else {
+        f32x16_t s[2];
+        tile_products(Qt, kf, s, n, g);  // S: rows x this lane's key
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int rbase = rb * 32 + q4 * 8 + g * 4;
+            const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(lse_t + rbase);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              // rows past the user's count read other rows or padding: P is forced to 0
+              const bool ok = full_tile || t * RT + rbase + i < nrows;
+              s[rb][q4 * 4 + i] = ok ? exp2_hw(s[rb][q4 * 4 + i] * c2 - l4[i]) : 0.0f;  // P
+            }
+          }
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int j0 = 0; j0 < 2; ++j0) {
+            const bf16x8_t bp = pack8(s[rb], j0 * 8);
+            const int K0 = rb * 32 + j0 * 16 + g * 4;
+#pragma unroll
+            for (int db = 0; db < kDB; ++db)
+              acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_rows(Dt, K0, db * 32 + half * 16, kq), bp, acc[db],
+                                                                0, 0, 0);
+          }
+      }
     }
   }
 
   // dK^T / dV^T block db: lane value v is d = db*32 + (v/4)*8 + 4*g + v%4 of key n.
   if (key_ok) {
-    uint16_t* dk = static_cast<uint16_t*>(P.dk) + koff;
-    uint16_t* dv = static_cast<uint16_t*>(P.dv) + koff;
+    uint16_t* dst = static_cast<uint16_t*>(dk_role ? P.dk : P.dv) + koff;
+    const float f = dk_role ? P.scale : 1.0f;
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = db * 32 + q4 * 8 + g * 4;
-        *reinterpret_cast<u32x2_t*>(dk + d0) =
-            pack4_bf16(P.scale * dka[db][q4 * 4 + 0], P.scale * dka[db][q4 * 4 + 1], P.scale * dka[db][q4 * 4 + 2],
-                       P.scale * dka[db][q4 * 4 + 3]);
-        *reinterpret_cast<u32x2_t*>(dv + d0) =
-            pack4_bf16(dva[db][q4 * 4 + 0], dva[db][q4 * 4 + 1], dva[db][q4 * 4 + 2], dva[db][q4 * 4 + 3]);
-      }
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<u32x2_t*>(dst + db * 32 + q4 * 8 + g * 4) =
+            pack4_bf16(f * acc[db][q4 * 4 + 0], f * acc[db][q4 * 4 + 1], f * acc[db][q4 * 4 + 2],
+                       f * acc[db][q4 * 4 + 3]);
   }
 }
 
@@ -544,9 +572,9 @@ hipError_t launch_bwd_merge(const BwdParams& p, int n_groups, hipStream_t stream
 hipError_t launch_bwd_dkv(const BwdParams& p, int n_items, hipStream_t stream, hipEvent_t* ev) {
   if (n_items <= 0) return hipSuccess;
   if (ev)
-    hipExtLaunchKernelGGL(ikbo_bwd_dkv_kernel, dim3(n_items), dim3(kNT), 0, stream, ev[0], ev[1], 0, p);
+    hipExtLaunchKernelGGL(ikbo_bwd_dkv_kernel, dim3(n_items), dim3(kNT8), 0, stream, ev[0], ev[1], 0, p);
   else
-    hipLaunchKernelGGL(ikbo_bwd_dkv_kernel, dim3(n_items), dim3(kNT), 0, stream, p);
+    hipLaunchKernelGGL(ikbo_bwd_dkv_kernel, dim3(n_items), dim3(kNT8), 0, stream, p);
   return hipGetLastError();
 }
 
