@@ -18,15 +18,21 @@ W along K into user and candidate columns (linearity, section 2.1), zero
 padding of each decomposed K (section 2.2, Proof 1), brute-force scalar loops
 on tiny inputs, and closed forms for an identity projection.
 
-Readings where the pages are silent: W holds the user columns first; the
-pages give K = 2044 without its split, read here as K_u = K_c = 1022.
+Three levels (user -> vendor -> item, the pages' conclusion): an item's K
+embeddings are its user's, its vendor's and its own blocks; the oracle builds
+both broadcast copies explicitly (``lce_baseline_nested``).
+
+Readings where the pages are silent: W holds the user columns first (then,
+with three levels, the vendor columns); the pages give K = 2044 without its
+split, read here as K_u = K_c = 1022.
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["lce_baseline", "lce_flops_baseline", "lce_flops_ikbo", "lce_bytes_ikbo", "lce_bytes_baseline"]
+__all__ = ["lce_baseline", "lce_baseline_nested", "lce_flops_baseline", "lce_flops_ikbo", "lce_flops_nested",
+           "lce_bytes_ikbo", "lce_bytes_baseline"]
 
 
 def _f64(x) -> np.ndarray:
@@ -74,3 +80,40 @@ def lce_bytes_ikbo(B: int, U: int, M: int, K_u: int, K_c: int, N: int, elem: int
 def lce_bytes_baseline(B: int, M: int, K: int, N: int, elem: int = 2) -> float:
     """App. 2's byte count of the batched product: (M K + B K N + B M N) elements."""
     return float(elem * (M * K + B * K * N + B * M * N))
+
+
+def lce_baseline_nested(w, x_user, x_vendor, x_cand, vendor_to_user, cand_to_vendor) -> np.ndarray:
+    """Three levels, user -> vendor -> item (IKBO blog, conclusion: a user sees
+    several vendors and each vendor offers several items, two nested broadcast
+    relations).  An item's K embeddings are its user's K_u block, its vendor's
+    K_v block and its own K_c block, concatenated along K in that order:
+
+        out[b] = W @ concat_K(x_user[u], x_vendor[v], x_cand[b]),  v = cand_to_vendor[b],
+                                                                    u = vendor_to_user[v]
+
+    built explicitly per item (both broadcast copies are real), fp64.
+    w [M, K_u + K_v + K_c]; x_user [U, K_u, N]; x_vendor [V, K_v, N]; x_cand [B, K_c, N].
+    """
+    w = _f64(w)
+    xu = _f64(x_user)
+    xv = _f64(x_vendor)
+    xc = _f64(x_cand)
+    v2u = np.asarray(vendor_to_user, dtype=np.int64)
+    c2v = np.asarray(cand_to_vendor, dtype=np.int64)
+    B, M, N = xc.shape[0], w.shape[0], xc.shape[2]
+    if w.shape[1] != xu.shape[1] + xv.shape[1] + xc.shape[1]:
+        raise ValueError("W columns must equal K_u + K_v + K_c")
+    if np.any(c2v < 0) or np.any(c2v >= xv.shape[0]) or np.any(v2u < 0) or np.any(v2u >= xu.shape[0]):
+        raise ValueError("mapping entry out of range")
+    out = np.empty((B, M, N), dtype=np.float64)
+    for b in range(B):
+        v = c2v[b]
+        u = v2u[v]
+        xb = np.concatenate([xu[u].copy(), xv[v].copy(), xc[b]], axis=0)  # both broadcast copies, [K, N]
+        out[b] = w @ xb
+    return out
+
+
+def lce_flops_nested(B: int, V: int, U: int, M: int, K_u: int, K_v: int, K_c: int, N: int) -> float:
+    """Executed FLOPs of the nested decomposition: each level's product at its own batch."""
+    return 2.0 * M * N * (U * K_u + V * K_v + B * K_c)

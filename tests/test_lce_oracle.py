@@ -132,3 +132,87 @@ def test_printed_arithmetic_intensity_and_user_side_saving():
     full_user = 2.0 * M * N * B * K_u
     ikbo_user = L.lce_flops_ikbo(B, 15, M, K_u, K_c, N) - 2.0 * M * N * B * K_c
     assert full_user / ikbo_user == pytest.approx(1024 / 15)
+
+
+# ---- three levels: user -> vendor -> item (IKBO blog, conclusion) ----
+
+from workloads import make_lce_nested, make_lce_nested_custom  # noqa: E402
+
+
+def _nested_small(seed=31, K_v=4):
+    v2u = np.array([1, 0, 1, 1, 0], np.int32)
+    c2v = np.array([3, 0, 4, 4, 1, 2, 0], np.int32)
+    return make_lce_nested_custom(seed, 2, v2u, c2v, M=5, K_u=3, K_v=K_v, K_c=2, N=6)
+
+
+def _nested_vals(w):
+    return (w.values("w"), w.values("x_user"), w.values("x_vendor"), w.values("x_cand"), w.vendor_to_user,
+            w.cand_to_vendor)
+
+
+def test_nested_brute_force_scalar_loops():
+    w = _nested_small()
+    W, xu, xv, xc, v2u, c2v = _nested_vals(w)
+    got = L.lce_baseline_nested(W, xu, xv, xc, v2u, c2v)
+    for b in range(w.n_cand):
+        v = int(c2v[b])
+        u = int(v2u[v])
+        for m in range(w.M):
+            for n in range(w.N):
+                terms = [float(W[m, k]) * float(xu[u, k, n]) for k in range(w.K_u)]
+                terms += [float(W[m, w.K_u + k]) * float(xv[v, k, n]) for k in range(w.K_v)]
+                terms += [float(W[m, w.K_u + w.K_v + k]) * float(xc[b, k, n]) for k in range(w.K_c)]
+                assert got[b, m, n] == pytest.approx(math.fsum(terms), rel=1e-13, abs=1e-13)
+
+
+def test_nested_without_vendor_block_is_two_levels():
+    w = _nested_small(K_v=0)
+    W, xu, xv, xc, v2u, c2v = _nested_vals(w)
+    got = L.lce_baseline_nested(W, xu, xv, xc, v2u, c2v)
+    ref = L.lce_baseline(W, xu, xc, v2u[c2v])
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_nested_decomposition_equals_the_batched_product():
+    """Each level at its own batch, the parent's result added: users, then
+    vendors (plus their user's result), then items (plus their vendor's)."""
+    w = make_lce_nested("lce3_tiny")
+    W, xu, xv, xc, v2u, c2v = (a.astype(np.float64) if a.dtype.kind == "f" else a for a in _nested_vals(w))
+    base = L.lce_baseline_nested(W, xu, xv, xc, v2u, c2v)
+    Wu, Wv, Wc = W[:, :w.K_u], W[:, w.K_u:w.K_u + w.K_v], W[:, w.K_u + w.K_v:]
+    yu = np.einsum("mk,ukn->umn", Wu, xu)
+    yv = np.einsum("mk,vkn->vmn", Wv, xv) + yu[v2u]
+    dec = np.einsum("mk,bkn->bmn", Wc, xc) + yv[c2v]
+    np.testing.assert_allclose(dec, base, rtol=1e-12, atol=1e-12)
+
+
+def test_nested_relabelling_and_permutation():
+    w = make_lce_nested("lce3_tiny")
+    W, xu, xv, xc, v2u, c2v = _nested_vals(w)
+    base = L.lce_baseline_nested(W, xu, xv, xc, v2u, c2v)
+    rng = np.random.default_rng(4)
+    pv = rng.permutation(w.n_vendors)           # new vendor id of old vendor i is inv[i]
+    inv = np.argsort(pv)
+    got = L.lce_baseline_nested(W, xu, xv[pv], xc, v2u[pv], inv[c2v])
+    assert np.array_equal(got, base)
+    pb = rng.permutation(w.n_cand)
+    got = L.lce_baseline_nested(W, xu, xv, xc[pb], v2u, c2v[pb])
+    assert np.array_equal(got, base[pb])
+
+
+@pytest.mark.parametrize("mistake", ["item_index_as_vendor_user", "no_vendor_block", "wrong_vendor"])
+def test_nested_planted_mistakes_fail_the_brute_force(mistake):
+    w = _nested_small()
+    W, xu, xv, xc, v2u, c2v = _nested_vals(w)
+    bad = np.empty((w.n_cand, w.M, w.N))
+    for b in range(w.n_cand):
+        v = int(c2v[b])
+        u = int(v2u[v]) if mistake != "item_index_as_vendor_user" else int(c2v[b]) % w.n_users
+        blocks = [xu[u], xv[v], xc[b]]
+        if mistake == "no_vendor_block":
+            blocks[1] = np.zeros_like(xv[v])
+        if mistake == "wrong_vendor":
+            blocks[1] = xv[(v + 1) % w.n_vendors]
+        bad[b] = W @ np.concatenate(blocks)
+    ref = L.lce_baseline_nested(W, xu, xv, xc, v2u, c2v)
+    assert np.abs(bad - ref).max() > 1e-3

@@ -17,4 +17,13 @@ from .ikbo import (  # noqa: F401
     make_custom,
     make_workload,
 )
-from .lce import LCE_NAMES, LceWorkload, make_lce, make_lce_custom  # noqa: F401
+from .lce import (  # noqa: F401
+    LCE_NAMES,
+    LCE_NESTED_NAMES,
+    LceNestedWorkload,
+    LceWorkload,
+    make_lce,
+    make_lce_custom,
+    make_lce_nested,
+    make_lce_nested_custom,
+)

@@ -94,3 +94,80 @@ def make_lce(name: str) -> LceWorkload:
     counts = rng.multinomial(B, [1.0 / U] * U)
     c2u = rng.permutation(np.repeat(np.arange(U, dtype=np.int32), counts)).astype(np.int32)
     return _fill(name, seed, rng, U, c2u, M, K_u, K_c, N)
+
+
+LCE_NESTED_NAMES = ("lce3_tiny", "lce3_typical")
+
+
+@dataclass
+class LceNestedWorkload:
+    """Three levels, user -> vendor -> item: vendor_to_user [V], cand_to_vendor [B];
+    w [M, K_u + K_v + K_c] (user, vendor, item columns), x_user [U, K_u, N],
+    x_vendor [V, K_v, N], x_cand [B, K_c, N]."""
+    name: str
+    seed: int
+    n_users: int
+    n_vendors: int
+    n_cand: int
+    M: int
+    K_u: int
+    K_v: int
+    K_c: int
+    N: int
+    vendor_to_user: np.ndarray
+    cand_to_vendor: np.ndarray
+    tensors: dict = field(default_factory=dict)
+
+    @property
+    def K(self) -> int:
+        return self.K_u + self.K_v + self.K_c
+
+    def raw(self, name: str) -> np.ndarray:
+        return self.tensors[name]
+
+    def values(self, name: str) -> np.ndarray:
+        return bf16_bits_to_f32(self.tensors[name])
+
+
+def _fill_nested(name, seed, rng, n_users, v2u, c2v, M, K_u, K_v, K_c, N) -> LceNestedWorkload:
+    K = K_u + K_v + K_c
+    V, B = len(v2u), len(c2v)
+    w = rng.standard_normal(M * K, dtype=np.float32).reshape(M, K) * np.float32(1.0 / np.sqrt(K))
+    t = {"w": f32_to_bf16_bits(w).reshape(M, K)}
+    for key, shape in (("x_user", (n_users, K_u, N)), ("x_vendor", (V, K_v, N)), ("x_cand", (B, K_c, N))):
+        x = rng.standard_normal(int(np.prod(shape)), dtype=np.float32).reshape(shape)
+        t[key] = f32_to_bf16_bits(x).reshape(shape)
+    return LceNestedWorkload(name=name, seed=seed, n_users=n_users, n_vendors=V, n_cand=B, M=M, K_u=K_u, K_v=K_v,
+                             K_c=K_c, N=N, vendor_to_user=np.asarray(v2u, np.int32),
+                             cand_to_vendor=np.asarray(c2v, np.int32), tensors=t)
+
+
+def make_lce_nested_custom(seed: int, n_users: int, vendor_to_user, cand_to_vendor, M: int, K_u: int, K_v: int,
+                           K_c: int, N: int, name: str = "lce3_custom") -> LceNestedWorkload:
+    rng = np.random.Generator(np.random.PCG64(int(seed)))
+    return _fill_nested(name, int(seed), rng, n_users, np.asarray(vendor_to_user, np.int32),
+                        np.asarray(cand_to_vendor, np.int32), M, K_u, K_v, K_c, N)
+
+
+def make_lce_nested(name: str) -> LceNestedWorkload:
+    """lce3_tiny     2 users, 5 vendors, 13 items, M=37, K_u=11, K_v=9, K_c=7, N=128 (oracle-sized).
+    lce3_typical  the two-level request's B, M, N and total K (1024 items, M=433, K=2044, N=256) with a
+                  vendor level: 15 users, 120 vendors (Multinomial over users), items Multinomial over
+                  vendors (about 8 vendors per user and 8.5 items per vendor, ratio ~68 overall), K read as
+                  K_u = 682, K_v = K_c = 681.
+    Draw order: vendor_to_user, cand_to_vendor (each counts then a permutation), w, x_user, x_vendor, x_cand.
+    """
+    seeds = {"lce3_tiny": 2101, "lce3_typical": 2102}
+    if name not in seeds:
+        raise KeyError(f"unknown nested LCE workload {name!r}; known: {LCE_NESTED_NAMES}")
+    seed = seeds[name]
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if name == "lce3_tiny":
+        U, V, B, M, K_u, K_v, K_c, N = 2, 5, 13, 37, 11, 9, 7, 128
+    else:
+        U, V, B, M, K_u, K_v, K_c, N = 15, 120, 1024, 433, 682, 681, 681, 256
+    vc = rng.multinomial(V, [1.0 / U] * U)
+    v2u = rng.permutation(np.repeat(np.arange(U, dtype=np.int32), vc)).astype(np.int32)
+    cc = rng.multinomial(B, [1.0 / V] * V)
+    c2v = rng.permutation(np.repeat(np.arange(V, dtype=np.int32), cc)).astype(np.int32)
+    return _fill_nested(name, seed, rng, U, v2u, c2v, M, K_u, K_v, K_c, N)
