@@ -79,15 +79,17 @@ __device__ __forceinline__ int w_off(int row, int chunk) { return (row * kWChunk
 // quarters of a 256-byte bank line.
 __device__ __forceinline__ int x_off(int row, int chunk) { return (row * kXChunks + (chunk ^ ((row & 3) << 2))) * 8; }
 
-// The user results of tile (user, mt, nt), wave `wave`: kNB * kMB blocks of
+// Level results of tile (index, mt, nt), wave `wave`: kNB * kMB blocks of
 // 4 x 64 lanes x 4 floats, in accumulator order (block (nb, mb), quarter q,
 // lane) so that the writer and the reader move whole 1 KB requests.
-__device__ __forceinline__ f32x4_t* y_tile(const LceParams& P, int user, int mt, int nt, int wave) {
-  const int64_t tile = (static_cast<int64_t>(user) * P.m_tiles + mt) * P.n_tiles + nt;
-  return reinterpret_cast<f32x4_t*>(P.y) + (tile * (kNT / 64) + wave) * (kNB * kMB * 4 * 64);
+__device__ __forceinline__ const f32x4_t* y_tile(const float* y, const LceParams& P, int index, int mt, int nt,
+                                                 int wave) {
+  const int64_t tile = (static_cast<int64_t>(index) * P.m_tiles + mt) * P.n_tiles + nt;
+  return reinterpret_cast<const f32x4_t*>(y) + (tile * (kNT / 64) + wave) * (kNB * kMB * 4 * 64);
 }
 
-// MODE 0: y[batch] = acc (fp32 store).  MODE 1: out[batch] = bf16(acc + y[user(batch)]).
+// MODE 0: y_out[batch] = acc (+ y_in[map[batch]]), fp32 in accumulator order.
+// MODE 1: out[batch] = bf16(acc + y_in[map[batch]]), row-major.
 template <int MODE>
 __global__ __launch_bounds__(kNT, 1) void ikbo_lce_gemm_kernel(LceParams P) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[kStages * kStageElems];
@@ -106,14 +108,14 @@ __global__ __launch_bounds__(kNT, 1) void ikbo_lce_gemm_kernel(LceParams P) {
   const int mt = L % P.m_tiles;
   const int nt = (L / P.m_tiles) % P.n_tiles;
   const int slot = L / (P.m_tiles * P.n_tiles);
-  const int batch = (MODE == 1 && P.order) ? P.order[slot] : slot;
+  const int batch = P.order ? P.order[slot] : slot;
   const int m0 = mt * kTM, n0 = nt * kTN;
 
-  int user = 0;
+  int parent = 0;
   bool bad = false;
-  if (MODE == 1) {
-    user = P.cand_to_user[batch];
-    bad = user < 0 || user >= P.n_users;
+  if (P.map) {
+    parent = P.map[batch];
+    bad = parent < 0 || parent >= P.n_parent;
   }
 
   const uint16_t* __restrict__ Wp = static_cast<const uint16_t*>(P.w) + static_cast<int64_t>(m0) * P.ldw;
@@ -175,16 +177,16 @@ __global__ __launch_bounds__(kNT, 1) void ikbo_lce_gemm_kernel(LceParams P) {
 
   // Accumulators.  Lane value v of block (nb, mb) is output row (M index)
   // m0 + wm*128 + mb*32 + n and column n0 + wn*64 + nb*32 + (v/4)*8 + g*4 + v%4.
-  // The candidate GEMM starts from its user's result, loaded while the first
-  // ring stages are in flight.  One full wait then covers those loads and the
-  // first stages: the compiler, which does not see the ring copies, would
-  // otherwise guard the accumulators with a wait for every load in flight at
-  // each ring step.
+  // A level with a parent starts from the parent's result, loaded while the
+  // first ring stages are in flight.  One full wait then covers those loads
+  // and the first stages: the compiler, which does not see the ring copies,
+  // would otherwise guard the accumulators with a wait for every load in
+  // flight at each ring step.
   f32x16_t acc[kNB][kMB];
   for (int s = 0; s < min(nstages, kStages - 1); ++s) issue(s);
-  // The user results are kept in accumulator order (see the MODE 0 store), so
+  // Level results are kept in accumulator order (see the MODE 0 store), so
   // each 16-byte lane load is part of one contiguous 1 KB request.
-  const f32x4_t* yt = (MODE == 1 && P.y && !bad) ? y_tile(P, user, mt, nt, wave) : nullptr;
+  const f32x4_t* yt = (P.y_in && !bad) ? y_tile(P.y_in, P, parent, mt, nt, wave) : nullptr;
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
@@ -267,13 +269,11 @@ __global__ __launch_bounds__(kNT, 1) void ikbo_lce_gemm_kernel(LceParams P) {
     mma_live(f1);
   }
 
-  if (MODE == 1 && bad) {
-    if (tid == 0) atomicAdd(P.errors, 1);
-  }
+  if (bad && mt == 0 && nt == 0 && tid == 0) atomicAdd(P.errors, 1);  // once per batch element
   if (MODE == 0) {
-    // User results, fp32, in accumulator order: the whole tile, blocks past M
+    // Level results, fp32, in accumulator order: the whole tile, blocks past M
     // or N included (they hold zeros), lane-contiguous 16-byte stores.
-    f32x4_t* yt = y_tile(P, batch, mt, nt, wave);
+    f32x4_t* yt = const_cast<f32x4_t*>(y_tile(P.y_out, P, batch, mt, nt, wave));
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
@@ -281,7 +281,9 @@ __global__ __launch_bounds__(kNT, 1) void ikbo_lce_gemm_kernel(LceParams P) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           yt[((nb * kMB + mb) * 4 + q) * 64 + lane] =
-              f32x4_t{acc[nb][mb][q * 4 + 0], acc[nb][mb][q * 4 + 1], acc[nb][mb][q * 4 + 2], acc[nb][mb][q * 4 + 3]};
+              bad ? f32x4_t{}
+                  : f32x4_t{acc[nb][mb][q * 4 + 0], acc[nb][mb][q * 4 + 1], acc[nb][mb][q * 4 + 2],
+                            acc[nb][mb][q * 4 + 3]};
     return;
   }
 
@@ -370,35 +372,43 @@ __global__ __launch_bounds__(kOrderThreads) void ikbo_lce_order_kernel(const int
   }
 }
 
-// W (M x ldw, user columns [0, K_u), candidate columns [K_u, K_u + K_c)) into
-// the two zero-padded blocks [M_pad, K_u_pad] and [M_pad, K_c_pad].
+// W (M x ldw; user columns [0, K_u), vendor columns [K_u, K_u + K_v), item
+// columns after) into the zero-padded blocks [M_pad, K_u_pad], [M_pad, K_v_pad]
+// and [M_pad, K_c_pad].
 __global__ __launch_bounds__(256) void ikbo_lce_pack_kernel(const uint16_t* __restrict__ w, int M, int ldw, int K_u,
-                                                           int K_c, int M_pad, int K_u_pad, int K_c_pad,
-                                                           uint16_t* __restrict__ wu, uint16_t* __restrict__ wc) {
-  const int64_t total = static_cast<int64_t>(M_pad) * (K_u_pad + K_c_pad);
+                                                           int K_v, int K_c, int M_pad, int K_u_pad, int K_v_pad,
+                                                           int K_c_pad, uint16_t* __restrict__ wu,
+                                                           uint16_t* __restrict__ wv, uint16_t* __restrict__ wc) {
+  const int row_len = K_u_pad + K_v_pad + K_c_pad;
+  const int64_t total = static_cast<int64_t>(M_pad) * row_len;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int m = static_cast<int>(i / (K_u_pad + K_c_pad));
-    const int k = static_cast<int>(i % (K_u_pad + K_c_pad));
+    const int m = static_cast<int>(i / row_len);
+    const int k = static_cast<int>(i % row_len);
     if (k < K_u_pad) {
       wu[static_cast<int64_t>(m) * K_u_pad + k] = (m < M && k < K_u) ? w[static_cast<int64_t>(m) * ldw + k] : 0;
+    } else if (k < K_u_pad + K_v_pad) {
+      const int kv = k - K_u_pad;
+      wv[static_cast<int64_t>(m) * K_v_pad + kv] =
+          (m < M && kv < K_v) ? w[static_cast<int64_t>(m) * ldw + K_u + kv] : 0;
     } else {
-      const int kc = k - K_u_pad;
+      const int kc = k - K_u_pad - K_v_pad;
       wc[static_cast<int64_t>(m) * K_c_pad + kc] =
-          (m < M && kc < K_c) ? w[static_cast<int64_t>(m) * ldw + K_u + kc] : 0;
+          (m < M && kc < K_c) ? w[static_cast<int64_t>(m) * ldw + K_u + K_v + kc] : 0;
     }
   }
 }
 
 }  // namespace
 
-hipError_t launch_lce_pack(const void* w, int M, int ldw, int K_u, int K_c, int M_pad, int K_u_pad, int K_c_pad,
-                           void* wu, void* wc, hipStream_t stream) {
-  const int64_t total = static_cast<int64_t>(M_pad) * (K_u_pad + K_c_pad);
+hipError_t launch_lce_pack(const void* w, int M, int ldw, int K_u, int K_v, int K_c, int M_pad, int K_u_pad,
+                           int K_v_pad, int K_c_pad, void* wu, void* wv, void* wc, hipStream_t stream) {
+  const int64_t total = static_cast<int64_t>(M_pad) * (K_u_pad + K_v_pad + K_c_pad);
   if (total <= 0) return hipSuccess;
   const int grid = static_cast<int>(std::min<int64_t>(4096, (total + 255) / 256));
   hipLaunchKernelGGL(ikbo_lce_pack_kernel, dim3(grid), dim3(256), 0, stream, static_cast<const uint16_t*>(w), M,
-                     ldw, K_u, K_c, M_pad, K_u_pad, K_c_pad, static_cast<uint16_t*>(wu), static_cast<uint16_t*>(wc));
+                     ldw, K_u, K_v, K_c, M_pad, K_u_pad, K_v_pad, K_c_pad, static_cast<uint16_t*>(wu),
+                     static_cast<uint16_t*>(wv), static_cast<uint16_t*>(wc));
   return hipGetLastError();
 }
 

@@ -58,6 +58,8 @@ SIGNATURES = {
     "ikbo_lce_timing_read": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
                                             _I, _IP]),
     "ikbo_lce_destroy": (None, [_P]),
+    "ikbo_lce3_create": (ctypes.c_int, [ctypes.POINTER(_P), _P, _I, _I, _I, _I, _I, _P]),
+    "ikbo_lce3_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "ikbo_bwd_create": (ctypes.c_int, [ctypes.POINTER(_P)]),
     "ikbo_attn_bwd": (ctypes.c_int, [_P, _IP, _IP, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "ikbo_bwd_info": (ctypes.c_int, [_P, _LP, _I]),
@@ -310,3 +312,19 @@ def ikbo_bwd_timing_read(bwd, max_n: int = 4096):
 
 def ikbo_bwd_destroy(bwd) -> None:
     load_library().ikbo_bwd_destroy(bwd)
+
+
+def ikbo_lce3_create(w, M, K_u, K_v, K_c, ldw=None, stream=None) -> int:
+    """Packs W [M, ldw] (device bf16; user, vendor, item columns) for three levels."""
+    h = _P()
+    _check(load_library().ikbo_lce3_create(ctypes.byref(h), _ptr(w), M, K_u, K_v, K_c,
+                                           K_u + K_v + K_c if ldw is None else ldw, _stream(stream)))
+    return h.value
+
+
+def ikbo_lce3_fwd(lce, x_user, x_vendor, x_cand, vendor_to_user, cand_to_vendor, n_users, n_vendors, n_cand, N, out,
+                  stream=None) -> int:
+    return _check(load_library().ikbo_lce3_fwd(lce, _ptr(x_user), _ptr(x_vendor), _ptr(x_cand), _ptr(vendor_to_user),
+                                               _ptr(cand_to_vendor), n_users, n_vendors, n_cand, N, _ptr(out),
+                                               _stream(stream)))
+

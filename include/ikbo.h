@@ -220,13 +220,42 @@ int ikbo_plan_trace_read(void* plan, int64_t* records, int32_t max_items, int32_
  *   ikbo_lce_errors).  Calls with one handle must be ordered on one stream (they
  *   share its user-result workspace).  n_cand = 0 is a no-op.
  * ikbo_lce_errors: synchronises the device and returns (and resets) the number
- *   of candidates seen with an out-of-range mapping entry since the last call.
+ *   of batch elements (candidates, or vendors and items of a three-level call)
+ *   seen with an out-of-range mapping entry since the last call.
  * ikbo_lce_timing / _timing_read: per-call durations of the user and candidate
  *   GEMMs from events stamped by the dispatches (measurement; as the plan
  *   timing functions, at most 4096 calls between resets).
  * ikbo_lce_destroy: frees the handle after synchronising its device.
  */
 int ikbo_lce_create(void** lce, const void* w, int32_t M, int32_t K_u, int32_t K_c, int32_t ldw, void* stream);
+/*
+ * Three levels, user -> ads vendor -> ads item (IKBO blog, conclusion: a user
+ * sees several vendors, each vendor offers several items; two nested broadcast
+ * relations with independent, uneven ratios).  An item's K embeddings are its
+ * user's K_u, its vendor's K_v and its own K_c embeddings; the product nests
+ * the Type I split:
+ *   y_user[u]   = W[:, :K_u] . x_user[u]                                    (fp32)
+ *   y_vendor[v] = W[:, K_u:K_u+K_v] . x_vendor[v] + y_user[vendor_to_user[v]]   (fp32)
+ *   out[b]      = W[:, K_u+K_v:] . x_cand[b] + y_vendor[cand_to_vendor[b]]      (bf16)
+ * each level at its own batch size, each parent result added in the child
+ * GEMM's epilogue; neither broadcast copy is ever written.
+ * ikbo_lce3_create: as ikbo_lce_create, W columns user, vendor, item (ldw >=
+ *   K_u + K_v + K_c; any block may be empty, the total may not).
+ * ikbo_lce3_fwd: x_user [n_users, K_u, N], x_vendor [n_vendors, K_v, N],
+ *   x_cand [n_cand, K_c, N], out [n_cand, M, N] (bf16 device tensors, 16-byte
+ *   aligned); vendor_to_user [n_vendors] and cand_to_vendor [n_cand] are int32
+ *   device arrays.  Four launches (item ordering, user, vendor and item GEMMs),
+ *   no synchronisation.  Out-of-range entries give zero results for that vendor
+ *   or item and are counted (ikbo_lce_errors).  Timing: the first slot spans the
+ *   user and vendor GEMMs, the second the item GEMM.  A handle from
+ *   ikbo_lce3_create takes only ikbo_lce3_fwd, one from ikbo_lce_create only
+ *   ikbo_lce_fwd (INVALID_ARG otherwise).
+ */
+int ikbo_lce3_create(void** lce, const void* w, int32_t M, int32_t K_u, int32_t K_v, int32_t K_c, int32_t ldw,
+                     void* stream);
+int ikbo_lce3_fwd(void* lce, const void* x_user, const void* x_vendor, const void* x_cand,
+                  const int32_t* vendor_to_user, const int32_t* cand_to_vendor, int32_t n_users, int32_t n_vendors,
+                  int32_t n_cand, int32_t N, void* out, void* stream);
 int ikbo_lce_fwd(void* lce, const void* x_user, const void* x_cand, const int32_t* cand_to_user, int32_t n_users,
                  int32_t n_cand, int32_t N, void* out, void* stream);
 int ikbo_lce_errors(void* lce, int64_t* count);

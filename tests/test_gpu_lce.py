@@ -147,3 +147,115 @@ def test_lce_errors():
         assert torch.count_nonzero(out).item() == 0
     finally:
         ikbo_lce_destroy(h)
+
+
+# ---- three levels: user -> vendor -> item ----
+
+from workloads import make_lce_nested, make_lce_nested_custom  # noqa: E402
+
+
+def _run3(w, v2u=None, c2v=None, n_users=None, n_vendors=None):
+    import torch
+    from broadcast_free_target_amd import ikbo_lce3_create, ikbo_lce3_fwd, ikbo_lce_destroy, ikbo_lce_errors
+    v2u = w.vendor_to_user if v2u is None else np.asarray(v2u, np.int32)
+    c2v = w.cand_to_vendor if c2v is None else np.asarray(c2v, np.int32)
+    U = w.n_users if n_users is None else n_users
+    V = len(v2u) if n_vendors is None else n_vendors
+    W = _dev(w.raw("w"))
+    xu = _dev(w.raw("x_user")) if w.K_u > 0 else None
+    xv = _dev(w.raw("x_vendor")) if w.K_v > 0 else None
+    xc = _dev(w.raw("x_cand")) if w.K_c > 0 else None
+    mv = torch.from_numpy(v2u.copy()).cuda()
+    mc = torch.from_numpy(c2v.copy()).cuda()
+    out = torch.full((len(c2v), w.M, w.N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    h = ikbo_lce3_create(W, w.M, w.K_u, w.K_v, w.K_c)
+    try:
+        ikbo_lce3_fwd(h, xu, xv, xc, mv, mc, U, V, len(c2v), w.N, out)
+        torch.cuda.synchronize()
+        errs = ikbo_lce_errors(h)
+    finally:
+        ikbo_lce_destroy(h)
+    return out.float().cpu().numpy().astype(np.float64), errs
+
+
+def _oracle3(w, cands=None):
+    xc, c2v = w.values("x_cand"), w.cand_to_vendor
+    if cands is not None:
+        xc, c2v = xc[cands], c2v[cands]
+    return L.lce_baseline_nested(w.values("w"), w.values("x_user"), w.values("x_vendor"), xc, w.vendor_to_user, c2v)
+
+
+def test_lce3_tiny_full():
+    w = make_lce_nested("lce3_tiny")
+    say("case lce3_tiny")
+    got, errs = _run3(w)
+    assert errs == 0
+    assert_close(got, _oracle3(w), "bf16", "lce3_tiny")
+
+
+def test_lce3_typical_sampled():
+    w = make_lce_nested("lce3_typical")
+    say(f"case lce3_typical U={w.n_users} V={w.n_vendors} B={w.n_cand}")
+    got, errs = _run3(w)
+    assert errs == 0 and np.all(np.isfinite(got))
+    cands = np.sort(np.random.default_rng(8).choice(w.n_cand, 24, replace=False))
+    assert_close(got[cands], _oracle3(w, cands), "bf16", "lce3_typical")
+
+
+EDGE3 = [
+    # users, vendor -> user, item -> vendor, M, K_u, K_v, K_c, N
+    (2, [1, 0, 1], [2, 0, 0, 2, 1], 40, 10, 9, 8, 128),
+    (3, [2, 2, 0, 0], [0, 3, 3, 0, 2], 129, 0, 70, 33, 256),    # no user block; user 1 has no vendor
+    (2, [0, 1, 1], [2, 1, 1, 0, 0, 0], 64, 50, 0, 20, 128),     # no vendor block
+    (2, [1, 0], [0, 1, 0], 33, 20, 15, 0, 384),                 # no item block
+    (1, [0, 0, 0, 0], [3, 3, 1], 300, 65, 64, 1, 128),          # vendors 0 and 2 have no item
+]
+
+
+@pytest.mark.parametrize("i", range(len(EDGE3)))
+def test_lce3_edges(i):
+    U, v2u, c2v, M, K_u, K_v, K_c, N = EDGE3[i]
+    w = make_lce_nested_custom(3800 + i, U, v2u, c2v, M, K_u, K_v, K_c, N, name=f"lce3_edge{i}")
+    say(f"case lce3 edge {i}")
+    got, errs = _run3(w)
+    assert errs == 0
+    assert_close(got, _oracle3(w), "bf16", f"lce3 edge {i}")
+
+
+def test_lce3_out_of_range_entries():
+    """A vendor with an out-of-range user contributes zeros (its own part and its
+    user's); an item with an out-of-range vendor is written as zeros."""
+    w = make_lce_nested_custom(3900, 2, [0, 1, 0], [0, 1, 2, 2], M=40, K_u=10, K_v=9, K_c=8, N=128)
+    v2u = np.array([0, 7, 0], np.int32)     # vendor 1 names no user
+    c2v = np.array([0, 1, 5, 2], np.int32)  # item 2 names no vendor
+    say("case lce3 bad mappings")
+    got, errs = _run3(w, v2u=v2u, c2v=c2v)
+    assert errs == 2
+    assert np.all(got[2] == 0)
+    Wc = w.values("w")[:, w.K_u + w.K_v:].astype(np.float64)
+    assert_close(got[1:2], (Wc @ w.values("x_cand")[1].astype(np.float64))[None], "bf16", "item of the bad vendor")
+    ok = [0, 3]
+    ref = L.lce_baseline_nested(w.values("w"), w.values("x_user"), w.values("x_vendor"), w.values("x_cand")[ok],
+                                w.vendor_to_user, w.cand_to_vendor[ok])
+    assert_close(got[ok], ref, "bf16", "valid items")
+
+
+def test_lce3_handle_kinds():
+    import torch
+    from broadcast_free_target_amd import (IkboError, ikbo_lce3_create, ikbo_lce3_fwd, ikbo_lce_create,
+                                           ikbo_lce_destroy, ikbo_lce_fwd)
+    w = make_lce_nested("lce3_tiny")
+    W = _dev(w.raw("w"))
+    out = torch.zeros((w.n_cand, w.M, w.N), dtype=torch.bfloat16, device="cuda")
+    m = torch.from_numpy(w.cand_to_vendor.copy()).cuda()
+    say("case lce3 handle kinds")
+    h3 = ikbo_lce3_create(W, w.M, w.K_u, w.K_v, w.K_c)
+    h2 = ikbo_lce_create(W, w.M, w.K_u + w.K_v, w.K_c)
+    try:
+        with pytest.raises(IkboError):
+            ikbo_lce_fwd(h3, _dev(w.raw("x_user")), _dev(w.raw("x_cand")), m, w.n_users, w.n_cand, w.N, out)
+        with pytest.raises(IkboError):
+            ikbo_lce3_fwd(h2, None, None, None, m, m, 1, 1, w.n_cand, w.N, out)
+    finally:
+        ikbo_lce_destroy(h3)
+        ikbo_lce_destroy(h2)
