@@ -43,6 +43,7 @@ WORKLOAD_TEXT = {
     "p_app11": "App. 11 shape: 32 users x 64 candidates, n_q=64, L=1024, H=2, d=128, bf16",
     "bwd_c2_typical": "backward of the typical request: 1024 candidates over 15 users, L~U[256,2048], n_q=1, H=4, d=128, bf16",
     "bwd_c4_large": "backward of the large request: 10000 candidates over 150 users, L~U[512,4096], n_q=4, H=8, d=128, bf16",
+    "lce3_typical": "three-level linear compression: 1024 items over 120 vendors over 15 users, M=433, K_u=682, K_v=K_c=681, N=256, bf16",
     "lce_typical": "linear compression: 1024 candidates over 15 users, M=433, K_u=K_c=1022, N=256, bf16",
     "lce_ratio1000": "linear compression: 2000 candidates over 2 users, M=433, K_u=K_c=1022, N=256, bf16",
 }
@@ -122,7 +123,7 @@ BWD_SOURCES = ("ikbo_bwd.hip", "ikbo_bwd.h", "ikbo_device.h", "ikbo_plan.cpp", "
 def traffic_from_profiles(workload):
     """Per-launch HBM bytes from the committed rocprofv3 --pmc summary, if it
     was taken on the current kernel sources; else None."""
-    lce = workload.startswith("lce_")
+    lce = workload.startswith("lce")
     bwd = workload.startswith("bwd_")
     name = (f"ikbo_lce_gemm_{workload}_pmc.json" if lce else f"ikbo_bwd_{workload}_pmc.json" if bwd
             else f"ikbo_attn_bf16_{workload}_pmc.json")
@@ -314,6 +315,156 @@ def main_bwd(args):
     print(json.dumps(result), flush=True)
 
 
+def lce3_counts(w):
+    """Executed and baseline FLOPs of a three-level call, and the item GEMM's
+    algorithmic FLOPs and bytes (W_c, x_cand, out, vendor results once per vendor)."""
+    U, V, B, M, N = w.n_users, w.n_vendors, w.n_cand, w.M, w.N
+    f_exec = 2.0 * M * N * (U * w.K_u + V * w.K_v + B * w.K_c)
+    f_base = 2.0 * M * N * B * w.K
+    f_item = 2.0 * M * N * B * w.K_c
+    b_item = 2.0 * (M * w.K_c + B * w.K_c * N + B * M * N) + 4.0 * V * M * N
+    return f_exec, f_base, f_item, b_item
+
+
+def cpu_baseline_lce3(w, n_sample, reps):
+    """The fp64 nested oracle (both broadcast copies explicit) on the first
+    n_sample items, its time scaled to the whole batch, counted in executed FLOPs."""
+    from oracle import lce_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    args = (w.values("w"), w.values("x_user"), w.values("x_vendor"), w.values("x_cand")[:n_sample],
+            w.vendor_to_user, w.cand_to_vendor[:n_sample])
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        O.lce_baseline_nested(*args)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    t_whole = t * w.n_cand / n_sample
+    return {"value": lce3_counts(w)[0] / t_whole / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n_sample} of {w.n_cand} items of {w.name}, fp64 numpy with both broadcast copies "
+                      f"explicit, median of {reps} runs of {t:.2f} s, scaled to the whole batch and counted in "
+                      f"the same executed FLOPs as the GPU value",
+            "seconds_whole_batch": t_whole}
+
+
+def main_lce3(args):
+    """One step = one ikbo_lce3_fwd: item ordering, user, vendor and item GEMMs."""
+    import torch
+    import broadcast_free_target_amd as ikbo
+    from workloads import make_lce_nested
+
+    w = make_lce_nested(args.config)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    W, xu, xv, xc = dev(w.raw("w")), dev(w.raw("x_user")), dev(w.raw("x_vendor")), dev(w.raw("x_cand"))
+    v2u = torch.from_numpy(w.vendor_to_user.copy()).cuda()
+    c2v = torch.from_numpy(w.cand_to_vendor.copy()).cuda()
+    out = torch.empty((w.n_cand, w.M, w.N), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    h = ikbo.ikbo_lce3_create(W, w.M, w.K_u, w.K_v, w.K_c, stream=stream)
+
+    def step():
+        ikbo.ikbo_lce3_fwd(h, xu, xv, xc, v2u, c2v, w.n_users, w.n_vendors, w.n_cand, w.N, out, stream)
+
+    def materialized():
+        hb = ikbo.ikbo_lce_create(W, w.M, 0, w.K, stream=stream)
+        xfull = torch.empty((w.n_cand, w.K, w.N), dtype=torch.bfloat16, device="cuda")
+        vi = c2v.long()
+        ui = v2u.long()[vi]
+
+        def copy():
+            xfull[:, :w.K_u].copy_(xu.index_select(0, ui))
+            xfull[:, w.K_u:w.K_u + w.K_v].copy_(xv.index_select(0, vi))
+            xfull[:, w.K_u + w.K_v:].copy_(xc)
+
+        def gemm():
+            ikbo.ikbo_lce_fwd(hb, None, xfull, c2v, w.n_vendors, w.n_cand, w.N, out, stream)
+
+        return hb, copy, gemm
+
+    if args.materialized_only:
+        hb, copy, gemm = materialized()
+        for _ in range(args.steps):
+            copy()
+            gemm()
+        torch.cuda.synchronize()
+        ikbo.ikbo_lce_destroy(hb)
+        ikbo.ikbo_lce_destroy(h)
+        print(json.dumps({"materialized_launches": args.steps, "config": args.config}), flush=True)
+        return
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ikbo.ikbo_lce_timing(h, True)
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    upper_ms, item_ms = ikbo.ikbo_lce_timing_read(h, K)
+    ikbo.ikbo_lce_timing(h, False)
+    if ikbo.ikbo_lce_errors(h) != 0:
+        raise RuntimeError("three-level linear compression reported out-of-range mappings")
+    u_avg, c_avg = float(np.mean(upper_ms)), float(np.mean(item_ms))
+    f_exec, f_base, f_item, b_item = lce3_counts(w)
+    ms_per_step = wall * 1e3 / K
+    ai = f_item / b_item
+    if ai < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        achieved = b_item / (c_avg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS}
+    else:
+        achieved = f_item / (c_avg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS}
+    roof["traffic"] = traffic_from_profiles(args.config)
+    roof["kernel"] = LCE_KERNEL
+    roof["kernel_avg_us"] = c_avg * 1e3
+    roof["user_and_vendor_kernels_us"] = u_avg * 1e3
+    roof["algorithmic_bytes_per_launch"] = b_item
+    roof["algorithmic_flops_per_launch"] = f_item
+    extra = {"executed_flops": f_exec, "baseline_flops": f_base, "flops_saved_frac": 1.0 - f_exec / f_base,
+             "baseline_equivalent_tflops": f_base / (ms_per_step * 1e-3) / 1e12,
+             "item_gemm_tflops": f_item / (c_avg * 1e-3) / 1e12, "items_per_s": w.n_cand / (ms_per_step * 1e-3)}
+    if args.report:
+        hb, copy, gemm = materialized()
+        for _ in range(3):
+            copy()
+            gemm()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(20):
+            copy()
+            gemm()
+        torch.cuda.synchronize()
+        extra["materialized_step_us"] = (time.perf_counter() - t1) / 20 * 1e6
+        extra["speedup_vs_materialized_step"] = extra["materialized_step_us"] / (ms_per_step * 1e3)
+        ikbo.ikbo_lce_destroy(hb)
+    ikbo.ikbo_lce_destroy(h)
+    result = {
+        "metric": LCE_METRIC, "value": f_exec / (ms_per_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs, W scaled by 1/sqrt(K), multinomial user->vendor->item mappings)",
+        "config": {"workload": f"{args.config}: {WORKLOAD_TEXT[args.config]}", "n_cand": w.n_cand,
+                   "n_vendors": w.n_vendors, "n_users": w.n_users, "M": w.M, "K_u": w.K_u, "K_v": w.K_v,
+                   "K_c": w.K_c, "N": w.N, "seed": w.seed},
+        "roofline": roof, "cpu_baseline": None, "extra": extra,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_lce3(w, 256, max(3, args.cpu_reps // 3))
+    print(json.dumps(result), flush=True)
+
+
 def main_lce(args):
     """One step = one ikbo_lce_fwd: user GEMM, then the candidate GEMM whose
     epilogue adds each candidate's user result."""
@@ -495,6 +646,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
                           "launches": args.steps}), flush=True)
+        return
+    if args.config.startswith("lce3_"):
+        main_lce3(args)
         return
     if args.config.startswith("lce_"):
         main_lce(args)
