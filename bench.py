@@ -108,7 +108,7 @@ def bwd_counts(w):
 
 
 def kernel_source_hash(files=("ikbo_kernels.hip", "ikbo_kernels.h", "ikbo_device.h", "ikbo_plan.cpp",
-                              "ikbo_plan.h", "ikbo_api.hip")):
+                              "ikbo_plan.h", "ikbo_api.hip", "ikbo_api_common.h")):
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(ROOT, "broadcast_free_target_amd", "csrc", f), "rb") as fh:
@@ -116,8 +116,9 @@ def kernel_source_hash(files=("ikbo_kernels.hip", "ikbo_kernels.h", "ikbo_device
     return h.hexdigest()[:16]
 
 
-LCE_SOURCES = ("ikbo_lce.hip", "ikbo_lce.h", "ikbo_device.h", "ikbo_api.hip")
-BWD_SOURCES = ("ikbo_bwd.hip", "ikbo_bwd.h", "ikbo_device.h", "ikbo_plan.cpp", "ikbo_api.hip")
+LCE_SOURCES = ("ikbo_lce.hip", "ikbo_lce.h", "ikbo_device.h", "ikbo_api_lce.hip", "ikbo_api_common.h")
+BWD_SOURCES = ("ikbo_bwd.hip", "ikbo_bwd.h", "ikbo_device.h", "ikbo_plan.cpp", "ikbo_plan.h", "ikbo_api_bwd.hip",
+               "ikbo_api_common.h")
 
 
 def traffic_from_profiles(workload):

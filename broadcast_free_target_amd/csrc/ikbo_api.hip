@@ -20,103 +20,21 @@
 #include <vector>
 
 #include "ikbo.h"
-#include "ikbo_bwd.h"
+#include "ikbo_api_common.h"
 #include "ikbo_kernels.h"
-#include "ikbo_lce.h"
 #include "ikbo_plan.h"
+
+namespace ikbo_host {
+thread_local std::string g_last_error;
+}  // namespace ikbo_host
+
+using namespace ikbo_host;
 
 namespace {
 
 using ikbo::HostPlan;
 using ikbo::PlanParams;
 using ikbo::WorkItem;
-
-thread_local std::string g_last_error;
-
-int fail(int code, const std::string& msg) {
-  g_last_error = msg;
-  return code;
-}
-
-int fail_hip(hipError_t e, const char* what) {
-  return fail(IKBO_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
-}
-
-#define IKBO_HIP(call)                          \
-  do {                                          \
-    hipError_t e_ = (call);                     \
-    if (e_ != hipSuccess) return fail_hip(e_, #call); \
-  } while (0)
-
-int env_int(const char* name, int dflt) {
-  const char* s = std::getenv(name);
-  if (!s || !*s) return dflt;
-  return std::atoi(s);
-}
-
-size_t elem_size(int32_t dtype) { return dtype == IKBO_DTYPE_F32 ? 4 : 2; }
-
-constexpr int kMaxTimed = 4096;  // launches a plan can time between resets
-
-// Grow-only device buffer.
-struct DevBuf {
-  void* ptr = nullptr;
-  size_t cap = 0;
-  int ensure(size_t bytes, bool zero) {
-    if (bytes <= cap) return IKBO_OK;
-    if (ptr) {
-      hipError_t e = hipFree(ptr);  // hipFree waits for work that may still use the buffer
-      ptr = nullptr;
-      cap = 0;
-      if (e != hipSuccess) return fail_hip(e, "hipFree");
-    }
-    size_t want = std::max<size_t>(bytes, 256);
-    hipError_t e = hipMalloc(&ptr, want);
-    if (e != hipSuccess) {
-      ptr = nullptr;
-      return fail(IKBO_ERR_NOMEM, std::string("hipMalloc: ") + hipGetErrorString(e));
-    }
-    if (zero) {
-      e = hipMemset(ptr, 0, want);
-      if (e != hipSuccess) return fail_hip(e, "hipMemset");
-    }
-    cap = want;
-    return IKBO_OK;
-  }
-  void release() {
-    if (ptr) (void)hipFree(ptr);
-    ptr = nullptr;
-    cap = 0;
-  }
-};
-
-// Grow-only pinned host buffer (host-cached).  Work lists read in place by a
-// kernel are written before the launch that reads them and never rewritten
-// until that launch has completed (stage events), so the kernel boundary
-// orders every host write before the device reads it.
-struct PinnedBuf {
-  void* ptr = nullptr;
-  size_t cap = 0;
-  int ensure(size_t bytes, bool coherent = false) {
-    if (bytes <= cap) return IKBO_OK;
-    if (ptr) (void)hipHostFree(ptr);
-    ptr = nullptr;
-    cap = 0;
-    size_t want = std::max<size_t>(bytes, 4096);
-    hipError_t e = hipHostMalloc(&ptr, want, coherent ? hipHostMallocCoherent : hipHostMallocDefault);
-    if (e != hipSuccess) {
-      ptr = nullptr;
-      return fail(IKBO_ERR_NOMEM, std::string("hipHostMalloc: ") + hipGetErrorString(e));
-    }
-    cap = want;
-    return IKBO_OK;
-  }
-  void release() {
-    if (ptr) (void)hipHostFree(ptr);
-    ptr = nullptr;
-    cap = 0;
-  }
-};
 
 struct Plan {
   int device = -1;
@@ -318,12 +236,6 @@ int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n
   return IKBO_OK;
 }
 
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  if (!a || !b || !na || !nb) return false;
-  const char* pa = static_cast<const char*>(a);
-  const char* pb = static_cast<const char*>(b);
-  return pa < pb + nb && pb < pa + na;
-}
 
 int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* k, const void* v, float scale,
                    void* out_cand, void* out_user, hipStream_t stream) {
@@ -479,63 +391,6 @@ struct BcastWs {
 };
 std::mutex g_bcast_mu;
 std::map<int, BcastWs*> g_bcast;
-
-// IKBO linear compression: packed W blocks, the user-result workspace and the
-// mapping error counter, bound to one device.
-struct Lce {
-  int device = -1;
-  bool nested = false;  // created for three levels (user -> vendor -> item)
-  int32_t M = 0, K_u = 0, K_v = 0, K_c = 0, M_pad = 0, K_u_pad = 0, K_v_pad = 0, K_c_pad = 0;
-  DevBuf wu, wv, wc, y, yv, errors, order;
-  bool timing = false;
-  std::vector<hipEvent_t> tev;  // 4 per timed call: upper levels start/end, item GEMM start/end
-  std::vector<char> timed_user;
-  int n_timed = 0;
-  ~Lce() {
-    for (hipEvent_t e : tev) (void)hipEventDestroy(e);
-    wu.release();
-    wv.release();
-    wc.release();
-    y.release();
-    yv.release();
-    errors.release();
-    order.release();
-  }
-};
-
-int32_t round_up(int32_t x, int32_t m) { return (x + m - 1) / m * m; }
-
-// Target-attention backward: the work lists of the last calls (two pinned
-// buffers used alternately, each guarded by an event after its last reader, the
-// kernels read them in place) and the sorted-row workspace.
-struct Bwd {
-  int device = -1;
-  PinnedBuf stage[2];
-  hipEvent_t stage_ev[2] = {nullptr, nullptr};
-  bool stage_used[2] = {false, false};
-  int next = 0;
-  int n_cu = 0;
-  DevBuf ws;              // qrow [R + pad] int32, then lse and dd [H][R + pad] fp32
-  DevBuf ws_dq, ws_rec;   // split dQ partials and their row records
-  DevBuf ws_rows;         // Q and dO rows in user-sorted order, per head (zeroed padding)
-  HostPlan hp;            // dQ work items (the forward's planner) and the CSR grouping
-  std::vector<WorkItem> items_b;
-  int64_t n_items_a = 0, n_items_b = 0, n_groups = 0;
-  bool timing = false;
-  std::vector<hipEvent_t> tev;  // 4 per timed call: dQ kernel start/end, dK/dV kernel start/end
-  int n_timed = 0;
-  ~Bwd() {
-    for (hipEvent_t e : tev) (void)hipEventDestroy(e);
-    for (int i = 0; i < 2; ++i) {
-      if (stage_ev[i]) (void)hipEventDestroy(stage_ev[i]);
-      stage[i].release();
-    }
-    ws.release();
-    ws_dq.release();
-    ws_rec.release();
-    ws_rows.release();
-  }
-};
 
 }  // namespace
 
@@ -814,494 +669,6 @@ int ikbo_attn_fwd_materialized(const void* q_cand, const void* k_user, const voi
   } catch (...) {
     return fail(IKBO_ERR_INVALID_ARG, "unexpected host error");
   }
-}
-
-}  // extern "C"
-
-namespace {
-
-int lce_create(void** lce, const void* w, int32_t M, int32_t K_u, int32_t K_v, int32_t K_c, int32_t ldw, bool nested,
-               void* stream_) {
-  if (!lce) return fail(IKBO_ERR_INVALID_ARG, "lce is null");
-  *lce = nullptr;
-  if (!w) return fail(IKBO_ERR_INVALID_ARG, "w is null");
-  if (M < 1 || K_u < 0 || K_v < 0 || K_c < 0 || K_u + K_v + K_c < 1)
-    return fail(IKBO_ERR_INVALID_ARG, "M >= 1, K blocks >= 0 and a positive total K required");
-  if (ldw < K_u + K_v + K_c) return fail(IKBO_ERR_INVALID_ARG, "ldw must be >= the total K");
-  if (static_cast<int64_t>(M) * ldw > std::numeric_limits<int32_t>::max()) return fail(IKBO_ERR_INVALID_ARG, "W too large");
-  Lce* l = new (std::nothrow) Lce();
-  if (!l) return fail(IKBO_ERR_NOMEM, "lce allocation");
-  hipError_t e = hipGetDevice(&l->device);
-  if (e != hipSuccess) {
-    delete l;
-    return fail_hip(e, "hipGetDevice");
-  }
-  l->nested = nested;
-  l->M = M;
-  l->K_u = K_u;
-  l->K_v = K_v;
-  l->K_c = K_c;
-  l->M_pad = round_up(M, ikbo::kLceTileM);
-  l->K_u_pad = round_up(K_u, ikbo::kLceTileK);
-  l->K_v_pad = round_up(K_v, ikbo::kLceTileK);
-  l->K_c_pad = round_up(K_c, ikbo::kLceTileK);
-  int rc;
-  if ((rc = l->wu.ensure(static_cast<size_t>(l->M_pad) * std::max(l->K_u_pad, 1) * 2, false)) != IKBO_OK ||
-      (rc = l->wv.ensure(static_cast<size_t>(l->M_pad) * std::max(l->K_v_pad, 1) * 2, false)) != IKBO_OK ||
-      (rc = l->wc.ensure(static_cast<size_t>(l->M_pad) * std::max(l->K_c_pad, 1) * 2, false)) != IKBO_OK ||
-      (rc = l->errors.ensure(sizeof(int32_t), true)) != IKBO_OK) {
-    delete l;
-    return rc;
-  }
-  e = ikbo::launch_lce_pack(w, M, ldw, K_u, K_v, K_c, l->M_pad, l->K_u_pad, l->K_v_pad, l->K_c_pad, l->wu.ptr,
-                            l->wv.ptr, l->wc.ptr, static_cast<hipStream_t>(stream_));
-  if (e != hipSuccess) {
-    delete l;
-    return fail_hip(e, "pack launch");
-  }
-  *lce = l;
-  return IKBO_OK;
-}
-
-// One level's GEMM: y_out (mode 0) or out (mode 1) for `batches` elements of x,
-// with the parent level's results y_in added through map.
-hipError_t lce_level(const Lce* l, const void* wblk, int32_t K_pad, const void* x, int32_t K, int32_t N,
-                     int32_t n_tiles, const float* y_in, const int32_t* map, int32_t n_parent, float* y_out,
-                     void* out, const int32_t* order, int mode, int32_t batches, hipStream_t stream, hipEvent_t* ev) {
-  ikbo::LceParams p{};
-  p.w = wblk;
-  p.ldw = std::max(K_pad, 1);
-  p.x = x;
-  p.K = K;
-  p.N = N;
-  p.M = l->M;
-  p.m_tiles = l->M_pad / ikbo::kLceTileM;
-  p.n_tiles = n_tiles;
-  p.y_in = y_in;
-  p.map = map;
-  p.n_parent = n_parent;
-  p.y_out = y_out;
-  p.out = out;
-  p.errors = static_cast<int32_t*>(l->errors.ptr);
-  p.order = order;
-  return ikbo::launch_lce_gemm(p, mode, batches, stream, ev);
-}
-
-hipEvent_t* lce_timing_slot(Lce* l, bool upper) {
-  if (!l->timing || l->n_timed >= kMaxTimed) return nullptr;
-  while (l->tev.size() < static_cast<size_t>(4 * (l->n_timed + 1))) {
-    hipEvent_t ev;
-    if (hipEventCreate(&ev) != hipSuccess) return nullptr;
-    l->tev.push_back(ev);
-  }
-  hipEvent_t* te = &l->tev[4 * l->n_timed];
-  l->timed_user.resize(l->n_timed + 1);
-  l->timed_user[l->n_timed] = upper;
-  ++l->n_timed;
-  return te;
-}
-
-// Checks shared by the two forward calls: device, sizes, N, grid limits.
-int lce_check(const Lce* l, int32_t n_parents_max, int32_t n_cand, int32_t N, int64_t* n_tiles_out) {
-  int dev = -1;
-  IKBO_HIP(hipGetDevice(&dev));
-  if (dev != l->device) return fail(IKBO_ERR_INVALID_ARG, "lce belongs to another device");
-  if (N < ikbo::kLceAlignN || N % ikbo::kLceAlignN != 0)
-    return fail(IKBO_ERR_UNSUPPORTED, "N must be a positive multiple of 128");
-  const int32_t n_tiles = (N + ikbo::kLceTileN - 1) / ikbo::kLceTileN;
-  const int64_t per = static_cast<int64_t>(l->M_pad / ikbo::kLceTileM) * n_tiles;
-  if (static_cast<int64_t>(std::max(n_parents_max, n_cand)) * per > std::numeric_limits<int32_t>::max() ||
-      static_cast<int64_t>(std::max(n_parents_max, n_cand)) * l->M * N > std::numeric_limits<int32_t>::max() * 8LL)
-    return fail(IKBO_ERR_INVALID_ARG, "problem too large");
-  *n_tiles_out = n_tiles;
-  return IKBO_OK;
-}
-
-}  // namespace
-
-extern "C" {
-
-int ikbo_lce_create(void** lce, const void* w, int32_t M, int32_t K_u, int32_t K_c, int32_t ldw, void* stream_) {
-  try {
-    return lce_create(lce, w, M, K_u, 0, K_c, ldw, false, stream_);
-  } catch (...) {
-    return fail(IKBO_ERR_NOMEM, "unexpected host error");
-  }
-}
-
-int ikbo_lce3_create(void** lce, const void* w, int32_t M, int32_t K_u, int32_t K_v, int32_t K_c, int32_t ldw,
-                     void* stream_) {
-  try {
-    return lce_create(lce, w, M, K_u, K_v, K_c, ldw, true, stream_);
-  } catch (...) {
-    return fail(IKBO_ERR_NOMEM, "unexpected host error");
-  }
-}
-
-int ikbo_lce_fwd(void* lce, const void* x_user, const void* x_cand, const int32_t* cand_to_user, int32_t n_users,
-                 int32_t n_cand, int32_t N, void* out, void* stream_) {
-  try {
-    if (!lce) return fail(IKBO_ERR_INVALID_ARG, "lce is null");
-    Lce* l = static_cast<Lce*>(lce);
-    if (l->nested) return fail(IKBO_ERR_INVALID_ARG, "a three-level handle takes ikbo_lce3_fwd");
-    hipStream_t stream = static_cast<hipStream_t>(stream_);
-    if (n_users < 0 || n_cand < 0) return fail(IKBO_ERR_INVALID_ARG, "n_users and n_cand must be >= 0");
-    int64_t n_tiles = 0;
-    int rc = lce_check(l, n_users, n_cand, N, &n_tiles);
-    if (rc != IKBO_OK) return rc;
-    if (n_cand == 0) return IKBO_OK;
-    if (n_users == 0) return fail(IKBO_ERR_BAD_MAPPING, "candidates present but n_users == 0");
-    if (!out || !cand_to_user || (l->K_c > 0 && !x_cand) || (l->K_u > 0 && !x_user))
-      return fail(IKBO_ERR_INVALID_ARG, "null tensor pointer");
-    const uintptr_t align_or = reinterpret_cast<uintptr_t>(x_user) | reinterpret_cast<uintptr_t>(x_cand) |
-                               reinterpret_cast<uintptr_t>(out);
-    if (align_or & 15) return fail(IKBO_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
-    const size_t out_bytes = static_cast<size_t>(n_cand) * l->M * N * 2;
-    if (overlaps(out, out_bytes, x_user, static_cast<size_t>(n_users) * l->K_u * N * 2) ||
-        overlaps(out, out_bytes, x_cand, static_cast<size_t>(n_cand) * l->K_c * N * 2) ||
-        overlaps(out, out_bytes, cand_to_user, static_cast<size_t>(n_cand) * 4))
-      return fail(IKBO_ERR_INVALID_ARG, "out aliases an input");
-    const int64_t per = static_cast<int64_t>(l->M_pad / ikbo::kLceTileM) * n_tiles;
-    if (l->K_u > 0 && (rc = l->y.ensure(static_cast<size_t>(n_users) * per * ikbo::kLceYTileFloats * 4, false)) != IKBO_OK)
-      return rc;
-    if ((rc = l->order.ensure(static_cast<size_t>(n_cand) * 4, false)) != IKBO_OK) return rc;
-    hipError_t e = ikbo::launch_lce_order(cand_to_user, n_cand, n_users, static_cast<int32_t*>(l->order.ptr), stream);
-    if (e != hipSuccess) return fail_hip(e, "candidate ordering launch");
-    hipEvent_t* te = lce_timing_slot(l, l->K_u > 0);
-    float* yu = l->K_u > 0 ? static_cast<float*>(l->y.ptr) : nullptr;
-    if (l->K_u > 0) {  // user GEMM at the user batch
-      e = lce_level(l, l->wu.ptr, l->K_u_pad, x_user, l->K_u, N, static_cast<int32_t>(n_tiles), nullptr, nullptr, 0, yu,
-                    nullptr, nullptr, 0, n_users, stream, te);
-      if (e != hipSuccess) return fail_hip(e, "user GEMM launch");
-    }
-    // candidate GEMM with the gathered user result added in the epilogue
-    e = lce_level(l, l->wc.ptr, l->K_c_pad, x_cand, l->K_c, N, static_cast<int32_t>(n_tiles), yu, cand_to_user, n_users,
-                  nullptr, out, static_cast<const int32_t*>(l->order.ptr), 1, n_cand, stream, te ? te + 2 : nullptr);
-    if (e != hipSuccess) return fail_hip(e, "candidate GEMM launch");
-    return IKBO_OK;
-  } catch (...) {
-    return fail(IKBO_ERR_NOMEM, "unexpected host error");
-  }
-}
-
-int ikbo_lce3_fwd(void* lce, const void* x_user, const void* x_vendor, const void* x_cand,
-                  const int32_t* vendor_to_user, const int32_t* cand_to_vendor, int32_t n_users, int32_t n_vendors,
-                  int32_t n_cand, int32_t N, void* out, void* stream_) {
-  try {
-    if (!lce) return fail(IKBO_ERR_INVALID_ARG, "lce is null");
-    Lce* l = static_cast<Lce*>(lce);
-    if (!l->nested) return fail(IKBO_ERR_INVALID_ARG, "a two-level handle takes ikbo_lce_fwd");
-    hipStream_t stream = static_cast<hipStream_t>(stream_);
-    if (n_users < 0 || n_vendors < 0 || n_cand < 0) return fail(IKBO_ERR_INVALID_ARG, "counts must be >= 0");
-    int64_t n_tiles = 0;
-    int rc = lce_check(l, std::max(n_users, n_vendors), n_cand, N, &n_tiles);
-    if (rc != IKBO_OK) return rc;
-    if (n_cand == 0) return IKBO_OK;
-    if (n_vendors == 0 || n_users == 0) return fail(IKBO_ERR_BAD_MAPPING, "items present but no vendors or users");
-    if (!out || !cand_to_vendor || !vendor_to_user || (l->K_c > 0 && !x_cand) || (l->K_v > 0 && !x_vendor) ||
-        (l->K_u > 0 && !x_user))
-      return fail(IKBO_ERR_INVALID_ARG, "null tensor pointer");
-    const uintptr_t align_or = reinterpret_cast<uintptr_t>(x_user) | reinterpret_cast<uintptr_t>(x_vendor) |
-                               reinterpret_cast<uintptr_t>(x_cand) | reinterpret_cast<uintptr_t>(out);
-    if (align_or & 15) return fail(IKBO_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
-    const size_t out_bytes = static_cast<size_t>(n_cand) * l->M * N * 2;
-    if (overlaps(out, out_bytes, x_user, static_cast<size_t>(n_users) * l->K_u * N * 2) ||
-        overlaps(out, out_bytes, x_vendor, static_cast<size_t>(n_vendors) * l->K_v * N * 2) ||
-        overlaps(out, out_bytes, x_cand, static_cast<size_t>(n_cand) * l->K_c * N * 2) ||
-        overlaps(out, out_bytes, cand_to_vendor, static_cast<size_t>(n_cand) * 4) ||
-        overlaps(out, out_bytes, vendor_to_user, static_cast<size_t>(n_vendors) * 4))
-      return fail(IKBO_ERR_INVALID_ARG, "out aliases an input");
-    const int64_t per = static_cast<int64_t>(l->M_pad / ikbo::kLceTileM) * n_tiles;
-    if ((l->K_u > 0 && (rc = l->y.ensure(static_cast<size_t>(n_users) * per * ikbo::kLceYTileFloats * 4, false)) != IKBO_OK) ||
-        (rc = l->yv.ensure(static_cast<size_t>(n_vendors) * per * ikbo::kLceYTileFloats * 4, false)) != IKBO_OK ||
-        (rc = l->order.ensure(static_cast<size_t>(n_cand) * 4, false)) != IKBO_OK)
-      return rc;
-    hipError_t e = ikbo::launch_lce_order(cand_to_vendor, n_cand, n_vendors, static_cast<int32_t*>(l->order.ptr), stream);
-    if (e != hipSuccess) return fail_hip(e, "item ordering launch");
-    hipEvent_t* te = lce_timing_slot(l, true);
-    hipEvent_t ev_upper[2] = {te ? te[0] : nullptr, nullptr};
-    float* yu = l->K_u > 0 ? static_cast<float*>(l->y.ptr) : nullptr;
-    if (l->K_u > 0) {  // users
-      e = lce_level(l, l->wu.ptr, l->K_u_pad, x_user, l->K_u, N, static_cast<int32_t>(n_tiles), nullptr, nullptr, 0, yu,
-                    nullptr, nullptr, 0, n_users, stream, te ? ev_upper : nullptr);
-      if (e != hipSuccess) return fail_hip(e, "user GEMM launch");
-    }
-    // vendors, each with its user's result added; the vendor GEMM runs even when
-    // K_v = 0 (it then forwards the user result to the vendor batch)
-    hipEvent_t ev_v[2] = {te && l->K_u == 0 ? te[0] : nullptr, te ? te[1] : nullptr};
-    e = lce_level(l, l->wv.ptr, l->K_v_pad, x_vendor, l->K_v, N, static_cast<int32_t>(n_tiles), yu, vendor_to_user,
-                  n_users, static_cast<float*>(l->yv.ptr), nullptr, nullptr, 0, n_vendors, stream, te ? ev_v : nullptr);
-    if (e != hipSuccess) return fail_hip(e, "vendor GEMM launch");
-    // items, each with its vendor's result added
-    e = lce_level(l, l->wc.ptr, l->K_c_pad, x_cand, l->K_c, N, static_cast<int32_t>(n_tiles),
-                  static_cast<const float*>(l->yv.ptr), cand_to_vendor, n_vendors, nullptr, out,
-                  static_cast<const int32_t*>(l->order.ptr), 1, n_cand, stream, te ? te + 2 : nullptr);
-    if (e != hipSuccess) return fail_hip(e, "item GEMM launch");
-    return IKBO_OK;
-  } catch (...) {
-    return fail(IKBO_ERR_NOMEM, "unexpected host error");
-  }
-}
-
-int ikbo_lce_errors(void* lce, int64_t* count) {
-  if (!lce || !count) return fail(IKBO_ERR_INVALID_ARG, "null argument");
-  Lce* l = static_cast<Lce*>(lce);
-  int cur = -1;
-  IKBO_HIP(hipGetDevice(&cur));
-  if (cur != l->device) return fail(IKBO_ERR_INVALID_ARG, "lce belongs to another device");
-  IKBO_HIP(hipDeviceSynchronize());
-  int32_t v = 0;
-  IKBO_HIP(hipMemcpy(&v, l->errors.ptr, sizeof(v), hipMemcpyDeviceToHost));
-  IKBO_HIP(hipMemset(l->errors.ptr, 0, sizeof(int32_t)));
-  *count = v;
-  return IKBO_OK;
-}
-
-int ikbo_lce_timing(void* lce, int32_t enable) {
-  if (!lce) return fail(IKBO_ERR_INVALID_ARG, "lce is null");
-  Lce* l = static_cast<Lce*>(lce);
-  l->timing = enable != 0;
-  l->n_timed = 0;
-  return IKBO_OK;
-}
-
-int ikbo_lce_timing_read(void* lce, float* user_ms, float* cand_ms, int32_t max_n, int32_t* n) {
-  if (!lce || !n || max_n < 0 || (max_n > 0 && (!user_ms || !cand_ms))) return fail(IKBO_ERR_INVALID_ARG, "null argument");
-  Lce* l = static_cast<Lce*>(lce);
-  const int m = std::min<int>(l->n_timed, max_n);
-  for (int i = 0; i < m; ++i) {
-    user_ms[i] = 0.0f;
-    if (l->timed_user[i]) {
-      IKBO_HIP(hipEventSynchronize(l->tev[4 * i + 1]));
-      IKBO_HIP(hipEventElapsedTime(&user_ms[i], l->tev[4 * i], l->tev[4 * i + 1]));
-    }
-    IKBO_HIP(hipEventSynchronize(l->tev[4 * i + 3]));
-    IKBO_HIP(hipEventElapsedTime(&cand_ms[i], l->tev[4 * i + 2], l->tev[4 * i + 3]));
-  }
-  *n = m;
-  return IKBO_OK;
-}
-
-void ikbo_lce_destroy(void* lce) {
-  if (!lce) return;
-  Lce* l = static_cast<Lce*>(lce);
-  int cur = -1;
-  if (hipGetDevice(&cur) == hipSuccess) {
-    (void)hipSetDevice(l->device);
-    (void)hipDeviceSynchronize();
-    (void)hipSetDevice(cur);
-  }
-  delete l;
-}
-
-int ikbo_bwd_create(void** bwd) {
-  try {
-    if (!bwd) return fail(IKBO_ERR_INVALID_ARG, "bwd is null");
-    *bwd = nullptr;
-    Bwd* b = new (std::nothrow) Bwd();
-    if (!b) return fail(IKBO_ERR_NOMEM, "bwd allocation");
-    hipError_t e = hipGetDevice(&b->device);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&b->n_cu, hipDeviceAttributeMultiprocessorCount, b->device);
-    for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&b->stage_ev[i], hipEventDisableTiming);
-    if (e != hipSuccess) {
-      delete b;
-      return fail_hip(e, "bwd create");
-    }
-    *bwd = b;
-    return IKBO_OK;
-  } catch (...) {
-    return fail(IKBO_ERR_NOMEM, "unexpected host error");
-  }
-}
-
-int ikbo_attn_bwd(void* bwd, const int32_t* user_offsets, const int32_t* cand_to_user, int32_t n_users, int32_t n_cand,
-                  int32_t n_q, int32_t H, int32_t d, float scale, const void* q_cand, const void* k_user,
-                  const void* v_user, const void* out, const void* dout, void* dq_cand, void* dk_user, void* dv_user,
-                  void* stream_) {
-  try {
-    if (!bwd) return fail(IKBO_ERR_INVALID_ARG, "bwd is null");
-    Bwd* b = static_cast<Bwd*>(bwd);
-    hipStream_t stream = static_cast<hipStream_t>(stream_);
-    int dev = -1;
-    IKBO_HIP(hipGetDevice(&dev));
-    if (dev != b->device) return fail(IKBO_ERR_INVALID_ARG, "bwd belongs to another device");
-    if (n_users < 0 || n_cand < 0 || n_q < 1 || H < 1) return fail(IKBO_ERR_INVALID_ARG, "n_users, n_cand >= 0 and n_q, H >= 1 required");
-    if (d != ikbo::kBwdHeadDim) return fail(IKBO_ERR_UNSUPPORTED, "the backward takes head dim 128");
-    if (!user_offsets || (n_cand > 0 && !cand_to_user)) return fail(IKBO_ERR_INVALID_ARG, "null mapping array");
-    std::string err;
-    int rc = ikbo::check_offsets(user_offsets, n_users, &err);
-    if (rc != ikbo::kOk) return fail(rc, err);
-    const int64_t T = n_users > 0 ? user_offsets[n_users] : 0;
-    // dQ items: the forward's work list (row tiles of every user and head, long
-    // key ranges split into chunks, longest first) and its CSR grouping.
-    PlanParams pp;
-    pp.bm = ikbo::kBwdRowsA;
-    pp.bn = ikbo::kBwdKeysA;
-    pp.grid_slots = std::max(1, 2 * b->n_cu);
-    pp.min_chunk = 256;
-    pp.allow_split = static_cast<int64_t>(n_cand) * n_q < ikbo::kBwdMaxSplitRows && !env_int("IKBO_NO_SPLIT", 0);
-    rc = ikbo::build_plan(user_offsets, cand_to_user, n_users, n_cand, n_q, H, false, pp, &b->hp, &err);
-    if (rc != ikbo::kOk) return fail(rc, err);
-    if (T == 0) return IKBO_OK;  // no keys: no gradient to write (and every query gradient row would be empty)
-    const int64_t R = static_cast<int64_t>(n_cand) * n_q;
-    const size_t qb = static_cast<size_t>(R) * H * d * 2, kb = static_cast<size_t>(T) * H * d * 2;
-    if (n_cand > 0 && (!q_cand || !out || !dout || !dq_cand)) return fail(IKBO_ERR_INVALID_ARG, "null query-side tensor");
-    if (!k_user || !v_user || !dk_user || !dv_user) return fail(IKBO_ERR_INVALID_ARG, "null key-side tensor");
-    const uintptr_t align_or = reinterpret_cast<uintptr_t>(q_cand) | reinterpret_cast<uintptr_t>(k_user) |
-                               reinterpret_cast<uintptr_t>(v_user) | reinterpret_cast<uintptr_t>(out) |
-                               reinterpret_cast<uintptr_t>(dout) | reinterpret_cast<uintptr_t>(dq_cand) |
-                               reinterpret_cast<uintptr_t>(dk_user) | reinterpret_cast<uintptr_t>(dv_user);
-    if (align_or & 15) return fail(IKBO_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
-    const void* ins[5] = {q_cand, k_user, v_user, out, dout};
-    const size_t in_sz[5] = {qb, kb, kb, qb, qb};
-    void* outs[3] = {dq_cand, dk_user, dv_user};
-    const size_t out_sz[3] = {qb, kb, kb};
-    for (int i = 0; i < 3; ++i) {
-      if (out_sz[i] == 0) continue;
-      for (int j = 0; j < 5; ++j)
-        if (in_sz[j] && overlaps(outs[i], out_sz[i], ins[j], in_sz[j])) return fail(IKBO_ERR_INVALID_ARG, "a gradient aliases an input");
-      for (int j = i + 1; j < 3; ++j)
-        if (out_sz[j] && overlaps(outs[i], out_sz[i], outs[j], out_sz[j])) return fail(IKBO_ERR_INVALID_ARG, "gradients overlap");
-    }
-    // dK/dV items: every kBwdKeysB keys of every user and head, most rows first.
-    b->items_b.clear();
-    for (int32_t u = 0; u < n_users; ++u) {
-      const int32_t L = user_offsets[u + 1] - user_offsets[u];
-      for (int32_t h = 0; h < H; ++h)
-        for (int32_t k0 = 0; k0 < L; k0 += ikbo::kBwdKeysB) {
-          WorkItem w{};
-          w.kv_base = user_offsets[u];
-          w.row_base = b->hp.cand_offsets[u];
-          w.row0 = 0;
-          w.nrows = b->hp.counts[u] * n_q;
-          w.k0 = k0;
-          w.k1 = std::min(L, k0 + ikbo::kBwdKeysB);
-          w.h = h;
-          w.grp = -1;
-          b->items_b.push_back(w);
-        }
-    }
-    std::stable_sort(b->items_b.begin(), b->items_b.end(),
-                     [](const WorkItem& x, const WorkItem& y) { return x.nrows > y.nrows; });
-    const int64_t na = static_cast<int64_t>(b->hp.items.size()), nb = static_cast<int64_t>(b->items_b.size());
-    if (na > std::numeric_limits<int32_t>::max() || nb > std::numeric_limits<int32_t>::max() ||
-        R + ikbo::kBwdPad > std::numeric_limits<int32_t>::max())
-      return fail(IKBO_ERR_INVALID_ARG, "problem too large");
-    b->n_items_a = na;
-    b->n_items_b = nb;
-    b->n_groups = b->hp.n_groups;
-    // workspace
-    const size_t rp = static_cast<size_t>(R + ikbo::kBwdPad);
-    if ((rc = b->ws.ensure(rp * 4 * (1 + 2 * static_cast<size_t>(H)), false)) != IKBO_OK) return rc;
-    // Sorted Q and dO copies, zero-filled when allocated: the padding rows the
-    // dK/dV kernel may read hold zeros or rows of an earlier call, finite either way.
-    const size_t rows_bytes = static_cast<size_t>(H) * rp * ikbo::kBwdHeadDim * 2;
-    if ((rc = b->ws_rows.ensure(2 * rows_bytes, true)) != IKBO_OK) return rc;
-    const size_t slot_rows = static_cast<size_t>(b->hp.n_slots) * ikbo::kBwdRowsA;
-    if (slot_rows > 0 && ((rc = b->ws_dq.ensure(slot_rows * ikbo::kBwdHeadDim * 4, false)) != IKBO_OK ||
-                          (rc = b->ws_rec.ensure(slot_rows * 16, false)) != IKBO_OK))
-      return rc;
-    // work lists into the next pinned buffer, once its last reader is done
-    const size_t items_bytes = static_cast<size_t>(na + nb) * sizeof(WorkItem);
-    const size_t bytes = items_bytes + static_cast<size_t>(std::max(n_cand, 1)) * 4;
-    const int si = b->next;
-    b->next ^= 1;
-    if (b->stage_used[si]) IKBO_HIP(hipEventSynchronize(b->stage_ev[si]));
-    if ((rc = b->stage[si].ensure(bytes)) != IKBO_OK) return rc;
-    char* base = static_cast<char*>(b->stage[si].ptr);
-    std::memcpy(base, b->hp.items.data(), static_cast<size_t>(na) * sizeof(WorkItem));
-    std::memcpy(base + na * sizeof(WorkItem), b->items_b.data(), static_cast<size_t>(nb) * sizeof(WorkItem));
-    if (n_cand > 0) std::memcpy(base + items_bytes, b->hp.cand_perm.data(), static_cast<size_t>(n_cand) * 4);
-    hipEvent_t* te = nullptr;
-    if (b->timing && b->n_timed < kMaxTimed) {
-      while (b->tev.size() < static_cast<size_t>(4 * (b->n_timed + 1))) {
-        hipEvent_t ev;
-        IKBO_HIP(hipEventCreate(&ev));
-        b->tev.push_back(ev);
-      }
-      te = &b->tev[4 * b->n_timed];
-      ++b->n_timed;
-    }
-    ikbo::BwdParams p{};
-    p.q = q_cand;
-    p.k = k_user;
-    p.v = v_user;
-    p.o = out;
-    p.dout = dout;
-    p.dq = dq_cand;
-    p.dk = dk_user;
-    p.dv = dv_user;
-    p.cand_perm = reinterpret_cast<const int32_t*>(base + items_bytes);
-    p.qrow = static_cast<int32_t*>(b->ws.ptr);
-    p.lse = reinterpret_cast<float*>(p.qrow + rp);
-    p.dd = p.lse + rp * H;
-    p.qs = static_cast<uint16_t*>(b->ws_rows.ptr);
-    p.dos = p.qs + rows_bytes / 2;
-    p.ws_dq = static_cast<float*>(b->ws_dq.ptr);
-    p.ws_rec = static_cast<float*>(b->ws_rec.ptr);
-    p.rows_total = static_cast<int32_t>(R);
-    p.H = H;
-    p.n_q = n_q;
-    p.scale = scale;
-    p.scale_log2 = scale * 1.4426950408889634f;
-    p.items = reinterpret_cast<const WorkItem*>(base);
-    // timing: the dQ span runs from the dQ kernel's start to the merge's end
-    hipEvent_t ev_dq[2] = {te ? te[0] : nullptr, te && b->n_groups == 0 ? te[1] : nullptr};
-    hipError_t e = ikbo::launch_bwd_dq(p, static_cast<int>(na), stream, te ? ev_dq : nullptr);
-    if (e != hipSuccess) return fail_hip(e, "dQ launch");
-    e = ikbo::launch_bwd_merge(p, static_cast<int>(b->n_groups), stream, te ? te[1] : nullptr);
-    if (e != hipSuccess) return fail_hip(e, "dQ merge launch");
-    p.items = reinterpret_cast<const WorkItem*>(base) + na;
-    e = ikbo::launch_bwd_dkv(p, static_cast<int>(nb), stream, te ? te + 2 : nullptr);
-    if (e != hipSuccess) return fail_hip(e, "dK/dV launch");
-    IKBO_HIP(hipEventRecord(b->stage_ev[si], stream));
-    b->stage_used[si] = true;
-    return IKBO_OK;
-  } catch (...) {
-    return fail(IKBO_ERR_NOMEM, "unexpected host error");
-  }
-}
-
-int ikbo_bwd_info(void* bwd, int64_t* info, int32_t n_info) {
-  if (!bwd || !info || n_info < 0) return fail(IKBO_ERR_INVALID_ARG, "null argument");
-  Bwd* b = static_cast<Bwd*>(bwd);
-  const int64_t v[3] = {b->n_items_a, b->n_items_b, b->n_groups};
-  for (int i = 0; i < std::min<int32_t>(n_info, 3); ++i) info[i] = v[i];
-  return IKBO_OK;
-}
-
-int ikbo_bwd_timing(void* bwd, int32_t enable) {
-  if (!bwd) return fail(IKBO_ERR_INVALID_ARG, "bwd is null");
-  Bwd* b = static_cast<Bwd*>(bwd);
-  b->timing = enable != 0;
-  b->n_timed = 0;
-  return IKBO_OK;
-}
-
-int ikbo_bwd_timing_read(void* bwd, float* dq_ms, float* dkv_ms, int32_t max_n, int32_t* n) {
-  if (!bwd || !n || max_n < 0 || (max_n > 0 && (!dq_ms || !dkv_ms))) return fail(IKBO_ERR_INVALID_ARG, "null argument");
-  Bwd* b = static_cast<Bwd*>(bwd);
-  const int m = std::min<int>(b->n_timed, max_n);
-  for (int i = 0; i < m; ++i) {
-    IKBO_HIP(hipEventSynchronize(b->tev[4 * i + 1]));
-    IKBO_HIP(hipEventElapsedTime(&dq_ms[i], b->tev[4 * i], b->tev[4 * i + 1]));
-    IKBO_HIP(hipEventSynchronize(b->tev[4 * i + 3]));
-    IKBO_HIP(hipEventElapsedTime(&dkv_ms[i], b->tev[4 * i + 2], b->tev[4 * i + 3]));
-  }
-  *n = m;
-  return IKBO_OK;
-}
-
-void ikbo_bwd_destroy(void* bwd) {
-  if (!bwd) return;
-  Bwd* b = static_cast<Bwd*>(bwd);
-  int cur = -1;
-  if (hipGetDevice(&cur) == hipSuccess) {
-    (void)hipSetDevice(b->device);
-    (void)hipDeviceSynchronize();
-    (void)hipSetDevice(cur);
-  }
-  delete b;
 }
 
 }  // extern "C"
