@@ -316,6 +316,60 @@ def test_p13_determinism_across_runs_and_grids(name, waves):
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"grid {grid}"
 
 
+@pytest.mark.parametrize("case", ["c2_typical", "c3_skewed", "many_chunks"])
+@pytest.mark.parametrize("waves", ["pipe", "w8", "w4"])
+def test_split_groups_merge_each_launchs_partials(case, waves):
+    """Launches of one plan alternate V and -V.  The softmax weights do not
+    depend on V, so the -V outputs are the negated V outputs up to the
+    accumulation rounding of the PV products, which the matrix cores do not
+    round symmetrically in sign (observed: a few values in 10^5 differ by one
+    bf16 ulp); a merge that read a partial left by the previous launch would
+    instead flip whole rows.  Launches with the same inputs give the same
+    bits; the first meets the oracle bar."""
+    import torch
+    from broadcast_free_target_amd import (ikbo_attn_fwd_planned, ikbo_plan_build, ikbo_plan_create,
+                                           ikbo_plan_destroy, ikbo_plan_info)
+    os.environ["IKBO_KERNEL"] = waves
+    if case == "many_chunks":
+        lengths = (4096, 1, 700, 2048, 129, 64)
+        counts = (200, 3, 1, 65, 129, 2)
+        c2u = np.random.default_rng(77).permutation(np.repeat(np.arange(len(lengths)), counts)).astype(np.int32)
+        w = make_custom(4242, lengths, c2u, n_q=1, H=3, d=128, dtype="bf16", name="many_chunks")
+        os.environ["IKBO_MIN_CHUNK"] = "64"
+        os.environ["IKBO_SPLIT_SLOTS"] = "4096"
+    else:
+        w = _wl(case)
+    dev = upload(w)
+    say(f"case split merge per launch {case} waves={waves}")
+    neg_v = (-dev["v_user"].float()).to(dev["v_user"].dtype)
+    plan = ikbo_plan_create()
+    try:
+        ikbo_plan_build(plan, w.user_offsets, w.cand_to_user, w.n_users, w.n_cand, 1, w.H, w.d, 0, 0)
+        groups = ikbo_plan_info(plan)["n_groups"]
+        runs = []
+        for rep in range(4):
+            out = empty_out(w.raw("q_cand").shape, "bf16")
+            out.fill_(float("nan"))
+            v = dev["v_user"] if rep % 2 == 0 else neg_v
+            ikbo_attn_fwd_planned(plan, dev["q_cand"], None, dev["k_user"], v, w.scale, out)
+            torch.cuda.synchronize()
+            runs.append(out)
+    finally:
+        ikbo_plan_destroy(plan)
+    assert groups > 0
+    ref = runs[0].float()
+    for rep, r in enumerate(runs):
+        if rep % 2 == 0:
+            assert torch.equal(r.view(torch.int16), runs[0].view(torch.int16)), f"launch {rep}"
+            continue
+        diff = (r.float() + ref).abs()
+        ulp = torch.clamp(ref.abs(), min=2.0 ** -126) * 2.0 ** -6  # two bf16 ulps (one across a binade edge)
+        assert bool(torch.all(diff <= ulp)), f"launch {rep}: max |out(-V) + out(V)| = {diff.max().item():.3g}"
+        n_diff = int((diff > 0).sum().item())
+        assert n_diff <= r.numel() // 1000, f"launch {rep}: {n_diff} values differ from the negation"
+    assert_close(to_f64(runs[0]), _oracle_target(w), "bf16", case)
+
+
 # ---------------------------------------------------------------------------
 # materialised-broadcast comparator
 # ---------------------------------------------------------------------------
