@@ -1,7 +1,8 @@
 """Seeded synthetic inputs for IKBO target attention and IKBO linear compression.
 
 This package draws inputs only: sequence lengths, candidate-to-user mappings and
-N(0,1) tensors quantised to the dtype the kernel receives.  It holds none of the
+N(0,1) tensors quantised to the dtype the kernel receives (MXFP8 codes drawn with
+torch's E4M3 conversion and randomly drawn block scales).  It holds none of the
 attention or projection arithmetic, so both the fp64 oracle's tests and the GPU
 path can use it without sharing any of the method's code.
 """
@@ -27,3 +28,4 @@ from .lce import (  # noqa: F401
     make_lce_nested,
     make_lce_nested_custom,
 )
+from .mxfp8 import MX_NAMES, MxWorkload, make_mxfp8, make_mxfp8_custom  # noqa: F401
