@@ -67,6 +67,13 @@ SIGNATURES = {
     "ikbo_bwd_timing_read": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
                                             _I, _IP]),
     "ikbo_bwd_destroy": (None, [_P]),
+    "ikbo_mx_create": (ctypes.c_int, [ctypes.POINTER(_P)]),
+    "ikbo_attn_fwd_mxfp8": (ctypes.c_int, [_P, _IP, _IP, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "ikbo_mx_info": (ctypes.c_int, [_P, _LP, _I]),
+    "ikbo_mx_timing": (ctypes.c_int, [_P, _I]),
+    "ikbo_mx_timing_read": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
+                                           _I, _IP]),
+    "ikbo_mx_destroy": (None, [_P]),
 }
 
 _lib = None
@@ -312,6 +319,46 @@ def ikbo_bwd_timing_read(bwd, max_n: int = 4096):
 
 def ikbo_bwd_destroy(bwd) -> None:
     load_library().ikbo_bwd_destroy(bwd)
+
+
+def ikbo_mx_create() -> int:
+    h = _P()
+    _check(load_library().ikbo_mx_create(ctypes.byref(h)))
+    return h.value
+
+
+def ikbo_attn_fwd_mxfp8(mx, user_offsets_host, cand_to_user_host, n_users, n_cand, n_q, H, d, scale, q_codes,
+                        q_scales, k_codes, k_scales, v_codes, v_scales, out, stream=None) -> int:
+    """MXFP8 target attention; the mapping arrays are host int32 arrays, the
+    codes and scales uint8 device tensors, out a bf16 device tensor."""
+    offs = np.ascontiguousarray(user_offsets_host, dtype=np.int32)
+    c2u = np.ascontiguousarray(cand_to_user_host, dtype=np.int32)
+    return _check(load_library().ikbo_attn_fwd_mxfp8(
+        mx, _i32(offs), _i32(c2u) if c2u.size else None, n_users, n_cand, n_q, H, d, float(scale), _ptr(q_codes),
+        _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales), _ptr(out), _stream(stream)))
+
+
+def ikbo_mx_info(mx) -> dict:
+    a = (ctypes.c_int64 * 3)()
+    _check(load_library().ikbo_mx_info(mx, a, 3))
+    return {"n_items": a[0], "n_groups": a[1], "grid": a[2]}
+
+
+def ikbo_mx_timing(mx, enable: bool) -> int:
+    return _check(load_library().ikbo_mx_timing(mx, 1 if enable else 0))
+
+
+def ikbo_mx_timing_read(mx, max_n: int = 4096):
+    """Per-call (attention kernel, merge kernel) durations in ms of the timed calls."""
+    a = (ctypes.c_float * max(max_n, 1))()
+    b = (ctypes.c_float * max(max_n, 1))()
+    n = ctypes.c_int32(0)
+    _check(load_library().ikbo_mx_timing_read(mx, a, b, max_n, ctypes.byref(n)))
+    return list(a[:n.value]), list(b[:n.value])
+
+
+def ikbo_mx_destroy(mx) -> None:
+    load_library().ikbo_mx_destroy(mx)
 
 
 def ikbo_lce3_create(w, M, K_u, K_v, K_c, ldw=None, stream=None) -> int:

@@ -312,6 +312,58 @@ int ikbo_bwd_timing_read(void* bwd, float* dq_ms, float* dkv_ms, int32_t max_n, 
 void ikbo_bwd_destroy(void* bwd);
 
 /*
+ * MXFP8 IKBO target attention (TLX attention post, section 3: the micro-scaled
+ * FP8 variant; IKBO blog, section 3.1, Fig. 10 for the broadcast-free target
+ * attention it runs).  Inputs are E4M3 codes (OCP FP8: 4 exponent bits, bias
+ * 7, 3 mantissa bits, largest finite 448, S.1111.111 NaN) with one E8M0 scale
+ * (value 2^(s - 127), 255 NaN) per 32 elements along each product's
+ * contraction.  For candidate c of user u, query row r and head h:
+ *   x_j = scale * log2(e) * (q^ . k^_j) over the user's keys j, m = an integer
+ *   >= max_j x_j (the result does not depend on which), p_j = 2^(x_j - m);
+ *   P^ = p quantized per block of 32 keys (blocks start at the user's first
+ *   key): the block's scale is the smallest 2^e with max p <= 448 * 2^e and
+ *   each p_j / 2^e is rounded to E4M3 (nearest, ties to even); a block whose
+ *   maximum is below 2^-100 contributes nothing;
+ *   out = sum_j P^_j v^_j / sum_j p_j  (bf16; zero rows for users with no keys).
+ * Both products run on the block-scaled FP8 matrix instruction with fp32
+ * accumulation; long key ranges are split and merged as in the bf16 path.
+ *
+ * ikbo_mx_create: a handle owning the work lists (pinned host memory, two
+ *   alternating buffers) and the split partials (64 KB + 2 KB per slot).
+ * ikbo_attn_fwd_mxfp8: user_offsets [n_users + 1] and cand_to_user [n_cand]
+ *   are HOST int32 arrays; the tensors are device arrays, row-major uint8:
+ *     q_codes [n_cand, n_q, H, d]   q_scales [n_cand, n_q, H, d/32]
+ *     k_codes [T, H, d]             k_scales [T, H, d/32]
+ *     v_codes [T, H, d]             v_scales [NVB, H, d]
+ *   with T = user_offsets[n_users], NVB = sum_u ceil(L_u / 32) (user u's
+ *   blocks follow user u-1's; block b of u covers its keys 32b .. 32b+31, for
+ *   every head and column); out [n_cand, n_q, H, d] bf16.  Codes and out must
+ *   be 16-byte aligned, scales 4-byte aligned; d must be 128.  NaN codes or
+ *   scales are the caller's to avoid (they propagate).  Enqueues one kernel (two
+ *   when key ranges are split) on `stream` and returns without synchronising
+ *   (it may wait for the call before last on the same handle to finish reading
+ *   its work list).  Errors (INVALID_ARG: null or misaligned tensors, out
+ *   aliasing an input, bad sizes, non-finite scale; BAD_OFFSETS; BAD_MAPPING;
+ *   UNSUPPORTED: d != 128) launch nothing.  Calls on one handle must be
+ *   ordered on one stream.
+ * ikbo_mx_info: info[0] work items, info[1] split groups, info[2] workgroups of
+ *   the last call.
+ * ikbo_mx_timing / _timing_read: per-call durations of the attention kernel
+ *   and of the merge (0 when nothing was split), from events stamped by the
+ *   dispatches (at most 4096 calls between resets).
+ * ikbo_mx_destroy: frees the handle after synchronising its device.
+ */
+int ikbo_mx_create(void** mx);
+int ikbo_attn_fwd_mxfp8(void* mx, const int32_t* user_offsets, const int32_t* cand_to_user, int32_t n_users,
+                        int32_t n_cand, int32_t n_q, int32_t H, int32_t d, float scale, const void* q_codes,
+                        const void* q_scales, const void* k_codes, const void* k_scales, const void* v_codes,
+                        const void* v_scales, void* out, void* stream);
+int ikbo_mx_info(void* mx, int64_t* info, int32_t n_info);
+int ikbo_mx_timing(void* mx, int32_t enable);
+int ikbo_mx_timing_read(void* mx, float* attn_ms, float* merge_ms, int32_t max_n, int32_t* n);
+void ikbo_mx_destroy(void* mx);
+
+/*
  * Introspection of a built plan (host values), for tests and measurement:
  * info[0] work items, [1] grid of the persistent launch, [2] split groups,
  * [3] partial-result slots, [4] bytes of the split-KV workspace, [5] target

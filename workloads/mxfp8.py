@@ -7,11 +7,12 @@ the bf16 workloads without drawing their values.  The values are then drawn
 directly in the MX format, from a second PCG64 stream (seed + 500), in the
 order q, k, v:
 
-* element codes: torch's fp32 -> float8_e4m3fn conversion of N(0,1) * 16 draws
-  (every code finite: the draws stay far below 448);
-* block scale codes: E8M0 123 + U{-1, 0, 1, 2}, i.e. 2^-4 * 2^{-1..2}, one per
-  block, so dequantized values are about N(0,1) * 2^{-1..2} and every block
-  has its own scale.
+* per block of 32 elements an offset u ~ U{-1, 0, 1, 2}: the block's scale
+  code is E8M0 123 + u (2^(u - 4)) and its element codes are torch's fp32 ->
+  float8_e4m3fn conversion of N(0,1) * 16 * 2^-u draws, so every block has
+  its own scale and code magnitudes while the dequantized values stay about
+  N(0,1), as for the bf16 workloads (every code finite: the draws stay far
+  below 448).
 
 No scale is derived from the values: this module holds no part of the
 quantization rule the method applies to P.
@@ -66,14 +67,21 @@ class MxWorkload:
         return (self.q_codes, self.q_scales, self.k_codes, self.k_scales, self.v_codes, self.v_scales)
 
 
-def _codes(rng: np.random.Generator, shape) -> np.ndarray:
+def _blocked(rng: np.random.Generator, shape, along_last: bool, v_blocks=None):
+    """Codes [shape] and scale codes: blocks of 32 along the last axis
+    (along_last), or along the token axis with v_blocks = (number of blocks,
+    block of each token)."""
     import torch
-    x = rng.standard_normal(int(np.prod(shape)), dtype=np.float32) * np.float32(16.0)
-    return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy().reshape(shape).copy()
-
-
-def _scales(rng: np.random.Generator, shape) -> np.ndarray:
-    return (123 + rng.integers(-1, 2, size=shape, endpoint=True)).astype(np.uint8)
+    x = rng.standard_normal(int(np.prod(shape)), dtype=np.float32).reshape(shape) * np.float32(16.0)
+    if along_last:
+        u = rng.integers(-1, 2, size=shape[:-1] + (shape[-1] // _BLOCK,), endpoint=True)
+        x = x * np.repeat(np.exp2(-u), _BLOCK, axis=-1).astype(np.float32)
+    else:
+        nvb, blk_of_tok = v_blocks
+        u = rng.integers(-1, 2, size=(nvb,) + tuple(shape[1:]), endpoint=True)
+        x = x * np.exp2(-u).astype(np.float32)[blk_of_tok]
+    codes = torch.from_numpy(np.ascontiguousarray(x)).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    return codes, (123 + u).astype(np.uint8)
 
 
 def _structure(name: str):
@@ -109,12 +117,12 @@ def _fill(name, seed, lengths, cand_to_user, n_q, H, d=128) -> MxWorkload:
     np.cumsum(nblk, out=vbo[1:])
     C, T, NVB = int(cand_to_user.size), int(offs[-1]), int(vbo[-1])
     rng = np.random.Generator(np.random.PCG64(seed + _VALUE_SEED_OFFSET))
-    q_codes = _codes(rng, (C, n_q, H, d))
-    q_scales = _scales(rng, (C, n_q, H, d // _BLOCK))
-    k_codes = _codes(rng, (T, H, d))
-    k_scales = _scales(rng, (T, H, d // _BLOCK))
-    v_codes = _codes(rng, (T, H, d))
-    v_scales = _scales(rng, (NVB, H, d))
+    q_codes, q_scales = _blocked(rng, (C, n_q, H, d), True)
+    k_codes, k_scales = _blocked(rng, (T, H, d), True)
+    # V blocks: 32 keys of one user, per head and column
+    u_of_tok = np.repeat(np.arange(lengths.size), lengths)
+    blk_of_tok = vbo[u_of_tok] + (np.arange(T) - offs[u_of_tok]) // _BLOCK
+    v_codes, v_scales = _blocked(rng, (T, H, d), False, (NVB, blk_of_tok))
     return MxWorkload(name=name, seed=seed, n_users=int(lengths.size), n_cand=C, n_q=n_q, H=H, d=d,
                       lengths=lengths, user_offsets=offs.astype(np.int32),
                       cand_to_user=np.asarray(cand_to_user, dtype=np.int32), v_block_offsets=vbo.astype(np.int32),
