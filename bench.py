@@ -41,6 +41,8 @@ WORKLOAD_TEXT = {
     "c4_large": "large: 10000 candidates over 150 users, L~U[512,4096], n_q=4, H=8, d=128, bf16",
     "c5_fused": "fused self+target: 2048 candidates over 30 users, causal self over L~U[256,2048], H=4, d=128, bf16",
     "p_app11": "App. 11 shape: 32 users x 64 candidates, n_q=64, L=1024, H=2, d=128, bf16",
+    "mx_c2_typical": "MXFP8 typical request: 1024 candidates over 15 users, L~U[256,2048], n_q=1, H=4, d=128, E4M3 codes with E8M0 scales per 32",
+    "mx_c4_large": "MXFP8 large request: 10,000 candidates over 150 users, L~U[512,4096], n_q=4, H=8, d=128, E4M3 codes with E8M0 scales per 32",
     "bwd_c2_typical": "backward of the typical request: 1024 candidates over 15 users, L~U[256,2048], n_q=1, H=4, d=128, bf16",
     "bwd_c4_large": "backward of the large request: 10000 candidates over 150 users, L~U[512,4096], n_q=4, H=8, d=128, bf16",
     "lce3_typical": "three-level linear compression: 1024 items over 120 vendors over 15 users, M=433, K_u=682, K_v=K_c=681, N=256, bf16",
@@ -50,6 +52,9 @@ WORKLOAD_TEXT = {
 LCE_METRIC = "IKBO linear compression BF16 TFLOP/s (executed work) and FLOPs vs materialized broadcast"
 BWD_METRIC = "IKBO attn backward BF16 TFLOP/s (five products: S, dP, dV, dK, dQ)"
 BWD_KERNELS = ("ikbo_bwd_dq_kernel", "ikbo_bwd_dkv_kernel")
+MX_METRIC = "IKBO attn MXFP8 TFLOP/s (QK^T and PV on block-scaled FP8 MFMA)"
+MX_KERNEL = "ikbo_attn_mx_kernel"
+PEAK_FP8_TFLOPS = 5000.0
 LCE_KERNEL = "ikbo_lce_gemm_kernel<1>"  # candidate GEMM with the broadcast-add epilogue
 
 
@@ -117,6 +122,8 @@ def kernel_source_hash(files=("ikbo_kernels.hip", "ikbo_kernels.h", "ikbo_device
 
 
 LCE_SOURCES = ("ikbo_lce.hip", "ikbo_lce.h", "ikbo_device.h", "ikbo_api_lce.hip", "ikbo_api_common.h")
+MX_SOURCES = ("ikbo_mx.hip", "ikbo_mx.h", "ikbo_device.h", "ikbo_plan.cpp", "ikbo_plan.h", "ikbo_api_mx.hip",
+              "ikbo_api_common.h")
 BWD_SOURCES = ("ikbo_bwd.hip", "ikbo_bwd.h", "ikbo_device.h", "ikbo_plan.cpp", "ikbo_plan.h", "ikbo_api_bwd.hip",
                "ikbo_api_common.h")
 
@@ -126,8 +133,9 @@ def traffic_from_profiles(workload):
     was taken on the current kernel sources; else None."""
     lce = workload.startswith("lce")
     bwd = workload.startswith("bwd_")
+    mx = workload.startswith("mx_")
     name = (f"ikbo_lce_gemm_{workload}_pmc.json" if lce else f"ikbo_bwd_{workload}_pmc.json" if bwd
-            else f"ikbo_attn_bf16_{workload}_pmc.json")
+            else f"ikbo_attn_mx_{workload}_pmc.json" if mx else f"ikbo_attn_bf16_{workload}_pmc.json")
     path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
@@ -135,7 +143,7 @@ def traffic_from_profiles(workload):
         with open(path) as fh:
             s = json.load(fh)
         want = (kernel_source_hash(LCE_SOURCES) if lce else kernel_source_hash(BWD_SOURCES) if bwd
-                else kernel_source_hash())
+                else kernel_source_hash(MX_SOURCES) if mx else kernel_source_hash())
         if s.get("kernel_source_hash") != want:
             return None
         return float(s["hbm_bytes_per_launch"])
@@ -313,6 +321,108 @@ def main_bwd(args):
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_bwd(w, 24 if w.n_cand > 2000 else 128, 3)
+    print(json.dumps(result), flush=True)
+
+
+def mx_counts(w):
+    """FLOPs of the two products and the MXFP8 kernel's algorithmic bytes: K/V
+    codes and scales once per (user, head), Q codes and scales, bf16 output."""
+    f = 4.0 * w.n_q * w.d * w.H * float(np.dot(w.counts, w.lengths))
+    nvb = int(w.v_block_offsets[-1])
+    b = (2.0 * w.total_len * w.H * w.d + w.total_len * w.H * (w.d // 32) + nvb * w.H * w.d
+         + w.n_cand * w.n_q * w.H * (w.d + w.d // 32) + 2.0 * w.n_cand * w.n_q * w.H * w.d)
+    return f, b
+
+
+def cpu_baseline_mx(w, n_sample, reps):
+    """The fp64 MXFP8 oracle on the first n_sample candidates, scaled to the batch."""
+    from oracle import mxfp8_oracle as M
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    sl = slice(0, n_sample)
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        M.target_attention_mxfp8(w.q_codes[sl], w.q_scales[sl], w.k_codes, w.k_scales, w.v_codes, w.v_scales,
+                                 w.user_offsets, w.cand_to_user[sl], w.scale)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    f_sample = 4.0 * w.n_q * w.d * w.H * float(w.lengths[w.cand_to_user[sl]].sum())
+    return {"value": f_sample / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n_sample} of {w.n_cand} candidates of {w.name}, fp64 numpy with an explicit K/V copy "
+                      f"per candidate and P quantized per 32-key block, median of {reps} runs of {t:.2f} s",
+            "seconds_whole_batch": t * w.n_cand / n_sample}
+
+
+def main_mx(args):
+    """One step = one ikbo_attn_fwd_mxfp8 call: host grouping and work lists from
+    the host mapping, the MXFP8 kernel and (for split key ranges) the merge."""
+    import torch
+    import broadcast_free_target_amd as ikbo
+    from workloads import make_mxfp8
+
+    w = make_mxfp8(args.config)
+    dev = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in w.arrays()]
+    out = torch.empty((w.n_cand, w.n_q, w.H, w.d), dtype=torch.bfloat16, device="cuda")
+    offs_h = np.ascontiguousarray(w.user_offsets, dtype=np.int32)
+    c2u_h = np.ascontiguousarray(w.cand_to_user, dtype=np.int32)
+    stream = torch.cuda.current_stream()
+    h = ikbo.ikbo_mx_create()
+
+    def step():
+        ikbo.ikbo_attn_fwd_mxfp8(h, offs_h, c2u_h, w.n_users, w.n_cand, w.n_q, w.H, w.d, w.scale, *dev, out, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ikbo.ikbo_mx_timing(h, True)
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    attn_ms, merge_ms = ikbo.ikbo_mx_timing_read(h, K)
+    ikbo.ikbo_mx_timing(h, False)
+    info = ikbo.ikbo_mx_info(h)
+    ikbo.ikbo_mx_destroy(h)
+    a_ms, m_ms = float(np.mean(attn_ms)), float(np.mean(merge_ms))
+    f, b = mx_counts(w)
+    ms_per_step = wall * 1e3 / K
+    if f / b < PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        achieved = b / (a_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS}
+    else:
+        achieved = f / (a_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_FP8_TFLOPS}
+    roof["traffic"] = traffic_from_profiles(args.config)
+    roof["kernel"] = MX_KERNEL
+    roof["kernel_avg_us"] = a_ms * 1e3
+    roof["merge_kernel_avg_us"] = m_ms * 1e3
+    roof["algorithmic_bytes_per_launch"] = b
+    roof["algorithmic_flops_per_launch"] = f
+    extra = {"kernel_tflops": f / (a_ms * 1e-3) / 1e12, "kernel_frac_fp8_mfma_peak": f / (a_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+             "kernel_hbm_gbs": b / (a_ms * 1e-3) / 1e9, "candidates_per_s": w.n_cand / (ms_per_step * 1e-3),
+             "work_items": info}
+    result = {
+        "metric": MX_METRIC, "value": f / (ms_per_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8 (E4M3 data, E8M0 block scales, fp32 accumulation)",
+        "data": "synthetic (seeded MX codes with per-block scales, dequantized values ~N(0,1); jagged lengths and "
+                "mappings of the bf16 configuration of the same name)",
+        "config": {"workload": f"{args.config}: {WORKLOAD_TEXT[args.config]}", "n_cand": w.n_cand,
+                   "n_users": w.n_users, "n_q": w.n_q, "H": w.H, "d": w.d, "total_len": w.total_len, "seed": w.seed},
+        "roofline": roof, "cpu_baseline": None, "extra": extra,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_mx(w, 8 if w.n_cand > 2000 else 256, 3)
     print(json.dumps(result), flush=True)
 
 
@@ -647,6 +757,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
                           "launches": args.steps}), flush=True)
+        return
+    if args.config.startswith("mx_"):
+        main_mx(args)
         return
     if args.config.startswith("lce3_"):
         main_lce3(args)
