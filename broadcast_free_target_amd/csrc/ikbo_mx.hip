@@ -25,6 +25,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "ikbo_device.h"
 #include "ikbo_mx.h"
@@ -82,23 +83,72 @@ __device__ __forceinline__ int p_block_exp(float amax) {
   return top - 8 + ((b & 0x7FFFFF) > 0x600000 ? 1 : 0);
 }
 
-// 16 weights of one key block, scaled by 2^-e and rounded to E4M3, packed
-// four per dword in value order (hardware conversion: nearest, ties to even).
-__device__ __forceinline__ void quantize16(const float (&p)[16], int e, int& w0, int& w1, int& w2, int& w3) {
-  int w[4];
+// One tile's online softmax (base 2, integer reference m) and P quantization,
+// for lane (row n, half g) holding scores s[b][v] of keys kk(b, v).
+//  * Block maxima are taken on the scores oriented by the scale's sign
+//    (NEG: the scale is negative), since fl(c * s) is monotone in s; the tile
+//    maximum of x = c * s raises m to the next integer at or above it, and O
+//    and l are rescaled by an exact power of two.
+//  * A block's largest weight is exp2(fma(s*, c, -m)) for its largest score s*,
+//    bit for bit the weight of that key, and gives the block's scale 2^e.
+//  * The scaled weights y = exp2(fma(s, c, -(m + e))) are rounded to E4M3 by
+//    the hardware conversion (nearest, ties to even; y <= 448 up to one
+//    rounding) and packed in value order; l gains 2^e * sum(y).
+//  * MASK: keys at or past kv_left (the item's last tile) get weight 0.
+// The block's 32 keys live in lanes n and n + 32 (half_max pairs them).
+template <bool NEG, bool MASK>
+__device__ __forceinline__ void softmax_quant(const f32x16_t (&s)[2], float c, int kv_left, int g, float& m_run,
+                                              float& l_run, f32x16_t (&oacc)[4], v8i& pf, int& psc) {
+  auto live = [&](int b, int v) { return !MASK || 32 * b + 8 * (v >> 2) + 4 * g + (v & 3) < kv_left; };
+  float smax[2], xb[2];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float y0 = __builtin_ldexpf(p[4 * k + 0], -e), y1 = __builtin_ldexpf(p[4 * k + 1], -e);
-    const float y2 = __builtin_ldexpf(p[4 * k + 2], -e), y3 = __builtin_ldexpf(p[4 * k + 3], -e);
-    int x = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-    w[k] = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, x, true);
+  for (int b = 0; b < 2; ++b) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, live(b, v) ? (NEG ? -s[b][v] : s[b][v]) : kNegInf);
+    smax[b] = half_max(mx);
+    smax[b] = NEG ? -smax[b] : smax[b];  // the block's largest-weight score (+-inf if the block is empty)
+    xb[b] = (smax[b] == kNegInf || smax[b] == -kNegInf) ? kNegInf : smax[b] * c;
   }
-  w0 = w[0];
-  w1 = w[1];
-  w2 = w[2];
-  w3 = w[3];
+  const float m_new = fmaxf(m_run, __builtin_ceilf(fmaxf(xb[0], xb[1])));
+  if (m_new > m_run) {
+    const float alpha = m_run == kNegInf ? 0.0f : __builtin_ldexpf(1.0f, static_cast<int>(m_run - m_new));
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) oacc[mb] *= alpha;
+    l_run *= alpha;
+    m_run = m_new;
+  }
+  int pw[8], e[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const float amax = xb[b] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(smax[b], c, -m_run));
+    if (amax >= 0x1p-100f) {
+      e[b] = p_block_exp(amax);
+      const float bias = -(m_run + static_cast<float>(e[b]));
+      float sum = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {  // four weights at a time: computed, summed, converted
+        float y[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int v = 4 * k + i;
+          y[i] = live(b, v) ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][v], c, bias)) : 0.0f;
+          sum += y[i];
+        }
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        pw[4 * b + k] = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+      }
+      l_run += __builtin_ldexpf(sum, e[b]);
+    } else {  // dropped block: no weight (the largest is below 2^-100)
+      e[b] = 0;
+      pw[4 * b] = pw[4 * b + 1] = pw[4 * b + 2] = pw[4 * b + 3] = 0;
+    }
+  }
+  psc = (g == 0 ? e[0] : e[1]) + 127;
+  pf = v8i{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
 }
 
+template <bool NEG>
 __global__ __launch_bounds__(kT, 2) void ikbo_attn_mx_kernel(MxParams P) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kNst * kStBytes];
 
@@ -200,7 +250,9 @@ __global__ __launch_bounds__(kT, 2) void ikbo_attn_mx_kernel(MxParams P) {
     const bool wave_has_rows = wave * 32 < it.nrows;
     const float c = P.scale_log2;
 
-    for (int t = 0; t < ntiles; ++t) {
+    // Tile t: wait for its copies, then the barrier that also frees stage
+    // (t - 1) % kNst for the copies of tile t + kNst - 1.
+    auto advance = [&](int t) {
       const int after = min(kNst - 2, ntiles - 1 - t);
       if (after <= 0)
         wait_vmcnt<0>();
@@ -210,10 +262,11 @@ __global__ __launch_bounds__(kT, 2) void ikbo_attn_mx_kernel(MxParams P) {
         wait_vmcnt<2 * kCopies>();
       __syncthreads();  // tile t is in LDS for every thread; stage (t-1) % kNst is free
       if (t + kNst - 1 < ntiles) issue(t + kNst - 1);
-      if (!wave_has_rows) continue;
+    };
+    auto compute = [&](int t, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
       const uint8_t* st = smem + (t % kNst) * kStBytes;
       const int kv_left = nkv - t * kMxKeys;  // keys of this tile inside the range (may exceed 64)
-
       // ---- S^T = K . Q^T, two 32-key blocks
       f32x16_t s[2];
 #pragma unroll
@@ -238,52 +291,10 @@ __global__ __launch_bounds__(kT, 2) void ikbo_attn_mx_kernel(MxParams P) {
         s[b] = acc;
       }
 
-      // ---- online softmax in base 2 with an integer reference
-      float x[2][16];
-      float mx = kNegInf;
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int kk = 32 * b + 8 * (v >> 2) + 4 * g + (v & 3);
-          x[b][v] = kk < kv_left ? s[b][v] * c : kNegInf;
-          mx = fmaxf(mx, x[b][v]);
-        }
-      mx = half_max(mx);  // the row's 64 keys live in lanes n and n + 32
-      const float m_new = fmaxf(m_run, __builtin_ceilf(mx));
-      if (m_new > m_run) {
-        const float alpha = m_run == kNegInf ? 0.0f : __builtin_ldexpf(1.0f, static_cast<int>(m_run - m_new));
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) oacc[mb] *= alpha;
-        l_run *= alpha;
-        m_run = m_new;
-      }
-      float p[2][16];
-      float amax[2] = {0.0f, 0.0f};
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          p[b][v] = __builtin_amdgcn_exp2f(x[b][v] - m_run);
-          l_run += p[b][v];
-          amax[b] = fmaxf(amax[b], p[b][v]);
-        }
-
-      // ---- P quantized per 32-key block (the block spans lanes n and n + 32)
-      int pw[8];
-      int e[2];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const float am = half_max(amax[b]);
-        e[b] = am >= 0x1p-100f ? p_block_exp(am) : 0;
-        if (am >= 0x1p-100f) {
-          quantize16(p[b], e[b], pw[4 * b + 0], pw[4 * b + 1], pw[4 * b + 2], pw[4 * b + 3]);
-        } else {
-          pw[4 * b + 0] = pw[4 * b + 1] = pw[4 * b + 2] = pw[4 * b + 3] = 0;
-        }
-      }
-      const int psc = (g == 0 ? e[0] : e[1]) + 127;
-      const v8i pf = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+      // ---- online softmax and P quantization
+      v8i pf;
+      int psc;
+      softmax_quant<NEG, MASK>(s, c, kv_left, g, m_run, l_run, oacc, pf, psc);
 
       // ---- O^T += V^T . P^T, four 32-column blocks
 #pragma unroll
@@ -305,6 +316,16 @@ __global__ __launch_bounds__(kT, 2) void ikbo_attn_mx_kernel(MxParams P) {
         const v8i vf = {va[0], va[1], va[2], va[3], va[4], va[5], va[6], va[7]};
         oacc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf, oacc[mb], 0, 0, 0, vsc, 0, psc);
       }
+    };
+    // Only the last tile can hold keys past the range: the loop runs unmasked
+    // and the last tile separately.
+    for (int t = 0; t + 1 < ntiles; ++t) {
+      advance(t);
+      if (wave_has_rows) compute(t, std::false_type{});
+    }
+    if (ntiles > 0) {
+      advance(ntiles - 1);
+      if (wave_has_rows) compute(ntiles - 1, std::true_type{});
     }
     __syncthreads();  // every stage read before the next item's copies
 
@@ -347,10 +368,11 @@ __global__ __launch_bounds__(kT, 2) void ikbo_attn_mx_kernel(MxParams P) {
 
 hipError_t launch_mx(const MxParams& p, int grid, hipStream_t stream, hipEvent_t* ev) {
   if (grid <= 0 || p.n_items <= 0) return hipSuccess;
+  auto kernel = p.scale_log2 < 0.0f ? ikbo_attn_mx_kernel<true> : ikbo_attn_mx_kernel<false>;
   if (ev)
-    hipExtLaunchKernelGGL(ikbo_attn_mx_kernel, dim3(grid), dim3(kT), 0, stream, ev[0], ev[1], 0, p);
+    hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(kT), 0, stream, ev[0], ev[1], 0, p);
   else
-    hipLaunchKernelGGL(ikbo_attn_mx_kernel, dim3(grid), dim3(kT), 0, stream, p);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kT), 0, stream, p);
   return hipGetLastError();
 }
 
