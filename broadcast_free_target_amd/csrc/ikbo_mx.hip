@@ -40,7 +40,7 @@ constexpr int kNst = 4;  // HBM -> LDS ring depth
 constexpr float kNegInf = -__builtin_inff();
 
 // One ring stage: K tile [64 keys][128 B], V tile [64][128 B] (16-byte
-// chunks swizzled per key), K scales [64 keys][4 B], V scales [2 blocks][128 B],
+// chunks swizzled per key, mx_swz), K scales [64 keys][4 B], V scales [2 blocks][128 B],
 // and a spare area the scale copies of waves 2-3 land in (every wave issues the
 // same number of copies, so one vmcnt wait fits all).
 constexpr int kStK = 0, kStV = 8192, kStKS = 16384, kStVS = 16640, kStSpare = 16896, kStBytes = 17408;
@@ -50,10 +50,14 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 
-// 16-byte chunk position of (key, chunk): the XOR of key bits 1-3 keeps the
-// K fragment reads (8 consecutive keys, one chunk) and the transposed V reads
-// (keys 8(r/4) + 4g + r%4, one chunk) on distinct banks.
-__device__ __forceinline__ int mx_off(int key, int chunk) { return key * 128 + ((chunk ^ ((key >> 1) & 7)) << 4); }
+// 16-byte chunk swizzle of a key row: bits 1, 3 and 2 of the key become bits
+// 1, 2 and 0 of the XOR.  Over 16 consecutive keys (a K fragment read) the
+// even keys, and the odd ones, get 8 distinct values; over the 8 keys of one
+// transposed V read (8(r/4) + 4g + r%4, read as column chunks 2mb and 2mb + 1
+// by the two 16-lane groups of a half) the even keys, and the odd ones, get
+// values that differ in bits 1-2, so the chunk pair stays on distinct banks.
+__device__ __forceinline__ int mx_swz(int key) { return (((key >> 1) & 1) << 1) | (((key >> 3) & 1) << 2) | ((key >> 2) & 1); }
+__device__ __forceinline__ int mx_off(int key, int chunk) { return key * 128 + ((chunk ^ mx_swz(key)) << 4); }
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -167,7 +171,7 @@ __global__ __launch_bounds__(kT, 2) void ikbo_attn_mx_kernel(MxParams P) {
   for (int r = 0; r < 2; ++r) {
     const int u = tid + kT * r;
     ld_key[r] = u >> 3;
-    ld_chunk[r] = (u & 7) ^ ((ld_key[r] >> 1) & 7);
+    ld_chunk[r] = (u & 7) ^ mx_swz(ld_key[r]);
   }
   // Transposed V reads: lane (2r + h) of each 16-lane group points at key row r
   // of the read, byte half h of the group's 16-column chunk.
