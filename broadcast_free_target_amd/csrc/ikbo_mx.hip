@@ -38,6 +38,7 @@ using namespace dev;
 constexpr int kT = 256;  // 4 wave64
 constexpr int kNst = 4;  // HBM -> LDS ring depth
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kLazyRef = 8.0f;  // headroom of the softmax reference (log2 units)
 
 // One ring stage: K tile [64 keys][128 B], V tile [64][128 B] (16-byte
 // chunks swizzled per key, mx_swz), K scales [64 keys][4 B], V scales [2 blocks][128 B],
@@ -90,9 +91,10 @@ __device__ __forceinline__ int p_block_exp(float amax) {
 // One tile's online softmax (base 2, integer reference m) and P quantization,
 // for lane (row n, half g) holding scores s[b][v] of keys kk(b, v).
 //  * Block maxima are taken on the scores oriented by the scale's sign
-//    (NEG: the scale is negative), since fl(c * s) is monotone in s; the tile
-//    maximum of x = c * s raises m to the next integer at or above it, and O
-//    and l are rescaled by an exact power of two.
+//    (NEG: the scale is negative), since fl(c * s) is monotone in s; when the
+//    tile maximum of x = c * s passes m by more than kLazyRef, m rises to the
+//    next integer at or above it and O and l are rescaled by an exact power
+//    of two.
 //  * A block's largest weight is exp2(fma(s*, c, -m)) for its largest score s*,
 //    bit for bit the weight of that key, and gives the block's scale 2^e.
 //  * The scaled weights y = exp2(fma(s, c, -(m + e))) are rounded to E4M3 by
@@ -114,9 +116,19 @@ __device__ __forceinline__ void softmax_quant(const f32x16_t (&s)[2], float c, i
     smax[b] = NEG ? -smax[b] : smax[b];  // the block's largest-weight score (+-inf if the block is empty)
     xb[b] = (smax[b] == kNegInf || smax[b] == -kNegInf) ? kNegInf : smax[b] * c;
   }
-  const float m_new = fmaxf(m_run, __builtin_ceilf(fmaxf(xb[0], xb[1])));
-  if (m_new > m_run) {
-    const float alpha = m_run == kNegInf ? 0.0f : __builtin_ldexpf(1.0f, static_cast<int>(m_run - m_new));
+  // The reference stays put while the row's maximum exceeds it by at most
+  // kLazyRef (weights up to 2^kLazyRef): every block's scale follows the
+  // weights by the same power of two, so the codes and the output do not
+  // change.  When a row passes that, its reference rises to the next integer
+  // at or above its maximum; the wave skips the rescale when no row rises
+  // (rows that do not rise multiply by exactly 1).
+  const float tmax = fmaxf(xb[0], xb[1]);
+  const bool rise = m_run == kNegInf || tmax > m_run + kLazyRef;
+  if (__any(rise)) {
+    const float m_new = rise ? __builtin_ceilf(tmax) : m_run;
+    const float alpha = m_new == m_run    ? 1.0f
+                        : m_run == kNegInf ? 0.0f
+                                           : __builtin_ldexpf(1.0f, static_cast<int>(m_run - m_new));
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) oacc[mb] *= alpha;
     l_run *= alpha;

@@ -319,7 +319,8 @@ void ikbo_bwd_destroy(void* bwd);
  * (value 2^(s - 127), 255 NaN) per 32 elements along each product's
  * contraction.  For candidate c of user u, query row r and head h:
  *   x_j = scale * log2(e) * (q^ . k^_j) over the user's keys j, m = an integer
- *   >= max_j x_j (the result does not depend on which), p_j = 2^(x_j - m);
+ *   (the result does not depend on which: the kernel lets it lag the running
+ *   maximum by up to 8), p_j = 2^(x_j - m);
  *   P^ = p quantized per block of 32 keys (blocks start at the user's first
  *   key): the block's scale is the smallest 2^e with max p <= 448 * 2^e and
  *   each p_j / 2^e is rounded to E4M3 (nearest, ties to even); a block whose

@@ -29,10 +29,12 @@ Readings where the pages leave a step open (also listed in the design notes):
   column (v_scales [NVB, H, d], user u's blocks from v_block_offsets(offs)[u],
   the last one partial).
 * Softmax in base 2 with an integer reference: x = scale * log2(e) * (q . k),
-  m = ceil(max_j x_j), p_j = 2^(x_j - m).  Any integer m >= max x gives the
-  same output exactly (every quantization step below is invariant under
-  powers of two), so a kernel may keep a running integer maximum and rescale by
-  exact powers of two; pinned.
+  m = ceil(max_j x_j), p_j = 2^(x_j - m).  Any integer m gives the same output
+  (every quantization step below is invariant under powers of two; only which
+  blocks fall below the 2^-100 drop threshold, relative to the row maximum,
+  moves), so a kernel may keep a running integer reference, let it lag the
+  running maximum by a few units (weights above 1), and rescale by exact
+  powers of two; pinned for references above and below ceil(max x).
 * P's block scale: the smallest power of two 2^e with max|p| <= 448 * 2^e over
   the block's 32 keys (blocks aligned like V's); each p_j / 2^e is rounded to
   E4M3 (nearest, ties to even) and multiplied back.  A block whose maximum is

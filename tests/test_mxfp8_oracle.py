@@ -148,13 +148,14 @@ def test_brute_force_scalar_loops_on_the_tiny_config():
 
 
 def test_invariant_to_the_integer_softmax_reference():
-    """Raising the integer reference by k scales every p by 2^-k; the block
+    """Moving the integer reference by k scales every p by 2^-k; the block
     scales follow and the codes do not change, so the output is the same up to
     the fp64 rounding of x - m (a rule that did not follow powers of two would
-    move outputs by up to 2^-4 of |v|)."""
+    move outputs by up to 2^-4 of |v|).  References below the maximum (weights
+    up to 2^8) are what a kernel with a lagging reference uses."""
     w = make_mxfp8("mx_tiny")
     base = _oracle(w)
-    for k in (1, 3, 17):
+    for k in (-8, -3, 1, 3, 17):
         np.testing.assert_allclose(_oracle(w, m_shift=k), base, rtol=1e-12, atol=1e-14)
 
 
