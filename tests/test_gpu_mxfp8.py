@@ -211,6 +211,16 @@ def test_mx_zero_scale_is_the_mean_of_v():
         assert np.all(np.abs(got[c, 0] - mean) <= tol)
 
 
+@pytest.mark.parametrize("scale", [-0.0883883, -1.5])
+def test_mx_negative_scale(scale):
+    """A negative softmax scale runs the kernel's other instance (block maxima
+    on the negated scores)."""
+    w = make_mxfp8_custom(4550, (1, 33, 70, 300, 1500), [0, 1, 2, 3, 4, 4, 2, 1, 3], n_q=2, H=2)
+    w.scale = np.float32(scale)
+    say(f"case mx negative scale {scale}")
+    _close(_run(w), _oracle(w), f"scale {scale}", _slack(w))
+
+
 def test_mx_handle_reuse_alternating_requests():
     import broadcast_free_target_amd as ikbo
     w1 = make_mxfp8_custom(4600, (90, 17, 300), [0, 1, 2, 2, 0, 1, 2], n_q=1, H=2)
