@@ -32,7 +32,8 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
 # Attention kernel a plan runs (ikbo_plan_info "kernel"), by head dim.
 KERNEL_NAMES = {0: "ikbo_attn_f32_kernel<{d}>", 1: "ikbo_attn_bf16_w8_kernel<{d}, 2>",
-                2: "ikbo_attn_bf16_kernel<{d}, 2>", 3: "ikbo_attn_bf16_pipe_kernel<{d}, 4, false>"}
+                2: "ikbo_attn_bf16_kernel<{d}, 2>", 3: "ikbo_attn_bf16_pipe_kernel<{d}, 4, false>",
+                4: "ikbo_attn_bf16_kernel<{d}, 2>"}  # 4: the 4-wave kernel visiting key tiles in reverse
 
 WORKLOAD_TEXT = {
     "c1_tiny_f32": "tiny fp32: 4 users, L~U[16,64], 20 candidates, n_q=1, H=2, d=32",

@@ -43,7 +43,7 @@ struct Plan {
   bool built = false;
   int32_t n_users = 0, n_cand = 0, n_q = 1, H = 0, d = 0, dtype = IKBO_DTYPE_BF16, with_self = 0;
   int32_t stages = 2;  // bf16 kernel ring depth chosen at build time
-  int32_t variant = 0;  // bf16 kernel: kVariantPipe, kVariantW8 or kVariantW4
+  int32_t variant = 0;  // bf16 kernel: kVariantPipe, kVariantW8, kVariantW4 or kVariantW4R
   int64_t total_len = 0;
   HostPlan hp;
   // device copies of the work list
@@ -107,11 +107,14 @@ int bf16_stages() {
 // the eight-wave kernel and keeps it when every workgroup gets at most one
 // item; otherwise it plans again for the 4-wave kernel, whose two independent
 // workgroups per CU keep the SIMDs busier over many items.  IKBO_KERNEL =
-// w8 | w4 | pipe forces a variant.
-enum { kVariantPipe = 0, kVariantW8 = 1, kVariantW4 = 2, kVariantAuto = 3 };
+// w8 | w4 | pipe forces a variant; w4r is the 4-wave kernel visiting each
+// item's key tiles last to first (the reverse-order variant of the TLX
+// attention post's persistent kernel).
+enum { kVariantPipe = 0, kVariantW8 = 1, kVariantW4 = 2, kVariantAuto = 3, kVariantW4R = 4 };
 int bf16_variant() {
   const char* s = std::getenv("IKBO_KERNEL");
   if (s && std::strcmp(s, "pipe") == 0) return kVariantPipe;
+  if (s && std::strcmp(s, "w4r") == 0) return kVariantW4R;
   if (s && std::strcmp(s, "w4") == 0) return kVariantW4;
   if (s && std::strcmp(s, "w8") == 0) return kVariantW8;
   return kVariantAuto;
@@ -119,7 +122,7 @@ int bf16_variant() {
 
 PlanParams params_for(const Plan& p, int32_t dtype, int variant) {
   PlanParams pp;
-  if (dtype == IKBO_DTYPE_BF16 && variant != kVariantW4) {
+  if (dtype == IKBO_DTYPE_BF16 && variant != kVariantW4 && variant != kVariantW4R) {
     // one resident workgroup per CU; the 8-wave kernel's chunks are whole ring stages
     pp.bm = ikbo::kBf16TileRows;
     pp.bn = (variant == kVariantW8 ? 2 : 1) * ikbo::kBf16TileKeys;
@@ -309,8 +312,10 @@ int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* 
     e = ikbo::launch_attn_bf16_pipe(ap, p->d, p->hp.grid, scale < 0.0f, stream, te);
   else if (p->variant == kVariantW8)
     e = ikbo::launch_attn_bf16_w8(ap, p->d, p->hp.grid, stream, te);
-  else
+  else {
+    ap.kv_reverse = p->variant == kVariantW4R ? 1 : 0;
     e = ikbo::launch_attn_bf16(ap, p->d, p->stages, p->hp.grid, stream, te);
+  }
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
   if (p->hp.n_groups > 0) {
     e = ikbo::launch_merge(ap, p->hp.n_groups, p->d, stream, te ? te + 2 : nullptr);
@@ -475,10 +480,12 @@ void ikbo_plan_destroy(void* plan) {
 int ikbo_plan_info(void* plan, int64_t* info, int32_t n_info) {
   if (!plan || !info || n_info < 1) return fail(IKBO_ERR_INVALID_ARG, "null plan or info");
   const Plan* p = static_cast<const Plan*>(plan);
-  // kernel: 0 fp32, 1 bf16 eight-wave, 2 bf16 4-wave, 3 bf16 software-pipelined
+  // kernel: 0 fp32, 1 bf16 eight-wave, 2 bf16 4-wave, 3 bf16 software-pipelined,
+  // 4 bf16 4-wave with key tiles in reverse order
   const int64_t kernel = p->dtype != IKBO_DTYPE_BF16 ? 0
                          : p->variant == kVariantW8  ? 1
                          : p->variant == kVariantW4  ? 2
+                         : p->variant == kVariantW4R ? 4
                                                      : 3;
   const int64_t v[9] = {static_cast<int64_t>(p->hp.items.size()),
                         p->hp.grid,

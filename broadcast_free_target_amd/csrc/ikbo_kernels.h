@@ -35,6 +35,7 @@ struct AttnParams {
                           // running sum l, output unit (row * H + h, -1: no row) and
                           // nchunk | kind << 16, the last two as int32 bits
   uint64_t* trace;        // optional: [n_items, 6] per-item records (bf16 kernel), or null
+  int32_t kv_reverse;     // 4-wave bf16 kernel: 1 = visit each item's key tiles last to first
 };
 
 // stages: depth of the HBM -> LDS ring (2, 3 or 4); 2 stages allow two

@@ -298,12 +298,16 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
     const uint16_t* kbase = Kg + (static_cast<int64_t>(it.kv_base) + it.k0) * row_stride + it.h * D;
     const uint16_t* vbase = Vg + (static_cast<int64_t>(it.kv_base) + it.k0) * row_stride + it.h * D;
 
-    // Issue the HBM -> LDS copies of tile t into stage t % NST.
+    // Issue the HBM -> LDS copies of the t-th tile visited into stage t % NST.
+    // Tiles are visited first to last, or last to first with kv_reverse (the
+    // masked partial tile then comes first; the result differs only in the
+    // order of the fp32 sums).
+    auto tile_of = [&](int t) { return P.kv_reverse ? ntiles - 1 - t : t; };
     auto issue = [&](int t) {
       const uint32_t st = lds_base + static_cast<uint32_t>((t % NST) * T::stage * 2);
 #pragma unroll
       for (int r = 0; r < T::loads; ++r) {
-        const int key = min(t * kBN + ld_row[r], nkv - 1);
+        const int key = min(tile_of(t) * kBN + ld_row[r], nkv - 1);
         const int64_t off = key * row_stride + ld_chunk[r] * 8;
         const uint32_t dk = st + static_cast<uint32_t>((kThreads * r + 64 * wave_u) * 16);
         copy16_to_lds(kbase + off, dk);
@@ -360,7 +364,7 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
       }
       __syncthreads();  // every thread's copies of tile t are in LDS; stage (t-1) % NST is free
       if (t + NST - 1 < ntiles) issue(t + NST - 1);
-      const int key_base = it.k0 + t * kBN;  // first key of this tile, user-relative
+      const int key_base = it.k0 + tile_of(t) * kBN;  // first key of this tile, user-relative
       const bool skip = !wave_has_rows || (causal && key_base > wave_last_tok);
       if (!skip) {
         const uint16_t* Ks = smem + (t % NST) * T::stage;

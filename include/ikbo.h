@@ -369,8 +369,8 @@ void ikbo_mx_destroy(void* mx);
  * info[0] work items, [1] grid of the persistent launch, [2] split groups,
  * [3] partial-result slots, [4] bytes of the split-KV workspace, [5] target
  * row tiles, [6] self row tiles, [7] compute units, [8] kernel (0 fp32, 1 bf16
- * eight-wave, 2 bf16 4-wave, 3 bf16 software-pipelined).  Writes the first
- * min(n_info, 9) values.
+ * eight-wave, 2 bf16 4-wave, 3 bf16 software-pipelined, 4 bf16 4-wave visiting
+ * each item's key tiles last to first).  Writes the first min(n_info, 9) values.
  */
 int ikbo_plan_info(void* plan, int64_t* info, int32_t n_info);
 

@@ -67,7 +67,7 @@ def test_c1_tiny_f32():
     assert_close(to_f64(out2), ref, "f32", "c1 ex")
 
 
-@pytest.mark.parametrize("waves", ["pipe", "w8", "w4"])
+@pytest.mark.parametrize("waves", ["pipe", "w8", "w4", "w4r"])
 def test_c2_typical_planned_and_north_star_call(waves):
     from broadcast_free_target_amd import ikbo_attn_fwd
     import torch
@@ -89,7 +89,7 @@ def test_c2_typical_planned_and_north_star_call(waves):
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
-@pytest.mark.parametrize("waves", ["pipe", "w8", "w4"])
+@pytest.mark.parametrize("waves", ["pipe", "w8", "w4", "w4r"])
 def test_c3_skewed_with_single_key_users(waves):
     os.environ["IKBO_KERNEL"] = waves
     w = _wl("c3_skewed")
@@ -199,7 +199,7 @@ def _custom(i, lengths, counts, n_q, H, d, dtype, with_self=False):
 
 @pytest.mark.parametrize("i", range(len(EDGE)))
 @pytest.mark.parametrize("split", ["default", "forced", "off"])
-@pytest.mark.parametrize("waves", ["pipe", "w8", "w4"])
+@pytest.mark.parametrize("waves", ["pipe", "w8", "w4", "w4r"])
 def test_edge_matrix(i, split, waves):
     lengths, counts, n_q, H, d, dtype = EDGE[i]
     if dtype != "bf16" and waves != "pipe":
@@ -225,7 +225,7 @@ def test_edge_matrix(i, split, waves):
 
 
 @pytest.mark.parametrize("scale", [-0.2, 0.0, 0.45])
-@pytest.mark.parametrize("kernel", ["pipe", "w8", "w4"])
+@pytest.mark.parametrize("kernel", ["pipe", "w8", "w4", "w4r"])
 def test_scale_sign_and_zero(scale, kernel):
     """Negative, zero and large scales: the softmax takes c*min(s) as the row
     maximum for c < 0, and c = 0 gives the plain mean of V."""
@@ -251,7 +251,8 @@ def test_scale_sign_and_zero(scale, kernel):
 
 @pytest.mark.parametrize("dtype,d,waves", [("bf16", 128, "pipe"), ("bf16", 64, "pipe"), ("bf16", 32, "pipe"),
                                           ("bf16", 128, "w8"), ("bf16", 64, "w8"), ("bf16", 128, "w4"),
-                                          ("bf16", 32, "w4"), ("f32", 32, "pipe")])
+                                          ("bf16", 32, "w4"), ("bf16", 128, "w4r"), ("bf16", 64, "w4r"),
+                                          ("f32", 32, "pipe")])
 @pytest.mark.parametrize("split", ["default", "forced"])
 def test_edge_fused(dtype, d, waves, split):
     from broadcast_free_target_amd import ikbo_self_target_fwd
@@ -296,8 +297,29 @@ def test_p6_permutation_bitwise():
     assert np.array_equal(a[perm], b)
 
 
+def test_reverse_key_order_matches_forward_order():
+    """The 4-wave kernel visiting key tiles last to first (causal self rows and
+    split chunks included) gives the forward order's result up to the order of
+    the fp32 sums."""
+    w = _wl("c5_fused")
+    dev = upload(w)
+    say("case reverse key order (c5_fused)")
+    outs = {}
+    for kern in ("w4", "w4r"):
+        os.environ["IKBO_KERNEL"] = kern
+        oc = empty_out(w.raw("q_cand").shape, "bf16")
+        ou = empty_out(w.raw("q_user").shape, "bf16")
+        run_planned(w, dev, oc, ou)
+        outs[kern] = (to_f64(oc), to_f64(ou))
+    for i in range(2):
+        a, b = outs["w4"][i], outs["w4r"][i]
+        diff = np.abs(a - b)
+        assert diff.max() <= 2.0 ** -6 * np.abs(a).max(), diff.max()
+        assert diff.mean() <= 2.0 ** -7 * np.abs(a).mean(), diff.mean()  # about one bf16 ulp on average
+
+
 @pytest.mark.parametrize("name", ["c2_typical", "c3_skewed"])
-@pytest.mark.parametrize("waves", ["pipe", "w8", "w4"])
+@pytest.mark.parametrize("waves", ["pipe", "w8", "w4", "w4r"])
 def test_p13_determinism_across_runs_and_grids(name, waves):
     import torch
     os.environ["IKBO_KERNEL"] = waves
@@ -317,7 +339,7 @@ def test_p13_determinism_across_runs_and_grids(name, waves):
 
 
 @pytest.mark.parametrize("case", ["c2_typical", "c3_skewed", "many_chunks"])
-@pytest.mark.parametrize("waves", ["pipe", "w8", "w4"])
+@pytest.mark.parametrize("waves", ["pipe", "w8", "w4", "w4r"])
 def test_split_groups_merge_each_launchs_partials(case, waves):
     """Launches of one plan alternate V and -V.  The softmax weights do not
     depend on V, so the -V outputs are the negated V outputs up to the
