@@ -110,9 +110,42 @@ def _check(status: int) -> int:
 
 
 def _ptr(t) -> Optional[int]:
-    if t is None:
-        return None
+    if t is None or isinstance(t, int):
+        return t
     return t.data_ptr()
+
+
+def _bad(msg: str):
+    return IkboError(IKBO_ERR_INVALID_ARG, msg)
+
+
+def _need(t, nbytes: int, name: str, elem: Optional[int] = None) -> None:
+    """Checks a device tensor argument against the extent the call will touch.
+
+    The C ABI receives bare pointers and cannot see a buffer's size, so a
+    mismatched dtype or shape would let the kernels read or write past the
+    allocation.  Tensors are checked here (device-resident, contiguous, element
+    size, at least nbytes); a raw integer pointer is the caller's to size."""
+    if t is None or isinstance(t, int):
+        return
+    if not getattr(t, "is_cuda", False):
+        raise _bad(f"{name}: expected a device tensor")
+    if elem is not None and t.element_size() != elem:
+        raise _bad(f"{name}: element size {t.element_size()}, expected {elem} (dtype {t.dtype})")
+    if not t.is_contiguous():
+        raise _bad(f"{name}: tensor must be contiguous")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise _bad(f"{name}: {have} bytes, the call needs {nbytes}")
+
+
+def _es(dtype: int) -> int:
+    return 2 if dtype == IKBO_DTYPE_BF16 else 4
+
+
+# dimensions each built plan / created handle was given, for _need
+_PLAN_DIMS: dict = {}
+_LCE_DIMS: dict = {}
 
 
 def _stream(stream) -> Optional[int]:
@@ -158,8 +191,22 @@ def ikbo_group_csr(cand_to_user_host: np.ndarray, n_users: int, n_q: int, bm: in
     return counts[:n_users], offs, perm[:n_cand], tiles[:nt.value]
 
 
+def _check_common(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, n_q, H, d, es, out):
+    rows = n_cand * n_q * H * d * es
+    _need(q_cand, rows, "q_cand", es)
+    _need(out, rows, "out", es)
+    _need(k_user, 0, "k_user", es)
+    _need(v_user, 0, "v_user", es)
+    if k_user is not None and v_user is not None and not isinstance(k_user, int) and not isinstance(v_user, int):
+        if k_user.numel() != v_user.numel():
+            raise _bad("k_user and v_user differ in size")
+    _need(user_offsets, (n_users + 1) * 4, "user_offsets", 4)
+    _need(cand_to_user, n_cand * 4, "cand_to_user", 4)
+
+
 def ikbo_attn_fwd(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, H, d, scale, out,
                   stream=None) -> int:
+    _check_common(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, 1, H, d, 2, out)
     return _check(load_library().ikbo_attn_fwd(
         _ptr(q_cand), _ptr(k_user), _ptr(v_user), _ptr(user_offsets), _ptr(cand_to_user),
         n_users, n_cand, H, d, float(scale), _ptr(out), _stream(stream)))
@@ -167,6 +214,7 @@ def ikbo_attn_fwd(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n
 
 def ikbo_attn_fwd_ex(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, n_q, H, d, scale,
                      dtype, out, stream=None) -> int:
+    _check_common(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, n_q, H, d, _es(dtype), out)
     return _check(load_library().ikbo_attn_fwd_ex(
         _ptr(q_cand), _ptr(k_user), _ptr(v_user), _ptr(user_offsets), _ptr(cand_to_user),
         n_users, n_cand, n_q, H, d, float(scale), dtype, _ptr(out), _stream(stream)))
@@ -174,6 +222,12 @@ def ikbo_attn_fwd_ex(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users
 
 def ikbo_self_target_fwd(q_user, q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, H, d,
                          scale, dtype, out_user, out_cand, stream=None) -> int:
+    es = _es(dtype)
+    _check_common(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, 1, H, d, es, out_cand)
+    if k_user is not None and not isinstance(k_user, int):
+        kv = k_user.numel() * es
+        _need(q_user, kv, "q_user", es)
+        _need(out_user, kv, "out_user", es)
     return _check(load_library().ikbo_self_target_fwd(
         _ptr(q_user), _ptr(q_cand), _ptr(k_user), _ptr(v_user), _ptr(user_offsets), _ptr(cand_to_user),
         n_users, n_cand, H, d, float(scale), dtype, _ptr(out_user), _ptr(out_cand), _stream(stream)))
@@ -181,6 +235,7 @@ def ikbo_self_target_fwd(q_user, q_cand, k_user, v_user, user_offsets, cand_to_u
 
 def ikbo_attn_fwd_materialized(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, n_q, H, d,
                                scale, dtype, out, stream=None) -> int:
+    _check_common(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, n_q, H, d, _es(dtype), out)
     return _check(load_library().ikbo_attn_fwd_materialized(
         _ptr(q_cand), _ptr(k_user), _ptr(v_user), _ptr(user_offsets), _ptr(cand_to_user),
         n_users, n_cand, n_q, H, d, float(scale), dtype, _ptr(out), _stream(stream)))
@@ -196,19 +251,34 @@ def ikbo_plan_build(plan, user_offsets_host, cand_to_user_host, n_users, n_cand,
                     with_self=0, stream=None) -> int:
     offs = np.ascontiguousarray(user_offsets_host, dtype=np.int32)
     c2u = np.ascontiguousarray(cand_to_user_host, dtype=np.int32)
-    return _check(load_library().ikbo_plan_build(
+    _PLAN_DIMS.pop(plan, None)
+    rc = _check(load_library().ikbo_plan_build(
         plan, _i32(offs), _i32(c2u) if c2u.size else None, n_users, n_cand, n_q, H, d, dtype,
         int(with_self), _stream(stream)))
+    es = _es(dtype)
+    _PLAN_DIMS[plan] = (es, n_cand * n_q * H * d * es, int(offs[n_users]) * H * d * es, bool(with_self))
+    return rc
 
 
 def ikbo_attn_fwd_planned(plan, q_cand, q_user, k_user, v_user, scale, out_cand, out_user=None,
                           stream=None) -> int:
+    dims = _PLAN_DIMS.get(plan)
+    if dims is not None:
+        es, cand_bytes, kv_bytes, with_self = dims
+        _need(q_cand, cand_bytes, "q_cand", es)
+        _need(out_cand, cand_bytes, "out_cand", es)
+        _need(k_user, kv_bytes, "k_user", es)
+        _need(v_user, kv_bytes, "v_user", es)
+        if with_self:
+            _need(q_user, kv_bytes, "q_user", es)
+            _need(out_user, kv_bytes, "out_user", es)
     return _check(load_library().ikbo_attn_fwd_planned(
         plan, _ptr(q_cand), _ptr(q_user), _ptr(k_user), _ptr(v_user), float(scale), _ptr(out_cand),
         _ptr(out_user), _stream(stream)))
 
 
 def ikbo_plan_destroy(plan) -> None:
+    _PLAN_DIMS.pop(plan, None)
     load_library().ikbo_plan_destroy(plan)
 
 
@@ -248,12 +318,21 @@ def ikbo_plan_trace_read(plan, max_items: int = 1 << 20) -> np.ndarray:
 def ikbo_lce_create(w, M, K_u, K_c, ldw=None, stream=None) -> int:
     """Packs W [M, ldw] (device bf16, user columns first) into a library handle."""
     h = _P()
-    _check(load_library().ikbo_lce_create(ctypes.byref(h), _ptr(w), M, K_u, K_c, K_u + K_c if ldw is None else ldw,
-                                          _stream(stream)))
+    ld = K_u + K_c if ldw is None else ldw
+    _need(w, M * ld * 2, "w", 2)
+    _check(load_library().ikbo_lce_create(ctypes.byref(h), _ptr(w), M, K_u, K_c, ld, _stream(stream)))
+    _LCE_DIMS[h.value] = (M, K_u, K_c)
     return h.value
 
 
 def ikbo_lce_fwd(lce, x_user, x_cand, cand_to_user, n_users, n_cand, N, out, stream=None) -> int:
+    dims = _LCE_DIMS.get(lce)
+    if dims is not None and len(dims) == 3:
+        M, K_u, K_c = dims
+        _need(x_user, n_users * K_u * N * 2, "x_user", 2)
+        _need(x_cand, n_cand * K_c * N * 2, "x_cand", 2)
+        _need(out, n_cand * M * N * 2, "out", 2)
+        _need(cand_to_user, n_cand * 4, "cand_to_user", 4)
     return _check(load_library().ikbo_lce_fwd(lce, _ptr(x_user), _ptr(x_cand), _ptr(cand_to_user), n_users, n_cand,
                                               N, _ptr(out), _stream(stream)))
 
@@ -278,6 +357,7 @@ def ikbo_lce_timing_read(lce, max_n: int = 4096):
 
 
 def ikbo_lce_destroy(lce) -> None:
+    _LCE_DIMS.pop(lce, None)
     load_library().ikbo_lce_destroy(lce)
 
 
@@ -292,6 +372,13 @@ def ikbo_attn_bwd(bwd, user_offsets_host, cand_to_user_host, n_users, n_cand, n_
     """Gradients of target attention; the mapping arrays are host int32 arrays."""
     offs = np.ascontiguousarray(user_offsets_host, dtype=np.int32)
     c2u = np.ascontiguousarray(cand_to_user_host, dtype=np.int32)
+    if offs.size >= n_users + 1:
+        rows = n_cand * n_q * H * d * 2
+        kv = int(offs[n_users]) * H * d * 2
+        for t, nm in ((q_cand, "q_cand"), (out, "out"), (dout, "dout"), (dq_cand, "dq_cand")):
+            _need(t, rows, nm, 2)
+        for t, nm in ((k_user, "k_user"), (v_user, "v_user"), (dk_user, "dk_user"), (dv_user, "dv_user")):
+            _need(t, kv, nm, 2)
     return _check(load_library().ikbo_attn_bwd(
         bwd, _i32(offs), _i32(c2u) if c2u.size else None, n_users, n_cand, n_q, H, d, float(scale), _ptr(q_cand),
         _ptr(k_user), _ptr(v_user), _ptr(out), _ptr(dout), _ptr(dq_cand), _ptr(dk_user), _ptr(dv_user),
@@ -333,6 +420,16 @@ def ikbo_attn_fwd_mxfp8(mx, user_offsets_host, cand_to_user_host, n_users, n_can
     codes and scales uint8 device tensors, out a bf16 device tensor."""
     offs = np.ascontiguousarray(user_offsets_host, dtype=np.int32)
     c2u = np.ascontiguousarray(cand_to_user_host, dtype=np.int32)
+    if offs.size >= n_users + 1 and d % 32 == 0:
+        T = int(offs[n_users])
+        nvb = int(((offs[1:n_users + 1] - offs[:n_users] + 31) // 32).sum())
+        _need(q_codes, n_cand * n_q * H * d, "q_codes", 1)
+        _need(q_scales, n_cand * n_q * H * (d // 32), "q_scales", 1)
+        _need(k_codes, T * H * d, "k_codes", 1)
+        _need(k_scales, T * H * (d // 32), "k_scales", 1)
+        _need(v_codes, T * H * d, "v_codes", 1)
+        _need(v_scales, nvb * H * d, "v_scales", 1)
+        _need(out, n_cand * n_q * H * d * 2, "out", 2)
     return _check(load_library().ikbo_attn_fwd_mxfp8(
         mx, _i32(offs), _i32(c2u) if c2u.size else None, n_users, n_cand, n_q, H, d, float(scale), _ptr(q_codes),
         _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales), _ptr(out), _stream(stream)))
@@ -364,13 +461,24 @@ def ikbo_mx_destroy(mx) -> None:
 def ikbo_lce3_create(w, M, K_u, K_v, K_c, ldw=None, stream=None) -> int:
     """Packs W [M, ldw] (device bf16; user, vendor, item columns) for three levels."""
     h = _P()
-    _check(load_library().ikbo_lce3_create(ctypes.byref(h), _ptr(w), M, K_u, K_v, K_c,
-                                           K_u + K_v + K_c if ldw is None else ldw, _stream(stream)))
+    ld = K_u + K_v + K_c if ldw is None else ldw
+    _need(w, M * ld * 2, "w", 2)
+    _check(load_library().ikbo_lce3_create(ctypes.byref(h), _ptr(w), M, K_u, K_v, K_c, ld, _stream(stream)))
+    _LCE_DIMS[h.value] = (M, K_u, K_v, K_c)
     return h.value
 
 
 def ikbo_lce3_fwd(lce, x_user, x_vendor, x_cand, vendor_to_user, cand_to_vendor, n_users, n_vendors, n_cand, N, out,
                   stream=None) -> int:
+    dims = _LCE_DIMS.get(lce)
+    if dims is not None and len(dims) == 4:
+        M, K_u, K_v, K_c = dims
+        _need(x_user, n_users * K_u * N * 2, "x_user", 2)
+        _need(x_vendor, n_vendors * K_v * N * 2, "x_vendor", 2)
+        _need(x_cand, n_cand * K_c * N * 2, "x_cand", 2)
+        _need(out, n_cand * M * N * 2, "out", 2)
+        _need(vendor_to_user, n_vendors * 4, "vendor_to_user", 4)
+        _need(cand_to_vendor, n_cand * 4, "cand_to_vendor", 4)
     return _check(load_library().ikbo_lce3_fwd(lce, _ptr(x_user), _ptr(x_vendor), _ptr(x_cand), _ptr(vendor_to_user),
                                                _ptr(cand_to_vendor), n_users, n_vendors, n_cand, N, _ptr(out),
                                                _stream(stream)))

@@ -255,8 +255,12 @@ def test_mx_errors():
         with pytest.raises(IkboError) as e:  # out aliases the key codes
             ikbo.ikbo_attn_fwd_mxfp8(h, *args, *dev, dev[2].view(torch.bfloat16).view(-1)[: out.numel()].view(out.shape))
         assert e.value.status == IKBO_ERR_INVALID_ARG
-        with pytest.raises(IkboError):  # misaligned key codes
+        with pytest.raises(IkboError) as e:  # misaligned key codes (raw pointer: the library's own check)
+            ikbo.ikbo_attn_fwd_mxfp8(h, *args, dev[0], dev[1], dev[2].data_ptr() + 1, dev[3], dev[4], dev[5], out)
+        assert e.value.status == IKBO_ERR_INVALID_ARG
+        with pytest.raises(IkboError) as e:  # key codes one byte short (the binding's size check)
             ikbo.ikbo_attn_fwd_mxfp8(h, *args, dev[0], dev[1], dev[2].view(-1)[1:], dev[3], dev[4], dev[5], out)
+        assert "bytes, the call needs" in str(e.value)
         with pytest.raises(IkboError):  # mapping out of range
             ikbo.ikbo_attn_fwd_mxfp8(h, w.user_offsets, np.array([0, 2, 1], np.int32), *args[2:], *dev, out)
         torch.cuda.synchronize()

@@ -520,6 +520,32 @@ def test_plan_timing_records_each_launch():
     assert all(a > 0 for a in attn) and all(m >= 0 for m in merge)
 
 
+def test_planned_call_rejects_tensors_that_do_not_fit_the_plan():
+    """A plan built for fp32 refuses bf16 tensors, and a bf16 plan refuses a key
+    tensor shorter than its users' rows; nothing is launched in either case."""
+    from broadcast_free_target_amd import (IKBO_ERR_INVALID_ARG, IkboError, ikbo_attn_fwd_planned, ikbo_plan_build,
+                                           ikbo_plan_create, ikbo_plan_destroy)
+    import torch
+    w = _custom(12, (10, 20), (3, 4), 1, 2, 128, "bf16")
+    dev = upload(w)
+    say("case planned call with tensors that do not fit the plan")
+    out = empty_out(w.raw("q_cand").shape, "bf16", fill=7.0)
+    plan = ikbo_plan_create()
+    try:
+        ikbo_plan_build(plan, w.user_offsets, w.cand_to_user, w.n_users, w.n_cand, 1, w.H, w.d, dtype_code("f32"), 0)
+        with pytest.raises(IkboError) as e:
+            ikbo_attn_fwd_planned(plan, dev["q_cand"], None, dev["k_user"], dev["v_user"], w.scale, out)
+        assert e.value.status == IKBO_ERR_INVALID_ARG and "element size" in str(e.value)
+        ikbo_plan_build(plan, w.user_offsets, w.cand_to_user, w.n_users, w.n_cand, 1, w.H, w.d, dtype_code("bf16"), 0)
+        with pytest.raises(IkboError) as e:
+            ikbo_attn_fwd_planned(plan, dev["q_cand"], None, dev["k_user"][:-1], dev["v_user"], w.scale, out)
+        assert e.value.status == IKBO_ERR_INVALID_ARG and "k_user" in str(e.value)
+    finally:
+        ikbo_plan_destroy(plan)
+    torch.cuda.synchronize()
+    assert torch.all(out.float() == 7.0)
+
+
 def test_plan_trace_records_every_item():
     from broadcast_free_target_amd import (ikbo_attn_fwd_planned, ikbo_plan_build, ikbo_plan_create,
                                            ikbo_plan_destroy, ikbo_plan_info, ikbo_plan_trace, ikbo_plan_trace_read)

@@ -294,3 +294,38 @@ def test_planner_edge_cases(driver):
     assert rc == -2
     rc, _ = _run_driver(driver, [0, 2], [1])
     assert rc == -3
+
+
+class _FakeDeviceTensor:
+    """Stands in for a device tensor: the binding's size check reads only these."""
+
+    def __init__(self, numel, elem, contiguous=True, cuda=True):
+        self.is_cuda, self._n, self._e, self._c = cuda, numel, elem, contiguous
+        self.dtype = f"{elem}-byte"
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return self._e
+
+    def is_contiguous(self):
+        return self._c
+
+
+def test_binding_rejects_buffers_smaller_than_the_call_touches():
+    """The C ABI gets bare pointers, so the binding compares each tensor with
+    the extent the call will read or write before anything is launched."""
+    from broadcast_free_target_amd import IKBO_ERR_INVALID_ARG, IkboError
+    from broadcast_free_target_amd.ikbo import _need
+    _need(None, 100, "x")
+    _need(12345, 100, "x")  # raw pointers are the caller's to size
+    _need(_FakeDeviceTensor(50, 2), 100, "x", 2)
+    cases = [(_FakeDeviceTensor(49, 2), 2, "bytes, the call needs"),
+             (_FakeDeviceTensor(50, 4), 2, "element size"),       # an fp32 tensor where bf16 is expected
+             (_FakeDeviceTensor(50, 2, contiguous=False), 2, "contiguous"),
+             (_FakeDeviceTensor(50, 2, cuda=False), 2, "device tensor")]
+    for t, elem, msg in cases:
+        with pytest.raises(IkboError) as e:
+            _need(t, 100, "x", elem)
+        assert e.value.status == IKBO_ERR_INVALID_ARG and msg in str(e.value)
