@@ -54,15 +54,11 @@ struct Plan {
   // one workgroup merging a whole group is slower than the merge kernel.
   bool fold = false;
   DevBuf d_grp_cnt;
-  // Two pinned plan buffers, used alternately by successive builds.  With
-  // in-place reads (the default) the kernels read the work list from them;
-  // otherwise they stage a copy to the device buffers above.  Each is guarded
-  // by an event recorded after its last reader.
+  // Pinned plan buffers, handed out in turn by the ring.  With in-place reads
+  // (the default) the kernels read the work list from them; otherwise
+  // (IKBO_PLAN_UPLOAD=copy) a copy to the device buffers above reads them.
   bool read_in_place = true;
-  PinnedBuf stage[2];
-  hipEvent_t stage_ev[2] = {nullptr, nullptr};
-  bool stage_used[2] = {false, false};
-  int next_stage = 0;
+  PinnedRing ring;
   int cur_stage = 0;
   const WorkItem* k_items = nullptr;            // what the kernels read
   const int32_t* k_perm = nullptr;
@@ -78,10 +74,7 @@ struct Plan {
 
   ~Plan() {
     for (hipEvent_t e : tev) (void)hipEventDestroy(e);
-    for (int i = 0; i < 2; ++i) {
-      if (stage_ev[i]) (void)hipEventDestroy(stage_ev[i]);
-      stage[i].release();
-    }
+    ring.release();
     d2h.release();
     d_items.release();
     d_ws_o.release();
@@ -96,7 +89,8 @@ int plan_init(Plan* p) {
   hipDeviceProp_t prop;
   IKBO_HIP(hipGetDeviceProperties(&prop, p->device));
   p->n_cu = prop.multiProcessorCount;
-  for (int i = 0; i < 2; ++i) IKBO_HIP(hipEventCreateWithFlags(&p->stage_ev[i], hipEventDisableTiming));
+  int rc = p->ring.init();
+  if (rc != IKBO_OK) return rc;
   const char* up = std::getenv("IKBO_PLAN_UPLOAD");
   p->read_in_place = !(up && std::strcmp(up, "copy") == 0);
   return IKBO_OK;
@@ -206,26 +200,21 @@ int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n
   if ((rc = p->d_ws_rec.ensure(static_cast<size_t>(hp.n_slots) * tile_rows * 4 * sizeof(float), false)) != IKBO_OK)
     return rc;
 
-  // Write the work list into the pinned buffer whose last reader has finished.
-  const int s = p->next_stage;
-  p->next_stage ^= 1;
-  if (p->stage_used[s]) IKBO_HIP(hipEventSynchronize(p->stage_ev[s]));
+  // Write the work list into the next pinned buffer whose last reader has finished.
   const size_t a0 = 0, a1 = (items_bytes + 255) & ~size_t(255), a2 = a1 + ((perm_bytes + 255) & ~size_t(255));
-  if ((rc = p->stage[s].ensure(a2 + 256)) != IKBO_OK) return rc;
-  char* hb = static_cast<char*>(p->stage[s].ptr);
+  int s = 0;
+  if ((rc = p->ring.acquire(a2 + 256, &s)) != IKBO_OK) return rc;
+  char* hb = static_cast<char*>(p->ring.buf[s].ptr);
   if (items_bytes) std::memcpy(hb + a0, hp.items.data(), items_bytes);
   if (perm_bytes) std::memcpy(hb + a1, hp.cand_perm.data(), perm_bytes);
   if (p->read_in_place) {
-    void* dev = nullptr;
-    IKBO_HIP(hipHostGetDevicePointer(&dev, hb, 0));
-    char* db = static_cast<char*>(dev);
+    char* db = static_cast<char*>(p->ring.buf[s].dev);
     p->k_items = reinterpret_cast<const WorkItem*>(db + a0);
     p->k_perm = reinterpret_cast<const int32_t*>(db + a1);
   } else {
     if ((rc = p->d_items.ensure(a2 + 256, false)) != IKBO_OK) return rc;
     IKBO_HIP(hipMemcpyAsync(p->d_items.ptr, hb, a2, hipMemcpyHostToDevice, stream));
-    IKBO_HIP(hipEventRecord(p->stage_ev[s], stream));
-    p->stage_used[s] = true;
+    if ((rc = p->ring.launched(s, stream)) != IKBO_OK) return rc;  // the copy reads the buffer
     char* db = static_cast<char*>(p->d_items.ptr);
     p->k_items = reinterpret_cast<const WorkItem*>(db + a0);
     p->k_perm = reinterpret_cast<const int32_t*>(db + a1);
@@ -336,8 +325,8 @@ int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* 
   }
   if (p->read_in_place) {
     // The pinned work list of this build stays in use until these kernels end.
-    IKBO_HIP(hipEventRecord(p->stage_ev[p->cur_stage], stream));
-    p->stage_used[p->cur_stage] = true;
+    int rc = p->ring.launched(p->cur_stage, stream);
+    if (rc != IKBO_OK) return rc;
   }
   return IKBO_OK;
 }

@@ -30,15 +30,12 @@ using ikbo::HostPlan;
 using ikbo::PlanParams;
 using ikbo::WorkItem;
 
-// Target-attention backward: the work lists of the last calls (two pinned
-// buffers used alternately, each guarded by an event after its last reader, the
-// kernels read them in place) and the sorted-row workspace.
+// Target-attention backward: the work lists of the last calls (pinned buffers
+// handed out in turn by the ring; the kernels read them in place) and the
+// sorted-row workspace.
 struct Bwd {
   int device = -1;
-  PinnedBuf stage[2];
-  hipEvent_t stage_ev[2] = {nullptr, nullptr};
-  bool stage_used[2] = {false, false};
-  int next = 0;
+  PinnedRing ring;
   int n_cu = 0;
   DevBuf ws;              // qrow [R + pad] int32, then lse and dd [H][R + pad] fp32
   DevBuf ws_dq, ws_rec;   // split dQ partials and their row records
@@ -51,10 +48,7 @@ struct Bwd {
   int n_timed = 0;
   ~Bwd() {
     for (hipEvent_t e : tev) (void)hipEventDestroy(e);
-    for (int i = 0; i < 2; ++i) {
-      if (stage_ev[i]) (void)hipEventDestroy(stage_ev[i]);
-      stage[i].release();
-    }
+    ring.release();
     ws.release();
     ws_dq.release();
     ws_rec.release();
@@ -74,10 +68,13 @@ int ikbo_bwd_create(void** bwd) {
     if (!b) return fail(IKBO_ERR_NOMEM, "bwd allocation");
     hipError_t e = hipGetDevice(&b->device);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&b->n_cu, hipDeviceAttributeMultiprocessorCount, b->device);
-    for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&b->stage_ev[i], hipEventDisableTiming);
     if (e != hipSuccess) {
       delete b;
       return fail_hip(e, "bwd create");
+    }
+    if (int rc = b->ring.init(); rc != IKBO_OK) {
+      delete b;
+      return rc;
     }
     *bwd = b;
     return IKBO_OK;
@@ -176,11 +173,9 @@ int ikbo_attn_bwd(void* bwd, const int32_t* user_offsets, const int32_t* cand_to
     // work lists into the next pinned buffer, once its last reader is done
     const size_t items_bytes = static_cast<size_t>(na + nb) * sizeof(WorkItem);
     const size_t bytes = items_bytes + static_cast<size_t>(std::max(n_cand, 1)) * 4;
-    const int si = b->next;
-    b->next ^= 1;
-    if (b->stage_used[si]) IKBO_HIP(hipEventSynchronize(b->stage_ev[si]));
-    if ((rc = b->stage[si].ensure(bytes)) != IKBO_OK) return rc;
-    char* base = static_cast<char*>(b->stage[si].ptr);
+    int si = 0;
+    if ((rc = b->ring.acquire(bytes, &si)) != IKBO_OK) return rc;
+    char* base = static_cast<char*>(b->ring.buf[si].ptr);
     std::memcpy(base, b->hp.items.data(), static_cast<size_t>(na) * sizeof(WorkItem));
     std::memcpy(base + na * sizeof(WorkItem), b->items_b.data(), static_cast<size_t>(nb) * sizeof(WorkItem));
     if (n_cand > 0) std::memcpy(base + items_bytes, b->hp.cand_perm.data(), static_cast<size_t>(n_cand) * 4);
@@ -226,9 +221,7 @@ int ikbo_attn_bwd(void* bwd, const int32_t* user_offsets, const int32_t* cand_to
     p.items = reinterpret_cast<const WorkItem*>(base) + na;
     e = ikbo::launch_bwd_dkv(p, static_cast<int>(nb), stream, te ? te + 2 : nullptr);
     if (e != hipSuccess) return fail_hip(e, "dK/dV launch");
-    IKBO_HIP(hipEventRecord(b->stage_ev[si], stream));
-    b->stage_used[si] = true;
-    return IKBO_OK;
+    return b->ring.launched(si, stream);
   } catch (...) {
     return fail(IKBO_ERR_NOMEM, "unexpected host error");
   }

@@ -80,11 +80,12 @@ struct DevBuf {
 // orders every host write before the device reads it.
 struct PinnedBuf {
   void* ptr = nullptr;
+  void* dev = nullptr;  // the device's address of the same memory, taken once per allocation
   size_t cap = 0;
   int ensure(size_t bytes, bool coherent = false) {
     if (bytes <= cap) return IKBO_OK;
     if (ptr) (void)hipHostFree(ptr);
-    ptr = nullptr;
+    ptr = dev = nullptr;
     cap = 0;
     size_t want = std::max<size_t>(bytes, 4096);
     hipError_t e = hipHostMalloc(&ptr, want, coherent ? hipHostMallocCoherent : hipHostMallocDefault);
@@ -92,13 +93,95 @@ struct PinnedBuf {
       ptr = nullptr;
       return fail(IKBO_ERR_NOMEM, std::string("hipHostMalloc: ") + hipGetErrorString(e));
     }
+    e = hipHostGetDevicePointer(&dev, ptr, 0);
+    if (e != hipSuccess) {
+      (void)hipHostFree(ptr);
+      ptr = dev = nullptr;
+      return fail_hip(e, "hipHostGetDevicePointer");
+    }
     cap = want;
     return IKBO_OK;
   }
   void release() {
     if (ptr) (void)hipHostFree(ptr);
-    ptr = nullptr;
+    ptr = dev = nullptr;
     cap = 0;
+  }
+};
+
+// Pinned host buffers handed out in turn to successive calls whose kernels
+// read them in place (work lists).  A buffer is reused only after the last
+// launch that read it has finished.  Completion is tracked by an event
+// recorded every kEventEvery launches, not after each one: an event after
+// every launch puts a barrier packet between consecutive calls on the stream
+// (measured at about 4.5 us per call).  Reusing a buffer means waiting for the
+// first periodic event at or after its last reader, which has normally long
+// fired: with kStages > kEventEvery buffers a call waits only when the host
+// is more than kStages - kEventEvery launches ahead of the device.  If that
+// event has not been recorded yet, one is recorded on the last launch's
+// stream and waited for.  One host thread per ring; launches on one stream.
+struct PinnedRing {
+  static constexpr int kStages = 16;
+  static constexpr int kEventEvery = 8;
+  static constexpr int kEvents = 4;
+  PinnedBuf buf[kStages];
+  int64_t last[kStages];        // last launch that read the buffer, -1 if none
+  hipEvent_t ev[kEvents] = {};
+  int64_t ev_seq[kEvents];      // launch each event was recorded after, -1 if none
+  hipEvent_t flush = nullptr;
+  int64_t n_launch = 0;
+  hipStream_t last_stream = nullptr;
+  int next = 0;
+
+  int init() {
+    for (int i = 0; i < kStages; ++i) last[i] = -1;
+    for (int i = 0; i < kEvents; ++i) {
+      ev_seq[i] = -1;
+      IKBO_HIP(hipEventCreateWithFlags(&ev[i], hipEventDisableTiming));
+    }
+    IKBO_HIP(hipEventCreateWithFlags(&flush, hipEventDisableTiming));
+    return IKBO_OK;
+  }
+  void release() {
+    for (int i = 0; i < kEvents; ++i)
+      if (ev[i]) (void)hipEventDestroy(ev[i]);
+    if (flush) (void)hipEventDestroy(flush);
+    for (int i = 0; i < kStages; ++i) buf[i].release();
+  }
+  // Waits until launch L and every earlier one have finished.
+  int wait(int64_t L) {
+    if (L < 0) return IKBO_OK;
+    const int64_t n_e = (L / kEventEvery) * kEventEvery + kEventEvery - 1;  // first event covering L
+    const int slot = static_cast<int>((n_e / kEventEvery) % kEvents);
+    if (ev_seq[slot] >= n_e) {  // that event, or a later one recorded in its slot
+      IKBO_HIP(hipEventSynchronize(ev[slot]));
+      return IKBO_OK;
+    }
+    IKBO_HIP(hipEventRecord(flush, last_stream));
+    IKBO_HIP(hipEventSynchronize(flush));
+    return IKBO_OK;
+  }
+  // The next buffer, grown to at least `bytes`, once its last reader is done.
+  int acquire(size_t bytes, int* idx) {
+    const int s = next;
+    next = (s + 1) % kStages;
+    int rc = wait(last[s]);
+    if (rc != IKBO_OK) return rc;
+    if ((rc = buf[s].ensure(bytes)) != IKBO_OK) return rc;
+    *idx = s;
+    return IKBO_OK;
+  }
+  // Notes that the launch just enqueued on `stream` reads buffer idx.
+  int launched(int idx, hipStream_t stream) {
+    const int64_t seq = n_launch++;
+    last[idx] = seq;
+    last_stream = stream;
+    if (seq % kEventEvery == kEventEvery - 1) {
+      const int slot = static_cast<int>((seq / kEventEvery) % kEvents);
+      IKBO_HIP(hipEventRecord(ev[slot], stream));
+      ev_seq[slot] = seq;
+    }
+    return IKBO_OK;
   }
 };
 

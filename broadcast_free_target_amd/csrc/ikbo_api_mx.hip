@@ -28,16 +28,12 @@ using ikbo::HostPlan;
 using ikbo::PlanParams;
 using ikbo::WorkItem;
 
-// MXFP8 attention: the work lists of the last calls (two pinned buffers used
-// alternately, each guarded by an event after its last reader) and the split
-// partials.
+// MXFP8 attention: the work lists of the last calls (pinned buffers handed
+// out in turn by the ring) and the split partials.
 struct Mx {
   int device = -1;
   int n_cu = 0;
-  PinnedBuf stage[2];
-  hipEvent_t stage_ev[2] = {nullptr, nullptr};
-  bool stage_used[2] = {false, false};
-  int next = 0;
+  PinnedRing ring;
   DevBuf ws_o, ws_rec;
   HostPlan hp;
   std::vector<int32_t> vblk;  // per item: first and last V-scale block
@@ -47,10 +43,7 @@ struct Mx {
   int n_timed = 0;
   ~Mx() {
     for (hipEvent_t e : tev) (void)hipEventDestroy(e);
-    for (int i = 0; i < 2; ++i) {
-      if (stage_ev[i]) (void)hipEventDestroy(stage_ev[i]);
-      stage[i].release();
-    }
+    ring.release();
     ws_o.release();
     ws_rec.release();
   }
@@ -68,10 +61,13 @@ int ikbo_mx_create(void** mx) {
     if (!m) return fail(IKBO_ERR_NOMEM, "mx allocation");
     hipError_t e = hipGetDevice(&m->device);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&m->n_cu, hipDeviceAttributeMultiprocessorCount, m->device);
-    for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&m->stage_ev[i], hipEventDisableTiming);
     if (e != hipSuccess) {
       delete m;
       return fail_hip(e, "mx create");
+    }
+    if (int rc = m->ring.init(); rc != IKBO_OK) {
+      delete m;
+      return rc;
     }
     *mx = m;
     return IKBO_OK;
@@ -158,11 +154,9 @@ int ikbo_attn_fwd_mxfp8(void* mx, const int32_t* user_offsets, const int32_t* ca
     const size_t perm_at = (items_bytes + 255) & ~size_t(255);
     const size_t vblk_at = perm_at + ((static_cast<size_t>(n_cand) * 4 + 255) & ~size_t(255));
     const size_t bytes = vblk_at + static_cast<size_t>(2 * n_items) * 4 + 256;
-    const int si = m->next;
-    m->next ^= 1;
-    if (m->stage_used[si]) IKBO_HIP(hipEventSynchronize(m->stage_ev[si]));
-    if ((rc = m->stage[si].ensure(bytes)) != IKBO_OK) return rc;
-    char* base = static_cast<char*>(m->stage[si].ptr);
+    int si = 0;
+    if ((rc = m->ring.acquire(bytes, &si)) != IKBO_OK) return rc;
+    char* base = static_cast<char*>(m->ring.buf[si].ptr);
     std::memcpy(base, m->hp.items.data(), items_bytes);
     std::memcpy(base + perm_at, m->hp.cand_perm.data(), static_cast<size_t>(n_cand) * 4);
     std::memcpy(base + vblk_at, m->vblk.data(), static_cast<size_t>(2 * n_items) * 4);
@@ -208,9 +202,7 @@ int ikbo_attn_fwd_mxfp8(void* mx, const int32_t* user_offsets, const int32_t* ca
       e = ikbo::launch_merge(ap, m->hp.n_groups, ikbo::kMxHeadDim, stream, te ? te + 2 : nullptr);
       if (e != hipSuccess) return fail_hip(e, "merge launch");
     }
-    IKBO_HIP(hipEventRecord(m->stage_ev[si], stream));
-    m->stage_used[si] = true;
-    return IKBO_OK;
+    return m->ring.launched(si, stream);
   } catch (...) {
     return fail(IKBO_ERR_NOMEM, "unexpected host error");
   }

@@ -10,6 +10,7 @@ All computation happens in the library's HIP kernels; there is no fallback.
 from __future__ import annotations
 
 import ctypes
+from collections import OrderedDict
 import os
 from typing import Optional
 
@@ -42,7 +43,7 @@ SIGNATURES = {
     "ikbo_self_target_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P]),
     "ikbo_attn_fwd_materialized": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P]),
     "ikbo_plan_create": (ctypes.c_int, [ctypes.POINTER(_P)]),
-    "ikbo_plan_build": (ctypes.c_int, [_P, _IP, _IP, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "ikbo_plan_build": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "ikbo_attn_fwd_planned": (ctypes.c_int, [_P, _P, _P, _P, _P, _F, _P, _P, _P]),
     "ikbo_plan_destroy": (None, [_P]),
     "ikbo_plan_info": (ctypes.c_int, [_P, _LP, _I]),
@@ -61,14 +62,14 @@ SIGNATURES = {
     "ikbo_lce3_create": (ctypes.c_int, [ctypes.POINTER(_P), _P, _I, _I, _I, _I, _I, _P]),
     "ikbo_lce3_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "ikbo_bwd_create": (ctypes.c_int, [ctypes.POINTER(_P)]),
-    "ikbo_attn_bwd": (ctypes.c_int, [_P, _IP, _IP, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "ikbo_attn_bwd": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "ikbo_bwd_info": (ctypes.c_int, [_P, _LP, _I]),
     "ikbo_bwd_timing": (ctypes.c_int, [_P, _I]),
     "ikbo_bwd_timing_read": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
                                             _I, _IP]),
     "ikbo_bwd_destroy": (None, [_P]),
     "ikbo_mx_create": (ctypes.c_int, [ctypes.POINTER(_P)]),
-    "ikbo_attn_fwd_mxfp8": (ctypes.c_int, [_P, _IP, _IP, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "ikbo_attn_fwd_mxfp8": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P]),
     "ikbo_mx_info": (ctypes.c_int, [_P, _LP, _I]),
     "ikbo_mx_timing": (ctypes.c_int, [_P, _I]),
     "ikbo_mx_timing_read": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
@@ -162,6 +163,31 @@ def _i32(a: np.ndarray):
     return a.ctypes.data_as(_IP)
 
 
+# Addresses of the last few host mapping arrays.  Reading an ndarray's address
+# through numpy's ctypes interface costs microseconds, a sizeable part of a
+# small request's host time when the same arrays come back call after call.
+# Each entry holds a reference to its array, so the array cannot be freed and
+# its id reused while the entry exists, and an ndarray's buffer does not move
+# while referenced.
+_HOST_PTRS: "OrderedDict[int, tuple]" = OrderedDict()
+
+
+def _host_i32(a: np.ndarray) -> Optional[int]:
+    """Address of a contiguous int32 host array, read by the C side during the call."""
+    if a.size == 0:
+        return None
+    e = _HOST_PTRS.get(id(a))
+    if e is not None and e[0] is a:
+        return e[1]
+    if a.dtype != np.int32 or not a.flags["C_CONTIGUOUS"]:
+        raise _bad("host mapping arrays must be contiguous int32")
+    ptr = a.ctypes.data
+    _HOST_PTRS[id(a)] = (a, ptr)
+    if len(_HOST_PTRS) > 8:
+        _HOST_PTRS.popitem(last=False)
+    return ptr
+
+
 def ikbo_version() -> int:
     return load_library().ikbo_version()
 
@@ -253,8 +279,7 @@ def ikbo_plan_build(plan, user_offsets_host, cand_to_user_host, n_users, n_cand,
     c2u = np.ascontiguousarray(cand_to_user_host, dtype=np.int32)
     _PLAN_DIMS.pop(plan, None)
     rc = _check(load_library().ikbo_plan_build(
-        plan, _i32(offs), _i32(c2u) if c2u.size else None, n_users, n_cand, n_q, H, d, dtype,
-        int(with_self), _stream(stream)))
+        plan, _host_i32(offs), _host_i32(c2u), n_users, n_cand, n_q, H, d, dtype, int(with_self), _stream(stream)))
     es = _es(dtype)
     _PLAN_DIMS[plan] = (es, n_cand * n_q * H * d * es, int(offs[n_users]) * H * d * es, bool(with_self))
     return rc
@@ -380,7 +405,7 @@ def ikbo_attn_bwd(bwd, user_offsets_host, cand_to_user_host, n_users, n_cand, n_
         for t, nm in ((k_user, "k_user"), (v_user, "v_user"), (dk_user, "dk_user"), (dv_user, "dv_user")):
             _need(t, kv, nm, 2)
     return _check(load_library().ikbo_attn_bwd(
-        bwd, _i32(offs), _i32(c2u) if c2u.size else None, n_users, n_cand, n_q, H, d, float(scale), _ptr(q_cand),
+        bwd, _host_i32(offs), _host_i32(c2u), n_users, n_cand, n_q, H, d, float(scale), _ptr(q_cand),
         _ptr(k_user), _ptr(v_user), _ptr(out), _ptr(dout), _ptr(dq_cand), _ptr(dk_user), _ptr(dv_user),
         _stream(stream)))
 
@@ -431,7 +456,7 @@ def ikbo_attn_fwd_mxfp8(mx, user_offsets_host, cand_to_user_host, n_users, n_can
         _need(v_scales, nvb * H * d, "v_scales", 1)
         _need(out, n_cand * n_q * H * d * 2, "out", 2)
     return _check(load_library().ikbo_attn_fwd_mxfp8(
-        mx, _i32(offs), _i32(c2u) if c2u.size else None, n_users, n_cand, n_q, H, d, float(scale), _ptr(q_codes),
+        mx, _host_i32(offs), _host_i32(c2u), n_users, n_cand, n_q, H, d, float(scale), _ptr(q_codes),
         _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales), _ptr(out), _stream(stream)))
 
 

@@ -151,8 +151,9 @@ int ikbo_attn_fwd_materialized(const void* q_cand, const void* k_user, const voi
  *   the load-balanced work list over (user, head, row tile, key chunk) in a
  *   pinned host buffer that the kernels read in place (no copy is enqueued).
  *   Does not synchronise.  A plan may be rebuilt for a new request at any
- *   time: it alternates between two buffers and waits, if needed, only for
- *   the launches of the build two builds earlier to finish.
+ *   time: it uses 16 pinned buffers in turn, and a build waits, if needed,
+ *   only for the launches that read its buffer 16 builds earlier (tracked
+ *   by an event recorded every 8th launch, not after each one).
  *   with_self = 1 adds causal self-attention rows (then n_q must be 1).
  * ikbo_attn_fwd_planned: launches the attention for the plan's last build.
  *   q_user/out_user are used only when the plan was built with with_self.
@@ -283,8 +284,8 @@ void ikbo_lce_destroy(void* lce);
  * 128 keys of a user with the reduction over candidates in registers (no
  * atomics; results are deterministic).
  *
- * ikbo_bwd_create: a handle owning the work lists (pinned host memory, two
- *   alternating buffers) and device workspaces: 4 * (1 + 2H) * (n_cand*n_q +
+ * ikbo_bwd_create: a handle owning the work lists (pinned host memory, 16
+ *   buffers used in turn, as for plans) and device workspaces: 4 * (1 + 2H) * (n_cand*n_q +
  *   128) bytes of per-row statistics, and 64 KB + 2 KB per split slot of dQ
  *   partials (long key ranges are split as in the forward and merged in chunk
  *   order, so results stay deterministic).
@@ -334,8 +335,9 @@ void ikbo_bwd_destroy(void* bwd);
  * Both products run on the block-scaled FP8 matrix instruction with fp32
  * accumulation; long key ranges are split and merged as in the bf16 path.
  *
- * ikbo_mx_create: a handle owning the work lists (pinned host memory, two
- *   alternating buffers) and the split partials (64 KB + 2 KB per slot).
+ * ikbo_mx_create: a handle owning the work lists (pinned host memory, 16
+ *   buffers used in turn, as for plans) and the split partials (64 KB + 2 KB
+ *   per slot).
  * ikbo_attn_fwd_mxfp8: user_offsets [n_users + 1] and cand_to_user [n_cand]
  *   are HOST int32 arrays; the tensors are device arrays, row-major uint8:
  *     q_codes [n_cand, n_q, H, d]   q_scales [n_cand, n_q, H, d/32]

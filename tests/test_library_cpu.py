@@ -329,3 +329,21 @@ def test_binding_rejects_buffers_smaller_than_the_call_touches():
         with pytest.raises(IkboError) as e:
             _need(t, 100, "x", elem)
         assert e.value.status == IKBO_ERR_INVALID_ARG and msg in str(e.value)
+
+
+def test_binding_host_array_addresses():
+    """Host mapping arrays go to the C side as addresses: contiguous int32 only,
+    the array's own buffer (cached per array, never another array's)."""
+    from broadcast_free_target_amd import IkboError
+    from broadcast_free_target_amd.ikbo import _host_i32
+    a = np.arange(10, dtype=np.int32)
+    b = np.arange(10, dtype=np.int32)
+    assert _host_i32(a) == a.ctypes.data and _host_i32(a) == a.ctypes.data
+    assert _host_i32(b) == b.ctypes.data != a.ctypes.data
+    assert _host_i32(np.zeros(0, np.int32)) is None
+    for bad in (np.arange(10, dtype=np.int64), np.arange(20, dtype=np.int32)[::2]):
+        with pytest.raises(IkboError):
+            _host_i32(bad)
+    for _ in range(20):  # more arrays than the cache keeps: each still maps to its own buffer
+        c = np.arange(5, dtype=np.int32)
+        assert _host_i32(c) == c.ctypes.data
