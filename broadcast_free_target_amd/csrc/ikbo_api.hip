@@ -48,12 +48,6 @@ struct Plan {
   HostPlan hp;
   // device copies of the work list
   DevBuf d_items, d_ws_o, d_ws_rec;  // d_items: device copy of the plan buffer (copy mode)
-  // IKBO_FOLD=1: split groups merged inside the attention kernel, by the
-  // workgroup that finishes a group's last chunk (one arrival counter per
-  // group, zeroed when allocated and reset by that workgroup).  Off by default:
-  // one workgroup merging a whole group is slower than the merge kernel.
-  bool fold = false;
-  DevBuf d_grp_cnt;
   // Pinned plan buffers, handed out in turn by the ring.  With in-place reads
   // (the default) the kernels read the work list from them; otherwise
   // (IKBO_PLAN_UPLOAD=copy) a copy to the device buffers above reads them.
@@ -79,7 +73,6 @@ struct Plan {
     d_items.release();
     d_ws_o.release();
     d_ws_rec.release();
-    d_grp_cnt.release();
     d_trace.release();
   }
 };
@@ -231,10 +224,6 @@ int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n
   p->stages = bf16_stages();
   p->variant = variant;
   p->total_len = offs[n_users];
-  p->fold = dtype == IKBO_DTYPE_BF16 && env_int("IKBO_FOLD", 0) != 0;
-  if (p->fold && hp.n_groups > 0 &&
-      (rc = p->d_grp_cnt.ensure(static_cast<size_t>(hp.n_groups) * sizeof(int32_t), true)) != IKBO_OK)
-    return rc;
   p->built = true;
   return IKBO_OK;
 }
@@ -302,11 +291,9 @@ int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* 
     }
     te = &p->tev[4 * p->n_timed];
     p->timed_merge.resize(p->n_timed + 1);
-    p->timed_merge[p->n_timed] = p->hp.n_groups > 0 && !p->fold;
+    p->timed_merge[p->n_timed] = p->hp.n_groups > 0;
     ++p->n_timed;
   }
-  const bool fold = p->fold && p->hp.n_groups > 0;
-  ap.grp_cnt = fold ? static_cast<int32_t*>(p->d_grp_cnt.ptr) : nullptr;
   hipError_t e;
   if (p->dtype != IKBO_DTYPE_BF16)
     e = ikbo::launch_attn_f32(ap, p->d, p->hp.grid, stream, te);
@@ -319,7 +306,7 @@ int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* 
     e = ikbo::launch_attn_bf16(ap, p->d, p->stages, p->hp.grid, stream, te);
   }
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
-  if (p->hp.n_groups > 0 && !fold) {
+  if (p->hp.n_groups > 0) {
     e = ikbo::launch_merge(ap, p->hp.n_groups, p->d, stream, te ? te + 2 : nullptr);
     if (e != hipSuccess) return fail_hip(e, "merge launch");
   }
@@ -489,7 +476,7 @@ int ikbo_plan_info(void* plan, int64_t* info, int32_t n_info) {
                          : p->variant == kVariantW4  ? 2
                          : p->variant == kVariantW4R ? 4
                                                      : 3;
-  const int64_t v[10] = {static_cast<int64_t>(p->hp.items.size()),
+  const int64_t v[9] = {static_cast<int64_t>(p->hp.items.size()),
                         p->hp.grid,
                         p->hp.n_groups,
                         p->hp.n_slots,
@@ -498,9 +485,8 @@ int ikbo_plan_info(void* plan, int64_t* info, int32_t n_info) {
                         p->hp.n_target_tiles,
                         p->hp.n_self_tiles,
                         p->n_cu,
-                        kernel,
-                        (p->fold && p->hp.n_groups > 0) ? 1 : 0};
-  for (int i = 0; i < n_info && i < 10; ++i) info[i] = v[i];
+                        kernel};
+  for (int i = 0; i < n_info && i < 9; ++i) info[i] = v[i];
   return IKBO_OK;
 }
 

@@ -62,40 +62,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Device-coherent 16-byte store and load, as two 8-byte relaxed atomics at
-// agent scope (global_store / global_load with sc1).  The L2 of one XCD does
-// not see another XCD's dirty lines, so data that a workgroup on any XCD reads
-// within the same launch goes through these; ordering comes from an explicit
-// vmcnt wait on the writer and a control dependence on the reader, not from an
-// agent-scope fence (which would write back the whole L2).
-__device__ __forceinline__ void store_coherent(float* p, f32x4_t v) {
-  const u32x4_t u = __builtin_bit_cast(u32x4_t, v);
-  uint64_t* q = reinterpret_cast<uint64_t*>(p);
-  __hip_atomic_store(q, static_cast<uint64_t>(u.x) | (static_cast<uint64_t>(u.y) << 32), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 1, static_cast<uint64_t>(u.z) | (static_cast<uint64_t>(u.w) << 32), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ f32x4_t load_coherent(const float* p) {
-  // global, not flat: p always points into device memory
-  typedef __attribute__((address_space(1))) uint64_t global_u64;
-  global_u64* q = (global_u64*)(const_cast<float*>(p));
-  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return __builtin_bit_cast(f32x4_t, u32x4_t{static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32),
-                                             static_cast<uint32_t>(b), static_cast<uint32_t>(b >> 32)});
-}
-
-// Store of one 16-byte piece of a split partial: device-coherent when the
-// launch folds its split groups itself, plain otherwise.
-__device__ __forceinline__ void store_partial(float* p, f32x4_t v, bool coherent) {
-  if (coherent)
-    store_coherent(p, v);
-  else
-    *reinterpret_cast<f32x4_t*>(p) = v;
-}
-
 // Logical workgroup id: ids w and w+1 share an XCD when the grid is a multiple of 8.
 __device__ __forceinline__ int logical_wg() {
   const int G = gridDim.x, b = blockIdx.x;

@@ -36,9 +36,6 @@ struct AttnParams {
                           // nchunk | kind << 16, the last two as int32 bits
   uint64_t* trace;        // optional: [n_items, 6] per-item records (bf16 kernel), or null
   int32_t kv_reverse;     // 4-wave bf16 kernel: 1 = visit each item's key tiles last to first
-  int32_t* grp_cnt;       // bf16 kernels: [n_groups] arrival counters, zero between launches; when
-                          // set, the last chunk of each split group to finish merges the group
-                          // (no merge launch); null: partials are left for launch_merge
 };
 
 // stages: depth of the HBM -> LDS ring (2, 3 or 4); 2 stages allow two

@@ -84,9 +84,8 @@ __device__ __forceinline__ f32x4_t split_record(float m, float l, int64_t qrow, 
 
 // Chunk weights of one row of a split group: w_c = 2^(m_c - M) / L with
 // M = max_c m_c and L = sum_c 2^(m_c - M) l_c, so that O = sum_c w_c O_c (the
-// log-sum-exp merge of split-K partial results, TLX attention post).  Shared
-// by the merge kernel and the in-kernel fold, with contraction off so that
-// both round alike.
+// log-sum-exp merge of split-K partial results, TLX attention post).
+// Contraction off: every build rounds the merge alike.
 __device__ __forceinline__ void chunk_weights(const float* m, const float* l, int nchunk, float* w) {
 #pragma clang fp contract(off)
   float M = kNegInf;
@@ -116,105 +115,6 @@ __device__ __forceinline__ u32x2_t weigh_slice(const float* w, const f32x4_t* o)
   return pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
 }
 
-typedef __attribute__((address_space(3))) float lds_f32;
-typedef __attribute__((address_space(3))) int lds_i32;
-
-// Rows of a split group with exactly N chunks: thread -> (row, 4 columns),
-// the N coherent loads of a slice issued together.
-template <int D, int N>
-__device__ __forceinline__ void fold_slices(const float* ws_o, const lds_f32* s_w, const lds_i32* s_unit,
-                                            uint16_t* out_cand, uint16_t* out_user, int64_t slot0, int nrows,
-                                            int tid, int nthreads) {
-  constexpr int TPR = D / 4;
-  for (int t = tid; t < nrows * TPR; t += nthreads) {
-    const int r = t / TPR, c0 = (t % TPR) * 4;
-    const int unit = s_unit[r];
-    if (unit < 0) continue;
-    f32x4_t o[N];
-#pragma unroll
-    for (int c = 0; c < N; ++c) o[c] = load_coherent(ws_o + ((slot0 + c) * kBM + r) * D + c0);
-    float w[N];
-#pragma unroll
-    for (int c = 0; c < N; ++c) w[c] = s_w[r * kMaxSplit + c];
-    uint16_t* ob = s_unit[kBM + r] == kKindSelf ? out_user : out_cand;
-    *reinterpret_cast<u32x2_t*>(ob + static_cast<int64_t>(unit) * D + c0) = weigh_slice<N>(w, o);
-  }
-}
-
-// Merge of one split group by the workgroup whose chunk finished last, with
-// the partials read device-coherently (the other chunks may have run on other
-// XCDs).  The group's row records go to LDS once (the K/V ring, idle between
-// items), each row's chunk weights are computed once, then every output slice
-// is a weighted sum of nchunk partial slices.  Out of line, with scalar
-// arguments, so the attention kernels' register allocation is left alone.
-template <int D>
-__device__ __noinline__ void fold_group(const float* ws_o, const float* ws_rec, uint16_t* out_cand,
-                                        uint16_t* out_user, int64_t slot0, int nrows, int nchunk, int tid,
-                                        int nthreads, lds_f32* scratch) {
-  lds_f32* s_m = scratch;                                  // [kBM][kMaxSplit]
-  lds_f32* s_l = s_m + kBM * kMaxSplit;                    // [kBM][kMaxSplit]
-  lds_f32* s_w = s_l + kBM * kMaxSplit;                    // [kBM][kMaxSplit]
-  lds_i32* s_unit = reinterpret_cast<lds_i32*>(s_w + kBM * kMaxSplit);  // [kBM] unit, then [kBM] kind
-  for (int i = tid; i < nrows * nchunk; i += nthreads) {
-    const int r = i / nchunk, c = i - r * nchunk;
-    const f32x4_t rec = load_coherent(ws_rec + ((slot0 + c) * kBM + r) * 4);
-    s_m[r * kMaxSplit + c] = rec[0];
-    s_l[r * kMaxSplit + c] = rec[1];
-    if (c == 0) {
-      const float unit_f = rec[2], tag_f = rec[3];
-      s_unit[r] = __builtin_bit_cast(int, unit_f);
-      s_unit[kBM + r] = __builtin_bit_cast(int, tag_f) >> 16;
-    }
-  }
-  __syncthreads();
-  for (int r = tid; r < nrows; r += nthreads) {
-    float m[kMaxSplit], l[kMaxSplit], w[kMaxSplit];
-#pragma unroll
-    for (int c = 0; c < kMaxSplit; ++c) {
-      m[c] = c < nchunk ? s_m[r * kMaxSplit + c] : kNegInf;
-      l[c] = c < nchunk ? s_l[r * kMaxSplit + c] : 0.0f;
-    }
-    chunk_weights(m, l, nchunk, w);
-#pragma unroll
-    for (int c = 0; c < kMaxSplit; ++c) s_w[r * kMaxSplit + c] = w[c];
-  }
-  __syncthreads();
-  switch (nchunk) {
-    case 1: fold_slices<D, 1>(ws_o, s_w, s_unit, out_cand, out_user, slot0, nrows, tid, nthreads); break;
-    case 2: fold_slices<D, 2>(ws_o, s_w, s_unit, out_cand, out_user, slot0, nrows, tid, nthreads); break;
-    case 3: fold_slices<D, 3>(ws_o, s_w, s_unit, out_cand, out_user, slot0, nrows, tid, nthreads); break;
-    case 4: fold_slices<D, 4>(ws_o, s_w, s_unit, out_cand, out_user, slot0, nrows, tid, nthreads); break;
-    case 5: fold_slices<D, 5>(ws_o, s_w, s_unit, out_cand, out_user, slot0, nrows, tid, nthreads); break;
-    case 6: fold_slices<D, 6>(ws_o, s_w, s_unit, out_cand, out_user, slot0, nrows, tid, nthreads); break;
-    case 7: fold_slices<D, 7>(ws_o, s_w, s_unit, out_cand, out_user, slot0, nrows, tid, nthreads); break;
-    default: fold_slices<D, 8>(ws_o, s_w, s_unit, out_cand, out_user, slot0, nrows, tid, nthreads); break;
-  }
-  __syncthreads();  // the ring is free again before the next item's copies land in it
-}
-
-// Called by every thread after the item's epilogue stores, each wave having
-// waited for its own stores (vmcnt 0).  The barrier makes the whole tile's
-// partial complete before one thread counts the chunk in; the chunk that
-// brings the count to nchunk merges the group and resets its counter for the
-// next launch.  Nothing waits on another workgroup, so there is no deadlock
-// however the items are scheduled.
-template <int D>
-__device__ __forceinline__ void fold_if_last(const AttnParams& P, const WorkItem& it, int tid, int nthreads,
-                                             int* s_last, void* ring) {
-  if (it.grp < 0 || P.grp_cnt == nullptr) return;
-  __syncthreads();
-  if (tid == 0)
-    *s_last = __hip_atomic_fetch_add(P.grp_cnt + it.grp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              it.nchunk - 1;
-  __syncthreads();
-  if (*s_last) {
-    fold_group<D>(P.ws_o, P.ws_rec, static_cast<uint16_t*>(P.out_cand), static_cast<uint16_t*>(P.out_user),
-                  static_cast<int64_t>(it.slot0), it.nrows, it.nchunk, tid, nthreads,
-                  reinterpret_cast<lds_f32*>(reinterpret_cast<__attribute__((address_space(3))) char*>(
-                      lds_address(ring))));
-    if (tid == 0) __hip_atomic_store(P.grp_cnt + it.grp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
 
 // {x[l], x[l ^ 32]} for every lane l, via v_permlane32_swap: with both
 // operands holding x, the first comes back with the lower half's values in
@@ -389,7 +289,6 @@ template <int D, int NST>
 __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_kernel(AttnParams P) {
   using T = Tile<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[NST * T::stage];
-  __shared__ int s_last;  // this workgroup finished its split group's last chunk
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -531,23 +430,19 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
       }
     } else {
       const int64_t slot = static_cast<int64_t>(it.slot0) + it.chunk;
-      const bool coh = P.grp_cnt != nullptr;
       if (r_w < it.nrows) {
         float* wo = P.ws_o + (slot * kBM + r_w) * D + g * 4;
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4)
-            store_partial(wo + mb * 32 + i4 * 8,
-                          f32x4_t{oacc[mb][i4 * 4 + 0], oacc[mb][i4 * 4 + 1], oacc[mb][i4 * 4 + 2],
-                                  oacc[mb][i4 * 4 + 3]},
-                          coh);
+            *reinterpret_cast<f32x4_t*>(wo + mb * 32 + i4 * 8) =
+                f32x4_t{oacc[mb][i4 * 4 + 0], oacc[mb][i4 * 4 + 1], oacc[mb][i4 * 4 + 2], oacc[mb][i4 * 4 + 3]};
       }
       if (g == 0)  // every tile row gets a record; empty rows are marked
-        store_partial(P.ws_rec + (slot * kBM + r_w) * 4, split_record(m_run, l_run, qrow, it, P.H), coh);
+        *reinterpret_cast<f32x4_t*>(P.ws_rec + (slot * kBM + r_w) * 4) = split_record(m_run, l_run, qrow, it, P.H);
     }
     wait_vmcnt<0>();  // epilogue stores retire before the next item's copies are counted
-    fold_if_last<D>(P, it, tid, kThreads, &s_last, smem);
     if (P.trace && tid == 0) {
       uint64_t* tr = P.trace + pos * 6;
       tr[0] = (static_cast<uint64_t>(w) << 32) | hw_place();
@@ -617,18 +512,17 @@ __device__ __forceinline__ void finish_half(const AttnParams& P, const WorkItem&
     }
   } else {
     const int64_t slot = static_cast<int64_t>(it.slot0) + it.chunk;
-    const bool coh = P.grp_cnt != nullptr;
     if (r_w < it.nrows) {
       float* wo = P.ws_o + (slot * kBM + r_w) * D + g * 4;
 #pragma unroll
       for (int j = 0; j < HV; j += 4) {
         const int v = V0 + j, mb = v / 16, i = v % 16;
-        store_partial(wo + mb * 32 + (i / 4) * 8, f32x4_t{oacc[mb][i], oacc[mb][i + 1], oacc[mb][i + 2], oacc[mb][i + 3]},
-                      coh);
+        *reinterpret_cast<f32x4_t*>(wo + mb * 32 + (i / 4) * 8) =
+            f32x4_t{oacc[mb][i], oacc[mb][i + 1], oacc[mb][i + 2], oacc[mb][i + 3]};
       }
     }
     if (write_rec)  // every tile row gets a record; empty rows are marked
-      store_partial(P.ws_rec + (slot * kBM + r_w) * 4, split_record(M, L, qrow, it, P.H), coh);
+      *reinterpret_cast<f32x4_t*>(P.ws_rec + (slot * kBM + r_w) * 4) = split_record(M, L, qrow, it, P.H);
   }
 }
 
@@ -637,7 +531,6 @@ __global__ __launch_bounds__(512, 1) void ikbo_attn_bf16_w8_kernel(AttnParams P)
   using S = Step<D>;
   constexpr int NT = S::threads;
   __shared__ __attribute__((aligned(16))) uint16_t smem[NST * S::stage];
-  __shared__ int s_last;  // this workgroup finished its split group's last chunk
   static_assert(NST * S::stage * 2 >= (8 * S::hv * 64 + 8 * 64 * 2) * 4, "exchange area fits in the ring");
 
   const int tid = threadIdx.x;
@@ -788,7 +681,6 @@ __global__ __launch_bounds__(512, 1) void ikbo_attn_bf16_w8_kernel(AttnParams P)
     }
     wait_vmcnt<0>();  // epilogue stores retire before the next item's copies are counted
     __syncthreads();  // the exchange area is read before the next item's copies overwrite it
-    fold_if_last<D>(P, it, tid, NT, &s_last, smem);
     if (P.trace && tid == 0) {
       uint64_t* tr = P.trace + pos * 6;
       tr[0] = (static_cast<uint64_t>(w) << 32) | hw_place();
@@ -962,19 +854,17 @@ __device__ __forceinline__ void write_tile_rows(const AttnParams& P, const WorkI
     }
   } else {
     const int64_t slot = static_cast<int64_t>(it.slot0) + it.chunk;
-    const bool coh = P.grp_cnt != nullptr;
     if (r_w < it.nrows) {
       float* wo = P.ws_o + (slot * kBM + r_w) * D + g * 4;
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4)
-          store_partial(wo + mb * 32 + i4 * 8,
-                        f32x4_t{oacc[mb][i4 * 4 + 0], oacc[mb][i4 * 4 + 1], oacc[mb][i4 * 4 + 2], oacc[mb][i4 * 4 + 3]},
-                        coh);
+          *reinterpret_cast<f32x4_t*>(wo + mb * 32 + i4 * 8) =
+              f32x4_t{oacc[mb][i4 * 4 + 0], oacc[mb][i4 * 4 + 1], oacc[mb][i4 * 4 + 2], oacc[mb][i4 * 4 + 3]};
     }
     if (g == 0)  // every tile row gets a record; empty rows are marked
-      store_partial(P.ws_rec + (slot * kBM + r_w) * 4, split_record(m_run, l_run, qrow, it, P.H), coh);
+      *reinterpret_cast<f32x4_t*>(P.ws_rec + (slot * kBM + r_w) * 4) = split_record(m_run, l_run, qrow, it, P.H);
   }
 }
 
@@ -1140,7 +1030,6 @@ __global__ __launch_bounds__(kThreads, 1) void ikbo_attn_bf16_pipe_kernel(AttnPa
   constexpr int TE = T::elems;
   static_assert(NR >= 3, "ring depth");
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * NR * TE];  // NR K tiles, then NR V tiles
-  __shared__ int s_last;  // this workgroup finished its split group's last chunk
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -1299,7 +1188,6 @@ __global__ __launch_bounds__(kThreads, 1) void ikbo_attn_bf16_pipe_kernel(AttnPa
     if (P.trace) t_loop = now_ticks();
     write_tile_rows<D>(P, it, ps.oacc, ps.m_run, ps.l_run, qrow, causal, r_w, g);
     wait_vmcnt<0>();  // epilogue stores retire before the next item's copies are counted
-    fold_if_last<D>(P, it, tid, kThreads, &s_last, smem);
     if (P.trace && tid == 0) {
       uint64_t* tr = P.trace + pos * 6;
       tr[0] = (static_cast<uint64_t>(w) << 32) | hw_place();
@@ -1320,8 +1208,7 @@ __global__ __launch_bounds__(kThreads, 1) void ikbo_attn_bf16_pipe_kernel(AttnPa
 // count, the output row and the kind.  A thread loads the records of all
 // kMaxSplit slots of its group at once (slots past nchunk hold stale records
 // and are ignored), then one 16-byte slice of O per chunk, computes its row's
-// chunk weights and sums the weighted slices in chunk order, as the in-kernel
-// fold does.
+// chunk weights and sums the weighted slices in chunk order.
 
 template <int D>
 __global__ __launch_bounds__(256) void ikbo_merge_kernel(AttnParams P) {
@@ -1354,7 +1241,7 @@ __global__ __launch_bounds__(256) void ikbo_merge_kernel(AttnParams P) {
   }
   chunk_weights(m, l, nchunk, w);
   u32x2_t packed;
-  switch (nchunk) {  // the same sums, in the same order, as the in-kernel fold
+  switch (nchunk) {  // straight-line sums over exactly nchunk slices
     case 1: packed = weigh_slice<1>(w, o); break;
     case 2: packed = weigh_slice<2>(w, o); break;
     case 3: packed = weigh_slice<3>(w, o); break;

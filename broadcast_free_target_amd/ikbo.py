@@ -308,10 +308,10 @@ def ikbo_plan_destroy(plan) -> None:
 
 
 def ikbo_plan_info(plan) -> dict:
-    info = (ctypes.c_int64 * 10)()
-    _check(load_library().ikbo_plan_info(plan, info, 10))
+    info = (ctypes.c_int64 * 9)()
+    _check(load_library().ikbo_plan_info(plan, info, 9))
     keys = ("n_items", "grid", "n_groups", "n_slots", "partial_bytes", "n_target_tiles", "n_self_tiles", "n_cu",
-            "kernel", "fold")
+            "kernel")
     return dict(zip(keys, list(info)))
 
 

@@ -158,11 +158,9 @@ int ikbo_attn_fwd_materialized(const void* q_cand, const void* k_user, const voi
  * ikbo_attn_fwd_planned: launches the attention for the plan's last build.
  *   q_user/out_user are used only when the plan was built with with_self.
  *   Launches of one plan must be ordered on one stream: they share the plan's
- *   split-KV workspace (and, with IKBO_FOLD=1, per-group arrival counters).
- *   Split groups are merged with the log-sum-exp rule of the TLX attention
- *   post's split-K section, in chunk order, by a merge kernel or, with
- *   IKBO_FOLD=1, by the workgroup that finishes a group's last chunk; both give
- *   the same bits.
+ *   split-KV workspace.  Split groups are merged by a second kernel with the
+ *   log-sum-exp rule of the TLX attention post's split-K section, in chunk
+ *   order, so results do not depend on the schedule or the launch grid.
  * ikbo_plan_destroy: frees the plan after synchronising its device.
  */
 int ikbo_plan_create(void** plan);
@@ -180,9 +178,8 @@ void ikbo_plan_destroy(void* plan);
  * split-KV merge kernel of each later ikbo_attn_fwd_planned call (at most 4096
  * launches; 0 stops and both calls reset the record).  ikbo_plan_timing_read
  * waits for the recorded events and writes per-launch durations in
- * milliseconds (merge_ms is 0 for launches without a merge kernel: nothing
- * split, or the groups merged inside the attention kernel); *n receives the
- * number written.
+ * milliseconds (merge_ms is 0 for launches without split groups); *n receives
+ * the number written.
  */
 int ikbo_plan_timing(void* plan, int32_t enable);
 int ikbo_plan_timing_read(void* plan, float* attn_ms, float* merge_ms, int32_t max_n, int32_t* n);
@@ -377,11 +374,7 @@ void ikbo_mx_destroy(void* mx);
  * [3] partial-result slots, [4] bytes of the split-KV workspace, [5] target
  * row tiles, [6] self row tiles, [7] compute units, [8] kernel (0 fp32, 1 bf16
  * eight-wave, 2 bf16 4-wave, 3 bf16 software-pipelined, 4 bf16 4-wave visiting
- * each item's key tiles last to first), [9] 1 when the split groups are merged
- * inside the attention kernel by the workgroup that finishes a group's last
- * chunk (bf16 with IKBO_FOLD=1), 0 when the merge kernel runs (the default) or
- * nothing is split.  Writes the first min(n_info, 10)
- * values.
+ * each item's key tiles last to first).  Writes the first min(n_info, 9) values.
  */
 int ikbo_plan_info(void* plan, int64_t* info, int32_t n_info);
 

@@ -36,7 +36,7 @@ def _oracle_target(w):
 @pytest.fixture(autouse=True)
 def _clean_env():
     saved = {k: os.environ.get(k) for k in ("IKBO_GRID_WGS", "IKBO_MIN_CHUNK", "IKBO_NO_SPLIT", "IKBO_SPLIT_SLOTS",
-                                            "IKBO_KERNEL", "IKBO_FOLD")}
+                                            "IKBO_KERNEL")}
     yield
     for k, v in saved.items():
         if v is None:
@@ -518,33 +518,6 @@ def test_plan_timing_records_each_launch():
         ikbo_plan_destroy(plan)
     assert len(attn) == 5 and len(merge) == 5
     assert all(a > 0 for a in attn) and all(m >= 0 for m in merge)
-
-
-@pytest.mark.parametrize("name", ["c2_typical", "c3_skewed", "c5_fused"])
-@pytest.mark.parametrize("waves", ["w8", "w4", "pipe"])
-def test_in_kernel_fold_matches_merge_kernel_bitwise(name, waves):
-    """Split groups merged by the workgroup finishing a group's last chunk give
-    the merge kernel's bits: same rule, same chunk order, and every partial read
-    is the one this launch wrote (a stale or half-written partial would show)."""
-    import torch
-    w = _wl(name)
-    dev = upload(w)
-    say(f"case fold vs merge kernel {name} waves={waves}")
-    os.environ["IKBO_KERNEL"] = waves
-    if name == "c5_fused":  # enough tiles to need no split: force chunks of 256 keys
-        os.environ["IKBO_SPLIT_SLOTS"] = "4096"
-    outs = {}
-    for fold in ("1", "0"):
-        os.environ["IKBO_FOLD"] = fold
-        oc = empty_out(w.raw("q_cand").shape, "bf16")
-        ou = empty_out(w.raw("q_user").shape, "bf16") if w.with_self else None
-        info = run_planned(w, dev, oc, ou)
-        assert info["n_groups"] > 0
-        assert info["fold"] == (1 if fold == "1" else 0)
-        outs[fold] = (oc, ou)
-    assert torch.equal(outs["1"][0].view(torch.int16), outs["0"][0].view(torch.int16))
-    if w.with_self:
-        assert torch.equal(outs["1"][1].view(torch.int16), outs["0"][1].view(torch.int16))
 
 
 def test_planned_call_rejects_tensors_that_do_not_fit_the_plan():
