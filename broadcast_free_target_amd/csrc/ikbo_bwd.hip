@@ -321,6 +321,30 @@ __global__ __launch_bounds__(kNT, 2) void ikbo_bwd_dq_kernel(BwdParams P) {
 // ---------------------------------------------------------------------------
 // merge of split dQ partials: block (group, 8 rows); thread -> (row, 4 d)
 // ---------------------------------------------------------------------------
+// dQ = scale * sum_c 2^(m_c - lse) dQ_c with lse = log2 sum_c 2^(m_c) over the
+// group's N chunks, in chunk order.  Straight-line over exactly N chunks: with
+// the loads guarded chunk by chunk the compiler waits between them.
+template <int N>
+__device__ __forceinline__ f32x4_t merge_dq(const f32x4_t (&rec)[kMaxSplit], const float* ws_dq, int64_t slot0,
+                                            int r, int d0, float* lse_out) {
+  f32x4_t o[N];
+#pragma unroll
+  for (int ch = 0; ch < N; ++ch)
+    o[ch] = *reinterpret_cast<const f32x4_t*>(ws_dq + ((slot0 + ch) * kBwdRowsA + r) * D + d0);
+  float mx = rec[0][0];
+#pragma unroll
+  for (int ch = 1; ch < N; ++ch) mx = fmaxf(mx, rec[ch][0]);
+  float sum = 0.0f;
+#pragma unroll
+  for (int ch = 0; ch < N; ++ch) sum += exp2f(rec[ch][0] - mx);
+  const float lse = mx + log2f(sum);
+  f32x4_t acc = f32x4_t{0, 0, 0, 0};
+#pragma unroll
+  for (int ch = 0; ch < N; ++ch) acc += o[ch] * exp2f(rec[ch][0] - lse);
+  *lse_out = lse;
+  return acc;
+}
+
 __global__ __launch_bounds__(256) void ikbo_bwd_merge_kernel(BwdParams P) {
   constexpr int TPR = D / 4;      // threads per row
   constexpr int RPB = 256 / TPR;  // rows per block
@@ -341,23 +365,18 @@ __global__ __launch_bounds__(256) void ikbo_bwd_merge_kernel(BwdParams P) {
   if (unit < 0) return;
   const int nchunk = tag >> 27;
   const int64_t srow = tag & ((1 << 27) - 1);
-  f32x4_t o[kMaxSplit];
-#pragma unroll
-  for (int ch = 0; ch < kMaxSplit; ++ch)
-    if (ch < nchunk) o[ch] = *reinterpret_cast<const f32x4_t*>(P.ws_dq + ((slot0 + ch) * kBwdRowsA + r) * D + d0);
-  float mx = rec[0][0];
-#pragma unroll
-  for (int ch = 1; ch < kMaxSplit; ++ch)
-    if (ch < nchunk) mx = fmaxf(mx, rec[ch][0]);
-  float sum = 0.0f;
-#pragma unroll
-  for (int ch = 0; ch < kMaxSplit; ++ch)
-    if (ch < nchunk) sum += exp2f(rec[ch][0] - mx);
-  const float lse = mx + log2f(sum);
-  f32x4_t acc = f32x4_t{0, 0, 0, 0};
-#pragma unroll
-  for (int ch = 0; ch < kMaxSplit; ++ch)
-    if (ch < nchunk) acc += o[ch] * exp2f(rec[ch][0] - lse);
+  float lse = 0.0f;
+  f32x4_t acc;
+  switch (nchunk) {
+    case 1: acc = merge_dq<1>(rec, P.ws_dq, slot0, r, d0, &lse); break;
+    case 2: acc = merge_dq<2>(rec, P.ws_dq, slot0, r, d0, &lse); break;
+    case 3: acc = merge_dq<3>(rec, P.ws_dq, slot0, r, d0, &lse); break;
+    case 4: acc = merge_dq<4>(rec, P.ws_dq, slot0, r, d0, &lse); break;
+    case 5: acc = merge_dq<5>(rec, P.ws_dq, slot0, r, d0, &lse); break;
+    case 6: acc = merge_dq<6>(rec, P.ws_dq, slot0, r, d0, &lse); break;
+    case 7: acc = merge_dq<7>(rec, P.ws_dq, slot0, r, d0, &lse); break;
+    default: acc = merge_dq<8>(rec, P.ws_dq, slot0, r, d0, &lse); break;
+  }
   acc *= P.scale;
   *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(P.dq) + static_cast<int64_t>(unit) * D + d0) =
       pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
