@@ -139,6 +139,39 @@ def test_bwd_repeatable_and_handle_reuse():
         _close(g, r, name)
 
 
+def test_bwd_work_list_ring_unsynchronised_calls():
+    """36 calls on one handle, two requests alternating, no synchronisation in
+    between (more calls than the handle's pinned work-list buffers, across
+    several periodic events): every call's gradients equal its request's first
+    ones bit for bit."""
+    import torch
+    import broadcast_free_target_amd as ikbo
+    ws = (_custom(3510, (90, 17, 300), (7, 1, 5), n_q=1, H=2), _custom(3511, (40, 260), (12, 30), n_q=2, H=2))
+    say("case bwd work-list ring, 36 unsynchronised calls")
+    ins = []
+    for w in ws:
+        t = {n: dev_tensor(w.raw(n), "bf16") for n in ("q_cand", "k_user", "v_user", "dout")}
+        t["out"] = dev_tensor(_forward_out_bits(w), "bf16")
+        ins.append(t)
+    h = ikbo.ikbo_bwd_create()
+    grads = []
+    try:
+        for i in range(36):
+            w, t = ws[i % 2], ins[i % 2]
+            g = [torch.full_like(t[n], float("nan")) for n in ("q_cand", "k_user", "v_user")]
+            ikbo.ikbo_attn_bwd(h, w.user_offsets, w.cand_to_user, w.n_users, w.n_cand, w.n_q, w.H, w.d, w.scale,
+                               t["q_cand"], t["k_user"], t["v_user"], t["out"], t["dout"], *g)
+            grads.append(g)
+        torch.cuda.synchronize()
+    finally:
+        ikbo.ikbo_bwd_destroy(h)
+    for i, g in enumerate(grads):
+        for x, y in zip(g, grads[i % 2]):
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16)), f"call {i}"
+    for g, r, name in zip(grads[1], _oracle(ws[1]), ("dq", "dk", "dv")):
+        _close(to_f64(g), r, name)
+
+
 def test_bwd_errors():
     import torch
     import broadcast_free_target_amd as ikbo

@@ -236,6 +236,34 @@ def test_mx_handle_reuse_alternating_requests():
     _close(b, _oracle(w2), "second request", _slack(w2))
 
 
+def test_mx_work_list_ring_unsynchronised_calls():
+    """40 calls on one handle, two requests alternating, no synchronisation in
+    between: more calls than the handle has pinned work-list buffers, across
+    several of its periodic events.  Every call's output equals its request's
+    first one, so no buffer was rewritten while a queued kernel still read it."""
+    import torch
+    import broadcast_free_target_amd as ikbo
+    w1 = make_mxfp8_custom(4610, (90, 17, 300), [0, 1, 2, 2, 0, 1, 2], n_q=1, H=2)
+    w2 = make_mxfp8_custom(4611, (40, 260, 5), [1, 0, 1, 1, 2], n_q=2, H=2)
+    say("case mx work-list ring, 40 unsynchronised calls")
+    h = ikbo.ikbo_mx_create()
+    try:
+        d = (_dev(w1), _dev(w2))
+        outs = []
+        for i in range(40):
+            w = (w1, w2)[i % 2]
+            o = torch.full((w.n_cand, w.n_q, w.H, w.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+            ikbo.ikbo_attn_fwd_mxfp8(h, w.user_offsets, w.cand_to_user, w.n_users, w.n_cand, w.n_q, w.H, w.d,
+                                     w.scale, *d[i % 2], o)
+            outs.append(o)
+        torch.cuda.synchronize()
+    finally:
+        ikbo.ikbo_mx_destroy(h)
+    for i, o in enumerate(outs):
+        assert torch.equal(o.view(torch.int16), outs[i % 2].view(torch.int16)), f"call {i}"
+    _close(outs[1].float().cpu().numpy().astype(np.float64), _oracle(w2), "ring", _slack(w2))
+
+
 def test_mx_errors():
     import torch
     import broadcast_free_target_amd as ikbo

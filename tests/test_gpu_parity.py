@@ -520,6 +520,38 @@ def test_plan_timing_records_each_launch():
     assert all(a > 0 for a in attn) and all(m >= 0 for m in merge)
 
 
+def test_plan_work_list_ring_unsynchronised_rebuilds():
+    """One plan rebuilt for two requests in turn, 40 build + launch pairs with no
+    synchronisation: more builds than the plan has pinned work-list buffers,
+    across several of its periodic events.  Every launch's output equals its
+    request's first one (and the oracle), so no work list was overwritten while
+    a queued kernel still read it."""
+    from broadcast_free_target_amd import (ikbo_attn_fwd_planned, ikbo_plan_build, ikbo_plan_create,
+                                           ikbo_plan_destroy)
+    import torch
+    wa = _custom(13, (300, 17, 90, 1), (5, 2, 9, 1), 1, 2, 128, "bf16")
+    wb = _custom(14, (40, 700), (12, 3), 1, 3, 128, "bf16")
+    da, db = upload(wa), upload(wb)
+    say("case plan work-list ring, 40 unsynchronised rebuilds")
+    plan = ikbo_plan_create()
+    outs = []
+    try:
+        for i in range(40):
+            w, dv = (wa, da) if i % 2 == 0 else (wb, db)
+            ikbo_plan_build(plan, w.user_offsets, w.cand_to_user, w.n_users, w.n_cand, w.n_q, w.H, w.d,
+                            dtype_code("bf16"), 0)
+            o = empty_out(w.raw("q_cand").shape, "bf16")
+            ikbo_attn_fwd_planned(plan, dv["q_cand"], None, dv["k_user"], dv["v_user"], w.scale, o)
+            outs.append(o)
+        torch.cuda.synchronize()
+    finally:
+        ikbo_plan_destroy(plan)
+    for i, o in enumerate(outs):
+        assert torch.equal(o.view(torch.int16), outs[i % 2].view(torch.int16)), f"launch {i}"
+    assert_close(to_f64(outs[0]), _oracle_target(wa), "bf16", "ring a")
+    assert_close(to_f64(outs[1]), _oracle_target(wb), "bf16", "ring b")
+
+
 def test_planned_call_rejects_tensors_that_do_not_fit_the_plan():
     """A plan built for fp32 refuses bf16 tensors, and a bf16 plan refuses a key
     tensor shorter than its users' rows; nothing is launched in either case."""
