@@ -206,6 +206,7 @@ int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n
     p->k_perm = reinterpret_cast<const int32_t*>(db + a1);
   } else {
     if ((rc = p->d_items.ensure(a2 + 256, false)) != IKBO_OK) return rc;
+    if ((rc = p->ring.on_stream(stream)) != IKBO_OK) return rc;
     IKBO_HIP(hipMemcpyAsync(p->d_items.ptr, hb, a2, hipMemcpyHostToDevice, stream));
     if ((rc = p->ring.launched(s, stream)) != IKBO_OK) return rc;  // the copy reads the buffer
     char* db = static_cast<char*>(p->d_items.ptr);
@@ -282,6 +283,7 @@ int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* 
     if (rc != IKBO_OK) return rc;
     ap.trace = static_cast<uint64_t*>(p->d_trace.ptr);
   }
+  if (int rc = p->ring.on_stream(stream); rc != IKBO_OK) return rc;  // before anything is enqueued
   hipEvent_t* te = nullptr;  // attention start/end, merge start/end (stamped by the dispatches)
   if (p->timing && p->n_timed < kMaxTimed) {
     while (p->tev.size() < static_cast<size_t>(4 * (p->n_timed + 1))) {

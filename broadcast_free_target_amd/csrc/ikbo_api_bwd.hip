@@ -214,6 +214,7 @@ int ikbo_attn_bwd(void* bwd, const int32_t* user_offsets, const int32_t* cand_to
     p.items = reinterpret_cast<const WorkItem*>(base);
     // timing: the dQ span runs from the dQ kernel's start to the merge's end
     hipEvent_t ev_dq[2] = {te ? te[0] : nullptr, te && b->n_groups == 0 ? te[1] : nullptr};
+    if ((rc = b->ring.on_stream(stream)) != IKBO_OK) return rc;  // before anything is enqueued
     hipError_t e = ikbo::launch_bwd_dq(p, static_cast<int>(na), stream, te ? ev_dq : nullptr);
     if (e != hipSuccess) return fail_hip(e, "dQ launch");
     e = ikbo::launch_bwd_merge(p, static_cast<int>(b->n_groups), stream, te ? te[1] : nullptr);

@@ -119,7 +119,11 @@ struct PinnedBuf {
 // fired: with kStages > kEventEvery buffers a call waits only when the host
 // is more than kStages - kEventEvery launches ahead of the device.  If that
 // event has not been recorded yet, one is recorded on the last launch's
-// stream and waited for.  One host thread per ring; launches on one stream.
+// stream and waited for.  The events only order launches on their own stream,
+// so before anything is enqueued on a different stream than the previous
+// launch's, on_stream waits for the previous stream to drain (every buffer,
+// and whatever else the owner's launches share, is then free).  One host
+// thread per ring.
 struct PinnedRing {
   static constexpr int kStages = 16;
   static constexpr int kEventEvery = 8;
@@ -131,6 +135,7 @@ struct PinnedRing {
   hipEvent_t flush = nullptr;
   int64_t n_launch = 0;
   hipStream_t last_stream = nullptr;
+  bool launched_any = false;
   int next = 0;
 
   int init() {
@@ -171,8 +176,20 @@ struct PinnedRing {
     *idx = s;
     return IKBO_OK;
   }
+  // To be called before enqueuing work on `stream`: if the previous launch
+  // went to another stream, waits for that stream to drain.
+  int on_stream(hipStream_t stream) {
+    if (launched_any && stream != last_stream) {
+      IKBO_HIP(hipStreamSynchronize(last_stream));
+      for (int i = 0; i < kStages; ++i) last[i] = -1;
+      for (int i = 0; i < kEvents; ++i) ev_seq[i] = -1;
+      last_stream = stream;
+    }
+    return IKBO_OK;
+  }
   // Notes that the launch just enqueued on `stream` reads buffer idx.
   int launched(int idx, hipStream_t stream) {
+    launched_any = true;
     const int64_t seq = n_launch++;
     last[idx] = seq;
     last_stream = stream;

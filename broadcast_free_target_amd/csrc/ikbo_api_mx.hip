@@ -190,6 +190,7 @@ int ikbo_attn_fwd_mxfp8(void* mx, const int32_t* user_offsets, const int32_t* ca
     p.out = out;
     p.ws_o = static_cast<float*>(m->ws_o.ptr);
     p.ws_rec = static_cast<float*>(m->ws_rec.ptr);
+    if ((rc = m->ring.on_stream(stream)) != IKBO_OK) return rc;  // before anything is enqueued
     hipError_t e = ikbo::launch_mx(p, m->hp.grid, stream, te);
     if (e != hipSuccess) return fail_hip(e, "MXFP8 kernel launch");
     if (m->hp.n_groups > 0) {

@@ -157,10 +157,12 @@ int ikbo_attn_fwd_materialized(const void* q_cand, const void* k_user, const voi
  *   with_self = 1 adds causal self-attention rows (then n_q must be 1).
  * ikbo_attn_fwd_planned: launches the attention for the plan's last build.
  *   q_user/out_user are used only when the plan was built with with_self.
- *   Launches of one plan must be ordered on one stream: they share the plan's
- *   split-KV workspace.  Split groups are merged by a second kernel with the
- *   log-sum-exp rule of the TLX attention post's split-K section, in chunk
- *   order, so results do not depend on the schedule or the launch grid.
+ *   Launches of one plan share its split-KV workspace and work-list buffers:
+ *   keep them on one stream; a launch on another stream than the plan's
+ *   previous one first waits, on the host, for that stream to drain.  Split
+ *   groups are merged by a second kernel with the log-sum-exp rule of the TLX
+ *   attention post's split-K section, in chunk order, so results do not
+ *   depend on the schedule or the launch grid.
  * ikbo_plan_destroy: frees the plan after synchronising its device.
  */
 int ikbo_plan_create(void** plan);
@@ -282,7 +284,8 @@ void ikbo_lce_destroy(void* lce);
  * atomics; results are deterministic).
  *
  * ikbo_bwd_create: a handle owning the work lists (pinned host memory, 16
- *   buffers used in turn, as for plans) and device workspaces: 4 * (1 + 2H) * (n_cand*n_q +
+ *   buffers used in turn, as for plans; a call on another stream than the
+ *   handle's previous one first waits for that stream) and device workspaces: 4 * (1 + 2H) * (n_cand*n_q +
  *   128) bytes of per-row statistics, and 64 KB + 2 KB per split slot of dQ
  *   partials (long key ranges are split as in the forward and merged in chunk
  *   order, so results stay deterministic).
@@ -333,8 +336,9 @@ void ikbo_bwd_destroy(void* bwd);
  * accumulation; long key ranges are split and merged as in the bf16 path.
  *
  * ikbo_mx_create: a handle owning the work lists (pinned host memory, 16
- *   buffers used in turn, as for plans) and the split partials (64 KB + 2 KB
- *   per slot).
+ *   buffers used in turn, as for plans; a call on another stream than the
+ *   handle's previous one first waits for that stream) and the split partials
+ *   (64 KB + 2 KB per slot).
  * ikbo_attn_fwd_mxfp8: user_offsets [n_users + 1] and cand_to_user [n_cand]
  *   are HOST int32 arrays; the tensors are device arrays, row-major uint8:
  *     q_codes [n_cand, n_q, H, d]   q_scales [n_cand, n_q, H, d/32]

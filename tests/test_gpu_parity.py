@@ -552,6 +552,39 @@ def test_plan_work_list_ring_unsynchronised_rebuilds():
     assert_close(to_f64(outs[1]), _oracle_target(wb), "bf16", "ring b")
 
 
+def test_plan_launches_alternating_between_streams():
+    """A plan launched on two streams in turn (rebuilt between launches, no
+    synchronisation by the caller): the library drains the previous stream
+    before enqueuing on the other, so each launch's output is its own
+    request's."""
+    from broadcast_free_target_amd import (ikbo_attn_fwd_planned, ikbo_plan_build, ikbo_plan_create,
+                                           ikbo_plan_destroy)
+    import torch
+    wa = _custom(15, (300, 17, 90), (5, 2, 9), 1, 2, 128, "bf16")
+    wb = _custom(16, (40, 700), (12, 3), 1, 2, 128, "bf16")
+    da, db = upload(wa), upload(wb)
+    streams = (torch.cuda.Stream(), torch.cuda.Stream())
+    say("case plan launches alternating between two streams")
+    plan = ikbo_plan_create()
+    outs = []
+    try:
+        for i in range(12):
+            w, dv, st = (wa, da, streams[0]) if i % 2 == 0 else (wb, db, streams[1])
+            ikbo_plan_build(plan, w.user_offsets, w.cand_to_user, w.n_users, w.n_cand, w.n_q, w.H, w.d,
+                            dtype_code("bf16"), 0, st)
+            o = empty_out(w.raw("q_cand").shape, "bf16")
+            torch.cuda.synchronize()  # the output buffer is ready before either stream uses it
+            ikbo_attn_fwd_planned(plan, dv["q_cand"], None, dv["k_user"], dv["v_user"], w.scale, o, None, st)
+            outs.append(o)
+        torch.cuda.synchronize()
+    finally:
+        ikbo_plan_destroy(plan)
+    for i, o in enumerate(outs):
+        assert torch.equal(o.view(torch.int16), outs[i % 2].view(torch.int16)), f"launch {i}"
+    assert_close(to_f64(outs[0]), _oracle_target(wa), "bf16", "stream a")
+    assert_close(to_f64(outs[1]), _oracle_target(wb), "bf16", "stream b")
+
+
 def test_planned_call_rejects_tensors_that_do_not_fit_the_plan():
     """A plan built for fp32 refuses bf16 tensors, and a bf16 plan refuses a key
     tensor shorter than its users' rows; nothing is launched in either case."""
