@@ -57,9 +57,7 @@ __all__ = [
     "chunk_partial",
     "merge_partials",
     "flops_target",
-    "flops_self_causal",
     "bytes_ikbo",
-    "bytes_materialized",
     "ai_standard",
     "ai_ikbo",
     "ai_gemm",
@@ -297,10 +295,6 @@ def flops_target(counts, lengths, n_q: int, H: int, d: int) -> float:
     return 4.0 * n_q * d * H * float(np.dot(np.asarray(counts, np.float64), np.asarray(lengths, np.float64)))
 
 
-def flops_self_causal(lengths, H: int, d: int) -> float:
-    """Causal self-attention FLOPs: 4 * d * L(L+1)/2 per (user, head)."""
-    L = np.asarray(lengths, np.float64)
-    return 4.0 * d * H * float(np.sum(L * (L + 1.0) / 2.0))
 
 
 def bytes_ikbo(n_cand: int, n_q: int, total_len: int, H: int, d: int, elem: int,
@@ -312,10 +306,6 @@ def bytes_ikbo(n_cand: int, n_q: int, total_len: int, H: int, d: int, elem: int,
     return b
 
 
-def bytes_materialized(n_cand: int, n_q: int, total_len: int, bcast_len: int, H: int, d: int,
-                       elem: int) -> float:
-    """IKBO bytes plus the broadcast K/V (sum over candidates of L_u) written once and read once."""
-    return bytes_ikbo(n_cand, n_q, total_len, H, d, elem) + 2.0 * 2.0 * elem * H * d * bcast_len
 
 
 def ai_standard(n_q: int, L: int) -> float:

@@ -31,8 +31,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["lce_baseline", "lce_baseline_nested", "lce_flops_baseline", "lce_flops_ikbo", "lce_flops_nested",
-           "lce_bytes_ikbo", "lce_bytes_baseline"]
+__all__ = ["lce_baseline", "lce_baseline_nested", "lce_flops_baseline", "lce_flops_ikbo", "lce_bytes_baseline"]
 
 
 def _f64(x) -> np.ndarray:
@@ -72,9 +71,6 @@ def lce_flops_ikbo(B: int, U: int, M: int, K_u: int, K_c: int, N: int) -> float:
     return 2.0 * M * N * (U * K_u + B * K_c)
 
 
-def lce_bytes_ikbo(B: int, U: int, M: int, K_u: int, K_c: int, N: int, elem: int = 2) -> float:
-    """W once, inputs once, output once; the user result [U, M, N] is written and read once in fp32."""
-    return float(elem * (M * (K_u + K_c) + U * K_u * N + B * K_c * N + B * M * N) + 2 * 4 * U * M * N)
 
 
 def lce_bytes_baseline(B: int, M: int, K: int, N: int, elem: int = 2) -> float:
@@ -113,7 +109,3 @@ def lce_baseline_nested(w, x_user, x_vendor, x_cand, vendor_to_user, cand_to_ven
         out[b] = w @ xb
     return out
 
-
-def lce_flops_nested(B: int, V: int, U: int, M: int, K_u: int, K_v: int, K_c: int, N: int) -> float:
-    """Executed FLOPs of the nested decomposition: each level's product at its own batch."""
-    return 2.0 * M * N * (U * K_u + V * K_v + B * K_c)
