@@ -53,6 +53,7 @@ struct Plan {
   // (IKBO_PLAN_UPLOAD=copy) a copy to the device buffers above reads them.
   bool read_in_place = true;
   PinnedRing ring;
+  std::mutex mu;  // held by the entry points that use a library-owned plan, for the whole call
   int cur_stage = 0;
   const WorkItem* k_items = nullptr;            // what the kernels read
   const int32_t* k_perm = nullptr;
@@ -374,6 +375,7 @@ int attn_device_mapping(const void* q_cand, const void* q_user, const void* k, c
   if (n_cand == 0 && !with_self) return IKBO_OK;
   Plan* p = nullptr;
   if ((rc = cached_plan(stream, 0, &p)) != IKBO_OK) return rc;
+  std::lock_guard<std::mutex> plan_lock(p->mu);
   const int32_t *ho = nullptr, *hc = nullptr;
   if ((rc = fetch_mapping(p, offs, c2u, n_users, n_cand, stream, &ho, &hc)) != IKBO_OK) return rc;
   if ((rc = build_and_upload(p, ho, hc, n_users, n_cand, n_q, H, d, dtype, with_self, stream)) != IKBO_OK) return rc;
@@ -583,6 +585,7 @@ int ikbo_attn_fwd_materialized(const void* q_cand, const void* k_user, const voi
     if (!q_cand || !out || !k_user || !v_user) return fail(IKBO_ERR_INVALID_ARG, "null tensor pointer");
     Plan* p = nullptr;
     if ((rc = cached_plan(stream, 1, &p)) != IKBO_OK) return rc;
+    std::lock_guard<std::mutex> plan_lock(p->mu);
     const int32_t *ho = nullptr, *hc = nullptr;
     if ((rc = fetch_mapping(p, user_offsets, cand_to_user, n_users, n_cand, stream, &ho, &hc)) != IKBO_OK) return rc;
     std::string err;

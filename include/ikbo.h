@@ -35,6 +35,10 @@
  *     where a call says it synchronises.
  *   - The caller owns every tensor and must keep it alive until the stream
  *     work completes.  The library owns only its plans and workspaces.
+ *   - A plan or handle (plan, LCE, backward, MXFP8) is used by one host thread
+ *     at a time; different plans and handles may be used concurrently.  The
+ *     entry points without a plan keep one internal plan per (device, stream)
+ *     and serialise on it.
  *   - A negative return is an error; nothing has been launched and no output
  *     has been written.  ikbo_last_error() gives a message (thread-local).
  *     No C++ exception crosses this boundary.

@@ -585,6 +585,43 @@ def test_plan_launches_alternating_between_streams():
     assert_close(to_f64(outs[1]), _oracle_target(wb), "bf16", "stream b")
 
 
+def test_entry_point_without_plan_from_two_threads():
+    """ikbo_attn_fwd keeps one internal plan per (device, stream); two host
+    threads calling it on the same stream with different requests (the binding
+    releases the interpreter lock during the call) each get their own
+    request's output."""
+    import threading
+    import torch
+    from broadcast_free_target_amd import ikbo_attn_fwd
+    ws = (_custom(17, (300, 17, 90), (5, 2, 9), 1, 2, 128, "bf16"), _custom(18, (40, 700), (12, 3), 1, 3, 128, "bf16"))
+    devs = [upload(w) for w in ws]
+    say("case entry point without a plan from two threads")
+    outs = [[empty_out(w.raw("q_cand").shape, "bf16") for _ in range(10)] for w in ws]
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(j):
+        try:
+            w, dv = ws[j], devs[j]
+            for o in outs[j]:
+                ikbo_attn_fwd(dv["q_cand"], dv["k_user"], dv["v_user"], dv["user_offsets"], dv["cand_to_user"],
+                              w.n_users, w.n_cand, w.H, w.d, w.scale, o)
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(j,)) for j in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for j, w in enumerate(ws):
+        for o in outs[j]:
+            assert torch.equal(o.view(torch.int16), outs[j][0].view(torch.int16))
+        assert_close(to_f64(outs[j][0]), _oracle_target(w), "bf16", f"thread {j}")
+
+
 def test_planned_call_rejects_tensors_that_do_not_fit_the_plan():
     """A plan built for fp32 refuses bf16 tensors, and a bf16 plan refuses a key
     tensor shorter than its users' rows; nothing is launched in either case."""
