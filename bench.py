@@ -739,7 +739,7 @@ def main():
                     help="loop only the materialised-broadcast comparator (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU only: this benchmark has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -883,7 +883,7 @@ def main():
         extra["cold_kernel_us_median"] = c_ms * 1e3
         extra["cold_kernel_tflops"] = flops / (c_ms * 1e-3) / 1e12
         extra["cold_kernel_hbm_gbs"] = byts / (c_ms * 1e-3) / 1e9
-        # end-to-end spec call (device mapping: D2H copy + sync + host plan + launch)
+        # end-to-end device-mapping entry point (D2H copy + sync + host plan + launch)
         if not w.with_self:
             for _ in range(5):
                 ikbo.ikbo_attn_fwd_ex(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"],

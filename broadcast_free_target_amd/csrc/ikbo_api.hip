@@ -165,7 +165,7 @@ int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n
   IKBO_HIP(hipGetDevice(&dev));
   if (dev != p->device) return fail(IKBO_ERR_INVALID_ARG, "plan belongs to another device");
   std::string err;
-  // Build into the plan's own storage (reused across builds); until this build
+  // Build into the plan's own storage (reused across builds); until this plan build
   // completes the plan cannot be launched.
   p->built = false;
   HostPlan& hp = p->hp;
@@ -314,7 +314,7 @@ int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* 
     if (e != hipSuccess) return fail_hip(e, "merge launch");
   }
   if (p->read_in_place) {
-    // The pinned work list of this build stays in use until these kernels end.
+    // The pinned work list of this plan build stays in use until these kernels end.
     int rc = p->ring.launched(p->cur_stage, stream);
     if (rc != IKBO_OK) return rc;
   }

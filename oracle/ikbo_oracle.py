@@ -21,7 +21,7 @@ What it computes, and where the pages say so:
 * Softmax is the two-pass definition: subtract the row maximum, exponentiate,
   normalise.  (The GPU uses the online recurrence of the AI-infra guide,
   section 4.6.1, which equals this in exact arithmetic.)
-* CSR grouping of candidates by user is this build's own contract (the pages
+* CSR grouping of candidates by user is this library's own contract (the pages
   hand the kernel a mapping tensor, section 1.3 and Alg. 1, and pair
   neighbouring candidates of one user): counts, exclusive prefix sum,
   a *stable* sort of candidate indices by user, and row tiles of at most

@@ -68,7 +68,7 @@ def test_c1_tiny_f32():
 
 
 @pytest.mark.parametrize("waves", ["pipe", "w8", "w4", "w4r"])
-def test_c2_typical_planned_and_north_star_call(waves):
+def test_c2_typical_planned_and_device_mapping_call(waves):
     from broadcast_free_target_amd import ikbo_attn_fwd
     import torch
     os.environ["IKBO_KERNEL"] = waves
