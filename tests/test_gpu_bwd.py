@@ -235,3 +235,34 @@ def test_bwd_split_and_unsplit(no_split, monkeypatch):
         assert np.array_equal(x, y)
     for g, r, name in zip(a, _oracle(w), ("dq", "dk", "dv")):
         _close(g, r, name)
+
+
+def test_binding_rejects_bwd_tensors_that_do_not_fit():
+    """A dK tensor one key row short and an fp32 dQ are refused by the binding
+    (sizes from the host offsets) before anything is launched."""
+    import torch
+    import broadcast_free_target_amd as ikbo
+    from broadcast_free_target_amd import IKBO_ERR_INVALID_ARG, IkboError
+    w = _custom(3520, (40, 90), (3, 5))
+    say("case bwd tensors that do not fit")
+    t = {n: dev_tensor(w.raw(n), "bf16") for n in ("q_cand", "k_user", "v_user", "dout")}
+    out = dev_tensor(_forward_out_bits(w), "bf16")
+    dq = torch.full_like(t["q_cand"], 7.0)
+    dk = torch.full_like(t["k_user"], 7.0)
+    dv = torch.full_like(t["v_user"], 7.0)
+    h = ikbo.ikbo_bwd_create()
+    try:
+        args = [w.user_offsets, w.cand_to_user, w.n_users, w.n_cand, w.n_q, w.H, w.d, w.scale,
+                t["q_cand"], t["k_user"], t["v_user"], out, t["dout"]]
+        with pytest.raises(IkboError) as e:
+            ikbo.ikbo_attn_bwd(h, *args, dq, dk[:-1], dv)
+        assert e.value.status == IKBO_ERR_INVALID_ARG and "dk_user" in str(e.value)
+        with pytest.raises(IkboError) as e:
+            ikbo.ikbo_attn_bwd(h, *args, dq.float(), dk, dv)
+        assert e.value.status == IKBO_ERR_INVALID_ARG and "element size" in str(e.value)
+        torch.cuda.synchronize()
+        for g in (dq, dk, dv):
+            assert torch.all(g.float() == 7.0)
+    finally:
+        ikbo.ikbo_bwd_destroy(h)
+

@@ -259,3 +259,29 @@ def test_lce3_handle_kinds():
     finally:
         ikbo_lce_destroy(h3)
         ikbo_lce_destroy(h2)
+
+
+def test_binding_rejects_lce_tensors_that_do_not_fit():
+    """The binding compares each tensor with what the call touches (from the
+    handle's M, K_u, K_c and the call's sizes): a candidate input one batch
+    element short and an fp32 output are refused before anything is launched."""
+    import torch
+    from broadcast_free_target_amd import IKBO_ERR_INVALID_ARG, IkboError, ikbo_lce_create, ikbo_lce_destroy, ikbo_lce_fwd
+    w = make_lce("lce_tiny")
+    say("case lce tensors that do not fit")
+    h = ikbo_lce_create(_dev(w.raw("w")), w.M, w.K_u, w.K_c)
+    try:
+        xu, xc = _dev(w.raw("x_user")), _dev(w.raw("x_cand"))
+        m = torch.from_numpy(w.cand_to_user.copy()).cuda()
+        out = torch.full((w.n_cand, w.M, w.N), 7.0, dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(IkboError) as e:
+            ikbo_lce_fwd(h, xu, xc[:-1], m, w.n_users, w.n_cand, w.N, out)
+        assert e.value.status == IKBO_ERR_INVALID_ARG and "x_cand" in str(e.value)
+        with pytest.raises(IkboError) as e:
+            ikbo_lce_fwd(h, xu, xc, m, w.n_users, w.n_cand, w.N, out.float())
+        assert e.value.status == IKBO_ERR_INVALID_ARG and "element size" in str(e.value)
+        torch.cuda.synchronize()
+        assert torch.all(out.float() == 7.0)
+    finally:
+        ikbo_lce_destroy(h)
+

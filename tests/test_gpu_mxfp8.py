@@ -295,3 +295,29 @@ def test_mx_errors():
         assert torch.count_nonzero(out).item() == 0
     finally:
         ikbo.ikbo_mx_destroy(h)
+
+
+def test_binding_rejects_mx_tensors_that_do_not_fit():
+    """V scales one block short (the count follows from the users' lengths) and
+    a float32 output are refused by the binding before anything is launched."""
+    import torch
+    import broadcast_free_target_amd as ikbo
+    from broadcast_free_target_amd import IKBO_ERR_INVALID_ARG, IkboError
+    w = make_mxfp8_custom(4620, (30, 20), [0, 1, 1], n_q=1, H=1)
+    dev = _dev(w)
+    out = torch.zeros((w.n_cand, 1, 1, 128), dtype=torch.bfloat16, device="cuda")
+    say("case mx tensors that do not fit")
+    h = ikbo.ikbo_mx_create()
+    try:
+        args = [w.user_offsets, w.cand_to_user, w.n_users, w.n_cand, 1, 1, 128, w.scale]
+        with pytest.raises(IkboError) as e:
+            ikbo.ikbo_attn_fwd_mxfp8(h, *args, *dev[:5], dev[5][:-1], out)
+        assert e.value.status == IKBO_ERR_INVALID_ARG and "v_scales" in str(e.value)
+        with pytest.raises(IkboError) as e:
+            ikbo.ikbo_attn_fwd_mxfp8(h, *args, *dev, out.float())
+        assert e.value.status == IKBO_ERR_INVALID_ARG and "element size" in str(e.value)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(out).item() == 0
+    finally:
+        ikbo.ikbo_mx_destroy(h)
+
