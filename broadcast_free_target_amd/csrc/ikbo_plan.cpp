@@ -175,6 +175,50 @@ int build_plan(const int32_t* user_offsets, const int32_t* cand_to_user, int32_t
   out->n_groups = 0;
   out->n_slots = 0;
   out->groups.clear();
+  const int64_t cap = p.launch_grid > 0 ? p.launch_grid : p.grid_slots;
+
+  // Chunks the rule below cuts a key range of len keys into.
+  auto n_chunks = [&](int64_t len) -> int64_t {
+    if (single_len > 0 && len > 0) {
+      const int64_t nc = chunks_of(len, single_len);
+      return ceil_div(len, ceil_div(ceil_div(len, nc), p.bn) * p.bn);
+    }
+    if (single_len == 0 && p.allow_split && len > target + target / 2) {
+      const int64_t nc = std::min<int64_t>(ceil_div(len, target), p.max_chunks);
+      return ceil_div(len, ceil_div(ceil_div(len, nc), p.bn) * p.bn);
+    }
+    return 1;
+  };
+  bool split_any = false;
+  for (int32_t u = 0; u < n_users && !split_any; ++u)
+    split_any = out->counts[u] > 0 && n_chunks(user_offsets[u + 1] - user_offsets[u]) > 1;
+  if (!with_self && !split_any) {
+    // Every item of a user then costs that user's key length, so longest first
+    // with ties in construction order is: users by decreasing length (ties by
+    // index), each user's items in construction order.  Same list as the
+    // general path below, without sorting the items.
+    std::vector<uint64_t>& ord = out->keys;
+    ord.resize(n_users);
+    for (int32_t u = 0; u < n_users; ++u)
+      ord[u] = (static_cast<uint64_t>(0xffffffffu - static_cast<uint32_t>(user_offsets[u + 1] - user_offsets[u])) << 32) |
+               static_cast<uint32_t>(u);
+    std::sort(ord.begin(), ord.end());
+    std::vector<WorkItem>& fast = out->items;
+    fast.clear();
+    for (int32_t k = 0; k < n_users; ++k) {
+      const int32_t u = static_cast<int32_t>(ord[k] & 0xffffffffu);
+      const int32_t L = user_offsets[u + 1] - user_offsets[u];
+      const int64_t rows = static_cast<int64_t>(out->counts[u]) * n_q;
+      for (int32_t h = 0; h < H; ++h)
+        for (int64_t r0 = 0; r0 < rows; r0 += p.bm)
+          fast.push_back(WorkItem{user_offsets[u], out->cand_offsets[u], static_cast<int32_t>(r0),
+                                  static_cast<int32_t>(std::min<int64_t>(p.bm, rows - r0)), 0, L, h, kKindTarget, -1,
+                                  0, 1, 0});
+    }
+    out->grid = static_cast<int32_t>(std::min<int64_t>(fast.size(), cap));
+    return kOk;
+  }
+
   std::vector<WorkItem>& items = out->unsorted;
   items.clear();
   items.reserve(static_cast<size_t>(n_base) * 2);
@@ -263,7 +307,6 @@ int build_plan(const int32_t* user_offsets, const int32_t* cand_to_user, int32_t
     out->items.resize(n);
     for (size_t i = 0; i < n; ++i) out->items[i] = items[keys[i] & 0xffffffffull];
   }
-  const int64_t cap = p.launch_grid > 0 ? p.launch_grid : p.grid_slots;
   out->grid = static_cast<int32_t>(std::min<int64_t>(out->items.size(), cap));
   return kOk;
 }

@@ -179,9 +179,15 @@ def _check_plan(plan, offs, c2u, n_q, H, with_self, bm, bn, grid_slots):
     for g, v in groups.items():
         s0, nc = next(iter(v))
         assert s0 == 8 * g and 2 <= nc <= 8
-    # longest first
+    # longest first; equal costs keep construction order (user, then target
+    # before self, head, row tile, chunk), so one user's tiles stay adjacent
     cost = items[:, 5] - items[:, 4]
     assert np.all(np.diff(cost) <= 0)
+    key = [(int(it[0]), int(it[7]), int(it[1]) if it[7] == 0 else 0, int(it[6]), int(it[2]), int(it[4]))
+           for it in items]
+    for i in range(len(items) - 1):
+        if cost[i] == cost[i + 1]:
+            assert key[i] < key[i + 1], (i, key[i], key[i + 1])
     # the boustrophedon deal gives every item to exactly one workgroup
     G = plan["grid"]
     hits = np.zeros(len(items), int)
