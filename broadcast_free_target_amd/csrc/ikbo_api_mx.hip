@@ -94,15 +94,24 @@ int ikbo_attn_fwd_mxfp8(void* mx, const int32_t* user_offsets, const int32_t* ca
     std::string err;
     int rc = ikbo::check_offsets(user_offsets, n_users, &err);
     if (rc != ikbo::kOk) return fail(rc, err);
+    // Small requests: one workgroup per CU, each with a longer key range (fewer
+    // split partials to merge), when every item then fits one pass; otherwise
+    // two resident workgroups per CU.  IKBO_SPLIT_SLOTS fixes the slot count.
     PlanParams pp;
     pp.bm = ikbo::kMxRows;
     pp.bn = ikbo::kMxKeys;
-    pp.grid_slots = std::max(1, env_int("IKBO_SPLIT_SLOTS", 2 * m->n_cu));
+    const int forced_slots = env_int("IKBO_SPLIT_SLOTS", 0);
+    pp.grid_slots = forced_slots > 0 ? forced_slots : std::max(1, m->n_cu);
     pp.min_chunk = std::max(pp.bn, env_int("IKBO_MIN_CHUNK", 256) / pp.bn * pp.bn);
     pp.launch_grid = std::max(0, env_int("IKBO_GRID_WGS", 0));
     pp.allow_split = !env_int("IKBO_NO_SPLIT", 0);
     rc = ikbo::build_plan(user_offsets, cand_to_user, n_users, n_cand, n_q, H, false, pp, &m->hp, &err);
     if (rc != ikbo::kOk) return fail(rc, err);
+    if (forced_slots <= 0 && m->hp.items.size() > static_cast<size_t>(pp.grid_slots)) {
+      pp.grid_slots = std::max(1, 2 * m->n_cu);
+      rc = ikbo::build_plan(user_offsets, cand_to_user, n_users, n_cand, n_q, H, false, pp, &m->hp, &err);
+      if (rc != ikbo::kOk) return fail(rc, err);
+    }
     if (n_cand == 0) return IKBO_OK;
     const int64_t T = user_offsets[n_users];
     const int64_t R = static_cast<int64_t>(n_cand) * n_q;
