@@ -8,8 +8,9 @@ mapping (as an inference runtime holds it) into pinned memory that the
 kernels read in place, the persistent attention kernel and, when key ranges
 were split, the merge kernel.  Inputs are resident in HBM before timing.
 Rank 0 prints one JSON line (the contract fields plus ``roofline`` and
-``cpu_baseline``); with ``--report`` extra measurements (cold-cache kernel
-times, the materialised-broadcast comparator) are added under ``extra``.
+``cpu_baseline``).  Under ``extra`` it also carries cold-cache kernel times,
+the host time of a plan build and of a launch, the end-to-end time of the
+device-mapping entry point and the materialised-broadcast comparator's time.
 """
 
 from __future__ import annotations
@@ -32,8 +33,9 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
 # Attention kernel a plan runs (ikbo_plan_info "kernel"), by head dim.
 KERNEL_NAMES = {0: "ikbo_attn_f32_kernel<{d}>", 1: "ikbo_attn_bf16_w8_kernel<{d}, 2>",
-                2: "ikbo_attn_bf16_kernel<{d}, 2>", 3: "ikbo_attn_bf16_pipe_kernel<{d}, 4, false>",
+                2: "ikbo_attn_bf16_kernel<{d}, 2>",
                 4: "ikbo_attn_bf16_kernel<{d}, 2>"}  # 4: the 4-wave kernel visiting key tiles in reverse
+MERGE_KERNEL = "ikbo_merge_kernel<{d}>"
 
 WORKLOAD_TEXT = {
     "c1_tiny_f32": "tiny fp32: 4 users, L~U[16,64], 20 candidates, n_q=1, H=2, d=32",
@@ -147,6 +149,8 @@ def traffic_from_profiles(workload):
                 else kernel_source_hash(MX_SOURCES) if mx else kernel_source_hash())
         if s.get("kernel_source_hash") != want:
             return None
+        if not (lce or bwd or mx) and "hbm_bytes_per_step_with_merge" in s:
+            return float(s["hbm_bytes_per_step_with_merge"])  # attention kernel + merge, as the roofline
         return float(s["hbm_bytes_per_launch"])
     except Exception:
         return None
@@ -731,7 +735,8 @@ def main():
     ap.add_argument("--config", default="c2_typical")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=15)
-    ap.add_argument("--report", action="store_true", help="add cold-cache and materialised-broadcast figures")
+    ap.add_argument("--report", action="store_true",
+                    help="linear compression: also time the materialised-broadcast comparator")
     ap.add_argument("--kernel-only", action="store_true", help="loop only the planned launch (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (to scale memory counters)")
@@ -778,10 +783,22 @@ def main():
     out_c = torch.empty(w.raw("q_cand").shape, dtype=tdt, device="cuda")
     out_u = torch.empty(w.raw("q_user").shape, dtype=tdt, device="cuda") if w.with_self else None
     stream = torch.cuda.current_stream()
-    plan = ikbo.ikbo_plan_create()
     offs_h = np.ascontiguousarray(w.user_offsets, dtype=np.int32)
     c2u_h = np.ascontiguousarray(w.cand_to_user, dtype=np.int32)
     ws = 1 if w.with_self else 0
+
+    def materialized():
+        ikbo.ikbo_attn_fwd_materialized(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"],
+                                        dev["cand_to_user"], w.n_users, w.n_cand, w.H, w.d, w.scale, out_c, stream,
+                                        n_q=w.n_q, dtype=dt_code)
+
+    if args.materialized_only:
+        for _ in range(args.steps):
+            materialized()
+        torch.cuda.synchronize()
+        print(json.dumps({"materialized_launches": args.steps, "config": args.config}), flush=True)
+        return
+    plan = ikbo.ikbo_plan_create(offs_h, c2u_h, w.n_users, w.n_cand, w.n_q, w.H, w.d, dt_code, ws, stream)
 
     def build():
         ikbo.ikbo_plan_build(plan, offs_h, c2u_h, w.n_users, w.n_cand, w.n_q, w.H, w.d, dt_code, ws, stream)
@@ -790,15 +807,6 @@ def main():
         ikbo.ikbo_attn_fwd_planned(plan, dev["q_cand"], dev.get("q_user"), dev["k_user"], dev["v_user"], w.scale,
                                    out_c, out_u, stream)
 
-    if args.materialized_only:
-        for _ in range(args.steps):
-            ikbo.ikbo_attn_fwd_materialized(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"],
-                                            dev["cand_to_user"], w.n_users, w.n_cand, w.n_q, w.H, w.d, w.scale,
-                                            dt_code, out_c, stream)
-        torch.cuda.synchronize()
-        print(json.dumps({"materialized_launches": args.steps, "config": args.config}), flush=True)
-        return
-    build()
     info = ikbo.ikbo_plan_info(plan)
     for _ in range(args.warmup):
         build()
@@ -817,8 +825,8 @@ def main():
         launch()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # Timed region 2: the same K steps with the kernel's dispatch stamping HIP
-    # events on this stream at its start and end (the roofline's duration).
+    # Timed region 2: the same K steps with the kernels' dispatches stamping HIP
+    # events on this stream at their start and end (the roofline's durations).
     ikbo.ikbo_plan_timing(plan, True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -832,6 +840,7 @@ def main():
     ikbo.ikbo_plan_timing(plan, False)
     k_avg_ms = float(np.mean(kern_ms))
     merge_avg_ms = float(np.mean(merge_ms))
+    path_ms = k_avg_ms + merge_avg_ms  # attention kernel + split-KV merge, per launch
 
     flops, byts, mat_bytes = algorithmic_counts(w)
     ms_per_step = wall * 1e3 / K
@@ -839,92 +848,101 @@ def main():
     ai = flops / byts
     peak_flops = (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS) * 1e12
     bound = "hbm" if ai < peak_flops / (PEAK_HBM_GBS * 1e9) else "mfma"
+    # The roofline covers the launch's kernels together: the attention kernel
+    # and, when key ranges were split, the merge of its partials.
     if bound == "hbm":
-        achieved = byts / (k_avg_ms * 1e-3) / 1e9
+        achieved = byts / (path_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS}
+        attn_only = byts / (k_avg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS
     else:
-        achieved = flops / (k_avg_ms * 1e-3) / 1e12
+        achieved = flops / (path_ms * 1e-3) / 1e12
         pk = peak_flops / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": pk, "unit": "TFLOP/s", "frac": achieved / pk}
+        attn_only = flops / (k_avg_ms * 1e-3) / peak_flops
+    attn_name = KERNEL_NAMES[int(info["kernel"])].format(d=w.d)
     roof["traffic"] = traffic_from_profiles(args.config)
-    roof["kernel"] = KERNEL_NAMES[int(info["kernel"])].format(d=w.d)
-    roof["kernel_avg_us"] = k_avg_ms * 1e3
-    roof["merge_kernel_avg_us"] = merge_avg_ms * 1e3  # split-KV merge, when key ranges were split
+    roof["kernel"] = attn_name + (" + " + MERGE_KERNEL.format(d=w.d) if merge_avg_ms > 0 else "")
+    roof["kernel_avg_us"] = path_ms * 1e3
+    roof["attn_kernel_avg_us"] = k_avg_ms * 1e3
+    roof["merge_kernel_avg_us"] = merge_avg_ms * 1e3
+    roof["frac_attention_kernel_only"] = attn_only
     roof["algorithmic_bytes_per_launch"] = byts
     roof["algorithmic_flops_per_launch"] = flops
 
     extra = {
         "ms_per_step_with_kernel_timing": wall_timed * 1e3 / K,
-        "attn_plus_merge_us": (k_avg_ms + merge_avg_ms) * 1e3,
-        "kernel_tflops": flops / (k_avg_ms * 1e-3) / 1e12,
-        "kernel_frac_mfma_peak": flops / (k_avg_ms * 1e-3) / peak_flops,
-        "kernel_hbm_gbs": byts / (k_avg_ms * 1e-3) / 1e9,
-        "kernel_us_median": float(np.median(kern_ms)) * 1e3,
+        "attn_plus_merge_us": path_ms * 1e3,
+        "kernel_tflops": flops / (path_ms * 1e-3) / 1e12,
+        "kernel_frac_mfma_peak": flops / (path_ms * 1e-3) / peak_flops,
+        "kernel_hbm_gbs": byts / (path_ms * 1e-3) / 1e9,
+        "attn_kernel_us_median": float(np.median(kern_ms)) * 1e3,
         "arith_intensity": ai,
+        "applicable_roof_tflops": min(peak_flops, ai * PEAK_HBM_GBS * 1e9) / 1e12,
         "cands_per_s": w.n_cand / (ms_per_step * 1e-3),
         "plan": info,
         "materialized_algorithmic_bytes": mat_bytes,
         "ikbo_vs_materialized_bytes_ratio": mat_bytes / byts,
     }
 
-    if args.report:
-        # cold cache: overwrite 2 GiB between launches so neither L2 nor MALL holds K/V
-        flush = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
-        ikbo.ikbo_plan_timing(plan, True)
-        for _ in range(30):
-            flush.fill_(1)
-            launch()
-            torch.cuda.synchronize()
-        cold, _ = ikbo.ikbo_plan_timing_read(plan, 30)
-        ikbo.ikbo_plan_timing(plan, False)
-        del flush
-        c_ms = float(np.median(cold))
-        extra["cold_kernel_us_median"] = c_ms * 1e3
-        extra["cold_kernel_tflops"] = flops / (c_ms * 1e-3) / 1e12
-        extra["cold_kernel_hbm_gbs"] = byts / (c_ms * 1e-3) / 1e9
-        # end-to-end device-mapping entry point (D2H copy + sync + host plan + launch)
-        if not w.with_self:
-            for _ in range(5):
-                ikbo.ikbo_attn_fwd_ex(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"],
-                                      dev["cand_to_user"], w.n_users, w.n_cand, w.n_q, w.H, w.d, w.scale,
-                                      dt_code, out_c, stream)
+    # Cold cache: 2 GiB overwritten between launches so that neither L2 nor the
+    # Infinity Cache holds K/V; the flush stays outside the kernels' events.
+    flush = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    n_cold = 20
+    ikbo.ikbo_plan_timing(plan, True)
+    for _ in range(n_cold):
+        flush.fill_(1)
+        launch()
+        torch.cuda.synchronize()
+    cold_a, cold_m = ikbo.ikbo_plan_timing_read(plan, n_cold)
+    ikbo.ikbo_plan_timing(plan, False)
+    del flush
+    c_ms = float(np.median(np.asarray(cold_a) + np.asarray(cold_m)))
+    extra["cold_attn_plus_merge_us_median"] = c_ms * 1e3
+    extra["cold_kernel_tflops"] = flops / (c_ms * 1e-3) / 1e12
+    extra["cold_kernel_hbm_gbs"] = byts / (c_ms * 1e-3) / 1e9
+    extra["cold_frac_applicable_roof"] = (flops / (c_ms * 1e-3)) / min(peak_flops, ai * PEAK_HBM_GBS * 1e9)
+    extra["warm_frac_applicable_roof"] = (flops / (path_ms * 1e-3)) / min(peak_flops, ai * PEAK_HBM_GBS * 1e9)
+    # Host time of each call of a step (the GPU idle first, so nothing waits on it).
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(100):
+        build()
+    extra["host_plan_build_us"] = (time.perf_counter() - t1) / 100 * 1e6
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(20):
+        launch()
+    extra["host_launch_us"] = (time.perf_counter() - t1) / 20 * 1e6
+    torch.cuda.synchronize()
+    if not w.with_self:
+        # End to end through the device-mapping entry point: D2H copy of the
+        # mapping, synchronisation, host plan and launch.
+        def e2e():
+            ikbo.ikbo_attn_fwd_mt(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"],
+                                  dev["cand_to_user"], w.n_users, w.n_cand, w.H, w.d, w.scale, out_c, stream,
+                                  n_q=w.n_q, dtype=dt_code)
+        for _ in range(5):
+            e2e()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        n_e2e = 50
+        for _ in range(n_e2e):
+            e2e()
+        torch.cuda.synchronize()
+        extra["e2e_device_mapping_us"] = (time.perf_counter() - t1) / n_e2e * 1e6
+        # The materialised-broadcast comparator: copy kernel + the same attention kernel.
+        if mat_bytes < 64e9:
+            for _ in range(2):
+                materialized()
             torch.cuda.synchronize()
             t1 = time.perf_counter()
-            n_e2e = 50
-            for _ in range(n_e2e):
-                ikbo.ikbo_attn_fwd_ex(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"],
-                                      dev["cand_to_user"], w.n_users, w.n_cand, w.n_q, w.H, w.d, w.scale,
-                                      dt_code, out_c, stream)
+            n_mat = 5
+            for _ in range(n_mat):
+                materialized()
             torch.cuda.synchronize()
-            extra["e2e_device_mapping_us"] = (time.perf_counter() - t1) / n_e2e * 1e6
-            # materialised broadcast comparator (copy kernel + the same attention kernel)
-            if mat_bytes < 64e9:
-                for _ in range(2):
-                    ikbo.ikbo_attn_fwd_materialized(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"],
-                                                    dev["cand_to_user"], w.n_users, w.n_cand, w.n_q, w.H, w.d,
-                                                    w.scale, dt_code, out_c, stream)
-                torch.cuda.synchronize()
-                t1 = time.perf_counter()
-                n_mat = 5
-                for _ in range(n_mat):
-                    ikbo.ikbo_attn_fwd_materialized(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"],
-                                                    dev["cand_to_user"], w.n_users, w.n_cand, w.n_q, w.H, w.d,
-                                                    w.scale, dt_code, out_c, stream)
-                torch.cuda.synchronize()
-                extra["materialized_us"] = (time.perf_counter() - t1) / n_mat * 1e6
-        # host time of each call of a step (GPU idle first, so nothing waits on it)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        for _ in range(100):
-            build()
-        extra["host_plan_build_us"] = (time.perf_counter() - t1) / 100 * 1e6
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        for _ in range(20):
-            launch()
-        extra["host_launch_us"] = (time.perf_counter() - t1) / 20 * 1e6
-        torch.cuda.synchronize()
+            extra["materialized_us"] = (time.perf_counter() - t1) / n_mat * 1e6
+            extra["materialized_vs_ikbo_step"] = extra["materialized_us"] / (ms_per_step * 1e3)
 
     ikbo.ikbo_plan_destroy(plan)
     result = {

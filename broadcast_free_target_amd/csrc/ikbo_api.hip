@@ -43,7 +43,7 @@ struct Plan {
   bool built = false;
   int32_t n_users = 0, n_cand = 0, n_q = 1, H = 0, d = 0, dtype = IKBO_DTYPE_BF16, with_self = 0;
   int32_t stages = 2;  // bf16 kernel ring depth chosen at build time
-  int32_t variant = 0;  // bf16 kernel: kVariantPipe, kVariantW8, kVariantW4 or kVariantW4R
+  int32_t variant = 0;  // bf16 kernel: kVariantW8, kVariantW4 or kVariantW4R
   int64_t total_len = 0;
   HostPlan hp;
   // device copies of the work list
@@ -58,17 +58,14 @@ struct Plan {
   const WorkItem* k_items = nullptr;            // what the kernels read
   const int32_t* k_perm = nullptr;
   // optional kernel timing (measurement)
-  bool timing = false;
+  TimedEvents timed;                            // flag: the launch had a merge kernel
   bool tracing = false;
   DevBuf d_trace;                               // [items, 6] uint64 per-item records
-  std::vector<hipEvent_t> tev;                  // 4 per timed launch
-  std::vector<char> timed_merge;                // that launch had a merge kernel
-  int n_timed = 0;
   // pinned landing area for device-resident mappings (synchronous entry points)
   PinnedBuf d2h;
 
   ~Plan() {
-    for (hipEvent_t e : tev) (void)hipEventDestroy(e);
+    timed.release();
     ring.release();
     d2h.release();
     d_items.release();
@@ -97,18 +94,16 @@ int bf16_stages() {
 }
 
 // bf16 kernel variants: the eight-wave kernel (one per CU, two waves per
-// SIMD), the plain 4-wave kernel (two resident per CU) and the
-// software-pipelined 4-wave kernel (one per CU).  By default a build plans for
-// the eight-wave kernel and keeps it when every workgroup gets at most one
+// SIMD) and the 4-wave kernel (two resident per CU).  By default a build plans
+// for the eight-wave kernel and keeps it when every workgroup gets at most one
 // item; otherwise it plans again for the 4-wave kernel, whose two independent
 // workgroups per CU keep the SIMDs busier over many items.  IKBO_KERNEL =
-// w8 | w4 | pipe forces a variant; w4r is the 4-wave kernel visiting each
-// item's key tiles last to first (the reverse-order variant of the TLX
-// attention post's persistent kernel).
-enum { kVariantPipe = 0, kVariantW8 = 1, kVariantW4 = 2, kVariantAuto = 3, kVariantW4R = 4 };
+// w8 | w4 forces a variant; w4r is the 4-wave kernel visiting each item's key
+// tiles last to first (the reverse-order variant of the TLX attention post's
+// persistent kernel).
+enum { kVariantW8 = 1, kVariantW4 = 2, kVariantAuto = 3, kVariantW4R = 4 };
 int bf16_variant() {
   const char* s = std::getenv("IKBO_KERNEL");
-  if (s && std::strcmp(s, "pipe") == 0) return kVariantPipe;
   if (s && std::strcmp(s, "w4r") == 0) return kVariantW4R;
   if (s && std::strcmp(s, "w4") == 0) return kVariantW4;
   if (s && std::strcmp(s, "w8") == 0) return kVariantW8;
@@ -286,22 +281,10 @@ int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* 
   }
   if (int rc = p->ring.on_stream(stream); rc != IKBO_OK) return rc;  // before anything is enqueued
   hipEvent_t* te = nullptr;  // attention start/end, merge start/end (stamped by the dispatches)
-  if (p->timing && p->n_timed < kMaxTimed) {
-    while (p->tev.size() < static_cast<size_t>(4 * (p->n_timed + 1))) {
-      hipEvent_t ev;
-      IKBO_HIP(hipEventCreate(&ev));
-      p->tev.push_back(ev);
-    }
-    te = &p->tev[4 * p->n_timed];
-    p->timed_merge.resize(p->n_timed + 1);
-    p->timed_merge[p->n_timed] = p->hp.n_groups > 0;
-    ++p->n_timed;
-  }
+  if (int rc = p->timed.next(&te, p->hp.n_groups > 0); rc != IKBO_OK) return rc;
   hipError_t e;
   if (p->dtype != IKBO_DTYPE_BF16)
     e = ikbo::launch_attn_f32(ap, p->d, p->hp.grid, stream, te);
-  else if (p->variant == kVariantPipe)
-    e = ikbo::launch_attn_bf16_pipe(ap, p->d, p->hp.grid, scale < 0.0f, stream, te);
   else if (p->variant == kVariantW8)
     e = ikbo::launch_attn_bf16_w8(ap, p->d, p->hp.grid, stream, te);
   else {
@@ -423,18 +406,29 @@ int ikbo_group_csr(const int32_t* cand_to_user_host, int32_t n_cand, int32_t n_u
   }
 }
 
-int ikbo_plan_create(void** plan) {
+int ikbo_plan_create(const int32_t* user_offsets_host, const int32_t* cand_to_user_host, int32_t n_users,
+                     int32_t n_cand, int32_t n_q, int32_t H, int32_t d, int32_t dtype, int32_t with_self, void* stream,
+                     void** plan) {
   if (!plan) return fail(IKBO_ERR_INVALID_ARG, "plan is null");
   *plan = nullptr;
-  Plan* p = new (std::nothrow) Plan();
-  if (!p) return fail(IKBO_ERR_NOMEM, "plan allocation");
-  int rc = plan_init(p);
-  if (rc != IKBO_OK) {
-    delete p;
-    return rc;
+  try {
+    Plan* p = new (std::nothrow) Plan();
+    if (!p) return fail(IKBO_ERR_NOMEM, "plan allocation");
+    int rc = plan_init(p);
+    if (rc == IKBO_OK)
+      rc = build_and_upload(p, user_offsets_host, cand_to_user_host, n_users, n_cand, n_q, H, d, dtype, with_self,
+                            static_cast<hipStream_t>(stream));
+    if (rc != IKBO_OK) {
+      delete p;
+      return rc;
+    }
+    *plan = p;
+    return IKBO_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(IKBO_ERR_NOMEM, "host allocation");
+  } catch (...) {
+    return fail(IKBO_ERR_INVALID_ARG, "unexpected host error");
   }
-  *plan = p;
-  return IKBO_OK;
 }
 
 int ikbo_plan_build(void* plan, const int32_t* user_offsets_host, const int32_t* cand_to_user_host, int32_t n_users,
@@ -473,13 +467,12 @@ void ikbo_plan_destroy(void* plan) {
 int ikbo_plan_info(void* plan, int64_t* info, int32_t n_info) {
   if (!plan || !info || n_info < 1) return fail(IKBO_ERR_INVALID_ARG, "null plan or info");
   const Plan* p = static_cast<const Plan*>(plan);
-  // kernel: 0 fp32, 1 bf16 eight-wave, 2 bf16 4-wave, 3 bf16 software-pipelined,
-  // 4 bf16 4-wave with key tiles in reverse order
+  // kernel: 0 fp32, 1 bf16 eight-wave, 2 bf16 4-wave, 4 bf16 4-wave with key
+  // tiles in reverse order (3 is no longer used)
   const int64_t kernel = p->dtype != IKBO_DTYPE_BF16 ? 0
                          : p->variant == kVariantW8  ? 1
-                         : p->variant == kVariantW4  ? 2
                          : p->variant == kVariantW4R ? 4
-                                                     : 3;
+                                                     : 2;
   const int64_t v[9] = {static_cast<int64_t>(p->hp.items.size()),
                         p->hp.grid,
                         p->hp.n_groups,
@@ -496,24 +489,22 @@ int ikbo_plan_info(void* plan, int64_t* info, int32_t n_info) {
 
 int ikbo_plan_timing(void* plan, int32_t enable) {
   if (!plan) return fail(IKBO_ERR_INVALID_ARG, "plan is null");
-  Plan* p = static_cast<Plan*>(plan);
-  p->timing = enable != 0;
-  p->n_timed = 0;
-  return IKBO_OK;
+  return static_cast<Plan*>(plan)->timed.enable(enable != 0);
 }
 
 int ikbo_plan_timing_read(void* plan, float* attn_ms, float* merge_ms, int32_t max_n, int32_t* n) {
   if (!plan || !n || max_n < 0 || (max_n > 0 && (!attn_ms || !merge_ms)))
     return fail(IKBO_ERR_INVALID_ARG, "null argument");
   Plan* p = static_cast<Plan*>(plan);
-  const int m = std::min<int>(p->n_timed, max_n);
+  const std::vector<hipEvent_t>& ev = p->timed.ev;
+  const int m = std::min<int>(p->timed.n, max_n);
   for (int i = 0; i < m; ++i) {
-    IKBO_HIP(hipEventSynchronize(p->tev[4 * i + 1]));
-    IKBO_HIP(hipEventElapsedTime(&attn_ms[i], p->tev[4 * i], p->tev[4 * i + 1]));
+    IKBO_HIP(hipEventSynchronize(ev[4 * i + 1]));
+    IKBO_HIP(hipEventElapsedTime(&attn_ms[i], ev[4 * i], ev[4 * i + 1]));
     merge_ms[i] = 0.0f;
-    if (p->timed_merge[i]) {
-      IKBO_HIP(hipEventSynchronize(p->tev[4 * i + 3]));
-      IKBO_HIP(hipEventElapsedTime(&merge_ms[i], p->tev[4 * i + 2], p->tev[4 * i + 3]));
+    if (p->timed.flag[i]) {
+      IKBO_HIP(hipEventSynchronize(ev[4 * i + 3]));
+      IKBO_HIP(hipEventElapsedTime(&merge_ms[i], ev[4 * i + 2], ev[4 * i + 3]));
     }
   }
   *n = m;
@@ -550,6 +541,28 @@ int ikbo_attn_fwd(const void* q_cand, const void* k_user, const void* v_user, co
   }
 }
 
+int ikbo_attn_fwd_f32(const void* q_cand, const void* k_user, const void* v_user, const int32_t* user_offsets,
+                      const int32_t* cand_to_user, int32_t n_users, int32_t n_cand, int32_t H, int32_t d, float scale,
+                      void* out, void* stream) {
+  try {
+    return attn_device_mapping(q_cand, nullptr, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, 1, H, d,
+                               scale, IKBO_DTYPE_F32, 0, out, nullptr, stream);
+  } catch (...) {
+    return fail(IKBO_ERR_NOMEM, "unexpected host error");
+  }
+}
+
+int ikbo_attn_fwd_mt(const void* q_cand, const void* k_user, const void* v_user, const int32_t* user_offsets,
+                     const int32_t* cand_to_user, int32_t n_users, int32_t n_cand, int32_t H, int32_t d, float scale,
+                     void* out, void* stream, int32_t n_q, int32_t dtype) {
+  try {
+    return attn_device_mapping(q_cand, nullptr, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, n_q, H,
+                               d, scale, dtype, 0, out, nullptr, stream);
+  } catch (...) {
+    return fail(IKBO_ERR_NOMEM, "unexpected host error");
+  }
+}
+
 int ikbo_attn_fwd_ex(const void* q_cand, const void* k_user, const void* v_user, const int32_t* user_offsets,
                      const int32_t* cand_to_user, int32_t n_users, int32_t n_cand, int32_t n_q, int32_t H, int32_t d,
                      float scale, int32_t dtype, void* out, void* stream) {
@@ -575,8 +588,8 @@ int ikbo_self_target_fwd(const void* q_user, const void* q_cand, const void* k_u
 
 int ikbo_attn_fwd_materialized(const void* q_cand, const void* k_user, const void* v_user,
                                const int32_t* user_offsets, const int32_t* cand_to_user, int32_t n_users,
-                               int32_t n_cand, int32_t n_q, int32_t H, int32_t d, float scale, int32_t dtype,
-                               void* out, void* stream_) {
+                               int32_t n_cand, int32_t H, int32_t d, float scale, void* out, void* stream_,
+                               int32_t n_q, int32_t dtype) {
   try {
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     int rc = check_dims(n_users, n_cand, n_q, H, d, dtype);

@@ -43,11 +43,9 @@ struct Bwd {
   HostPlan hp;            // dQ work items (the forward's planner) and the CSR grouping
   std::vector<WorkItem> items_b;
   int64_t n_items_a = 0, n_items_b = 0, n_groups = 0;
-  bool timing = false;
-  std::vector<hipEvent_t> tev;  // 4 per timed call: dQ kernel start/end, dK/dV kernel start/end
-  int n_timed = 0;
+  TimedEvents timed;      // per timed call: dQ kernel start/end, dK/dV kernel start/end
   ~Bwd() {
-    for (hipEvent_t e : tev) (void)hipEventDestroy(e);
+    timed.release();
     ring.release();
     ws.release();
     ws_dq.release();
@@ -111,11 +109,13 @@ int ikbo_attn_bwd(void* bwd, const int32_t* user_offsets, const int32_t* cand_to
     pp.allow_split = static_cast<int64_t>(n_cand) * n_q < ikbo::kBwdMaxSplitRows && !env_int("IKBO_NO_SPLIT", 0);
     rc = ikbo::build_plan(user_offsets, cand_to_user, n_users, n_cand, n_q, H, false, pp, &b->hp, &err);
     if (rc != ikbo::kOk) return fail(rc, err);
-    if (T == 0) return IKBO_OK;  // no keys: no gradient to write (and every query gradient row would be empty)
     const int64_t R = static_cast<int64_t>(n_cand) * n_q;
+    if (R == 0 && T == 0) return IKBO_OK;  // nothing to write
     const size_t qb = static_cast<size_t>(R) * H * d * 2, kb = static_cast<size_t>(T) * H * d * 2;
     if (n_cand > 0 && (!q_cand || !out || !dout || !dq_cand)) return fail(IKBO_ERR_INVALID_ARG, "null query-side tensor");
-    if (!k_user || !v_user || !dk_user || !dv_user) return fail(IKBO_ERR_INVALID_ARG, "null key-side tensor");
+    if (T > 0 && (!k_user || !v_user || !dk_user || !dv_user)) return fail(IKBO_ERR_INVALID_ARG, "null key-side tensor");
+    // With no keys at all (T = 0) the dQ kernel still runs: its items have empty
+    // key ranges and write zero query-gradient rows.
     const uintptr_t align_or = reinterpret_cast<uintptr_t>(q_cand) | reinterpret_cast<uintptr_t>(k_user) |
                                reinterpret_cast<uintptr_t>(v_user) | reinterpret_cast<uintptr_t>(out) |
                                reinterpret_cast<uintptr_t>(dout) | reinterpret_cast<uintptr_t>(dq_cand) |
@@ -180,15 +180,7 @@ int ikbo_attn_bwd(void* bwd, const int32_t* user_offsets, const int32_t* cand_to
     std::memcpy(base + na * sizeof(WorkItem), b->items_b.data(), static_cast<size_t>(nb) * sizeof(WorkItem));
     if (n_cand > 0) std::memcpy(base + items_bytes, b->hp.cand_perm.data(), static_cast<size_t>(n_cand) * 4);
     hipEvent_t* te = nullptr;
-    if (b->timing && b->n_timed < kMaxTimed) {
-      while (b->tev.size() < static_cast<size_t>(4 * (b->n_timed + 1))) {
-        hipEvent_t ev;
-        IKBO_HIP(hipEventCreate(&ev));
-        b->tev.push_back(ev);
-      }
-      te = &b->tev[4 * b->n_timed];
-      ++b->n_timed;
-    }
+    if ((rc = b->timed.next(&te, true)) != IKBO_OK) return rc;
     ikbo::BwdParams p{};
     p.q = q_cand;
     p.k = k_user;
@@ -238,21 +230,19 @@ int ikbo_bwd_info(void* bwd, int64_t* info, int32_t n_info) {
 
 int ikbo_bwd_timing(void* bwd, int32_t enable) {
   if (!bwd) return fail(IKBO_ERR_INVALID_ARG, "bwd is null");
-  Bwd* b = static_cast<Bwd*>(bwd);
-  b->timing = enable != 0;
-  b->n_timed = 0;
-  return IKBO_OK;
+  return static_cast<Bwd*>(bwd)->timed.enable(enable != 0);
 }
 
 int ikbo_bwd_timing_read(void* bwd, float* dq_ms, float* dkv_ms, int32_t max_n, int32_t* n) {
   if (!bwd || !n || max_n < 0 || (max_n > 0 && (!dq_ms || !dkv_ms))) return fail(IKBO_ERR_INVALID_ARG, "null argument");
   Bwd* b = static_cast<Bwd*>(bwd);
-  const int m = std::min<int>(b->n_timed, max_n);
+  const std::vector<hipEvent_t>& ev = b->timed.ev;
+  const int m = std::min<int>(b->timed.n, max_n);
   for (int i = 0; i < m; ++i) {
-    IKBO_HIP(hipEventSynchronize(b->tev[4 * i + 1]));
-    IKBO_HIP(hipEventElapsedTime(&dq_ms[i], b->tev[4 * i], b->tev[4 * i + 1]));
-    IKBO_HIP(hipEventSynchronize(b->tev[4 * i + 3]));
-    IKBO_HIP(hipEventElapsedTime(&dkv_ms[i], b->tev[4 * i + 2], b->tev[4 * i + 3]));
+    IKBO_HIP(hipEventSynchronize(ev[4 * i + 1]));
+    IKBO_HIP(hipEventElapsedTime(&dq_ms[i], ev[4 * i], ev[4 * i + 1]));
+    IKBO_HIP(hipEventSynchronize(ev[4 * i + 3]));
+    IKBO_HIP(hipEventElapsedTime(&dkv_ms[i], ev[4 * i + 2], ev[4 * i + 3]));
   }
   *n = m;
   return IKBO_OK;

@@ -9,6 +9,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <string>
+#include <vector>
 
 #include "ikbo.h"
 
@@ -166,13 +167,26 @@ struct PinnedRing {
     IKBO_HIP(hipEventSynchronize(flush));
     return IKBO_OK;
   }
-  // The next buffer, grown to at least `bytes`, once its last reader is done.
+  // The next buffer, at least `bytes` long, once its last reader is done.
+  // When a request outgrows the buffers, all of them are reallocated at once
+  // (with half again as much room), after every launch that may still read
+  // one has finished: buffers are never allocated one call at a time, so a
+  // steady stream of requests of similar size allocates nothing after its
+  // first call.
   int acquire(size_t bytes, int* idx) {
     const int s = next;
     next = (s + 1) % kStages;
-    int rc = wait(last[s]);
-    if (rc != IKBO_OK) return rc;
-    if ((rc = buf[s].ensure(bytes)) != IKBO_OK) return rc;
+    int rc = IKBO_OK;
+    if (bytes > buf[s].cap) {
+      if ((rc = wait(n_launch - 1)) != IKBO_OK) return rc;
+      const size_t want = bytes + bytes / 2;
+      for (int i = 0; i < kStages; ++i) {
+        if ((rc = buf[i].ensure(want)) != IKBO_OK) return rc;
+        last[i] = -1;
+      }
+    } else if ((rc = wait(last[s])) != IKBO_OK) {
+      return rc;
+    }
     *idx = s;
     return IKBO_OK;
   }
@@ -199,6 +213,56 @@ struct PinnedRing {
       ev_seq[slot] = seq;
     }
     return IKBO_OK;
+  }
+};
+
+// Timing events of the measurement entry points: four per timed call (two
+// kernels' start and end, stamped by their dispatches), created in batches
+// when timing is switched on and when a batch runs out, so that a timed call
+// normally creates none.  `flag` records per timed call whether its optional
+// second kernel ran.
+struct TimedEvents {
+  static constexpr int kBatch = 256;  // calls per batch of events
+  std::vector<hipEvent_t> ev;
+  std::vector<char> flag;
+  int n = 0;
+  bool on = false;
+
+  int reserve(int calls) {
+    calls = std::min(calls, kMaxTimed);
+    while (ev.size() < static_cast<size_t>(4 * calls)) {
+      hipEvent_t e;
+      IKBO_HIP(hipEventCreate(&e));
+      ev.push_back(e);
+    }
+    if (flag.size() < static_cast<size_t>(calls)) flag.resize(calls);
+    return IKBO_OK;
+  }
+  // Switches timing on or off; both reset the record.
+  int enable(bool e) {
+    on = e;
+    n = 0;
+    return e ? reserve(kBatch) : IKBO_OK;
+  }
+  // The four events of the next timed call (null when timing is off or the
+  // record is full) and notes its flag.
+  int next(hipEvent_t** te, bool flag_value) {
+    *te = nullptr;
+    if (!on || n >= kMaxTimed) return IKBO_OK;
+    if (static_cast<size_t>(4 * (n + 1)) > ev.size()) {
+      int rc = reserve(n + kBatch);
+      if (rc != IKBO_OK) return rc;
+    }
+    *te = &ev[4 * n];
+    flag[n] = flag_value ? 1 : 0;
+    ++n;
+    return IKBO_OK;
+  }
+  void release() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+    ev.clear();
+    flag.clear();
+    n = 0;
   }
 };
 

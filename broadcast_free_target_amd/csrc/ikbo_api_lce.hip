@@ -32,12 +32,9 @@ struct Lce {
   bool nested = false;  // created for three levels (user -> vendor -> item)
   int32_t M = 0, K_u = 0, K_v = 0, K_c = 0, M_pad = 0, K_u_pad = 0, K_v_pad = 0, K_c_pad = 0;
   DevBuf wu, wv, wc, y, yv, errors, order;
-  bool timing = false;
-  std::vector<hipEvent_t> tev;  // 4 per timed call: upper levels start/end, item GEMM start/end
-  std::vector<char> timed_user;
-  int n_timed = 0;
+  TimedEvents timed;  // per timed call: upper levels start/end, item GEMM start/end; flag: upper ran
   ~Lce() {
-    for (hipEvent_t e : tev) (void)hipEventDestroy(e);
+    timed.release();
     wu.release();
     wv.release();
     wc.release();
@@ -118,17 +115,8 @@ hipError_t lce_level(const Lce* l, const void* wblk, int32_t K_pad, const void* 
 }
 
 hipEvent_t* lce_timing_slot(Lce* l, bool upper) {
-  if (!l->timing || l->n_timed >= kMaxTimed) return nullptr;
-  while (l->tev.size() < static_cast<size_t>(4 * (l->n_timed + 1))) {
-    hipEvent_t ev;
-    if (hipEventCreate(&ev) != hipSuccess) return nullptr;
-    l->tev.push_back(ev);
-  }
-  hipEvent_t* te = &l->tev[4 * l->n_timed];
-  l->timed_user.resize(l->n_timed + 1);
-  l->timed_user[l->n_timed] = upper;
-  ++l->n_timed;
-  return te;
+  hipEvent_t* te = nullptr;
+  return l->timed.next(&te, upper) == IKBO_OK ? te : nullptr;
 }
 
 // Checks shared by the two forward calls: device, sizes, N, grid limits.
@@ -289,24 +277,22 @@ int ikbo_lce_errors(void* lce, int64_t* count) {
 
 int ikbo_lce_timing(void* lce, int32_t enable) {
   if (!lce) return fail(IKBO_ERR_INVALID_ARG, "lce is null");
-  Lce* l = static_cast<Lce*>(lce);
-  l->timing = enable != 0;
-  l->n_timed = 0;
-  return IKBO_OK;
+  return static_cast<Lce*>(lce)->timed.enable(enable != 0);
 }
 
 int ikbo_lce_timing_read(void* lce, float* user_ms, float* cand_ms, int32_t max_n, int32_t* n) {
   if (!lce || !n || max_n < 0 || (max_n > 0 && (!user_ms || !cand_ms))) return fail(IKBO_ERR_INVALID_ARG, "null argument");
   Lce* l = static_cast<Lce*>(lce);
-  const int m = std::min<int>(l->n_timed, max_n);
+  const std::vector<hipEvent_t>& ev = l->timed.ev;
+  const int m = std::min<int>(l->timed.n, max_n);
   for (int i = 0; i < m; ++i) {
     user_ms[i] = 0.0f;
-    if (l->timed_user[i]) {
-      IKBO_HIP(hipEventSynchronize(l->tev[4 * i + 1]));
-      IKBO_HIP(hipEventElapsedTime(&user_ms[i], l->tev[4 * i], l->tev[4 * i + 1]));
+    if (l->timed.flag[i]) {
+      IKBO_HIP(hipEventSynchronize(ev[4 * i + 1]));
+      IKBO_HIP(hipEventElapsedTime(&user_ms[i], ev[4 * i], ev[4 * i + 1]));
     }
-    IKBO_HIP(hipEventSynchronize(l->tev[4 * i + 3]));
-    IKBO_HIP(hipEventElapsedTime(&cand_ms[i], l->tev[4 * i + 2], l->tev[4 * i + 3]));
+    IKBO_HIP(hipEventSynchronize(ev[4 * i + 3]));
+    IKBO_HIP(hipEventElapsedTime(&cand_ms[i], ev[4 * i + 2], ev[4 * i + 3]));
   }
   *n = m;
   return IKBO_OK;

@@ -37,12 +37,9 @@ struct Mx {
   DevBuf ws_o, ws_rec;
   HostPlan hp;
   std::vector<int32_t> vblk;  // per item: first and last V-scale block
-  bool timing = false;
-  std::vector<hipEvent_t> tev;  // 4 per timed call: kernel start/end, merge start/end
-  std::vector<char> timed_merge;
-  int n_timed = 0;
+  TimedEvents timed;  // per timed call: kernel start/end, merge start/end; flag: merged
   ~Mx() {
-    for (hipEvent_t e : tev) (void)hipEventDestroy(e);
+    timed.release();
     ring.release();
     ws_o.release();
     ws_rec.release();
@@ -171,17 +168,7 @@ int ikbo_attn_fwd_mxfp8(void* mx, const int32_t* user_offsets, const int32_t* ca
     std::memcpy(base + vblk_at, m->vblk.data(), static_cast<size_t>(2 * n_items) * 4);
 
     hipEvent_t* te = nullptr;
-    if (m->timing && m->n_timed < kMaxTimed) {
-      while (m->tev.size() < static_cast<size_t>(4 * (m->n_timed + 1))) {
-        hipEvent_t ev;
-        IKBO_HIP(hipEventCreate(&ev));
-        m->tev.push_back(ev);
-      }
-      te = &m->tev[4 * m->n_timed];
-      m->timed_merge.resize(m->n_timed + 1);
-      m->timed_merge[m->n_timed] = m->hp.n_groups > 0;
-      ++m->n_timed;
-    }
+    if ((rc = m->timed.next(&te, m->hp.n_groups > 0)) != IKBO_OK) return rc;
     ikbo::MxParams p{};
     p.q = static_cast<const uint8_t*>(q_codes);
     p.qs = static_cast<const uint8_t*>(q_scales);
@@ -229,24 +216,22 @@ int ikbo_mx_info(void* mx, int64_t* info, int32_t n_info) {
 
 int ikbo_mx_timing(void* mx, int32_t enable) {
   if (!mx) return fail(IKBO_ERR_INVALID_ARG, "mx is null");
-  Mx* m = static_cast<Mx*>(mx);
-  m->timing = enable != 0;
-  m->n_timed = 0;
-  return IKBO_OK;
+  return static_cast<Mx*>(mx)->timed.enable(enable != 0);
 }
 
 int ikbo_mx_timing_read(void* mx, float* attn_ms, float* merge_ms, int32_t max_n, int32_t* n) {
   if (!mx || !n || max_n < 0 || (max_n > 0 && (!attn_ms || !merge_ms)))
     return fail(IKBO_ERR_INVALID_ARG, "null argument");
   Mx* m = static_cast<Mx*>(mx);
-  const int cnt = std::min(m->n_timed, max_n);
+  const std::vector<hipEvent_t>& ev = m->timed.ev;
+  const int cnt = std::min(m->timed.n, max_n);
   for (int i = 0; i < cnt; ++i) {
-    IKBO_HIP(hipEventSynchronize(m->tev[4 * i + 1]));
-    IKBO_HIP(hipEventElapsedTime(&attn_ms[i], m->tev[4 * i], m->tev[4 * i + 1]));
+    IKBO_HIP(hipEventSynchronize(ev[4 * i + 1]));
+    IKBO_HIP(hipEventElapsedTime(&attn_ms[i], ev[4 * i], ev[4 * i + 1]));
     merge_ms[i] = 0.0f;
-    if (m->timed_merge[i]) {
-      IKBO_HIP(hipEventSynchronize(m->tev[4 * i + 3]));
-      IKBO_HIP(hipEventElapsedTime(&merge_ms[i], m->tev[4 * i + 2], m->tev[4 * i + 3]));
+    if (m->timed.flag[i]) {
+      IKBO_HIP(hipEventSynchronize(ev[4 * i + 3]));
+      IKBO_HIP(hipEventElapsedTime(&merge_ms[i], ev[4 * i + 2], ev[4 * i + 3]));
     }
   }
   *n = cnt;

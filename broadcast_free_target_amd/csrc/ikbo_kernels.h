@@ -47,10 +47,6 @@ hipError_t launch_attn_bf16(const AttnParams& p, int d, int stages, int grid, hi
 // two wave halves, one resident workgroup per CU).  Work items are the same;
 // key chunks should be multiples of 2 * kBf16TileKeys to keep both halves busy.
 hipError_t launch_attn_bf16_w8(const AttnParams& p, int d, int grid, hipStream_t stream, hipEvent_t* ev = nullptr);
-// Software-pipelined variant (one wave per SIMD, one resident workgroup per
-// CU).  neg_scale selects the instance for a negative softmax scale.
-hipError_t launch_attn_bf16_pipe(const AttnParams& p, int d, int grid, bool neg_scale, hipStream_t stream,
-                                 hipEvent_t* ev = nullptr);
 hipError_t launch_attn_f32(const AttnParams& p, int d, int grid, hipStream_t stream, hipEvent_t* ev = nullptr);
 // Merges the split-KV partials of groups 0 .. n_groups-1 into the bf16 outputs.
 hipError_t launch_merge(const AttnParams& p, int n_groups, int d, hipStream_t stream, hipEvent_t* ev = nullptr);

@@ -84,7 +84,8 @@ __device__ __forceinline__ f32x4_t split_record(float m, float l, int64_t qrow, 
 
 // Chunk weights of one row of a split group: w_c = 2^(m_c - M) / L with
 // M = max_c m_c and L = sum_c 2^(m_c - M) l_c, so that O = sum_c w_c O_c (the
-// log-sum-exp merge of split-K partial results, TLX attention post).
+// log-sum-exp merge of Flash-Decoding's split-KV partials, AI-infra guide,
+// section 4.6.4).
 // Contraction off: every build rounds the merge alike.
 __device__ __forceinline__ void chunk_weights(const float* m, const float* l, int nchunk, float* w) {
 #pragma clang fp contract(off)
@@ -139,13 +140,6 @@ __device__ __forceinline__ float pair_sum(float x) {
   float a, b;
   swap_halves(x, a, b);
   return a + b;
-}
-// The same pair reductions through ds_bpermute: an ordinary instruction to
-// the scheduler (inline assembly bounds its scheduling regions).
-__device__ __forceinline__ float pair_max_bp(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float pair_sum_bp(float x) {
-  const float y = __shfl_xor(x, 32);
-  return (threadIdx.x & 32) ? y + x : x + y;  // same operand order in both lanes of a pair
 }
 
 
@@ -694,513 +688,6 @@ __global__ __launch_bounds__(512, 1) void ikbo_attn_bf16_w8_kernel(AttnParams P)
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernel, software pipelined: 4 wave64 (one per SIMD), 128 rows
-// ---------------------------------------------------------------------------
-//
-// Iteration t of a wave issues the MFMAs of S(t+1) = K(t+1) Q^T and of
-// O += V(t-1)^T P(t-1) while it does the softmax arithmetic of tile t, so
-// the matrix pipe and the vector ALU work on independent data.  K and V have
-// separate rings of NR tiles: K(j) is read in iteration j-1 and V(j) in
-// iteration j+1, so iteration t issues K(t+NR) and V(t+NR-2), both NR-1
-// iterations ahead of their use.  LDS addresses are per-lane offsets fixed
-// for the whole kernel plus compile-time displacements.
-
-template <int D>
-struct LaneOff {
-  int k[D / 16];     // K operand, MFMA K-step st, key block 0 (key block b adds 32*b*D)
-  int v[D / 32][2];  // V^T operand, column block mb, first / second 4-key read (keys b*32+16*s2 add that*D)
-};
-
-template <int D>
-__device__ __forceinline__ LaneOff<D> lane_offsets(int lane) {
-  LaneOff<D> o;
-  const int n = lane & 31, g = lane >> 5, kq = lane & 15, half = (lane >> 4) & 1;
-#pragma unroll
-  for (int st = 0; st < D / 16; ++st) o.k[st] = tile_off<D>(n, st * 2 + g);
-#pragma unroll
-  for (int mb = 0; mb < D / 32; ++mb) {
-    const int col = mb * 32 + half * 16 + 4 * (kq & 3);
-    const int r = g * 4 + (kq >> 2);
-    o.v[mb][0] = tile_off<D>(r, col >> 3) + (col & 4);
-    o.v[mb][1] = tile_off<D>(r + 8, col >> 3) + (col & 4);
-  }
-  return o;
-}
-
-// S^T block pair for one K tile: s[b] = K[b*32 .. b*32+31] . Q^T.
-template <int D>
-__device__ __forceinline__ void qk_tile(const uint16_t* __restrict__ Ks, const LaneOff<D>& o,
-                                        const u32x4_t (&qf)[D / 16], f32x16_t (&s)[2]) {
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    u32x4_t a[D / 16];
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) a[st] = *reinterpret_cast<const u32x4_t*>(Ks + o.k[st] + b * 32 * D);
-    s[b] = f32x16_t{};
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st)
-      s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[st]), as_bf16x8(qf[st]), s[b], 0, 0, 0);
-  }
-}
-
-// O^T += V^T . P^T for one V tile (P^T operand of K-step (b, s2) = pb[b][s2]).
-template <int D>
-__device__ __forceinline__ void pv_tile(const uint16_t* __restrict__ Vs, const LaneOff<D>& o,
-                                        const bf16x8_t (&pb)[2][2], f32x16_t (&oacc)[D / 32]) {
-#pragma unroll
-  for (int mb = 0; mb < D / 32; ++mb) {
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int disp = (b * 32 + 16 * s2) * D;
-        const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(Vs + o.v[mb][0] + disp));
-        const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(Vs + o.v[mb][1] + disp));
-        const i16x8_t v8 = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, v8), pb[b][s2], oacc[mb],
-                                                          0, 0, 0);
-      }
-    }
-  }
-}
-
-// Online softmax of one tile of scores s (unscaled; p = exp2(c*s - m)).  Writes
-// the bf16 probabilities, updates (m_run, l_run) and returns the factor by
-// which O must be scaled before the next P.V (1 unless the reference moved).
-// Lazy reference: m_run moves only when the tile max exceeds it by more than 8.
-// NEG: the scale is negative, so the largest scaled score is c * min(s).
-template <bool MASK, bool NEG>
-__device__ __forceinline__ float softmax_tile(f32x16_t (&s)[2], bf16x8_t (&pb)[2][2], float& m_run, float& l_run,
-                                              int key_base, int key_end, bool causal, int row_tok, float c, int g) {
-  uint32_t live = 0xffffffffu;
-  if (MASK) {
-    live = 0u;
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = key_base + b * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-        const bool ok = key < key_end && (!causal || key <= row_tok);
-        live |= (ok ? 1u : 0u) << (b * 16 + i);
-      }
-  }
-  const float dead = NEG ? -kNegInf : kNegInf;
-  float mx = dead;
-#pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float v = (MASK && !((live >> (b * 16 + i)) & 1u)) ? dead : s[b][i];
-      mx = NEG ? fminf(mx, v) : fmaxf(mx, v);
-    }
-  float m_tile = mx * c;
-  if (!(m_tile == m_tile)) m_tile = kNegInf;  // no live key and c == 0
-  m_tile = pair_max_bp(m_tile);
-  const bool need = m_tile > m_run + 8.0f;
-  const float m_new = need ? m_tile : m_run;
-  const float alpha = (m_new == m_run) ? 1.0f : exp2_fast(m_run - m_new);  // 0 when m_run was -inf
-  m_run = m_new;
-  const float m_use = (m_run == kNegInf) ? 0.0f : m_run;
-  float rs = 0.0f;
-#pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float p = exp2_fast(fmaf(s[b][i], c, -m_use));
-      if (MASK) p = ((live >> (b * 16 + i)) & 1u) ? p : 0.0f;
-      s[b][i] = p;
-      rs += p;
-    }
-  l_run = l_run * alpha + pair_sum_bp(rs);
-#pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pb[b][s2][j] = static_cast<__bf16>(s[b][s2 * 8 + j]);
-  return alpha;
-}
-
-// s_waitcnt vmcnt(k * STEP) for a run-time k in [0, MAXK].
-template <int STEP, int MAXK>
-__device__ __forceinline__ void wait_vmcnt_steps(int k) {
-  if constexpr (MAXK == 0) {
-    wait_vmcnt<0>();
-  } else {
-    if (k >= MAXK)
-      wait_vmcnt<MAXK * STEP>();
-    else
-      wait_vmcnt_steps<STEP, MAXK - 1>(k);
-  }
-}
-
-// Final rows of a tile (bf16) or its split partial and row records.
-template <int D>
-__device__ __forceinline__ void write_tile_rows(const AttnParams& P, const WorkItem& it, const f32x16_t (&oacc)[D / 32],
-                                                float m_run, float l_run, int64_t qrow, bool causal, int r_w, int g) {
-  // Lane holds O^T rows d = mb*32 + (i/4)*8 + g*4 + i%4 of query row r_w.
-  if (it.grp < 0) {
-    if (qrow >= 0) {
-      uint16_t* ob = static_cast<uint16_t*>(causal ? P.out_user : P.out_cand);
-      uint16_t* op = ob + (qrow * P.H + it.h) * D + g * 4;
-      const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-#pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4)
-          *reinterpret_cast<u32x2_t*>(op + mb * 32 + i4 * 8) =
-              pack4_bf16(oacc[mb][i4 * 4 + 0] * inv, oacc[mb][i4 * 4 + 1] * inv, oacc[mb][i4 * 4 + 2] * inv,
-                         oacc[mb][i4 * 4 + 3] * inv);
-    }
-  } else {
-    const int64_t slot = static_cast<int64_t>(it.slot0) + it.chunk;
-    if (r_w < it.nrows) {
-      float* wo = P.ws_o + (slot * kBM + r_w) * D + g * 4;
-#pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4)
-          *reinterpret_cast<f32x4_t*>(wo + mb * 32 + i4 * 8) =
-              f32x4_t{oacc[mb][i4 * 4 + 0], oacc[mb][i4 * 4 + 1], oacc[mb][i4 * 4 + 2], oacc[mb][i4 * 4 + 3]};
-    }
-    if (g == 0)  // every tile row gets a record; empty rows are marked
-      *reinterpret_cast<f32x4_t*>(P.ws_rec + (slot * kBM + r_w) * 4) = split_record(m_run, l_run, qrow, it, P.H);
-  }
-}
-
-// Per-wave state of the pipelined loop.
-template <int D>
-struct PipeState {
-  f32x16_t oacc[D / 32];
-  float m_run, l_run;
-};
-
-// Softmax state carried between the micro-steps of one iteration.
-struct SoftmaxTmp {
-  float mpart[4];  // partial maxima
-  float m_tile, bp, m_use, rs[2];
-  bool need;
-};
-
-// Micro-step k (0..31) of the online softmax of one tile (see pipe_body).
-// Value v = b*16 + i of the lane is s[b][i], the score of key offset
-// koff(v) = b*32 + (i/4)*8 + g*4 + i%4 from the tile's first key; with MASK a
-// value is live when koff(v) - g*4 < lim.
-template <int K, bool MASK, bool NEG>
-__device__ __forceinline__ void softmax_micro(f32x16_t (&s)[2], bf16x8_t (&pb)[2][2], SoftmaxTmp& tm, float& m_run,
-                                              float& l_run, float& alpha, float c, int lim) {
-  constexpr float dead = NEG ? -kNegInf : kNegInf;
-  auto live = [&](int v) { return ((v >> 4) * 32 + ((v & 15) >> 2) * 8 + (v & 3)) < lim; };
-  if constexpr (K < 4) {  // partial max over values 8K .. 8K+7
-    float m = dead;
-#pragma unroll
-    for (int v = 8 * K; v < 8 * K + 8; ++v) {
-      const float x = (MASK && !live(v)) ? dead : s[v >> 4][v & 15];
-      m = NEG ? fminf(m, x) : fmaxf(m, x);
-    }
-    tm.mpart[K] = m;
-  } else if constexpr (K == 4) {
-    const float mx = NEG ? fminf(fminf(tm.mpart[0], tm.mpart[1]), fminf(tm.mpart[2], tm.mpart[3]))
-                         : fmaxf(fmaxf(tm.mpart[0], tm.mpart[1]), fmaxf(tm.mpart[2], tm.mpart[3]));
-    float mt = mx * c;
-    if (!(mt == mt)) mt = kNegInf;  // no live key and c == 0
-    tm.m_tile = mt;
-    tm.bp = __shfl_xor(mt, 32);
-  } else if constexpr (K == 6) {
-    const float mt = fmaxf(tm.m_tile, tm.bp);
-    tm.need = mt > m_run + 8.0f;  // lazy reference: moves only for a jump above 8
-    const float m_new = tm.need ? mt : m_run;
-    alpha = (m_new == m_run) ? 1.0f : exp2_fast(m_run - m_new);  // 0 when m_run was -inf
-    m_run = m_new;
-    tm.m_use = (m_run == kNegInf) ? 0.0f : m_run;
-    tm.rs[0] = 0.0f;
-    tm.rs[1] = 0.0f;
-  } else if constexpr (K >= 7 && K < 23) {  // probabilities of values 2(K-7), 2(K-7)+1
-#pragma unroll
-    for (int v = 2 * (K - 7); v < 2 * (K - 7) + 2; ++v) {
-      float p = exp2_fast(fmaf(s[v >> 4][v & 15], c, -tm.m_use));
-      if (MASK) p = live(v) ? p : 0.0f;
-      s[v >> 4][v & 15] = p;
-      tm.rs[v & 1] += p;
-    }
-  } else if constexpr (K >= 23 && K < 27) {  // bf16 P^T operand for K-step (b, s2) = K - 23
-    const int b = (K - 23) >> 1, s2 = (K - 23) & 1;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) pb[b][s2][j] = static_cast<__bf16>(s[b][s2 * 8 + j]);
-  } else if constexpr (K == 27) {
-    tm.rs[0] += tm.rs[1];
-    tm.bp = __shfl_xor(tm.rs[0], 32);
-  } else if constexpr (K == 29) {
-    const float pair = (threadIdx.x & 32) ? tm.bp + tm.rs[0] : tm.rs[0] + tm.bp;  // same order in both lanes
-    l_run = l_run * alpha + pair;
-  }
-}
-
-template <int D, int NM, int I, bool MASK, bool NEG>
-__device__ __forceinline__ void softmax_slot(f32x16_t (&s)[2], bf16x8_t (&pb)[2][2], SoftmaxTmp& tm, float& m_run,
-                                             float& l_run, float& alpha, float c, int lim) {
-  // micro-step k runs in MFMA slot (k * NM) / 32
-#define IKBO_MICRO(KK)                                                                        \
-  if constexpr ((KK) * NM / 32 == I) softmax_micro<KK, MASK, NEG>(s, pb, tm, m_run, l_run, alpha, c, lim);
-  IKBO_MICRO(0) IKBO_MICRO(1) IKBO_MICRO(2) IKBO_MICRO(3) IKBO_MICRO(4) IKBO_MICRO(5) IKBO_MICRO(6) IKBO_MICRO(7)
-  IKBO_MICRO(8) IKBO_MICRO(9) IKBO_MICRO(10) IKBO_MICRO(11) IKBO_MICRO(12) IKBO_MICRO(13) IKBO_MICRO(14)
-  IKBO_MICRO(15) IKBO_MICRO(16) IKBO_MICRO(17) IKBO_MICRO(18) IKBO_MICRO(19) IKBO_MICRO(20) IKBO_MICRO(21)
-  IKBO_MICRO(22) IKBO_MICRO(23) IKBO_MICRO(24) IKBO_MICRO(25) IKBO_MICRO(26) IKBO_MICRO(27) IKBO_MICRO(28)
-  IKBO_MICRO(29) IKBO_MICRO(30) IKBO_MICRO(31)
-#undef IKBO_MICRO
-}
-
-// LDS operands of MFMA slot i: QK slots (i < D/8) read one K fragment (key
-// block b = i & 1, K-step st = i >> 1); PV slots read two 4-key V^T pieces
-// (j = i - D/8: column block mb = j >> 2, key block b = (j >> 1) & 1, s2 = j & 1).
-template <int D>
-struct Operands {
-  u32x4_t k;
-  i16x4_t va, vb;
-};
-
-template <int D, int I>
-__device__ __forceinline__ void read_operands(Operands<D>& op, const uint16_t* __restrict__ Kn,
-                                              const uint16_t* __restrict__ Vp, const LaneOff<D>& lo) {
-  constexpr int NQ = D / 8;
-  if constexpr (I < NQ) {
-    constexpr int b = I & 1, st = I >> 1;
-    op.k = *reinterpret_cast<const u32x4_t*>(Kn + lo.k[st] + b * 32 * D);
-  } else {
-    constexpr int j = I - NQ, mb = j >> 2, b = (j >> 1) & 1, s2 = j & 1;
-    constexpr int disp = (b * 32 + 16 * s2) * D;
-    op.va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(Vp + lo.v[mb][0] + disp));
-    op.vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(Vp + lo.v[mb][1] + disp));
-  }
-}
-
-template <int D, int I>
-__device__ __forceinline__ void mfma_slot(const Operands<D>& op, const u32x4_t (&qf)[D / 16], f32x16_t (&s_nxt)[2],
-                                          const bf16x8_t (&p_prev)[2][2], f32x16_t (&oacc)[D / 32]) {
-  constexpr int NQ = D / 8;
-  if constexpr (I < NQ) {
-    constexpr int b = I & 1, st = I >> 1;
-    s_nxt[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(op.k), as_bf16x8(qf[st]),
-                                                       st == 0 ? f32x16_t{} : s_nxt[b], 0, 0, 0);
-  } else {
-    constexpr int j = I - NQ, mb = j >> 2, b = (j >> 1) & 1, s2 = j & 1;
-    const i16x8_t v8 = __builtin_shufflevector(op.va, op.vb, 0, 1, 2, 3, 4, 5, 6, 7);
-    oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, v8), p_prev[b][s2], oacc[mb],
-                                                      0, 0, 0);
-  }
-}
-
-// One iteration body: S(t+1) into s_nxt, O += V(t-1)^T P(t-1) (DO_PV), softmax
-// of S(t) into p_cur.  The instruction order is fixed slot by slot: slot i
-// issues the LDS reads of MFMA i + LA, then MFMA i, then its share of the
-// softmax micro-steps, and a scheduling fence keeps the slots apart, so the
-// matrix pipe runs while the VALU works on tile t.  Returns whether any lane
-// moved its softmax reference (then O must be scaled by alpha).
-template <int D, bool DO_PV, bool MASK, bool NEG>
-__device__ __forceinline__ bool pipe_body(PipeState<D>& ps, const uint16_t* __restrict__ Kn,
-                                          const uint16_t* __restrict__ Vp, const LaneOff<D>& lo,
-                                          const u32x4_t (&qf)[D / 16], f32x16_t (&s_cur)[2], f32x16_t (&s_nxt)[2],
-                                          const bf16x8_t (&p_prev)[2][2], bf16x8_t (&p_cur)[2][2], int lim, float c,
-                                          float& alpha) {
-  constexpr int NQ = D / 8;
-  constexpr int NM = NQ + (DO_PV ? D / 8 : 0);  // MFMA slots
-  constexpr int LA = 4;                         // operand reads run LA slots ahead
-  Operands<D> ring[LA + 1];
-  SoftmaxTmp tm;
-  const float m_before = ps.m_run;
-  alpha = 1.0f;
-  [&]<int... Is>(std::integer_sequence<int, Is...>) {
-    ((Is < LA && Is < NM ? read_operands<D, (Is < NM ? Is : 0)>(ring[Is % (LA + 1)], Kn, Vp, lo) : void()), ...);
-    ((
-         [&] {
-           constexpr int I = Is;
-           if constexpr (I + LA < NM) read_operands<D, I + LA>(ring[(I + LA) % (LA + 1)], Kn, Vp, lo);
-           mfma_slot<D, I>(ring[I % (LA + 1)], qf, s_nxt, p_prev, ps.oacc);
-           softmax_slot<D, NM, I, MASK, NEG>(s_cur, p_cur, tm, ps.m_run, ps.l_run, alpha, c, lim);
-           __builtin_amdgcn_sched_barrier(0);
-         }()),
-     ...);
-  }(std::make_integer_sequence<int, NM>{});
-  return __any(ps.m_run != m_before);
-}
-
-template <int D, int NR, bool NEG>
-__global__ __launch_bounds__(kThreads, 1) void ikbo_attn_bf16_pipe_kernel(AttnParams P) {
-  using T = Tile<D>;
-  constexpr int TE = T::elems;
-  static_assert(NR >= 3, "ring depth");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * NR * TE];  // NR K tiles, then NR V tiles
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 31, g = lane >> 5;
-  const int r_w = wave * 32 + n;
-
-  const uint16_t* __restrict__ Kg = static_cast<const uint16_t*>(P.k);
-  const uint16_t* __restrict__ Vg = static_cast<const uint16_t*>(P.v);
-  const int64_t row_stride = static_cast<int64_t>(P.H) * D;
-
-  int ld_row[T::loads], ld_chunk[T::loads];
-#pragma unroll
-  for (int r = 0; r < T::loads; ++r) {
-    const int u = tid + kThreads * r;
-    ld_row[r] = u / T::NCH;
-    ld_chunk[r] = (u % T::NCH) ^ (swz(ld_row[r]) & (T::NCH - 1));
-  }
-  const LaneOff<D> lo = lane_offsets<D>(lane);
-  const uint32_t lds_base = lds_address(smem);
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-
-  const int G = gridDim.x;
-  const int w = logical_wg();
-  for (int64_t pass = 0;; ++pass) {
-    const int64_t pos = deal_position(pass, w, G);
-    if (pos >= P.n_items) break;
-    const WorkItem it = P.items[pos];
-    const bool causal = it.kind == kKindSelf;
-    uint64_t t_start = 0, t_ready = 0, t_loop = 0;
-    if (P.trace) t_start = now_ticks();
-
-    const int nkv = it.k1 - it.k0;
-    const int ntl = (nkv + kBN - 1) / kBN;
-    const uint16_t* kbase = Kg + (static_cast<int64_t>(it.kv_base) + it.k0) * row_stride + it.h * D;
-    const uint16_t* vbase = Vg + (static_cast<int64_t>(it.kv_base) + it.k0) * row_stride + it.h * D;
-
-    // Copies of K (is_v = 0) or V tile j into its ring slot.
-    auto issue = [&](int j, int is_v) {
-      const uint32_t st = lds_base + static_cast<uint32_t>((is_v * NR + j % NR) * TE * 2);
-      const uint16_t* src = is_v ? vbase : kbase;
-#pragma unroll
-      for (int r = 0; r < T::loads; ++r) {
-        const int key = min(j * kBN + ld_row[r], nkv - 1);
-        copy16_to_lds(src + key * row_stride + ld_chunk[r] * 8,
-                      st + static_cast<uint32_t>((kThreads * r + 64 * wave_u) * 16));
-      }
-    };
-    // Virtual iteration i issues K(i + NR) and V(i + NR - 2) when they exist.
-    auto issue_iter = [&](int i) {
-      if (i + NR < ntl) issue(i + NR, 0);
-      if (i + NR - 2 >= 0 && i + NR - 2 < ntl) issue(i + NR - 2, 1);
-    };
-    // Copies issued after those that iteration t needs (K(t+1), V(t-1), both
-    // from virtual iteration t+1-NR), in units of T::loads.
-    auto later_copies = [&](int t) {
-      int k = 0;
-#pragma unroll
-      for (int i = t + 2 - NR; i <= t - 1; ++i) k += (i + NR < ntl) + (i + NR - 2 < ntl);
-      return k;
-    };
-
-#pragma unroll
-    for (int i = -NR; i < 0; ++i) issue_iter(i);
-
-    int64_t qrow = -1;
-    if (r_w < it.nrows) {
-      const int r = it.row0 + r_w;
-      if (!causal) {
-        const int cand = P.cand_perm[it.row_base + r / P.n_q];
-        qrow = static_cast<int64_t>(cand) * P.n_q + r % P.n_q;
-      } else {
-        qrow = static_cast<int64_t>(it.row_base) + r;
-      }
-    }
-    u32x4_t qf[D / 16];
-    {
-      const uint16_t* qb = static_cast<const uint16_t*>(causal ? P.q_user : P.q_cand);
-      const uint16_t* qp = qb + (qrow < 0 ? 0 : (qrow * P.H + it.h) * D) + g * 8;
-#pragma unroll
-      for (int st = 0; st < D / 16; ++st)
-        qf[st] = (qrow < 0) ? u32x4_t{0, 0, 0, 0} : *reinterpret_cast<const u32x4_t*>(qp + st * 16);
-    }
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) asm volatile("" ::"v"(qf[st]));  // also retires the prologue copies
-    if (P.trace) t_ready = now_ticks();
-
-    PipeState<D> ps;
-#pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) ps.oacc[mb] = f32x16_t{};
-    ps.m_run = kNegInf;
-    ps.l_run = 0.0f;
-    const int row_tok = it.row0 + r_w;
-    const int wave_first_tok = it.row0 + wave * 32;
-    const bool wave_has_rows = wave * 32 < it.nrows;
-    const float c = P.scale_log2;
-
-    if (ntl > 0) {
-      __syncthreads();  // prologue copies of every thread are in LDS
-      f32x16_t sa[2], sb[2];
-      bf16x8_t pa[2][2], pb[2][2];
-      if (wave_has_rows) qk_tile<D>(smem, lo, qf, sa);  // S(0): K slot 0
-
-      // Iteration t: S(t) in s_cur, P(t-1) in p_prev; see pipe_body.
-      auto iter = [&](int t, auto do_pv, f32x16_t (&s_cur)[2], f32x16_t (&s_nxt)[2], bf16x8_t (&p_prev)[2][2],
-                      bf16x8_t (&p_cur)[2][2]) {
-        constexpr bool DPV = decltype(do_pv)::value;
-        // K(t+1), V(t-1) in LDS (at t = 0 the prologue wait covered them); the
-        // slots of K(t) and V(t-2), read in iteration t-1, are free.
-        if (t > 0) wait_vmcnt_steps<T::loads, 2 * (NR - 2)>(later_copies(t));
-        __syncthreads();
-        issue_iter(t);
-        // At t = ntl-1, S(t+1) is computed from a stale K slot and discarded.
-        const uint16_t* Kn = smem + ((t + 1) % NR) * TE;
-        const uint16_t* Vp = smem + (NR + (t + NR - 1) % NR) * TE;
-        const int key_base = it.k0 + t * kBN;
-        const bool mask = (key_base + kBN > it.k1) || (causal && key_base + kBN - 1 > wave_first_tok);
-        // live keys of this lane: offsets (from key_base, less g*4) below lim
-        const int lim = min(it.k1 - key_base, causal ? row_tok - key_base + 1 : kBN) - g * 4;
-        float alpha = 1.0f;
-        bool moved = false;
-        if (!wave_has_rows) {
-          // no row of this wave in the tile: only the ring bookkeeping runs
-        } else if (mask)
-          moved = pipe_body<D, DPV, true, NEG>(ps, Kn, Vp, lo, qf, s_cur, s_nxt, p_prev, p_cur, lim, c, alpha);
-        else
-          moved = pipe_body<D, DPV, false, NEG>(ps, Kn, Vp, lo, qf, s_cur, s_nxt, p_prev, p_cur, lim, c, alpha);
-        if (moved) {
-#pragma unroll
-          for (int mb = 0; mb < D / 32; ++mb) ps.oacc[mb] *= alpha;
-        }
-      };
-      using no_pv = std::integral_constant<bool, false>;
-      using with_pv = std::integral_constant<bool, true>;
-      iter(0, no_pv{}, sa, sb, pb, pa);
-      int t = 1;
-      for (; t + 1 < ntl; t += 2) {
-        iter(t, with_pv{}, sb, sa, pa, pb);
-        iter(t + 1, with_pv{}, sa, sb, pb, pa);
-      }
-      if (t < ntl) {
-        iter(t, with_pv{}, sb, sa, pa, pb);
-        ++t;
-      }
-      // Tail: O += V(ntl-1)^T P(ntl-1).
-      wait_vmcnt<0>();
-      __syncthreads();
-      const uint16_t* Vl = smem + (NR + (ntl - 1) % NR) * TE;
-      if (!wave_has_rows) {
-      } else if ((ntl - 1) & 1) {
-        pv_tile<D>(Vl, lo, pb, ps.oacc);
-      } else {
-        pv_tile<D>(Vl, lo, pa, ps.oacc);
-      }
-    }
-    __syncthreads();  // every slot is free before the next item's copies
-    if (P.trace) t_loop = now_ticks();
-    write_tile_rows<D>(P, it, ps.oacc, ps.m_run, ps.l_run, qrow, causal, r_w, g);
-    wait_vmcnt<0>();  // epilogue stores retire before the next item's copies are counted
-    if (P.trace && tid == 0) {
-      uint64_t* tr = P.trace + pos * 6;
-      tr[0] = (static_cast<uint64_t>(w) << 32) | hw_place();
-      tr[1] = t_start;
-      tr[2] = t_ready;
-      tr[3] = t_loop;
-      tr[4] = now_ticks();
-      tr[5] = static_cast<uint64_t>(ntl);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // split-KV merge: block (group, row block); thread -> (row, 4 d)
 // ---------------------------------------------------------------------------
 //
@@ -1425,29 +912,6 @@ hipError_t launch_attn_bf16_w8(const AttnParams& p, int d, int grid, hipStream_t
     case 32: IKBO_LAUNCH((ikbo_attn_bf16_w8_kernel<32, 2>), dim3(grid), dim3(512), p); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_bf16_pipe(const AttnParams& p, int d, int grid, bool neg_scale, hipStream_t stream,
-                                 hipEvent_t* ev) {
-  if (grid <= 0 || p.n_items <= 0) return hipSuccess;
-#define IKBO_LAUNCH_PIPE(DD, NEG) IKBO_LAUNCH((ikbo_attn_bf16_pipe_kernel<DD, 4, NEG>), dim3(grid), dim3(kThreads), p)
-  if (neg_scale) {
-    switch (d) {
-      case 128: IKBO_LAUNCH_PIPE(128, true); break;
-      case 64: IKBO_LAUNCH_PIPE(64, true); break;
-      case 32: IKBO_LAUNCH_PIPE(32, true); break;
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    switch (d) {
-      case 128: IKBO_LAUNCH_PIPE(128, false); break;
-      case 64: IKBO_LAUNCH_PIPE(64, false); break;
-      case 32: IKBO_LAUNCH_PIPE(32, false); break;
-      default: return hipErrorInvalidValue;
-    }
-  }
-#undef IKBO_LAUNCH_PIPE
   return hipGetLastError();
 }
 

@@ -39,10 +39,12 @@ SIGNATURES = {
     "ikbo_last_error": (ctypes.c_char_p, []),
     "ikbo_group_csr": (ctypes.c_int, [_IP, _I, _I, _I, _I, _IP, _IP, _IP, _IP, _I, _IP]),
     "ikbo_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P]),
+    "ikbo_attn_fwd_f32": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P]),
+    "ikbo_attn_fwd_mt": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _I, _I]),
     "ikbo_attn_fwd_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P]),
     "ikbo_self_target_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P]),
-    "ikbo_attn_fwd_materialized": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P]),
-    "ikbo_plan_create": (ctypes.c_int, [ctypes.POINTER(_P)]),
+    "ikbo_attn_fwd_materialized": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _I, _I]),
+    "ikbo_plan_create": (ctypes.c_int, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, ctypes.POINTER(_P)]),
     "ikbo_plan_build": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "ikbo_attn_fwd_planned": (ctypes.c_int, [_P, _P, _P, _P, _P, _F, _P, _P, _P]),
     "ikbo_plan_destroy": (None, [_P]),
@@ -217,17 +219,28 @@ def ikbo_group_csr(cand_to_user_host: np.ndarray, n_users: int, n_q: int, bm: in
     return counts[:n_users], offs, perm[:n_cand], tiles[:nt.value]
 
 
+def _total_len(user_offsets, n_users) -> Optional[int]:
+    """user_offsets[n_users] of a device offsets tensor (one 4-byte copy; the
+    device-mapping calls synchronise on the mapping anyway), or None for a raw
+    pointer or an offsets tensor too short to hold it."""
+    if user_offsets is None or isinstance(user_offsets, int) or user_offsets.numel() < n_users + 1 or n_users < 0:
+        return None
+    return int(user_offsets[n_users].item())
+
+
 def _check_common(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, n_q, H, d, es, out):
+    """Checks every tensor against the extent the call touches.  Returns the
+    total key count user_offsets[n_users] when it could be read, else None."""
     rows = n_cand * n_q * H * d * es
     _need(q_cand, rows, "q_cand", es)
     _need(out, rows, "out", es)
-    _need(k_user, 0, "k_user", es)
-    _need(v_user, 0, "v_user", es)
-    if k_user is not None and v_user is not None and not isinstance(k_user, int) and not isinstance(v_user, int):
-        if k_user.numel() != v_user.numel():
-            raise _bad("k_user and v_user differ in size")
     _need(user_offsets, (n_users + 1) * 4, "user_offsets", 4)
     _need(cand_to_user, n_cand * 4, "cand_to_user", 4)
+    total = _total_len(user_offsets, n_users)
+    kv = 0 if total is None or total < 0 else total * H * d * es
+    _need(k_user, kv, "k_user", es)
+    _need(v_user, kv, "v_user", es)
+    return total
 
 
 def ikbo_attn_fwd(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, H, d, scale, out,
@@ -236,6 +249,22 @@ def ikbo_attn_fwd(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n
     return _check(load_library().ikbo_attn_fwd(
         _ptr(q_cand), _ptr(k_user), _ptr(v_user), _ptr(user_offsets), _ptr(cand_to_user),
         n_users, n_cand, H, d, float(scale), _ptr(out), _stream(stream)))
+
+
+def ikbo_attn_fwd_f32(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, H, d, scale, out,
+                      stream=None) -> int:
+    _check_common(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, 1, H, d, 4, out)
+    return _check(load_library().ikbo_attn_fwd_f32(
+        _ptr(q_cand), _ptr(k_user), _ptr(v_user), _ptr(user_offsets), _ptr(cand_to_user),
+        n_users, n_cand, H, d, float(scale), _ptr(out), _stream(stream)))
+
+
+def ikbo_attn_fwd_mt(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, H, d, scale, out,
+                     stream=None, n_q=1, dtype=IKBO_DTYPE_BF16) -> int:
+    _check_common(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, n_q, H, d, _es(dtype), out)
+    return _check(load_library().ikbo_attn_fwd_mt(
+        _ptr(q_cand), _ptr(k_user), _ptr(v_user), _ptr(user_offsets), _ptr(cand_to_user),
+        n_users, n_cand, H, d, float(scale), _ptr(out), _stream(stream), n_q, dtype))
 
 
 def ikbo_attn_fwd_ex(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, n_q, H, d, scale,
@@ -249,28 +278,38 @@ def ikbo_attn_fwd_ex(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users
 def ikbo_self_target_fwd(q_user, q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, H, d,
                          scale, dtype, out_user, out_cand, stream=None) -> int:
     es = _es(dtype)
-    _check_common(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, 1, H, d, es, out_cand)
-    if k_user is not None and not isinstance(k_user, int):
-        kv = k_user.numel() * es
-        _need(q_user, kv, "q_user", es)
-        _need(out_user, kv, "out_user", es)
+    total = _check_common(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, 1, H, d, es, out_cand)
+    kv = 0 if total is None or total < 0 else total * H * d * es
+    _need(q_user, kv, "q_user", es)
+    _need(out_user, kv, "out_user", es)
     return _check(load_library().ikbo_self_target_fwd(
         _ptr(q_user), _ptr(q_cand), _ptr(k_user), _ptr(v_user), _ptr(user_offsets), _ptr(cand_to_user),
         n_users, n_cand, H, d, float(scale), dtype, _ptr(out_user), _ptr(out_cand), _stream(stream)))
 
 
-def ikbo_attn_fwd_materialized(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, n_q, H, d,
-                               scale, dtype, out, stream=None) -> int:
+def ikbo_attn_fwd_materialized(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, H, d, scale,
+                               out, stream=None, n_q=1, dtype=IKBO_DTYPE_BF16) -> int:
     _check_common(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, n_q, H, d, _es(dtype), out)
     return _check(load_library().ikbo_attn_fwd_materialized(
         _ptr(q_cand), _ptr(k_user), _ptr(v_user), _ptr(user_offsets), _ptr(cand_to_user),
-        n_users, n_cand, n_q, H, d, float(scale), dtype, _ptr(out), _stream(stream)))
+        n_users, n_cand, H, d, float(scale), _ptr(out), _stream(stream), n_q, dtype))
 
 
-def ikbo_plan_create() -> int:
+def ikbo_plan_create(user_offsets_host, cand_to_user_host, n_users, n_cand, n_q, H, d, dtype, with_self=0,
+                     stream=None) -> int:
+    """A plan built for the request the host mapping arrays describe."""
+    offs = np.ascontiguousarray(user_offsets_host, dtype=np.int32)
+    c2u = np.ascontiguousarray(cand_to_user_host, dtype=np.int32)
     h = _P()
-    _check(load_library().ikbo_plan_create(ctypes.byref(h)))
+    _check(load_library().ikbo_plan_create(_host_i32(offs), _host_i32(c2u), n_users, n_cand, n_q, H, d, dtype,
+                                           int(with_self), _stream(stream), ctypes.byref(h)))
+    _PLAN_DIMS[h.value] = _plan_dims(offs, n_users, n_cand, n_q, H, d, dtype, with_self)
     return h.value
+
+
+def _plan_dims(offs, n_users, n_cand, n_q, H, d, dtype, with_self):
+    es = _es(dtype)
+    return (es, n_cand * n_q * H * d * es, int(offs[n_users]) * H * d * es, bool(with_self))
 
 
 def ikbo_plan_build(plan, user_offsets_host, cand_to_user_host, n_users, n_cand, n_q, H, d, dtype,
@@ -280,8 +319,7 @@ def ikbo_plan_build(plan, user_offsets_host, cand_to_user_host, n_users, n_cand,
     _PLAN_DIMS.pop(plan, None)
     rc = _check(load_library().ikbo_plan_build(
         plan, _host_i32(offs), _host_i32(c2u), n_users, n_cand, n_q, H, d, dtype, int(with_self), _stream(stream)))
-    es = _es(dtype)
-    _PLAN_DIMS[plan] = (es, n_cand * n_q * H * d * es, int(offs[n_users]) * H * d * es, bool(with_self))
+    _PLAN_DIMS[plan] = _plan_dims(offs, n_users, n_cand, n_q, H, d, dtype, with_self)
     return rc
 
 

@@ -112,7 +112,29 @@ int ikbo_attn_fwd(const void* q_cand, const void* k_user, const void* v_user,
                   int32_t n_users, int32_t n_cand, int32_t H, int32_t d, float scale,
                   void* out, void* stream);
 
-/* As ikbo_attn_fwd, with n_q query tokens per candidate and a dtype. */
+/*
+ * As ikbo_attn_fwd with fp32 q, k, v and out (the same arguments; fp32
+ * accumulation and exponentials, one query token per candidate).
+ */
+int ikbo_attn_fwd_f32(const void* q_cand, const void* k_user, const void* v_user,
+                      const int32_t* user_offsets, const int32_t* cand_to_user,
+                      int32_t n_users, int32_t n_cand, int32_t H, int32_t d, float scale,
+                      void* out, void* stream);
+
+/*
+ * Multi-target form: as ikbo_attn_fwd, followed by n_q (query tokens per
+ * candidate, >= 1) and dtype.  q_cand and out are [n_cand, n_q, H, d]; each
+ * query token of a candidate attends on its own over the whole sequence of
+ * the candidate's user (IKBO blog section 3.2: several query tokens per
+ * candidate).  ikbo_attn_fwd_ex is the same call with n_q and dtype placed
+ * next to the other sizes.
+ */
+int ikbo_attn_fwd_mt(const void* q_cand, const void* k_user, const void* v_user,
+                     const int32_t* user_offsets, const int32_t* cand_to_user,
+                     int32_t n_users, int32_t n_cand, int32_t H, int32_t d, float scale,
+                     void* out, void* stream, int32_t n_q, int32_t dtype);
+
+/* As ikbo_attn_fwd_mt, with n_q and dtype next to the other sizes. */
 int ikbo_attn_fwd_ex(const void* q_cand, const void* k_user, const void* v_user,
                      const int32_t* user_offsets, const int32_t* cand_to_user,
                      int32_t n_users, int32_t n_cand, int32_t n_q, int32_t H, int32_t d,
@@ -136,21 +158,23 @@ int ikbo_self_target_fwd(const void* q_user, const void* q_cand, const void* k_u
  * before dispatch that the IKBO blog section 1.4 and Fig. 10 (left) describe).  A copy kernel first writes a
  * per-candidate copy of its user's K and V into a library-owned buffer
  * [sum_c L_{u(c)}, H, d]; the same attention kernel then runs with the
- * identity mapping.  Output equals ikbo_attn_fwd_ex.  Candidates are processed
+ * identity mapping.  Arguments as ikbo_attn_fwd_mt; output equals it.  Candidates are processed
  * in chunks so the broadcast buffer stays within IKBO_BCAST_MAX_GB
  * (environment, default 32).  Synchronises like ikbo_attn_fwd.
  */
 int ikbo_attn_fwd_materialized(const void* q_cand, const void* k_user, const void* v_user,
                                const int32_t* user_offsets, const int32_t* cand_to_user,
-                               int32_t n_users, int32_t n_cand, int32_t n_q, int32_t H,
-                               int32_t d, float scale, int32_t dtype, void* out, void* stream);
+                               int32_t n_users, int32_t n_cand, int32_t H, int32_t d, float scale,
+                               void* out, void* stream, int32_t n_q, int32_t dtype);
 
 /*
  * Plans: the host grouping and work list, built from HOST copies of the
  * mapping (as an inference runtime holds them), then reused by launches
  * without any host-device synchronisation.
  *
- * ikbo_plan_create: allocates an empty plan bound to the current device.
+ * ikbo_plan_create: allocates a plan bound to the current device and builds
+ *   it for the request the host mapping describes (as ikbo_plan_build; on
+ *   error no plan is returned).
  * ikbo_plan_build: validates, groups candidates (ikbo_group_csr) and builds
  *   the load-balanced work list over (user, head, row tile, key chunk) in a
  *   pinned host buffer that the kernels read in place (no copy is enqueued).
@@ -164,12 +188,14 @@ int ikbo_attn_fwd_materialized(const void* q_cand, const void* k_user, const voi
  *   Launches of one plan share its split-KV workspace and work-list buffers:
  *   keep them on one stream; a launch on another stream than the plan's
  *   previous one first waits, on the host, for that stream to drain.  Split
- *   groups are merged by a second kernel with the log-sum-exp rule of the TLX
- *   attention post's split-K section, in chunk order, so results do not
- *   depend on the schedule or the launch grid.
+ *   groups are merged by a second kernel with the log-sum-exp rule of the
+ *   Flash-Decoding split-KV reduction (AI-infra guide, section 4.6.4), in
+ *   chunk order, so results do not depend on the schedule or the launch grid.
  * ikbo_plan_destroy: frees the plan after synchronising its device.
  */
-int ikbo_plan_create(void** plan);
+int ikbo_plan_create(const int32_t* user_offsets_host, const int32_t* cand_to_user_host,
+                     int32_t n_users, int32_t n_cand, int32_t n_q, int32_t H, int32_t d,
+                     int32_t dtype, int32_t with_self, void* stream, void** plan);
 int ikbo_plan_build(void* plan, const int32_t* user_offsets_host, const int32_t* cand_to_user_host,
                     int32_t n_users, int32_t n_cand, int32_t n_q, int32_t H, int32_t d,
                     int32_t dtype, int32_t with_self, void* stream);
@@ -381,8 +407,8 @@ void ikbo_mx_destroy(void* mx);
  * info[0] work items, [1] grid of the persistent launch, [2] split groups,
  * [3] partial-result slots, [4] bytes of the split-KV workspace, [5] target
  * row tiles, [6] self row tiles, [7] compute units, [8] kernel (0 fp32, 1 bf16
- * eight-wave, 2 bf16 4-wave, 3 bf16 software-pipelined, 4 bf16 4-wave visiting
- * each item's key tiles last to first).  Writes the first min(n_info, 9) values.
+ * eight-wave, 2 bf16 4-wave, 4 bf16 4-wave visiting each item's key tiles last
+ * to first).  Writes the first min(n_info, 9) values.
  */
 int ikbo_plan_info(void* plan, int64_t* info, int32_t n_info);
 

@@ -51,7 +51,7 @@ import math
 import numpy as np
 
 __all__ = ["e4m3_decode", "e8m0_decode", "e4m3_round", "p_block_exponent", "v_block_offsets", "dequantize_rows",
-           "dequantize_v", "target_attention_mxfp8", "flops_target"]
+           "dequantize_v", "target_attention_mxfp8"]
 
 E4M3_MAX = 448.0
 P_BLOCK = 32
@@ -166,10 +166,3 @@ def target_attention_mxfp8(q_codes, q_scales, k_codes, k_scales, v_codes, v_scal
                 p = np.exp2(x - m)
                 out[c, r, h, :] = (_quantize_p(p) @ vc[:, h, :]) / p.sum()
     return out
-
-
-def flops_target(counts, lengths, n_q: int, H: int, d: int) -> float:
-    """The forward's two products, 4 * n_q * L_u * d per candidate and head."""
-    c = np.asarray(counts, dtype=np.float64)
-    L = np.asarray(lengths, dtype=np.float64)
-    return 4.0 * n_q * d * H * float(np.dot(c, L))

@@ -177,3 +177,22 @@ def test_flop_count_is_the_five_products():
     assert B.flops_target_bwd([1], [1], w.n_q, 1, w.d) == per
     total = B.flops_target_bwd(w.counts, w.lengths, w.n_q, w.H, w.d)
     assert total == pytest.approx(2.5 * w.flops()["target"])
+
+
+def test_per_user_calls_assemble_the_whole_call():
+    """Users do not interact: calling the oracle once per user (that user's
+    key/value rows, offsets [0, L] and its candidates) and placing the results
+    gives the whole call's gradients bit for bit (the same candidate order
+    within each user, so the same sums in the same order)."""
+    w = _case()
+    q, k, v, do = w.values("q_cand"), w.values("k_user"), w.values("v_user"), w.values("dout")
+    whole = B.target_attention_bwd(q, k, v, do, w.user_offsets, w.cand_to_user, w.scale)
+    dq, dk, dv = (np.zeros_like(x) for x in whole)
+    for u in range(w.n_users):
+        cands = np.flatnonzero(w.cand_to_user == u)
+        a, b = int(w.user_offsets[u]), int(w.user_offsets[u + 1])
+        gq, gk, gv = B.target_attention_bwd(q[cands], k[a:b], v[a:b], do[cands], np.array([0, b - a], np.int32),
+                                            np.zeros(len(cands), np.int32), w.scale)
+        dq[cands], dk[a:b], dv[a:b] = gq, gk, gv
+    for x, y in zip((dq, dk, dv), whole):
+        assert np.array_equal(x, y)

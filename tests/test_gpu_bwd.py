@@ -19,7 +19,7 @@ from oracle import ikbo_bwd_oracle as B
 from oracle import ikbo_oracle as O
 from workloads import add_output_grad, f32_to_bf16_bits, make_bwd_workload, make_custom
 
-from gpu_helpers import dev_tensor, say, to_f64
+from gpu_helpers import dev_tensor, oracle_in_chunks, say, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -94,6 +94,58 @@ def test_bwd_edges(i):
         _close(g, r, name)
 
 
+def _oracle_by_user(w):
+    """The backward oracle evaluated one user at a time: each call gets one
+    user's key and value rows and that user's candidates (users do not interact,
+    so the assembled result is the whole call's; pinned on the CPU), the calls
+    running side by side in a thread pool."""
+    q, k, v, do = w.values("q_cand"), w.values("k_user"), w.values("v_user"), w.values("dout")
+    offs, c2u = w.user_offsets, w.cand_to_user
+
+    def users(us):
+        res = []
+        for u in us:
+            cands = np.flatnonzero(c2u == u)
+            a, b = int(offs[u]), int(offs[u + 1])
+            g = B.target_attention_bwd(q[cands], k[a:b], v[a:b], do[cands], np.array([0, b - a], np.int32),
+                                       np.zeros(len(cands), np.int32), w.scale)
+            res.append((u, cands, g))
+        return res
+
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for part in oracle_in_chunks(users, range(w.n_users)):
+        for u, cands, (gq, gk, gv) in part:
+            a, b = int(offs[u]), int(offs[u + 1])
+            dq[cands] = gq
+            dk[a:b] = gk
+            dv[a:b] = gv
+    return dq, dk, dv
+
+
+@pytest.mark.timeout(900)
+def test_bwd_large_request_full():
+    """The backward at the large request it is benchmarked on (10,000
+    candidates over 150 users, 4 query tokens, 8 heads): every element of dq,
+    dk and dv against the oracle."""
+    w = make_bwd_workload("c4_large")
+    say("case bwd c4_large (full tensors)")
+    q, k, v = w.values("q_cand"), w.values("k_user"), w.values("v_user")
+
+    def fwd(cands):
+        return O.target_attention(q, k, v, w.user_offsets, w.cand_to_user, w.scale, cands=cands)
+
+    out = np.concatenate(oracle_in_chunks(fwd, range(w.n_cand)), axis=0)
+    out_bits = f32_to_bf16_bits(out.astype(np.float32)).reshape(out.shape)
+    del out
+    got = _run(w, out_bits)
+    say("  gradients computed; oracle by user")
+    ref = _oracle_by_user(w)
+    for g, r, name in zip(got, ref, ("dq", "dk", "dv")):
+        _close(g, r, name)
+
+
 def test_bwd_single_key_users():
     """One key: dq and dk vanish up to the rounding of dP - D; dv_0 sums dout."""
     w = _custom(3400, (1, 1, 40), (6, 3, 2), n_q=2, H=2)
@@ -115,6 +167,32 @@ def test_bwd_typical_request_full():
     ref = _oracle(w)
     for g, r, name in zip(got, ref, ("dq", "dk", "dv")):
         _close(g, r, name)
+
+
+def test_bwd_no_keys_at_all():
+    """Every user has zero keys but there are candidates: the forward output is
+    the constant 0, so every query-gradient row must be written as zero (the
+    prefilled value must not survive) and there is no key gradient to write."""
+    import torch
+    import broadcast_free_target_amd as ikbo
+    w = _custom(3450, (0, 0, 0), (3, 2, 4), n_q=2, H=2)
+    say("case bwd no keys at all")
+    assert w.total_len == 0
+    t = {n: dev_tensor(w.raw(n), "bf16") for n in ("q_cand", "dout")}
+    out = torch.zeros_like(t["q_cand"])
+    dq = torch.full_like(t["q_cand"], 7.0)
+    empty = torch.empty((0, w.H, w.d), dtype=torch.bfloat16, device="cuda")
+    h = ikbo.ikbo_bwd_create()
+    try:
+        ikbo.ikbo_attn_bwd(h, w.user_offsets, w.cand_to_user, w.n_users, w.n_cand, w.n_q, w.H, w.d, w.scale,
+                           t["q_cand"], empty, empty, out, t["dout"], dq, torch.empty_like(empty),
+                           torch.empty_like(empty))
+        torch.cuda.synchronize()
+    finally:
+        ikbo.ikbo_bwd_destroy(h)
+    ref_dq = _oracle(w)[0]
+    assert np.all(ref_dq == 0.0)
+    assert torch.count_nonzero(dq).item() == 0
 
 
 def test_bwd_repeatable_and_handle_reuse():

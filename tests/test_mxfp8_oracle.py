@@ -247,7 +247,19 @@ def test_planted_mistakes_fail_the_brute_force(mistake):
     assert worst > 1e-3, worst
 
 
-def test_flop_count():
-    w = make_mxfp8("mx_c2_typical")
-    assert M.flops_target(w.counts, w.lengths, w.n_q, w.H, w.d) == 4.0 * w.H * w.d * float(
-        np.dot(w.counts, w.lengths))
+def test_per_user_calls_assemble_the_whole_call():
+    """Users do not interact: one call per user (its candidates, its key and
+    value rows, its value-scale blocks, offsets [0, L]) placed back together
+    gives the whole call's output bit for bit."""
+    w = make_mxfp8("mx_tiny")
+    whole = M.target_attention_mxfp8(*w.arrays(), w.user_offsets, w.cand_to_user, w.scale)
+    vbo = M.v_block_offsets(w.user_offsets)
+    out = np.zeros_like(whole)
+    for u in range(w.n_users):
+        cands = np.flatnonzero(w.cand_to_user == u)
+        a, b = int(w.user_offsets[u]), int(w.user_offsets[u + 1])
+        out[cands] = M.target_attention_mxfp8(w.q_codes[cands], w.q_scales[cands], w.k_codes[a:b],
+                                              w.k_scales[a:b], w.v_codes[a:b], w.v_scales[vbo[u]:vbo[u + 1]],
+                                              np.array([0, b - a], np.int32), np.zeros(len(cands), np.int32),
+                                              w.scale)
+    assert np.array_equal(out, whole)
