@@ -20,21 +20,168 @@
 #include <vector>
 
 #include "ikbo.h"
+#include "ikbo_api_attn.h"
 #include "ikbo_api_common.h"
 #include "ikbo_kernels.h"
 #include "ikbo_plan.h"
 
 namespace ikbo_host {
 thread_local std::string g_last_error;
+
+using ikbo::HostPlan;
+using ikbo::PlanParams;
+using ikbo::WorkItem;
+
+// Depth of the bf16 kernel's HBM -> LDS ring (IKBO_STAGES overrides; 2, 3 or 4).
+int bf16_stages() {
+  const int s = env_int("IKBO_STAGES", ikbo::kBf16DefaultStages);
+  return (s == 2 || s == 3 || s == 4) ? s : ikbo::kBf16DefaultStages;
+}
+
+// bf16 kernel variants: the eight-wave kernel (one per CU, two waves per
+// SIMD) and the 4-wave kernel (two resident per CU).  By default a build plans
+// for the eight-wave kernel and keeps it when every workgroup gets at most one
+// item; otherwise it plans again for the 4-wave kernel, whose two independent
+// workgroups per CU keep the SIMDs busier over many items.  IKBO_KERNEL =
+// w8 | w4 forces a variant; w4r is the 4-wave kernel visiting each item's key
+// tiles last to first (the reverse-order variant of the TLX attention post's
+// persistent kernel).  The variant codes are in ikbo_api_attn.h.
+int bf16_variant() {
+  const char* s = std::getenv("IKBO_KERNEL");
+  if (s && std::strcmp(s, "w4r") == 0) return kVariantW4R;
+  if (s && std::strcmp(s, "w4") == 0) return kVariantW4;
+  if (s && std::strcmp(s, "w8") == 0) return kVariantW8;
+  return kVariantAuto;
+}
+
+PlanParams params_for(int n_cu, int32_t dtype, int variant) {
+  PlanParams pp;
+  if (dtype == IKBO_DTYPE_BF16 && variant != kVariantW4 && variant != kVariantW4R) {
+    // one resident workgroup per CU; the 8-wave kernel's chunks are whole ring stages
+    pp.bm = ikbo::kBf16TileRows;
+    pp.bn = (variant == kVariantW8 ? 2 : 1) * ikbo::kBf16TileKeys;
+    pp.grid_slots = std::max(1, n_cu);
+    pp.min_chunk = 256;
+    pp.allow_split = true;
+    pp.single_pass = true;
+  } else if (dtype == IKBO_DTYPE_BF16) {
+    pp.bm = ikbo::kBf16TileRows;
+    pp.bn = ikbo::kBf16TileKeys;
+    pp.grid_slots = std::max(1, n_cu * (bf16_stages() == 2 ? 2 : 1));
+    pp.min_chunk = 256;
+    pp.allow_split = true;
+  } else {
+    pp.bm = ikbo::kF32TileRows;
+    pp.bn = ikbo::kF32TileKeys;
+    pp.grid_slots = std::max(1, n_cu * 4);
+    pp.allow_split = false;
+  }
+  // Test and tuning overrides.  IKBO_GRID_WGS changes only the launched grid;
+  // IKBO_SPLIT_SLOTS and IKBO_MIN_CHUNK change how key ranges are split.
+  pp.grid_slots = std::max(1, env_int("IKBO_SPLIT_SLOTS", pp.grid_slots));
+  pp.launch_grid = std::max(0, env_int("IKBO_GRID_WGS", 0));
+  pp.min_chunk = std::max(pp.bn, env_int("IKBO_MIN_CHUNK", pp.min_chunk));
+  if (env_int("IKBO_NO_SPLIT", 0)) pp.allow_split = false;
+  return pp;
+}
+
+int check_dims(int32_t n_users, int32_t n_cand, int32_t n_q, int32_t H, int32_t d, int32_t dtype) {
+  if (n_users < 0 || n_cand < 0) return fail(IKBO_ERR_INVALID_ARG, "n_users and n_cand must be >= 0");
+  if (H < 1) return fail(IKBO_ERR_INVALID_ARG, "H must be >= 1");
+  if (n_q < 1) return fail(IKBO_ERR_INVALID_ARG, "n_q must be >= 1");
+  if (dtype != IKBO_DTYPE_BF16 && dtype != IKBO_DTYPE_F32) return fail(IKBO_ERR_UNSUPPORTED, "dtype");
+  if (d != 32 && d != 64 && d != 128) return fail(IKBO_ERR_UNSUPPORTED, "head dim must be 32, 64 or 128");
+  if (n_cand > 0 && n_users == 0) return fail(IKBO_ERR_BAD_MAPPING, "candidates present but n_users == 0");
+  return IKBO_OK;
+}
+
+// Plans one request: validation, grouping and the work list for the eight-wave
+// kernel, or, when that plan needs more items than there are CUs, for the
+// 4-wave kernel.  allow_split = false keeps every key range whole.
+int plan_request(int n_cu, const int32_t* offs, const int32_t* c2u, int32_t n_users, int32_t n_cand, int32_t n_q,
+                 int32_t H, int32_t d, int32_t dtype, int32_t with_self, bool allow_split, HostPlan* hp,
+                 int* variant_out) {
+  int rc = check_dims(n_users, n_cand, n_q, H, d, dtype);
+  if (rc != IKBO_OK) return rc;
+  if (!offs || (n_cand > 0 && !c2u)) return fail(IKBO_ERR_INVALID_ARG, "null host mapping");
+  std::string err;
+  // Split partials name their output row as row * H + h in an int32.
+  const int64_t out_units = std::max<int64_t>(static_cast<int64_t>(n_cand) * n_q, with_self ? offs[n_users] : 0) * H;
+  const bool split_ok = allow_split && out_units < std::numeric_limits<int32_t>::max();
+  const int forced = bf16_variant();
+  int variant = forced == kVariantAuto ? kVariantW8 : forced;
+  PlanParams pp = params_for(n_cu, dtype, variant);
+  if (!split_ok) pp.allow_split = false;
+  rc = ikbo::build_plan(offs, c2u, n_users, n_cand, n_q, H, with_self != 0, pp, hp, &err);
+  if (rc != ikbo::kOk) return fail(rc, err);
+  if (dtype == IKBO_DTYPE_BF16 && forced == kVariantAuto && hp->items.size() > static_cast<size_t>(n_cu)) {
+    variant = kVariantW4;
+    pp = params_for(n_cu, dtype, variant);
+    if (!split_ok) pp.allow_split = false;
+    rc = ikbo::build_plan(offs, c2u, n_users, n_cand, n_q, H, with_self != 0, pp, hp, &err);
+    if (rc != ikbo::kOk) return fail(rc, err);
+  }
+  *variant_out = variant;
+  return IKBO_OK;
+}
+
+// Checks the tensors of one launch against the sizes the plan touches: null
+// pointers, outputs overlapping inputs or each other, 16-byte alignment.
+int check_tensors(int32_t dtype, int32_t n_cand, int32_t n_q, int32_t H, int32_t d, int64_t total_len,
+                  int32_t with_self, const void* q_cand, const void* q_user, const void* k, const void* v,
+                  const void* out_cand, const void* out_user) {
+  const size_t es = elem_size(dtype);
+  const size_t row = static_cast<size_t>(H) * d * es;
+  const size_t cand_bytes = static_cast<size_t>(n_cand) * n_q * row;
+  const size_t kv_bytes = static_cast<size_t>(total_len) * row;
+  const bool has_target = n_cand > 0;
+  const bool has_self = with_self && total_len > 0;
+  if (has_target && (!q_cand || !out_cand)) return fail(IKBO_ERR_INVALID_ARG, "null q_cand or out");
+  if ((has_target || has_self) && total_len > 0 && (!k || !v)) return fail(IKBO_ERR_INVALID_ARG, "null k or v");
+  if (has_self && (!q_user || !out_user)) return fail(IKBO_ERR_INVALID_ARG, "null q_user or out_user");
+  const void* ins[4] = {q_cand, k, v, q_user};
+  const size_t in_sz[4] = {cand_bytes, kv_bytes, kv_bytes, has_self ? kv_bytes : 0};
+  for (int i = 0; i < 4; ++i) {
+    if (has_target && overlaps(out_cand, cand_bytes, ins[i], in_sz[i]))
+      return fail(IKBO_ERR_INVALID_ARG, "out_cand aliases an input");
+    if (has_self && overlaps(out_user, kv_bytes, ins[i], in_sz[i]))
+      return fail(IKBO_ERR_INVALID_ARG, "out_user aliases an input");
+  }
+  if (has_target && has_self && overlaps(out_cand, cand_bytes, out_user, kv_bytes))
+    return fail(IKBO_ERR_INVALID_ARG, "out_cand and out_user overlap");
+  const uintptr_t align_or = reinterpret_cast<uintptr_t>(q_cand) | reinterpret_cast<uintptr_t>(k) |
+                             reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out_cand) |
+                             reinterpret_cast<uintptr_t>(q_user) | reinterpret_cast<uintptr_t>(out_user);
+  if (align_or & 15) return fail(IKBO_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  return IKBO_OK;
+}
+
+// Enqueues the attention kernel the plan chose and, for split key ranges, the
+// merge.  te: optional events (attention start/end, merge start/end).
+int launch_kernels(ikbo::AttnParams& ap, int32_t dtype, int variant, int d, int stages, const HostPlan& hp,
+                   hipStream_t stream, hipEvent_t* te) {
+  hipError_t e;
+  if (dtype != IKBO_DTYPE_BF16)
+    e = ikbo::launch_attn_f32(ap, d, hp.grid, stream, te);
+  else if (variant == kVariantW8)
+    e = ikbo::launch_attn_bf16_w8(ap, d, hp.grid, stream, te);
+  else {
+    ap.kv_reverse = variant == kVariantW4R ? 1 : 0;
+    e = ikbo::launch_attn_bf16(ap, d, stages, hp.grid, stream, te);
+  }
+  if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  if (hp.n_groups > 0) {
+    e = ikbo::launch_merge(ap, hp.n_groups, d, stream, te ? te + 2 : nullptr);
+    if (e != hipSuccess) return fail_hip(e, "merge launch");
+  }
+  return IKBO_OK;
+}
+
 }  // namespace ikbo_host
 
 using namespace ikbo_host;
 
 namespace {
-
-using ikbo::HostPlan;
-using ikbo::PlanParams;
-using ikbo::WorkItem;
 
 struct Plan {
   int device = -1;
@@ -87,99 +234,18 @@ int plan_init(Plan* p) {
   return IKBO_OK;
 }
 
-// Depth of the bf16 kernel's HBM -> LDS ring (IKBO_STAGES overrides; 2, 3 or 4).
-int bf16_stages() {
-  const int s = env_int("IKBO_STAGES", ikbo::kBf16DefaultStages);
-  return (s == 2 || s == 3 || s == 4) ? s : ikbo::kBf16DefaultStages;
-}
-
-// bf16 kernel variants: the eight-wave kernel (one per CU, two waves per
-// SIMD) and the 4-wave kernel (two resident per CU).  By default a build plans
-// for the eight-wave kernel and keeps it when every workgroup gets at most one
-// item; otherwise it plans again for the 4-wave kernel, whose two independent
-// workgroups per CU keep the SIMDs busier over many items.  IKBO_KERNEL =
-// w8 | w4 forces a variant; w4r is the 4-wave kernel visiting each item's key
-// tiles last to first (the reverse-order variant of the TLX attention post's
-// persistent kernel).
-enum { kVariantW8 = 1, kVariantW4 = 2, kVariantAuto = 3, kVariantW4R = 4 };
-int bf16_variant() {
-  const char* s = std::getenv("IKBO_KERNEL");
-  if (s && std::strcmp(s, "w4r") == 0) return kVariantW4R;
-  if (s && std::strcmp(s, "w4") == 0) return kVariantW4;
-  if (s && std::strcmp(s, "w8") == 0) return kVariantW8;
-  return kVariantAuto;
-}
-
-PlanParams params_for(const Plan& p, int32_t dtype, int variant) {
-  PlanParams pp;
-  if (dtype == IKBO_DTYPE_BF16 && variant != kVariantW4 && variant != kVariantW4R) {
-    // one resident workgroup per CU; the 8-wave kernel's chunks are whole ring stages
-    pp.bm = ikbo::kBf16TileRows;
-    pp.bn = (variant == kVariantW8 ? 2 : 1) * ikbo::kBf16TileKeys;
-    pp.grid_slots = std::max(1, p.n_cu);
-    pp.min_chunk = 256;
-    pp.allow_split = true;
-    pp.single_pass = true;
-  } else if (dtype == IKBO_DTYPE_BF16) {
-    pp.bm = ikbo::kBf16TileRows;
-    pp.bn = ikbo::kBf16TileKeys;
-    pp.grid_slots = std::max(1, p.n_cu * (bf16_stages() == 2 ? 2 : 1));
-    pp.min_chunk = 256;
-    pp.allow_split = true;
-  } else {
-    pp.bm = ikbo::kF32TileRows;
-    pp.bn = ikbo::kF32TileKeys;
-    pp.grid_slots = std::max(1, p.n_cu * 4);
-    pp.allow_split = false;
-  }
-  // Test and tuning overrides.  IKBO_GRID_WGS changes only the launched grid;
-  // IKBO_SPLIT_SLOTS and IKBO_MIN_CHUNK change how key ranges are split.
-  pp.grid_slots = std::max(1, env_int("IKBO_SPLIT_SLOTS", pp.grid_slots));
-  pp.launch_grid = std::max(0, env_int("IKBO_GRID_WGS", 0));
-  pp.min_chunk = std::max(pp.bn, env_int("IKBO_MIN_CHUNK", pp.min_chunk));
-  if (env_int("IKBO_NO_SPLIT", 0)) pp.allow_split = false;
-  return pp;
-}
-
-int check_dims(int32_t n_users, int32_t n_cand, int32_t n_q, int32_t H, int32_t d, int32_t dtype) {
-  if (n_users < 0 || n_cand < 0) return fail(IKBO_ERR_INVALID_ARG, "n_users and n_cand must be >= 0");
-  if (H < 1) return fail(IKBO_ERR_INVALID_ARG, "H must be >= 1");
-  if (n_q < 1) return fail(IKBO_ERR_INVALID_ARG, "n_q must be >= 1");
-  if (dtype != IKBO_DTYPE_BF16 && dtype != IKBO_DTYPE_F32) return fail(IKBO_ERR_UNSUPPORTED, "dtype");
-  if (d != 32 && d != 64 && d != 128) return fail(IKBO_ERR_UNSUPPORTED, "head dim must be 32, 64 or 128");
-  if (n_cand > 0 && n_users == 0) return fail(IKBO_ERR_BAD_MAPPING, "candidates present but n_users == 0");
-  return IKBO_OK;
-}
-
 int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n_users, int32_t n_cand,
                      int32_t n_q, int32_t H, int32_t d, int32_t dtype, int32_t with_self, hipStream_t stream) {
-  int rc = check_dims(n_users, n_cand, n_q, H, d, dtype);
-  if (rc != IKBO_OK) return rc;
-  if (!offs || (n_cand > 0 && !c2u)) return fail(IKBO_ERR_INVALID_ARG, "null host mapping");
   int dev = -1;
   IKBO_HIP(hipGetDevice(&dev));
   if (dev != p->device) return fail(IKBO_ERR_INVALID_ARG, "plan belongs to another device");
-  std::string err;
   // Build into the plan's own storage (reused across builds); until this plan build
   // completes the plan cannot be launched.
   p->built = false;
   HostPlan& hp = p->hp;
-  // Split partials name their output row as row * H + h in an int32.
-  const int64_t out_units = std::max<int64_t>(static_cast<int64_t>(n_cand) * n_q, with_self ? offs[n_users] : 0) * H;
-  const bool split_ok = out_units < std::numeric_limits<int32_t>::max();
-  const int forced = bf16_variant();
-  int variant = forced == kVariantAuto ? kVariantW8 : forced;
-  PlanParams pp = params_for(*p, dtype, variant);
-  if (!split_ok) pp.allow_split = false;
-  rc = ikbo::build_plan(offs, c2u, n_users, n_cand, n_q, H, with_self != 0, pp, &hp, &err);
-  if (rc != ikbo::kOk) return fail(rc, err);
-  if (dtype == IKBO_DTYPE_BF16 && forced == kVariantAuto && hp.items.size() > static_cast<size_t>(p->n_cu)) {
-    variant = kVariantW4;
-    pp = params_for(*p, dtype, variant);
-    if (!split_ok) pp.allow_split = false;
-    rc = ikbo::build_plan(offs, c2u, n_users, n_cand, n_q, H, with_self != 0, pp, &hp, &err);
-    if (rc != ikbo::kOk) return fail(rc, err);
-  }
+  int variant = kVariantW8;
+  int rc = plan_request(p->n_cu, offs, c2u, n_users, n_cand, n_q, H, d, dtype, with_self, true, &hp, &variant);
+  if (rc != IKBO_OK) return rc;
 
   const int tile_rows = dtype == IKBO_DTYPE_BF16 ? ikbo::kBf16TileRows : ikbo::kF32TileRows;
   const size_t items_bytes = hp.items.size() * sizeof(WorkItem);
@@ -233,29 +299,9 @@ int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* 
   IKBO_HIP(hipGetDevice(&dev));
   if (dev != p->device) return fail(IKBO_ERR_INVALID_ARG, "plan belongs to another device");
   if (!std::isfinite(scale)) return fail(IKBO_ERR_INVALID_ARG, "scale must be finite");
-  const size_t es = elem_size(p->dtype);
-  const size_t row = static_cast<size_t>(p->H) * p->d * es;
-  const size_t cand_bytes = static_cast<size_t>(p->n_cand) * p->n_q * row;
-  const size_t kv_bytes = static_cast<size_t>(p->total_len) * row;
-  const bool has_target = p->n_cand > 0;
-  const bool has_self = p->with_self && p->total_len > 0;
-  if (has_target && (!q_cand || !out_cand)) return fail(IKBO_ERR_INVALID_ARG, "null q_cand or out");
-  if ((has_target || has_self) && p->total_len > 0 && (!k || !v)) return fail(IKBO_ERR_INVALID_ARG, "null k or v");
-  if (has_self && (!q_user || !out_user)) return fail(IKBO_ERR_INVALID_ARG, "null q_user or out_user");
-  const void* ins[4] = {q_cand, k, v, q_user};
-  const size_t in_sz[4] = {cand_bytes, kv_bytes, kv_bytes, has_self ? kv_bytes : 0};
-  for (int i = 0; i < 4; ++i) {
-    if (has_target && overlaps(out_cand, cand_bytes, ins[i], in_sz[i]))
-      return fail(IKBO_ERR_INVALID_ARG, "out_cand aliases an input");
-    if (has_self && overlaps(out_user, kv_bytes, ins[i], in_sz[i]))
-      return fail(IKBO_ERR_INVALID_ARG, "out_user aliases an input");
-  }
-  if (has_target && has_self && overlaps(out_cand, cand_bytes, out_user, kv_bytes))
-    return fail(IKBO_ERR_INVALID_ARG, "out_cand and out_user overlap");
-  const uintptr_t align_or = reinterpret_cast<uintptr_t>(q_cand) | reinterpret_cast<uintptr_t>(k) |
-                             reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out_cand) |
-                             reinterpret_cast<uintptr_t>(q_user) | reinterpret_cast<uintptr_t>(out_user);
-  if (align_or & 15) return fail(IKBO_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  int rc = check_tensors(p->dtype, p->n_cand, p->n_q, p->H, p->d, p->total_len, p->with_self, q_cand, q_user, k, v,
+                         out_cand, out_user);
+  if (rc != IKBO_OK) return rc;
   if (p->hp.items.empty()) return IKBO_OK;
 
   ikbo::AttnParams ap{};
@@ -275,31 +321,16 @@ int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* 
   ap.ws_rec = static_cast<float*>(p->d_ws_rec.ptr);
   ap.trace = nullptr;
   if (p->tracing && p->dtype == IKBO_DTYPE_BF16) {
-    int rc = p->d_trace.ensure(p->hp.items.size() * 6 * sizeof(uint64_t), false);
-    if (rc != IKBO_OK) return rc;
+    if ((rc = p->d_trace.ensure(p->hp.items.size() * 6 * sizeof(uint64_t), false)) != IKBO_OK) return rc;
     ap.trace = static_cast<uint64_t*>(p->d_trace.ptr);
   }
-  if (int rc = p->ring.on_stream(stream); rc != IKBO_OK) return rc;  // before anything is enqueued
+  if ((rc = p->ring.on_stream(stream)) != IKBO_OK) return rc;  // before anything is enqueued
   hipEvent_t* te = nullptr;  // attention start/end, merge start/end (stamped by the dispatches)
-  if (int rc = p->timed.next(&te, p->hp.n_groups > 0); rc != IKBO_OK) return rc;
-  hipError_t e;
-  if (p->dtype != IKBO_DTYPE_BF16)
-    e = ikbo::launch_attn_f32(ap, p->d, p->hp.grid, stream, te);
-  else if (p->variant == kVariantW8)
-    e = ikbo::launch_attn_bf16_w8(ap, p->d, p->hp.grid, stream, te);
-  else {
-    ap.kv_reverse = p->variant == kVariantW4R ? 1 : 0;
-    e = ikbo::launch_attn_bf16(ap, p->d, p->stages, p->hp.grid, stream, te);
-  }
-  if (e != hipSuccess) return fail_hip(e, "kernel launch");
-  if (p->hp.n_groups > 0) {
-    e = ikbo::launch_merge(ap, p->hp.n_groups, p->d, stream, te ? te + 2 : nullptr);
-    if (e != hipSuccess) return fail_hip(e, "merge launch");
-  }
+  if ((rc = p->timed.next(&te, p->hp.n_groups > 0)) != IKBO_OK) return rc;
+  if ((rc = launch_kernels(ap, p->dtype, p->variant, p->d, p->stages, p->hp, stream, te)) != IKBO_OK) return rc;
   if (p->read_in_place) {
     // The pinned work list of this plan build stays in use until these kernels end.
-    int rc = p->ring.launched(p->cur_stage, stream);
-    if (rc != IKBO_OK) return rc;
+    if ((rc = p->ring.launched(p->cur_stage, stream)) != IKBO_OK) return rc;
   }
   return IKBO_OK;
 }
