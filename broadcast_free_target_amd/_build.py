@@ -23,7 +23,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libikbo.so")
 
 SOURCES = ("ikbo_plan.cpp", "ikbo_kernels.hip", "ikbo_lce.hip", "ikbo_bwd.hip", "ikbo_mx.hip", "ikbo_api.hip",
-           "ikbo_api_lce.hip", "ikbo_api_bwd.hip", "ikbo_api_mx.hip")
+           "ikbo_api_lce.hip", "ikbo_api_bwd.hip", "ikbo_api_mx.hip", "ikbo_api_noalloc.hip")
 ARCH = os.environ.get("IKBO_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 VALU forms are disabled for all device code.

@@ -41,6 +41,7 @@ SIGNATURES = {
     "ikbo_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P]),
     "ikbo_attn_fwd_f32": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P]),
     "ikbo_attn_fwd_mt": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _I, _I]),
+    "ikbo_attn_fwd_mt_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _I, _I]),
     "ikbo_attn_fwd_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P]),
     "ikbo_self_target_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P]),
     "ikbo_attn_fwd_materialized": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _I, _I]),
@@ -263,6 +264,14 @@ def ikbo_attn_fwd_mt(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users
                      stream=None, n_q=1, dtype=IKBO_DTYPE_BF16) -> int:
     _check_common(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, n_q, H, d, _es(dtype), out)
     return _check(load_library().ikbo_attn_fwd_mt(
+        _ptr(q_cand), _ptr(k_user), _ptr(v_user), _ptr(user_offsets), _ptr(cand_to_user),
+        n_users, n_cand, H, d, float(scale), _ptr(out), _stream(stream), n_q, dtype))
+
+
+def ikbo_attn_fwd_mt_noalloc(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, H, d, scale, out,
+                             stream=None, n_q=1, dtype=IKBO_DTYPE_BF16) -> int:
+    _check_common(q_cand, k_user, v_user, user_offsets, cand_to_user, n_users, n_cand, n_q, H, d, _es(dtype), out)
+    return _check(load_library().ikbo_attn_fwd_mt_noalloc(
         _ptr(q_cand), _ptr(k_user), _ptr(v_user), _ptr(user_offsets), _ptr(cand_to_user),
         n_users, n_cand, H, d, float(scale), _ptr(out), _stream(stream), n_q, dtype))
 

@@ -134,6 +134,28 @@ int ikbo_attn_fwd_mt(const void* q_cand, const void* k_user, const void* v_user,
                      int32_t n_users, int32_t n_cand, int32_t H, int32_t d, float scale,
                      void* out, void* stream, int32_t n_q, int32_t dtype);
 
+/*
+ * Allocation-free form of ikbo_attn_fwd_mt, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, same planner and kernels; the
+ * kernels' scratch (split-KV partials and their row records, the work list and
+ * the candidate order) is one fixed library array per device, 64 MiB, held by
+ * every device the call runs on until the process ends.  Nothing is allocated
+ * per call, on the device or the host: host planning storage is reserved at
+ * the first call.  Limits: n_users <= 65536, n_cand <= 1048576, and
+ * H * (n_cand * n_q / 128 + n_users + 1) <= 131072 (IKBO_ERR_INVALID_ARG
+ * beyond them, before anything is enqueued); when the split partials would
+ * not fit, key ranges are left whole (same result within rounding).  The call
+ * copies the mapping to the host and waits for the stream, like
+ * ikbo_attn_fwd_mt.  All calls on one device share its scratch: calls that
+ * overlap in time on one device (other streams, other host threads' streams)
+ * race; the library serialises only the host side.
+ */
+int ikbo_attn_fwd_mt_noalloc(const void* q_cand, const void* k_user, const void* v_user,
+                             const int32_t* user_offsets, const int32_t* cand_to_user,
+                             int32_t n_users, int32_t n_cand, int32_t H, int32_t d, float scale,
+                             void* out, void* stream, int32_t n_q, int32_t dtype);
+
 /* As ikbo_attn_fwd_mt, with n_q and dtype next to the other sizes. */
 int ikbo_attn_fwd_ex(const void* q_cand, const void* k_user, const void* v_user,
                      const int32_t* user_offsets, const int32_t* cand_to_user,
