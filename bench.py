@@ -2,11 +2,12 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2_typical]
 
-One step is the whole hot path for one request batch: validation, the host
-grouping pass and work list built from the host copy of the candidate-to-user
-mapping (as an inference runtime holds it) into pinned memory that the
-kernels read in place, the persistent attention kernel and, when key ranges
-were split, the merge kernel.  Inputs are resident in HBM before timing.
+One step is the whole hot path for one request batch, one library call
+(ikbo_attn_fwd_hostmap): validation, the host grouping pass and work list
+built from the host copy of the candidate-to-user mapping (as an inference
+runtime holds it) into pinned memory that the kernels read in place, the
+persistent attention kernel and, when key ranges were split, the merge
+kernel.  Inputs are resident in HBM before timing.
 Rank 0 prints one JSON line (the contract fields plus ``roofline`` and
 ``cpu_baseline``).  Under ``extra`` it also carries cold-cache kernel times,
 the host time of a plan build and of a launch, the end-to-end time of the
@@ -727,6 +728,101 @@ def main_lce(args):
     print(json.dumps(result), flush=True)
 
 
+def _pmc_rows(path):
+    """Per-dispatch counter values from a rocprofv3 --pmc run: {(dispatch, kernel): {counter: value}}.
+    `path` is the output directory (searched for *counter_collection.csv) or the file."""
+    import csv
+    import glob
+    files = [path] if os.path.isfile(path) else sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"),
+                                                                 recursive=True))
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {path}")
+    rows = {}
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                key = (f, r.get("Dispatch_Id") or r.get("Correlation_Id"), r["Kernel_Name"])
+                d = rows.setdefault(key, {})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return rows
+
+
+def _pmc_mean(rows, counter, match):
+    """Mean of a counter (KiB) over the dispatches whose kernel name contains `match`."""
+    vals = [d[counter] for (_, _, name), d in rows.items() if match in name and counter in d]
+    return (float(np.mean(vals)), len(vals)) if vals else (0.0, 0)
+
+
+def summarize_pmc(args):
+    """HBM bytes per launch from two rocprofv3 --pmc runs (FETCH_SIZE, then
+    WRITE_SIZE, KiB per dispatch) of the benchmark command, scaled by the same
+    counters taken on a plain 1 GiB device-to-device copy (--copy-calibration),
+    written as the JSON summary that the roofline's `traffic` field reads."""
+    n = 1 << 30
+    cf = _pmc_rows(args.copy_fetch)
+    cw = _pmc_rows(args.copy_write)
+    copy_f = max((d.get("FETCH_SIZE", 0.0) for d in cf.values()), default=0.0)
+    copy_w = max((d.get("WRITE_SIZE", 0.0) for d in cw.values()), default=0.0)
+    if copy_f <= 0 or copy_w <= 0:
+        raise RuntimeError("copy calibration runs hold no FETCH_SIZE / WRITE_SIZE")
+    f_scale, w_scale = n / (copy_f * 1024.0), n / (copy_w * 1024.0)
+    fr, wr = _pmc_rows(args.fetch), _pmc_rows(args.write)
+    kernels = [k.strip() for k in args.kernels.split(";") if k.strip()]
+    out = {"workload": args.config, "kernel_source_hash": None, "commands": {
+               "fetch": args.fetch_cmd, "write": "the same with --pmc WRITE_SIZE",
+               "copy_calibration": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <dir> -o run "
+                                   "-- python3 bench.py --copy-calibration --steps 5"},
+           "copy_calibration": {"bytes": n, "fetch_kib_per_dispatch": copy_f, "fetch_scale": f_scale,
+                                "write_kib_per_dispatch": copy_w, "write_scale": w_scale},
+           "kernels": {}}
+    total = 0.0
+    for k in kernels:
+        f, nf = _pmc_mean(fr, "FETCH_SIZE", k)
+        w_, nw = _pmc_mean(wr, "WRITE_SIZE", k)
+        rb, wb = f * 1024.0 * f_scale, w_ * 1024.0 * w_scale
+        out["kernels"][k] = {"read_bytes": rb, "write_bytes": wb, "dispatches": [nf, nw]}
+        total += rb + wb
+    first = out["kernels"][kernels[0]]
+    out["hbm_bytes_per_launch"] = first["read_bytes"] + first["write_bytes"]
+    out["hbm_bytes_per_step_with_merge"] = total
+    lce, bwd, mx = args.config.startswith("lce"), args.config.startswith("bwd_"), args.config.startswith("mx_")
+    out["kernel_source_hash"] = (kernel_source_hash(LCE_SOURCES) if lce else kernel_source_hash(BWD_SOURCES) if bwd
+                                 else kernel_source_hash(MX_SOURCES) if mx else kernel_source_hash())
+    with open(args.out, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out), flush=True)
+
+
+def summarize_trace(args):
+    """Per-kernel durations from a rocprofv3 --kernel-trace run of the
+    benchmark: over all dispatches, and over the dispatches of timed region 2
+    (the ones bench.py's roofline durations come from: each kernel's dispatches
+    number warmup + steps .. warmup + 2 * steps - 1, in launch order)."""
+    import csv
+    import glob
+    path = args.trace
+    files = [path] if os.path.isfile(path) else sorted(glob.glob(os.path.join(path, "**", "*kernel_trace.csv"),
+                                                                 recursive=True))
+    if not files:
+        raise FileNotFoundError(f"no kernel_trace.csv under {path}")
+    per = {}
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                per.setdefault(r["Kernel_Name"], []).append(
+                    (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    out = {}
+    for name, v in per.items():
+        v.sort()
+        d = np.array([x[1] for x in v], dtype=np.float64) / 1e3  # ns -> us
+        rec = {"dispatches": int(d.size), "avg_us_all": float(d.mean())}
+        lo, hi = args.warmup + args.steps, args.warmup + 2 * args.steps
+        if d.size >= hi:
+            rec["avg_us_timed_region_2"] = float(d[lo:hi].mean())
+        out[name] = rec
+    print(json.dumps(out, indent=1), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -742,7 +838,25 @@ def main():
                     help="run only a plain 1 GiB device-to-device copy (to scale memory counters)")
     ap.add_argument("--materialized-only", action="store_true",
                     help="loop only the materialised-broadcast comparator (for profiling)")
+    ap.add_argument("--summarize-pmc", action="store_true",
+                    help="CPU only: turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs into the traffic summary JSON")
+    ap.add_argument("--fetch", help="--summarize-pmc: output directory of the FETCH_SIZE run")
+    ap.add_argument("--write", help="--summarize-pmc: output directory of the WRITE_SIZE run")
+    ap.add_argument("--copy-fetch", help="--summarize-pmc: FETCH_SIZE run of --copy-calibration")
+    ap.add_argument("--copy-write", help="--summarize-pmc: WRITE_SIZE run of --copy-calibration")
+    ap.add_argument("--kernels", default="ikbo_attn_bf16;ikbo_merge_kernel",
+                    help="--summarize-pmc: ';'-separated kernel-name substrings, the roofline's kernel first")
+    ap.add_argument("--fetch-cmd", default="", help="--summarize-pmc: the profiled command, recorded in the summary")
+    ap.add_argument("--out", help="--summarize-pmc: path of the JSON summary")
+    ap.add_argument("--summarize-trace", dest="trace",
+                    help="CPU only: per-kernel durations from a rocprofv3 --kernel-trace output directory")
     args = ap.parse_args()
+    if args.trace:
+        summarize_trace(args)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this benchmark has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -807,22 +921,23 @@ def main():
         ikbo.ikbo_attn_fwd_planned(plan, dev["q_cand"], dev.get("q_user"), dev["k_user"], dev["v_user"], w.scale,
                                    out_c, out_u, stream)
 
+    def step():  # plan build from the host mapping and launch, in one library call
+        ikbo.ikbo_attn_fwd_hostmap(plan, offs_h, c2u_h, w.n_users, w.n_cand, w.n_q, w.H, w.d, dt_code, ws,
+                                   dev["q_cand"], dev.get("q_user"), dev["k_user"], dev["v_user"], w.scale, out_c,
+                                   out_u, stream)
+
     info = ikbo.ikbo_plan_info(plan)
     for _ in range(args.warmup):
-        build()
-        launch()
+        step()
     torch.cuda.synchronize()
 
     K = args.steps
-    if args.kernel_only:
-        build()
+    one = launch if args.kernel_only else step
     # Timed region 1: K whole steps, nothing else on the stream (the value).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        if not args.kernel_only:
-            build()
-        launch()
+        one()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # Timed region 2: the same K steps with the kernels' dispatches stamping HIP
@@ -831,9 +946,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for i in range(K):
-        if not args.kernel_only:
-            build()
-        launch()
+        one()
     torch.cuda.synchronize()
     wall_timed = time.perf_counter() - t1
     kern_ms, merge_ms = ikbo.ikbo_plan_timing_read(plan, K)
@@ -885,64 +998,76 @@ def main():
         "ikbo_vs_materialized_bytes_ratio": mat_bytes / byts,
     }
 
-    # Cold cache: 2 GiB overwritten between launches so that neither L2 nor the
-    # Infinity Cache holds K/V; the flush stays outside the kernels' events.
-    flush = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
-    n_cold = 20
-    ikbo.ikbo_plan_timing(plan, True)
-    for _ in range(n_cold):
-        flush.fill_(1)
-        launch()
-        torch.cuda.synchronize()
-    cold_a, cold_m = ikbo.ikbo_plan_timing_read(plan, n_cold)
-    ikbo.ikbo_plan_timing(plan, False)
-    del flush
-    c_ms = float(np.median(np.asarray(cold_a) + np.asarray(cold_m)))
-    extra["cold_attn_plus_merge_us_median"] = c_ms * 1e3
-    extra["cold_kernel_tflops"] = flops / (c_ms * 1e-3) / 1e12
-    extra["cold_kernel_hbm_gbs"] = byts / (c_ms * 1e-3) / 1e9
-    extra["cold_frac_applicable_roof"] = (flops / (c_ms * 1e-3)) / min(peak_flops, ai * PEAK_HBM_GBS * 1e9)
-    extra["warm_frac_applicable_roof"] = (flops / (path_ms * 1e-3)) / min(peak_flops, ai * PEAK_HBM_GBS * 1e9)
-    # Host time of each call of a step (the GPU idle first, so nothing waits on it).
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for _ in range(100):
-        build()
-    extra["host_plan_build_us"] = (time.perf_counter() - t1) / 100 * 1e6
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for _ in range(20):
-        launch()
-    extra["host_launch_us"] = (time.perf_counter() - t1) / 20 * 1e6
-    torch.cuda.synchronize()
-    if not w.with_self:
-        # End to end through the device-mapping entry point: D2H copy of the
-        # mapping, synchronisation, host plan and launch.
-        def e2e():
-            ikbo.ikbo_attn_fwd_mt(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"],
-                                  dev["cand_to_user"], w.n_users, w.n_cand, w.H, w.d, w.scale, out_c, stream,
-                                  n_q=w.n_q, dtype=dt_code)
-        for _ in range(5):
-            e2e()
+    def extras():
+        """Cold-cache kernel times, host times of the step's calls, the
+        device-mapping entry point end to end and the materialised comparator
+        (skipped with --kernel-only, which profiles the timed launches alone)."""
+        # Cold cache: 2 GiB overwritten between launches so that neither L2 nor the
+        # Infinity Cache holds K/V; the flush stays outside the kernels' events.
+        flush = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+        n_cold = 20
+        ikbo.ikbo_plan_timing(plan, True)
+        for _ in range(n_cold):
+            flush.fill_(1)
+            launch()
+            torch.cuda.synchronize()
+        cold_a, cold_m = ikbo.ikbo_plan_timing_read(plan, n_cold)
+        ikbo.ikbo_plan_timing(plan, False)
+        del flush
+        c_ms = float(np.median(np.asarray(cold_a) + np.asarray(cold_m)))
+        extra["cold_attn_plus_merge_us_median"] = c_ms * 1e3
+        extra["cold_kernel_tflops"] = flops / (c_ms * 1e-3) / 1e12
+        extra["cold_kernel_hbm_gbs"] = byts / (c_ms * 1e-3) / 1e9
+        extra["cold_frac_applicable_roof"] = (flops / (c_ms * 1e-3)) / min(peak_flops, ai * PEAK_HBM_GBS * 1e9)
+        extra["warm_frac_applicable_roof"] = (flops / (path_ms * 1e-3)) / min(peak_flops, ai * PEAK_HBM_GBS * 1e9)
+        # Host time of each call of a step (the GPU idle first, so nothing waits on it).
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        n_e2e = 50
-        for _ in range(n_e2e):
-            e2e()
+        for _ in range(100):
+            build()
+        extra["host_plan_build_us"] = (time.perf_counter() - t1) / 100 * 1e6
         torch.cuda.synchronize()
-        extra["e2e_device_mapping_us"] = (time.perf_counter() - t1) / n_e2e * 1e6
-        # The materialised-broadcast comparator: copy kernel + the same attention kernel.
-        if mat_bytes < 64e9:
-            for _ in range(2):
-                materialized()
+        t1 = time.perf_counter()
+        for _ in range(20):
+            launch()
+        extra["host_launch_us"] = (time.perf_counter() - t1) / 20 * 1e6
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(20):
+            step()
+        extra["host_step_us"] = (time.perf_counter() - t1) / 20 * 1e6  # one ikbo_attn_fwd_hostmap call
+        torch.cuda.synchronize()
+        if not w.with_self:
+            # End to end through the device-mapping entry point: D2H copy of the
+            # mapping, synchronisation, host plan and launch.
+            def e2e():
+                ikbo.ikbo_attn_fwd_mt(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"],
+                                      dev["cand_to_user"], w.n_users, w.n_cand, w.H, w.d, w.scale, out_c, stream,
+                                      n_q=w.n_q, dtype=dt_code)
+            for _ in range(5):
+                e2e()
             torch.cuda.synchronize()
             t1 = time.perf_counter()
-            n_mat = 5
-            for _ in range(n_mat):
-                materialized()
+            n_e2e = 50
+            for _ in range(n_e2e):
+                e2e()
             torch.cuda.synchronize()
-            extra["materialized_us"] = (time.perf_counter() - t1) / n_mat * 1e6
-            extra["materialized_vs_ikbo_step"] = extra["materialized_us"] / (ms_per_step * 1e3)
+            extra["e2e_device_mapping_us"] = (time.perf_counter() - t1) / n_e2e * 1e6
+            # The materialised-broadcast comparator: copy kernel + the same attention kernel.
+            if mat_bytes < 64e9:
+                for _ in range(2):
+                    materialized()
+                torch.cuda.synchronize()
+                t1 = time.perf_counter()
+                n_mat = 5
+                for _ in range(n_mat):
+                    materialized()
+                torch.cuda.synchronize()
+                extra["materialized_us"] = (time.perf_counter() - t1) / n_mat * 1e6
+                extra["materialized_vs_ikbo_step"] = extra["materialized_us"] / (ms_per_step * 1e3)
+
+    if not args.kernel_only:
+        extras()
 
     ikbo.ikbo_plan_destroy(plan)
     result = {

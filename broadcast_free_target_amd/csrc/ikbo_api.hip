@@ -483,6 +483,36 @@ int ikbo_attn_fwd_planned(void* plan, const void* q_cand, const void* q_user, co
                         static_cast<hipStream_t>(stream));
 }
 
+int ikbo_attn_fwd_hostmap(void* plan, const int32_t* user_offsets_host, const int32_t* cand_to_user_host,
+                          int32_t n_users, int32_t n_cand, int32_t n_q, int32_t H, int32_t d, int32_t dtype,
+                          int32_t with_self, const void* q_cand, const void* q_user, const void* k_user,
+                          const void* v_user, float scale, void* out_cand, void* out_user, void* stream) {
+  if (!plan) return fail(IKBO_ERR_INVALID_ARG, "plan is null");
+  try {
+    Plan* p = static_cast<Plan*>(plan);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!std::isfinite(scale)) return fail(IKBO_ERR_INVALID_ARG, "scale must be finite");
+    // The tensor checks need the request's sizes: run them before the build so
+    // that an error leaves the plan's previous build in place.
+    int rc = check_dims(n_users, n_cand, n_q, H, d, dtype);
+    if (rc != IKBO_OK) return rc;
+    if (!user_offsets_host) return fail(IKBO_ERR_INVALID_ARG, "null host mapping");
+    std::string err;
+    if ((rc = ikbo::check_offsets(user_offsets_host, n_users, &err)) != ikbo::kOk) return fail(rc, err);
+    if ((rc = check_tensors(dtype, n_cand, n_q, H, d, user_offsets_host[n_users], with_self, q_cand, q_user, k_user,
+                            v_user, out_cand, out_user)) != IKBO_OK)
+      return rc;
+    if ((rc = build_and_upload(p, user_offsets_host, cand_to_user_host, n_users, n_cand, n_q, H, d, dtype, with_self,
+                               st)) != IKBO_OK)
+      return rc;
+    return launch_planned(p, q_cand, q_user, k_user, v_user, scale, out_cand, out_user, st);
+  } catch (const std::bad_alloc&) {
+    return fail(IKBO_ERR_NOMEM, "host allocation");
+  } catch (...) {
+    return fail(IKBO_ERR_INVALID_ARG, "unexpected host error");
+  }
+}
+
 void ikbo_plan_destroy(void* plan) {
   if (!plan) return;
   Plan* p = static_cast<Plan*>(plan);

@@ -48,6 +48,8 @@ SIGNATURES = {
     "ikbo_plan_create": (ctypes.c_int, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, ctypes.POINTER(_P)]),
     "ikbo_plan_build": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "ikbo_attn_fwd_planned": (ctypes.c_int, [_P, _P, _P, _P, _P, _F, _P, _P, _P]),
+    "ikbo_attn_fwd_hostmap": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _F, _P, _P,
+                                             _P]),
     "ikbo_plan_destroy": (None, [_P]),
     "ikbo_plan_info": (ctypes.c_int, [_P, _LP, _I]),
     "ikbo_plan_timing": (ctypes.c_int, [_P, _I]),
@@ -347,6 +349,30 @@ def ikbo_attn_fwd_planned(plan, q_cand, q_user, k_user, v_user, scale, out_cand,
     return _check(load_library().ikbo_attn_fwd_planned(
         plan, _ptr(q_cand), _ptr(q_user), _ptr(k_user), _ptr(v_user), float(scale), _ptr(out_cand),
         _ptr(out_user), _stream(stream)))
+
+
+def ikbo_attn_fwd_hostmap(plan, user_offsets_host, cand_to_user_host, n_users, n_cand, n_q, H, d, dtype, with_self,
+                          q_cand, q_user, k_user, v_user, scale, out_cand, out_user=None, stream=None) -> int:
+    """Rebuilds the plan for the request the host mapping arrays describe and
+    launches it, in one library call."""
+    offs = np.ascontiguousarray(user_offsets_host, dtype=np.int32)
+    c2u = np.ascontiguousarray(cand_to_user_host, dtype=np.int32)
+    dims = _plan_dims(offs, n_users, n_cand, n_q, H, d, dtype, with_self) if offs.size > n_users >= 0 else None
+    if dims is not None:
+        es, cand_bytes, kv_bytes, _ = dims
+        _need(q_cand, cand_bytes, "q_cand", es)
+        _need(out_cand, cand_bytes, "out_cand", es)
+        _need(k_user, kv_bytes, "k_user", es)
+        _need(v_user, kv_bytes, "v_user", es)
+        if with_self:
+            _need(q_user, kv_bytes, "q_user", es)
+            _need(out_user, kv_bytes, "out_user", es)
+    _PLAN_DIMS.pop(plan, None)
+    rc = _check(load_library().ikbo_attn_fwd_hostmap(
+        plan, _host_i32(offs), _host_i32(c2u), n_users, n_cand, n_q, H, d, dtype, int(with_self), _ptr(q_cand),
+        _ptr(q_user), _ptr(k_user), _ptr(v_user), float(scale), _ptr(out_cand), _ptr(out_user), _stream(stream)))
+    _PLAN_DIMS[plan] = dims
+    return rc
 
 
 def ikbo_plan_destroy(plan) -> None:

@@ -213,6 +213,11 @@ int ikbo_attn_fwd_materialized(const void* q_cand, const void* k_user, const voi
  *   groups are merged by a second kernel with the log-sum-exp rule of the
  *   Flash-Decoding split-KV reduction (AI-infra guide, section 4.6.4), in
  *   chunk order, so results do not depend on the schedule or the launch grid.
+ * ikbo_attn_fwd_hostmap: ikbo_plan_build followed by ikbo_attn_fwd_planned
+ *   in one call (the per-request step of a runtime that holds the mapping on
+ *   the host).  The tensors are checked against the new request first; on
+ *   any error nothing is launched and the plan keeps its previous build
+ *   unless the error came from the build itself.
  * ikbo_plan_destroy: frees the plan after synchronising its device.
  */
 int ikbo_plan_create(const int32_t* user_offsets_host, const int32_t* cand_to_user_host,
@@ -224,6 +229,10 @@ int ikbo_plan_build(void* plan, const int32_t* user_offsets_host, const int32_t*
 int ikbo_attn_fwd_planned(void* plan, const void* q_cand, const void* q_user,
                           const void* k_user, const void* v_user, float scale,
                           void* out_cand, void* out_user, void* stream);
+int ikbo_attn_fwd_hostmap(void* plan, const int32_t* user_offsets_host, const int32_t* cand_to_user_host,
+                          int32_t n_users, int32_t n_cand, int32_t n_q, int32_t H, int32_t d, int32_t dtype,
+                          int32_t with_self, const void* q_cand, const void* q_user, const void* k_user,
+                          const void* v_user, float scale, void* out_cand, void* out_user, void* stream);
 void ikbo_plan_destroy(void* plan);
 
 /*

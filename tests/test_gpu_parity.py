@@ -492,6 +492,47 @@ def test_plan_rebuilt_for_alternating_requests():
             assert torch.equal(outs[i][rep].view(torch.int16), outs[i][0].view(torch.int16))
 
 
+def test_hostmap_call_equals_build_then_launch():
+    """ikbo_attn_fwd_hostmap (build and launch in one call) gives the bits of a
+    build followed by a planned launch, over alternating requests; a call whose
+    tensors do not fit launches nothing and keeps the previous build."""
+    from broadcast_free_target_amd import (IkboError, ikbo_attn_fwd_hostmap, ikbo_attn_fwd_planned, ikbo_plan_create,
+                                           ikbo_plan_destroy)
+    import torch
+    ws = [_wl("c2_typical"), _custom(63, (65, 700, 1, 513), (5, 60, 9, 33), 2, 2, 128, "bf16")]
+    devs = [upload(w) for w in ws]
+    say("case ikbo_attn_fwd_hostmap")
+    plan = ikbo_plan_create(ws[0].user_offsets, ws[0].cand_to_user, ws[0].n_users, ws[0].n_cand, ws[0].n_q, ws[0].H,
+                            ws[0].d, 0, 0)
+    try:
+        for rep in range(2):
+            for w, dv in zip(ws, devs):
+                a = empty_out(w.raw("q_cand").shape, "bf16")
+                b = empty_out(w.raw("q_cand").shape, "bf16")
+                ikbo_attn_fwd_hostmap(plan, w.user_offsets, w.cand_to_user, w.n_users, w.n_cand, w.n_q, w.H, w.d, 0,
+                                      0, dv["q_cand"], None, dv["k_user"], dv["v_user"], w.scale, a)
+                ikbo_attn_fwd_planned(plan, dv["q_cand"], None, dv["k_user"], dv["v_user"], w.scale, b)
+                torch.cuda.synchronize()
+                assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+                if rep == 0:
+                    assert_close(to_f64(a), _oracle_target(w), "bf16", f"hostmap {w.name}")
+        w, dv = ws[1], devs[1]
+        out = empty_out(w.raw("q_cand").shape, "bf16", fill=7.0)
+        with pytest.raises(IkboError):  # k shorter than the request's keys
+            ikbo_attn_fwd_hostmap(plan, w.user_offsets, w.cand_to_user, w.n_users, w.n_cand, w.n_q, w.H, w.d, 0, 0,
+                                  dv["q_cand"], None, dv["k_user"][:-1], dv["v_user"], w.scale, out)
+        with pytest.raises(IkboError):  # an unsupported head dim, refused by the library before the build
+            ikbo_attn_fwd_hostmap(plan, w.user_offsets, w.cand_to_user, w.n_users, w.n_cand, w.n_q, w.H, 96, 0, 0,
+                                  dv["q_cand"], None, dv["k_user"], dv["v_user"], w.scale, out)
+        torch.cuda.synchronize()
+        assert torch.all(out.float() == 7.0)
+        ikbo_attn_fwd_planned(plan, dv["q_cand"], None, dv["k_user"], dv["v_user"], w.scale, out)
+        torch.cuda.synchronize()
+        assert_close(to_f64(out), _oracle_target(w), "bf16", "hostmap previous build kept")
+    finally:
+        ikbo_plan_destroy(plan)
+
+
 def test_plan_timing_records_each_launch():
     from broadcast_free_target_amd import (ikbo_attn_fwd_planned, ikbo_plan_build, ikbo_plan_create,
                                            ikbo_plan_destroy, ikbo_plan_timing, ikbo_plan_timing_read)
