@@ -67,6 +67,7 @@ PlanParams params_for(int n_cu, int32_t dtype, int variant) {
   } else if (dtype == IKBO_DTYPE_BF16) {
     pp.bm = ikbo::kBf16TileRows;
     pp.bn = ikbo::kBf16TileKeys;
+    pp.xcd_bins = env_int("IKBO_XCD_BINS", ikbo::kMaxBins);  // 0 or 1: no bins
     pp.grid_slots = std::max(1, n_cu * (bf16_stages() == 2 ? 2 : 1));
     pp.min_chunk = 256;
     pp.allow_split = true;
@@ -319,6 +320,8 @@ int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* 
   ap.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   ap.ws_o = static_cast<float*>(p->d_ws_o.ptr);
   ap.ws_rec = static_cast<float*>(p->d_ws_rec.ptr);
+  ap.n_bins = p->hp.n_bins;
+  for (int b = 0; b <= ikbo::kMaxBins; ++b) ap.bin_off[b] = p->hp.bin_off[b];
   ap.trace = nullptr;
   if (p->tracing && p->dtype == IKBO_DTYPE_BF16) {
     if ((rc = p->d_trace.ensure(p->hp.items.size() * 6 * sizeof(uint64_t), false)) != IKBO_OK) return rc;

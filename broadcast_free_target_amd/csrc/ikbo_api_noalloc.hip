@@ -84,7 +84,9 @@ void na_reserve() {
   HostPlan& hp = g_na.hp;
   hp.counts.reserve(kNaMaxUsers);
   hp.cand_offsets.reserve(kNaMaxUsers + 1);
-  hp.cursor.reserve(kNaMaxUsers);
+  hp.cursor.reserve(kNaMaxItems);  // also the per-item group ids of the XCD bins
+  hp.group_cost.reserve(kNaMaxItems);  // (user, head) groups: H * n_users <= the item limit
+  hp.group_bin.reserve(kNaMaxItems);
   hp.cand_perm.reserve(kNaMaxCand);
   hp.items.reserve(kNaMaxItems);
   hp.unsorted.reserve(2 * kNaMaxItems);
@@ -168,6 +170,8 @@ int attn_noalloc(const void* q_cand, const void* k, const void* v, const int32_t
   ap.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   ap.ws_o = reinterpret_cast<float*>(part);
   ap.ws_rec = reinterpret_cast<float*>(part + (hp.n_slots > 0 ? rec_at : 0));
+  ap.n_bins = hp.n_bins;
+  for (int b = 0; b <= ikbo::kMaxBins; ++b) ap.bin_off[b] = hp.bin_off[b];
   ap.trace = nullptr;
   return launch_kernels(ap, dtype, variant, d, bf16_stages(), hp, stream, nullptr);
 }

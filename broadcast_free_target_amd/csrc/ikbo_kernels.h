@@ -36,6 +36,8 @@ struct AttnParams {
                           // nchunk | kind << 16, the last two as int32 bits
   uint64_t* trace;        // optional: [n_items, 6] per-item records (bf16 kernel), or null
   int32_t kv_reverse;     // 4-wave bf16 kernel: 1 = visit each item's key tiles last to first
+  int32_t n_bins;         // 4-wave bf16 kernel: XCD bins of the work list (0: none), see HostPlan
+  int32_t bin_off[kMaxBins + 1];
 };
 
 // stages: depth of the HBM -> LDS ring (2, 3 or 4); 2 stages allow two

@@ -306,11 +306,21 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
   const uint32_t lds_base = lds_address(smem);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
-  const int G = gridDim.x;
-  const int w = logical_wg();
+  // The items this workgroup deals from: its XCD's bin (workgroup i runs on
+  // XCD i % 8, as the i / 8-th of that XCD's workgroups), or the whole list.
+  const int wid = logical_wg();
+  int w = wid, G = gridDim.x;
+  int64_t first = 0, end = P.n_items;
+  if (P.n_bins > 1) {
+    const int x = blockIdx.x % P.n_bins;
+    w = blockIdx.x / P.n_bins;
+    G = gridDim.x / P.n_bins;
+    first = P.bin_off[x];
+    end = P.bin_off[x + 1];
+  }
   for (int64_t pass = 0;; ++pass) {
-    const int64_t pos = deal_position(pass, w, G);
-    if (pos >= P.n_items) break;
+    const int64_t pos = first + deal_position(pass, w, G);
+    if (pos >= end) break;
     const WorkItem it = P.items[pos];
     const bool causal = it.kind == kKindSelf;
     uint64_t t_start = 0, t_ready = 0, t_loop = 0;
@@ -439,7 +449,7 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
     wait_vmcnt<0>();  // epilogue stores retire before the next item's copies are counted
     if (P.trace && tid == 0) {
       uint64_t* tr = P.trace + pos * 6;
-      tr[0] = (static_cast<uint64_t>(w) << 32) | hw_place();
+      tr[0] = (static_cast<uint64_t>(wid) << 32) | hw_place();
       tr[1] = t_start;
       tr[2] = t_ready;
       tr[3] = t_loop;
@@ -551,11 +561,21 @@ __global__ __launch_bounds__(512, 1) void ikbo_attn_bf16_w8_kernel(AttnParams P)
   const uint32_t lds_base = lds_address(smem);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
-  const int G = gridDim.x;
-  const int w = logical_wg();
+  // The items this workgroup deals from: its XCD's bin (workgroup i runs on
+  // XCD i % 8, as the i / 8-th of that XCD's workgroups), or the whole list.
+  const int wid = logical_wg();
+  int w = wid, G = gridDim.x;
+  int64_t first = 0, end = P.n_items;
+  if (P.n_bins > 1) {
+    const int x = blockIdx.x % P.n_bins;
+    w = blockIdx.x / P.n_bins;
+    G = gridDim.x / P.n_bins;
+    first = P.bin_off[x];
+    end = P.bin_off[x + 1];
+  }
   for (int64_t pass = 0;; ++pass) {
-    const int64_t pos = deal_position(pass, w, G);
-    if (pos >= P.n_items) break;
+    const int64_t pos = first + deal_position(pass, w, G);
+    if (pos >= end) break;
     const WorkItem it = P.items[pos];
     const bool causal = it.kind == kKindSelf;
     uint64_t t_start = 0, t_ready = 0, t_loop = 0;
@@ -677,7 +697,7 @@ __global__ __launch_bounds__(512, 1) void ikbo_attn_bf16_w8_kernel(AttnParams P)
     __syncthreads();  // the exchange area is read before the next item's copies overwrite it
     if (P.trace && tid == 0) {
       uint64_t* tr = P.trace + pos * 6;
-      tr[0] = (static_cast<uint64_t>(w) << 32) | hw_place();
+      tr[0] = (static_cast<uint64_t>(wid) << 32) | hw_place();
       tr[1] = t_start;
       tr[2] = t_ready;
       tr[3] = t_loop;

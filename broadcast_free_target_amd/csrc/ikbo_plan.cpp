@@ -88,6 +88,69 @@ int group_csr(const int32_t* cand_to_user, int32_t n_cand, int32_t n_users, int3
   return kOk;
 }
 
+namespace {
+
+// Reorders a longest-first item list into XCD bins (see HostPlan::bin_off):
+// (user, head) groups by decreasing total cost, each into the least loaded bin;
+// within a bin the items keep their longest-first order.  Only for plans whose
+// grid is a multiple of the bin count and which give workgroups more than one
+// item (in a single-pass plan every workgroup runs one item whatever its bin).
+void assign_bins(const int32_t* user_offsets, int32_t n_users, int32_t H, const PlanParams& p, HostPlan* out) {
+  out->n_bins = 0;
+  const int32_t nb = p.xcd_bins;
+  const int64_t n = static_cast<int64_t>(out->items.size());
+  if (nb <= 1 || nb > kMaxBins || out->grid < nb || out->grid % nb != 0 || n <= out->grid) return;
+  // group of an item: user * H + head (the user is found from its K/V base).
+  std::vector<int64_t>& cost = out->group_cost;
+  std::vector<int32_t>& bin = out->group_bin;
+  const int64_t n_groups = static_cast<int64_t>(n_users) * H;
+  cost.assign(n_groups, 0);
+  auto group_of = [&](const WorkItem& it) {
+    const int32_t u = static_cast<int32_t>(
+        std::upper_bound(user_offsets, user_offsets + n_users + 1, it.kv_base) - user_offsets - 1);
+    // users with zero keys share their K/V base with the next user; the item's
+    // key range is empty then and any of them is as good
+    return static_cast<int64_t>(std::min(std::max(u, 0), n_users - 1)) * H + it.h;
+  };
+  std::vector<int32_t>& gid = out->cursor;  // reused as per-item group ids
+  gid.resize(n);
+  for (int64_t i = 0; i < n; ++i) {
+    const WorkItem& it = out->items[i];
+    const int64_t g = group_of(it);
+    gid[i] = static_cast<int32_t>(g);
+    cost[g] += (it.k1 - it.k0) + p.overhead;
+  }
+  // groups by decreasing cost (ties by index), then each to the least loaded bin
+  std::vector<uint64_t>& ord = out->keys;
+  ord.clear();
+  for (int64_t g = 0; g < n_groups; ++g)
+    if (cost[g] > 0) ord.push_back((static_cast<uint64_t>(0xffffffffull - std::min<int64_t>(cost[g], 0xffffffffll)) << 32) |
+                                   static_cast<uint64_t>(g));
+  std::sort(ord.begin(), ord.end());
+  int64_t load[kMaxBins] = {};
+  bin.assign(n_groups, 0);
+  for (uint64_t k : ord) {
+    const int64_t g = static_cast<int64_t>(k & 0xffffffffull);
+    int b = 0;
+    for (int j = 1; j < nb; ++j)
+      if (load[j] < load[b]) b = j;
+    bin[g] = b;
+    load[b] += cost[g];
+  }
+  // stable partition of the items by bin
+  int32_t cnt[kMaxBins + 1] = {};
+  for (int64_t i = 0; i < n; ++i) ++cnt[bin[gid[i]] + 1];
+  for (int b = 0; b < nb; ++b) cnt[b + 1] += cnt[b];
+  for (int b = 0; b <= nb; ++b) out->bin_off[b] = cnt[b];
+  std::vector<WorkItem>& tmp = out->unsorted;
+  tmp.resize(n);
+  for (int64_t i = 0; i < n; ++i) tmp[cnt[bin[gid[i]]]++] = out->items[i];
+  out->items.swap(tmp);
+  out->n_bins = nb;
+}
+
+}  // namespace
+
 int build_plan(const int32_t* user_offsets, const int32_t* cand_to_user, int32_t n_users,
                int32_t n_cand, int32_t n_q, int32_t H, bool with_self, const PlanParams& p,
                HostPlan* out, std::string* err) {
@@ -102,6 +165,7 @@ int build_plan(const int32_t* user_offsets, const int32_t* cand_to_user, int32_t
   }
   int rc = check_offsets(user_offsets, n_users, err);
   if (rc != kOk) return rc;
+  out->n_bins = 0;
   out->counts.resize(n_users);
   out->cand_offsets.resize(static_cast<size_t>(n_users) + 1);
   out->cand_perm.resize(n_cand);
@@ -216,6 +280,7 @@ int build_plan(const int32_t* user_offsets, const int32_t* cand_to_user, int32_t
                                   0, 1, 0});
     }
     out->grid = static_cast<int32_t>(std::min<int64_t>(fast.size(), cap));
+    assign_bins(user_offsets, n_users, H, p, out);
     return kOk;
   }
 
@@ -308,6 +373,7 @@ int build_plan(const int32_t* user_offsets, const int32_t* cand_to_user, int32_t
     for (size_t i = 0; i < n; ++i) out->items[i] = items[keys[i] & 0xffffffffull];
   }
   out->grid = static_cast<int32_t>(std::min<int64_t>(out->items.size(), cap));
+  assign_bins(user_offsets, n_users, H, p, out);
   return kOk;
 }
 

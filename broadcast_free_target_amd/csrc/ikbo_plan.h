@@ -60,7 +60,12 @@ struct PlanParams {
   bool allow_split = true;    // split long key ranges (log-sum-exp merge)
   bool single_pass = false;   // split to the shortest chunk length whose items still
                               // fit grid_slots (one item per workgroup), else by cost
+  int32_t xcd_bins = 0;       // > 1: multi-pass plans keep all items of one (user, head)
+                              // in one of this many bins, one bin per XCD (see HostPlan)
 };
+
+// Most XCD bins a plan may use (the kernels take the bin offsets by value).
+constexpr int32_t kMaxBins = 8;
 
 struct HostPlan {
   std::vector<int32_t> counts;        // [n_users]
@@ -73,11 +78,23 @@ struct HostPlan {
   int32_t grid = 0;                   // workgroups to launch
   int64_t n_target_tiles = 0;
   int64_t n_self_tiles = 0;
+  // XCD bins (0 when the plan has none): items [bin_off[b], bin_off[b+1]) are
+  // bin b's, each bin longest first.  Workgroup i of the launch serves bin
+  // i % n_bins (the XCD the dispatcher places it on) as its (i / n_bins)-th
+  // workgroup, dealing the bin's items boustrophedon-style.  Every item of one
+  // (user, head) -- its row tiles, self and target, and key chunks, all reading
+  // that user's K/V of that head -- is in one bin, so its re-reads stay in one
+  // XCD's L2.  Bins are filled largest (user, head) first, each into the least
+  // loaded bin.
+  int32_t n_bins = 0;
+  int32_t bin_off[kMaxBins + 1] = {};
   // scratch reused by successive builds (no allocation once warm)
   std::vector<int32_t> cursor;
   std::vector<WorkItem> unsorted;
   std::vector<uint64_t> keys;
   std::vector<int64_t> lens;
+  std::vector<int64_t> group_cost;
+  std::vector<int32_t> group_bin;
 };
 
 // Status codes mirror include/ikbo.h.

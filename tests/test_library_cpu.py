@@ -106,8 +106,8 @@ def driver(tmp_path_factory):
 
 
 def _run_driver(driver, offs, c2u, n_q=1, H=2, with_self=0, bm=128, bn=64, grid=512, min_chunk=256, split=1,
-                single=0):
-    nums = [len(offs) - 1, len(c2u), n_q, H, with_self, bm, bn, grid, min_chunk, split, single, *offs, *c2u]
+                single=0, bins=0):
+    nums = [len(offs) - 1, len(c2u), n_q, H, with_self, bm, bn, grid, min_chunk, split, single, bins, *offs, *c2u]
     r = subprocess.run([driver], input=" ".join(map(str, nums)), capture_output=True, text=True, check=True,
                        env={**os.environ, "ASAN_OPTIONS": "detect_leaks=1"})
     lines = r.stdout.splitlines()
@@ -115,10 +115,11 @@ def _run_driver(driver, offs, c2u, n_q=1, H=2, with_self=0, bm=128, bn=64, grid=
     if rc != 0:
         return rc, None
     _, n_items, grid_, n_groups, n_slots = lines[1].split()
-    perm = np.array(lines[2].split()[1:], dtype=np.int64)
-    items = np.array([l.split()[1:] for l in lines[3:]], dtype=np.int64).reshape(-1, 12)
+    bins = [int(x) for x in lines[2].split()[1:]]
+    perm = np.array(lines[3].split()[1:], dtype=np.int64)
+    items = np.array([l.split()[1:] for l in lines[4:]], dtype=np.int64).reshape(-1, 12)
     return 0, dict(n_items=int(n_items), grid=int(grid_), n_groups=int(n_groups), n_slots=int(n_slots),
-                   perm=perm, items=items)
+                   perm=perm, items=items, n_bins=bins[0], bin_off=bins[1:bins[0] + 2] if bins[0] else [0, len(items)])
 
 
 def _check_plan(plan, offs, c2u, n_q, H, with_self, bm, bn, grid_slots):
@@ -179,27 +180,52 @@ def _check_plan(plan, offs, c2u, n_q, H, with_self, bm, bn, grid_slots):
     for g, v in groups.items():
         s0, nc = next(iter(v))
         assert s0 == 8 * g and 2 <= nc <= 8
-    # longest first; equal costs keep construction order (user, then target
-    # before self, head, row tile, chunk), so one user's tiles stay adjacent
+    # longest first within each XCD bin (the whole list when there are none);
+    # equal costs keep construction order (user, then target before self, head,
+    # row tile, chunk), so one user's tiles stay adjacent
+    off = plan["bin_off"]
+    nb = max(plan["n_bins"], 1)
+    assert off[0] == 0 and off[-1] == len(items) and len(off) == nb + 1 and np.all(np.diff(off) >= 0)
     cost = items[:, 5] - items[:, 4]
-    assert np.all(np.diff(cost) <= 0)
     key = [(int(it[0]), int(it[7]), int(it[1]) if it[7] == 0 else 0, int(it[6]), int(it[2]), int(it[4]))
            for it in items]
-    for i in range(len(items) - 1):
-        if cost[i] == cost[i + 1]:
-            assert key[i] < key[i + 1], (i, key[i], key[i + 1])
-    # the boustrophedon deal gives every item to exactly one workgroup
+    for b in range(nb):
+        assert np.all(np.diff(cost[off[b]:off[b + 1]]) <= 0)
+        for i in range(off[b], off[b + 1] - 1):
+            if cost[i] == cost[i + 1]:
+                assert key[i] < key[i + 1], (i, key[i], key[i + 1])
+    # the boustrophedon deal over each bin's workgroups (workgroup i serves bin
+    # i % n_bins) gives every item to exactly one workgroup
     G = plan["grid"]
+    assert G % nb == 0
     hits = np.zeros(len(items), int)
-    for w in range(G):
+    for i in range(G):
+        b, w, Gb = i % nb, i // nb, G // nb
         p = 0
         while True:
-            pos = p * G + ((G - 1 - w) if p & 1 else w)
-            if pos >= len(items):
+            pos = off[b] + p * Gb + ((Gb - 1 - w) if p & 1 else w)
+            if pos >= off[b + 1]:
                 break
             hits[pos] += 1
             p += 1
     assert np.all(hits == 1)
+    if plan["n_bins"]:
+        # every (user, head) -- all its tiles, both kinds, all chunks -- in one bin
+        where = {}
+        for b in range(nb):
+            for it in items[off[b]:off[b + 1]]:
+                u = user_of(int(it[7]), int(it[0]), int(it[1]))
+                assert where.setdefault((u, int(it[6])), b) == b
+        # greedy largest-first filling: no bin exceeds the mean load by more than
+        # the largest (user, head) cost
+        gcost = {}
+        for it in items:
+            u = user_of(int(it[7]), int(it[0]), int(it[1]))
+            gcost[(u, int(it[6]))] = gcost.get((u, int(it[6])), 0) + int(it[5] - it[4]) + 128
+        load = np.zeros(nb)
+        for g, c in gcost.items():
+            load[where[g]] += c
+        assert load.max() <= load.mean() + max(gcost.values()) + 1e-9
     assert np.array_equal(plan["perm"], np.argsort(c2u, kind="stable"))
 
 
@@ -219,6 +245,32 @@ def test_planner_on_configs(driver, name):
         rc, plan = _run_driver(driver, offs, c2u, n_q=n_q, H=H, with_self=with_self, grid=grid, min_chunk=min_chunk)
         assert rc == 0
         _check_plan(plan, offs, c2u, n_q, H, with_self, 128, 64, grid)
+
+
+@pytest.mark.parametrize("name", ["c3_skewed", "c4_large", "c5_fused"])
+def test_planner_xcd_bins(driver, name):
+    """Multi-pass plans with XCD bins: every invariant above, plus each (user,
+    head) in one bin, each bin longest first and dealt over its own workgroups,
+    and bin loads within one (user, head) of the mean."""
+    if name == "c5_fused":
+        rng = np.random.Generator(np.random.PCG64(1005))
+        L = rng.integers(256, 2048, size=30, endpoint=True)
+        counts = rng.multinomial(2048, [1 / 30] * 30)
+        c2u = rng.permutation(np.repeat(np.arange(30), counts)).astype(np.int32)
+        offs = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+        n_q, H, with_self = 1, 4, 1
+    else:
+        w = make_workload(name)
+        offs, c2u, n_q, H, with_self = w.user_offsets, w.cand_to_user, w.n_q, w.H, 0
+    for grid in (512, 64, 8):
+        rc, plan = _run_driver(driver, offs, c2u, n_q=n_q, H=H, with_self=with_self, grid=grid, bins=8)
+        assert rc == 0
+        assert plan["n_bins"] == (8 if plan["n_items"] > plan["grid"] else 0)
+        _check_plan(plan, offs, c2u, n_q, H, with_self, 128, 64, grid)
+    # a grid that is not a multiple of the bin count keeps one list
+    rc, plan = _run_driver(driver, offs, c2u, n_q=n_q, H=H, with_self=with_self, grid=37, bins=8)
+    assert rc == 0 and plan["n_bins"] == 0
+    _check_plan(plan, offs, c2u, n_q, H, with_self, 128, 64, 37)
 
 
 def _single_pass_count(lens, c, bn, max_chunks=8):
