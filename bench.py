@@ -101,9 +101,10 @@ def bwd_counts(w):
     FLOPs: 2 per multiply-add, softmax not counted; per (candidate row, head,
     key) the five products S, dP, dV, dK, dQ take 2*d each.  The dQ kernel
     must form S, dP and dQ; the dK/dV kernel S, dP, dV and dK.
-    Bytes (bf16): dQ kernel reads Q, O, dO and the user's K and V once per
-    (user, head), writes dQ; dK/dV kernel reads K, V, Q and dO once, writes dK
-    and dV (per-row statistics, 8 bytes per row and head, are counted too).
+    Bytes (bf16): dQ kernel reads Q, O, dO, the forward's log-sum-exp and the
+    user's K and V once per (user, head), writes dQ; dK/dV kernel reads K, V, Q
+    and dO once, writes dK and dV (per-row statistics, 8 bytes per row and
+    head, are counted too).
     """
     L = w.lengths.astype(np.float64)
     cnt = w.counts.astype(np.float64)
@@ -111,7 +112,7 @@ def bwd_counts(w):
     rows = float(w.n_cand * w.n_q)
     act = 2.0 * w.H * w.d                                   # bytes of one row (all heads)
     kv_users = float(np.sum(L[cnt > 0]))                      # keys of users that have candidates
-    b_dq = act * (4.0 * rows + 2.0 * kv_users) + 8.0 * rows * w.H
+    b_dq = act * (4.0 * rows + 2.0 * kv_users) + 12.0 * rows * w.H  # + the given log-sum-exp read
     b_dkv = act * (2.0 * rows + 4.0 * w.total_len) + 8.0 * rows * w.H
     return 5.0 * per, 3.0 * per, 4.0 * per, b_dq, b_dkv
 
@@ -250,8 +251,9 @@ def cpu_baseline_bwd(w, n_sample, reps):
 
 def main_bwd(args):
     """One step = one ikbo_attn_bwd call: host grouping and work lists from the
-    host mapping, the dQ kernel and the dK/dV kernel.  The forward output it
-    consumes is produced once, before timing, by the forward path."""
+    host mapping, the dQ kernel and the dK/dV kernel.  The forward output and
+    the rows' log-sum-exp it consumes are produced once, before timing, by the
+    training forward (ikbo_attn_fwd_train), as a training step would."""
     import torch
     import broadcast_free_target_amd as ikbo
     from workloads import make_bwd_workload
@@ -260,19 +262,23 @@ def main_bwd(args):
     w = make_bwd_workload(cfg)
     dev = upload(w)
     out = torch.empty_like(dev["q_cand"])
+    lse = torch.empty((w.n_cand, w.n_q, w.H), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
-    ikbo.ikbo_attn_fwd_ex(dev["q_cand"], dev["k_user"], dev["v_user"], dev["user_offsets"], dev["cand_to_user"],
-                          w.n_users, w.n_cand, w.n_q, w.H, w.d, w.scale, ikbo.IKBO_DTYPE_BF16, out, stream)
+    offs_h = np.ascontiguousarray(w.user_offsets, dtype=np.int32)
+    c2u_h = np.ascontiguousarray(w.cand_to_user, dtype=np.int32)
+    fplan = ikbo.ikbo_plan_create(offs_h, c2u_h, w.n_users, w.n_cand, w.n_q, w.H, w.d, ikbo.IKBO_DTYPE_BF16, 0, stream)
+    ikbo.ikbo_attn_fwd_train(fplan, dev["q_cand"], dev["k_user"], dev["v_user"], w.scale, out, lse, stream)
+    torch.cuda.synchronize()
+    ikbo.ikbo_plan_destroy(fplan)
     dq = torch.empty_like(dev["q_cand"])
     dk = torch.empty_like(dev["k_user"])
     dv = torch.empty_like(dev["v_user"])
-    offs_h = np.ascontiguousarray(w.user_offsets, dtype=np.int32)
-    c2u_h = np.ascontiguousarray(w.cand_to_user, dtype=np.int32)
     h = ikbo.ikbo_bwd_create()
+    given = [lse]
 
     def step():
         ikbo.ikbo_attn_bwd(h, offs_h, c2u_h, w.n_users, w.n_cand, w.n_q, w.H, w.d, w.scale, dev["q_cand"],
-                           dev["k_user"], dev["v_user"], out, dev["dout"], dq, dk, dv, stream)
+                           dev["k_user"], dev["v_user"], out, dev["dout"], dq, dk, dv, stream, lse=given[0])
 
     for _ in range(args.warmup):
         step()
@@ -290,6 +296,17 @@ def main_bwd(args):
     dq_ms, dkv_ms = ikbo.ikbo_bwd_timing_read(h, K)
     ikbo.ikbo_bwd_timing(h, False)
     info = ikbo.ikbo_bwd_info(h)
+    # the same calls with the log-sum-exp recomputed by the dQ kernel (for
+    # comparison; not with --kernel-only, which profiles the timed calls alone)
+    dq_re_ms = [float("nan")]
+    if not args.kernel_only:
+        given[0] = None
+        ikbo.ikbo_bwd_timing(h, True)
+        for _ in range(K):
+            step()
+        torch.cuda.synchronize()
+        dq_re_ms, _ = ikbo.ikbo_bwd_timing_read(h, K)
+        ikbo.ikbo_bwd_timing(h, False)
     ikbo.ikbo_bwd_destroy(h)
     a_ms, b_ms = float(np.mean(dq_ms)), float(np.mean(dkv_ms))
 
@@ -312,6 +329,7 @@ def main_bwd(args):
     roof["algorithmic_flops_per_launch"] = f_k
     extra = {
         "dq_kernel_us": a_ms * 1e3, "dkv_kernel_us": b_ms * 1e3,
+        "dq_kernel_us_lse_recomputed": float(np.mean(dq_re_ms)) * 1e3,
         "dq_kernel_tflops": f_dq / (a_ms * 1e-3) / 1e12, "dkv_kernel_tflops": f_dkv / (b_ms * 1e-3) / 1e12,
         "dq_kernel_hbm_gbs": b_dq / (a_ms * 1e-3) / 1e9, "dkv_kernel_hbm_gbs": b_dkv / (b_ms * 1e-3) / 1e9,
         "kernels_tflops": f_all / ((a_ms + b_ms) * 1e-3) / 1e12,

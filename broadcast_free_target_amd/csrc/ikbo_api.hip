@@ -294,7 +294,7 @@ int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n
 
 
 int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* k, const void* v, float scale,
-                   void* out_cand, void* out_user, hipStream_t stream) {
+                   void* out_cand, void* out_user, hipStream_t stream, float* lse = nullptr) {
   if (!p->built) return fail(IKBO_ERR_INVALID_ARG, "plan has not been built");
   int dev = -1;
   IKBO_HIP(hipGetDevice(&dev));
@@ -303,9 +303,22 @@ int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* 
   int rc = check_tensors(p->dtype, p->n_cand, p->n_q, p->H, p->d, p->total_len, p->with_self, q_cand, q_user, k, v,
                          out_cand, out_user);
   if (rc != IKBO_OK) return rc;
+  if (lse) {
+    if (p->dtype != IKBO_DTYPE_BF16 || p->with_self)
+      return fail(IKBO_ERR_UNSUPPORTED, "the log-sum-exp output needs a bf16 plan without self rows");
+    const size_t es = elem_size(p->dtype);
+    const size_t cand_bytes = static_cast<size_t>(p->n_cand) * p->n_q * p->H * p->d * es;
+    const size_t kv_bytes = static_cast<size_t>(p->total_len) * p->H * p->d * es;
+    const size_t lse_bytes = static_cast<size_t>(p->n_cand) * p->n_q * p->H * sizeof(float);
+    if (reinterpret_cast<uintptr_t>(lse) & 3) return fail(IKBO_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    if (overlaps(lse, lse_bytes, q_cand, cand_bytes) || overlaps(lse, lse_bytes, k, kv_bytes) ||
+        overlaps(lse, lse_bytes, v, kv_bytes) || overlaps(lse, lse_bytes, out_cand, cand_bytes))
+      return fail(IKBO_ERR_INVALID_ARG, "lse overlaps another tensor");
+  }
   if (p->hp.items.empty()) return IKBO_OK;
 
   ikbo::AttnParams ap{};
+  ap.lse = lse;
   ap.q_cand = q_cand;
   ap.q_user = q_user;
   ap.k = k;
@@ -514,6 +527,15 @@ int ikbo_attn_fwd_hostmap(void* plan, const int32_t* user_offsets_host, const in
   } catch (...) {
     return fail(IKBO_ERR_INVALID_ARG, "unexpected host error");
   }
+}
+
+int ikbo_attn_fwd_train(void* plan, const void* q_cand, const void* k_user, const void* v_user, float scale,
+                        void* out_cand, float* lse, void* stream) {
+  if (!plan) return fail(IKBO_ERR_INVALID_ARG, "plan is null");
+  Plan* p = static_cast<Plan*>(plan);
+  if (p->built && p->n_cand > 0 && !lse) return fail(IKBO_ERR_INVALID_ARG, "lse is null");
+  return launch_planned(p, q_cand, nullptr, k_user, v_user, scale, out_cand, nullptr,
+                        static_cast<hipStream_t>(stream), lse);
 }
 
 void ikbo_plan_destroy(void* plan) {

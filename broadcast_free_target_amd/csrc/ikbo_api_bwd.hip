@@ -42,7 +42,11 @@ struct Bwd {
   DevBuf ws_rows;         // Q and dO rows in user-sorted order, per head (zeroed padding)
   HostPlan hp;            // dQ work items (the forward's planner) and the CSR grouping
   std::vector<WorkItem> items_b;
+  std::vector<WorkItem> tmp;        // scratch of the XCD interleave
+  std::vector<int64_t> gcost;
+  std::vector<int32_t> gbin;
   int64_t n_items_a = 0, n_items_b = 0, n_groups = 0;
+  int64_t n_real_a = 0, n_real_b = 0;  // items before the interleave's padding
   TimedEvents timed;      // per timed call: dQ kernel start/end, dK/dV kernel start/end
   ~Bwd() {
     timed.release();
@@ -53,6 +57,56 @@ struct Bwd {
     ws_rows.release();
   }
 };
+
+// Reorders a longest-first list of one-workgroup-per-item launches so that all
+// items of one (user, head) run on one XCD and every XCD still gets a
+// longest-first, balanced share: the dispatcher places workgroup b on XCD
+// b % 8 and starts an XCD's workgroups in order of b.  (user, head) groups go to
+// 8 bins, largest total cost first, each into the least loaded bin; position
+// 8 j + x then holds bin x's j-th item, and the list is padded with empty items
+// (no keys, no rows: a workgroup that writes nothing) to 8 times the largest
+// bin.  cost(item) estimates an item's time.
+template <typename Cost>
+void xcd_interleave(std::vector<WorkItem>* items, const int32_t* offs, int32_t n_users, int32_t H, Cost cost,
+                    std::vector<WorkItem>* tmp, std::vector<int64_t>* gcost, std::vector<int32_t>* gbin) {
+  constexpr int kBins = 8;
+  const size_t n = items->size();
+  if (n < 2 * kBins || n_users < 1) return;
+  auto group_of = [&](const WorkItem& it) {
+    const int32_t u = static_cast<int32_t>(std::upper_bound(offs, offs + n_users + 1, it.kv_base) - offs - 1);
+    return static_cast<int64_t>(std::min(std::max(u, 0), n_users - 1)) * H + it.h;
+  };
+  const int64_t n_groups = static_cast<int64_t>(n_users) * H;
+  gcost->assign(n_groups, 0);
+  for (const WorkItem& it : *items) (*gcost)[group_of(it)] += cost(it);
+  std::vector<std::pair<int64_t, int64_t>> ord;
+  ord.reserve(n_groups);
+  for (int64_t g = 0; g < n_groups; ++g)
+    if ((*gcost)[g] > 0) ord.emplace_back(-(*gcost)[g], g);
+  std::sort(ord.begin(), ord.end());
+  int64_t load[kBins] = {};
+  gbin->assign(n_groups, 0);
+  for (const auto& o : ord) {
+    int b = 0;
+    for (int j = 1; j < kBins; ++j)
+      if (load[j] < load[b]) b = j;
+    (*gbin)[o.second] = b;
+    load[b] -= o.first;
+  }
+  size_t cnt[kBins] = {};
+  for (const WorkItem& it : *items) ++cnt[(*gbin)[group_of(it)]];
+  const size_t per = *std::max_element(cnt, cnt + kBins);
+  WorkItem empty{};
+  empty.grp = -1;
+  empty.nchunk = 1;
+  tmp->assign(per * kBins, empty);
+  size_t next[kBins] = {};
+  for (const WorkItem& it : *items) {  // longest first within each bin, as in the input
+    const int b = (*gbin)[group_of(it)];
+    (*tmp)[next[b]++ * kBins + b] = it;
+  }
+  items->swap(*tmp);
+}
 
 }  // namespace
 
@@ -84,7 +138,7 @@ int ikbo_bwd_create(void** bwd) {
 int ikbo_attn_bwd(void* bwd, const int32_t* user_offsets, const int32_t* cand_to_user, int32_t n_users, int32_t n_cand,
                   int32_t n_q, int32_t H, int32_t d, float scale, const void* q_cand, const void* k_user,
                   const void* v_user, const void* out, const void* dout, void* dq_cand, void* dk_user, void* dv_user,
-                  void* stream_) {
+                  const float* lse, void* stream_) {
   try {
     if (!bwd) return fail(IKBO_ERR_INVALID_ARG, "bwd is null");
     Bwd* b = static_cast<Bwd*>(bwd);
@@ -121,13 +175,14 @@ int ikbo_attn_bwd(void* bwd, const int32_t* user_offsets, const int32_t* cand_to
                                reinterpret_cast<uintptr_t>(dout) | reinterpret_cast<uintptr_t>(dq_cand) |
                                reinterpret_cast<uintptr_t>(dk_user) | reinterpret_cast<uintptr_t>(dv_user);
     if (align_or & 15) return fail(IKBO_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
-    const void* ins[5] = {q_cand, k_user, v_user, out, dout};
-    const size_t in_sz[5] = {qb, kb, kb, qb, qb};
+    if (reinterpret_cast<uintptr_t>(lse) & 3) return fail(IKBO_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    const void* ins[6] = {q_cand, k_user, v_user, out, dout, lse};
+    const size_t in_sz[6] = {qb, kb, kb, qb, qb, lse ? static_cast<size_t>(R) * H * sizeof(float) : 0};
     void* outs[3] = {dq_cand, dk_user, dv_user};
     const size_t out_sz[3] = {qb, kb, kb};
     for (int i = 0; i < 3; ++i) {
       if (out_sz[i] == 0) continue;
-      for (int j = 0; j < 5; ++j)
+      for (int j = 0; j < 6; ++j)
         if (in_sz[j] && overlaps(outs[i], out_sz[i], ins[j], in_sz[j])) return fail(IKBO_ERR_INVALID_ARG, "a gradient aliases an input");
       for (int j = i + 1; j < 3; ++j)
         if (out_sz[j] && overlaps(outs[i], out_sz[i], outs[j], out_sz[j])) return fail(IKBO_ERR_INVALID_ARG, "gradients overlap");
@@ -152,6 +207,18 @@ int ikbo_attn_bwd(void* bwd, const int32_t* user_offsets, const int32_t* cand_to
     }
     std::stable_sort(b->items_b.begin(), b->items_b.end(),
                      [](const WorkItem& x, const WorkItem& y) { return x.nrows > y.nrows; });
+    // Items of one (user, head) share its K/V (dQ: row tiles) or its sorted
+    // Q/dO rows (dK/dV: key blocks): keep them on one XCD's L2.
+    b->n_real_a = static_cast<int64_t>(b->hp.items.size());
+    b->n_real_b = static_cast<int64_t>(b->items_b.size());
+    if (env_int("IKBO_XCD_BINS", 8) > 1) {
+      xcd_interleave(&b->hp.items, user_offsets, n_users, H,
+                     [](const WorkItem& it) { return static_cast<int64_t>(it.k1 - it.k0) + 128; }, &b->tmp, &b->gcost,
+                     &b->gbin);
+      xcd_interleave(&b->items_b, user_offsets, n_users, H,
+                     [](const WorkItem& it) { return static_cast<int64_t>(it.nrows + 64) * (it.k1 - it.k0); }, &b->tmp,
+                     &b->gcost, &b->gbin);
+    }
     const int64_t na = static_cast<int64_t>(b->hp.items.size()), nb = static_cast<int64_t>(b->items_b.size());
     if (na > std::numeric_limits<int32_t>::max() || nb > std::numeric_limits<int32_t>::max() ||
         R + ikbo::kBwdPad > std::numeric_limits<int32_t>::max())
@@ -191,6 +258,7 @@ int ikbo_attn_bwd(void* bwd, const int32_t* user_offsets, const int32_t* cand_to
     p.dk = dk_user;
     p.dv = dv_user;
     p.cand_perm = reinterpret_cast<const int32_t*>(base + items_bytes);
+    p.lse_in = lse;
     p.qrow = static_cast<int32_t*>(b->ws.ptr);
     p.lse = reinterpret_cast<float*>(p.qrow + rp);
     p.dd = p.lse + rp * H;
@@ -223,7 +291,7 @@ int ikbo_attn_bwd(void* bwd, const int32_t* user_offsets, const int32_t* cand_to
 int ikbo_bwd_info(void* bwd, int64_t* info, int32_t n_info) {
   if (!bwd || !info || n_info < 0) return fail(IKBO_ERR_INVALID_ARG, "null argument");
   Bwd* b = static_cast<Bwd*>(bwd);
-  const int64_t v[3] = {b->n_items_a, b->n_items_b, b->n_groups};
+  const int64_t v[3] = {b->n_real_a, b->n_real_b, b->n_groups};
   for (int i = 0; i < std::min<int32_t>(n_info, 3); ++i) info[i] = v[i];
   return IKBO_OK;
 }

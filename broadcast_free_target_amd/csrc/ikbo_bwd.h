@@ -44,6 +44,11 @@ struct BwdParams {
   // padding rows are zero (never written).
   uint16_t* qs;
   uint16_t* dos;
+  // Optional: the forward's natural-log log-sum-exp per (row, head), [C, n_q, H]
+  // fp32.  Given, the dQ kernel skips its log-sum-exp pass over the keys, every
+  // key chunk of a split row uses the row's whole-range value, and the merge
+  // sums the chunks' partials; null, the dQ kernel recomputes it.
+  const float* lse_in;
   int32_t rows_total;   // R = n_cand * n_q
   int32_t H;
   int32_t n_q;

@@ -198,11 +198,14 @@ __global__ __launch_bounds__(kNT, 2) void ikbo_bwd_dq_kernel(BwdParams P) {
   };
   const float c2 = P.scale_log2;
 
-  // Pass 1: base-2 log-sum-exp of each row over the user's keys.
+  // Pass 1: base-2 log-sum-exp of each row over the user's keys (skipped when
+  // the forward's value is given: natural log, converted to base 2).
   float m = kNegInf, l = 0.0f;
-  if (ntiles > 0) issue(0, false);
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) {
+  const bool given = P.lse_in != nullptr;
+  const int ntiles1 = given ? 0 : ntiles;
+  if (ntiles1 > 0) issue(0, false);
+  for (int t = 0; t < ntiles1; ++t) {
+    if (t + 1 < ntiles1) {
       issue(t + 1, false);
       wait_vmcnt<LPT>();
     } else {
@@ -236,7 +239,8 @@ __global__ __launch_bounds__(kNT, 2) void ikbo_bwd_dq_kernel(BwdParams P) {
     }
     __syncthreads();
   }
-  const float lse = L > 0 ? m + log2f(l) : 0.0f;
+  const float lse = given ? (row_ok && L > 0 ? P.lse_in[qrow * P.H + it.h] * 1.4426950408889634f : 0.0f)
+                          : (L > 0 ? m + log2f(l) : 0.0f);
 
   // Pass 2: dQ^T += K^T dS^T.
   f32x16_t dqa[kDB];
@@ -367,7 +371,12 @@ __global__ __launch_bounds__(256) void ikbo_bwd_merge_kernel(BwdParams P) {
   const int64_t srow = tag & ((1 << 27) - 1);
   float lse = 0.0f;
   f32x4_t acc;
-  switch (nchunk) {
+  if (P.lse_in) {  // every chunk used the row's whole-range log-sum-exp: the partials add up
+    lse = rec[0][0];
+    acc = f32x4_t{0, 0, 0, 0};
+    for (int ch = 0; ch < nchunk; ++ch)
+      acc += *reinterpret_cast<const f32x4_t*>(P.ws_dq + ((slot0 + ch) * kBwdRowsA + r) * D + d0);
+  } else switch (nchunk) {
     case 1: acc = merge_dq<1>(rec, P.ws_dq, slot0, r, d0, &lse); break;
     case 2: acc = merge_dq<2>(rec, P.ws_dq, slot0, r, d0, &lse); break;
     case 3: acc = merge_dq<3>(rec, P.ws_dq, slot0, r, d0, &lse); break;

@@ -34,6 +34,8 @@ struct AttnParams {
   float* ws_rec;          // split partials: [slots, tile_rows, 4] row records: running max m,
                           // running sum l, output unit (row * H + h, -1: no row) and
                           // nchunk | kind << 16, the last two as int32 bits
+  float* lse;             // optional (bf16 kernels, target rows): [n_cand, n_q, H] natural-log
+                          // log-sum-exp of each row's scaled scores, or null
   uint64_t* trace;        // optional: [n_items, 6] per-item records (bf16 kernel), or null
   int32_t kv_reverse;     // 4-wave bf16 kernel: 1 = visit each item's key tiles last to first
   int32_t n_bins;         // 4-wave bf16 kernel: XCD bins of the work list (0: none), see HostPlan

@@ -75,6 +75,12 @@ __device__ __forceinline__ int tile_off(int row, int chunk) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Natural-log log-sum-exp of a row from its base-2 reference m and sum l
+// (l = sum_j 2^(x_j - m)); -inf for a row without keys.
+__device__ __forceinline__ float row_lse(float m, float l) {
+  return l > 0.0f ? (m + __log2f(l)) * 0.69314718055994531f : kNegInf;
+}
+
 // Row record of a split partial: m, l, output unit (-1 when the tile row is
 // empty) and nchunk | kind << 16.
 __device__ __forceinline__ f32x4_t split_record(float m, float l, int64_t qrow, const WorkItem& it, int H) {
@@ -421,6 +427,7 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
     // Lane holds O^T rows d = mb*32 + (i/4)*8 + g*4 + i%4 of query row r_w.
     if (it.grp < 0) {
       if (qrow >= 0) {
+        if (P.lse && !causal && g == 0) P.lse[qrow * P.H + it.h] = row_lse(m_run, l_run);
         uint16_t* ob = static_cast<uint16_t*>(causal ? P.out_user : P.out_cand);
         uint16_t* op = ob + (qrow * P.H + it.h) * D + g * 4;
         const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
@@ -504,6 +511,7 @@ __device__ __forceinline__ void finish_half(const AttnParams& P, const WorkItem&
   }
   if (it.grp < 0) {
     if (qrow >= 0) {
+      if (P.lse && !causal && V0 == 0 && g == 0) P.lse[qrow * P.H + it.h] = row_lse(M, L);
       uint16_t* ob = static_cast<uint16_t*>(causal ? P.out_user : P.out_cand);
       uint16_t* op = ob + (qrow * P.H + it.h) * D + g * 4;
       const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -760,6 +768,17 @@ __global__ __launch_bounds__(256) void ikbo_merge_kernel(AttnParams P) {
   }
   uint16_t* ob = static_cast<uint16_t*>((tag >> 16) == kKindSelf ? P.out_user : P.out_cand);
   *reinterpret_cast<u32x2_t*>(ob + static_cast<int64_t>(unit) * D + d0) = packed;
+  if (P.lse && d0 == 0 && (tag >> 16) == kKindTarget) {
+    // the row's log-sum-exp over all chunks: 2^M sum_c 2^(m_c - M) l_c
+    float M = kNegInf;
+#pragma unroll
+    for (int ch = 0; ch < kMaxSplit; ++ch) M = fmaxf(M, m[ch]);
+    const float mu = (M == kNegInf) ? 0.0f : M;
+    float L = 0.0f;
+#pragma unroll
+    for (int ch = 0; ch < kMaxSplit; ++ch) L += ch < nchunk ? exp2_fast(m[ch] - mu) * l[ch] : 0.0f;
+    P.lse[unit] = row_lse(mu, L);
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -50,6 +50,7 @@ SIGNATURES = {
     "ikbo_attn_fwd_planned": (ctypes.c_int, [_P, _P, _P, _P, _P, _F, _P, _P, _P]),
     "ikbo_attn_fwd_hostmap": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _F, _P, _P,
                                              _P]),
+    "ikbo_attn_fwd_train": (ctypes.c_int, [_P, _P, _P, _P, _F, _P, _P, _P]),
     "ikbo_plan_destroy": (None, [_P]),
     "ikbo_plan_info": (ctypes.c_int, [_P, _LP, _I]),
     "ikbo_plan_timing": (ctypes.c_int, [_P, _I]),
@@ -67,7 +68,8 @@ SIGNATURES = {
     "ikbo_lce3_create": (ctypes.c_int, [ctypes.POINTER(_P), _P, _I, _I, _I, _I, _I, _P]),
     "ikbo_lce3_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "ikbo_bwd_create": (ctypes.c_int, [ctypes.POINTER(_P)]),
-    "ikbo_attn_bwd": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "ikbo_attn_bwd": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                     _P]),
     "ikbo_bwd_info": (ctypes.c_int, [_P, _LP, _I]),
     "ikbo_bwd_timing": (ctypes.c_int, [_P, _I]),
     "ikbo_bwd_timing_read": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
@@ -319,8 +321,9 @@ def ikbo_plan_create(user_offsets_host, cand_to_user_host, n_users, n_cand, n_q,
 
 
 def _plan_dims(offs, n_users, n_cand, n_q, H, d, dtype, with_self):
+    """(element size, q/out bytes, k/v bytes, with_self, lse bytes) of a request."""
     es = _es(dtype)
-    return (es, n_cand * n_q * H * d * es, int(offs[n_users]) * H * d * es, bool(with_self))
+    return (es, n_cand * n_q * H * d * es, int(offs[n_users]) * H * d * es, bool(with_self), n_cand * n_q * H * 4)
 
 
 def ikbo_plan_build(plan, user_offsets_host, cand_to_user_host, n_users, n_cand, n_q, H, d, dtype,
@@ -338,7 +341,7 @@ def ikbo_attn_fwd_planned(plan, q_cand, q_user, k_user, v_user, scale, out_cand,
                           stream=None) -> int:
     dims = _PLAN_DIMS.get(plan)
     if dims is not None:
-        es, cand_bytes, kv_bytes, with_self = dims
+        es, cand_bytes, kv_bytes, with_self, _ = dims
         _need(q_cand, cand_bytes, "q_cand", es)
         _need(out_cand, cand_bytes, "out_cand", es)
         _need(k_user, kv_bytes, "k_user", es)
@@ -359,7 +362,7 @@ def ikbo_attn_fwd_hostmap(plan, user_offsets_host, cand_to_user_host, n_users, n
     c2u = np.ascontiguousarray(cand_to_user_host, dtype=np.int32)
     dims = _plan_dims(offs, n_users, n_cand, n_q, H, d, dtype, with_self) if offs.size > n_users >= 0 else None
     if dims is not None:
-        es, cand_bytes, kv_bytes, _ = dims
+        es, cand_bytes, kv_bytes, _, _ = dims
         _need(q_cand, cand_bytes, "q_cand", es)
         _need(out_cand, cand_bytes, "out_cand", es)
         _need(k_user, kv_bytes, "k_user", es)
@@ -373,6 +376,20 @@ def ikbo_attn_fwd_hostmap(plan, user_offsets_host, cand_to_user_host, n_users, n
         _ptr(q_user), _ptr(k_user), _ptr(v_user), float(scale), _ptr(out_cand), _ptr(out_user), _stream(stream)))
     _PLAN_DIMS[plan] = dims
     return rc
+
+
+def ikbo_attn_fwd_train(plan, q_cand, k_user, v_user, scale, out_cand, lse, stream=None) -> int:
+    """The planned launch that also writes each row's log-sum-exp (fp32 [n_cand, n_q, H])."""
+    dims = _PLAN_DIMS.get(plan)
+    if dims is not None:
+        es, cand_bytes, kv_bytes, _, lse_bytes = dims
+        _need(q_cand, cand_bytes, "q_cand", es)
+        _need(out_cand, cand_bytes, "out_cand", es)
+        _need(k_user, kv_bytes, "k_user", es)
+        _need(v_user, kv_bytes, "v_user", es)
+        _need(lse, lse_bytes, "lse", 4)
+    return _check(load_library().ikbo_attn_fwd_train(
+        plan, _ptr(q_cand), _ptr(k_user), _ptr(v_user), float(scale), _ptr(out_cand), _ptr(lse), _stream(stream)))
 
 
 def ikbo_plan_destroy(plan) -> None:
@@ -466,8 +483,10 @@ def ikbo_bwd_create() -> int:
 
 
 def ikbo_attn_bwd(bwd, user_offsets_host, cand_to_user_host, n_users, n_cand, n_q, H, d, scale, q_cand, k_user,
-                  v_user, out, dout, dq_cand, dk_user, dv_user, stream=None) -> int:
-    """Gradients of target attention; the mapping arrays are host int32 arrays."""
+                  v_user, out, dout, dq_cand, dk_user, dv_user, stream=None, lse=None) -> int:
+    """Gradients of target attention; the mapping arrays are host int32 arrays.
+    lse (optional): the forward's log-sum-exp, fp32 [n_cand, n_q, H]."""
+    _need(lse, n_cand * n_q * H * 4, "lse", 4)
     offs = np.ascontiguousarray(user_offsets_host, dtype=np.int32)
     c2u = np.ascontiguousarray(cand_to_user_host, dtype=np.int32)
     if offs.size >= n_users + 1:
@@ -479,7 +498,7 @@ def ikbo_attn_bwd(bwd, user_offsets_host, cand_to_user_host, n_users, n_cand, n_
             _need(t, kv, nm, 2)
     return _check(load_library().ikbo_attn_bwd(
         bwd, _host_i32(offs), _host_i32(c2u), n_users, n_cand, n_q, H, d, float(scale), _ptr(q_cand),
-        _ptr(k_user), _ptr(v_user), _ptr(out), _ptr(dout), _ptr(dq_cand), _ptr(dk_user), _ptr(dv_user),
+        _ptr(k_user), _ptr(v_user), _ptr(out), _ptr(dout), _ptr(dq_cand), _ptr(dk_user), _ptr(dv_user), _ptr(lse),
         _stream(stream)))
 
 

@@ -218,6 +218,13 @@ int ikbo_attn_fwd_materialized(const void* q_cand, const void* k_user, const voi
  *   the host).  The tensors are checked against the new request first; on
  *   any error nothing is launched and the plan keeps its previous build
  *   unless the error came from the build itself.
+ * ikbo_attn_fwd_train: ikbo_attn_fwd_planned for a bf16 plan without self
+ *   rows that also writes lse [n_cand, n_q, H] (fp32, 4-byte aligned): the
+ *   natural-log log-sum-exp of each row's scaled scores over its user's keys,
+ *   ln sum_j exp(scale * q . k_j) (-inf for users with no keys), which the
+ *   backward takes instead of recomputing it (AI-infra guide, section 4.6.3:
+ *   the backward rebuilds P from the scores and the saved statistic).
+ *   UNSUPPORTED for fp32 plans and plans with self rows.
  * ikbo_plan_destroy: frees the plan after synchronising its device.
  */
 int ikbo_plan_create(const int32_t* user_offsets_host, const int32_t* cand_to_user_host,
@@ -233,6 +240,8 @@ int ikbo_attn_fwd_hostmap(void* plan, const int32_t* user_offsets_host, const in
                           int32_t n_users, int32_t n_cand, int32_t n_q, int32_t H, int32_t d, int32_t dtype,
                           int32_t with_self, const void* q_cand, const void* q_user, const void* k_user,
                           const void* v_user, float scale, void* out_cand, void* out_user, void* stream);
+int ikbo_attn_fwd_train(void* plan, const void* q_cand, const void* k_user, const void* v_user, float scale,
+                        void* out_cand, float* lse, void* stream);
 void ikbo_plan_destroy(void* plan);
 
 /*
@@ -354,7 +363,10 @@ void ikbo_lce_destroy(void* lce);
  *   int32 arrays (as an inference or training runtime holds them); the tensors
  *   are bf16 device arrays, 16-byte aligned, row-major: q_cand, out (the
  *   forward output), dout, dq_cand [n_cand, n_q, H, d]; k_user, v_user,
- *   dk_user, dv_user [user_offsets[n_users], H, d].  d must be 128.  Every
+ *   dk_user, dv_user [user_offsets[n_users], H, d].  d must be 128.  lse is
+ *   optional: the forward's log-sum-exp [n_cand, n_q, H] fp32 as
+ *   ikbo_attn_fwd_train writes it; given, the dQ kernel takes it instead of
+ *   recomputing it (one pass over the keys less), null, it recomputes.  Every
  *   gradient element is written: users with no candidates get zero dk/dv
  *   rows, candidates of users with no keys zero dq rows.  Enqueues two kernels
  *   on `stream` and returns without synchronising (it may wait for the call
@@ -372,7 +384,7 @@ int ikbo_bwd_create(void** bwd);
 int ikbo_attn_bwd(void* bwd, const int32_t* user_offsets, const int32_t* cand_to_user, int32_t n_users,
                   int32_t n_cand, int32_t n_q, int32_t H, int32_t d, float scale, const void* q_cand,
                   const void* k_user, const void* v_user, const void* out, const void* dout, void* dq_cand,
-                  void* dk_user, void* dv_user, void* stream);
+                  void* dk_user, void* dv_user, const float* lse, void* stream);
 int ikbo_bwd_info(void* bwd, int64_t* info, int32_t n_info);
 int ikbo_bwd_timing(void* bwd, int32_t enable);
 int ikbo_bwd_timing_read(void* bwd, float* dq_ms, float* dkv_ms, int32_t max_n, int32_t* n);

@@ -52,6 +52,7 @@ __all__ = [
     "group_csr",
     "target_attention",
     "target_attention_rows",
+    "target_attention_lse",
     "self_attention_causal",
     "self_attention_rows",
     "chunk_partial",
@@ -209,6 +210,34 @@ def target_attention_rows(q_cand, k_user, v_user, user_offsets, cand_to_user, sc
         kc, vc = _broadcast_user_kv(k_user, v_user, offs, int(c2u[c]))
         q = _as_f64(q_cand[c, i, h]).reshape(1, 1, d)
         out[n] = _attend(q, kc[:, h:h + 1, :], vc[:, h:h + 1, :], sc)[0, 0]
+    return out
+
+
+def target_attention_lse(q_cand, k_user, user_offsets, cand_to_user, scale,
+                         cands: Optional[Iterable[int]] = None) -> np.ndarray:
+    """The per-row statistic a training forward keeps for its backward: the
+    natural-log log-sum-exp of each row's scaled scores over its user's keys,
+    lse = log sum_j exp(s_j) = m + log sum_j exp(s_j - m) with m = max_j s_j
+    (AI-infra guide, section 4.6.3).  Computed on each candidate's own copy of
+    its user's keys, like ``target_attention``.  fp64 [C, n_q, H] (or the given
+    candidates); -inf for users with no keys (the log of an empty sum).
+    """
+    q_cand = np.asarray(q_cand)
+    offs = np.asarray(user_offsets, dtype=np.int64)
+    c2u = np.asarray(cand_to_user, dtype=np.int64)
+    sc = _fp32_scale(scale)
+    idx = range(q_cand.shape[0]) if cands is None else list(cands)
+    out = np.empty((len(idx),) + q_cand.shape[1:3], dtype=np.float64)
+    for n, c in enumerate(idx):
+        u = int(c2u[c])
+        lo, hi = int(offs[u]), int(offs[u + 1])
+        if hi == lo:
+            out[n] = -np.inf
+            continue
+        kc = np.array(k_user[lo:hi], dtype=np.float64, copy=True)  # this candidate's copy
+        s = _scores(_as_f64(q_cand[c]), kc, sc)                   # [H, n_q, L]
+        m = np.max(s, axis=-1)
+        out[n] = np.transpose(m + np.log(np.sum(np.exp(s - m[..., None]), axis=-1)), (1, 0))
     return out
 
 

@@ -43,7 +43,18 @@ def _forward_out_bits(w):
     return f32_to_bf16_bits(out.astype(np.float32)).reshape(out.shape)
 
 
-def _run(w, out_bits, bwd=None):
+def _lse(w):
+    """The oracle's row log-sum-exp as fp32 on the device (the statistic a
+    training forward hands the backward), independent of the forward kernels."""
+    q, k = w.values("q_cand"), w.values("k_user")
+    ref = np.concatenate(oracle_in_chunks(
+        lambda c: O.target_attention_lse(q, k, w.user_offsets, w.cand_to_user, w.scale, cands=c),
+        range(w.n_cand)), axis=0)
+    import torch
+    return torch.from_numpy(ref.astype(np.float32)).cuda()
+
+
+def _run(w, out_bits, bwd=None, lse=None):
     import torch
     import broadcast_free_target_amd as ikbo
     t = {n: dev_tensor(w.raw(n), "bf16") for n in ("q_cand", "k_user", "v_user", "dout")}
@@ -55,7 +66,7 @@ def _run(w, out_bits, bwd=None):
     h = ikbo.ikbo_bwd_create() if own else bwd
     try:
         ikbo.ikbo_attn_bwd(h, w.user_offsets, w.cand_to_user, w.n_users, w.n_cand, w.n_q, w.H, w.d, w.scale,
-                           t["q_cand"], t["k_user"], t["v_user"], out, t["dout"], dq, dk, dv)
+                           t["q_cand"], t["k_user"], t["v_user"], out, t["dout"], dq, dk, dv, lse=lse)
         torch.cuda.synchronize()
     finally:
         if own:
@@ -83,12 +94,13 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("given_lse", [False, True])
 @pytest.mark.parametrize("i", range(len(CASES)))
-def test_bwd_edges(i):
+def test_bwd_edges(i, given_lse):
     lengths, counts, n_q, H = CASES[i]
     w = _custom(3300 + i, lengths, counts, n_q, H)
-    say(f"case bwd {CASES[i]}")
-    got = _run(w, _forward_out_bits(w))
+    say(f"case bwd {CASES[i]} given lse {given_lse}")
+    got = _run(w, _forward_out_bits(w), lse=_lse(w) if given_lse else None)
     ref = _oracle(w)
     for g, r, name in zip(got, ref, ("dq", "dk", "dv")):
         _close(g, r, name)
@@ -140,10 +152,12 @@ def test_bwd_large_request_full():
     out_bits = f32_to_bf16_bits(out.astype(np.float32)).reshape(out.shape)
     del out
     got = _run(w, out_bits)
-    say("  gradients computed; oracle by user")
+    got_lse = _run(w, out_bits, lse=_lse(w))
+    say("  gradients computed (recomputed and given log-sum-exp); oracle by user")
     ref = _oracle_by_user(w)
-    for g, r, name in zip(got, ref, ("dq", "dk", "dv")):
+    for g, g2, r, name in zip(got, got_lse, ref, ("dq", "dk", "dv")):
         _close(g, r, name)
+        _close(g2, r, name + " (given lse)")
 
 
 def test_bwd_single_key_users():
@@ -160,10 +174,11 @@ def test_bwd_single_key_users():
         _close(dv[k0:k0 + 1], ref[2][k0:k0 + 1], f"dv user {u}")
 
 
-def test_bwd_typical_request_full():
+@pytest.mark.parametrize("given_lse", [False, True])
+def test_bwd_typical_request_full(given_lse):
     w = make_bwd_workload("c2_typical")
-    say("case bwd c2_typical")
-    got = _run(w, _forward_out_bits(w))
+    say(f"case bwd c2_typical given lse {given_lse}")
+    got = _run(w, _forward_out_bits(w), lse=_lse(w) if given_lse else None)
     ref = _oracle(w)
     for g, r, name in zip(got, ref, ("dq", "dk", "dv")):
         _close(g, r, name)
@@ -292,20 +307,23 @@ def test_bwd_errors():
         ikbo.ikbo_bwd_destroy(h)
 
 
+@pytest.mark.parametrize("given_lse", [False, True])
 @pytest.mark.parametrize("no_split", ["1", "0"])
-def test_bwd_split_and_unsplit(no_split, monkeypatch):
+def test_bwd_split_and_unsplit(no_split, given_lse, monkeypatch):
     """Long key ranges split into chunks (merged in chunk order) and the
-    unsplit path both meet the bar; each is bitwise repeatable."""
+    unsplit path both meet the bar, with the log-sum-exp recomputed or given;
+    each is bitwise repeatable."""
     import broadcast_free_target_amd as ikbo
     monkeypatch.setenv("IKBO_NO_SPLIT", no_split)
     w = _custom(3700, (2048, 1500, 64, 900), (3, 40, 5, 1), n_q=2, H=2)
-    say(f"case bwd split disabled={no_split}")
+    say(f"case bwd split disabled={no_split} given lse {given_lse}")
     o = _forward_out_bits(w)
+    lse = _lse(w) if given_lse else None
     h = ikbo.ikbo_bwd_create()
     try:
-        a = _run(w, o, h)
+        a = _run(w, o, h, lse)
         groups = ikbo.ikbo_bwd_info(h)["dq_split_groups"]
-        b = _run(w, o, h)
+        b = _run(w, o, h, lse)
     finally:
         ikbo.ikbo_bwd_destroy(h)
     assert (groups == 0) == (no_split == "1")

@@ -270,6 +270,104 @@ def test_edge_fused(dtype, d, waves, split):
 
 
 # ---------------------------------------------------------------------------
+# the training forward's log-sum-exp
+# ---------------------------------------------------------------------------
+#
+# Bar: |lse - oracle| <= 1e-3.  The kernel's scores are fp32 sums of exact
+# bf16 products (relative error ~d * 2^-24 of sum |q k|, ~1e-5 here), kept in
+# base 2 and turned into ln with the hardware log2 (~1 ulp); |lse| is ~8 for
+# these inputs, so the error is ~1e-5 and the bar leaves ample margin.  Rows of
+# users with no keys must be -inf exactly.
+
+LSE_MAX_ABS = 1e-3
+
+
+def _train_forward(w, dev, lse_fill=float("nan")):
+    import torch
+    from broadcast_free_target_amd import ikbo_attn_fwd_train, ikbo_plan_create, ikbo_plan_destroy, ikbo_plan_info
+    out = empty_out(w.raw("q_cand").shape, "bf16")
+    lse = torch.full((w.n_cand, w.n_q, w.H), lse_fill, dtype=torch.float32, device="cuda")
+    plan = ikbo_plan_create(w.user_offsets, w.cand_to_user, w.n_users, w.n_cand, w.n_q, w.H, w.d, 0, 0)
+    try:
+        ikbo_attn_fwd_train(plan, dev["q_cand"], dev["k_user"], dev["v_user"], w.scale, out, lse)
+        torch.cuda.synchronize()
+        info = ikbo_plan_info(plan)
+    finally:
+        ikbo_plan_destroy(plan)
+    return out, lse.cpu().numpy().astype(np.float64), info
+
+
+def _check_lse(got, ref, what):
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), fin), f"{what}: finite pattern"
+    assert np.all(got[~fin] == -np.inf), f"{what}: rows without keys"
+    err = np.abs(got[fin] - ref[fin])
+    mx = float(err.max()) if err.size else 0.0
+    say(f"  {what} lse: max {mx:.3g}")
+    assert mx <= LSE_MAX_ABS, f"{what}: lse max {mx:.3g}"
+
+
+@pytest.mark.parametrize("name", ["c2_typical", "c3_skewed", "c4_large"])
+def test_train_forward_writes_lse(name):
+    """ikbo_attn_fwd_train: the same output bits as the planned launch, and each
+    row's log-sum-exp against the oracle (split rows through the merge, the
+    eight-wave and 4-wave kernels)."""
+    import torch
+    w = _wl(name)
+    say(f"case train forward {name}")
+    dev = upload(w)
+    out, lse, info = _train_forward(w, dev)
+    say(f"  plan {info}")
+    ref_out = empty_out(w.raw("q_cand").shape, "bf16")
+    run_planned(w, dev, ref_out)
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+    del dev
+    q, k = w.values("q_cand"), w.values("k_user")
+    ref = np.concatenate(oracle_in_chunks(
+        lambda c: O.target_attention_lse(q, k, w.user_offsets, w.cand_to_user, w.scale, cands=c),
+        range(w.n_cand)), axis=0)
+    _check_lse(lse, ref, name)
+
+
+@pytest.mark.parametrize("split", ["default", "forced", "off"])
+@pytest.mark.parametrize("waves", ["w8", "w4"])
+def test_train_forward_lse_edges(split, waves):
+    os.environ["IKBO_KERNEL"] = waves
+    if split == "forced":
+        os.environ["IKBO_MIN_CHUNK"] = "64"
+        os.environ["IKBO_SPLIT_SLOTS"] = "4096"
+    elif split == "off":
+        os.environ["IKBO_NO_SPLIT"] = "1"
+    w = _custom(70, (129, 0, 7, 1, 2100), (127, 2, 0, 3, 129), 2, 3, 128, "bf16")
+    say(f"case train forward edges split={split} waves={waves}")
+    dev = upload(w)
+    out, lse, _ = _train_forward(w, dev)
+    assert_close(to_f64(out), _oracle_target(w), "bf16", "train edges out")
+    _check_lse(lse, O.target_attention_lse(w.values("q_cand"), w.values("k_user"), w.user_offsets, w.cand_to_user,
+                                           w.scale), "edges")
+
+
+def test_train_forward_refuses_fp32_and_self_plans():
+    import torch
+    from broadcast_free_target_amd import (IKBO_ERR_UNSUPPORTED, IkboError, ikbo_attn_fwd_train, ikbo_plan_create,
+                                           ikbo_plan_destroy)
+    w = _custom(71, (10, 20), (3, 4), 1, 2, 128, "f32")
+    dev = upload(w)
+    say("case train forward refusals")
+    lse = torch.full((w.n_cand, 1, w.H), 7.0, device="cuda")
+    out = empty_out(w.raw("q_cand").shape, "f32", fill=7.0)
+    plan = ikbo_plan_create(w.user_offsets, w.cand_to_user, w.n_users, w.n_cand, 1, w.H, w.d, dtype_code("f32"), 0)
+    try:
+        with pytest.raises(IkboError) as e:
+            ikbo_attn_fwd_train(plan, dev["q_cand"], dev["k_user"], dev["v_user"], w.scale, out, lse)
+        assert e.value.status == IKBO_ERR_UNSUPPORTED
+    finally:
+        ikbo_plan_destroy(plan)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0) and torch.all(lse == 7.0)
+
+
+# ---------------------------------------------------------------------------
 # bitwise properties
 # ---------------------------------------------------------------------------
 

@@ -424,3 +424,76 @@ def test_planted_mistakes_are_caught(monkeypatch, name):
     ref = _brute_force(q, k, v, offs, c2u, sc)
     got = O.target_attention(q, k, v, offs, c2u, sc)
     assert not np.allclose(got, ref, atol=1e-12, rtol=0), f"mutant {name} slipped past the brute-force pin"
+
+
+# log-sum-exp of the rows (the statistic a training forward keeps) ------------
+def _brute_force_lse(q, k, offs, c2u, scale):
+    """log(sum_j exp(s_j)) with Python floats: math.fsum of exp(s_j - max) plus the max."""
+    C, n_q, H, d = q.shape
+    sc = float(np.float32(scale))
+    out = np.full((C, n_q, H), -np.inf)
+    for c in range(C):
+        u = int(c2u[c])
+        lo, hi = int(offs[u]), int(offs[u + 1])
+        for i in range(n_q):
+            for h in range(H):
+                if hi == lo:
+                    continue
+                s = [sc * math.fsum(float(q[c, i, h, e]) * float(k[j, h, e]) for e in range(d)) for j in range(lo, hi)]
+                mx = max(s)
+                out[c, i, h] = mx + math.log(math.fsum(math.exp(x - mx) for x in s))
+    return out
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_lse_brute_force(seed):
+    q, k, v, offs, c2u, sc = _tiny(seed=seed, lengths=(5, 0, 3, 1), c2u=(2, 0, 1, 3, 0, 2))
+    ref = _brute_force_lse(q, k, offs, c2u, sc)
+    got = O.target_attention_lse(q, k, offs, c2u, sc)
+    finite = np.isfinite(ref)
+    assert np.array_equal(finite, np.isfinite(got)) and np.all(got[~finite] == -np.inf)
+    assert np.max(np.abs(got[finite] - ref[finite])) <= 1e-12
+
+
+def test_lse_equals_library_logsumexp_and_normalises_the_weights():
+    """scipy's logsumexp of the score matrix, and exp(s - lse) sums to one."""
+    from scipy.special import logsumexp
+    q, k, v, offs, c2u, sc = _tiny(seed=9, lengths=(40, 7), c2u=(1, 0, 0, 1), n_q=3, H=2, d=16)
+    got = O.target_attention_lse(q, k, offs, c2u, sc)
+    for c in range(len(c2u)):
+        lo, hi = int(offs[c2u[c]]), int(offs[c2u[c] + 1])
+        for i in range(3):
+            for h in range(2):
+                s = float(sc) * (k[lo:hi, h] @ q[c, i, h])
+                assert abs(got[c, i, h] - logsumexp(s)) <= 1e-12
+                assert abs(np.exp(s - got[c, i, h]).sum() - 1.0) <= 1e-12
+
+
+def test_lse_closed_forms():
+    """Equal scores give s + log L; one key gives its score; scale 0 gives log L."""
+    q, k, v, offs, c2u, sc = _tiny(seed=4, lengths=(6, 1), c2u=(0, 1, 0), n_q=1, H=1, d=8)
+    k[0:6] = k[0]  # user 0: six equal keys
+    got = O.target_attention_lse(q, k, offs, c2u, sc)
+    s0 = float(sc) * float(q[0, 0, 0] @ k[0, 0])
+    assert abs(got[0, 0, 0] - (s0 + math.log(6))) <= 1e-12
+    s1 = float(sc) * float(q[1, 0, 0] @ k[6, 0])
+    assert abs(got[1, 0, 0] - s1) <= 1e-14
+    z = O.target_attention_lse(q, k, offs, c2u, 0.0)
+    assert abs(z[2, 0, 0] - math.log(6)) <= 1e-14
+
+
+def test_lse_planted_mistakes_fail_the_brute_force():
+    """Base-2 in place of natural log, a dropped scale, and the row maximum in
+    place of the log-sum-exp all leave the brute force."""
+    q, k, v, offs, c2u, sc = _tiny(seed=3)
+    ref = _brute_force_lse(q, k, offs, c2u, sc)
+    good = O.target_attention_lse(q, k, offs, c2u, sc)
+    assert np.max(np.abs(good - ref)) <= 1e-12
+    base2 = good / math.log(2)
+    unscaled = O.target_attention_lse(q, k, offs, c2u, 1.0)
+    rowmax = np.empty_like(good)
+    for c in range(len(c2u)):
+        lo, hi = int(offs[c2u[c]]), int(offs[c2u[c] + 1])
+        rowmax[c] = np.transpose(np.max(float(sc) * np.einsum("ihe,jhe->hij", q[c], k[lo:hi]), axis=-1), (1, 0))
+    for bad in (base2, unscaled, rowmax):
+        assert np.max(np.abs(bad - ref)) > 1e-3
