@@ -939,10 +939,22 @@ def main():
         ikbo.ikbo_attn_fwd_planned(plan, dev["q_cand"], dev.get("q_user"), dev["k_user"], dev["v_user"], w.scale,
                                    out_c, out_u, stream)
 
+    # One step is one ikbo_attn_fwd_hostmap call, made on the C ABI directly as
+    # a runtime would; the binding checks the same arguments once, here.
+    ikbo.ikbo_attn_fwd_hostmap(plan, offs_h, c2u_h, w.n_users, w.n_cand, w.n_q, w.H, w.d, dt_code, ws,
+                               dev["q_cand"], dev.get("q_user"), dev["k_user"], dev["v_user"], w.scale, out_c,
+                               out_u, stream)
+    c_hostmap = ikbo.load_library().ikbo_attn_fwd_hostmap
+    qu = dev.get("q_user")
+    c_args = (plan, offs_h.ctypes.data, c2u_h.ctypes.data, w.n_users, w.n_cand, w.n_q, w.H, w.d, dt_code, ws,
+              dev["q_cand"].data_ptr(), qu.data_ptr() if qu is not None else None, dev["k_user"].data_ptr(),
+              dev["v_user"].data_ptr(), float(w.scale), out_c.data_ptr(),
+              out_u.data_ptr() if out_u is not None else None, stream.cuda_stream)
+
     def step():  # plan build from the host mapping and launch, in one library call
-        ikbo.ikbo_attn_fwd_hostmap(plan, offs_h, c2u_h, w.n_users, w.n_cand, w.n_q, w.H, w.d, dt_code, ws,
-                                   dev["q_cand"], dev.get("q_user"), dev["k_user"], dev["v_user"], w.scale, out_c,
-                                   out_u, stream)
+        rc = c_hostmap(*c_args)
+        if rc != 0:
+            raise ikbo.IkboError(rc, ikbo.ikbo_last_error())
 
     info = ikbo.ikbo_plan_info(plan)
     for _ in range(args.warmup):
