@@ -811,6 +811,35 @@ def summarize_pmc(args):
     print(json.dumps(out), flush=True)
 
 
+def summarize_sq(args):
+    """Per-kernel SQ ratios from one rocprofv3 --pmc run holding SQ_INSTS_MFMA,
+    SQ_INSTS_VALU, SQ_INSTS_LDS, SQ_VALU_MFMA_BUSY_CYCLES, SQ_LDS_IDX_ACTIVE,
+    SQ_LDS_BANK_CONFLICT, SQ_WAIT_ANY, SQ_ACTIVE_INST_ANY and GRBM_GUI_ACTIVE.
+    GRBM_GUI_ACTIVE is counted per XCC (8 of them), so one XCC's active cycles
+    are the sum over 8; the MFMA and LDS busy fractions divide by those cycles
+    times the SIMD (1024) or CU (256) count, as the MfmaUtil and LdsUtil
+    metrics rocprofv3 lists do."""
+    rows = _pmc_rows(args.sq)
+    per = {}
+    for (_, _, name), d in rows.items():
+        if "ikbo" not in name:
+            continue
+        per.setdefault(name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", ""), []).append(d)
+    out = {}
+    for name, ds in per.items():
+        keys = set().union(*ds)
+        m = {k: float(np.mean([d.get(k, 0.0) for d in ds])) for k in keys}
+        g = lambda k: m.get(k, float("nan"))  # noqa: E731
+        cyc = g("GRBM_GUI_ACTIVE") / 8.0
+        mfma = max(g("SQ_INSTS_MFMA"), 1.0)
+        out[name] = {"dispatches": len(ds), "mfma_busy": g("SQ_VALU_MFMA_BUSY_CYCLES") / (cyc * 1024),
+                     "valu_per_mfma": (g("SQ_INSTS_VALU") - g("SQ_INSTS_MFMA")) / mfma,
+                     "lds_per_mfma": g("SQ_INSTS_LDS") / mfma, "lds_busy": g("SQ_LDS_IDX_ACTIVE") / (cyc * 256),
+                     "lds_bank_conflicts": g("SQ_LDS_BANK_CONFLICT"),
+                     "wait_share": g("SQ_WAIT_ANY") / max(g("SQ_WAIT_ANY") + g("SQ_ACTIVE_INST_ANY"), 1.0)}
+    print(json.dumps(out, indent=1), flush=True)
+
+
 def summarize_trace(args):
     """Per-kernel durations from a rocprofv3 --kernel-trace run of the
     benchmark: over all dispatches, and over the dispatches of timed region 2
@@ -868,7 +897,12 @@ def main():
     ap.add_argument("--out", help="--summarize-pmc: path of the JSON summary")
     ap.add_argument("--summarize-trace", dest="trace",
                     help="CPU only: per-kernel durations from a rocprofv3 --kernel-trace output directory")
+    ap.add_argument("--summarize-sq", dest="sq",
+                    help="CPU only: per-kernel SQ ratios from a rocprofv3 --pmc output directory")
     args = ap.parse_args()
+    if args.sq:
+        summarize_sq(args)
+        return
     if args.trace:
         summarize_trace(args)
         return
@@ -940,7 +974,8 @@ def main():
                                    out_c, out_u, stream)
 
     # One step is one ikbo_attn_fwd_hostmap call, made on the C ABI directly as
-    # a runtime would; the binding checks the same arguments once, here.
+    # a runtime would; the binding checks the same arguments once, in the first
+    # warm-up step.
     ikbo.ikbo_attn_fwd_hostmap(plan, offs_h, c2u_h, w.n_users, w.n_cand, w.n_q, w.H, w.d, dt_code, ws,
                                dev["q_cand"], dev.get("q_user"), dev["k_user"], dev["v_user"], w.scale, out_c,
                                out_u, stream)
@@ -957,7 +992,7 @@ def main():
             raise ikbo.IkboError(rc, ikbo.ikbo_last_error())
 
     info = ikbo.ikbo_plan_info(plan)
-    for _ in range(args.warmup):
+    for _ in range(args.warmup - 1):
         step()
     torch.cuda.synchronize()
 
