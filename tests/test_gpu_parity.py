@@ -139,6 +139,28 @@ def test_c4_large_full():
     say(f"  c4 full tensor ({got.size} values): max {mx:.3g} mean {mean:.3g}")
 
 
+def test_app11_shape_full():
+    """The App. 11 shape (32 users x 64 candidates, 64 query tokens each, L =
+    1024, H = 2): the 4-wave kernel's many-item plan, compared element by
+    element over the whole output tensor."""
+    w = _wl("p_app11")
+    say("case app11 planned (whole output tensor against the oracle)")
+    dev = upload(w)
+    out = empty_out(w.raw("q_cand").shape, "bf16")
+    info = run_planned(w, dev, out)
+    say(f"  plan {info}")
+    got = to_f64(out)
+    del dev, out
+    q, k, v = w.values("q_cand"), w.values("k_user"), w.values("v_user")
+
+    def chunk(cands):
+        return O.target_attention(q, k, v, w.user_offsets, w.cand_to_user, w.scale, cands=cands)
+
+    ref = np.concatenate(oracle_in_chunks(chunk, range(w.n_cand)), axis=0)
+    mx, mean = assert_close(got, ref, "bf16", "app11 full")
+    say(f"  app11 full tensor ({got.size} values): max {mx:.3g} mean {mean:.3g}")
+
+
 def test_c5_fused_self_target():
     from broadcast_free_target_amd import ikbo_self_target_fwd
     import torch
