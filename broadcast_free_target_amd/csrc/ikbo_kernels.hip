@@ -191,6 +191,16 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const
     for (int st = 0; st < D / 16; ++st)
       s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[st]), as_bf16x8(qf[st]), s[b], 0, 0, 0);
   }
+  // Issue order: K fragments three ahead of the MFMAs that use them (the
+  // scheduler would otherwise put each read right before its MFMA and wait on
+  // it, leaving the matrix cores idle for a whole LDS latency per MFMA).
+  __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+  for (int k = 0; k < D / 8 - 3; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
   // Lane value i of block b holds key  b*32 + (i/4)*8 + g*4 + i%4  of query row n.
   // Scores stay unscaled; p = exp2(c*s - m_ref).  The masked variant keeps a
   // bit per value for live keys (key inside the range, and not in the causal
@@ -263,26 +273,38 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const
       for (int j = 0; j < 8; ++j) pb[b][s2][j] = static_cast<__bf16>(s[b][s2 * 8 + j]);
 
   // V^T operand: lane k of each 16-lane group points at V[K0 + k/4][D0 + 4*(k%4)];
-  // the transposed read returns V[K0 .. K0+3][D0 + k] to lane k.
+  // the transposed read returns V[K0 .. K0+3][D0 + k] to lane k.  MFMA j of the
+  // tile is K-step (b, s2) = j / (D/32) of O^T block mb = j % (D/32): blocks
+  // alternate, so consecutive MFMAs are independent, and each one's V^T reads
+  // are issued two MFMAs ahead.
   const int kq = lane & 15, half = (lane >> 4) & 1;
-#pragma unroll
-  for (int mb = 0; mb < D / 32; ++mb) {
+  constexpr int NMB = D / 32, NJ = 4 * NMB;
+  auto vload = [&](int j) {
+    const int bs = j / NMB, mb = j % NMB;
     const int col = mb * 32 + half * 16 + 4 * (kq & 3);
+    const int r0 = (bs >> 1) * 32 + 16 * (bs & 1) + g * 4 + (kq >> 2);
+    const int offa = tile_off<D>(r0, col >> 3) + (col & 4);
+    const int offb = tile_off<D>(r0 + 8, col >> 3) + (col & 4);
+    const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(Vs + offa));
+    const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(Vs + offb));
+    return __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  i16x8_t vf[NJ];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+  for (int j = 0; j < NJ; ++j) vf[j] = vload(j);
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int r0 = b * 32 + 16 * s2 + g * 4 + (kq >> 2);
-        const int offa = tile_off<D>(r0, col >> 3) + (col & 4);
-        const int offb = tile_off<D>(r0 + 8, col >> 3) + (col & 4);
-        const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(Vs + offa));
-        const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(Vs + offb));
-        const i16x8_t v8 = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, v8), pb[b][s2], oacc[mb],
-                                                          0, 0, 0);
-      }
-    }
+  for (int j = 0; j < NJ; ++j) {
+    const int bs = j / NMB, mb = j % NMB;
+    oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[j]), pb[bs >> 1][bs & 1],
+                                                      oacc[mb], 0, 0, 0);
   }
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+  for (int k = 0; k < NJ - 2; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
 }
 
 template <int D, int NST>
