@@ -196,6 +196,8 @@ struct Plan {
   HostPlan hp;
   // device copies of the work list
   DevBuf d_items, d_ws_o, d_ws_rec;  // d_items: device copy of the plan buffer (copy mode)
+  DevBuf d_queue;                     // the 4-wave kernel's per-bin item counters (zeroed once)
+  bool static_deal = false;           // IKBO_STATIC_DEAL=1 at build: deal items statically instead
   // Pinned plan buffers, handed out in turn by the ring.  With in-place reads
   // (the default) the kernels read the work list from them; otherwise
   // (IKBO_PLAN_UPLOAD=copy) a copy to the device buffers above reads them.
@@ -219,6 +221,7 @@ struct Plan {
     d_items.release();
     d_ws_o.release();
     d_ws_rec.release();
+    d_queue.release();
     d_trace.release();
   }
 };
@@ -230,6 +233,7 @@ int plan_init(Plan* p) {
   p->n_cu = prop.multiProcessorCount;
   int rc = p->ring.init();
   if (rc != IKBO_OK) return rc;
+  if ((rc = p->d_queue.ensure(2 * ikbo::kMaxBins * sizeof(int32_t), true)) != IKBO_OK) return rc;
   const char* up = std::getenv("IKBO_PLAN_UPLOAD");
   p->read_in_place = !(up && std::strcmp(up, "copy") == 0);
   return IKBO_OK;
@@ -287,6 +291,7 @@ int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n
   p->with_self = with_self;
   p->stages = bf16_stages();
   p->variant = variant;
+  p->static_deal = env_int("IKBO_STATIC_DEAL", 0) != 0;
   p->total_len = offs[n_users];
   p->built = true;
   return IKBO_OK;
@@ -335,6 +340,7 @@ int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* 
   ap.ws_rec = static_cast<float*>(p->d_ws_rec.ptr);
   ap.n_bins = p->hp.n_bins;
   for (int b = 0; b <= ikbo::kMaxBins; ++b) ap.bin_off[b] = p->hp.bin_off[b];
+  ap.queue = p->static_deal ? nullptr : static_cast<int32_t*>(p->d_queue.ptr);
   ap.trace = nullptr;
   if (p->tracing && p->dtype == IKBO_DTYPE_BF16) {
     if ((rc = p->d_trace.ensure(p->hp.items.size() * 6 * sizeof(uint64_t), false)) != IKBO_OK) return rc;

@@ -40,6 +40,9 @@ struct AttnParams {
   int32_t kv_reverse;     // 4-wave bf16 kernel: 1 = visit each item's key tiles last to first
   int32_t n_bins;         // 4-wave bf16 kernel: XCD bins of the work list (0: none), see HostPlan
   int32_t bin_off[kMaxBins + 1];
+  int32_t* queue;         // 4-wave bf16 kernel: [2 * kMaxBins] per-bin next-item and finished-workgroup
+                          // counters, zero before a launch and left zero by it (the last workgroup
+                          // of a bin resets them); null: items dealt statically
 };
 
 // stages: depth of the HBM -> LDS ring (2, 3 or 4); 2 stages allow two

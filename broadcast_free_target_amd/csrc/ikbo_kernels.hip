@@ -171,14 +171,15 @@ __device__ __forceinline__ int64_t deal_position(int64_t pass, int w, int grid) 
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------
 
-// One K/V tile for one wave: S^T, online softmax update, O^T += V^T P^T.
-template <int D, bool MASK>
-__device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const uint16_t* __restrict__ Vs,
-                                          const u32x4_t (&qf)[D / 16], f32x16_t (&oacc)[D / 32],
-                                          float& m_run, float& l_run, int key_base, int key_end,
-                                          bool causal, int row_tok, float c, int lane) {
+// One K/V tile for one wave in three parts: S^T = K Q^T (qk_tile), the online
+// softmax update that turns S into the bf16 P^T operands (softmax_tile), and
+// O^T += V^T P^T (pv_tile).  tile_step runs the three in a row.
+
+// S^T of the tile's two 32-key blocks for this lane's query row.
+template <int D>
+__device__ __forceinline__ void qk_tile(const uint16_t* __restrict__ Ks, const u32x4_t (&qf)[D / 16],
+                                        f32x16_t (&s)[2], int lane) {
   const int n = lane & 31, g = lane >> 5;
-  f32x16_t s[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int row = b * 32 + n;
@@ -201,38 +202,54 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-  // Lane value i of block b holds key  b*32 + (i/4)*8 + g*4 + i%4  of query row n.
-  // Scores stay unscaled; p = exp2(c*s - m_ref).  The masked variant keeps a
-  // bit per value for live keys (key inside the range, and not in the causal
-  // future of the row).
-  uint32_t live = 0xffffffffu;
-  if (MASK) {
-    live = 0u;
+}
+
+// Kernel-side softmax scale in base 2.  A zero scale is replaced by a tiny
+// one: every weight is then 2^(tiny * s - tiny * max s) = 1.0f exactly, as
+// with a zero scale, while masked keys (scores set to -inf or +inf, see
+// mask_scores) still get weight 0 instead of 0 * inf = NaN.
+__device__ __forceinline__ float kernel_scale(float scale_log2) {
+  return scale_log2 != 0.0f ? scale_log2 : 1e-30f;
+}
+
+// Masks one tile's scores: lane value i of block b holds key
+// key_base + g*4 + off(b, i) of query row n, off(b, i) = b*32 + (i/4)*8 + i%4;
+// keys past key_end and, for causal rows, keys after the row's own token get a
+// score whose scaled value is -inf (weight 0).  Keys grow with off, so one bound
+// per lane decides every value; off is a constant of the unrolled code.
+__device__ __forceinline__ void mask_scores(f32x16_t (&s)[2], int key_base, int key_end, bool causal, int row_tok,
+                                            float c, int lane) {
+  const int kb = key_base + (lane >> 5) * 4;
+  const int lim = causal ? min(key_end, row_tok + 1) - kb : key_end - kb;
+  const float fill = c > 0.0f ? kNegInf : -kNegInf;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+  for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = key_base + b * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-        const bool ok = key < key_end && (!causal || key <= row_tok);
-        live |= (ok ? 1u : 0u) << (b * 16 + i);
-      }
-  }
+    for (int i = 0; i < 16; ++i)
+      if (!(b * 32 + (i >> 2) * 8 + (i & 3) < lim)) s[b][i] = fill;
+}
+
+// Online softmax of one tile (scores already masked): lazy reference update,
+// weights, row sum, and the bf16 P^T operands pb[b][s2] of the PV K-steps.
+// Scores stay unscaled; p = exp2(c*s - m_ref), c != 0.
+template <int D>
+__device__ __forceinline__ void softmax_tile(f32x16_t (&s)[2], f32x16_t (&oacc)[D / 32], float& m_run,
+                                             float& l_run, float c, bf16x8_t (&pb)[2][2]) {
   float mx;
   if (c >= 0.0f) {
     mx = kNegInf;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, (MASK && !((live >> (b * 16 + i)) & 1u)) ? kNegInf : s[b][i]);
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[b][i]);
   } else {
     mx = -kNegInf;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fminf(mx, (MASK && !((live >> (b * 16 + i)) & 1u)) ? -kNegInf : s[b][i]);
+      for (int i = 0; i < 16; ++i) mx = fminf(mx, s[b][i]);
   }
-  // Largest scaled score of the row in this tile; -inf when no key is live
-  // (mx * c is then -inf, or NaN for c == 0, both mapped to -inf).
+  // Largest scaled score of the row in this tile; -inf when every key is masked.
   float m_tile = mx * c;
   if (!(m_tile == m_tile)) m_tile = kNegInf;
   m_tile = pair_max(m_tile);
@@ -254,8 +271,7 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const
   for (int b = 0; b < 2; ++b) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float p = exp2_fast(fmaf(s[b][i], c, -m_use));
-      if (MASK) p = ((live >> (b * 16 + i)) & 1u) ? p : 0.0f;
+      const float p = exp2_fast(fmaf(s[b][i], c, -m_use));
       s[b][i] = p;
       rs += p;
     }
@@ -264,14 +280,19 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const
 
   // P^T operand of K-step (b, s2): the lane's values i = 8*s2 .. 8*s2+7, i.e. keys
   // b*32 + 16*s2 + {g*4 + 0..3, 8 + g*4 + 0..3}.
-  bf16x8_t pb[2][2];
 #pragma unroll
   for (int b = 0; b < 2; ++b)
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int j = 0; j < 8; ++j) pb[b][s2][j] = static_cast<__bf16>(s[b][s2 * 8 + j]);
+}
 
+// O^T += V^T P^T over the tile.
+template <int D>
+__device__ __forceinline__ void pv_tile(const uint16_t* __restrict__ Vs, const bf16x8_t (&pb)[2][2],
+                                        f32x16_t (&oacc)[D / 32], int lane) {
+  const int g = lane >> 5;
   // V^T operand: lane k of each 16-lane group points at V[K0 + k/4][D0 + 4*(k%4)];
   // the transposed read returns V[K0 .. K0+3][D0 + k] to lane k.  MFMA j of the
   // tile is K-step (b, s2) = j / (D/32) of O^T block mb = j % (D/32): blocks
@@ -307,6 +328,19 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const
   __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
 }
 
+template <int D, bool MASK>
+__device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const uint16_t* __restrict__ Vs,
+                                          const u32x4_t (&qf)[D / 16], f32x16_t (&oacc)[D / 32],
+                                          float& m_run, float& l_run, int key_base, int key_end,
+                                          bool causal, int row_tok, float c, int lane) {
+  f32x16_t s[2];
+  qk_tile<D>(Ks, qf, s, lane);
+  if (MASK) mask_scores(s, key_base, key_end, causal, row_tok, c, lane);
+  bf16x8_t pb[2][2];
+  softmax_tile<D>(s, oacc, m_run, l_run, c, pb);
+  pv_tile<D>(Vs, pb, oacc, lane);
+}
+
 template <int D, int NST>
 __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_kernel(AttnParams P) {
   using T = Tile<D>;
@@ -334,22 +368,30 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
   const uint32_t lds_base = lds_address(smem);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
-  // The items this workgroup deals from: its XCD's bin (workgroup i runs on
+  // The items this workgroup takes from: its XCD's bin (workgroup i runs on
   // XCD i % 8, as the i / 8-th of that XCD's workgroups), or the whole list.
+  // Without a queue the workgroups deal the bin boustrophedon-style.  With one,
+  // workgroup w starts with item w and then takes the bin's next untaken item
+  // (list order, longest first) whenever it finishes one; it asks for it while
+  // computing its current item's last tile, so the counter's latency hides
+  // behind that tile.
   const int wid = logical_wg();
-  int w = wid, G = gridDim.x;
+  int w = wid, G = gridDim.x, x = 0;
   int64_t first = 0, end = P.n_items;
   if (P.n_bins > 1) {
-    const int x = blockIdx.x % P.n_bins;
+    x = blockIdx.x % P.n_bins;
     w = blockIdx.x / P.n_bins;
     G = gridDim.x / P.n_bins;
     first = P.bin_off[x];
     end = P.bin_off[x + 1];
   }
+  __shared__ int32_t q_next;
+  int32_t* const queue = P.queue;
+  int64_t pos = first + (queue ? w : deal_position(0, w, G));
   for (int64_t pass = 0;; ++pass) {
-    const int64_t pos = first + deal_position(pass, w, G);
     if (pos >= end) break;
     const WorkItem it = P.items[pos];
+    int32_t q_mine = 0;  // with a queue: this workgroup's next item (thread 0)
     const bool causal = it.kind == kKindSelf;
     uint64_t t_start = 0, t_ready = 0, t_loop = 0;
     if (P.trace) t_start = now_ticks();
@@ -384,7 +426,7 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
     const bool wave_has_rows = wave * 32 < it.nrows;
     const int row_tok = it.row0 + r_w;                   // token index (self rows)
     const int wave_last_tok = it.row0 + wave * 32 + 31;  // largest token of this wave's rows
-    const float c = P.scale_log2;
+    const float c = kernel_scale(P.scale_log2);
 
     // The ring's first copies depend only on the item: issue them before the
     // candidate gather, so their latency overlaps the cand_perm -> Q chain.
@@ -430,6 +472,7 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
       }
       __syncthreads();  // every thread's copies of tile t are in LDS; stage (t-1) % NST is free
       if (t + NST - 1 < ntiles) issue(t + NST - 1);
+      if (queue && tid == 0 && t == ntiles - 1) q_mine = G + atomicAdd(&queue[x], 1);
       const int key_base = it.k0 + tile_of(t) * kBN;  // first key of this tile, user-relative
       const bool skip = !wave_has_rows || (causal && key_base > wave_last_tok);
       if (!skip) {
@@ -443,6 +486,7 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
       }
     }
     __syncthreads();  // all stages free before the next item's copies
+    if (queue && tid == 0 && ntiles == 0) q_mine = G + atomicAdd(&queue[x], 1);  // an item without keys
     if (P.trace) t_loop = now_ticks();
 
     // ---- epilogue
@@ -484,6 +528,22 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
       tr[3] = t_loop;
       tr[4] = now_ticks();
       tr[5] = static_cast<uint64_t>(ntiles);
+    }
+    if (queue) {
+      if (tid == 0) q_next = q_mine;
+      __syncthreads();
+      pos = first + q_next;
+    } else {
+      pos = first + deal_position(pass + 1, w, G);
+    }
+  }
+  if (queue && tid == 0) {
+    // Every workgroup of the bin is done taking items (its last answer, or its
+    // first item, was past the bin's end); the last one to get here leaves
+    // both counters at zero for the next launch.
+    if (atomicAdd(&queue[kMaxBins + x], 1) == G - 1) {
+      atomicExch(&queue[x], 0);
+      atomicExch(&queue[kMaxBins + x], 0);
     }
   }
 }
@@ -639,7 +699,7 @@ __global__ __launch_bounds__(512, 1) void ikbo_attn_bf16_w8_kernel(AttnParams P)
     const bool wave_has_rows = rb * 32 < it.nrows;
     const int row_tok = it.row0 + r_w;
     const int wave_last_tok = it.row0 + rb * 32 + 31;
-    const float c = P.scale_log2;
+    const float c = kernel_scale(P.scale_log2);
 
 #pragma unroll
     for (int s = 0; s < NST - 1; ++s)

@@ -36,7 +36,7 @@ def _oracle_target(w):
 @pytest.fixture(autouse=True)
 def _clean_env():
     saved = {k: os.environ.get(k) for k in ("IKBO_GRID_WGS", "IKBO_MIN_CHUNK", "IKBO_NO_SPLIT", "IKBO_SPLIT_SLOTS",
-                                            "IKBO_KERNEL")}
+                                            "IKBO_KERNEL", "IKBO_STATIC_DEAL")}
     yield
     for k, v in saved.items():
         if v is None:
@@ -610,6 +610,50 @@ def test_plan_rebuilt_for_alternating_requests():
         for rep in range(4):
             assert_close(to_f64(outs[i][rep]), refs[i], "bf16", f"request {i} round {rep}")
             assert torch.equal(outs[i][rep].view(torch.int16), outs[i][0].view(torch.int16))
+
+
+def test_work_queue_matches_static_deal():
+    """The 4-wave kernel's workgroups take items from per-bin counters as they
+    become free; each item's arithmetic does not depend on who runs it, so the
+    outputs equal the static deal's bit for bit.  Two multi-pass requests (the
+    fused one with self rows, the App. 11 shape) alternate on one plan for three
+    rounds with no synchronisation between launches: every launch finds the
+    counters the previous one left at zero."""
+    from broadcast_free_target_amd import (ikbo_attn_fwd_planned, ikbo_plan_build, ikbo_plan_create,
+                                           ikbo_plan_destroy, ikbo_plan_info)
+    import torch
+    wa, wb = _wl("c5_fused"), _wl("p_app11")
+    da, db = upload(wa), upload(wb)
+    say("case work queue vs static deal")
+    outs = {}
+    for mode in ("1", "0"):
+        os.environ["IKBO_STATIC_DEAL"] = mode
+        plan = ikbo_plan_create(wa.user_offsets, wa.cand_to_user, wa.n_users, wa.n_cand, wa.n_q, wa.H, wa.d, 0, 1)
+        rounds = 1 if mode == "1" else 3
+        res = []
+        try:
+            for _ in range(rounds):
+                oa_c = empty_out(wa.raw("q_cand").shape, "bf16")
+                oa_u = empty_out(wa.raw("q_user").shape, "bf16")
+                ob = empty_out(wb.raw("q_cand").shape, "bf16")
+                ikbo_plan_build(plan, wa.user_offsets, wa.cand_to_user, wa.n_users, wa.n_cand, wa.n_q, wa.H, wa.d,
+                                0, 1)
+                assert ikbo_plan_info(plan)["kernel"] == 2
+                ikbo_attn_fwd_planned(plan, da["q_cand"], da["q_user"], da["k_user"], da["v_user"], wa.scale, oa_c,
+                                      oa_u)
+                ikbo_plan_build(plan, wb.user_offsets, wb.cand_to_user, wb.n_users, wb.n_cand, wb.n_q, wb.H, wb.d,
+                                0, 0)
+                assert ikbo_plan_info(plan)["kernel"] == 2
+                ikbo_attn_fwd_planned(plan, db["q_cand"], None, db["k_user"], db["v_user"], wb.scale, ob)
+                res.append((oa_c, oa_u, ob))
+            torch.cuda.synchronize()
+        finally:
+            ikbo_plan_destroy(plan)
+        outs[mode] = res
+    ref = outs["1"][0]
+    for r, got in enumerate(outs["0"]):
+        for a, b, what in zip(got, ref, ("fused target", "fused self", "App. 11")):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"round {r}: {what}"
 
 
 def test_hostmap_call_equals_build_then_launch():
