@@ -49,6 +49,13 @@ __device__ __forceinline__ u32x2_t pack4_bf16(float a, float b, float c, float d
 __device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds_byte) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_byte) : "memory", "m0");
 }
+// The same copy from a wave-uniform base held in SGPRs plus a per-lane byte
+// offset (the saddr form): the per-tile address then costs no vector
+// arithmetic, only the scalar base moves.
+__device__ __forceinline__ void copy16_to_lds_s(const void* sbase, uint32_t voff_bytes, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff_bytes), "s"(sbase), "s"(lds_byte)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ uint32_t lds_address(const void* p) {

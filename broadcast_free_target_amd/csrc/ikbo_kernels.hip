@@ -175,18 +175,39 @@ __device__ __forceinline__ int64_t deal_position(int64_t pass, int w, int grid) 
 // softmax update that turns S into the bf16 P^T operands (softmax_tile), and
 // O^T += V^T P^T (pv_tile).  tile_step runs the three in a row.
 
+// Per-lane LDS element offsets of the tile reads, computed once per kernel:
+// koff[st] for the K fragment of K-step st of rows 0..31 (rows 32..63 add
+// 32 * D), voff[2 mb + h] for the transposed V reads of O^T block mb of the
+// tile's first K-step (h = 1: the read eight keys further; later K-steps add
+// whole rows).
+template <int D>
+struct TileOffsets {
+  int koff[D / 16];
+  int voff[D / 16];
+  __device__ __forceinline__ explicit TileOffsets(int lane) {
+    const int n = lane & 31, g = lane >> 5, kq = lane & 15, half = (lane >> 4) & 1;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) koff[st] = tile_off<D>(n, st * 2 + g);
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) {
+      const int col = mb * 32 + half * 16 + 4 * (kq & 3);
+      const int r0 = g * 4 + (kq >> 2);
+      voff[2 * mb] = tile_off<D>(r0, col >> 3) + (col & 4);
+      voff[2 * mb + 1] = tile_off<D>(r0 + 8, col >> 3) + (col & 4);
+    }
+  }
+};
+
 // S^T of the tile's two 32-key blocks for this lane's query row.
 template <int D>
 __device__ __forceinline__ void qk_tile(const uint16_t* __restrict__ Ks, const u32x4_t (&qf)[D / 16],
-                                        f32x16_t (&s)[2], int lane) {
-  const int n = lane & 31, g = lane >> 5;
+                                        f32x16_t (&s)[2], const TileOffsets<D>& to) {
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    const int row = b * 32 + n;
     u32x4_t a[D / 16];
 #pragma unroll
     for (int st = 0; st < D / 16; ++st)
-      a[st] = *reinterpret_cast<const u32x4_t*>(Ks + tile_off<D>(row, st * 2 + g));
+      a[st] = *reinterpret_cast<const u32x4_t*>(Ks + b * 32 * D + to.koff[st]);
     s[b] = f32x16_t{};
 #pragma unroll
     for (int st = 0; st < D / 16; ++st)
@@ -291,23 +312,18 @@ __device__ __forceinline__ void softmax_tile(f32x16_t (&s)[2], f32x16_t (&oacc)[
 // O^T += V^T P^T over the tile.
 template <int D>
 __device__ __forceinline__ void pv_tile(const uint16_t* __restrict__ Vs, const bf16x8_t (&pb)[2][2],
-                                        f32x16_t (&oacc)[D / 32], int lane) {
-  const int g = lane >> 5;
+                                        f32x16_t (&oacc)[D / 32], const TileOffsets<D>& to) {
   // V^T operand: lane k of each 16-lane group points at V[K0 + k/4][D0 + 4*(k%4)];
   // the transposed read returns V[K0 .. K0+3][D0 + k] to lane k.  MFMA j of the
   // tile is K-step (b, s2) = j / (D/32) of O^T block mb = j % (D/32): blocks
   // alternate, so consecutive MFMAs are independent, and each one's V^T reads
   // are issued two MFMAs ahead.
-  const int kq = lane & 15, half = (lane >> 4) & 1;
   constexpr int NMB = D / 32, NJ = 4 * NMB;
   auto vload = [&](int j) {
     const int bs = j / NMB, mb = j % NMB;
-    const int col = mb * 32 + half * 16 + 4 * (kq & 3);
-    const int r0 = (bs >> 1) * 32 + 16 * (bs & 1) + g * 4 + (kq >> 2);
-    const int offa = tile_off<D>(r0, col >> 3) + (col & 4);
-    const int offb = tile_off<D>(r0 + 8, col >> 3) + (col & 4);
-    const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(Vs + offa));
-    const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(Vs + offb));
+    const int rows = (bs >> 1) * 32 + 16 * (bs & 1);  // first key of K-step bs
+    const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(Vs + rows * D + to.voff[2 * mb]));
+    const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(Vs + rows * D + to.voff[2 * mb + 1]));
     return __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
   };
   i16x8_t vf[NJ];
@@ -332,13 +348,13 @@ template <int D, bool MASK>
 __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const uint16_t* __restrict__ Vs,
                                           const u32x4_t (&qf)[D / 16], f32x16_t (&oacc)[D / 32],
                                           float& m_run, float& l_run, int key_base, int key_end,
-                                          bool causal, int row_tok, float c, int lane) {
+                                          bool causal, int row_tok, float c, int lane, const TileOffsets<D>& to) {
   f32x16_t s[2];
-  qk_tile<D>(Ks, qf, s, lane);
+  qk_tile<D>(Ks, qf, s, to);
   if (MASK) mask_scores(s, key_base, key_end, causal, row_tok, c, lane);
   bf16x8_t pb[2][2];
   softmax_tile<D>(s, oacc, m_run, l_run, c, pb);
-  pv_tile<D>(Vs, pb, oacc, lane);
+  pv_tile<D>(Vs, pb, oacc, to);
 }
 
 template <int D, int NST>
@@ -358,15 +374,21 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
   // Loader mapping: 16-byte unit u = tid + 256*r of a tile lands at LDS unit u;
   // it holds row u / NCH and (swizzled) chunk u % NCH.
   int ld_row[T::loads], ld_chunk[T::loads];
+  uint32_t ld_off[T::loads];  // byte offset of the copy within a whole tile
 #pragma unroll
   for (int r = 0; r < T::loads; ++r) {
     const int u = tid + kThreads * r;
     ld_row[r] = u / T::NCH;
     ld_chunk[r] = (u % T::NCH) ^ (swz(ld_row[r]) & (T::NCH - 1));
+    ld_off[r] = static_cast<uint32_t>((ld_row[r] * row_stride + ld_chunk[r] * 8) * 2);
   }
+  // Whole tiles are copied from a scalar tile base plus these offsets when a
+  // tile's byte span fits 32 bits (always, short of ~8M elements per key row).
+  const bool whole_fast = static_cast<int64_t>(kBN) * row_stride * 2 < (int64_t{1} << 31);
 
   const uint32_t lds_base = lds_address(smem);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const TileOffsets<D> to(lane);
 
   // The items this workgroup takes from: its XCD's bin (workgroup i runs on
   // XCD i % 8, as the i / 8-th of that XCD's workgroups), or the whole list.
@@ -413,9 +435,21 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
     auto tile_of = [&](int t) { return P.kv_reverse ? ntiles - 1 - t : t; };
     auto issue = [&](int t) {
       const uint32_t st = lds_base + static_cast<uint32_t>((t % NST) * T::stage * 2);
+      const int tt = tile_of(t);
+      if (whole_fast && (tt + 1) * kBN <= nkv) {
+        const uint16_t* kt = kbase + static_cast<int64_t>(tt) * kBN * row_stride;
+        const uint16_t* vt = vbase + static_cast<int64_t>(tt) * kBN * row_stride;
+#pragma unroll
+        for (int r = 0; r < T::loads; ++r) {
+          const uint32_t dk = st + static_cast<uint32_t>((kThreads * r + 64 * wave_u) * 16);
+          copy16_to_lds_s(kt, ld_off[r], dk);
+          copy16_to_lds_s(vt, ld_off[r], dk + static_cast<uint32_t>(T::elems * 2));
+        }
+        return;
+      }
 #pragma unroll
       for (int r = 0; r < T::loads; ++r) {
-        const int key = min(tile_of(t) * kBN + ld_row[r], nkv - 1);
+        const int key = min(tt * kBN + ld_row[r], nkv - 1);
         const int64_t off = key * row_stride + ld_chunk[r] * 8;
         const uint32_t dk = st + static_cast<uint32_t>((kThreads * r + 64 * wave_u) * 16);
         copy16_to_lds(kbase + off, dk);
@@ -480,9 +514,9 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
         const uint16_t* Vs = Ks + T::elems;
         const bool need_mask = (key_base + kBN > it.k1) || (causal && key_base + kBN - 1 > it.row0 + wave * 32);
         if (need_mask)
-          tile_step<D, true>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, lane);
+          tile_step<D, true>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, lane, to);
         else
-          tile_step<D, false>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, lane);
+          tile_step<D, false>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, lane, to);
       }
     }
     __syncthreads();  // all stages free before the next item's copies
@@ -641,15 +675,19 @@ __global__ __launch_bounds__(512, 1) void ikbo_attn_bf16_w8_kernel(AttnParams P)
   // LDS unit u; it holds key row u / NCH (0..127: two tiles) and, swizzled,
   // chunk u % NCH.  The V half mirrors it.
   int ld_row[S::loads], ld_chunk[S::loads];
+  uint32_t ld_off[S::loads];  // byte offset of the copy within a whole stage
 #pragma unroll
   for (int r = 0; r < S::loads; ++r) {
     const int u = tid + NT * r;
     ld_row[r] = u / S::NCH;
     ld_chunk[r] = (u % S::NCH) ^ (swz(ld_row[r]) & (S::NCH - 1));
+    ld_off[r] = static_cast<uint32_t>((ld_row[r] * row_stride + ld_chunk[r] * 8) * 2);
   }
+  const bool whole_fast = static_cast<int64_t>(2 * kBN) * row_stride * 2 < (int64_t{1} << 31);
 
   const uint32_t lds_base = lds_address(smem);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const TileOffsets<D> to(lane);
 
   // The items this workgroup deals from: its XCD's bin (workgroup i runs on
   // XCD i % 8, as the i / 8-th of that XCD's workgroups), or the whole list.
@@ -686,6 +724,17 @@ __global__ __launch_bounds__(512, 1) void ikbo_attn_bf16_w8_kernel(AttnParams P)
     // Keys past the range load the last key again (in bounds, masked later).
     auto issue = [&](int st_idx) {
       const uint32_t st = lds_base + static_cast<uint32_t>((st_idx % NST) * S::stage * 2);
+      if (whole_fast && (st_idx + 1) * 2 * kBN <= nkv) {
+        const uint16_t* kt = kbase + static_cast<int64_t>(st_idx) * 2 * kBN * row_stride;
+        const uint16_t* vt = vbase + static_cast<int64_t>(st_idx) * 2 * kBN * row_stride;
+#pragma unroll
+        for (int r = 0; r < S::loads; ++r) {
+          const uint32_t dk = st + static_cast<uint32_t>((NT * r + 64 * wave_u) * 16);
+          copy16_to_lds_s(kt, ld_off[r], dk);
+          copy16_to_lds_s(vt, ld_off[r], dk + static_cast<uint32_t>(2 * S::tile * 2));
+        }
+        return;
+      }
 #pragma unroll
       for (int r = 0; r < S::loads; ++r) {
         const int key = min(st_idx * 2 * kBN + ld_row[r], nkv - 1);
@@ -747,9 +796,9 @@ __global__ __launch_bounds__(512, 1) void ikbo_attn_bf16_w8_kernel(AttnParams P)
         const uint16_t* Vs = smem + (s % NST) * S::stage + 2 * S::tile + kh * S::tile;
         const bool need_mask = (key_base + kBN > it.k1) || (causal && key_base + kBN - 1 > it.row0 + rb * 32);
         if (need_mask)
-          tile_step<D, true>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, lane);
+          tile_step<D, true>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, lane, to);
         else
-          tile_step<D, false>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, lane);
+          tile_step<D, false>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, lane, to);
       }
     }
     __syncthreads();  // every ring read is done: the ring becomes the exchange area
