@@ -100,7 +100,7 @@ int check_dims(int32_t n_users, int32_t n_cand, int32_t n_q, int32_t H, int32_t 
 // kernel, or, when that plan needs more items than there are CUs, for the
 // 4-wave kernel.  allow_split = false keeps every key range whole.
 int plan_request(int n_cu, const int32_t* offs, const int32_t* c2u, int32_t n_users, int32_t n_cand, int32_t n_q,
-                 int32_t H, int32_t d, int32_t dtype, int32_t with_self, bool allow_split, HostPlan* hp,
+                 int32_t H, int32_t d, int32_t dtype, int32_t with_self, bool allow_split, bool queued, HostPlan* hp,
                  int* variant_out) {
   int rc = check_dims(n_users, n_cand, n_q, H, d, dtype);
   if (rc != IKBO_OK) return rc;
@@ -111,14 +111,21 @@ int plan_request(int n_cu, const int32_t* offs, const int32_t* c2u, int32_t n_us
   const bool split_ok = allow_split && out_units < std::numeric_limits<int32_t>::max();
   const int forced = bf16_variant();
   int variant = forced == kVariantAuto ? kVariantW8 : forced;
-  PlanParams pp = params_for(n_cu, dtype, variant);
-  if (!split_ok) pp.allow_split = false;
+  auto params = [&](int v) {
+    PlanParams pp = params_for(n_cu, dtype, v);
+    if (!split_ok) pp.allow_split = false;
+    if (queued) {
+      pp.group_span = std::max(0, env_int("IKBO_GROUP_SPAN", 0));
+      pp.span_tail = std::max(0, env_int("IKBO_SPAN_TAIL", 0));
+    }
+    return pp;
+  };
+  PlanParams pp = params(variant);
   rc = ikbo::build_plan(offs, c2u, n_users, n_cand, n_q, H, with_self != 0, pp, hp, &err);
   if (rc != ikbo::kOk) return fail(rc, err);
   if (dtype == IKBO_DTYPE_BF16 && forced == kVariantAuto && hp->items.size() > static_cast<size_t>(n_cu)) {
     variant = kVariantW4;
-    pp = params_for(n_cu, dtype, variant);
-    if (!split_ok) pp.allow_split = false;
+    pp = params(variant);
     rc = ikbo::build_plan(offs, c2u, n_users, n_cand, n_q, H, with_self != 0, pp, hp, &err);
     if (rc != ikbo::kOk) return fail(rc, err);
   }
@@ -249,7 +256,9 @@ int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n
   p->built = false;
   HostPlan& hp = p->hp;
   int variant = kVariantW8;
-  int rc = plan_request(p->n_cu, offs, c2u, n_users, n_cand, n_q, H, d, dtype, with_self, true, &hp, &variant);
+  const bool static_deal = env_int("IKBO_STATIC_DEAL", 0) != 0;
+  int rc = plan_request(p->n_cu, offs, c2u, n_users, n_cand, n_q, H, d, dtype, with_self, true, !static_deal, &hp,
+                        &variant);
   if (rc != IKBO_OK) return rc;
 
   const int tile_rows = dtype == IKBO_DTYPE_BF16 ? ikbo::kBf16TileRows : ikbo::kF32TileRows;
@@ -291,7 +300,7 @@ int build_and_upload(Plan* p, const int32_t* offs, const int32_t* c2u, int32_t n
   p->with_self = with_self;
   p->stages = bf16_stages();
   p->variant = variant;
-  p->static_deal = env_int("IKBO_STATIC_DEAL", 0) != 0;
+  p->static_deal = static_deal;
   p->total_len = offs[n_users];
   p->built = true;
   return IKBO_OK;

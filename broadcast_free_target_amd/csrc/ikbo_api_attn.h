@@ -24,9 +24,11 @@ int check_dims(int32_t n_users, int32_t n_cand, int32_t n_q, int32_t H, int32_t 
 // Validates and plans one request from host mapping arrays into *hp: the
 // eight-wave kernel's plan, or the 4-wave kernel's when the former needs more
 // items than the device has CUs.  allow_split = false keeps key ranges whole.
+// queued: the launch deals items from the per-bin work queue, so each XCD bin
+// may list its items group by group (a static deal needs them longest first).
 int plan_request(int n_cu, const int32_t* offs, const int32_t* c2u, int32_t n_users, int32_t n_cand, int32_t n_q,
-                 int32_t H, int32_t d, int32_t dtype, int32_t with_self, bool allow_split, ikbo::HostPlan* hp,
-                 int* variant_out);
+                 int32_t H, int32_t d, int32_t dtype, int32_t with_self, bool allow_split, bool queued,
+                 ikbo::HostPlan* hp, int* variant_out);
 
 // Null, aliasing and alignment checks of one launch's tensors.
 int check_tensors(int32_t dtype, int32_t n_cand, int32_t n_q, int32_t H, int32_t d, int64_t total_len,

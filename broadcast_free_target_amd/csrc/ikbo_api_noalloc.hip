@@ -132,14 +132,16 @@ int attn_noalloc(const void* q_cand, const void* k, const void* v, const int32_t
   IKBO_HIP(hipStreamSynchronize(stream));
   HostPlan& hp = g_na.hp;
   int variant = kVariantW8;
-  if ((rc = plan_request(n_cu, ho, hc, n_users, n_cand, n_q, H, d, dtype, 0, split_fits, &hp, &variant)) != IKBO_OK)
+  if ((rc = plan_request(n_cu, ho, hc, n_users, n_cand, n_q, H, d, dtype, 0, split_fits, false, &hp, &variant)) !=
+      IKBO_OK)
     return rc;
   const int64_t total_len = ho[n_users];
   const size_t o_bytes = static_cast<size_t>(hp.n_slots) * tile_rows * d * sizeof(float);
   const size_t rec_at = (o_bytes + 255) & ~size_t(255);
   if (rec_at + static_cast<size_t>(hp.n_slots) * tile_rows * 4 * sizeof(float) > kNaPartialBytes) {
     // The split partials would not fit: plan again with whole key ranges.
-    if ((rc = plan_request(n_cu, ho, hc, n_users, n_cand, n_q, H, d, dtype, 0, false, &hp, &variant)) != IKBO_OK)
+    if ((rc = plan_request(n_cu, ho, hc, n_users, n_cand, n_q, H, d, dtype, 0, false, false, &hp, &variant)) !=
+        IKBO_OK)
       return rc;
   }
   if ((rc = check_tensors(dtype, n_cand, n_q, H, d, total_len, 0, q_cand, nullptr, k, v, out, nullptr)) != IKBO_OK)

@@ -309,52 +309,87 @@ __device__ __forceinline__ void softmax_tile(f32x16_t (&s)[2], f32x16_t (&oacc)[
       for (int j = 0; j < 8; ++j) pb[b][s2][j] = static_cast<__bf16>(s[b][s2 * 8 + j]);
 }
 
-// O^T += V^T P^T over the tile.
+// V^T operand of PV MFMA j of the tile (see pv_tile): lane k of each 16-lane
+// group points at V[K0 + k/4][D0 + 4*(k%4)]; the transposed read returns
+// V[K0 .. K0+3][D0 + k] to lane k.
 template <int D>
+__device__ __forceinline__ i16x8_t v_operand(const uint16_t* __restrict__ Vs, int j, const TileOffsets<D>& to) {
+  constexpr int NMB = D / 32;
+  const int bs = j / NMB, mb = j % NMB;
+  const int rows = (bs >> 1) * 32 + 16 * (bs & 1);  // first key of K-step bs
+  const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(Vs + rows * D + to.voff[2 * mb]));
+  const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(Vs + rows * D + to.voff[2 * mb + 1]));
+  return __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Operands of the first kPvPre<D> PV MFMAs (of 4 * D / 32), read before the
+// softmax so their LDS latency passes under its VALU work.
+template <int D>
+constexpr int kPvPre = D >= 64 ? 4 : 2;
+
+// O^T += V^T P^T over the tile.  MFMA j is K-step (b, s2) = j / (D/32) of O^T
+// block mb = j % (D/32): blocks alternate, so consecutive MFMAs are
+// independent.  The operands of MFMAs 0 .. kPvPre<D>-1 arrive in vpre; every
+// later one is read kPvPre<D> MFMAs ahead.
+template <int D, int PRE>
 __device__ __forceinline__ void pv_tile(const uint16_t* __restrict__ Vs, const bf16x8_t (&pb)[2][2],
-                                        f32x16_t (&oacc)[D / 32], const TileOffsets<D>& to) {
-  // V^T operand: lane k of each 16-lane group points at V[K0 + k/4][D0 + 4*(k%4)];
-  // the transposed read returns V[K0 .. K0+3][D0 + k] to lane k.  MFMA j of the
-  // tile is K-step (b, s2) = j / (D/32) of O^T block mb = j % (D/32): blocks
-  // alternate, so consecutive MFMAs are independent, and each one's V^T reads
-  // are issued two MFMAs ahead.
+                                        f32x16_t (&oacc)[D / 32], const TileOffsets<D>& to,
+                                        const i16x8_t (&vpre)[PRE > 0 ? PRE : 1]) {
   constexpr int NMB = D / 32, NJ = 4 * NMB;
-  auto vload = [&](int j) {
-    const int bs = j / NMB, mb = j % NMB;
-    const int rows = (bs >> 1) * 32 + 16 * (bs & 1);  // first key of K-step bs
-    const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(Vs + rows * D + to.voff[2 * mb]));
-    const i16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(Vs + rows * D + to.voff[2 * mb + 1]));
-    return __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
-  };
+  static_assert(NJ > PRE, "more PV MFMAs than prefetched operands");
   i16x8_t vf[NJ];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) vf[j] = vload(j);
+  for (int j = 0; j < NJ; ++j) vf[j] = j < PRE ? vpre[j] : v_operand<D>(Vs, j, to);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int bs = j / NMB, mb = j % NMB;
     oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[j]), pb[bs >> 1][bs & 1],
                                                       oacc[mb], 0, 0, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+  if constexpr (PRE > 0) {
 #pragma unroll
-  for (int k = 0; k < NJ - 2; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    for (int k = 0; k < NJ - PRE; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, PRE, 1);
+  } else {  // reads two MFMAs ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int k = 0; k < NJ - 2; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
 }
 
-template <int D, bool MASK>
+// PRIO: the wave raises its priority while it issues MFMAs (s_setprio), so
+// that when the other wave on its SIMD (of the other resident workgroup) also
+// wants to issue, the next MFMA goes first and the softmax fills the matrix
+// cores' busy cycles.  PRE: operands of the first PRE PV MFMAs are read before
+// the softmax (0: each PV operand two MFMAs ahead of its MFMA).
+template <int D, bool MASK, bool PRIO, int PRE>
 __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const uint16_t* __restrict__ Vs,
                                           const u32x4_t (&qf)[D / 16], f32x16_t (&oacc)[D / 32],
                                           float& m_run, float& l_run, int key_base, int key_end,
                                           bool causal, int row_tok, float c, int lane, const TileOffsets<D>& to) {
   f32x16_t s[2];
+  if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
   qk_tile<D>(Ks, qf, s, to);
+  i16x8_t vpre[PRE > 0 ? PRE : 1];
+  if constexpr (PRE > 0) {
+#pragma unroll
+    for (int j = 0; j < PRE; ++j) vpre[j] = v_operand<D>(Vs, j, to);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
   if (MASK) mask_scores(s, key_base, key_end, causal, row_tok, c, lane);
   bf16x8_t pb[2][2];
   softmax_tile<D>(s, oacc, m_run, l_run, c, pb);
-  pv_tile<D>(Vs, pb, oacc, to);
+  if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
+  pv_tile<D, PRE>(Vs, pb, oacc, to, vpre);
+  if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
 }
 
 template <int D, int NST>
@@ -513,10 +548,15 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
         const uint16_t* Ks = smem + (t % NST) * T::stage;
         const uint16_t* Vs = Ks + T::elems;
         const bool need_mask = (key_base + kBN > it.k1) || (causal && key_base + kBN - 1 > it.row0 + wave * 32);
+        // two resident workgroups per CU (NST 2): priority while issuing MFMAs
+        constexpr bool kPrio = NST <= 2;
+        constexpr int kPre = kPrio ? kPvPre<D> : 0;
         if (need_mask)
-          tile_step<D, true>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, lane, to);
+          tile_step<D, true, kPrio, kPre>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, lane,
+                                          to);
         else
-          tile_step<D, false>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, lane, to);
+          tile_step<D, false, kPrio, kPre>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c,
+                                           lane, to);
       }
     }
     __syncthreads();  // all stages free before the next item's copies
@@ -796,9 +836,11 @@ __global__ __launch_bounds__(512, 1) void ikbo_attn_bf16_w8_kernel(AttnParams P)
         const uint16_t* Vs = smem + (s % NST) * S::stage + 2 * S::tile + kh * S::tile;
         const bool need_mask = (key_base + kBN > it.k1) || (causal && key_base + kBN - 1 > it.row0 + rb * 32);
         if (need_mask)
-          tile_step<D, true>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, lane, to);
+          tile_step<D, true, false, 0>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, lane,
+                                       to);
         else
-          tile_step<D, false>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, lane, to);
+          tile_step<D, false, false, 0>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c,
+                                        lane, to);
       }
     }
     __syncthreads();  // every ring read is done: the ring becomes the exchange area

@@ -283,8 +283,11 @@ __global__ __launch_bounds__(kT, 2) void ikbo_attn_mx_kernel(MxParams P) {
       constexpr bool MASK = decltype(mask_tag)::value;
       const uint8_t* st = smem + (t % kNst) * kStBytes;
       const int kv_left = nkv - t * kMxKeys;  // keys of this tile inside the range (may exceed 64)
-      // ---- S^T = K . Q^T, two 32-key blocks
+      // ---- S^T = K . Q^T, two 32-key blocks (raised priority while the
+      // MFMAs issue: the other resident workgroup's wave on this SIMD
+      // fills the matrix cores' busy cycles with its softmax)
       f32x16_t s[2];
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const int key = 32 * b + n;
@@ -307,10 +310,12 @@ __global__ __launch_bounds__(kT, 2) void ikbo_attn_mx_kernel(MxParams P) {
         s[b] = acc;
       }
 
+      __builtin_amdgcn_s_setprio(0);
       // ---- online softmax and P quantization
       v8i pf;
       int psc;
       softmax_quant<NEG, MASK>(s, c, kv_left, g, m_run, l_run, oacc, pf, psc);
+      __builtin_amdgcn_s_setprio(1);
 
       // ---- O^T += V^T . P^T, four 32-column blocks
 #pragma unroll
@@ -332,6 +337,7 @@ __global__ __launch_bounds__(kT, 2) void ikbo_attn_mx_kernel(MxParams P) {
         const v8i vf = {va[0], va[1], va[2], va[3], va[4], va[5], va[6], va[7]};
         oacc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf, oacc[mb], 0, 0, 0, vsc, 0, psc);
       }
+      __builtin_amdgcn_s_setprio(0);
     };
     // Only the last tile can hold keys past the range: the loop runs unmasked
     // and the last tile separately.

@@ -92,9 +92,12 @@ namespace {
 
 // Reorders a longest-first item list into XCD bins (see HostPlan::bin_off):
 // (user, head) groups by decreasing total cost, each into the least loaded bin;
-// within a bin the items keep their longest-first order.  Only for plans whose
-// grid is a multiple of the bin count and which give workgroups more than one
-// item (in a single-pass plan every workgroup runs one item whatever its bin).
+// within a bin the items keep their longest-first order, or with group_span
+// come in spans of that many groups of the bin, in that same group order
+// (items of a span longest first), so the workgroups of one XCD share the K/V
+// of a few groups at a time.  Only for plans whose grid is a multiple of the bin count and which
+// give workgroups more than one item (in a single-pass plan every workgroup
+// runs one item whatever its bin).
 void assign_bins(const int32_t* user_offsets, int32_t n_users, int32_t H, const PlanParams& p, HostPlan* out) {
   out->n_bins = 0;
   const int32_t nb = p.xcd_bins;
@@ -137,13 +140,38 @@ void assign_bins(const int32_t* user_offsets, int32_t n_users, int32_t H, const 
     bin[g] = b;
     load[b] += cost[g];
   }
+  std::vector<WorkItem>& tmp = out->unsorted;
+  tmp.resize(n);
+  if (p.group_span > 0) {
+    // stable counting sort of the items by the span their group falls in
+    // within its bin, short items (span_tail) and groups without cost
+    // (possible only with overhead 0) last; the stable partition by bin below
+    // keeps that order inside each bin
+    const int64_t nr = static_cast<int64_t>(ord.size()) + 1;
+    std::vector<int64_t>& start = out->lens;  // reused as per-span start positions
+    start.assign(nr + 1, 0);
+    std::vector<int64_t>& rank = out->group_cost;  // cost is no longer needed
+    rank.assign(n_groups, nr - 1);
+    int64_t seen[kMaxBins] = {};  // groups of each bin placed so far
+    for (int64_t r = 0; r + 1 < nr; ++r) {
+      const int64_t g = static_cast<int64_t>(ord[r] & 0xffffffffull);
+      rank[g] = seen[bin[g]]++ / p.group_span;
+    }
+    auto bucket = [&](int64_t i) {
+      const WorkItem& it = out->items[i];
+      return it.k1 - it.k0 <= p.span_tail ? nr - 1 : rank[gid[i]];
+    };
+    for (int64_t i = 0; i < n; ++i) ++start[bucket(i) + 1];
+    for (int64_t r = 0; r < nr; ++r) start[r + 1] += start[r];
+    for (int64_t i = 0; i < n; ++i) tmp[start[bucket(i)]++] = out->items[i];
+    out->items.swap(tmp);
+    for (int64_t i = 0; i < n; ++i) gid[i] = static_cast<int32_t>(group_of(out->items[i]));
+  }
   // stable partition of the items by bin
   int32_t cnt[kMaxBins + 1] = {};
   for (int64_t i = 0; i < n; ++i) ++cnt[bin[gid[i]] + 1];
   for (int b = 0; b < nb; ++b) cnt[b + 1] += cnt[b];
   for (int b = 0; b <= nb; ++b) out->bin_off[b] = cnt[b];
-  std::vector<WorkItem>& tmp = out->unsorted;
-  tmp.resize(n);
   for (int64_t i = 0; i < n; ++i) tmp[cnt[bin[gid[i]]]++] = out->items[i];
   out->items.swap(tmp);
   out->n_bins = nb;

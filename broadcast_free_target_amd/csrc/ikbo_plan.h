@@ -62,6 +62,13 @@ struct PlanParams {
                               // fit grid_slots (one item per workgroup), else by cost
   int32_t xcd_bins = 0;       // > 1: multi-pass plans keep all items of one (user, head)
                               // in one of this many bins, one bin per XCD (see HostPlan)
+  int32_t group_span = 0;     // > 0, with bins: each bin lists its (user, head) groups in
+                              // spans of this many, largest groups first, the items of a
+                              // span longest first (for workgroups that take items from a
+                              // queue; a static deal needs the whole bin longest first)
+  int32_t span_tail = 0;      // with group_span: items of at most this many keys leave
+                              // their span for the end of the bin, longest first, so
+                              // the bin still ends on its shortest items
 };
 
 // Most XCD bins a plan may use (the kernels take the bin offsets by value).
@@ -79,7 +86,7 @@ struct HostPlan {
   int64_t n_target_tiles = 0;
   int64_t n_self_tiles = 0;
   // XCD bins (0 when the plan has none): items [bin_off[b], bin_off[b+1]) are
-  // bin b's, each bin longest first.  Workgroup i of the launch serves bin
+  // bin b's, each bin longest first (or span by span, see PlanParams::group_span).  Workgroup i of the launch serves bin
   // i % n_bins (the XCD the dispatcher places it on) as its (i / n_bins)-th
   // workgroup, dealing the bin's items boustrophedon-style.  Every item of one
   // (user, head) -- its row tiles, self and target, and key chunks, all reading

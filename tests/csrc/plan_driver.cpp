@@ -1,7 +1,7 @@
 // Test driver for the host planner (built with g++ and sanitizers by the
 // CPU test suite).  Reads one problem from stdin as whitespace-separated
 // integers:
-//   n_users n_cand n_q H with_self bm bn grid_slots min_chunk allow_split single_pass xcd_bins
+//   n_users n_cand n_q H with_self bm bn grid_slots min_chunk allow_split single_pass xcd_bins group_span span_tail
 //   user_offsets[n_users+1] cand_to_user[n_cand]
 // and prints "rc <status>", then "plan <n_items> <grid> <n_groups> <n_slots>",
 // "bins <n_bins> <bin_off[0..kMaxBins]>", "perm <cand_perm...>", and one "item"
@@ -14,9 +14,10 @@
 #include "ikbo_plan.h"
 
 int main() {
-  int32_t n_users, n_cand, n_q, H, with_self, bm, bn, grid_slots, min_chunk, allow_split, single_pass, xcd_bins;
+  int32_t n_users, n_cand, n_q, H, with_self, bm, bn, grid_slots, min_chunk, allow_split, single_pass, xcd_bins,
+      group_span, span_tail;
   if (!(std::cin >> n_users >> n_cand >> n_q >> H >> with_self >> bm >> bn >> grid_slots >> min_chunk >>
-        allow_split >> single_pass >> xcd_bins))
+        allow_split >> single_pass >> xcd_bins >> group_span >> span_tail))
     return 2;
   std::vector<int32_t> offs(static_cast<size_t>(n_users) + 1), c2u(n_cand);
   for (auto& x : offs) std::cin >> x;
@@ -29,6 +30,8 @@ int main() {
   p.allow_split = allow_split != 0;
   p.single_pass = single_pass != 0;
   p.xcd_bins = xcd_bins;
+  p.group_span = group_span;
+  p.span_tail = span_tail;
   ikbo::HostPlan hp;
   std::string err;
   const int rc = ikbo::build_plan(offs.data(), c2u.data(), n_users, n_cand, n_q, H, with_self != 0, p, &hp, &err);

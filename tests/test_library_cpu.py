@@ -106,8 +106,10 @@ def driver(tmp_path_factory):
 
 
 def _run_driver(driver, offs, c2u, n_q=1, H=2, with_self=0, bm=128, bn=64, grid=512, min_chunk=256, split=1,
-                single=0, bins=0):
-    nums = [len(offs) - 1, len(c2u), n_q, H, with_self, bm, bn, grid, min_chunk, split, single, bins, *offs, *c2u]
+                single=0, bins=0, group_span=0, span_tail=0):
+    nums = [len(offs) - 1, len(c2u), n_q, H, with_self, bm, bn, grid, min_chunk, split, single, bins, group_span,
+            span_tail,
+            *offs, *c2u]
     r = subprocess.run([driver], input=" ".join(map(str, nums)), capture_output=True, text=True, check=True,
                        env={**os.environ, "ASAN_OPTIONS": "detect_leaks=1"})
     lines = r.stdout.splitlines()
@@ -122,7 +124,7 @@ def _run_driver(driver, offs, c2u, n_q=1, H=2, with_self=0, bm=128, bn=64, grid=
                    perm=perm, items=items, n_bins=bins[0], bin_off=bins[1:bins[0] + 2] if bins[0] else [0, len(items)])
 
 
-def _check_plan(plan, offs, c2u, n_q, H, with_self, bm, bn, grid_slots):
+def _check_plan(plan, offs, c2u, n_q, H, with_self, bm, bn, grid_slots, group_span=0, span_tail=0):
     offs = np.asarray(offs, dtype=np.int64)
     c2u = np.asarray(c2u, dtype=np.int64)
     U = len(offs) - 1
@@ -182,18 +184,39 @@ def _check_plan(plan, offs, c2u, n_q, H, with_self, bm, bn, grid_slots):
         assert s0 == 8 * g and 2 <= nc <= 8
     # longest first within each XCD bin (the whole list when there are none);
     # equal costs keep construction order (user, then target before self, head,
-    # row tile, chunk), so one user's tiles stay adjacent
+    # row tile, chunk), so one user's tiles stay adjacent.  With group spans:
+    # the bin's (user, head) groups by decreasing total cost (ties by
+    # user * H + head) in spans of group_span groups, each span's items
+    # contiguous and in that same order, then the items of at most span_tail
+    # keys, longest first.
     off = plan["bin_off"]
     nb = max(plan["n_bins"], 1)
     assert off[0] == 0 and off[-1] == len(items) and len(off) == nb + 1 and np.all(np.diff(off) >= 0)
     cost = items[:, 5] - items[:, 4]
     key = [(int(it[0]), int(it[7]), int(it[1]) if it[7] == 0 else 0, int(it[6]), int(it[2]), int(it[4]))
            for it in items]
+    grp = [user_of(int(it[7]), int(it[0]), int(it[1])) * H + int(it[6]) for it in items]
+    gtot = {}
+    for g, c in zip(grp, cost):
+        gtot[g] = gtot.get(g, 0) + int(c) + 128
     for b in range(nb):
-        assert np.all(np.diff(cost[off[b]:off[b + 1]]) <= 0)
-        for i in range(off[b], off[b + 1] - 1):
-            if cost[i] == cost[i + 1]:
-                assert key[i] < key[i + 1], (i, key[i], key[i + 1])
+        if group_span and plan["n_bins"]:
+            order = sorted(set(grp[off[b]:off[b + 1]]), key=lambda g: (-gtot[g], g))
+            span = {g: k // group_span for k, g in enumerate(order)}
+            sp = [len(order) if cost[i] <= span_tail else span[grp[i]] for i in range(off[b], off[b + 1])]
+            assert sp == sorted(sp)  # spans in order, each span's items contiguous
+            runs, a = [], off[b]
+            for i in range(off[b] + 1, off[b + 1] + 1):
+                if i == off[b + 1] or sp[i - off[b]] != sp[i - 1 - off[b]]:
+                    runs.append((a, i))
+                    a = i
+        else:
+            runs = [(off[b], off[b + 1])]
+        for a, e in runs:
+            assert np.all(np.diff(cost[a:e]) <= 0)
+            for i in range(a, e - 1):
+                if cost[i] == cost[i + 1]:
+                    assert key[i] < key[i + 1], (i, key[i], key[i + 1])
     # the boustrophedon deal over each bin's workgroups (workgroup i serves bin
     # i % n_bins) gives every item to exactly one workgroup
     G = plan["grid"]
@@ -263,10 +286,12 @@ def test_planner_xcd_bins(driver, name):
         w = make_workload(name)
         offs, c2u, n_q, H, with_self = w.user_offsets, w.cand_to_user, w.n_q, w.H, 0
     for grid in (512, 64, 8):
-        rc, plan = _run_driver(driver, offs, c2u, n_q=n_q, H=H, with_self=with_self, grid=grid, bins=8)
-        assert rc == 0
-        assert plan["n_bins"] == (8 if plan["n_items"] > plan["grid"] else 0)
-        _check_plan(plan, offs, c2u, n_q, H, with_self, 128, 64, grid)
+        for span, tail in ((0, 0), (1, 0), (3, 0), (2, 256)):
+            rc, plan = _run_driver(driver, offs, c2u, n_q=n_q, H=H, with_self=with_self, grid=grid, bins=8,
+                                   group_span=span, span_tail=tail)
+            assert rc == 0
+            assert plan["n_bins"] == (8 if plan["n_items"] > plan["grid"] else 0)
+            _check_plan(plan, offs, c2u, n_q, H, with_self, 128, 64, grid, group_span=span, span_tail=tail)
     # a grid that is not a multiple of the bin count keeps one list
     rc, plan = _run_driver(driver, offs, c2u, n_q=n_q, H=H, with_self=with_self, grid=37, bins=8)
     assert rc == 0 and plan["n_bins"] == 0
