@@ -355,7 +355,10 @@ int launch_planned(Plan* p, const void* q_cand, const void* q_user, const void* 
   ap.ws_rec = static_cast<float*>(p->d_ws_rec.ptr);
   ap.n_bins = p->hp.n_bins;
   for (int b = 0; b <= ikbo::kMaxBins; ++b) ap.bin_off[b] = p->hp.bin_off[b];
-  ap.queue = p->static_deal ? nullptr : static_cast<int32_t*>(p->d_queue.ptr);
+  // the queue only where workgroups take several items (a one-pass plan gives
+  // each one item; its workgroups would only meet on the counters at the end)
+  const bool multi_pass = p->hp.items.size() > static_cast<size_t>(p->hp.grid);
+  ap.queue = p->static_deal || !multi_pass ? nullptr : static_cast<int32_t*>(p->d_queue.ptr);
   ap.trace = nullptr;
   if (p->tracing && p->dtype == IKBO_DTYPE_BF16) {
     if ((rc = p->d_trace.ensure(p->hp.items.size() * 6 * sizeof(uint64_t), false)) != IKBO_OK) return rc;
