@@ -78,15 +78,23 @@ __device__ __forceinline__ float dot8(u32x4_t a, u32x4_t b) {
   return s;
 }
 
-// B operand from accumulator values base .. base+7 (rounded to bf16).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// One 4-byte-per-lane HBM -> LDS copy (global_load_lds_dword, saddr form):
+// lane l's 4 bytes from sbase + voff_bytes land at LDS byte lds_byte + 4*l.
+__device__ __forceinline__ void copy4_to_lds_s(const void* sbase, uint32_t voff_bytes, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff_bytes), "s"(sbase), "s"(lds_byte)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// B operand from accumulator values base .. base+7 (rounded to bf16, nearest
+// even; one v_cvt_pk_bf16_f32 per pair).
 __device__ __forceinline__ bf16x8_t pack8(const f32x16_t& x, int base) {
-  u32x4_t r;
+  bf16x8_t r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = x[base + 2 * i], hi = x[base + 2 * i + 1];
-    r[i] = bf16_bits(lo) | (bf16_bits(hi) << 16);
-  }
-  return as_bf16x8(r);
+  for (int i = 0; i < 8; ++i) r[i] = static_cast<__bf16>(x[base + i]);
+  return r;
 }
 
 // 2^x with the hardware instruction (no denormal range handling: softmax
@@ -255,6 +263,17 @@ __global__ __launch_bounds__(kNT, 2) void ikbo_bwd_dq_kernel(BwdParams P) {
       wait_vmcnt<0>();
     }
     __syncthreads();
+    if ((t + 1) * KT > L) {
+      // The item's last tile: its keys past the range hold copies of the last
+      // key.  Their K rows are zeroed here, so whatever dS they get adds
+      // nothing to dQ = dS K (dS is finite: P and dP come from finite rows),
+      // and the products below take no per-value mask.
+      uint16_t* Kw = smem + (t & 1) * 2 * TE;
+      const int dead = KT - (L - t * KT);  // rows lim .. KT-1, 16 chunks of 16 bytes each
+      for (int u = tid; u < dead * kCH; u += kNT)
+        *reinterpret_cast<u32x4_t*>(Kw + (KT - dead) * D + u * 8) = u32x4_t{0u, 0u, 0u, 0u};
+      __syncthreads();
+    }
     if (wave_live) {
       const uint16_t* Kt = smem + (t & 1) * 2 * TE;
       const uint16_t* Vt = Kt + TE;
@@ -265,8 +284,7 @@ __global__ __launch_bounds__(kNT, 2) void ikbo_bwd_dq_kernel(BwdParams P) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int key = t * KT + kb * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
-          const float p = key < L ? exp2_hw(s[kb][v] * c2 - lse) : 0.0f;
+          const float p = exp2_hw(s[kb][v] * c2 - lse);
           s[kb][v] = p * (dp[kb][v] - dsum);  // dS^T
         }
 #pragma unroll
@@ -401,6 +419,51 @@ __global__ __launch_bounds__(256) void ikbo_bwd_merge_kernel(BwdParams P) {
 // ---------------------------------------------------------------------------
 // dK / dV kernel
 // ---------------------------------------------------------------------------
+// Lane constants of the tile read offsets (elements), from which each read's
+// offset takes one XOR and one shift-add.  Row reads (16 bytes of row
+// kb*32 + n, chunk 2 ks + g): the swizzle only sees the row's low four bits,
+// and (2 ks + g) ^ swz(n) = 2 ks ^ t with t = g ^ swz(n).  Transposed reads
+// (tr_rows at K0 = R16 + 4 g, a multiple of 16 plus the lane's 4 g, and
+// D0 = 32 db + 16 half): the lane's rows are R16 + r and R16 + r + 8 with
+// r = 4 g + kq / 4 < 8, its chunk is 4 db + c with c = 2 half + (kq % 4) / 2 < 4,
+// so chunk ^ swz(row) = 4 db ^ (c ^ swz(row)).  Sixteen per-lane offsets
+// otherwise stay live across the tile loop and push the kernel past the
+// register file (the spill reloads then wait on every ring copy in flight).
+struct LaneOffs {
+  int nb;        // n * 128
+  int t;         // g ^ swz(n)
+  int rb;        // r * 128 + 4 (kq % 2)
+  int ta, tb;    // c ^ swz(r), c ^ swz(r + 8)
+  __device__ __forceinline__ LaneOffs(int n, int g, int kq, int half) {
+    const int r = 4 * g + (kq >> 2), c = 2 * half + ((kq & 3) >> 1);
+    nb = n * kCH * 8;
+    t = g ^ swz(n);
+    rb = r * kCH * 8 + 4 * (kq & 1);
+    ta = c ^ swz(r);
+    tb = c ^ swz(r + 8);
+  }
+  // Fresh copies the compiler cannot hoist out of a loop: the offsets built
+  // from them are recomputed where they are used instead of held.
+  __device__ __forceinline__ LaneOffs opaque() const {
+    LaneOffs o = *this;
+    asm volatile("" : "+v"(o.nb), "+v"(o.t), "+v"(o.rb), "+v"(o.ta), "+v"(o.tb));
+    return o;
+  }
+  // t_off(kb * 32 + n, 2 ks + g)
+  __device__ __forceinline__ int row(int kb, int ks) const { return kb * 32 * kCH * 8 + nb + (((2 * ks) ^ t) << 3); }
+  // tr_rows(T, R16 + 4 g, 32 db + 16 half, kq) as two offsets
+  __device__ __forceinline__ int tr_lo(int r16, int db) const { return r16 * kCH * 8 + rb + (((4 * db) ^ ta) << 3); }
+  __device__ __forceinline__ int tr_hi(int r16, int db) const {
+    return (r16 + 8) * kCH * 8 + rb + (((4 * db) ^ tb) << 3);
+  }
+};
+
+__device__ __forceinline__ bf16x8_t tr_rows_at(const uint16_t* T, int lo_off, int hi_off) {
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(T + lo_off));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(T + hi_off));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // Eight waves in two roles over the same 128 keys and the same staged rows:
 // waves 0-3 form P and accumulate dV, waves 4-7 form P, dP and dS and
 // accumulate dK (S is formed by both).  Waves w and w+4 share a SIMD, so each
@@ -412,10 +475,10 @@ __global__ __launch_bounds__(kNT8, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
   constexpr int TE = RT * D;             // elements per Q or dO tile
   constexpr int LPT = RT * kCH / kNT8;   // copies per thread per tile and tensor
   constexpr int NST = 3;                 // ring stages: two tiles in flight while one is used
-  constexpr int META = 4 * RT * 4;       // bytes per stage: lse[RT], dd[RT], then 512 spare bytes
+  constexpr int META = 4 * RT * 4;       // bytes per stage: lse[RT], dd[RT], then 512 spare bytes (alignment)
   constexpr int STAGE = 2 * TE * 2 + META;
-  constexpr int L0 = 2 * LPT;            // copies per stage of waves 1-7; wave 0 adds one
-  static_assert(LPT * kNT8 == RT * kCH && RT == 64 && META == 64 * 16, "tile shape; the meta copy lands 64 x 16 bytes");
+  constexpr int L0 = 2 * LPT;            // copies per stage of waves 1-7; wave 0 adds two
+  static_assert(LPT * kNT8 == RT * kCH && RT == 64 && META >= 2 * RT * 4, "tile shape; lse and D of the tile's rows");
   __shared__ __attribute__((aligned(16))) uint8_t smem[NST * STAGE];
 
   const WorkItem it = P.items[blockIdx.x];
@@ -447,30 +510,37 @@ __global__ __launch_bounds__(kNT8, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
   // Stage t: rows t*RT .. t*RT + RT-1 of the user's sorted Q and dO (contiguous;
   // rows past the user's count belong to the next user or to the zeroed
   // padding), then one copy by wave 0 of those rows' log-sum-exp and D.
+  // Copies from a scalar base (the stage's first row) plus per-lane byte
+  // offsets, fixed per thread: no per-lane 64-bit address is held across the
+  // loop.
+  uint32_t ld_off[LPT];
+#pragma unroll
+  for (int c = 0; c < LPT; ++c) {
+    const int u = tid + kNT8 * c;
+    const int row = u / kCH, pos = u % kCH;
+    ld_off[c] = static_cast<uint32_t>((row * D + (pos ^ swz(row)) * 8) * 2);
+  }
   auto issue = [&](int t) {
     const uint32_t st = lds_base + static_cast<uint32_t>((t % NST) * STAGE);
-    const int64_t e0 = (hrow0 + static_cast<int64_t>(t) * RT) * D;
+    const int64_t r0 = hrow0 + static_cast<int64_t>(t) * RT;
+    const uint16_t* qb = P.qs + r0 * D;
+    const uint16_t* db = P.dos + r0 * D;
 #pragma unroll
     for (int c = 0; c < LPT; ++c) {
-      const int u = tid + kNT8 * c;
-      const int row = u / kCH, pos = u % kCH;
-      const int64_t go = e0 + row * D + (pos ^ swz(row)) * 8;
       const uint32_t dst = st + static_cast<uint32_t>((kNT8 * c + 64 * wave_u) * 16);
-      copy16_to_lds(P.qs + go, dst);
-      copy16_to_lds(P.dos + go, dst + TE * 2);
+      copy16_to_lds_s(qb, ld_off[c], dst);
+      copy16_to_lds_s(db, ld_off[c], dst + TE * 2);
     }
     if (wave_u == 0) {
-      const int part = lane >> 4, j = lane & 15;
-      const int64_t at = hrow0 + static_cast<int64_t>(t) * RT + 4 * j;
-      // one 16-byte copy per lane lands at 16 * lane: lanes 0-15 lse, 16-31 D,
-      // 32-63 the spare bytes (they repeat the lse source)
-      copy16_to_lds(part == 1 ? P.dd + at : P.lse + at, st + 2 * TE * 2);
+      // the tile rows' log-sum-exp and D, 4 bytes per lane each
+      copy4_to_lds_s(P.lse + r0, static_cast<uint32_t>(4 * lane), st + 2 * TE * 2);
+      copy4_to_lds_s(P.dd + r0, static_cast<uint32_t>(4 * lane), st + 2 * TE * 2 + RT * 4);
     }
   };
   // Waits until stage t has landed: `ahead` later stages may stay in flight.
   auto wait_stage = [&](int ahead) {
     if (wave_u == 0) {
-      if (ahead >= 1) wait_vmcnt<L0 + 1>();
+      if (ahead >= 1) wait_vmcnt<L0 + 2>();
       else wait_vmcnt<0>();
     } else {
       if (ahead >= 1) wait_vmcnt<L0>();
@@ -479,6 +549,7 @@ __global__ __launch_bounds__(kNT8, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
   };
   static_assert(NST == 3, "wait_stage covers one stage in flight behind the awaited one");
 
+  const LaneOffs lane_offs(n, g, kq, half);
   f32x16_t acc[kDB];  // dV^T (waves 0-3) or dK^T (waves 4-7)
 #pragma unroll
   for (int db = 0; db < kDB; ++db) acc[db] = f32x16_t{};
@@ -488,13 +559,22 @@ __global__ __launch_bounds__(kNT8, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
     wait_stage(min(ntiles - 1 - t, NST - 2));
     __syncthreads();  // tile t is in LDS; every wave is done with tile t-1's slot
     if (t + NST - 1 < ntiles) issue(t + NST - 1);
-    const uint8_t* slot = smem + (t % NST) * STAGE;
+    uint8_t* slot = smem + (t % NST) * STAGE;
+    if ((t + 1) * RT > nrows) {
+      // The user's last tile: its rows past the count belong to the next user
+      // or to the padding.  Their staged log-sum-exp becomes +inf, so their
+      // weight exp2(s c - lse) is exactly 0 (s c is finite) and so is
+      // dS = P (dP - D): the products below take no per-value mask.
+      if (tid < RT && tid >= nrows - t * RT) reinterpret_cast<float*>(slot + 2 * TE * 2)[tid] = __builtin_huge_valf();
+      __syncthreads();
+    }
+    const LaneOffs lo = lane_offs.opaque();
     if (wave_live) {
       const uint16_t* Qt = reinterpret_cast<const uint16_t*>(slot);
       const uint16_t* Dt = Qt + TE;
       const float* lse_t = reinterpret_cast<const float*>(slot + 2 * TE * 2);
       const float* dd_t = lse_t + RT;
-      const bool full_tile = (t + 1) * RT <= nrows;
+
       if (dk_role) {
         // one 32-row block at a time keeps S and dP of one block live
 #pragma unroll
@@ -502,10 +582,10 @@ __global__ __launch_bounds__(kNT8, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
           f32x16_t sb = f32x16_t{}, dpb = f32x16_t{};
 #pragma unroll
           for (int ks = 0; ks < kKS; ++ks) {
-            sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(Qt + t_off(rb * 32 + n, ks * 2 + g))),
-                                                         as_bf16x8(kf[ks]), sb, 0, 0, 0);
-            dpb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(Dt + t_off(rb * 32 + n, ks * 2 + g))),
-                                                          as_bf16x8(vf[ks]), dpb, 0, 0, 0);
+            sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(Qt + lo.row(rb, ks))), as_bf16x8(kf[ks]), sb,
+                                                         0, 0, 0);
+            dpb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(Dt + lo.row(rb, ks))), as_bf16x8(vf[ks]),
+                                                          dpb, 0, 0, 0);
           }
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
@@ -514,26 +594,31 @@ __global__ __launch_bounds__(kNT8, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
             const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(dd_t + rbase);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              // rows past the user's count read other rows or padding: dS is forced to 0
-              const bool ok = full_tile || t * RT + rbase + i < nrows;
               const float p = exp2_hw(sb[q4 * 4 + i] * c2 - l4[i]);
-              sb[q4 * 4 + i] = ok ? p * (dpb[q4 * 4 + i] - d4[i]) : 0.0f;  // dS
+              sb[q4 * 4 + i] = p * (dpb[q4 * 4 + i] - d4[i]);  // dS
             }
           }
 #pragma unroll
           for (int j0 = 0; j0 < 2; ++j0) {
             const bf16x8_t bs = pack8(sb, j0 * 8);
-            const int K0 = rb * 32 + j0 * 16 + g * 4;
+            const int r16 = rb * 32 + j0 * 16;
 #pragma unroll
             for (int db = 0; db < kDB; ++db)
-              acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_rows(Qt, K0, db * 32 + half * 16, kq), bs, acc[db],
-                                                                0, 0, 0);
+              acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_rows_at(Qt, lo.tr_lo(r16, db), lo.tr_hi(r16, db)),
+                                                                bs, acc[db], 0, 0, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
-        f32x16_t s[2];
-        tile_products(Qt, kf, s, n, g);  // S: rows x this lane's key
+        f32x16_t s[2];  // S: rows x this lane's key
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb] = f32x16_t{};
+#pragma unroll
+          for (int ks = 0; ks < kKS; ++ks)
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(Qt + lo.row(kb, ks))), as_bf16x8(kf[ks]),
+                                                            s[kb], 0, 0, 0);
+        }
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -541,22 +626,18 @@ __global__ __launch_bounds__(kNT8, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
             const int rbase = rb * 32 + q4 * 8 + g * 4;
             const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(lse_t + rbase);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              // rows past the user's count read other rows or padding: P is forced to 0
-              const bool ok = full_tile || t * RT + rbase + i < nrows;
-              s[rb][q4 * 4 + i] = ok ? exp2_hw(s[rb][q4 * 4 + i] * c2 - l4[i]) : 0.0f;  // P
-            }
+            for (int i = 0; i < 4; ++i) s[rb][q4 * 4 + i] = exp2_hw(s[rb][q4 * 4 + i] * c2 - l4[i]);  // P
           }
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
           for (int j0 = 0; j0 < 2; ++j0) {
             const bf16x8_t bp = pack8(s[rb], j0 * 8);
-            const int K0 = rb * 32 + j0 * 16 + g * 4;
+            const int r16 = rb * 32 + j0 * 16;
 #pragma unroll
             for (int db = 0; db < kDB; ++db)
-              acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_rows(Dt, K0, db * 32 + half * 16, kq), bp, acc[db],
-                                                                0, 0, 0);
+              acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_rows_at(Dt, lo.tr_lo(r16, db), lo.tr_hi(r16, db)),
+                                                                bp, acc[db], 0, 0, 0);
           }
       }
     }
