@@ -185,7 +185,7 @@ int launch_kernels(ikbo::AttnParams& ap, int32_t dtype, int variant, int d, int 
   }
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
   if (hp.n_groups > 0) {
-    e = ikbo::launch_merge(ap, hp.n_groups, d, stream, te ? te + 2 : nullptr);
+    e = ikbo::launch_merge(ap, hp.n_groups, d, true, stream, te ? te + 2 : nullptr);
     if (e != hipSuccess) return fail_hip(e, "merge launch");
   }
   return IKBO_OK;

@@ -196,7 +196,7 @@ int ikbo_attn_fwd_mxfp8(void* mx, const int32_t* user_offsets, const int32_t* ca
       ap.n_q = n_q;
       ap.ws_o = p.ws_o;
       ap.ws_rec = p.ws_rec;
-      e = ikbo::launch_merge(ap, m->hp.n_groups, ikbo::kMxHeadDim, stream, te ? te + 2 : nullptr);
+      e = ikbo::launch_merge(ap, m->hp.n_groups, ikbo::kMxHeadDim, false, stream, te ? te + 2 : nullptr);
       if (e != hipSuccess) return fail_hip(e, "merge launch");
     }
     return m->ring.launched(si, stream);

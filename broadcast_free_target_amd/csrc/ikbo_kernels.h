@@ -30,10 +30,12 @@ struct AttnParams {
   int32_t H;
   int32_t n_q;
   float scale_log2;       // scale * log2(e): scores are kept in base 2
-  float* ws_o;            // split partials: [slots, tile_rows, d] fp32, unnormalised
+  void* ws_o;             // split partials: [slots, tile_rows, d] unnormalised O, fp16 with
+                          // per-half-row power-of-two scales (bf16 kernels) or fp32 (MXFP8)
   float* ws_rec;          // split partials: [slots, tile_rows, 4] row records: running max m,
-                          // running sum l, output unit (row * H + h, -1: no row) and
-                          // nchunk | kind << 16, the last two as int32 bits
+                          // running sum l, output unit (row * H + h, -1: no row) and a tag,
+                          // the last two as int32 bits: nchunk | kind << 4 | c0 << 8 | c1 << 16
+                          // (c_h: the half-row scale codes; 0 for fp32 partials)
   float* lse;             // optional (bf16 kernels, target rows): [n_cand, n_q, H] natural-log
                           // log-sum-exp of each row's scaled scores, or null
   uint64_t* trace;        // optional: [n_items, 6] per-item records (bf16 kernel), or null
@@ -56,7 +58,10 @@ hipError_t launch_attn_bf16(const AttnParams& p, int d, int stages, int grid, hi
 hipError_t launch_attn_bf16_w8(const AttnParams& p, int d, int grid, hipStream_t stream, hipEvent_t* ev = nullptr);
 hipError_t launch_attn_f32(const AttnParams& p, int d, int grid, hipStream_t stream, hipEvent_t* ev = nullptr);
 // Merges the split-KV partials of groups 0 .. n_groups-1 into the bf16 outputs.
-hipError_t launch_merge(const AttnParams& p, int n_groups, int d, hipStream_t stream, hipEvent_t* ev = nullptr);
+// half_partials: the bf16 kernels' fp16 partials (any d); else fp32 partials
+// (the MXFP8 kernel's, d = 128).
+hipError_t launch_merge(const AttnParams& p, int n_groups, int d, bool half_partials, hipStream_t stream,
+                        hipEvent_t* ev = nullptr);
 
 // Materialised broadcast: for each of n local candidates, copy `len[c]` rows of
 // `row_bytes` bytes from k/v at src_row[c] to kb/vb at dst_row[c].

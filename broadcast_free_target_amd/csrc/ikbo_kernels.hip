@@ -81,11 +81,32 @@ __device__ __forceinline__ float row_lse(float m, float l) {
   return l > 0.0f ? (m + __log2f(l)) * 0.69314718055994531f : kNegInf;
 }
 
-// Row record of a split partial: m, l, output unit (-1 when the tile row is
-// empty) and nchunk | kind << 16.
-__device__ __forceinline__ f32x4_t split_record(float m, float l, int64_t qrow, const WorkItem& it, int H) {
+// Split partials of the bf16 kernels: per row and chunk, the unnormalised O in
+// fp16, each half-row (d < D/2, d >= D/2) scaled by its own power of two, and
+// a 16-byte row record {m, l, output unit (-1 when the tile row is empty),
+// tag}.  tag = nchunk | kind << 4 | c0 << 8 | c1 << 16, where c_h is the
+// biased fp32 exponent field of the half-row's largest |O|: the stored value
+// is O * 2^(141 - c_h), whose largest magnitude then lies in [2^14, 2^15)
+// (fp16's top binade; a half-row of zeros stores zeros), and the merge
+// multiplies back by 2^(c_h - 141), exactly.  (The MXFP8 kernel's partials
+// stay fp32, with tag = nchunk.)
+__device__ __forceinline__ int half_code(float maxabs) {
+  return static_cast<int>((__builtin_bit_cast(uint32_t, maxabs) >> 23) & 255u);
+}
+__device__ __forceinline__ int split_tag(const WorkItem& it, int c0, int c1) {
+  return it.nchunk | (it.kind << 4) | (c0 << 8) | (c1 << 16);
+}
+__device__ __forceinline__ f32x4_t split_record(float m, float l, int64_t qrow, const WorkItem& it, int H, int tag) {
   const int unit = qrow < 0 ? -1 : static_cast<int>(qrow * H + it.h);
-  return f32x4_t{m, l, __builtin_bit_cast(float, unit), __builtin_bit_cast(float, it.nchunk | (it.kind << 16))};
+  return f32x4_t{m, l, __builtin_bit_cast(float, unit), __builtin_bit_cast(float, tag)};
+}
+// Four values times 2^(141 - code), rounded to fp16 (nearest even), packed.
+__device__ __forceinline__ u32x2_t pack4_f16_scaled(float a, float b, float c, float d, int code) {
+  typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+  const int e = 141 - code;
+  const f16x4_t v = {static_cast<_Float16>(__builtin_ldexpf(a, e)), static_cast<_Float16>(__builtin_ldexpf(b, e)),
+                     static_cast<_Float16>(__builtin_ldexpf(c, e)), static_cast<_Float16>(__builtin_ldexpf(d, e))};
+  return __builtin_bit_cast(u32x2_t, v);
 }
 
 // Chunk weights of one row of a split group: w_c = 2^(m_c - M) / L with
@@ -581,17 +602,31 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
       }
     } else {
       const int64_t slot = static_cast<int64_t>(it.slot0) + it.chunk;
+      // value i of block mb is column mb*32 + (i/4)*8 + g*4 + i%4: in half-row 1
+      // when mb*32 + (i/4)*8 >= D/2 (the lane part never crosses it)
+      auto upper = [](int mb, int i) { return mb * 32 + (i / 4) * 8 >= D / 2; };
+      float mx0 = 0.0f, mx1 = 0.0f;
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (upper(mb, i)) mx1 = fmaxf(mx1, __builtin_fabsf(oacc[mb][i]));
+          else mx0 = fmaxf(mx0, __builtin_fabsf(oacc[mb][i]));
+        }
+      const int c0 = half_code(pair_max(mx0)), c1 = half_code(pair_max(mx1));
       if (r_w < it.nrows) {
-        float* wo = P.ws_o + (slot * kBM + r_w) * D + g * 4;
+        uint16_t* wo = static_cast<uint16_t*>(P.ws_o) + (slot * kBM + r_w) * D + g * 4;
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4)
-            *reinterpret_cast<f32x4_t*>(wo + mb * 32 + i4 * 8) =
-                f32x4_t{oacc[mb][i4 * 4 + 0], oacc[mb][i4 * 4 + 1], oacc[mb][i4 * 4 + 2], oacc[mb][i4 * 4 + 3]};
+            *reinterpret_cast<u32x2_t*>(wo + mb * 32 + i4 * 8) =
+                pack4_f16_scaled(oacc[mb][i4 * 4 + 0], oacc[mb][i4 * 4 + 1], oacc[mb][i4 * 4 + 2],
+                                 oacc[mb][i4 * 4 + 3], upper(mb, i4 * 4) ? c1 : c0);
       }
       if (g == 0)  // every tile row gets a record; empty rows are marked
-        *reinterpret_cast<f32x4_t*>(P.ws_rec + (slot * kBM + r_w) * 4) = split_record(m_run, l_run, qrow, it, P.H);
+        *reinterpret_cast<f32x4_t*>(P.ws_rec + (slot * kBM + r_w) * 4) =
+            split_record(m_run, l_run, qrow, it, P.H, split_tag(it, c0, c1));
     }
     wait_vmcnt<0>();  // epilogue stores retire before the next item's copies are counted
     if (P.trace && tid == 0) {
@@ -648,7 +683,7 @@ struct Step {
 
 // Merge the partner half's (O, m, l) into this wave's own values v in
 // [V0, V0 + hv) and write them: the final bf16 rows, or the split partial
-// (write_rec: this lane also writes the row's record).
+// (write_rec: this lane also writes its half's part of the row's record).
 template <int D, int V0>
 __device__ __forceinline__ void finish_half(const AttnParams& P, const WorkItem& it, f32x16_t (&oacc)[D / 32],
                                             float m_run, float l_run, const float* __restrict__ xo,
@@ -679,18 +714,38 @@ __device__ __forceinline__ void finish_half(const AttnParams& P, const WorkItem&
       }
     }
   } else {
+    // This wave's values v = V0 .. V0+HV-1 (column (v/16)*32 + ((v%16)/4)*8 +
+    // g*4 + v%4) all lie in half-row V0 / HV (d < D/2 or d >= D/2); the other
+    // half-row's wave writes that half's exponent into the record.
     const int64_t slot = static_cast<int64_t>(it.slot0) + it.chunk;
+    float mx = 0.0f;
+#pragma unroll
+    for (int j = 0; j < HV; ++j) mx = fmaxf(mx, __builtin_fabsf(oacc[(V0 + j) / 16][(V0 + j) % 16]));
+    const int code = half_code(pair_max(mx));
     if (r_w < it.nrows) {
-      float* wo = P.ws_o + (slot * kBM + r_w) * D + g * 4;
+      uint16_t* wo = static_cast<uint16_t*>(P.ws_o) + (slot * kBM + r_w) * D + g * 4;
 #pragma unroll
       for (int j = 0; j < HV; j += 4) {
         const int v = V0 + j, mb = v / 16, i = v % 16;
-        *reinterpret_cast<f32x4_t*>(wo + mb * 32 + (i / 4) * 8) =
-            f32x4_t{oacc[mb][i], oacc[mb][i + 1], oacc[mb][i + 2], oacc[mb][i + 3]};
+        *reinterpret_cast<u32x2_t*>(wo + mb * 32 + (i / 4) * 8) =
+            pack4_f16_scaled(oacc[mb][i], oacc[mb][i + 1], oacc[mb][i + 2], oacc[mb][i + 3], code);
       }
     }
-    if (write_rec)  // every tile row gets a record; empty rows are marked
-      *reinterpret_cast<f32x4_t*>(P.ws_rec + (slot * kBM + r_w) * 4) = split_record(M, L, qrow, it, P.H);
+    // every tile row gets a record (empty rows are marked): m, l, unit and the
+    // tag's low half from half-row 0's wave, the tag's high half (c1) from
+    // half-row 1's: separate bytes, no overlap
+    float* rec = P.ws_rec + (slot * kBM + r_w) * 4;
+    if (write_rec) {
+      if (V0 == 0) {
+        const f32x4_t r = split_record(M, L, qrow, it, P.H, 0);
+        rec[0] = r[0];
+        rec[1] = r[1];
+        rec[2] = r[2];
+        reinterpret_cast<uint16_t*>(rec + 3)[0] = static_cast<uint16_t>(split_tag(it, code, 0) & 0xffff);
+      } else {
+        reinterpret_cast<uint16_t*>(rec + 3)[1] = static_cast<uint16_t>(code);
+      }
+    }
   }
 }
 
@@ -868,7 +923,7 @@ __global__ __launch_bounds__(512, 1) void ikbo_attn_bf16_w8_kernel(AttnParams P)
       const float* xo = xbuf + partner * S::hv * 64 + lane;
       const float pm = mlbuf[(partner * 64 + lane) * 2 + 0];
       const float pl = mlbuf[(partner * 64 + lane) * 2 + 1];
-      const bool write_rec = kh == 0 && (lane >> 5) == 0;
+      const bool write_rec = (lane >> 5) == 0;  // one lane per row in each half
       if (kh == 0)
         finish_half<D, 0>(P, it, oacc, m_run, l_run, xo, pm, pl, qrow, causal, r_w, lane, write_rec);
       else
@@ -898,7 +953,7 @@ __global__ __launch_bounds__(512, 1) void ikbo_attn_bf16_w8_kernel(AttnParams P)
 // and are ignored), then one 16-byte slice of O per chunk, computes its row's
 // chunk weights and sums the weighted slices in chunk order.
 
-template <int D>
+template <int D, bool HALF>
 __global__ __launch_bounds__(256) void ikbo_merge_kernel(AttnParams P) {
   constexpr int TPR = D / 4;      // threads per row
   constexpr int RPB = 256 / TPR;  // rows per block
@@ -914,13 +969,26 @@ __global__ __launch_bounds__(256) void ikbo_merge_kernel(AttnParams P) {
   const float unit_f = rec[0][2], tag_f = rec[0][3];
   const int unit = __builtin_bit_cast(int, unit_f);
   const int tag = __builtin_bit_cast(int, tag_f);
-  const int nchunk = tag & 0xffff;
+  const int nchunk = tag & 15, kind = (tag >> 4) & 1;
   if (unit < 0) return;  // no row here
   f32x4_t o[kMaxSplit];
 #pragma unroll
-  for (int ch = 0; ch < kMaxSplit; ++ch)
-    o[ch] = ch < nchunk ? *reinterpret_cast<const f32x4_t*>(P.ws_o + ((slot0 + ch) * kBM + r) * D + d0)
-                        : f32x4_t{0, 0, 0, 0};
+  for (int ch = 0; ch < kMaxSplit; ++ch) {
+    const int64_t at = ((slot0 + ch) * kBM + r) * D + d0;
+    if constexpr (HALF) {
+      typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+      // this slice's half-row exponent, from the chunk's own record
+      const float ct = rec[ch][3];
+      const int e = ((__builtin_bit_cast(int, ct) >> (d0 < D / 2 ? 8 : 16)) & 255) - 141;
+      const f16x4_t x = ch < nchunk ? *reinterpret_cast<const f16x4_t*>(static_cast<const uint16_t*>(P.ws_o) + at)
+                                    : f16x4_t{0, 0, 0, 0};
+      o[ch] = f32x4_t{__builtin_ldexpf(static_cast<float>(x[0]), e), __builtin_ldexpf(static_cast<float>(x[1]), e),
+                      __builtin_ldexpf(static_cast<float>(x[2]), e), __builtin_ldexpf(static_cast<float>(x[3]), e)};
+    } else {
+      o[ch] = ch < nchunk ? *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(P.ws_o) + at)
+                          : f32x4_t{0, 0, 0, 0};
+    }
+  }
   float m[kMaxSplit], l[kMaxSplit], w[kMaxSplit];
 #pragma unroll
   for (int ch = 0; ch < kMaxSplit; ++ch) {
@@ -939,9 +1007,9 @@ __global__ __launch_bounds__(256) void ikbo_merge_kernel(AttnParams P) {
     case 7: packed = weigh_slice<7>(w, o); break;
     default: packed = weigh_slice<8>(w, o); break;
   }
-  uint16_t* ob = static_cast<uint16_t*>((tag >> 16) == kKindSelf ? P.out_user : P.out_cand);
+  uint16_t* ob = static_cast<uint16_t*>(kind == kKindSelf ? P.out_user : P.out_cand);
   *reinterpret_cast<u32x2_t*>(ob + static_cast<int64_t>(unit) * D + d0) = packed;
-  if (P.lse && d0 == 0 && (tag >> 16) == kKindTarget) {
+  if (P.lse && d0 == 0 && kind == kKindTarget) {
     // the row's log-sum-exp over all chunks: 2^M sum_c 2^(m_c - M) l_c
     float M = kNegInf;
 #pragma unroll
@@ -1127,14 +1195,20 @@ hipError_t launch_attn_bf16_w8(const AttnParams& p, int d, int grid, hipStream_t
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const AttnParams& p, int n_groups, int d, hipStream_t stream, hipEvent_t* ev) {
+hipError_t launch_merge(const AttnParams& p, int n_groups, int d, bool half_partials, hipStream_t stream,
+                        hipEvent_t* ev) {
   if (n_groups <= 0) return hipSuccess;
   const dim3 grid(n_groups, kBM / (256 / (d / 4)));
-  switch (d) {
-    case 128: IKBO_LAUNCH(ikbo_merge_kernel<128>, grid, dim3(256), p); break;
-    case 64: IKBO_LAUNCH(ikbo_merge_kernel<64>, grid, dim3(256), p); break;
-    case 32: IKBO_LAUNCH(ikbo_merge_kernel<32>, grid, dim3(256), p); break;
-    default: return hipErrorInvalidValue;
+  if (half_partials) {
+    switch (d) {
+      case 128: IKBO_LAUNCH((ikbo_merge_kernel<128, true>), grid, dim3(256), p); break;
+      case 64: IKBO_LAUNCH((ikbo_merge_kernel<64, true>), grid, dim3(256), p); break;
+      case 32: IKBO_LAUNCH((ikbo_merge_kernel<32, true>), grid, dim3(256), p); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    if (d != 128) return hipErrorInvalidValue;
+    IKBO_LAUNCH((ikbo_merge_kernel<128, false>), grid, dim3(256), p);
   }
   return hipGetLastError();
 }
