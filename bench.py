@@ -36,7 +36,7 @@ PEAK_F32_TFLOPS = 157.3
 KERNEL_NAMES = {0: "ikbo_attn_f32_kernel<{d}>", 1: "ikbo_attn_bf16_w8_kernel<{d}, 2>",
                 2: "ikbo_attn_bf16_kernel<{d}, 2>",
                 4: "ikbo_attn_bf16_kernel<{d}, 2>"}  # 4: the 4-wave kernel visiting key tiles in reverse
-MERGE_KERNEL = "ikbo_merge_kernel<{d}>"
+MERGE_KERNEL = "ikbo_merge_kernel<{d}, true>"
 
 WORKLOAD_TEXT = {
     "c1_tiny_f32": "tiny fp32: 4 users, L~U[16,64], 20 candidates, n_q=1, H=2, d=32",
