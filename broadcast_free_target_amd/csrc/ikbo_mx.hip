@@ -48,6 +48,7 @@ constexpr int kStK = 0, kStV = 8192, kStKS = 16384, kStVS = 16640, kStSpare = 16
 constexpr int kCopies = 5;  // copies per thread per stage: 2 K, 2 V, 1 scale
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 
@@ -58,7 +59,6 @@ typedef __attribute__((address_space(3))) v2i lds_v2i;
 // by the two 16-lane groups of a half) the even keys, and the odd ones, get
 // values that differ in bits 1-2, so the chunk pair stays on distinct banks.
 __device__ __forceinline__ int mx_swz(int key) { return (((key >> 1) & 1) << 1) | (((key >> 3) & 1) << 2) | ((key >> 2) & 1); }
-__device__ __forceinline__ int mx_off(int key, int chunk) { return key * 128 + ((chunk ^ mx_swz(key)) << 4); }
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -188,6 +188,23 @@ __global__ __launch_bounds__(kT, 2) void ikbo_attn_mx_kernel(MxParams P) {
   // Transposed V reads: lane (2r + h) of each 16-lane group points at key row r
   // of the read, byte half h of the group's 16-column chunk.
   const int tr_r = (lane & 15) >> 1, tr_h = lane & 1, tr_grp = (lane >> 4) & 1;
+  // Per-lane LDS byte offsets of the tile reads, computed once: the swizzle
+  // only sees key bits 1-3, so it is a lane constant and the block (K: 32
+  // keys) or read (V: 16 keys) index only adds an immediate.
+  //   K fragment i (chunk 2i + g) of key 32b + n:  koffs[i] + 4096 b
+  //   V^T read rd of column block mb, key 16 rd + kl with
+  //   kl = 8 (tr_r / 4) + 4 g + tr_r % 4:          voffs[mb] + 2048 rd
+  int koffs[4], voffs[4];
+  {
+    const int swk = mx_swz(n);
+    const int kl = 8 * (tr_r >> 2) + 4 * g + (tr_r & 3);
+    const int swv = mx_swz(kl);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      koffs[i] = n * 128 + (((2 * i + g) ^ swk) << 4);
+      voffs[i] = kl * 128 + (((2 * i + tr_grp) ^ swv) << 4) + 8 * tr_h;
+    }
+  }
 
   const int G = gridDim.x;
   const int wg = logical_wg();
@@ -291,17 +308,15 @@ __global__ __launch_bounds__(kT, 2) void ikbo_attn_mx_kernel(MxParams P) {
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const int key = 32 * b + n;
-        const u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(st + kStK + mx_off(key, g));
-        const u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(st + kStK + mx_off(key, 2 + g));
-        const u32x4_t k2 = *reinterpret_cast<const u32x4_t*>(st + kStK + mx_off(key, 4 + g));
-        const u32x4_t k3 = *reinterpret_cast<const u32x4_t*>(st + kStK + mx_off(key, 6 + g));
+        const uint8_t* kt = st + kStK + 4096 * b;
+        const v4i k0 = *reinterpret_cast<const v4i*>(kt + koffs[0]);
+        const v4i k1 = *reinterpret_cast<const v4i*>(kt + koffs[1]);
+        const v4i k2 = *reinterpret_cast<const v4i*>(kt + koffs[2]);
+        const v4i k3 = *reinterpret_cast<const v4i*>(kt + koffs[3]);
         const uint32_t ksc = *reinterpret_cast<const uint32_t*>(st + kStKS + key * 4) >> (8 * g);
-        const v8i ka = {static_cast<int>(k0[0]), static_cast<int>(k0[1]), static_cast<int>(k0[2]),
-                        static_cast<int>(k0[3]), static_cast<int>(k1[0]), static_cast<int>(k1[1]),
-                        static_cast<int>(k1[2]), static_cast<int>(k1[3])};
-        const v8i kb = {static_cast<int>(k2[0]), static_cast<int>(k2[1]), static_cast<int>(k2[2]),
-                        static_cast<int>(k2[3]), static_cast<int>(k3[0]), static_cast<int>(k3[1]),
-                        static_cast<int>(k3[2]), static_cast<int>(k3[3])};
+        // the 32-byte operands as concatenations, so the loads can land in place
+        const v8i ka = __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const v8i kb = __builtin_shufflevector(k2, k3, 0, 1, 2, 3, 4, 5, 6, 7);
         f32x16_t acc = f32x16_t{};
         acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qa, acc, 0, 0, 0, static_cast<int>(ksc), 0,
                                                               static_cast<int>(qsc));
@@ -320,21 +335,15 @@ __global__ __launch_bounds__(kT, 2) void ikbo_attn_mx_kernel(MxParams P) {
       // ---- O^T += V^T . P^T, four 32-column blocks
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        const int chunk = 2 * mb + tr_grp;
-        int va[8];
+        // bytes 8rd .. 8rd+7 of the operand: keys of value indices j = 8rd + r
+        // (block j / 16), key 32 (j / 16) + 8 ((j % 16) / 4) + 4 g + j % 4 = 16 rd + kl
+        v2i w[4];
 #pragma unroll
-        for (int rd = 0; rd < 4; ++rd) {
-          // bytes 8rd .. 8rd+7: keys of value indices j = 8rd + r (block j / 16)
-          const int j = 8 * rd + tr_r;
-          const int jb = j & 15;
-          const int key = 32 * (j >> 4) + 8 * (jb >> 2) + 4 * g + (jb & 3);
-          const v2i w2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (lds_v2i*)(st + kStV + mx_off(key, chunk) + 8 * tr_h));
-          va[2 * rd] = w2[0];
-          va[2 * rd + 1] = w2[1];
-        }
+        for (int rd = 0; rd < 4; ++rd)
+          w[rd] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(st + kStV + voffs[mb] + 2048 * rd));
         const int vsc = st[kStVS + 128 * g + 32 * mb + n];
-        const v8i vf = {va[0], va[1], va[2], va[3], va[4], va[5], va[6], va[7]};
+        const v8i vf = __builtin_shufflevector(__builtin_shufflevector(w[0], w[1], 0, 1, 2, 3),
+                                               __builtin_shufflevector(w[2], w[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf, oacc[mb], 0, 0, 0, vsc, 0, psc);
       }
       __builtin_amdgcn_s_setprio(0);
