@@ -271,12 +271,9 @@ __device__ __forceinline__ void mask_scores(f32x16_t (&s)[2], int key_base, int 
       if (!(b * 32 + (i >> 2) * 8 + (i & 3) < lim)) s[b][i] = fill;
 }
 
-// Online softmax of one tile (scores already masked): lazy reference update,
-// weights, row sum, and the bf16 P^T operands pb[b][s2] of the PV K-steps.
-// Scores stay unscaled; p = exp2(c*s - m_ref), c != 0.
-template <int D>
-__device__ __forceinline__ void softmax_tile(f32x16_t (&s)[2], f32x16_t (&oacc)[D / 32], float& m_run,
-                                             float& l_run, float c, bf16x8_t (&pb)[2][2]) {
+// Largest scaled score of each row in one tile (scores already masked), over
+// both lanes of the row; -inf when every key is masked.
+__device__ __forceinline__ float tile_max(const f32x16_t (&s)[2], float c) {
   float mx;
   if (c >= 0.0f) {
     mx = kNegInf;
@@ -291,13 +288,18 @@ __device__ __forceinline__ void softmax_tile(f32x16_t (&s)[2], f32x16_t (&oacc)[
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fminf(mx, s[b][i]);
   }
-  // Largest scaled score of the row in this tile; -inf when every key is masked.
   float m_tile = mx * c;
   if (!(m_tile == m_tile)) m_tile = kNegInf;
-  m_tile = pair_max(m_tile);
-  // Lazy rescale: the reference m_ref only moves when the row max exceeds it by
-  // more than 8 (a factor 256 in p), so most tiles skip the O rescale.  O and l
-  // always share one reference, so the final O / l is unchanged.
+  return pair_max(m_tile);
+}
+
+// Lazy reference update of the online softmax for a tile with row max m_tile:
+// the reference m_ref only moves when the row max exceeds it by more than 8 (a
+// factor 256 in p), so most tiles skip the O rescale.  O and l always share
+// one reference, so the final O / l is unchanged.  Returns the reference the
+// tile's weights are taken against: p = exp2(c*s - m_ref), c != 0.
+template <int D>
+__device__ __forceinline__ float ref_update(float m_tile, f32x16_t (&oacc)[D / 32], float& m_run, float& l_run) {
   const bool need = m_tile > m_run + 8.0f;
   if (__any(need)) {
     const float m_new = need ? m_tile : m_run;
@@ -307,7 +309,20 @@ __device__ __forceinline__ void softmax_tile(f32x16_t (&s)[2], f32x16_t (&oacc)[
     for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
     m_run = m_new;
   }
-  const float m_use = (m_run == kNegInf) ? 0.0f : m_run;  // a row with no live key yet
+  return (m_run == kNegInf) ? 0.0f : m_run;  // a row with no live key yet
+}
+
+// First half of the online softmax of one tile: row max and reference update.
+template <int D>
+__device__ __forceinline__ float softmax_ref(const f32x16_t (&s)[2], f32x16_t (&oacc)[D / 32], float& m_run,
+                                             float& l_run, float c) {
+  return ref_update<D>(tile_max(s, c), oacc, m_run, l_run);
+}
+
+// Second half: the weights, their row sum and the bf16 P^T operands pb[b][s2]
+// of the PV K-steps.
+__device__ __forceinline__ void softmax_exp(f32x16_t (&s)[2], float m_use, float c, float& l_run,
+                                            bf16x8_t (&pb)[2][2]) {
   float rs = 0.0f;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
@@ -328,6 +343,14 @@ __device__ __forceinline__ void softmax_tile(f32x16_t (&s)[2], f32x16_t (&oacc)[
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int j = 0; j < 8; ++j) pb[b][s2][j] = static_cast<__bf16>(s[b][s2 * 8 + j]);
+}
+
+// Online softmax of one tile: both halves.
+template <int D>
+__device__ __forceinline__ void softmax_tile(f32x16_t (&s)[2], f32x16_t (&oacc)[D / 32], float& m_run,
+                                             float& l_run, float c, bf16x8_t (&pb)[2][2]) {
+  const float m_use = softmax_ref<D>(s, oacc, m_run, l_run, c);
+  softmax_exp(s, m_use, c, l_run, pb);
 }
 
 // V^T operand of PV MFMA j of the tile (see pv_tile): lane k of each 16-lane
@@ -385,32 +408,74 @@ __device__ __forceinline__ void pv_tile(const uint16_t* __restrict__ Vs, const b
   }
 }
 
-// PRIO: the wave raises its priority while it issues MFMAs (s_setprio), so
-// that when the other wave on its SIMD (of the other resident workgroup) also
-// wants to issue, the next MFMA goes first and the softmax fills the matrix
-// cores' busy cycles.  PRE: operands of the first PRE PV MFMAs are read before
-// the softmax (0: each PV operand two MFMAs ahead of its MFMA).
-template <int D, bool MASK, bool PRIO, int PRE>
+// One tile, computed in order: S, mask, softmax, PV.
+template <int D, bool MASK>
 __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const uint16_t* __restrict__ Vs,
                                           const u32x4_t (&qf)[D / 16], f32x16_t (&oacc)[D / 32],
                                           float& m_run, float& l_run, int key_base, int key_end,
                                           bool causal, int row_tok, float c, int lane, const TileOffsets<D>& to) {
   f32x16_t s[2];
-  if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
   qk_tile<D>(Ks, qf, s, to);
-  i16x8_t vpre[PRE > 0 ? PRE : 1];
-  if constexpr (PRE > 0) {
+  if (MASK) mask_scores(s, key_base, key_end, causal, row_tok, c, lane);
+  bf16x8_t pb[2][2];
+  softmax_tile<D>(s, oacc, m_run, l_run, c, pb);
+  const i16x8_t none[1] = {};
+  pv_tile<D, 0>(Vs, pb, oacc, to, none);
+}
+
+// One tile of the K-ahead loop of the two-per-CU kernel: the softmax and PV of
+// tile t, whose scores s were computed during tile t-1.  With NEXT, the S MFMAs
+// of tile t+1 (into sn, from the K tile at Kn) are interleaved with tile t's
+// exponentials: the matrix cores work on the next scores while the VALU forms
+// this tile's weights, inside one wave.
+template <int D, bool MASK, bool NEXT>
+__device__ __forceinline__ void tile_step_ahead(const uint16_t* __restrict__ Kn, const uint16_t* __restrict__ Vs,
+                                                const u32x4_t (&qf)[D / 16], f32x16_t (&s)[2], f32x16_t (&sn)[2],
+                                                f32x16_t (&oacc)[D / 32], float& m_run, float& l_run, int key_base,
+                                                int key_end, bool causal, int row_tok, float c, int lane,
+                                                const TileOffsets<D>& to) {
+  if (MASK) mask_scores(s, key_base, key_end, causal, row_tok, c, lane);
+  const float m_use = softmax_ref<D>(s, oacc, m_run, l_run, c);
+  constexpr int PRE = kPvPre<D>;
+  bf16x8_t pb[2][2];
+  i16x8_t vpre[PRE];
+  if constexpr (NEXT) {
+    constexpr int NS = D / 16;  // MFMA K-steps per 32-key block
+    u32x4_t a[2][NS];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int st = 0; st < NS; ++st) a[b][st] = *reinterpret_cast<const u32x4_t*>(Kn + b * 32 * D + to.koff[st]);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      sn[b] = f32x16_t{};
+#pragma unroll
+      for (int st = 0; st < NS; ++st)
+        sn[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[b][st]), as_bf16x8(qf[st]), sn[b], 0, 0, 0);
+    }
+    softmax_exp(s, m_use, c, l_run, pb);
+#pragma unroll
+    for (int j = 0; j < PRE; ++j) vpre[j] = v_operand<D>(Vs, j, to);
+    // K fragments three ahead of their MFMAs; between consecutive MFMAs a
+    // share of the exponential phase's VALU work (about 112 instructions).
+    constexpr int NM = 2 * NS, kVal = 112 / NM;
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+    for (int j = 0; j < NM; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (j < NM - 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, kVal, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    softmax_exp(s, m_use, c, l_run, pb);
 #pragma unroll
     for (int j = 0; j < PRE; ++j) vpre[j] = v_operand<D>(Vs, j, to);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
-  if (MASK) mask_scores(s, key_base, key_end, causal, row_tok, c, lane);
-  bf16x8_t pb[2][2];
-  softmax_tile<D>(s, oacc, m_run, l_run, c, pb);
-  if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_s_setprio(1);
   pv_tile<D, PRE>(Vs, pb, oacc, to, vpre);
-  if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_s_setprio(0);
 }
 
 template <int D, int NST>
@@ -512,6 +577,25 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
         copy16_to_lds(vbase + off, dk + static_cast<uint32_t>(T::elems * 2));
       }
     };
+    // One K or V tile (base kbase or vbase) of the t-th tile visited, to the
+    // LDS byte address dst (the K-ahead ring of the two-per-CU kernel).
+    auto issue_one = [&](int t, uint32_t dst, const uint16_t* base) {
+      const int tt = tile_of(t);
+      if (whole_fast && (tt + 1) * kBN <= nkv) {
+        const uint16_t* bt = base + static_cast<int64_t>(tt) * kBN * row_stride;
+#pragma unroll
+        for (int r = 0; r < T::loads; ++r)
+          copy16_to_lds_s(bt, ld_off[r], dst + static_cast<uint32_t>((kThreads * r + 64 * wave_u) * 16));
+        return;
+      }
+#pragma unroll
+      for (int r = 0; r < T::loads; ++r) {
+        const int key = min(tt * kBN + ld_row[r], nkv - 1);
+        copy16_to_lds(base + key * row_stride + ld_chunk[r] * 8,
+                      dst + static_cast<uint32_t>((kThreads * r + 64 * wave_u) * 16));
+      }
+    };
+    constexpr uint32_t kStageBytes = T::stage * 2, kTileBytes = T::elems * 2;
 
     const bool wave_has_rows = wave * 32 < it.nrows;
     const int row_tok = it.row0 + r_w;                   // token index (self rows)
@@ -520,9 +604,19 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
 
     // The ring's first copies depend only on the item: issue them before the
     // candidate gather, so their latency overlaps the cand_perm -> Q chain.
+    if constexpr (NST == 2) {
+      // K-ahead ring: stage s holds K tile t and V tile t' with t = t' + 1 once
+      // the loop runs; the prologue brings K(0), V(0) and K(1).
+      if (ntiles > 0) {
+        issue_one(0, lds_base, kbase);
+        issue_one(0, lds_base + kTileBytes, vbase);
+      }
+      if (ntiles > 1) issue_one(1, lds_base + kStageBytes, kbase);
+    } else {
 #pragma unroll
-    for (int t = 0; t < NST - 1; ++t)
-      if (t < ntiles) issue(t);
+      for (int t = 0; t < NST - 1; ++t)
+        if (t < ntiles) issue(t);
+    }
 
     // ---- query fragment (B operand of S^T): row r_w, 16 bytes per MFMA K-step
     int64_t qrow = -1;
@@ -550,6 +644,59 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) asm volatile("" ::"v"(qf[st]));
     if (P.trace) t_ready = now_ticks();
+    // Tile t's keys lie past every row of this wave (causal) or the wave has no rows.
+    auto skip_of = [&](int t) {
+      return !wave_has_rows || (causal && it.k0 + tile_of(t) * kBN > wave_last_tok);
+    };
+    if constexpr (NST == 2) {
+      // K-ahead loop.  At the top of tile t, K(t+1) and V(t) are resident (both
+      // copied during tile t-1) and every wave is done with tile t-1, so K(t+2)
+      // goes to the slot of K(t) (read during tile t-1) and V(t+1) to that of
+      // V(t-1).  S(t) was computed during tile t-1; tile t computes S(t+1)
+      // alongside its own exponentials.  Unrolled by two so that the ring slots and
+      // the two score buffers are compile-time choices.
+      f32x16_t sa[2], sb[2];
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (ntiles > 0 && !skip_of(0)) qk_tile<D>(smem, qf, sa, to);
+      auto body = [&](int t, auto par, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
+        constexpr int p = decltype(par)::value;
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (t + 2 < ntiles) issue_one(t + 2, lds_base + p * kStageBytes, kbase);
+        if (t + 1 < ntiles) issue_one(t + 1, lds_base + (p ^ 1) * kStageBytes + kTileBytes, vbase);
+        if (queue && tid == 0 && t == ntiles - 1) q_mine = G + atomicAdd(&queue[x], 1);
+        const int key_base = it.k0 + tile_of(t) * kBN;
+        const bool next = t + 1 < ntiles && !skip_of(t + 1);
+        const uint16_t* Kn = smem + (p ^ 1) * T::stage;
+        const uint16_t* Vs = smem + p * T::stage + T::elems;
+        if (!skip_of(t)) {
+          const bool need_mask =
+              (key_base + kBN > it.k1) || (causal && key_base + kBN - 1 > it.row0 + wave * 32);
+          if (next) {
+            if (need_mask)
+              tile_step_ahead<D, true, true>(Kn, Vs, qf, sc, sn, oacc, m_run, l_run, key_base, it.k1, causal,
+                                             row_tok, c, lane, to);
+            else
+              tile_step_ahead<D, false, true>(Kn, Vs, qf, sc, sn, oacc, m_run, l_run, key_base, it.k1, causal,
+                                              row_tok, c, lane, to);
+          } else {
+            if (need_mask)
+              tile_step_ahead<D, true, false>(Kn, Vs, qf, sc, sn, oacc, m_run, l_run, key_base, it.k1, causal,
+                                              row_tok, c, lane, to);
+            else
+              tile_step_ahead<D, false, false>(Kn, Vs, qf, sc, sn, oacc, m_run, l_run, key_base, it.k1, causal,
+                                               row_tok, c, lane, to);
+          }
+        } else if (next) {
+          qk_tile<D>(Kn, qf, sn, to);
+        }
+      };
+      for (int t = 0; t < ntiles; t += 2) {
+        body(t, std::integral_constant<int, 0>{}, sa, sb);
+        if (t + 1 < ntiles) body(t + 1, std::integral_constant<int, 1>{}, sb, sa);
+      }
+    } else
     for (int t = 0; t < ntiles; ++t) {
       // Wait for this thread's copies of tile t: later tiles may stay in flight.
       const int after = min(NST - 2, ntiles - 1 - t);
@@ -564,19 +711,15 @@ __global__ __launch_bounds__(kThreads, (NST <= 2 ? 2 : 1)) void ikbo_attn_bf16_k
       if (t + NST - 1 < ntiles) issue(t + NST - 1);
       if (queue && tid == 0 && t == ntiles - 1) q_mine = G + atomicAdd(&queue[x], 1);
       const int key_base = it.k0 + tile_of(t) * kBN;  // first key of this tile, user-relative
-      const bool skip = !wave_has_rows || (causal && key_base > wave_last_tok);
-      if (!skip) {
+      if (!skip_of(t)) {
         const uint16_t* Ks = smem + (t % NST) * T::stage;
         const uint16_t* Vs = Ks + T::elems;
         const bool need_mask = (key_base + kBN > it.k1) || (causal && key_base + kBN - 1 > it.row0 + wave * 32);
-        // two resident workgroups per CU (NST 2): priority while issuing MFMAs
-        constexpr bool kPrio = NST <= 2;
-        constexpr int kPre = kPrio ? kPvPre<D> : 0;
         if (need_mask)
-          tile_step<D, true, kPrio, kPre>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, lane,
+          tile_step<D, true>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, lane,
                                           to);
         else
-          tile_step<D, false, kPrio, kPre>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c,
+          tile_step<D, false>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c,
                                            lane, to);
       }
     }
@@ -891,10 +1034,10 @@ __global__ __launch_bounds__(512, 1) void ikbo_attn_bf16_w8_kernel(AttnParams P)
         const uint16_t* Vs = smem + (s % NST) * S::stage + 2 * S::tile + kh * S::tile;
         const bool need_mask = (key_base + kBN > it.k1) || (causal && key_base + kBN - 1 > it.row0 + rb * 32);
         if (need_mask)
-          tile_step<D, true, false, 0>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, lane,
+          tile_step<D, true>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c, lane,
                                        to);
         else
-          tile_step<D, false, false, 0>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c,
+          tile_step<D, false>(Ks, Vs, qf, oacc, m_run, l_run, key_base, it.k1, causal, row_tok, c,
                                         lane, to);
       }
     }
