@@ -158,6 +158,23 @@ def traffic_from_profiles(workload):
         return None
 
 
+def materialized_traffic_from_profiles(workload):
+    """HBM bytes of one materialised-broadcast step (copy kernel + attention)
+    from the committed rocprofv3 --pmc summary of --materialized-only, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"ikbo_materialized_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as fh:
+            s = json.load(fh)
+        if s.get("kernel_source_hash") != kernel_source_hash():
+            return None
+        return float(s["hbm_bytes_per_step_with_merge"])
+    except Exception:
+        return None
+
+
 def upload(w):
     import torch
     t = {}
@@ -1062,6 +1079,11 @@ def main():
         "materialized_algorithmic_bytes": mat_bytes,
         "ikbo_vs_materialized_bytes_ratio": mat_bytes / byts,
     }
+    mat_measured = materialized_traffic_from_profiles(args.config)
+    if mat_measured is not None and roof.get("traffic"):
+        # both sides' bytes as rocprofv3 counted them (FETCH_SIZE + WRITE_SIZE)
+        extra["materialized_measured_bytes"] = mat_measured
+        extra["ikbo_vs_materialized_bytes_ratio_measured"] = mat_measured / roof["traffic"]
 
     def extras():
         """Cold-cache kernel times, host times of the step's calls, the

@@ -43,3 +43,22 @@ def test_summary_scales_by_the_copy(tmp_path):
     assert s["hbm_bytes_per_launch"] == attn["read_bytes"] + attn["write_bytes"]
     assert s["hbm_bytes_per_step_with_merge"] == s["hbm_bytes_per_launch"] + 50.0 * 1024 * 2 + 5.0 * 1024
     assert s["copy_calibration"]["fetch_scale"] == 2.0 and s["copy_calibration"]["write_scale"] == 1.0
+
+
+def test_committed_traffic_summaries_load_only_on_their_sources(monkeypatch):
+    """The roofline's traffic and the measured materialised ratio come from the
+    committed summaries only while the kernel sources hash as they did when the
+    counters were taken."""
+    sys.path.insert(0, ROOT)
+    import bench
+    with open(os.path.join(ROOT, "profiles", "ikbo_materialized_c2_typical_pmc.json")) as fh:
+        mat = json.load(fh)
+    assert mat["hbm_bytes_per_step_with_merge"] == sum(
+        k["read_bytes"] + k["write_bytes"] for k in mat["kernels"].values())
+    assert mat["kernels"]["ikbo_bcast_copy_kernel"]["dispatches"][0] > 0
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda *a, **k: mat["kernel_source_hash"])
+    assert bench.materialized_traffic_from_profiles("c2_typical") == mat["hbm_bytes_per_step_with_merge"]
+    assert bench.materialized_traffic_from_profiles("c3_skewed") is None  # no summary for it
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda *a, **k: "0" * 16)
+    assert bench.materialized_traffic_from_profiles("c2_typical") is None
+    assert bench.traffic_from_profiles("c2_typical") is None
