@@ -9,7 +9,9 @@
 // bf16 kernel, one workgroup = 4 wave64s = 128 rows (32 rows per wave):
 //   * K/V tiles of 64 keys move HBM -> LDS with global_load_lds_dwordx4
 //     (no register staging) through a ring of NST stages, so up to NST-1
-//     tiles are in flight while one is being computed.  Each tile is stored
+//     tiles are in flight while one is being computed (with two stages, the
+//     two-per-CU variant copies K one tile ahead of V and forms the next
+//     tile's scores during the current tile's exponentials).  Each tile is stored
 //     in natural [key][d] order with its 16-byte chunks XOR-swizzled per row
 //     (bank-conflict-free reads).  Keys past the user's end load the user's
 //     last key again (finite data) and are masked to -inf in the scores.
