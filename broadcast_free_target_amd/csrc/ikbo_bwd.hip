@@ -44,6 +44,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "ikbo_bwd.h"
 #include "ikbo_device.h"
@@ -555,6 +556,12 @@ __global__ __launch_bounds__(kNT8, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
   for (int db = 0; db < kDB; ++db) acc[db] = f32x16_t{};
   const float c2 = P.scale_log2;
   for (int t = 0; t < min(ntiles, NST - 1); ++t) issue(t);
+  // One copy of the tile loop per role (the role is fixed per wave), so that
+  // each loop keeps its accumulators in registers of its own: a loop shared
+  // by both roles had the register allocator copy all 64 accumulator values
+  // at the end of every dK tile to match the dV branch's registers.
+  auto tiles = [&](auto role) {
+  constexpr bool DK = decltype(role)::value;
   for (int t = 0; t < ntiles; ++t) {
     wait_stage(min(ntiles - 1 - t, NST - 2));
     __syncthreads();  // tile t is in LDS; every wave is done with tile t-1's slot
@@ -575,7 +582,7 @@ __global__ __launch_bounds__(kNT8, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
       const float* lse_t = reinterpret_cast<const float*>(slot + 2 * TE * 2);
       const float* dd_t = lse_t + RT;
 
-      if (dk_role) {
+      if constexpr (DK) {
         // one 32-row block at a time keeps S and dP of one block live
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
@@ -642,6 +649,11 @@ __global__ __launch_bounds__(kNT8, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
       }
     }
   }
+  };
+  if (dk_role)
+    tiles(std::true_type{});
+  else
+    tiles(std::false_type{});
 
   // dK^T / dV^T block db: lane value v is d = db*32 + (v/4)*8 + 4*g + v%4 of key n.
   if (key_ok) {
