@@ -466,10 +466,11 @@ __device__ __forceinline__ bf16x8_t tr_rows_at(const uint16_t* T, int lo_off, in
 }
 
 // Eight waves in two roles over the same 128 keys and the same staged rows:
-// waves 0-3 form P and accumulate dV, waves 4-7 form P, dP and dS and
-// accumulate dK (S is formed by both).  Waves w and w+4 share a SIMD, so each
-// SIMD holds one wave of each role and the softmax work of one overlaps the
-// products of the other; each role fits two waves per SIMD.
+// waves 0-3 form S and P and accumulate dV, waves 4-7 form dP meanwhile, take
+// P of the same keys through LDS, form dS and accumulate dK (64 MFMAs per tile
+// and SIMD, S formed once).  Waves w and w+4 share a SIMD, so each SIMD holds
+// one wave of each role and the softmax work of one overlaps the products of
+// the other; each role fits two waves per SIMD.
 constexpr int kNT8 = 512;
 __global__ __launch_bounds__(kNT8, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
   constexpr int RT = kBwdRowsB;          // rows per tile
@@ -481,6 +482,10 @@ __global__ __launch_bounds__(kNT8, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
   constexpr int L0 = 2 * LPT;            // copies per stage of waves 1-7; wave 0 adds two
   static_assert(LPT * kNT8 == RT * kCH && RT == 64 && META >= 2 * RT * 4, "tile shape; lse and D of the tile's rows");
   __shared__ __attribute__((aligned(16))) uint8_t smem[NST * STAGE];
+  // P of the current tile, [key block][row block][value quad][lane]: written by
+  // the dV wave of each 32-key block, read by the dK wave of the same keys in
+  // the same lane layout.
+  __shared__ f32x4_t pshare[4 * 2 * 4 * 64];
 
   const WorkItem it = P.items[blockIdx.x];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -497,11 +502,12 @@ __global__ __launch_bounds__(kNT8, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
   const bool wave_live = it.k0 + kw * 32 < it.k1;
   const int64_t koff = (static_cast<int64_t>(it.kv_base) + key) * rs + static_cast<int64_t>(it.h) * D;
 
-  // This lane's key row of K (and, for the dK role, of V) as B operands.
+  // This lane's key row of K (dV role, for S) or of V (dK role, for dP) as B operands.
   u32x4_t kf[kKS], vf[kKS];
 #pragma unroll
   for (int ks = 0; ks < kKS; ++ks) {
-    kf[ks] = key_ok ? ld16(static_cast<const uint16_t*>(P.k) + koff + ks * 16 + g * 8) : u32x4_t{0u, 0u, 0u, 0u};
+    kf[ks] = key_ok && !dk_role ? ld16(static_cast<const uint16_t*>(P.k) + koff + ks * 16 + g * 8)
+                                : u32x4_t{0u, 0u, 0u, 0u};
     vf[ks] = key_ok && dk_role ? ld16(static_cast<const uint16_t*>(P.v) + koff + ks * 16 + g * 8)
                                : u32x4_t{0u, 0u, 0u, 0u};
   }
@@ -576,70 +582,74 @@ __global__ __launch_bounds__(kNT8, 1) void ikbo_bwd_dkv_kernel(BwdParams P) {
       __syncthreads();
     }
     const LaneOffs lo = lane_offs.opaque();
+    const uint16_t* Qt = reinterpret_cast<const uint16_t*>(slot);
+    const uint16_t* Dt = Qt + TE;
+    const float* lse_t = reinterpret_cast<const float*>(slot + 2 * TE * 2);
+    const float* dd_t = lse_t + RT;
+    // dV waves: S, then P (also handed to the dK wave of the same keys through
+    // LDS); dK waves: dP, formed meanwhile.
+    f32x16_t x[2];
     if (wave_live) {
-      const uint16_t* Qt = reinterpret_cast<const uint16_t*>(slot);
-      const uint16_t* Dt = Qt + TE;
-      const float* lse_t = reinterpret_cast<const float*>(slot + 2 * TE * 2);
-      const float* dd_t = lse_t + RT;
-
       if constexpr (DK) {
-        // one 32-row block at a time keeps S and dP of one block live
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-          f32x16_t sb = f32x16_t{}, dpb = f32x16_t{};
+          x[rb] = f32x16_t{};
 #pragma unroll
-          for (int ks = 0; ks < kKS; ++ks) {
-            sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(Qt + lo.row(rb, ks))), as_bf16x8(kf[ks]), sb,
-                                                         0, 0, 0);
-            dpb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(Dt + lo.row(rb, ks))), as_bf16x8(vf[ks]),
-                                                          dpb, 0, 0, 0);
-          }
+          for (int ks = 0; ks < kKS; ++ks)
+            x[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(Dt + lo.row(rb, ks))), as_bf16x8(vf[ks]),
+                                                            x[rb], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          x[kb] = f32x16_t{};
+#pragma unroll
+          for (int ks = 0; ks < kKS; ++ks)
+            x[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(Qt + lo.row(kb, ks))), as_bf16x8(kf[ks]),
+                                                            x[kb], 0, 0, 0);
+        }
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
             const int rbase = rb * 32 + q4 * 8 + g * 4;
             const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(lse_t + rbase);
-            const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(dd_t + rbase);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float p = exp2_hw(sb[q4 * 4 + i] * c2 - l4[i]);
-              sb[q4 * 4 + i] = p * (dpb[q4 * 4 + i] - d4[i]);  // dS
-            }
+            for (int i = 0; i < 4; ++i) x[rb][q4 * 4 + i] = exp2_hw(x[rb][q4 * 4 + i] * c2 - l4[i]);  // P
+            pshare[((kw * 2 + rb) * 4 + q4) * 64 + lane] =
+                f32x4_t{x[rb][q4 * 4 + 0], x[rb][q4 * 4 + 1], x[rb][q4 * 4 + 2], x[rb][q4 * 4 + 3]};
+          }
+      }
+    }
+    __syncthreads();  // every live key block's P is in LDS
+    if (wave_live) {
+      if constexpr (DK) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int rbase = rb * 32 + q4 * 8 + g * 4;
+            const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(dd_t + rbase);
+            const f32x4_t p4 = pshare[((kw * 2 + rb) * 4 + q4) * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[rb][q4 * 4 + i] = p4[i] * (x[rb][q4 * 4 + i] - d4[i]);  // dS
           }
 #pragma unroll
           for (int j0 = 0; j0 < 2; ++j0) {
-            const bf16x8_t bs = pack8(sb, j0 * 8);
+            const bf16x8_t bs = pack8(x[rb], j0 * 8);
             const int r16 = rb * 32 + j0 * 16;
 #pragma unroll
             for (int db = 0; db < kDB; ++db)
               acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_rows_at(Qt, lo.tr_lo(r16, db), lo.tr_hi(r16, db)),
                                                                 bs, acc[db], 0, 0, 0);
           }
-          __builtin_amdgcn_sched_barrier(0);
         }
       } else {
-        f32x16_t s[2];  // S: rows x this lane's key
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          s[kb] = f32x16_t{};
-#pragma unroll
-          for (int ks = 0; ks < kKS; ++ks)
-            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(Qt + lo.row(kb, ks))), as_bf16x8(kf[ks]),
-                                                            s[kb], 0, 0, 0);
-        }
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int rbase = rb * 32 + q4 * 8 + g * 4;
-            const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(lse_t + rbase);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s[rb][q4 * 4 + i] = exp2_hw(s[rb][q4 * 4 + i] * c2 - l4[i]);  // P
-          }
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
           for (int j0 = 0; j0 < 2; ++j0) {
-            const bf16x8_t bp = pack8(s[rb], j0 * 8);
+            const bf16x8_t bp = pack8(x[rb], j0 * 8);
             const int r16 = rb * 32 + j0 * 16;
 #pragma unroll
             for (int db = 0; db < kDB; ++db)
